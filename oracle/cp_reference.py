@@ -1,0 +1,195 @@
+"""O2: context-parallel decomposition of attention in fp64, plus work counts.
+
+TEST INFRASTRUCTURE ONLY -- see ``oracle/__init__.py``.
+
+This module has its own chunk map; it does not use the HIP library's plan.
+
+* Chunk placement ("Sequence Parallelism IV: Megatron Context Parallel and
+  Load-Balanced Rings", section 3 "Naive Ring Attention Is Imbalanced Under
+  Causal Masks"): the sequence is cut into ``2*cp`` equal chunks and rank ``r``
+  owns one early and one late chunk, ``{r, 2*cp-1-r}`` (the page's cp=4 example
+  is ranks {0,7},{1,6},{2,5},{3,4}).  A rank keeps its two chunks in that
+  order, early chunk first.  The naive placement gives rank ``r`` the
+  contiguous slice ``[r*S/cp, (r+1)*S/cp)`` (same section, and the shard
+  coverage check of "Context Parallelism for Long-Context Training", section
+  "Test sequence divisibility and padding").  Per-rank length is
+  ``S // cp`` ("Context Parallelism in MegaDLMs", section "Sequence
+  Partitioning Across GPUs").
+* Ring (same page, sections 4 "What Actually Moves" and 5 "Overlap"): Q stays
+  on its rank; K/V chunks move to a neighbour each iteration.  The pages fix no
+  direction; rank ``r`` receives from ``r-1``, so at step ``s`` it holds the
+  K/V of rank ``(r - s) mod cp`` and step 0 is its own K/V.
+* Exact merge (section 4): each step yields a partial ``(O_s, lse_s)`` over the
+  keys present; partials are folded with log-sum-exp weights, which reproduces
+  the unsplit softmax exactly up to rounding.
+* Work counts (section 3): per ring iteration, the number of valid (q, k)
+  pairs and of BMxBN tiles holding at least one valid pair, per rank; the
+  imbalance of an iteration is max over ranks / mean over ranks, and the
+  lockstep cost of a whole pass is sum of maxima / sum of means.
+"""
+
+import numpy as np
+
+from .attention import attention
+
+ZIGZAG = "zigzag"
+CONTIGUOUS = "contiguous"
+
+
+def _check(seq_len, cp, layout):
+    if cp < 1:
+        raise ValueError("cp must be >= 1")
+    if layout == ZIGZAG:
+        if seq_len % (2 * cp):
+            raise ValueError("zigzag needs seq_len divisible by 2*cp")
+    elif layout == CONTIGUOUS:
+        if seq_len % cp:
+            raise ValueError("contiguous needs seq_len divisible by cp")
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+
+
+def chunk_size(seq_len, cp, layout):
+    """Length of one chunk: ``S/(2cp)`` for zigzag, ``S/cp`` for contiguous."""
+    _check(seq_len, cp, layout)
+    return seq_len // (2 * cp) if layout == ZIGZAG else seq_len // cp
+
+
+def rank_chunks(cp, layout):
+    """Chunk indices owned by each rank, in the rank's local order."""
+    if layout == ZIGZAG:
+        return [(r, 2 * cp - 1 - r) for r in range(cp)]
+    if layout == CONTIGUOUS:
+        return [(r,) for r in range(cp)]
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def rank_positions(seq_len, cp, rank, layout):
+    """Global token positions of rank ``rank``'s local rows, in local order."""
+    c = chunk_size(seq_len, cp, layout)
+    parts = [np.arange(ch * c, (ch + 1) * c, dtype=np.int64) for ch in rank_chunks(cp, layout)[rank]]
+    return np.concatenate(parts)
+
+
+def ring_source(rank, step, cp):
+    """Rank whose K/V chunks rank ``rank`` holds at ring step ``step``."""
+    return (rank - step) % cp
+
+
+def merge_partial(o_acc, lse_acc, o_s, lse_s):
+    """Fold a partial ``(o_s, lse_s)`` into ``(o_acc, lse_acc)`` exactly.
+
+    Shapes: ``o_* [N, H, D]``, ``lse_* [H, N]``.  A partial with ``lse = -inf``
+    (no valid key) changes nothing; an empty accumulator takes the partial.
+    Otherwise ``lse' = max + log1p(exp(-|lse_acc - lse_s|))`` and
+    ``O' = exp(lse_acc - lse') O_acc + exp(lse_s - lse') O_s``.
+    Returns new arrays.
+    """
+    o_acc = np.array(o_acc, dtype=np.float64)
+    lse_acc = np.array(lse_acc, dtype=np.float64)
+    o_s = np.asarray(o_s, dtype=np.float64)
+    lse_s = np.asarray(lse_s, dtype=np.float64)
+    a = lse_acc.T  # [N, H]
+    b = lse_s.T
+    take = np.isneginf(a) & ~np.isneginf(b)
+    both = ~np.isneginf(a) & ~np.isneginf(b)
+    new = a.copy()
+    new[take] = b[take]
+    o_new = o_acc.copy()
+    o_new[take] = o_s[take]
+    if np.any(both):
+        aa, bb = a[both], b[both]
+        lse_new = np.maximum(aa, bb) + np.log1p(np.exp(-np.abs(aa - bb)))
+        wa = np.exp(aa - lse_new)
+        wb = np.exp(bb - lse_new)
+        o_new[both] = wa[:, None] * o_acc[both] + wb[:, None] * o_s[both]
+        new[both] = lse_new
+    return o_new, new.T.copy()
+
+
+def rank_forward(q, k, v, cp, rank, *, layout=ZIGZAG, causal=True, scale=None, step_order=None):
+    """One rank's share: its Q rows against every rank's K/V, one ring step at a time.
+
+    q, k, v: natural-order ``[S, H, D]``.  Returns ``(O_loc [n, H, D],
+    LSE_loc [H, n], positions [n])`` for the rank's local rows.
+    ``step_order`` permutes the ring steps (the merge is order-invariant).
+    """
+    seq_len, heads, dim = np.shape(q)
+    qpos = rank_positions(seq_len, cp, rank, layout)
+    qloc = np.asarray(q)[qpos]
+    o_acc = np.zeros((qpos.size, heads, dim), dtype=np.float64)
+    lse_acc = np.full((heads, qpos.size), -np.inf, dtype=np.float64)
+    steps = range(cp) if step_order is None else step_order
+    for s in steps:
+        j = ring_source(rank, s, cp)
+        kpos = rank_positions(seq_len, cp, j, layout)
+        o_s, lse_s = attention(qloc, np.asarray(k)[kpos], np.asarray(v)[kpos],
+                               causal=causal, scale=scale, q_pos=qpos, k_pos=kpos)
+        o_acc, lse_acc = merge_partial(o_acc, lse_acc, o_s, lse_s)
+    return o_acc, lse_acc, qpos
+
+
+def full_forward(q, k, v, cp, *, layout=ZIGZAG, causal=True, scale=None, step_orders=None):
+    """Every rank's share, assembled back to natural token order.
+
+    Returns ``(O [S, H, D], LSE [H, S])``.
+    """
+    seq_len, heads, dim = np.shape(q)
+    out = np.zeros((seq_len, heads, dim), dtype=np.float64)
+    lse = np.full((heads, seq_len), -np.inf, dtype=np.float64)
+    for r in range(cp):
+        order = None if step_orders is None else step_orders[r]
+        o, l, pos = rank_forward(q, k, v, cp, r, layout=layout, causal=causal, scale=scale, step_order=order)
+        out[pos] = o
+        lse[:, pos] = l
+    return out, lse
+
+
+def step_valid_pairs(seq_len, cp, layout, causal, rank, step):
+    """Valid (q, k) pairs of one head in ring step ``step`` of rank ``rank``."""
+    qpos = rank_positions(seq_len, cp, rank, layout)
+    kpos = rank_positions(seq_len, cp, ring_source(rank, step, cp), layout)
+    if not causal:
+        return int(qpos.size * kpos.size)
+    ks = np.sort(kpos)
+    return int(np.searchsorted(ks, qpos, side="right").sum())
+
+
+def step_valid_tiles(seq_len, cp, layout, causal, rank, step, bm, bn):
+    """Tiles of ``bm`` local rows x ``bn`` local keys holding a valid pair.
+
+    Tiles are laid on the rank's local row index and on the source's local key
+    index from 0, the last tile of each axis clipped at the buffer end.
+    """
+    qpos = rank_positions(seq_len, cp, rank, layout)
+    kpos = rank_positions(seq_len, cp, ring_source(rank, step, cp), layout)
+    if not causal:
+        return -(-qpos.size // bm) * -(-kpos.size // bn)
+    # A tile holds a causal pair (k <= q) exactly when its smallest key
+    # position is not after its largest query position.
+    qmax = [int(qpos[i0:i0 + bm].max()) for i0 in range(0, qpos.size, bm)]
+    kmin = [int(kpos[j0:j0 + bn].min()) for j0 in range(0, kpos.size, bn)]
+    return sum(1 for a in qmax for b in kmin if b <= a)
+
+
+def imbalance(work):
+    """Load imbalance of a ``[cp, cp]`` (rank, step) work table.
+
+    Returns ``(per_step, aggregate)``: per step ``max_r w / mean_r w`` (1.0 when
+    the step has no work at all) and ``sum_s max_r w / sum_s mean_r w``.
+    """
+    w = np.asarray(work, dtype=np.float64)
+    mx = w.max(axis=0)
+    mean = w.mean(axis=0)
+    per_step = [float(a / b) if b > 0 else 1.0 for a, b in zip(mx, mean)]
+    aggregate = float(mx.sum() / mean.sum()) if mean.sum() > 0 else 1.0
+    return per_step, aggregate
+
+
+def valid_flops(pairs, heads, head_dim):
+    """Mask-valid FLOPs: ``4 * head_dim`` per valid pair per head.
+
+    ``Q K^T`` and ``P V`` each cost ``head_dim`` multiply-adds (two flops each)
+    per valid pair; softmax and masked or skipped work are not counted.
+    """
+    return 4 * int(head_dim) * int(heads) * int(pairs)

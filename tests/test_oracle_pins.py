@@ -1,0 +1,422 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test fixes one part of the oracle with a closed form, an invariant, brute
+force on tiny inputs, an independent library routine, or a value printed on
+the pages (``tests/golden/page_facts.json``).  The mutation tests at the end
+plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch them.
+"""
+
+import importlib
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+
+oracle_attention_mod = importlib.import_module("oracle.attention")
+cp_reference = importlib.import_module("oracle.cp_reference")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# --------------------------------------------------------------------------
+# O1: unsplit attention
+# --------------------------------------------------------------------------
+
+def _brute_force(q, k, v, causal, scale):
+    """Pure-Python loops with math.exp; tiny inputs only."""
+    sq, heads, dim = q.shape
+    sk = k.shape[0]
+    out = [[[0.0] * dim for _ in range(heads)] for _ in range(sq)]
+    lse = [[-math.inf] * sq for _ in range(heads)]
+    for h in range(heads):
+        for i in range(sq):
+            keys = [j for j in range(sk) if (not causal or j <= i)]
+            if not keys:
+                continue
+            s = {j: scale * sum(float(q[i, h, d]) * float(k[j, h, d]) for d in range(dim)) for j in keys}
+            m = max(s.values())
+            w = {j: math.exp(s[j] - m) for j in keys}
+            l = sum(w.values())
+            for d in range(dim):
+                out[i][h][d] = sum(w[j] * float(v[j, h, d]) for j in keys) / l
+            lse[h][i] = m + math.log(l)
+    return np.array(out), np.array(lse)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("sq,dim", [(1, 1), (5, 3), (8, 4)])
+def test_o1_matches_brute_force(causal, sq, dim):
+    q, k, v = (_rand((sq, 2, dim), s) for s in (1, 2, 3))
+    scale = 1.0 / math.sqrt(dim)
+    o, lse = oracle.attention(q, k, v, causal=causal)
+    bo, blse = _brute_force(q, k, v, causal, scale)
+    assert np.max(np.abs(o - bo)) <= 1e-13
+    assert np.max(np.abs(lse - blse)) <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_o1_matches_torch_sdpa_fp64(causal):
+    """Independent implementation: torch's CPU scaled-dot-product attention in fp64."""
+    sq, heads, dim = 48, 3, 16
+    q, k, v = (_rand((sq, heads, dim), s) for s in (4, 5, 6))
+    o, lse = oracle.attention(q, k, v, causal=causal)
+    tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2).contiguous() for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
+    ref = ref.permute(1, 0, 2).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_o1_lse_matches_scipy_logsumexp(causal):
+    sq, heads, dim = 32, 2, 8
+    q, k, v = (_rand((sq, heads, dim), s) for s in (7, 8, 9))
+    _, lse = oracle.attention(q, k, v, causal=causal)
+    scale = 1.0 / math.sqrt(dim)
+    for h in range(heads):
+        s = scale * np.einsum("id,jd->ij", q[:, h], k[:, h])
+        if causal:
+            s = np.where(np.tril(np.ones((sq, sq), bool)), s, -np.inf)
+        assert np.max(np.abs(lse[h] - scipy.special.logsumexp(s, axis=1))) <= 1e-12
+
+
+def test_o1_closed_form_zero_query_causal():
+    """q = 0: uniform weights over the valid keys, O_i = mean_{j<=i} V_j, LSE_i = ln(i+1)."""
+    sq, heads, dim = 40, 2, 6
+    q = np.zeros((sq, heads, dim))
+    k = _rand((sq, heads, dim), 10)
+    v = _rand((sq, heads, dim), 11)
+    o, lse = oracle.attention(q, k, v, causal=True)
+    expect_o = np.cumsum(v, axis=0) / np.arange(1, sq + 1)[:, None, None]
+    assert np.max(np.abs(o - expect_o)) <= 1e-13
+    assert np.max(np.abs(lse - np.log(np.arange(1, sq + 1))[None, :])) <= 1e-13
+
+
+def test_o1_closed_form_zero_key_bidirectional():
+    sq, heads, dim = 33, 2, 5
+    q = _rand((sq, heads, dim), 12)
+    k = np.zeros((sq, heads, dim))
+    v = _rand((sq, heads, dim), 13)
+    o, lse = oracle.attention(q, k, v, causal=False)
+    assert np.max(np.abs(o - v.mean(axis=0)[None])) <= 1e-13
+    assert np.max(np.abs(lse - math.log(sq))) <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_o1_constant_values_are_reproduced(causal):
+    sq, heads, dim = 20, 2, 4
+    q, k = _rand((sq, heads, dim), 14), _rand((sq, heads, dim), 15)
+    v = np.full((sq, heads, dim), 2.75)
+    o, _ = oracle.attention(q, k, v, causal=causal)
+    assert np.max(np.abs(o - 2.75)) <= 1e-13
+
+
+def test_o1_probability_rows_sum_to_one_and_future_is_zero():
+    sq, heads, dim = 24, 2, 8
+    q, k = _rand((sq, heads, dim), 16), _rand((sq, heads, dim), 17)
+    p = oracle.attention_probabilities(q, k, causal=True)
+    assert np.max(np.abs(p.sum(axis=2) - 1.0)) <= 1e-12
+    upper = np.triu(np.ones((sq, sq), bool), k=1)
+    assert np.all(p[:, upper] == 0.0)
+    assert np.all(p[:, ~upper] > 0.0)
+    # O computed from the explicit P equals O1.
+    v = _rand((sq, heads, dim), 18)
+    o, _ = oracle.attention(q, k, v, causal=True)
+    assert np.max(np.abs(np.einsum("hij,jhd->ihd", p, v) - o)) <= 1e-13
+
+
+@pytest.mark.parametrize("u_scale", [1.0, 1e3])
+def test_o1_key_shift_invariance(u_scale):
+    """K -> K + u leaves O unchanged and shifts LSE_i by scale * <q_i, u>."""
+    sq, heads, dim = 16, 2, 8
+    q, k, v = (_rand((sq, heads, dim), s) for s in (19, 20, 21))
+    u = u_scale * _rand((1, heads, dim), 22)
+    o, lse = oracle.attention(q, k, v, causal=True)
+    o2, lse2 = oracle.attention(q, k + u, v, causal=True)
+    shift = np.einsum("ihd,hd->hi", q, u[0]) / math.sqrt(dim)
+    assert np.all(np.isfinite(o2)) and np.all(np.isfinite(lse2))
+    assert np.max(np.abs(o2 - o)) <= 1e-10
+    assert np.max(np.abs((lse2 - lse) - shift)) <= 1e-9 * max(1.0, np.abs(shift).max())
+
+
+def test_o1_single_token_and_causal_row_zero():
+    q, k, v = (_rand((1, 3, 8), s) for s in (23, 24, 25))
+    o, lse = oracle.attention(q, k, v, causal=False)
+    assert np.array_equal(o, v)
+    assert np.max(np.abs(lse[:, 0] - np.einsum("hd,hd->h", q[0], k[0]) / math.sqrt(8))) <= 1e-14
+    q, k, v = (_rand((12, 3, 8), s) for s in (26, 27, 28))
+    o, lse = oracle.attention(q, k, v, causal=True)
+    assert np.array_equal(o[0], v[0])  # one valid key: weight exactly 1
+    assert np.max(np.abs(lse[:, 0] - np.einsum("hd,hd->h", q[0], k[0]) / math.sqrt(8))) <= 1e-14
+
+
+def test_o1_explicit_positions_equal_reordering():
+    """Masking by global position: permuting rows with their positions permutes the result."""
+    sq, heads, dim = 30, 2, 4
+    q, k, v = (_rand((sq, heads, dim), s) for s in (29, 30, 31))
+    perm = np.random.default_rng(32).permutation(sq)
+    o, lse = oracle.attention(q, k, v, causal=True)
+    o2, lse2 = oracle.attention(q[perm], k[perm], v[perm], causal=True, q_pos=perm, k_pos=perm)
+    assert np.max(np.abs(o2 - o[perm])) <= 1e-13
+    assert np.max(np.abs(lse2 - lse[:, perm])) <= 1e-13
+
+
+# --------------------------------------------------------------------------
+# Chunk placement and ring
+# --------------------------------------------------------------------------
+
+def _facts():
+    with open(os.path.join(GOLDEN, "page_facts.json")) as f:
+        return json.load(f)
+
+
+def test_zigzag_map_matches_page_example():
+    f = _facts()["zigzag_cp4"]
+    got = [list(c) for c in oracle.rank_chunks(f["cp"], "zigzag")]
+    assert got == f["ranks"]
+    assert sorted(itertools.chain(*got)) == list(range(f["chunks"]))
+
+
+def test_per_gpu_length_matches_page_example():
+    f = _facts()["per_gpu_length"]
+    for layout in ("zigzag", "contiguous"):
+        for r in range(f["cp"]):
+            assert oracle.rank_positions(f["seq_length"], f["cp"], r, layout).size == f["per_gpu"]
+
+
+def test_contiguous_shards_cover_each_token_once():
+    f = _facts()["shard_cover"]
+    flat = np.concatenate([oracle.rank_positions(f["n"], f["p"], r, "contiguous") for r in range(f["p"])])
+    assert flat.tolist() == f["flat"]
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
+def test_every_token_owned_exactly_once(layout, cp):
+    seq = 2 * cp * 6
+    flat = np.concatenate([oracle.rank_positions(seq, cp, r, layout) for r in range(cp)])
+    assert sorted(flat.tolist()) == list(range(seq))
+
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 5, 8])
+def test_ring_sources_visit_every_rank_once(cp):
+    for r in range(cp):
+        assert oracle.ring_source(r, 0, cp) == r  # step 0 uses the local K/V
+        assert sorted(oracle.ring_source(r, s, cp) for s in range(cp)) == list(range(cp))
+    for s in range(cp):  # at every step the sources form a permutation of the ranks
+        assert sorted(oracle.ring_source(r, s, cp) for r in range(cp)) == list(range(cp))
+        for r in range(cp):  # neighbour exchange: what r holds at s+1 is what r-1 held at s
+            assert oracle.ring_source(r, s + 1, cp) == oracle.ring_source((r - 1) % cp, s, cp)
+
+
+def test_bad_divisibility_rejected():
+    with pytest.raises(ValueError):
+        oracle.rank_positions(100, 3, 0, "zigzag")
+    with pytest.raises(ValueError):
+        oracle.rank_positions(10, 4, 0, "contiguous")
+
+
+# --------------------------------------------------------------------------
+# Merge and CP decomposition (exactness)
+# --------------------------------------------------------------------------
+
+def test_merge_neg_inf_rules():
+    o_a = _rand((3, 2, 4), 40)
+    o_b = _rand((3, 2, 4), 41)
+    lse_a = np.array([[-np.inf, 1.0, 0.5], [2.0, -np.inf, -np.inf]])
+    lse_b = np.array([[0.3, -np.inf, 0.5], [-np.inf, 1.5, -np.inf]])
+    o, lse = oracle.merge_partial(o_a, lse_a, o_b, lse_b)
+    assert lse[0, 0] == 0.3 and np.array_equal(o[0, 0], o_b[0, 0])   # empty acc takes the partial
+    assert lse[0, 1] == 1.0 and np.array_equal(o[1, 0], o_a[1, 0])   # empty partial changes nothing
+    assert abs(lse[0, 2] - (0.5 + math.log(2))) <= 1e-15                # equal weights
+    assert np.max(np.abs(o[2, 0] - 0.5 * (o_a[2, 0] + o_b[2, 0]))) <= 1e-15
+    assert lse[1, 2] == -np.inf
+
+
+def test_merge_of_key_split_equals_whole():
+    """Attention over a key set split in two, merged, equals attention over the union."""
+    sq, sk, heads, dim = 10, 17, 2, 5
+    q = _rand((sq, heads, dim), 42)
+    k, v = _rand((sk, heads, dim), 43), _rand((sk, heads, dim), 44)
+    perm = np.random.default_rng(45).permutation(sk)
+    a, b = perm[:7], perm[7:]
+    o, lse = oracle.attention(q, k, v, causal=False)
+    oa, la = oracle.attention(q, k[a], v[a], causal=False)
+    ob, lb = oracle.attention(q, k[b], v[b], causal=False)
+    om, lm = oracle.merge_partial(oa, la, ob, lb)
+    om2, lm2 = oracle.merge_partial(ob, lb, oa, la)
+    for x, y in ((om, o), (om2, o), (lm, lse), (lm2, lse)):
+        assert np.max(np.abs(x - y)) <= 1e-13
+
+
+CASES = [(256, 2, "zigzag", True), (96, 3, "zigzag", True), (64, 4, "contiguous", True),
+         (64, 4, "zigzag", False), (48, 1, "zigzag", True), (80, 5, "contiguous", False),
+         (128, 8, "zigzag", True)]
+
+
+@pytest.mark.parametrize("seq,cp,layout,causal", CASES)
+def test_cp_decomposition_equals_unsplit(seq, cp, layout, causal):
+    heads, dim = 2, 8
+    q, k, v = (_rand((seq, heads, dim), 50 + i) for i in range(3))
+    o, lse = oracle.attention(q, k, v, causal=causal)
+    o2, lse2 = oracle.full_forward(q, k, v, cp, layout=layout, causal=causal)
+    assert np.max(np.abs(o2 - o)) <= 1e-12
+    assert np.max(np.abs(lse2 - lse)) <= 1e-12
+
+
+def test_cp_decomposition_is_step_order_invariant():
+    seq, cp, heads, dim = 96, 4, 2, 8
+    q, k, v = (_rand((seq, heads, dim), 60 + i) for i in range(3))
+    rng = np.random.default_rng(63)
+    base, lb = oracle.full_forward(q, k, v, cp)
+    orders = [list(rng.permutation(cp)) for _ in range(cp)]
+    o2, l2 = oracle.full_forward(q, k, v, cp, step_orders=orders)
+    assert np.max(np.abs(o2 - base)) <= 1e-13
+    assert np.max(np.abs(l2 - lb)) <= 1e-13
+
+
+def test_tiny_workload_decomposition_against_torch_sdpa():
+    """The tiny fp32 workload: CP-decomposed oracle vs torch fp64 SDPA, every row."""
+    from ring_context_parallelism_amd.inputs import WORKLOADS, workload_qkv, to_numpy_f64
+    w = WORKLOADS["causal_s256_cp2_zigzag_h2_d64_fp32"]
+    q, k, v = (to_numpy_f64(t) for t in workload_qkv(w))
+    o, lse = oracle.full_forward(q, k, v, w.cp, layout=w.layout, causal=True)
+    tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2).contiguous() for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True).permute(1, 0, 2).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# Work counts and imbalance (closed forms)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cp,c", [(2, 4), (4, 3), (8, 2), (3, 5)])
+def test_zigzag_pairs_closed_form(cp, c):
+    seq = 2 * cp * c
+    for r in range(cp):
+        assert oracle.step_valid_pairs(seq, cp, "zigzag", True, r, 0) == 2 * c * c + c
+        for s in range(1, cp):
+            assert oracle.step_valid_pairs(seq, cp, "zigzag", True, r, s) == 2 * c * c
+
+
+@pytest.mark.parametrize("cp,l", [(4, 6), (3, 5), (1, 7)])
+def test_contiguous_pairs_closed_form(cp, l):
+    seq = cp * l
+    for r in range(cp):
+        for s in range(cp):
+            got = oracle.step_valid_pairs(seq, cp, "contiguous", True, r, s)
+            want = l * (l + 1) // 2 if s == 0 else (l * l if r >= s else 0)
+            assert got == want
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+def test_pairs_sum_to_causal_triangle(layout):
+    seq, cp = 96, 4
+    tot = sum(oracle.step_valid_pairs(seq, cp, layout, True, r, s) for r in range(cp) for s in range(cp))
+    assert tot == seq * (seq + 1) // 2
+    tot = sum(oracle.step_valid_pairs(seq, cp, layout, False, r, s) for r in range(cp) for s in range(cp))
+    assert tot == seq * seq
+
+
+def test_imbalance_contiguous_cp4_and_zigzag_at_16k_tile128():
+    seq, cp, t = 16384, 4, 128
+    wz = [[oracle.step_valid_tiles(seq, cp, "zigzag", True, r, s, t, t) for s in range(cp)] for r in range(cp)]
+    wc = [[oracle.step_valid_tiles(seq, cp, "contiguous", True, r, s, t, t) for s in range(cp)] for r in range(cp)]
+    n = seq // (2 * cp) // t
+    for r in range(cp):
+        assert wz[r] == [2 * n * n + n] + [2 * n * n] * (cp - 1)  # 528, 512, 512, 512
+    per, agg = oracle.imbalance(wz)
+    assert per == [1.0] * cp and agg == 1.0
+    per, agg = oracle.imbalance(wc)
+    assert np.allclose(per, [1.0, 4.0 / 3.0, 2.0, 4.0], rtol=0, atol=1e-12)
+    assert round(agg, 3) == 1.744
+    # Pairs are tile-independent: zigzag is exactly balanced at every step.
+    pz = [[oracle.step_valid_pairs(seq, cp, "zigzag", True, r, s) for s in range(cp)] for r in range(cp)]
+    assert oracle.imbalance(pz) == ([1.0] * cp, 1.0)
+
+
+def test_valid_flops_formula():
+    assert oracle.valid_flops(1, 1, 128) == 512
+    c = 2048  # rank 0 of the 32k, cp 8 share: 16 C^2 + C pairs per head
+    pairs = sum(oracle.step_valid_pairs(32768, 8, "zigzag", True, 0, s) for s in range(8))
+    assert pairs == 16 * c * c + c
+    assert oracle.valid_flops(pairs, 32, 128) == 4 * 128 * 32 * (16 * c * c + c)
+
+
+def test_golden_hashes_and_oracle_summary():
+    """Hashed equivalence fixtures: the input recipe and the oracle's tiny result."""
+    from ring_context_parallelism_amd.inputs import WORKLOADS, workload_qkv, sha256_of, to_numpy_f64
+    with open(os.path.join(GOLDEN, "inputs_sha256.json")) as f:
+        g = json.load(f)
+    name = "causal_s256_cp2_zigzag_h2_d64_fp32"
+    q, k, v = workload_qkv(WORKLOADS[name])
+    assert sha256_of(q, k, v) == g["inputs"][name]
+    o, lse = oracle.attention(*(to_numpy_f64(t) for t in (q, k, v)), causal=True)
+    ref = g["oracle"][name]
+    assert abs(o.sum() - ref["sum_O"]) <= 1e-9
+    assert abs(lse.sum() - ref["sum_LSE"]) <= 1e-9
+    assert np.allclose(o[255, 1, :4], ref["O_row255_h1_d0_3"], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Planted mistakes must be caught by the pins above
+# --------------------------------------------------------------------------
+
+def test_planted_mask_off_by_one_is_caught(monkeypatch):
+    """A mask that drops the diagonal breaks the zero-query closed form."""
+    def strict(q_pos, k_pos, causal):
+        q_pos = np.asarray(q_pos)
+        k_pos = np.asarray(k_pos)
+        return k_pos[None, :] < q_pos[:, None] if causal else np.ones((q_pos.size, k_pos.size), bool)
+    monkeypatch.setattr(oracle_attention_mod, "valid_mask", strict)
+    with pytest.raises(AssertionError):
+        test_o1_closed_form_zero_query_causal()
+
+
+def test_planted_position_seam_is_caught(monkeypatch):
+    """A rank whose late chunk is shifted by one position breaks exactness."""
+    real = cp_reference.rank_positions
+
+    def shifted(seq_len, cp, rank, layout):
+        pos = real(seq_len, cp, rank, layout).copy()
+        if layout == "zigzag" and rank == 0:
+            pos[pos.size // 2:] -= 1
+        return pos
+    monkeypatch.setattr(cp_reference, "rank_positions", shifted)
+    with pytest.raises(AssertionError):
+        test_cp_decomposition_equals_unsplit(256, 2, "zigzag", True)
+
+
+def test_planted_merge_sign_error_is_caught(monkeypatch):
+    real = cp_reference.merge_partial
+
+    def wrong(o_acc, lse_acc, o_s, lse_s):
+        o, lse = real(o_acc, lse_acc, o_s, lse_s)
+        return o, np.where(np.isfinite(lse), lse - 1e-6, lse)
+    monkeypatch.setattr(cp_reference, "merge_partial", wrong)
+    with pytest.raises(AssertionError):
+        test_cp_decomposition_equals_unsplit(96, 3, "zigzag", True)
+
+
+def test_planted_transposed_operand_is_caught(monkeypatch):
+    """Using K where V belongs fails the constant-V invariant."""
+    real = oracle_attention_mod.attention
+
+    def swapped(q, k, v, **kw):
+        return real(q, k, k, **kw)
+    monkeypatch.setattr(oracle, "attention", swapped)
+    with pytest.raises(AssertionError):
+        test_o1_constant_values_are_reproduced(True)
