@@ -1,0 +1,244 @@
+"""Benchmark: zigzag ring context-parallel attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One timed step = one call of the library's hot path over the workload's share:
+for the default workload, rank 0's share of a causal 32768-token sequence at
+cp 8 (zigzag chunks {0, 15}, 32 heads x 128, bf16): 8 ring steps, each with the
+next K/V received on a side stream, blockwise MFMA attention with the merge in
+the epilogue, and the final scatter of O/LSE to token positions.  Inputs are
+resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is effective TFLOP/s over mask-valid FLOPs
+(4 * head_dim per valid (query, key) pair per head).
+"""
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+DEFAULT_WORKLOAD = "causal_s32768_cp8_zigzag_h32_d128_bf16_rank0"
+METRIC = "effective causal attn TFLOP/s (valid FLOPs) + % bf16 MFMA peak; zigzag imbalance"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip imbalance / mode / parity side measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def share_pairs(plan, w):
+    ranks = range(w.cp) if w.rank is None else [w.rank]
+    return sum(plan.valid_work(r, s, 128, 64)[1] for r in ranks for s in range(w.cp))
+
+
+def run_call(plan, w, bufs, stream):
+    q, k, v, out, lse = bufs
+    if w.rank is None:
+        plan.full_forward(q, k, v, out, lse, stream=stream)
+    else:
+        plan.rank_forward(q, k, v, out, lse, w.rank, stream=stream)
+
+
+def time_calls(plan, w, bufs, stream, steps, warmup):
+    for _ in range(warmup):
+        run_call(plan, w, bufs, stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run_call(plan, w, bufs, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def step_kernel_times(plan, w, bufs, stream, reps):
+    """Per-(rank, step) attention-kernel ms from the library's own HIP events."""
+    plan.set_step_timing(True)
+    acc = None
+    for _ in range(reps):
+        run_call(plan, w, bufs, stream)
+        t = np.array(plan.last_step_times())
+        acc = t if acc is None else acc + t
+    plan.set_step_timing(False)
+    return acc / reps
+
+
+def cpu_baseline(w, q, k, v, target_s):
+    """The fp64 oracle on a bounded sample of the same share, timed on the host."""
+    import oracle
+    from ring_context_parallelism_amd.inputs import to_numpy_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    ranks = range(w.cp) if w.rank is None else [w.rank]
+    rows = np.concatenate([oracle.rank_positions(w.seq_len, w.cp, r, w.layout) for r in ranks])
+    rows = rows[:: max(1, rows.size // 1024)][:1024]
+    kpos = np.arange(w.seq_len)
+    flops = 0
+    heads_done = 0
+    t0 = time.perf_counter()
+    for h in range(w.heads):
+        qh = to_numpy_f64(q[torch.from_numpy(rows), h:h + 1])
+        kh = to_numpy_f64(k[:, h:h + 1])
+        vh = to_numpy_f64(v[:, h:h + 1])
+        oracle.attention(qh, kh, vh, causal=w.causal, q_pos=rows, k_pos=kpos)
+        pairs = int((rows + 1).sum()) if w.causal else rows.size * w.seq_len
+        flops += oracle.valid_flops(pairs, 1, w.head_dim)
+        heads_done += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows.size} of the share's rows (evenly spaced) x {heads_done} head(s), every valid key, "
+                      f"fp64 numpy; {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
+
+
+def imbalance_section(stream):
+    """Zigzag vs contiguous at 16384 tokens, cp 4: plan tiles and measured step times."""
+    import ring_context_parallelism_amd as R
+    from ring_context_parallelism_amd.inputs import WORKLOADS, workload_qkv
+    res = {}
+    for layout in ("zigzag", "contiguous"):
+        w = WORKLOADS[f"causal_s16384_cp4_{layout}_h16_d128_bf16"]
+        p = R.Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout)
+        tiles = [[p.valid_work(r, s, 128, 64)[0] for s in range(w.cp)] for r in range(w.cp)]
+        q, k, v = (t.cuda() for t in workload_qkv(w))
+        out = torch.empty_like(q)
+        lse = torch.empty(w.heads, w.seq_len, device="cuda")
+        bufs = (q, k, v, out, lse)
+        run_call(p, w, bufs, stream)
+        times = step_kernel_times(p, w, bufs, stream, 3)
+        ms = time_calls(p, w, bufs, stream, 5, 1)
+        def imb(tab):
+            t = np.asarray(tab, dtype=np.float64)
+            mx, mean = t.max(axis=0), t.mean(axis=0)
+            return [round(float(a / b), 4) if b > 0 else 1.0 for a, b in zip(mx, mean)], round(
+                float(mx.sum() / mean.sum()), 4)
+        per_t, agg_t = imb(tiles)
+        per_m, agg_m = imb(times)
+        res[layout] = {"tiles_128x64": tiles, "tile_imbalance_per_step": per_t, "tile_imbalance": agg_t,
+                       "step_ms": [[round(float(x), 4) for x in row] for row in times],
+                       "time_imbalance_per_step": per_m, "time_imbalance": agg_m,
+                       "full_forward_ms": round(ms, 4)}
+        p.close()
+        del q, k, v, out, lse, bufs
+        torch.cuda.empty_cache()
+    return res
+
+
+def sampled_parity(w, q, k, v, out, lse):
+    import oracle
+    from ring_context_parallelism_amd.inputs import to_numpy_f64
+    ranks = range(w.cp) if w.rank is None else [w.rank]
+    rng = np.random.default_rng(w.seed)
+    rows = np.concatenate([oracle.rank_positions(w.seq_len, w.cp, r, w.layout) for r in ranks])
+    rows = np.unique(np.concatenate([rows[:2], rows[-2:], rng.choice(rows, 24, replace=False)]))
+    oc, lc = out.cpu(), lse.cpu()
+    d_o = d_l = 0.0
+    for h in sorted({0, w.heads - 1}):
+        o_ref, l_ref = oracle.attention(to_numpy_f64(q[torch.from_numpy(rows), h:h + 1]),
+                                        to_numpy_f64(k[:, h:h + 1]), to_numpy_f64(v[:, h:h + 1]),
+                                        causal=w.causal, q_pos=rows)
+        d_o = max(d_o, float(np.abs(oc[rows, h:h + 1].double().numpy() - o_ref).max()))
+        d_l = max(d_l, float(np.abs(lc[h, rows].double().numpy() - l_ref[0]).max()))
+    return {"rows": int(rows.size), "heads": 2, "max_abs_dO": d_o, "max_abs_dLSE": d_l}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the one-GPU ring schedule has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import ring_context_parallelism_amd as R
+    from ring_context_parallelism_amd.inputs import WORKLOADS, workload_qkv
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    q_cpu, k_cpu, v_cpu = workload_qkv(w)
+    q, k, v = (t.cuda() for t in (q_cpu, k_cpu, v_cpu))
+    out = torch.empty_like(q)
+    lse = torch.empty(w.heads, w.seq_len, device="cuda", dtype=torch.float32)
+    bufs = (q, k, v, out, lse)
+    plan = R.Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout, dtype=w.torch_dtype)
+
+    pairs = share_pairs(plan, w)
+    flops = 4 * w.head_dim * w.heads * pairs
+    ms = time_calls(plan, w, bufs, stream, args.steps, args.warmup)
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] {w.name}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    # dominant kernel: the attention step kernel, timed with HIP events on its own stream
+    times = step_kernel_times(plan, w, bufs, stream, min(args.steps, 10))
+    ranks = range(w.cp) if w.rank is None else [w.rank]
+    launches = [times[r][s] for r in ranks for s in range(w.cp) if times[r][s] > 0]
+    avg_ms = float(np.mean(launches))
+    flops_per_launch = flops / len(launches)
+    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    roofline = {"kernel": "attn_step_bf16" if w.dtype == "bf16" else "attn_step_f32", "bound": "mfma",
+                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(avg_ms, 5), "launches_per_step": len(launches),
+                "valid_flops_per_launch": flops_per_launch}
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic: i.i.d. N(0,1) Q/K/V, seeded, CPU-drawn",
+        "config": {"workload": w.name, "seq_len": w.seq_len, "cp_size": w.cp, "layout": w.layout,
+                   "causal": w.causal, "rank": w.rank, "heads": w.heads, "head_dim": w.head_dim,
+                   "ring_steps": w.cp, "valid_flops": flops},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+    }
+
+    if not args.no_extras:
+        # same share, other schedule modes (exposed copy / merge cost)
+        plan.set_serialize(True)
+        ms_serial = time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1)
+        plan.set_serialize(False)
+        plan.set_merge(True)
+        ms_sep = time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1)
+        plan.set_merge(False)
+        result["modes_ms"] = {"overlapped_fused_merge": round(ms, 5), "serialized_fused_merge": round(ms_serial, 5),
+                              "overlapped_separate_merge": round(ms_sep, 5),
+                              "exposed_copy_ms": round(ms_serial - ms, 5)}
+        run_call(plan, w, bufs, stream)
+        torch.cuda.synchronize()
+        result["parity_sampled"] = sampled_parity(w, q_cpu, k_cpu, v_cpu, out, lse)
+        result["imbalance"] = imbalance_section(stream)
+        result["imbalance"]["zigzag_step_time_imbalance"] = result["imbalance"]["zigzag"]["time_imbalance"]
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, args.cpu_seconds)
+
+    props = torch.cuda.get_device_properties(0)
+    result["env"] = {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
+                     "torch": torch.__version__, "hip": torch.version.hip, "host": platform.node(),
+                     "host_cpus": os.cpu_count()}
+    plan.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * cp_attn.h -- C ABI of the MI355X (gfx950) zigzag ring context-parallel
+ * attention library, libcpattn.so.
+ *
+ * What the library computes.  One context-parallel (CP) rank's exact softmax
+ * attention over its share of a long sequence, the core of context parallelism
+ * as described in "Sequence Parallelism IV: Megatron Context Parallel and
+ * Load-Balanced Rings" (duoan.github.io):
+ *   - the sequence of S tokens is cut into 2*cp chunks and rank r owns chunks
+ *     r and 2*cp-1-r (zigzag placement, section 3 "Naive Ring Attention Is
+ *     Imbalanced Under Causal Masks"), or the contiguous slice
+ *     [r*S/cp, (r+1)*S/cp) (naive placement, same section);
+ *   - the rank's queries stay resident while the K/V chunks of every rank pass
+ *     by, one source rank per ring step (section 4 "What Actually Moves");
+ *   - each step's partial result is folded into a running (O, LSE) state by
+ *     log-sum-exp correction, which keeps the result exact (section 4);
+ *   - sub-blocks that the causal mask puts entirely in the future are skipped
+ *     (section 4);
+ *   - the next step's K/V is received while the current step computes
+ *     (section 5 "Overlap: More Than One Stream").
+ * On one GPU the ring is a step schedule: the K/V of ring source
+ * src(r, s) = (r - s) mod cp is copied device-to-device into one of two
+ * receive slots on a side HIP stream while step s-1 computes.
+ *
+ * Attention semantics (the plain definition the result must equal):
+ *   causal: key j is valid for query i iff pos(j) <= pos(i) (global token
+ *   positions; the diagonal is valid); bidirectional: every key is valid.
+ *   s_ij = <q_i, k_j> / sqrt(head_dim);  O_i = sum_j softmax_j(s_ij) v_j;
+ *   LSE_i = ln sum_j exp(s_ij)  (natural log, fp32).
+ *
+ * Tensor layouts (all device memory, row-major, contiguous):
+ *   q, k, v, out : [S][heads][head_dim] in natural token order, element type
+ *                  set by cp_attn_set_dtype (bf16 by default);
+ *   lse          : [heads][S] fp32.
+ * Pointers are device pointers and must be 16-byte aligned.  Streams are HIP
+ * streams (hipStream_t) passed as void*; NULL means the null stream.
+ *
+ * Errors: every call returns a status code (CP_ATTN_OK = 0 or a negative
+ * error); nothing is enqueued when argument validation fails; no exception or
+ * abort crosses the ABI.  cp_attn_last_error() gives a text for the calling
+ * thread's last failure.  A plan is not reentrant: keep at most one forward
+ * call per plan in flight, and do not destroy a plan while its work is queued.
+ */
+#ifndef CP_ATTN_H
+#define CP_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct cp_attn_plan_s* cp_attn_plan_t;
+
+/* Status codes. */
+#define CP_ATTN_OK 0
+#define CP_ATTN_EINVAL (-1)       /* bad argument: sizes, divisibility, rank, null or misaligned pointer */
+#define CP_ATTN_EUNSUPPORTED (-2) /* valid request this build does not implement (head_dim, cp_size) */
+#define CP_ATTN_ENOWORKSPACE (-3) /* caller workspace missing or too small, or allocation failed */
+#define CP_ATTN_EHIP (-4)         /* a HIP runtime call or kernel launch failed */
+
+/* Chunk placement. */
+#define CP_ATTN_CONTIGUOUS 0 /* rank r owns tokens [r*S/cp, (r+1)*S/cp) */
+#define CP_ATTN_ZIGZAG 1     /* rank r owns chunks r and 2*cp-1-r of S/(2*cp) tokens, early chunk first */
+
+/* Element types of q, k, v and out (lse is always fp32). */
+#define CP_ATTN_BF16 0
+#define CP_ATTN_FP32 1
+
+/* Options for cp_attn_set_option. */
+#define CP_ATTN_OPT_MERGE 1       /* 0: merge fused into the attention epilogue (default);
+                                     1: separate LSE-merge kernel on the merge stream + finalize kernel */
+#define CP_ATTN_OPT_SERIALIZE 2   /* 0: copy/merge on side streams (default); 1: everything on the caller's stream */
+#define CP_ATTN_OPT_RECV 3        /* 0: ring receive by the layout gather kernel (default); 1: hipMemcpyAsync */
+#define CP_ATTN_OPT_POISON 4      /* 1: fill each receive slot / partial buffer with NaN once consumed */
+#define CP_ATTN_OPT_STEP_TIMING 5 /* 1: time every ring step's attention kernel with HIP events */
+
+/*
+ * Create a plan (host only: no device memory, no HIP call).
+ *   seq_len  S > 0, tokens of the whole sequence (batch 1);
+ *   cp_size  number of CP ranks, 1..256;
+ *   heads    > 0 (K/V heads equal query heads);
+ *   head_dim 64 or 128;
+ *   causal   1 causal, 0 bidirectional;
+ *   layout   CP_ATTN_ZIGZAG (S % (2*cp_size) == 0) or CP_ATTN_CONTIGUOUS (S % cp_size == 0).
+ * Per-rank length is S / cp_size ("Context Parallelism in MegaDLMs", section
+ * "Sequence Partitioning Across GPUs").  Degrees that do not divide the
+ * sequence are rejected ("Context Parallelism for Long-Context Training",
+ * section "Sweep the smallest useful degree").
+ * Returns EINVAL for non-positive sizes, a bad flag or layout, or a
+ * non-dividing length; EUNSUPPORTED for another head_dim or cp_size > 256.
+ * On success *out owns the plan; free it with cp_attn_plan_destroy.
+ */
+int cp_attn_plan(int64_t seq_len, int cp_size, int heads, int head_dim, int causal, int layout,
+                 cp_attn_plan_t* out);
+
+/* Free the plan, its library-owned streams, events and workspace.  Waits for
+ * the plan's queued work first.  NULL is accepted. */
+int cp_attn_plan_destroy(cp_attn_plan_t plan);
+
+/* Element type of q, k, v, out: CP_ATTN_BF16 (default) or CP_ATTN_FP32. */
+int cp_attn_set_dtype(cp_attn_plan_t plan, int dtype);
+
+/* Set one of the CP_ATTN_OPT_* options (values as documented above). */
+int cp_attn_set_option(cp_attn_plan_t plan, int option, int value);
+
+/* Bytes of device workspace a forward call needs: two K/V receive slots, the
+ * fp32 running state (O, LSE) and two fp32 partial buffers for the separate
+ * merge mode, each rounded up to 256 bytes. */
+int cp_attn_workspace_bytes(cp_attn_plan_t plan, int64_t* bytes);
+
+/* Hand the plan caller-owned device memory of at least cp_attn_workspace_bytes
+ * bytes (256-byte aligned); the caller keeps ownership and must keep it alive
+ * while the plan uses it.  NULL/0 returns to library-allocated workspace
+ * (hipMalloc'd on the first forward call, freed by cp_attn_plan_destroy).
+ * ENOWORKSPACE if bytes is too small, EINVAL if misaligned. */
+int cp_attn_set_workspace(cp_attn_plan_t plan, void* device_ptr, int64_t bytes);
+
+/* Side streams for the ring receive copies and the separate merge (hipStream_t
+ * as void*).  NULL lets the library create and own non-blocking streams of
+ * default priority on first use. */
+int cp_attn_set_streams(cp_attn_plan_t plan, void* copy_stream, void* merge_stream);
+
+/*
+ * One rank's share, asynchronous on `stream`: for s = 0..cp_size-1 the rank's
+ * queries attend to the K/V chunks of src(rank, s) = (rank - s) mod cp_size,
+ * the next source is received into the other slot while step s computes, and
+ * partials are merged exactly.  Writes only the rank's rows of out (token
+ * positions owned by `rank`) and the matching columns of lse; inputs are read
+ * only.  q, k, v, out: [S][heads][head_dim] plan dtype; lse: [heads][S] fp32.
+ * EINVAL for rank outside [0, cp_size) or a null/misaligned pointer;
+ * ENOWORKSPACE if workspace allocation fails; EHIP if a launch fails.
+ */
+int cp_attn_rank_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
+                         float* lse, int rank, void* stream);
+
+/* Every rank's share back to back on `stream` (ranks 0..cp_size-1); fills all
+ * rows of out and lse.  Same arguments and errors as cp_attn_rank_forward. */
+int cp_attn_full_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
+                         float* lse, void* stream);
+
+/* ---- host-only introspection (no HIP calls; CPU-testable) ---- */
+
+/* Rows (tokens) each rank owns: 2*S/(2*cp) zigzag, S/cp contiguous. */
+int cp_attn_local_rows(cp_attn_plan_t plan, int64_t* rows);
+
+/* Chunk indices owned by `rank`, local order; *count = 2 (zigzag) or 1
+ * (contiguous, where the chunk index equals the rank). */
+int cp_attn_rank_chunks(cp_attn_plan_t plan, int rank, int32_t chunks[2], int32_t* count);
+
+/* Ring source of (rank, step): (rank - step) mod cp_size. */
+int cp_attn_step_source(cp_attn_plan_t plan, int rank, int step, int32_t* source);
+
+/*
+ * Step descriptor of (rank, step): up to two query-row segments of the rank's
+ * local buffer, each row of which attends to a prefix of the source's local
+ * K/V buffer.  out[i*7 + 0..6] for segment i = {q_start, q_len, kv_full, diag,
+ * first, last, q_global}: local rows [q_start, q_start + q_len), whose local
+ * row q_start + t (global token q_global + t) sees local keys
+ * [0, kv_full + (diag ? t + 1 : 0)); first/last = 1 when this step is the
+ * segment's first/last active step.  Rows in no segment have no valid key in
+ * this step (their sub-blocks are skipped).  *count in {0, 1, 2}.
+ */
+int cp_attn_step_segments(cp_attn_plan_t plan, int rank, int step, int64_t out[14], int32_t* count);
+
+/* Valid (query, key) pairs of one head in (rank, step), and tiles of
+ * bm local rows x bn local keys holding at least one valid pair (tiles laid
+ * from local index 0, last tile of each axis clipped). */
+int cp_attn_valid_work(cp_attn_plan_t plan, int rank, int step, int bm, int bn, int64_t* tiles,
+                       int64_t* pairs);
+
+/* ---- layout kernels (zigzag / contiguous reordering) ---- */
+
+/* src: [S][heads][head_dim] natural order -> dst: [cp][local_rows][heads][head_dim],
+ * each rank's rows in its local order.  Plan dtype, bit-exact copy. */
+int cp_attn_layout_gather(cp_attn_plan_t plan, const void* src, void* dst, void* stream);
+
+/* Inverse of cp_attn_layout_gather. */
+int cp_attn_layout_scatter(cp_attn_plan_t plan, const void* src, void* dst, void* stream);
+
+/*
+ * Exact LSE merge of a partial into a running state, fp32, on `stream`:
+ * o_acc, o_s: [rows][heads][head_dim]; lse_acc, lse_s: [heads][rows].
+ * Per (row, head): lse_s = -inf leaves the state; lse_acc = -inf takes the
+ * partial; otherwise lse' = max + log1p(exp(-|lse_acc - lse_s|)) and
+ * O' = exp(lse_acc - lse') O_acc + exp(lse_s - lse') O_s.  Section 4 of the
+ * same page: the online softmax state keeps the result exact.
+ * head_dim must be a multiple of 4; pointers 16-byte aligned.
+ */
+int cp_attn_lse_merge(float* o_acc, float* lse_acc, const float* o_s, const float* lse_s, int64_t rows,
+                      int heads, int head_dim, void* stream);
+
+/* Per (rank, step) attention-kernel milliseconds of the last forward call
+ * made with CP_ATTN_OPT_STEP_TIMING = 1, row-major [cp][cp]; entries of ranks
+ * the call did not run are -1.  Blocks until those events complete.
+ * n must be >= cp_size * cp_size. */
+int cp_attn_last_step_times(cp_attn_plan_t plan, float* ms, int n);
+
+/* Static text for a status code. */
+const char* cp_attn_status_string(int status);
+
+/* Text describing the calling thread's last failed call (empty if none). */
+const char* cp_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_ATTN_H */

@@ -1,0 +1,185 @@
+"""Python binding of libcpattn.so with the C ABI's names.
+
+Only argument marshalling happens here: torch tensors are checked for shape,
+dtype, device and contiguity and passed as raw pointers with torch's current
+HIP stream; every step of the computation runs in the library's kernels.
+"""
+
+import ctypes
+
+import torch
+
+from . import _native as N
+
+_DTYPES = {torch.bfloat16: N.BF16, torch.float32: N.FP32}
+_LAYOUTS = {"zigzag": N.ZIGZAG, "contiguous": N.CONTIGUOUS}
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Plan:
+    """``cp_attn_plan(seq_len, cp_size, heads, head_dim, causal, layout)`` and its calls."""
+
+    def __init__(self, seq_len, cp_size, heads, head_dim, causal=True, layout="zigzag", dtype=torch.bfloat16):
+        self._h = ctypes.c_void_p()
+        self.lib = N.lib()
+        N.check(self.lib.cp_attn_plan(int(seq_len), int(cp_size), int(heads), int(head_dim), int(bool(causal)),
+                                      _LAYOUTS[layout], ctypes.byref(self._h)), "cp_attn_plan")
+        self.seq_len, self.cp_size, self.heads, self.head_dim = int(seq_len), int(cp_size), int(heads), int(head_dim)
+        self.causal, self.layout = bool(causal), layout
+        self.dtype = dtype
+        self._workspace = None
+        N.check(self.lib.cp_attn_set_dtype(self._h, _DTYPES[dtype]), "cp_attn_set_dtype")
+
+    # -- lifetime -------------------------------------------------------
+    def close(self):
+        if self._h is not None and self._h.value:
+            N.check(self.lib.cp_attn_plan_destroy(self._h), "cp_attn_plan_destroy")
+        self._h = None
+        self._workspace = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # -- options --------------------------------------------------------
+    def set_option(self, option, value):
+        N.check(self.lib.cp_attn_set_option(self._h, int(option), int(value)), "cp_attn_set_option")
+
+    def set_merge(self, separate):
+        self.set_option(N.OPT_MERGE, 1 if separate else 0)
+
+    def set_serialize(self, on):
+        self.set_option(N.OPT_SERIALIZE, int(bool(on)))
+
+    def set_recv(self, mode):
+        self.set_option(N.OPT_RECV, {"kernel": 0, "memcpy": 1}[mode])
+
+    def set_poison(self, on):
+        self.set_option(N.OPT_POISON, int(bool(on)))
+
+    def set_step_timing(self, on):
+        self.set_option(N.OPT_STEP_TIMING, int(bool(on)))
+
+    def workspace_bytes(self):
+        n = ctypes.c_int64()
+        N.check(self.lib.cp_attn_workspace_bytes(self._h, ctypes.byref(n)), "cp_attn_workspace_bytes")
+        return n.value
+
+    def set_workspace(self, tensor):
+        """Caller-owned workspace (a uint8 CUDA tensor of >= workspace_bytes()); None to release."""
+        if tensor is None:
+            N.check(self.lib.cp_attn_set_workspace(self._h, None, 0), "cp_attn_set_workspace")
+        else:
+            N.check(self.lib.cp_attn_set_workspace(self._h, _ptr(tensor), tensor.numel() * tensor.element_size()),
+                    "cp_attn_set_workspace")
+        self._workspace = tensor
+
+    def set_streams(self, copy_stream, merge_stream):
+        c = ctypes.c_void_p(copy_stream.cuda_stream) if copy_stream is not None else None
+        m = ctypes.c_void_p(merge_stream.cuda_stream) if merge_stream is not None else None
+        N.check(self.lib.cp_attn_set_streams(self._h, c, m), "cp_attn_set_streams")
+        self._streams = (copy_stream, merge_stream)
+
+    # -- forward --------------------------------------------------------
+    def _check_io(self, q, k, v, out, lse):
+        shape = (self.seq_len, self.heads, self.head_dim)
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+            if tuple(t.shape) != shape or t.dtype != self.dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {self.dtype} CUDA tensor of shape {shape}")
+        if tuple(lse.shape) != (self.heads, self.seq_len) or lse.dtype != torch.float32 or not lse.is_cuda \
+                or not lse.is_contiguous():
+            raise ValueError(f"lse must be a contiguous float32 CUDA tensor of shape {(self.heads, self.seq_len)}")
+
+    def rank_forward(self, q, k, v, out, lse, rank, stream=None):
+        self._check_io(q, k, v, out, lse)
+        N.check(self.lib.cp_attn_rank_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(rank),
+                                              _stream_ptr(stream)), "cp_attn_rank_forward")
+
+    def full_forward(self, q, k, v, out, lse, stream=None):
+        self._check_io(q, k, v, out, lse)
+        N.check(self.lib.cp_attn_full_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                              _stream_ptr(stream)), "cp_attn_full_forward")
+
+    # -- host-only introspection -----------------------------------------
+    def local_rows(self):
+        n = ctypes.c_int64()
+        N.check(self.lib.cp_attn_local_rows(self._h, ctypes.byref(n)), "cp_attn_local_rows")
+        return n.value
+
+    def rank_chunks(self, rank):
+        ch = (ctypes.c_int32 * 2)()
+        cnt = ctypes.c_int32()
+        N.check(self.lib.cp_attn_rank_chunks(self._h, int(rank), ch, ctypes.byref(cnt)), "cp_attn_rank_chunks")
+        return tuple(ch[i] for i in range(cnt.value))
+
+    def step_source(self, rank, step):
+        j = ctypes.c_int32()
+        N.check(self.lib.cp_attn_step_source(self._h, int(rank), int(step), ctypes.byref(j)), "cp_attn_step_source")
+        return j.value
+
+    def step_segments(self, rank, step):
+        buf = (ctypes.c_int64 * 14)()
+        cnt = ctypes.c_int32()
+        N.check(self.lib.cp_attn_step_segments(self._h, int(rank), int(step), buf, ctypes.byref(cnt)),
+                "cp_attn_step_segments")
+        keys = ("q_start", "q_len", "kv_full", "diag", "first", "last", "q_global")
+        return [dict(zip(keys, (buf[7 * i + j] for j in range(7)))) for i in range(cnt.value)]
+
+    def valid_work(self, rank, step, bm, bn):
+        t = ctypes.c_int64()
+        p = ctypes.c_int64()
+        N.check(self.lib.cp_attn_valid_work(self._h, int(rank), int(step), int(bm), int(bn), ctypes.byref(t),
+                                            ctypes.byref(p)), "cp_attn_valid_work")
+        return t.value, p.value
+
+    # -- layout -----------------------------------------------------------
+    def layout_gather(self, src, dst, stream=None):
+        self._check_layout(src, dst)
+        N.check(self.lib.cp_attn_layout_gather(self._h, _ptr(src), _ptr(dst), _stream_ptr(stream)),
+                "cp_attn_layout_gather")
+
+    def layout_scatter(self, src, dst, stream=None):
+        self._check_layout(src, dst)
+        N.check(self.lib.cp_attn_layout_scatter(self._h, _ptr(src), _ptr(dst), _stream_ptr(stream)),
+                "cp_attn_layout_scatter")
+
+    def _check_layout(self, src, dst):
+        n = self.seq_len * self.heads * self.head_dim
+        for name, t in (("src", src), ("dst", dst)):
+            if t.numel() != n or t.dtype != self.dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {self.dtype} CUDA tensor with {n} elements")
+
+    def last_step_times(self):
+        n = self.cp_size * self.cp_size
+        buf = (ctypes.c_float * n)()
+        N.check(self.lib.cp_attn_last_step_times(self._h, buf, n), "cp_attn_last_step_times")
+        return [[buf[r * self.cp_size + s] for s in range(self.cp_size)] for r in range(self.cp_size)]
+
+
+def lse_merge(o_acc, lse_acc, o_s, lse_s, stream=None):
+    """In-place exact LSE merge: o_* ``[rows, H, D]`` fp32, lse_* ``[H, rows]`` fp32."""
+    rows, heads, dim = o_acc.shape
+    for name, t, shp in (("o_acc", o_acc, (rows, heads, dim)), ("o_s", o_s, (rows, heads, dim)),
+                         ("lse_acc", lse_acc, (heads, rows)), ("lse_s", lse_s, (heads, rows))):
+        if tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape {shp}")
+    lib = N.lib()
+    N.check(lib.cp_attn_lse_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_s), _ptr(lse_s), int(rows), int(heads),
+                                  int(dim), _stream_ptr(stream)), "cp_attn_lse_merge")

@@ -1,0 +1,684 @@
+// C ABI of libcpattn.so and the one-GPU ring step scheduler.
+//
+// The ring ("Sequence Parallelism IV: Megatron Context Parallel and
+// Load-Balanced Rings", section 4 "What Actually Moves" and section 5
+// "Overlap: More Than One Stream"): the rank's queries stay put while the K/V
+// of source (r - s) mod cp arrives at step s.  On one GPU the arrival is a
+// device-to-device copy into one of two receive slots, issued on a side
+// stream one step ahead so it runs under the current step's attention; the
+// softmax-state correction either runs in the attention kernel's epilogue
+// (default) or as a separate LSE-merge kernel on its own stream, so it does
+// not serialize the ring steps.  HIP events carry the cross-stream edges:
+//   copy(s+1 -> slot (s+1)&1) waits attn_done[(s+1)&1]   (step s-1 released it)
+//   attn(s, slot s&1)          waits recv_done[s&1]
+//   attn(s) -> part[s&1]       waits merge_done[s&1]      (separate merge only)
+//   merge(s)                   waits attn_done[s&1]
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "cp_attn.h"
+#include "kernels.h"
+#include "plan.h"
+
+struct cp_attn_plan_s {
+  cpattn::Plan* p;
+};
+
+namespace cpattn {
+
+struct DeviceState {
+  int device = -1;
+  hipStream_t copy = nullptr;
+  hipStream_t merge = nullptr;
+  bool own_copy = false, own_merge = false;
+  bool events_ready = false;
+  hipEvent_t start = nullptr, merge_join = nullptr;
+  hipEvent_t recv_done[2] = {nullptr, nullptr};
+  hipEvent_t attn_done[2] = {nullptr, nullptr};
+  hipEvent_t merge_done[2] = {nullptr, nullptr};
+  void* ws = nullptr;
+  int64_t ws_bytes = 0;
+  bool own_ws = false;
+  std::vector<hipEvent_t> t0, t1;  // per (rank, step) timing events
+  std::vector<int> timed;          // 1 if (rank, step) was timed by the last call
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define CPA_HIP(call)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess) return fail(CP_ATTN_EHIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+struct WsLayout {
+  int64_t slot_k[2], slot_v[2], acc_o, acc_lse, part_o[2], part_lse[2], total;
+  int64_t kv_bytes, o_bytes, lse_bytes;
+};
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+WsLayout ws_layout(const Plan& p) {
+  WsLayout w{};
+  w.kv_bytes = p.n_loc * p.heads * p.head_dim * p.elem_bytes();
+  w.o_bytes = p.n_loc * p.heads * p.head_dim * 4;
+  w.lse_bytes = int64_t(p.heads) * p.n_loc * 4;
+  int64_t off = 0;
+  auto take = [&](int64_t n) {
+    const int64_t at = off;
+    off += align256(n);
+    return at;
+  };
+  for (int b = 0; b < 2; ++b) {
+    w.slot_k[b] = take(w.kv_bytes);
+    w.slot_v[b] = take(w.kv_bytes);
+  }
+  w.acc_o = take(w.o_bytes);
+  w.acc_lse = take(w.lse_bytes);
+  for (int b = 0; b < 2; ++b) {
+    w.part_o[b] = take(w.o_bytes);
+    w.part_lse[b] = take(w.lse_bytes);
+  }
+  w.total = off;
+  return w;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ensure_device(Plan& p) {
+  DeviceState& d = *p.dev;
+  int dev = 0;
+  CPA_HIP(hipGetDevice(&dev));
+  if (d.device >= 0 && d.device != dev)
+    return fail(CP_ATTN_EINVAL, "plan was first used on another device");
+  d.device = dev;
+  if (!d.events_ready) {
+    CPA_HIP(hipEventCreateWithFlags(&d.start, hipEventDisableTiming));
+    CPA_HIP(hipEventCreateWithFlags(&d.merge_join, hipEventDisableTiming));
+    for (int b = 0; b < 2; ++b) {
+      CPA_HIP(hipEventCreateWithFlags(&d.recv_done[b], hipEventDisableTiming));
+      CPA_HIP(hipEventCreateWithFlags(&d.attn_done[b], hipEventDisableTiming));
+      CPA_HIP(hipEventCreateWithFlags(&d.merge_done[b], hipEventDisableTiming));
+    }
+    d.events_ready = true;
+  }
+  if (!d.copy) {
+    CPA_HIP(hipStreamCreateWithFlags(&d.copy, hipStreamNonBlocking));
+    d.own_copy = true;
+  }
+  if (!d.merge) {
+    CPA_HIP(hipStreamCreateWithFlags(&d.merge, hipStreamNonBlocking));
+    d.own_merge = true;
+  }
+  const WsLayout w = ws_layout(p);
+  if (d.ws && d.ws_bytes < w.total) {
+    if (!d.own_ws) return fail(CP_ATTN_ENOWORKSPACE, "caller workspace smaller than cp_attn_workspace_bytes");
+    CPA_HIP(hipFree(d.ws));
+    d.ws = nullptr;
+    d.ws_bytes = 0;
+  }
+  if (!d.ws) {
+    if (hipMalloc(&d.ws, size_t(w.total)) != hipSuccess) {
+      d.ws = nullptr;
+      return fail(CP_ATTN_ENOWORKSPACE, "hipMalloc of the workspace failed");
+    }
+    d.ws_bytes = w.total;
+    d.own_ws = true;
+  }
+  if (p.opt_step_timing && d.t0.empty()) {
+    const size_t n = size_t(p.cp) * p.cp;
+    d.t0.assign(n, nullptr);
+    d.t1.assign(n, nullptr);
+    for (size_t i = 0; i < n; ++i) {
+      CPA_HIP(hipEventCreate(&d.t0[i]));
+      CPA_HIP(hipEventCreate(&d.t1[i]));
+    }
+  }
+  return CP_ATTN_OK;
+}
+
+// Copy the K and V rows of ring source `src` (its local order) into slot b.
+int recv_kv(Plan& p, const void* k, const void* v, int src, int b, hipStream_t s) {
+  DeviceState& d = *p.dev;
+  const WsLayout w = ws_layout(p);
+  char* ws = static_cast<char*>(d.ws);
+  void* dk = ws + w.slot_k[b];
+  void* dv = ws + w.slot_v[b];
+  const int64_t row_bytes = int64_t(p.heads) * p.head_dim * p.elem_bytes();
+  if (p.opt_recv == 1) {
+    const int nch = p.layout == 1 ? 2 : 1;
+    const int64_t ch_bytes = p.chunk * row_bytes;
+    for (int c = 0; c < nch; ++c) {
+      const int64_t g = p.chunk_of(src, c) * ch_bytes;
+      CPA_HIP(hipMemcpyAsync(static_cast<char*>(dk) + c * ch_bytes, static_cast<const char*>(k) + g, size_t(ch_bytes),
+                             hipMemcpyDeviceToDevice, s));
+      CPA_HIP(hipMemcpyAsync(static_cast<char*>(dv) + c * ch_bytes, static_cast<const char*>(v) + g, size_t(ch_bytes),
+                             hipMemcpyDeviceToDevice, s));
+    }
+    return CP_ATTN_OK;
+  }
+  LayoutArgs la{};
+  la.src[0] = k;
+  la.src[1] = v;
+  la.dst[0] = dk;
+  la.dst[1] = dv;
+  la.ntensors = 2;
+  la.rank_begin = src;
+  la.rank_count = 1;
+  la.cp = p.cp;
+  la.zigzag = p.layout == 1;
+  la.to_local = 1;
+  la.chunk = p.chunk;
+  la.n_loc = p.n_loc;
+  la.row_vec = row_bytes / 16;
+  la.dst_rank0 = src;
+  CPA_HIP(launch_layout(la, s));
+  return CP_ATTN_OK;
+}
+
+int launch_step(Plan& p, const void* q, void* out, float* lse, int r, int s, int b, hipStream_t st) {
+  DeviceState& d = *p.dev;
+  const WsLayout w = ws_layout(p);
+  char* ws = static_cast<char*>(d.ws);
+  const StepDesc& sd = p.step(r, s);
+  if (sd.nseg == 0) return CP_ATTN_OK;
+  const bool bf16 = p.dtype == CP_ATTN_BF16;
+  const int bm = bf16 ? attn_bf16_block_m() : attn_f32_block_m();
+  StepArgs a{};
+  a.q = q;
+  a.k = ws + w.slot_k[b];
+  a.v = ws + w.slot_v[b];
+  a.acc_o = reinterpret_cast<float*>(ws + w.acc_o);
+  a.acc_lse = reinterpret_cast<float*>(ws + w.acc_lse);
+  a.part_o = reinterpret_cast<float*>(ws + w.part_o[b]);
+  a.part_lse = reinterpret_cast<float*>(ws + w.part_lse[b]);
+  a.out = out;
+  a.lse = lse;
+  a.seq_len = p.seq_len;
+  a.n_loc = int32_t(p.n_loc);
+  a.heads = p.heads;
+  a.scale = 1.0f / std::sqrt(float(p.head_dim));
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.out_f32 = p.dtype == CP_ATTN_FP32;
+  a.nseg = sd.nseg;
+  a.total_tiles = 0;
+  const bool separate = p.opt_merge == 1;
+  for (int i = 0; i < sd.nseg; ++i) {
+    const Segment& g = sd.seg[i];
+    SegArgs& x = a.seg[i];
+    x.q_global = g.q_global;
+    x.q_start = int32_t(g.q_start);
+    x.q_len = int32_t(g.q_len);
+    x.kv_full = int32_t(g.kv_full);
+    x.diag = g.diag;
+    x.tiles = int32_t((g.q_len + bm - 1) / bm);
+    if (separate) {
+      x.epi = g.first ? kEpiInit : kEpiPartial;
+    } else {
+      x.epi = (g.first ? kEpiInit : kEpiMerge) | (g.last ? kEpiFinal : 0);
+    }
+    a.total_tiles += x.tiles;
+  }
+  if (sd.nseg == 1) a.seg[1] = SegArgs{};
+  const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
+  if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
+  return CP_ATTN_OK;
+}
+
+// Separate-merge mode: fold part[b] of step (r, s) into the running state.
+int launch_step_merge(Plan& p, int r, int s, int b, hipStream_t ms) {
+  DeviceState& d = *p.dev;
+  const WsLayout w = ws_layout(p);
+  char* ws = static_cast<char*>(d.ws);
+  const StepDesc& sd = p.step(r, s);
+  MergeArgs m{};
+  m.o_s = reinterpret_cast<const float*>(ws + w.part_o[b]);
+  m.lse_s = reinterpret_cast<const float*>(ws + w.part_lse[b]);
+  m.o_acc = reinterpret_cast<float*>(ws + w.acc_o);
+  m.lse_acc = reinterpret_cast<float*>(ws + w.acc_lse);
+  m.n_rows_total = p.n_loc;
+  m.heads = p.heads;
+  m.head_dim = p.head_dim;
+  for (int i = 0; i < sd.nseg; ++i) {
+    if (sd.seg[i].first) continue;  // written straight into the state
+    m.seg_start[m.nseg] = int32_t(sd.seg[i].q_start);
+    m.seg_len[m.nseg] = int32_t(sd.seg[i].q_len);
+    ++m.nseg;
+  }
+  if (m.nseg == 0) return CP_ATTN_OK;
+  CPA_HIP(launch_merge(m, ms));
+  return CP_ATTN_OK;
+}
+
+int launch_rank_finalize(Plan& p, void* out, float* lse, int r, hipStream_t st) {
+  DeviceState& d = *p.dev;
+  const WsLayout w = ws_layout(p);
+  char* ws = static_cast<char*>(d.ws);
+  FinalizeArgs f{};
+  f.acc_o = reinterpret_cast<const float*>(ws + w.acc_o);
+  f.acc_lse = reinterpret_cast<const float*>(ws + w.acc_lse);
+  f.out = out;
+  f.lse = lse;
+  f.seq_len = p.seq_len;
+  f.n_loc = int32_t(p.n_loc);
+  f.heads = p.heads;
+  f.head_dim = p.head_dim;
+  f.out_f32 = p.dtype == CP_ATTN_FP32;
+  const int nch = p.layout == 1 ? 2 : 1;
+  f.nseg = nch;
+  for (int c = 0; c < nch; ++c) {
+    f.seg_start[c] = int32_t(c * p.chunk);
+    f.seg_len[c] = int32_t(p.chunk);
+    f.seg_global[c] = p.global_row(r, c * p.chunk);
+  }
+  CPA_HIP(launch_finalize(f, st));
+  return CP_ATTN_OK;
+}
+
+#define CPA_TRY(x)                \
+  do {                            \
+    const int rc_ = (x);          \
+    if (rc_ != CP_ATTN_OK) return rc_; \
+  } while (0)
+
+int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, float* lse, int r, hipStream_t st) {
+  DeviceState& d = *p.dev;
+  const WsLayout w = ws_layout(p);
+  char* ws = static_cast<char*>(d.ws);
+  const int P = p.cp;
+  const bool serial = p.opt_serialize != 0;
+  const bool separate = p.opt_merge == 1;
+  hipStream_t cs = serial ? st : d.copy;
+  hipStream_t ms = serial ? st : d.merge;
+
+  if (!serial) {
+    CPA_HIP(hipEventRecord(d.start, st));
+    CPA_HIP(hipStreamWaitEvent(cs, d.start, 0));
+    if (separate) CPA_HIP(hipStreamWaitEvent(ms, d.start, 0));
+  }
+  CPA_TRY(recv_kv(p, k, v, p.step(r, 0).src, 0, cs));
+  if (!serial) CPA_HIP(hipEventRecord(d.recv_done[0], cs));
+
+  for (int s = 0; s < P; ++s) {
+    const int b = s & 1;
+    if (s + 1 < P) {
+      const int nb = (s + 1) & 1;
+      if (!serial && s >= 1) CPA_HIP(hipStreamWaitEvent(cs, d.attn_done[nb], 0));
+      CPA_TRY(recv_kv(p, k, v, p.step(r, s + 1).src, nb, cs));
+      if (!serial) CPA_HIP(hipEventRecord(d.recv_done[nb], cs));
+    }
+    if (!serial) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
+    if (separate && !serial && s >= 2) CPA_HIP(hipStreamWaitEvent(st, d.merge_done[b], 0));
+    const size_t ti = size_t(r) * P + s;
+    if (p.opt_step_timing) CPA_HIP(hipEventRecord(d.t0[ti], st));
+    CPA_TRY(launch_step(p, q, out, lse, r, s, b, st));
+    if (p.opt_step_timing) {
+      CPA_HIP(hipEventRecord(d.t1[ti], st));
+      d.timed[ti] = 1;
+    }
+    if (p.opt_poison) {
+      CPA_HIP(launch_poison(ws + w.slot_k[b], w.kv_bytes, st));
+      CPA_HIP(launch_poison(ws + w.slot_v[b], w.kv_bytes, st));
+    }
+    if (!serial) CPA_HIP(hipEventRecord(d.attn_done[b], st));
+    if (separate && s > 0) {
+      if (!serial) CPA_HIP(hipStreamWaitEvent(ms, d.attn_done[b], 0));
+      CPA_TRY(launch_step_merge(p, r, s, b, ms));
+      if (p.opt_poison) {
+        CPA_HIP(launch_poison(ws + w.part_o[b], w.o_bytes, ms));
+        CPA_HIP(launch_poison(ws + w.part_lse[b], w.lse_bytes, ms));
+      }
+      if (!serial) CPA_HIP(hipEventRecord(d.merge_done[b], ms));
+    }
+  }
+  if (separate) {
+    if (!serial) {
+      CPA_HIP(hipEventRecord(d.merge_join, ms));
+      CPA_HIP(hipStreamWaitEvent(st, d.merge_join, 0));
+    }
+    CPA_TRY(launch_rank_finalize(p, out, lse, r, st));
+  }
+  return CP_ATTN_OK;
+}
+
+int check_plan(cp_attn_plan_t h) {
+  if (!h || !h->p) return fail(CP_ATTN_EINVAL, "plan is null");
+  return CP_ATTN_OK;
+}
+
+int check_io(const void* q, const void* k, const void* v, const void* out, const void* lse) {
+  const void* ptrs[5] = {q, k, v, out, lse};
+  const char* names[5] = {"q", "k", "v", "out", "lse"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(CP_ATTN_EINVAL, std::string(names[i]) + " is null");
+    if (!aligned16(ptrs[i])) return fail(CP_ATTN_EINVAL, std::string(names[i]) + " is not 16-byte aligned");
+  }
+  return CP_ATTN_OK;
+}
+
+void reset_timing(Plan& p) {
+  DeviceState& d = *p.dev;
+  d.timed.assign(size_t(p.cp) * p.cp, 0);
+}
+
+}  // namespace
+}  // namespace cpattn
+
+using namespace cpattn;
+
+#define CPA_GUARD_BEGIN try {
+#define CPA_GUARD_END                                              \
+  }                                                                \
+  catch (const std::bad_alloc&) {                                  \
+    return fail(CP_ATTN_EINVAL, "host allocation failed");         \
+  }                                                                \
+  catch (...) {                                                    \
+    return fail(CP_ATTN_EINVAL, "unexpected C++ exception");       \
+  }
+
+extern "C" {
+
+int cp_attn_plan(int64_t seq_len, int cp_size, int heads, int head_dim, int causal, int layout,
+                 cp_attn_plan_t* out) {
+  CPA_GUARD_BEGIN
+  if (!out) return fail(CP_ATTN_EINVAL, "out is null");
+  *out = nullptr;
+  Plan* p = nullptr;
+  std::string err;
+  const int rc = make_plan(seq_len, cp_size, heads, head_dim, causal, layout, &p, &err);
+  if (rc != CP_ATTN_OK) return fail(rc, err);
+  p->dev = new DeviceState;
+  *out = new cp_attn_plan_s{p};
+  return CP_ATTN_OK;
+  CPA_GUARD_END
+}
+
+int cp_attn_plan_destroy(cp_attn_plan_t h) {
+  CPA_GUARD_BEGIN
+  if (!h) return CP_ATTN_OK;
+  Plan* p = h->p;
+  int rc = CP_ATTN_OK;
+  if (p && p->dev) {
+    DeviceState& d = *p->dev;
+    if (d.device >= 0) {
+      int cur = 0;
+      (void)hipGetDevice(&cur);
+      (void)hipSetDevice(d.device);
+      if (hipDeviceSynchronize() != hipSuccess) rc = fail(CP_ATTN_EHIP, "hipDeviceSynchronize failed in destroy");
+      if (d.own_ws && d.ws) (void)hipFree(d.ws);
+      if (d.own_copy && d.copy) (void)hipStreamDestroy(d.copy);
+      if (d.own_merge && d.merge) (void)hipStreamDestroy(d.merge);
+      if (d.events_ready) {
+        (void)hipEventDestroy(d.start);
+        (void)hipEventDestroy(d.merge_join);
+        for (int b = 0; b < 2; ++b) {
+          (void)hipEventDestroy(d.recv_done[b]);
+          (void)hipEventDestroy(d.attn_done[b]);
+          (void)hipEventDestroy(d.merge_done[b]);
+        }
+      }
+      for (hipEvent_t e : d.t0) (void)hipEventDestroy(e);
+      for (hipEvent_t e : d.t1) (void)hipEventDestroy(e);
+      (void)hipSetDevice(cur);
+    }
+    delete p->dev;
+  }
+  delete p;
+  delete h;
+  return rc;
+  CPA_GUARD_END
+}
+
+int cp_attn_set_dtype(cp_attn_plan_t h, int dtype) {
+  CPA_TRY(check_plan(h));
+  if (dtype != CP_ATTN_BF16 && dtype != CP_ATTN_FP32) return fail(CP_ATTN_EINVAL, "dtype must be BF16 or FP32");
+  h->p->dtype = dtype;
+  return CP_ATTN_OK;
+}
+
+int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
+  CPA_TRY(check_plan(h));
+  Plan& p = *h->p;
+  switch (option) {
+    case CP_ATTN_OPT_MERGE:
+      if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "merge option must be 0 or 1");
+      p.opt_merge = value;
+      return CP_ATTN_OK;
+    case CP_ATTN_OPT_SERIALIZE:
+      p.opt_serialize = value != 0;
+      return CP_ATTN_OK;
+    case CP_ATTN_OPT_RECV:
+      if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "recv option must be 0 or 1");
+      p.opt_recv = value;
+      return CP_ATTN_OK;
+    case CP_ATTN_OPT_POISON:
+      p.opt_poison = value != 0;
+      return CP_ATTN_OK;
+    case CP_ATTN_OPT_STEP_TIMING:
+      p.opt_step_timing = value != 0;
+      return CP_ATTN_OK;
+    default:
+      return fail(CP_ATTN_EINVAL, "unknown option");
+  }
+}
+
+int cp_attn_workspace_bytes(cp_attn_plan_t h, int64_t* bytes) {
+  CPA_TRY(check_plan(h));
+  if (!bytes) return fail(CP_ATTN_EINVAL, "bytes is null");
+  *bytes = ws_layout(*h->p).total;
+  return CP_ATTN_OK;
+}
+
+int cp_attn_set_workspace(cp_attn_plan_t h, void* ptr, int64_t bytes) {
+  CPA_TRY(check_plan(h));
+  DeviceState& d = *h->p->dev;
+  if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 255u)) return fail(CP_ATTN_EINVAL, "workspace not 256-byte aligned");
+  if (ptr && bytes < ws_layout(*h->p).total) return fail(CP_ATTN_ENOWORKSPACE, "workspace too small");
+  if (d.own_ws && d.ws) {
+    CPA_HIP(hipDeviceSynchronize());
+    CPA_HIP(hipFree(d.ws));
+  }
+  d.ws = ptr;
+  d.ws_bytes = ptr ? bytes : 0;
+  d.own_ws = false;
+  return CP_ATTN_OK;
+}
+
+int cp_attn_set_streams(cp_attn_plan_t h, void* copy_stream, void* merge_stream) {
+  CPA_TRY(check_plan(h));
+  DeviceState& d = *h->p->dev;
+  if (d.own_copy && d.copy) CPA_HIP(hipStreamDestroy(d.copy));
+  if (d.own_merge && d.merge) CPA_HIP(hipStreamDestroy(d.merge));
+  d.copy = static_cast<hipStream_t>(copy_stream);
+  d.merge = static_cast<hipStream_t>(merge_stream);
+  d.own_copy = d.own_merge = false;
+  return CP_ATTN_OK;
+}
+
+int cp_attn_rank_forward(cp_attn_plan_t h, const void* q, const void* k, const void* v, void* out, float* lse,
+                         int rank, void* stream) {
+  CPA_GUARD_BEGIN
+  CPA_TRY(check_plan(h));
+  Plan& p = *h->p;
+  if (rank < 0 || rank >= p.cp) return fail(CP_ATTN_EINVAL, "rank outside [0, cp_size)");
+  CPA_TRY(check_io(q, k, v, out, lse));
+  CPA_TRY(ensure_device(p));
+  reset_timing(p);
+  return run_rank(p, q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
+  CPA_GUARD_END
+}
+
+int cp_attn_full_forward(cp_attn_plan_t h, const void* q, const void* k, const void* v, void* out, float* lse,
+                         void* stream) {
+  CPA_GUARD_BEGIN
+  CPA_TRY(check_plan(h));
+  Plan& p = *h->p;
+  CPA_TRY(check_io(q, k, v, out, lse));
+  CPA_TRY(ensure_device(p));
+  reset_timing(p);
+  for (int r = 0; r < p.cp; ++r) CPA_TRY(run_rank(p, q, k, v, out, lse, r, static_cast<hipStream_t>(stream)));
+  return CP_ATTN_OK;
+  CPA_GUARD_END
+}
+
+int cp_attn_local_rows(cp_attn_plan_t h, int64_t* rows) {
+  CPA_TRY(check_plan(h));
+  if (!rows) return fail(CP_ATTN_EINVAL, "rows is null");
+  *rows = h->p->n_loc;
+  return CP_ATTN_OK;
+}
+
+int cp_attn_rank_chunks(cp_attn_plan_t h, int rank, int32_t chunks[2], int32_t* count) {
+  CPA_TRY(check_plan(h));
+  const Plan& p = *h->p;
+  if (!chunks || !count) return fail(CP_ATTN_EINVAL, "output is null");
+  if (rank < 0 || rank >= p.cp) return fail(CP_ATTN_EINVAL, "rank outside [0, cp_size)");
+  *count = p.layout == 1 ? 2 : 1;
+  chunks[0] = int32_t(p.chunk_of(rank, 0));
+  chunks[1] = p.layout == 1 ? int32_t(p.chunk_of(rank, 1)) : -1;
+  return CP_ATTN_OK;
+}
+
+int cp_attn_step_source(cp_attn_plan_t h, int rank, int step, int32_t* source) {
+  CPA_TRY(check_plan(h));
+  const Plan& p = *h->p;
+  if (!source) return fail(CP_ATTN_EINVAL, "source is null");
+  if (rank < 0 || rank >= p.cp || step < 0 || step >= p.cp) return fail(CP_ATTN_EINVAL, "rank or step out of range");
+  *source = p.step(rank, step).src;
+  return CP_ATTN_OK;
+}
+
+int cp_attn_step_segments(cp_attn_plan_t h, int rank, int step, int64_t out[14], int32_t* count) {
+  CPA_TRY(check_plan(h));
+  const Plan& p = *h->p;
+  if (!out || !count) return fail(CP_ATTN_EINVAL, "output is null");
+  if (rank < 0 || rank >= p.cp || step < 0 || step >= p.cp) return fail(CP_ATTN_EINVAL, "rank or step out of range");
+  const StepDesc& d = p.step(rank, step);
+  *count = d.nseg;
+  for (int i = 0; i < 2; ++i) {
+    const Segment g = i < d.nseg ? d.seg[i] : Segment{};
+    int64_t* o = out + 7 * i;
+    o[0] = g.q_start;
+    o[1] = g.q_len;
+    o[2] = g.kv_full;
+    o[3] = g.diag;
+    o[4] = g.first;
+    o[5] = g.last;
+    o[6] = g.q_global;
+  }
+  return CP_ATTN_OK;
+}
+
+int cp_attn_valid_work(cp_attn_plan_t h, int rank, int step, int bm, int bn, int64_t* tiles, int64_t* pairs) {
+  CPA_TRY(check_plan(h));
+  const Plan& p = *h->p;
+  if (rank < 0 || rank >= p.cp || step < 0 || step >= p.cp) return fail(CP_ATTN_EINVAL, "rank or step out of range");
+  if (bm <= 0 || bn <= 0) return fail(CP_ATTN_EINVAL, "tile sizes must be positive");
+  if (tiles) *tiles = step_tiles(p, rank, step, bm, bn);
+  if (pairs) *pairs = step_pairs(p, rank, step);
+  return CP_ATTN_OK;
+}
+
+static int layout_all(cp_attn_plan_t h, const void* src, void* dst, void* stream, int to_local) {
+  CPA_TRY(check_plan(h));
+  const Plan& p = *h->p;
+  if (!src || !dst) return fail(CP_ATTN_EINVAL, "src or dst is null");
+  if (!aligned16(src) || !aligned16(dst)) return fail(CP_ATTN_EINVAL, "src or dst not 16-byte aligned");
+  LayoutArgs la{};
+  la.src[0] = src;
+  la.dst[0] = dst;
+  la.ntensors = 1;
+  la.rank_begin = 0;
+  la.rank_count = p.cp;
+  la.cp = p.cp;
+  la.zigzag = p.layout == 1;
+  la.to_local = to_local;
+  la.chunk = p.chunk;
+  la.n_loc = p.n_loc;
+  la.row_vec = int64_t(p.heads) * p.head_dim * p.elem_bytes() / 16;
+  la.dst_rank0 = 0;
+  CPA_HIP(launch_layout(la, static_cast<hipStream_t>(stream)));
+  return CP_ATTN_OK;
+}
+
+int cp_attn_layout_gather(cp_attn_plan_t h, const void* src, void* dst, void* stream) {
+  return layout_all(h, src, dst, stream, 1);
+}
+
+int cp_attn_layout_scatter(cp_attn_plan_t h, const void* src, void* dst, void* stream) {
+  return layout_all(h, src, dst, stream, 0);
+}
+
+int cp_attn_lse_merge(float* o_acc, float* lse_acc, const float* o_s, const float* lse_s, int64_t rows, int heads,
+                      int head_dim, void* stream) {
+  if (!o_acc || !lse_acc || !o_s || !lse_s) return fail(CP_ATTN_EINVAL, "null pointer");
+  if (!aligned16(o_acc) || !aligned16(o_s)) return fail(CP_ATTN_EINVAL, "O pointers not 16-byte aligned");
+  if (rows < 0 || heads <= 0 || head_dim <= 0 || head_dim % 4 || 64 % (head_dim / 4) || rows > INT32_MAX)
+    return fail(CP_ATTN_EINVAL, "bad sizes (head_dim/4 must divide 64)");
+  if (rows == 0) return CP_ATTN_OK;
+  MergeArgs m{};
+  m.o_s = o_s;
+  m.lse_s = lse_s;
+  m.o_acc = o_acc;
+  m.lse_acc = lse_acc;
+  m.n_rows_total = rows;
+  m.heads = heads;
+  m.head_dim = head_dim;
+  m.nseg = 1;
+  m.seg_start[0] = 0;
+  m.seg_len[0] = int32_t(rows);
+  CPA_HIP(launch_merge(m, static_cast<hipStream_t>(stream)));
+  return CP_ATTN_OK;
+}
+
+int cp_attn_last_step_times(cp_attn_plan_t h, float* ms, int n) {
+  CPA_TRY(check_plan(h));
+  const Plan& p = *h->p;
+  if (!ms) return fail(CP_ATTN_EINVAL, "ms is null");
+  const size_t nn = size_t(p.cp) * p.cp;
+  if (n < 0 || size_t(n) < nn) return fail(CP_ATTN_EINVAL, "n < cp_size * cp_size");
+  DeviceState& d = *p.dev;
+  for (size_t i = 0; i < nn; ++i) {
+    ms[i] = -1.f;
+    if (i < d.timed.size() && d.timed[i] && i < d.t1.size()) {
+      CPA_HIP(hipEventSynchronize(d.t1[i]));
+      float t = 0.f;
+      CPA_HIP(hipEventElapsedTime(&t, d.t0[i], d.t1[i]));
+      ms[i] = t;
+    }
+  }
+  return CP_ATTN_OK;
+}
+
+const char* cp_attn_status_string(int status) {
+  switch (status) {
+    case CP_ATTN_OK:
+      return "ok";
+    case CP_ATTN_EINVAL:
+      return "invalid argument";
+    case CP_ATTN_EUNSUPPORTED:
+      return "unsupported configuration";
+    case CP_ATTN_ENOWORKSPACE:
+      return "workspace missing, too small or not allocatable";
+    case CP_ATTN_EHIP:
+      return "HIP runtime error";
+    default:
+      return "unknown status";
+  }
+}
+
+const char* cp_attn_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Step epilogue shared by the attention kernels: turn one row's step result
+// (normalised O_s, lse_s) into the running state, a partial, or the output.
+//
+// Exact merge ("Sequence Parallelism IV: Megatron Context Parallel and
+// Load-Balanced Rings", section 4 "What Actually Moves": the online softmax
+// state keeps the result exact across block updates).  In (O, LSE) form:
+//   lse' = max(a, b) + log1p(exp(-|a - b|)),
+//   O'   = exp(a - lse') O_acc + exp(b - lse') O_s,
+// where a = lse_acc, b = lse_s; an empty state (a = -inf) takes the partial.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "kernels.h"
+
+namespace cpattn {
+
+struct RowEpi {
+  float wa;  // weight of the running state (0: not read)
+  float ws;  // weight of this step's partial
+  float L;   // resulting LSE (natural log)
+};
+
+__device__ __forceinline__ RowEpi row_epi_begin(const StepArgs& a, const SegArgs& g, int h, int lrow,
+                                                float lse_s) {
+  RowEpi e{0.f, 1.f, lse_s};
+  if ((g.epi & 3) == kEpiMerge) {
+    const float la = a.acc_lse[int64_t(h) * a.n_loc + lrow];
+    if (la != -INFINITY) {
+      if (lse_s == -INFINITY) {
+        e.wa = 1.f;
+        e.ws = 0.f;
+        e.L = la;
+      } else {
+        const float mx = fmaxf(la, lse_s);
+        const float L = mx + log1pf(expf(-fabsf(la - lse_s)));
+        e.wa = expf(la - L);
+        e.ws = expf(lse_s - L);
+        e.L = L;
+      }
+    }
+  }
+  return e;
+}
+
+// Four consecutive head-dim values d0..d0+3 of local row lrow, head h.
+__device__ __forceinline__ void row_epi_store4(const StepArgs& a, const SegArgs& g, const RowEpi& e, int h,
+                                               int lrow, int64_t grow, int d0, int head_dim, float4 o) {
+  const int mode = g.epi & 3;
+  const int64_t lidx = (int64_t(lrow) * a.heads + h) * head_dim + d0;
+  if (mode == kEpiPartial) {
+    *reinterpret_cast<float4*>(a.part_o + lidx) = o;
+    return;
+  }
+  float4 r = make_float4(o.x * e.ws, o.y * e.ws, o.z * e.ws, o.w * e.ws);
+  if (mode == kEpiMerge && e.wa != 0.f) {
+    const float4 c = *reinterpret_cast<const float4*>(a.acc_o + lidx);
+    r.x += e.wa * c.x;
+    r.y += e.wa * c.y;
+    r.z += e.wa * c.z;
+    r.w += e.wa * c.w;
+  }
+  if (g.epi & kEpiFinal) {
+    const int64_t gidx = (grow * a.heads + h) * head_dim + d0;
+    if (a.out_f32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + gidx) = r;
+    } else {
+      __bf16* op = static_cast<__bf16*>(a.out) + gidx;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 b;
+      b[0] = static_cast<__bf16>(r.x);
+      b[1] = static_cast<__bf16>(r.y);
+      b[2] = static_cast<__bf16>(r.z);
+      b[3] = static_cast<__bf16>(r.w);
+      *reinterpret_cast<bf16x4*>(op) = b;
+    }
+  } else {
+    *reinterpret_cast<float4*>(a.acc_o + lidx) = r;
+  }
+}
+
+__device__ __forceinline__ void row_epi_store_lse(const StepArgs& a, const SegArgs& g, const RowEpi& e, int h,
+                                                  int lrow, int64_t grow, float lse_s) {
+  const int mode = g.epi & 3;
+  if (mode == kEpiPartial) {
+    a.part_lse[int64_t(h) * a.n_loc + lrow] = lse_s;
+  } else if (g.epi & kEpiFinal) {
+    a.lse[int64_t(h) * a.seq_len + grow] = e.L;
+  } else {
+    a.acc_lse[int64_t(h) * a.n_loc + lrow] = e.L;
+  }
+}
+
+}  // namespace cpattn

@@ -1,0 +1,112 @@
+// Kernel argument structs and launcher declarations shared by the HIP
+// translation units of libcpattn.so (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace cpattn {
+
+// Epilogue of a step for one row segment.
+enum EpiMode : int32_t {
+  kEpiInit = 0,     // running state := this step's partial
+  kEpiMerge = 1,    // running state := LSE-merge(running state, partial)
+  kEpiPartial = 2,  // write the partial to the partial buffer (separate merge)
+};
+constexpr int32_t kEpiFinal = 4;  // with Init/Merge: write the result to out/lse instead of the state
+
+struct SegArgs {
+  int64_t q_global;  // global token of local row q_start
+  int32_t q_start;   // first local row
+  int32_t q_len;     // rows
+  int32_t kv_full;   // keys every row sees
+  int32_t diag;      // 1: row t also sees keys kv_full .. kv_full + t
+  int32_t epi;       // EpiMode | kEpiFinal
+  int32_t tiles;     // ceil(q_len / BM) for the launching kernel
+};
+
+struct StepArgs {
+  const void* q;     // [S][H][D] natural order, plan dtype
+  const void* k;     // receive slot [n_loc][H][D]
+  const void* v;
+  float* acc_o;      // [n_loc][H][D] running O (normalised)
+  float* acc_lse;    // [H][n_loc] running LSE (natural log)
+  float* part_o;     // [n_loc][H][D] partial O (separate merge mode)
+  float* part_lse;   // [H][n_loc]
+  void* out;         // [S][H][D] plan dtype
+  float* lse;        // [H][S]
+  int64_t seq_len;
+  int32_t n_loc;
+  int32_t heads;
+  float scale_log2;  // softmax scale * log2(e)
+  float scale;       // softmax scale 1/sqrt(D)
+  int32_t out_f32;   // 1: out is fp32, 0: bf16
+  int32_t nseg;
+  int32_t total_tiles;  // sum of seg[i].tiles
+  SegArgs seg[2];
+};
+
+// attention step kernels: return hipError_t of the launch
+hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_attn_f32(const StepArgs& a, int head_dim, hipStream_t stream);
+int attn_bf16_block_m();
+int attn_f32_block_m();
+
+// Row copies between natural order and rank-local order.
+//   gather (to_local=1): dst row (rank_begin+i)*n_loc + li  <-  src global_row(rank, li)
+//   scatter (to_local=0): the inverse.  ntensors (1 or 2) pairs src/dst.
+struct LayoutArgs {
+  const void* src[2];
+  void* dst[2];
+  int32_t ntensors;
+  int32_t rank_begin;
+  int32_t rank_count;
+  int32_t cp;
+  int32_t zigzag;
+  int32_t to_local;
+  int64_t chunk;       // rows per chunk
+  int64_t n_loc;       // rows per rank
+  int64_t row_vec;     // 16-byte vectors per row
+  int64_t dst_rank0;   // rank whose local buffer starts at dst (gather) / src (scatter) row 0
+};
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+
+// Fill with NaN (all-ones bytes) -- a kernel, not a memset, so it is safe in captured graphs.
+hipError_t launch_poison(void* ptr, int64_t bytes, hipStream_t stream);
+
+// Separate LSE merge (part -> acc) for up to two row segments, optionally
+// writing the final output.  rows_* are local rows.
+struct MergeArgs {
+  const float* o_s;
+  const float* lse_s;
+  float* o_acc;
+  float* lse_acc;
+  int64_t n_rows_total;  // row stride of the lse arrays
+  int32_t heads;
+  int32_t head_dim;
+  int32_t nseg;
+  int32_t seg_start[2];
+  int32_t seg_len[2];
+};
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+// Finalize: running state -> out (plan dtype, RNE) and lse at global rows.
+struct FinalizeArgs {
+  const float* acc_o;
+  const float* acc_lse;
+  void* out;
+  float* lse;
+  int64_t seq_len;
+  int32_t n_loc;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t out_f32;
+  int32_t nseg;
+  int32_t seg_start[2];
+  int32_t seg_len[2];
+  int64_t seg_global[2];
+};
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t stream);
+
+}  // namespace cpattn

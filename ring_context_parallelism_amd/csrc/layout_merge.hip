@@ -1,0 +1,157 @@
+// Bandwidth-bound kernels: zigzag/contiguous layout copies (also the one-GPU
+// ring receive), NaN poisoning, the separate LSE merge, and finalize.
+//
+// Layout ("Sequence Parallelism IV: Megatron Context Parallel and
+// Load-Balanced Rings", section 3): rank r's local rows are chunk r followed
+// by chunk 2cp-1-r (zigzag), or the contiguous slice r.  Each token row is
+// heads*head_dim elements and is moved as whole 16-byte vectors; one
+// workgroup walks whole rows so the row -> global-token arithmetic is done
+// once per row.
+//
+// Merge (section 4 "What Actually Moves"): the running state and a step's
+// partial are folded with log-sum-exp weights, which is exact.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace cpattn {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int64_t local_to_global(int64_t r, int64_t li, int64_t chunk, int64_t n_loc, int cp,
+                                                   int zigzag) {
+  if (!zigzag) return r * n_loc + li;
+  const bool late = li >= chunk;
+  const int64_t ch = late ? 2 * int64_t(cp) - 1 - r : r;
+  return ch * chunk + (late ? li - chunk : li);
+}
+
+__global__ __launch_bounds__(kThreads) void layout_copy(LayoutArgs a) {
+  const int tsel = blockIdx.y;
+  const uint4* src = static_cast<const uint4*>(a.src[tsel]);
+  uint4* dst = static_cast<uint4*>(a.dst[tsel]);
+  const int64_t rows = int64_t(a.rank_count) * a.n_loc;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const int64_t r = a.rank_begin + row / a.n_loc;
+    const int64_t li = row % a.n_loc;
+    const int64_t g = local_to_global(r, li, a.chunk, a.n_loc, a.cp, a.zigzag);
+    const int64_t lrow = (r - a.dst_rank0) * a.n_loc + li;
+    const int64_t from = (a.to_local ? g : lrow) * a.row_vec;
+    const int64_t to = (a.to_local ? lrow : g) * a.row_vec;
+    for (int64_t c = threadIdx.x; c < a.row_vec; c += kThreads) dst[to + c] = src[from + c];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void poison_fill(uint4* p, int64_t n) {
+  const uint4 nan4 = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads)
+    p[i] = nan4;
+}
+
+// One lane per 4 head-dim values; the head_dim/4 lanes of one (row, head)
+// are consecutive and lie inside one wavefront (head_dim/4 divides 64 and the
+// loop stride is a multiple of 64), so every lane has read the old lse_acc
+// before the lane with d4 == 0 overwrites it.
+__global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
+  const int d4n = a.head_dim / 4;
+  const int64_t per_row = int64_t(a.heads) * d4n;
+  const int64_t total = int64_t(a.seg_len[0] + (a.nseg > 1 ? a.seg_len[1] : 0)) * per_row;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total; i += int64_t(gridDim.x) * kThreads) {
+    int64_t rr = i / per_row;
+    const int64_t rem = i % per_row;
+    const int h = int(rem / d4n), d4 = int(rem % d4n);
+    const int64_t lrow = rr < a.seg_len[0] ? a.seg_start[0] + rr : a.seg_start[1] + (rr - a.seg_len[0]);
+    const int64_t li = int64_t(h) * a.n_rows_total + lrow;
+    const float ls = a.lse_s[li];
+    const float la = a.lse_acc[li];
+    const int64_t oi = (lrow * a.heads + h) * a.head_dim + 4 * d4;
+    if (ls == -INFINITY) continue;  // nothing to fold in
+    float wa = 0.f, ws = 1.f, L = ls;
+    if (la != -INFINITY) {
+      const float mx = fmaxf(la, ls);
+      L = mx + log1pf(expf(-fabsf(la - ls)));
+      wa = expf(la - L);
+      ws = expf(ls - L);
+    }
+    const float4 os = *reinterpret_cast<const float4*>(a.o_s + oi);
+    float4 r = make_float4(ws * os.x, ws * os.y, ws * os.z, ws * os.w);
+    if (wa != 0.f) {
+      const float4 oa = *reinterpret_cast<const float4*>(a.o_acc + oi);
+      r.x += wa * oa.x;
+      r.y += wa * oa.y;
+      r.z += wa * oa.z;
+      r.w += wa * oa.w;
+    }
+    *reinterpret_cast<float4*>(a.o_acc + oi) = r;
+    if (d4 == 0) a.lse_acc[li] = L;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void finalize_rows(FinalizeArgs a) {
+  const int d4n = a.head_dim / 4;
+  const int64_t per_row = int64_t(a.heads) * d4n;
+  const int64_t total = int64_t(a.seg_len[0] + (a.nseg > 1 ? a.seg_len[1] : 0)) * per_row;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total; i += int64_t(gridDim.x) * kThreads) {
+    const int64_t rr = i / per_row;
+    const int64_t rem = i % per_row;
+    const int h = int(rem / d4n), d4 = int(rem % d4n);
+    const bool second = rr >= a.seg_len[0];
+    const int64_t off = second ? rr - a.seg_len[0] : rr;
+    const int64_t lrow = (second ? a.seg_start[1] : a.seg_start[0]) + off;
+    const int64_t grow = (second ? a.seg_global[1] : a.seg_global[0]) + off;
+    const float4 o = *reinterpret_cast<const float4*>(a.acc_o + (lrow * a.heads + h) * a.head_dim + 4 * d4);
+    const int64_t gi = (grow * a.heads + h) * a.head_dim + 4 * d4;
+    if (a.out_f32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + gi) = o;
+    } else {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 b;
+      b[0] = static_cast<__bf16>(o.x);
+      b[1] = static_cast<__bf16>(o.y);
+      b[2] = static_cast<__bf16>(o.z);
+      b[3] = static_cast<__bf16>(o.w);
+      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + gi) = b;
+    }
+    if (d4 == 0) a.lse[int64_t(h) * a.seq_len + grow] = a.acc_lse[int64_t(h) * a.n_loc + lrow];
+  }
+}
+
+unsigned grid_for(int64_t work_items, int64_t per_block, unsigned cap) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return unsigned(g);
+}
+
+}  // namespace
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
+  const int64_t rows = int64_t(a.rank_count) * a.n_loc;
+  const dim3 grid(grid_for(rows, 1, 65536u), unsigned(a.ntensors));
+  layout_copy<<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_poison(void* ptr, int64_t bytes, hipStream_t stream) {
+  const int64_t n = bytes / 16;
+  poison_fill<<<grid_for(n, kThreads, 8192u), kThreads, 0, stream>>>(static_cast<uint4*>(ptr), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+  const int64_t total = int64_t(a.seg_len[0] + (a.nseg > 1 ? a.seg_len[1] : 0)) * a.heads * (a.head_dim / 4);
+  lse_merge<<<grid_for(total, kThreads, 16384u), kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t stream) {
+  const int64_t total = int64_t(a.seg_len[0] + (a.nseg > 1 ? a.seg_len[1] : 0)) * a.heads * (a.head_dim / 4);
+  finalize_rows<<<grid_for(total, kThreads, 16384u), kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

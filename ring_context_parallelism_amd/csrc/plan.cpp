@@ -1,0 +1,187 @@
+// Host-side plan for zigzag / contiguous ring context-parallel attention.
+//
+// Chunk placement follows "Sequence Parallelism IV: Megatron Context Parallel
+// and Load-Balanced Rings", section 3 (Naive Ring Attention Is Imbalanced
+// Under Causal Masks): 2*cp chunks, rank r owns the early chunk r and the late
+// chunk 2*cp-1-r, kept early first in the rank's local buffer; the naive
+// placement gives rank r the contiguous slice r.  The ring (sections 4 and 5)
+// moves K/V to a neighbour each step; rank r receives from r-1, so at step s
+// it holds the K/V of source j = (r - s) mod cp.
+//
+// Causal step descriptors (section 4: the mask must know which local query
+// positions and remote key positions are valid; future sub-blocks are
+// skipped).  For a query chunk a and key chunk b of equal length, the pair is
+// fully visible if b < a, causal on the diagonal if b == a, and skipped if
+// b > a.  With a in {r, 2cp-1-r} and b in {j, 2cp-1-j}:
+//   j == r : (r, r) diagonal; (2cp-1-r, r) full; (2cp-1-r, 2cp-1-r) diagonal;
+//            (r, 2cp-1-r) skipped -- causal over the local buffer.
+//   j <  r : both query chunks see key chunk j fully and skip 2cp-1-j.
+//   j >  r : query chunk r sees nothing; chunk 2cp-1-r sees both key chunks.
+// In every case a local row's valid keys form a prefix of the source's local
+// buffer, which is what a Segment records.
+#include "plan.h"
+
+#include <algorithm>
+
+namespace cpattn {
+
+namespace {
+constexpr int kOk = 0, kInval = -1, kUnsupported = -2;
+}
+
+int64_t Plan::chunk_of(int r, int which) const {
+  if (layout == 0) return r;
+  return which == 0 ? r : 2 * int64_t(cp) - 1 - r;
+}
+
+int64_t Plan::global_row(int r, int64_t i) const {
+  if (layout == 0) return int64_t(r) * chunk + i;
+  int which = i < chunk ? 0 : 1;
+  return chunk_of(r, which) * chunk + (i - which * chunk);
+}
+
+static void build_steps(Plan& p) {
+  const int P = p.cp;
+  const int64_t C = p.chunk;
+  p.steps.assign(size_t(P) * P, StepDesc{});
+  for (int r = 0; r < P; ++r) {
+    for (int s = 0; s < P; ++s) {
+      StepDesc& d = p.steps[size_t(r) * P + s];
+      const int j = ((r - s) % P + P) % P;
+      d.src = j;
+      auto add = [&](int64_t q_start, int64_t q_len, int64_t kv_full, int diag) {
+        Segment& g = d.seg[d.nseg++];
+        g.q_start = q_start;
+        g.q_len = q_len;
+        g.kv_full = kv_full;
+        g.diag = diag;
+        g.q_global = p.global_row(r, q_start);
+      };
+      if (p.layout == 1) {  // zigzag: local rows [0,C) chunk r, [C,2C) chunk 2P-1-r
+        if (!p.causal) {
+          add(0, C, 2 * C, 0);
+          add(C, C, 2 * C, 0);
+        } else if (j == r) {
+          add(C, C, C, 1);  // late chunk first: the longer rows (longest-first order)
+          add(0, C, 0, 1);
+        } else if (j < r) {
+          add(0, C, C, 0);
+          add(C, C, C, 0);
+        } else {
+          add(C, C, 2 * C, 0);
+        }
+      } else {  // contiguous: local rows [0,L) chunk r
+        if (!p.causal) {
+          add(0, C, C, 0);
+        } else if (j == r) {
+          add(0, C, 0, 1);
+        } else if (j < r) {
+          add(0, C, C, 0);
+        }
+      }
+    }
+  }
+  // first / last active step of each row run (identified by q_start)
+  for (int r = 0; r < P; ++r) {
+    for (int s = 0; s < P; ++s) {
+      StepDesc& d = p.steps[size_t(r) * P + s];
+      for (int i = 0; i < d.nseg; ++i) {
+        Segment& g = d.seg[i];
+        int first = s, last = s;
+        for (int t = 0; t < P; ++t) {
+          const StepDesc& e = p.steps[size_t(r) * P + t];
+          for (int k = 0; k < e.nseg; ++k) {
+            if (e.seg[k].q_start == g.q_start) {
+              first = std::min(first, t);
+              last = std::max(last, t);
+            }
+          }
+        }
+        g.first = (first == s);
+        g.last = (last == s);
+      }
+    }
+  }
+}
+
+int make_plan(int64_t seq_len, int cp, int heads, int head_dim, int causal, int layout, Plan** out,
+              std::string* err) {
+  if (!out) {
+    *err = "out is null";
+    return kInval;
+  }
+  *out = nullptr;
+  if (seq_len <= 0 || cp <= 0 || heads <= 0 || head_dim <= 0) {
+    *err = "seq_len, cp_size, heads and head_dim must be positive";
+    return kInval;
+  }
+  if (causal != 0 && causal != 1) {
+    *err = "causal must be 0 or 1";
+    return kInval;
+  }
+  if (layout != 0 && layout != 1) {
+    *err = "layout must be CP_ATTN_CONTIGUOUS or CP_ATTN_ZIGZAG";
+    return kInval;
+  }
+  if (cp > 256) {
+    *err = "cp_size above 256 is not supported";
+    return kUnsupported;
+  }
+  const int64_t parts = layout == 1 ? 2 * int64_t(cp) : int64_t(cp);
+  if (seq_len % parts != 0) {
+    *err = layout == 1 ? "zigzag needs seq_len divisible by 2*cp_size"
+                       : "contiguous needs seq_len divisible by cp_size";
+    return kInval;
+  }
+  if (head_dim != 64 && head_dim != 128) {
+    *err = "head_dim must be 64 or 128";
+    return kUnsupported;
+  }
+  if (seq_len * int64_t(heads) * head_dim > (int64_t(1) << 36)) {
+    *err = "seq_len * heads * head_dim too large";
+    return kUnsupported;
+  }
+  Plan* p = new Plan;
+  p->seq_len = seq_len;
+  p->cp = cp;
+  p->heads = heads;
+  p->head_dim = head_dim;
+  p->causal = causal;
+  p->layout = layout;
+  p->chunk = seq_len / parts;
+  p->n_loc = seq_len / cp;
+  build_steps(*p);
+  *out = p;
+  return kOk;
+}
+
+int64_t step_pairs(const Plan& p, int r, int s) {
+  const StepDesc& d = p.step(r, s);
+  int64_t n = 0;
+  for (int i = 0; i < d.nseg; ++i) {
+    const Segment& g = d.seg[i];
+    n += g.q_len * g.kv_full;
+    if (g.diag) n += g.q_len * (g.q_len + 1) / 2;
+  }
+  return n;
+}
+
+int64_t step_tiles(const Plan& p, int r, int s, int bm, int bn) {
+  const StepDesc& d = p.step(r, s);
+  int64_t tiles = 0;
+  for (int64_t i0 = 0; i0 < p.n_loc; i0 += bm) {
+    const int64_t i1 = std::min<int64_t>(p.n_loc, i0 + bm);
+    int64_t maxpre = 0;  // longest valid key prefix among the tile's rows
+    for (int k = 0; k < d.nseg; ++k) {
+      const Segment& g = d.seg[k];
+      const int64_t a = std::max(i0, g.q_start), b = std::min(i1, g.q_start + g.q_len);
+      if (a >= b) continue;
+      const int64_t pre = g.kv_full + (g.diag ? (b - 1 - g.q_start) + 1 : 0);
+      maxpre = std::max(maxpre, pre);
+    }
+    tiles += (maxpre + bn - 1) / bn;
+  }
+  return tiles;
+}
+
+}  // namespace cpattn

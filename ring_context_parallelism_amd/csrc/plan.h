@@ -1,0 +1,66 @@
+// Host-side plan: chunk map, ring sources and per-(rank, step) descriptors.
+// Pure C++ (no HIP), so it builds with any host compiler.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace cpattn {
+
+// One run of local query rows that all see a prefix of the source's local
+// K/V buffer: local row q_start + t sees keys [0, kv_full + (diag ? t + 1 : 0)).
+struct Segment {
+  int64_t q_start = 0;
+  int64_t q_len = 0;
+  int64_t kv_full = 0;
+  int32_t diag = 0;
+  int32_t first = 0;  // first ring step in which these rows are active
+  int32_t last = 0;   // last ring step in which these rows are active
+  int64_t q_global = 0;  // global token position of local row q_start
+};
+
+struct StepDesc {
+  int32_t src = 0;
+  int32_t nseg = 0;
+  Segment seg[2];
+};
+
+struct DeviceState;  // streams, events, workspace (defined with the HIP code)
+
+struct Plan {
+  int64_t seq_len = 0;
+  int32_t cp = 1;
+  int32_t heads = 0;
+  int32_t head_dim = 0;
+  int32_t causal = 1;
+  int32_t layout = 1;
+  int32_t dtype = 0;
+  int64_t chunk = 0;   // S/(2cp) zigzag, S/cp contiguous
+  int64_t n_loc = 0;   // rows per rank
+  std::vector<StepDesc> steps;  // [rank * cp + step]
+
+  // options
+  int32_t opt_merge = 0;
+  int32_t opt_serialize = 0;
+  int32_t opt_recv = 0;
+  int32_t opt_poison = 0;
+  int32_t opt_step_timing = 0;
+
+  DeviceState* dev = nullptr;
+
+  const StepDesc& step(int r, int s) const { return steps[size_t(r) * cp + s]; }
+  int64_t elem_bytes() const { return dtype == 1 ? 4 : 2; }
+  // global token position of local row i of rank r
+  int64_t global_row(int r, int64_t i) const;
+  int64_t chunk_of(int r, int which) const;  // which in {0, 1}
+};
+
+// Returns a status code; on success *out is a new plan.
+int make_plan(int64_t seq_len, int cp, int heads, int head_dim, int causal, int layout, Plan** out,
+              std::string* err);
+
+int64_t step_pairs(const Plan& p, int r, int s);
+int64_t step_tiles(const Plan& p, int r, int s, int bm, int bn);
+
+}  // namespace cpattn

@@ -1,0 +1,268 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: fp32 inputs max|dO| <= 1e-5 and max|dLSE| <= 1e-5; bf16 inputs
+max|dO| <= 2e-2 and max|dLSE| <= 1e-3 (O rounded to bf16 once; P rounded to
+bf16 before the P.V product on the GPU side only).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_context_parallelism_amd import Plan, lse_merge
+from ring_context_parallelism_amd.inputs import WORKLOADS, make_qkv, workload_qkv, to_numpy_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: (1e-5, 1e-5), torch.bfloat16: (2e-2, 1e-3)}
+
+
+def _dev():
+    assert torch.cuda.is_available(), "no GPU"
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _run(plan, q, k, v, rank=None):
+    dev = _dev()
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((plan.heads, plan.seq_len), float("nan"), device=dev)
+    if rank is None:
+        plan.full_forward(qd, kd, vd, out, lse)
+    else:
+        plan.rank_forward(qd, kd, vd, out, lse, rank)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def _compare(out, lse, q, k, v, causal, dtype, rows=None, heads=None):
+    """max |dO|, max |dLSE| on the given rows/heads (all by default)."""
+    qn, kn, vn = (to_numpy_f64(t) for t in (q, k, v))
+    rows = np.arange(qn.shape[0]) if rows is None else np.asarray(rows)
+    heads = range(qn.shape[1]) if heads is None else heads
+    d_o = d_l = 0.0
+    for h in heads:
+        o_ref, l_ref = oracle.attention(qn[rows][:, h:h + 1], kn[:, h:h + 1], vn[:, h:h + 1], causal=causal,
+                                        q_pos=rows)
+        o_got = out[rows][:, h:h + 1].to(torch.float64).numpy()
+        l_got = lse[h, rows].to(torch.float64).numpy()
+        assert np.all(np.isfinite(o_got)) and np.all(np.isfinite(l_got))
+        d_o = max(d_o, float(np.max(np.abs(o_got - o_ref))))
+        d_l = max(d_l, float(np.max(np.abs(l_got - l_ref[0]))))
+    return d_o, d_l
+
+
+# ---------------------------------------------------------------- layout ----
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("layout,seq,cp", [("zigzag", 768, 3), ("contiguous", 640, 5), ("zigzag", 8192, 4)])
+def test_layout_gather_scatter_bit_exact(dtype, layout, seq, cp):
+    _say(f"layout {layout} seq={seq} cp={cp} {dtype}")
+    dev = _dev()
+    heads, dim = 3, 64
+    p = Plan(seq, cp, heads, dim, True, layout, dtype=dtype)
+    src = torch.randn(seq, heads, dim, device=dev).to(dtype)
+    dst = torch.empty_like(src)
+    p.layout_gather(src, dst)
+    order = np.concatenate([oracle.rank_positions(seq, cp, r, layout) for r in range(cp)])
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), src.cpu()[torch.from_numpy(order)])
+    back = torch.empty_like(src)
+    p.layout_scatter(dst, back)
+    torch.cuda.synchronize()
+    assert torch.equal(back, src)
+
+
+# -------------------------------------------------------------- fp32 path ----
+
+def test_tiny_fp32_workload_every_row():
+    w = WORKLOADS["causal_s256_cp2_zigzag_h2_d64_fp32"]
+    _say(f"workload {w.name}")
+    q, k, v = workload_qkv(w)
+    p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout, dtype=torch.float32)
+    out, lse = _run(p, q, k, v)
+    d_o, d_l = _compare(out, lse, q, k, v, True, torch.float32)
+    _say(f"  max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= 1e-5 and d_l <= 1e-5
+    assert torch.equal(out[0], v[0])  # one valid key: weight exactly 1
+
+
+@pytest.mark.parametrize("seq,cp,layout,causal,heads,dim", [
+    (384, 3, "contiguous", True, 2, 128), (320, 2, "zigzag", False, 2, 64), (200, 1, "zigzag", True, 1, 128),
+    (520, 2, "zigzag", True, 2, 64),
+])
+def test_fp32_cases(seq, cp, layout, causal, heads, dim):
+    _say(f"fp32 seq={seq} cp={cp} {layout} causal={causal} H={heads} D={dim}")
+    q, k, v = make_qkv(seq, heads, dim, "fp32", 7)
+    p = Plan(seq, cp, heads, dim, causal, layout, dtype=torch.float32)
+    out, lse = _run(p, q, k, v)
+    d_o, d_l = _compare(out, lse, q, k, v, causal, torch.float32)
+    _say(f"  max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= 1e-5 and d_l <= 1e-5
+
+
+# -------------------------------------------------------------- bf16 path ----
+
+BF16_CASES = [
+    (1536, 2, "zigzag", True, 2, 128),      # 3 row tiles per chunk
+    (800, 2, "zigzag", True, 2, 128),       # chunk 200: ragged row and key tiles
+    (768, 3, "contiguous", True, 2, 128),
+    (1024, 4, "zigzag", False, 2, 128),
+    (512, 1, "zigzag", True, 3, 64),
+    (2560, 5, "zigzag", True, 1, 128),
+    (640, 2, "contiguous", False, 2, 64),
+    (96, 3, "zigzag", True, 2, 128),        # chunk 16: a single partial tile
+]
+
+
+@pytest.mark.parametrize("seq,cp,layout,causal,heads,dim", BF16_CASES)
+def test_bf16_cases_every_row(seq, cp, layout, causal, heads, dim):
+    _say(f"bf16 seq={seq} cp={cp} {layout} causal={causal} H={heads} D={dim}")
+    q, k, v = make_qkv(seq, heads, dim, "bf16", 11)
+    p = Plan(seq, cp, heads, dim, causal, layout)
+    out, lse = _run(p, q, k, v)
+    d_o, d_l = _compare(out, lse, q, k, v, causal, torch.bfloat16)
+    _say(f"  max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= 2e-2 and d_l <= 1e-3
+    if causal:
+        assert torch.equal(out[0], v[0])
+
+
+def test_bf16_rank_forward_writes_only_its_rows():
+    seq, cp, heads, dim = 1024, 4, 2, 128
+    q, k, v = make_qkv(seq, heads, dim, "bf16", 12)
+    p = Plan(seq, cp, heads, dim, True, "zigzag")
+    for r in (0, 3):
+        out, lse = _run(p, q, k, v, rank=r)
+        mine = oracle.rank_positions(seq, cp, r, "zigzag")
+        other = np.setdiff1d(np.arange(seq), mine)
+        assert torch.isnan(out[other].float()).all() and torch.isnan(lse[:, other]).all()
+        d_o, d_l = _compare(out, lse, q, k, v, True, torch.bfloat16, rows=mine)
+        assert d_o <= 2e-2 and d_l <= 1e-3
+
+
+def _bitwise_equal(a, b):
+    return torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_schedule_modes_agree(dtype):
+    """Serial == overlapped and poison-on == off bit for bit; memcpy receive == kernel
+    receive bit for bit; separate merge within tolerance of the oracle."""
+    seq, cp, heads, dim = 1536, 3, 2, 128
+    _say(f"modes {dtype}")
+    q, k, v = make_qkv(seq, heads, dim, "bf16" if dtype == torch.bfloat16 else "fp32", 13)
+    p = Plan(seq, cp, heads, dim, True, "zigzag", dtype=dtype)
+    base = _run(p, q, k, v)
+    p.set_serialize(True)
+    ser = _run(p, q, k, v)
+    p.set_serialize(False)
+    p.set_poison(True)
+    poi = _run(p, q, k, v)
+    p.set_poison(False)
+    p.set_recv("memcpy")
+    mem = _run(p, q, k, v)
+    p.set_recv("kernel")
+    for o, l in (ser, poi, mem):
+        assert _bitwise_equal(o, base[0]) and _bitwise_equal(l, base[1])
+    p.set_merge(True)
+    sep = _run(p, q, k, v)
+    p.set_poison(True)
+    sep_poi = _run(p, q, k, v)
+    p.set_serialize(True)
+    sep_ser = _run(p, q, k, v)
+    assert _bitwise_equal(sep_poi[0], sep[0]) and _bitwise_equal(sep_ser[0], sep[0])
+    tol_o, tol_l = TOL[dtype]
+    d_o, d_l = _compare(sep[0], sep[1], q, k, v, True, dtype)
+    _say(f"  separate merge: max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= tol_o and d_l <= tol_l
+
+
+def test_caller_workspace_and_streams():
+    seq, cp, heads, dim = 1024, 2, 2, 128
+    q, k, v = make_qkv(seq, heads, dim, "bf16", 14)
+    p = Plan(seq, cp, heads, dim, True, "zigzag")
+    base = _run(p, q, k, v)
+    p2 = Plan(seq, cp, heads, dim, True, "zigzag")
+    ws = torch.empty(p2.workspace_bytes(), dtype=torch.uint8, device=_dev())
+    p2.set_workspace(ws)
+    p2.set_streams(torch.cuda.Stream(), torch.cuda.Stream())
+    got = _run(p2, q, k, v)
+    assert _bitwise_equal(got[0], base[0]) and _bitwise_equal(got[1], base[1])
+
+
+def test_step_timing_reports_run_steps():
+    seq, cp, heads, dim = 2048, 4, 2, 128
+    q, k, v = make_qkv(seq, heads, dim, "bf16", 15)
+    p = Plan(seq, cp, heads, dim, True, "zigzag")
+    p.set_step_timing(True)
+    _run(p, q, k, v, rank=2)
+    t = p.last_step_times()
+    for r in range(cp):
+        for s in range(cp):
+            assert (t[r][s] > 0) if r == 2 else (t[r][s] == -1)
+
+
+def test_lse_merge_kernel_matches_oracle():
+    dev = _dev()
+    rows, heads, dim = 300, 3, 128
+    g = torch.Generator().manual_seed(16)
+    o_a = torch.randn(rows, heads, dim, generator=g)
+    o_b = torch.randn(rows, heads, dim, generator=g)
+    l_a = 3 * torch.randn(heads, rows, generator=g)
+    l_b = 3 * torch.randn(heads, rows, generator=g)
+    l_a[0, :7] = -float("inf")
+    l_b[1, 5:9] = -float("inf")
+    l_a[2, 10] = l_b[2, 10] = -float("inf")
+    o_ref, l_ref = oracle.merge_partial(o_a.double().numpy(), l_a.double().numpy(), o_b.double().numpy(),
+                                        l_b.double().numpy())
+    oa, la = o_a.to(dev), l_a.to(dev)
+    lse_merge(oa, la, o_b.to(dev), l_b.to(dev))
+    torch.cuda.synchronize()
+    finite = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(la.cpu().numpy()), finite)
+    assert np.max(np.abs(la.cpu().double().numpy()[finite] - l_ref[finite])) <= 1e-5
+    assert np.max(np.abs(oa.cpu().double().numpy() - o_ref)[finite.T]) <= 1e-5
+
+
+# ------------------------------------------------- full workloads (sampled) --
+
+def _sample_rows(seq, cp, layout, rank, rng, per_chunk=6):
+    ranks = range(cp) if rank is None else [rank]
+    rows = []
+    c = oracle.chunk_size(seq, cp, layout)
+    for r in ranks:
+        pos = oracle.rank_positions(seq, cp, r, layout)
+        for i0 in range(0, pos.size, c):
+            chunk = pos[i0:i0 + c]
+            rows += [chunk[0], chunk[1], chunk[-1], chunk[c // 2]]
+            rows += list(rng.choice(chunk, size=per_chunk, replace=False))
+    return np.unique(np.asarray(rows))
+
+
+@pytest.mark.parametrize("name", [n for n in WORKLOADS if "fp32" not in n])
+def test_full_workload_sampled(name):
+    """The configuration the bench times, compared on sampled rows and heads."""
+    w = WORKLOADS[name]
+    _say(f"workload {name}")
+    q, k, v = workload_qkv(w)
+    p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout)
+    out, lse = _run(p, q, k, v, rank=w.rank)
+    rng = np.random.default_rng(w.seed)
+    rows = _sample_rows(w.seq_len, w.cp, w.layout, w.rank, rng)
+    heads = sorted({0, w.heads - 1, int(rng.integers(w.heads))})
+    d_o, d_l = _compare(out, lse, q, k, v, w.causal, torch.bfloat16, rows=rows, heads=heads)
+    _say(f"  rows={rows.size} heads={heads} max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= 2e-2 and d_l <= 1e-3
+    mine = np.concatenate([oracle.rank_positions(w.seq_len, w.cp, r, w.layout)
+                           for r in (range(w.cp) if w.rank is None else [w.rank])])
+    assert torch.isfinite(out[torch.from_numpy(mine)].float()).all()
+    assert torch.isfinite(lse[:, torch.from_numpy(mine)]).all()
+    if w.causal and (w.rank is None or w.rank == 0):
+        assert torch.equal(out[0], v[0])

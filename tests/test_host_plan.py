@@ -1,0 +1,197 @@
+"""Host-side tests of the C ABI (no GPU): exports, plan, descriptors, counts, errors.
+
+These call only host-only entry points of libcpattn.so (no device work) and
+compare the plan against the fp64 oracle's own chunk map and brute-force
+global-position masks.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from ring_context_parallelism_amd import _native as N
+from ring_context_parallelism_amd import Plan, CpAttnError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cp_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(N.LIB_PATH), reason="libcpattn.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cp_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 15
+    lib = N.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(N.SIGNATURES), "binding table and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", N.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (cp_attn_\w+)", out))
+    assert set(names) <= exported
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
+def test_chunk_map_and_sources_match_oracle(layout, cp):
+    seq = 2 * cp * 32
+    p = Plan(seq, cp, 2, 64, True, layout)
+    want = oracle.rank_chunks(cp, layout)
+    for r in range(cp):
+        assert p.rank_chunks(r) == tuple(want[r])
+        for s in range(cp):
+            assert p.step_source(r, s) == oracle.ring_source(r, s, cp)
+    assert p.local_rows() == oracle.rank_positions(seq, cp, 0, layout).size
+
+
+def test_page_example_map():
+    p = Plan(8192, 4, 32, 128)
+    assert [p.rank_chunks(r) for r in range(4)] == [(0, 7), (1, 6), (2, 5), (3, 4)]
+    assert p.local_rows() == 2048
+
+
+def _descriptor_mask(p, r, s, seq, cp, layout):
+    n = oracle.rank_positions(seq, cp, r, layout).size
+    mask = np.zeros((n, n), dtype=bool)
+    firsts = []
+    for g in p.step_segments(r, s):
+        for t in range(g["q_len"]):
+            row = g["q_start"] + t
+            mask[row, : g["kv_full"] + (t + 1 if g["diag"] else 0)] = True
+            assert g["q_global"] + t == oracle.rank_positions(seq, cp, r, layout)[row]
+        firsts.append(g)
+    return mask
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+def test_descriptors_equal_global_position_mask_exhaustive(causal, layout):
+    """Every (rank, step) for S <= 64, cp <= 8: descriptor mask == brute-force mask."""
+    checked = 0
+    for cp in range(1, 9):
+        parts = 2 * cp if layout == "zigzag" else cp
+        for seq in range(parts, 65, parts):
+            p = Plan(seq, cp, 1, 64, causal, layout)
+            for r in range(cp):
+                qpos = oracle.rank_positions(seq, cp, r, layout)
+                for s in range(cp):
+                    kpos = oracle.rank_positions(seq, cp, oracle.ring_source(r, s, cp), layout)
+                    want = oracle.valid_mask(qpos, kpos, causal)
+                    got = _descriptor_mask(p, r, s, seq, cp, layout)
+                    assert np.array_equal(got, want), (cp, seq, r, s)
+                    checked += 1
+            p.close()
+    assert checked > 500
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+def test_first_last_flags(layout):
+    """Each run of local rows is initialised once and finalised once, in ring order."""
+    cp, seq = 4, 128
+    p = Plan(seq, cp, 1, 64, True, layout)
+    for r in range(cp):
+        seen = {}
+        for s in range(cp):
+            for g in p.step_segments(r, s):
+                seen.setdefault(g["q_start"], []).append((s, g["first"], g["last"]))
+        covered = sum(p.step_segments(r, s)[0]["q_len"] for s in range(1) for _ in [0])
+        assert covered > 0
+        for steps in seen.values():
+            assert [f for _, f, _ in steps] == [1] + [0] * (len(steps) - 1)
+            assert [l for _, _, l in steps] == [0] * (len(steps) - 1) + [1]
+        rows = sorted(q for q in seen)
+        total = sum(next(g["q_len"] for s in range(cp) for g in p.step_segments(r, s) if g["q_start"] == q)
+                    for q in rows)
+        assert total == p.local_rows()  # every local row gets a result
+
+
+@pytest.mark.parametrize("seq,cp,layout,causal,bm,bn", [
+    (16384, 4, "zigzag", True, 128, 128), (16384, 4, "contiguous", True, 128, 128),
+    (16384, 4, "contiguous", True, 64, 64), (8192, 4, "zigzag", True, 128, 64),
+    (32768, 8, "zigzag", True, 128, 64), (4096, 16, "contiguous", False, 128, 64),
+    (800, 2, "zigzag", True, 128, 64), (960, 3, "contiguous", True, 64, 48),
+])
+def test_work_counts_match_oracle(seq, cp, layout, causal, bm, bn):
+    p = Plan(seq, cp, 1, 128, causal, layout)
+    for r in range(cp):
+        for s in range(cp):
+            tiles, pairs = p.valid_work(r, s, bm, bn)
+            assert pairs == oracle.step_valid_pairs(seq, cp, layout, causal, r, s)
+            assert tiles == oracle.step_valid_tiles(seq, cp, layout, causal, r, s, bm, bn)
+
+
+def _status(fn):
+    try:
+        fn()
+    except CpAttnError as e:
+        return e.status
+    return N.OK
+
+
+def test_plan_error_codes():
+    lib = N.lib()
+    h = ctypes.c_void_p()
+    cases = [
+        ((100, 3, 2, 128, 1, N.ZIGZAG), N.EINVAL),       # 100 % 6 != 0
+        ((10, 4, 2, 128, 1, N.CONTIGUOUS), N.EINVAL),    # 10 % 4 != 0
+        ((0, 1, 2, 128, 1, N.ZIGZAG), N.EINVAL),
+        ((64, 0, 2, 128, 1, N.ZIGZAG), N.EINVAL),
+        ((64, 2, 0, 128, 1, N.ZIGZAG), N.EINVAL),
+        ((64, 2, 2, 128, 2, N.ZIGZAG), N.EINVAL),        # causal flag
+        ((64, 2, 2, 128, 1, 7), N.EINVAL),               # layout
+        ((64, 2, 2, 96, 1, N.ZIGZAG), N.EUNSUPPORTED),   # head_dim
+        ((1024, 512, 2, 128, 1, N.ZIGZAG), N.EUNSUPPORTED),  # cp > 256
+    ]
+    for args, want in cases:
+        assert lib.cp_attn_plan(*args, ctypes.byref(h)) == want, args
+        assert not h.value
+        assert lib.cp_attn_last_error()
+    assert lib.cp_attn_plan(64, 2, 2, 128, 1, N.ZIGZAG, None) == N.EINVAL
+    for s in (N.OK, N.EINVAL, N.EUNSUPPORTED, N.ENOWORKSPACE, N.EHIP, 12345):
+        assert lib.cp_attn_status_string(s)
+
+
+def test_call_error_codes_enqueue_nothing():
+    lib = N.lib()
+    p = Plan(256, 2, 2, 64, True, "zigzag", dtype=__import__("torch").float32)
+    h = p._h
+    dummy = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert lib.cp_attn_rank_forward(h, dummy, dummy, dummy, dummy, dummy, 2, None) == N.EINVAL
+    assert lib.cp_attn_rank_forward(h, dummy, dummy, dummy, dummy, dummy, -1, None) == N.EINVAL
+    assert lib.cp_attn_rank_forward(h, None, dummy, dummy, dummy, dummy, 0, None) == N.EINVAL
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.cp_attn_full_forward(h, dummy, mis, dummy, dummy, dummy, None) == N.EINVAL
+    assert lib.cp_attn_rank_forward(None, dummy, dummy, dummy, dummy, dummy, 0, None) == N.EINVAL
+    assert lib.cp_attn_set_dtype(h, 5) == N.EINVAL
+    assert lib.cp_attn_set_option(h, 99, 1) == N.EINVAL
+    assert lib.cp_attn_set_option(h, N.OPT_MERGE, 3) == N.EINVAL
+    assert lib.cp_attn_set_workspace(h, ctypes.c_void_p(256), 16) == N.ENOWORKSPACE
+    assert lib.cp_attn_set_workspace(h, ctypes.c_void_p(100), 1 << 30) == N.EINVAL
+    assert lib.cp_attn_step_source(h, 0, 5, ctypes.byref(ctypes.c_int32())) == N.EINVAL
+    assert lib.cp_attn_valid_work(h, 0, 0, 0, 64, None, None) == N.EINVAL
+    assert lib.cp_attn_lse_merge(None, None, None, None, 4, 1, 128, None) == N.EINVAL
+    buf = (ctypes.c_float * 1)()
+    assert lib.cp_attn_last_step_times(h, buf, 1) == N.EINVAL
+    p.close()
+
+
+def test_workspace_size_formula():
+    import torch
+    p = Plan(32768, 8, 32, 128, True, "zigzag")
+    n, hd = 4096, 32 * 128
+    kv = n * hd * 2
+    o = n * hd * 4
+    lse = 32 * n * 4
+    assert p.workspace_bytes() == 4 * kv + o + lse + 2 * (o + lse)
+    q = Plan(256, 2, 2, 64, True, "zigzag", dtype=torch.float32)
+    assert q.workspace_bytes() == 4 * (128 * 128 * 4) + 3 * (128 * 128 * 4 + 2 * 128 * 4)
