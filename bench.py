@@ -220,8 +220,16 @@ def main():
         plan.set_merge(True)
         ms_sep = time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1)
         plan.set_merge(False)
+        plan.set_recv("memcpy")
+        ms_memcpy = time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1)
+        plan.set_recv("kernel")
+        plan.set_recv_blocks(0)
+        ms_fullgrid = time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1)
+        plan.set_recv_blocks(256)
         result["modes_ms"] = {"overlapped_fused_merge": round(ms, 5), "serialized_fused_merge": round(ms_serial, 5),
                               "overlapped_separate_merge": round(ms_sep, 5),
+                              "overlapped_memcpy_receive": round(ms_memcpy, 5),
+                              "overlapped_full_grid_receive": round(ms_fullgrid, 5),
                               "exposed_copy_ms": round(ms_serial - ms, 5)}
         run_call(plan, w, bufs, stream)
         torch.cuda.synchronize()

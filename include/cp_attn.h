@@ -74,6 +74,9 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
 #define CP_ATTN_OPT_RECV 3        /* 0: ring receive by the layout gather kernel (default); 1: hipMemcpyAsync */
 #define CP_ATTN_OPT_POISON 4      /* 1: fill each receive slot / partial buffer with NaN once consumed */
 #define CP_ATTN_OPT_STEP_TIMING 5 /* 1: time every ring step's attention kernel with HIP events */
+#define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel per tensor (default 256;
+                                     0: one workgroup per 4 KiB); a small grid shares the GPU with the
+                                     attention kernel it overlaps */
 
 /*
  * Create a plan (host only: no device memory, no HIP call).

@@ -71,6 +71,9 @@ class Plan:
     def set_recv(self, mode):
         self.set_option(N.OPT_RECV, {"kernel": 0, "memcpy": 1}[mode])
 
+    def set_recv_blocks(self, n):
+        self.set_option(N.OPT_RECV_BLOCKS, int(n))
+
     def set_poison(self, on):
         self.set_option(N.OPT_POISON, int(bool(on)))
 

@@ -184,7 +184,7 @@ int recv_kv(Plan& p, const void* k, const void* v, int src, int b, hipStream_t s
   la.n_loc = p.n_loc;
   la.row_vec = row_bytes / 16;
   la.dst_rank0 = src;
-  CPA_HIP(launch_layout(la, s));
+  CPA_HIP(launch_layout(la, p.opt_recv_blocks, s));
   return CP_ATTN_OK;
 }
 
@@ -469,6 +469,10 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
     case CP_ATTN_OPT_STEP_TIMING:
       p.opt_step_timing = value != 0;
       return CP_ATTN_OK;
+    case CP_ATTN_OPT_RECV_BLOCKS:
+      if (value < 0) return fail(CP_ATTN_EINVAL, "recv_blocks must be >= 0");
+      p.opt_recv_blocks = value;
+      return CP_ATTN_OK;
     default:
       return fail(CP_ATTN_EINVAL, "unknown option");
   }
@@ -609,7 +613,7 @@ static int layout_all(cp_attn_plan_t h, const void* src, void* dst, void* stream
   la.n_loc = p.n_loc;
   la.row_vec = int64_t(p.heads) * p.head_dim * p.elem_bytes() / 16;
   la.dst_rank0 = 0;
-  CPA_HIP(launch_layout(la, static_cast<hipStream_t>(stream)));
+  CPA_HIP(launch_layout(la, 0, static_cast<hipStream_t>(stream)));
   return CP_ATTN_OK;
 }
 

@@ -24,9 +24,11 @@
 //     V is transposed on its way into LDS and, within every 16-key group, the
 //     key order is permuted to match the order in which the score registers
 //     hold keys, so P never leaves registers.
-//   * K/V tiles of 64 keys are prefetched into registers one tile ahead and
-//     written to LDS (K row-major, V transposed), 16-byte rows padded so the
-//     matrix-operand reads are bank-conflict free.
+//   * K/V tiles of 64 keys are fetched with buffer loads (hardware range
+//     check: keys past the slot read as zero) two tiles ahead into registers,
+//     then written to a double-buffered LDS tile (K row-major, V transposed);
+//     16-byte padded rows keep the matrix-operand reads bank-conflict free and
+//     the transposed V writes are spread over distinct banks.
 //   * softmax in base 2: p = exp2(s * scale * log2 e - m); the reference max m
 //     is only raised when a tile's max exceeds it by more than 8 (p <= 2^8 in
 //     between), which skips most O rescales and is exact for any choice of m.
@@ -66,6 +68,12 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 // 16-key group, offsets 8a + 4b + e live at column 8b + 4a + e.
 __device__ __forceinline__ int vt_col(int k) { return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // raw buffer (stride 0): loads at byte offsets >= bytes return zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
 __device__ __forceinline__ unsigned pack_lo(unsigned a, unsigned b) { return (a & 0xffffu) | (b << 16); }
 __device__ __forceinline__ unsigned pack_hi(unsigned a, unsigned b) { return (a >> 16) | (b & 0xffff0000u); }
 
@@ -82,8 +90,8 @@ void attn_step_bf16(StepArgs a) {
   static_assert(KCH >= 1 && kBN * CPR % kThreads == 0, "K staging");
   static_assert(VITEMS <= kThreads, "V staging");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sk[kBN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kBN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * VS];
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int h = L / a.total_tiles;
@@ -131,35 +139,41 @@ void attn_step_bf16(StepArgs a) {
   for (int b = 0; b < NB; ++b) o[b] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  const __bf16* kbase = static_cast<const __bf16*>(a.k) + int64_t(h) * D;
-  const __bf16* vbase = static_cast<const __bf16*>(a.v) + int64_t(h) * D;
+  // K/V slot reads go through buffer resources: a key past the slot's last
+  // row is outside num_records and loads as zero (and is masked anyway).
+  const uint32_t row_bytes = uint32_t(a.heads) * D * 2;
+  const uint32_t slot_bytes = uint32_t(a.n_loc) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, slot_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, slot_bytes);
+  const uint32_t head_off = uint32_t(h) * D * 2;
 
   u32x4 kreg[KCH];
   u32x4 vreg[4];
-  const int vkg = tid / CPR, vdg = tid % CPR;  // V item: keys 4 vkg.., dims 8 vdg..
+  // V item of this thread: keys 4 vkg .. 4 vkg + 3, dims 8 vdg .. 8 vdg + 7.
+  // Sixteen consecutive lanes take sixteen key groups of one dim group, so
+  // their 8-byte transposed writes land on sixteen different bank pairs.
+  const int vkg = tid & 15, vdg = tid >> 4;
 
   auto load_tile = [&](int j0) {
+    const uint32_t base = uint32_t(j0) * row_bytes + head_off;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + kThreads * i;
       const int kr = c / CPR, cc = c % CPR;
-      const int key = j0 + kr;
-      kreg[i] = key < a.n_loc ? *reinterpret_cast<const u32x4*>(kbase + int64_t(key) * hd + cc * 8) : u32x4{};
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + uint32_t(kr) * row_bytes + cc * 16, 0, 0);
     }
     if (tid < VITEMS) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = j0 + 4 * vkg + e;
-        vreg[e] = key < a.n_loc ? *reinterpret_cast<const u32x4*>(vbase + int64_t(key) * hd + vdg * 8) : u32x4{};
-      }
+      for (int e = 0; e < 4; ++e)
+        vreg[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, base + uint32_t(4 * vkg + e) * row_bytes + vdg * 16, 0, 0);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + kThreads * i;
       const int kr = c / CPR, cc = c % CPR;
-      *reinterpret_cast<u32x4*>(&sk[kr * KS + cc * 8]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&sk[buf][kr * KS + cc * 8]) = kreg[i];
     }
     if (tid < VITEMS) {
       const int col = vt_col(4 * vkg);
@@ -170,81 +184,95 @@ void attn_step_bf16(StepArgs a) {
         lo[1] = pack_lo(vreg[2][w], vreg[3][w]);
         hi[0] = pack_hi(vreg[0][w], vreg[1][w]);
         hi[1] = pack_hi(vreg[2][w], vreg[3][w]);
-        *reinterpret_cast<u32x2*>(&sv[(8 * vdg + 2 * w) * VS + col]) = lo;
-        *reinterpret_cast<u32x2*>(&sv[(8 * vdg + 2 * w + 1) * VS + col]) = hi;
+        *reinterpret_cast<u32x2*>(&sv[buf][(8 * vdg + 2 * w) * VS + col]) = lo;
+        *reinterpret_cast<u32x2*>(&sv[buf][(8 * vdg + 2 * w + 1) * VS + col]) = hi;
       }
     }
   };
 
-  if (kv_end > 0) load_tile(0);
-  for (int j0 = 0; j0 < kv_end; j0 += kBN) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (j0 + kBN < kv_end) load_tile(j0 + kBN);
-    if (j0 >= w_max) continue;  // every row of this wave is past its prefix
-
-    // S^T tile: s[kb][i] = score(key j0 + 32 kb + 8 (i/4) + 4 hf + i%4, query row)
-    f32x16 s[2];
+  // Double-buffered LDS: tile it is read from buffer it&1 while tile it+1 is
+  // written to the other buffer and tile it+2 is in flight in registers; one
+  // barrier per tile.
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  if (ntiles > 1) load_tile(kBN);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = it * kBN;
+    const int buf = it & 1;
+    if (j0 < w_max) {
+      const uint16_t* skb = sk[buf];
+      const uint16_t* svb = sv[buf];
+      // S^T tile: s[kb][i] = score(key j0 + 32 kb + 8 (i/4) + 4 hf + i%4, query row)
+      f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sk[(32 * kb + qc) * KS + 16 * i + 8 * hf]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i], s[kb], 0, 0, 0);
+        for (int i = 0; i < NT; ++i) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&skb[(32 * kb + qc) * KS + 16 * i + 8 * hf]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i], s[kb], 0, 0, 0);
+        }
       }
-    }
-    if (j0 + kBN > w_min) {
+      if (j0 + kBN > w_min) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+            if (key >= prefix) s[kb][i] = -INFINITY;
+          }
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mt = mx * a.scale_log2;
+      if (__any(mt > m + kRescaleSlack)) {
+        const float mn = fmaxf(m, mt);
+        const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) o[b] *= alpha;
+        m = mn;
+      }
+      const float mref = (m == -INFINITY) ? 0.f : m;
+      bf16x8 pb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if (key >= prefix) s[kb][i] = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -mref));
+          l += p;
+          pb[kb][i >> 3][i & 7] = static_cast<__bf16>(p);
+        }
+      }
+      // O^T += V^T P^T over the 64 keys, 16 at a time
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const bf16x8 va =
+                *reinterpret_cast<const bf16x8*>(&svb[(32 * b + qc) * VS + 32 * kb + 16 * u + 8 * hf]);
+            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][u], o[b], 0, 0, 0);
+          }
         }
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    if (it + 1 < ntiles) {
+      store_tile(buf ^ 1);
+      if (it + 2 < ntiles) load_tile((it + 2) * kBN);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mt = mx * a.scale_log2;
-    if (__any(mt > m + kRescaleSlack)) {
-      const float mn = fmaxf(m, mt);
-      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-      l *= alpha;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) o[b] *= alpha;
-      m = mn;
-    }
-    const float mref = (m == -INFINITY) ? 0.f : m;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -mref));
-        l += p;
-        pb[kb][i >> 3][i & 7] = static_cast<__bf16>(p);
-      }
-    }
-    // O^T += V^T P^T over the 64 keys, 16 at a time
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 va =
-              *reinterpret_cast<const bf16x8*>(&sv[(32 * b + qc) * VS + 32 * kb + 16 * u + 8 * hf]);
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][u], o[b], 0, 0, 0);
-        }
-      }
-    }
+    __syncthreads();
   }
 
   l += __shfl_xor(l, 32);

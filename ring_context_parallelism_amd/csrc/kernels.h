@@ -70,7 +70,8 @@ struct LayoutArgs {
   int64_t row_vec;     // 16-byte vectors per row
   int64_t dst_rank0;   // rank whose local buffer starts at dst (gather) / src (scatter) row 0
 };
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+// max_blocks > 0 bounds the grid (per tensor); 0 sizes it to the data.
+hipError_t launch_layout(const LayoutArgs& a, int max_blocks, hipStream_t stream);
 
 // Fill with NaN (all-ones bytes) -- a kernel, not a memset, so it is safe in captured graphs.
 hipError_t launch_poison(void* ptr, int64_t bytes, hipStream_t stream);

@@ -30,19 +30,38 @@ __device__ __forceinline__ int64_t local_to_global(int64_t r, int64_t li, int64_
   return ch * chunk + (late ? li - chunk : li);
 }
 
+// Walks whole rows; each thread keeps up to four 16-byte loads in flight
+// before storing, so a small grid (co-resident with a running attention
+// kernel) still moves data at a useful rate.
 __global__ __launch_bounds__(kThreads) void layout_copy(LayoutArgs a) {
   const int tsel = blockIdx.y;
   const uint4* src = static_cast<const uint4*>(a.src[tsel]);
   uint4* dst = static_cast<uint4*>(a.dst[tsel]);
   const int64_t rows = int64_t(a.rank_count) * a.n_loc;
-  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-    const int64_t r = a.rank_begin + row / a.n_loc;
-    const int64_t li = row % a.n_loc;
-    const int64_t g = local_to_global(r, li, a.chunk, a.n_loc, a.cp, a.zigzag);
-    const int64_t lrow = (r - a.dst_rank0) * a.n_loc + li;
-    const int64_t from = (a.to_local ? g : lrow) * a.row_vec;
-    const int64_t to = (a.to_local ? lrow : g) * a.row_vec;
-    for (int64_t c = threadIdx.x; c < a.row_vec; c += kThreads) dst[to + c] = src[from + c];
+  const int64_t total = rows * a.row_vec;
+  constexpr int kIlp = 4;
+  const int64_t step = int64_t(gridDim.x) * kThreads;
+  for (int64_t base = int64_t(blockIdx.x) * kThreads + threadIdx.x; base < total; base += step * kIlp) {
+    uint4 v[kIlp];
+    int64_t to[kIlp];
+#pragma unroll
+    for (int u = 0; u < kIlp; ++u) {
+      const int64_t i = base + u * step;
+      to[u] = -1;
+      if (i < total) {
+        const int64_t row = i / a.row_vec, c = i - row * a.row_vec;
+        const int64_t r = a.rank_begin + row / a.n_loc;
+        const int64_t li = row % a.n_loc;
+        const int64_t g = local_to_global(r, li, a.chunk, a.n_loc, a.cp, a.zigzag);
+        const int64_t lrow = (r - a.dst_rank0) * a.n_loc + li;
+        const int64_t from = (a.to_local ? g : lrow) * a.row_vec + c;
+        to[u] = (a.to_local ? lrow : g) * a.row_vec + c;
+        v[u] = src[from];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kIlp; ++u)
+      if (to[u] >= 0) dst[to[u]] = v[u];
   }
 }
 
@@ -129,9 +148,10 @@ unsigned grid_for(int64_t work_items, int64_t per_block, unsigned cap) {
 
 }  // namespace
 
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-  const int64_t rows = int64_t(a.rank_count) * a.n_loc;
-  const dim3 grid(grid_for(rows, 1, 65536u), unsigned(a.ntensors));
+hipError_t launch_layout(const LayoutArgs& a, int max_blocks, hipStream_t stream) {
+  const int64_t total = int64_t(a.rank_count) * a.n_loc * a.row_vec;
+  const unsigned cap = max_blocks > 0 ? unsigned(max_blocks) : 65536u;
+  const dim3 grid(grid_for(total, int64_t(kThreads) * 4, cap), unsigned(a.ntensors));
   layout_copy<<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }

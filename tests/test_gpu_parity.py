@@ -169,7 +169,12 @@ def test_schedule_modes_agree(dtype):
     p.set_recv("memcpy")
     mem = _run(p, q, k, v)
     p.set_recv("kernel")
-    for o, l in (ser, poi, mem):
+    p.set_recv_blocks(0)
+    full_grid = _run(p, q, k, v)
+    p.set_recv_blocks(3)
+    small_grid = _run(p, q, k, v)
+    p.set_recv_blocks(256)
+    for o, l in (ser, poi, mem, full_grid, small_grid):
         assert _bitwise_equal(o, base[0]) and _bitwise_equal(l, base[1])
     p.set_merge(True)
     sep = _run(p, q, k, v)
