@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip imbalance / mode / parity side measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--recv", choices=["kernel", "memcpy"], default=None, help="ring receive path (default: library's)")
+    ap.add_argument("--recv-blocks", type=int, default=None, help="grid bound of the receive copy kernel")
+    ap.add_argument("--serialize", action="store_true", help="run the whole schedule on one stream")
     return ap.parse_args()
 
 
@@ -181,6 +184,12 @@ def main():
     lse = torch.empty(w.heads, w.seq_len, device="cuda", dtype=torch.float32)
     bufs = (q, k, v, out, lse)
     plan = R.Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout, dtype=w.torch_dtype)
+    if args.recv is not None:
+        plan.set_recv(args.recv)
+    if args.recv_blocks is not None:
+        plan.set_recv_blocks(args.recv_blocks)
+    if args.serialize:
+        plan.set_serialize(True)
 
     pairs = share_pairs(plan, w)
     flops = 4 * w.head_dim * w.heads * pairs
@@ -220,16 +229,16 @@ def main():
         plan.set_merge(True)
         ms_sep = time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1)
         plan.set_merge(False)
-        plan.set_recv("memcpy")
-        ms_memcpy = time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1)
         plan.set_recv("kernel")
-        plan.set_recv_blocks(0)
-        ms_fullgrid = time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1)
-        plan.set_recv_blocks(256)
+        ms_blocks = {}
+        for nb in (256, 512, 1024, 2048, 0):
+            plan.set_recv_blocks(nb)
+            ms_blocks[nb] = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
+        plan.set_recv_blocks(512 if args.recv_blocks is None else args.recv_blocks)
+        plan.set_recv(args.recv or "memcpy")
         result["modes_ms"] = {"overlapped_fused_merge": round(ms, 5), "serialized_fused_merge": round(ms_serial, 5),
                               "overlapped_separate_merge": round(ms_sep, 5),
-                              "overlapped_memcpy_receive": round(ms_memcpy, 5),
-                              "overlapped_full_grid_receive": round(ms_fullgrid, 5),
+                              "receive_kernel_grid_blocks_ms": ms_blocks,
                               "exposed_copy_ms": round(ms_serial - ms, 5)}
         run_call(plan, w, bufs, stream)
         torch.cuda.synchronize()

@@ -18,9 +18,10 @@
  *     (section 4);
  *   - the next step's K/V is received while the current step computes
  *     (section 5 "Overlap: More Than One Stream").
- * On one GPU the ring is a step schedule: the K/V of ring source
- * src(r, s) = (r - s) mod cp is copied device-to-device into one of two
- * receive slots on a side HIP stream while step s-1 computes.
+ * On one GPU the ring is a step schedule: step 0 reads the rank's own K/V in
+ * place, and for s >= 1 the K/V of ring source src(r, s) = (r - s) mod cp is
+ * copied device-to-device into one of two receive slots on a side HIP stream
+ * while step s-1 computes.
  *
  * Attention semantics (the plain definition the result must equal):
  *   causal: key j is valid for query i iff pos(j) <= pos(i) (global token
@@ -71,11 +72,12 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
 #define CP_ATTN_OPT_MERGE 1       /* 0: merge fused into the attention epilogue (default);
                                      1: separate LSE-merge kernel on the merge stream + finalize kernel */
 #define CP_ATTN_OPT_SERIALIZE 2   /* 0: copy/merge on side streams (default); 1: everything on the caller's stream */
-#define CP_ATTN_OPT_RECV 3        /* 0: ring receive by the layout gather kernel (default); 1: hipMemcpyAsync */
+#define CP_ATTN_OPT_RECV 3        /* 1: ring receive by hipMemcpyAsync (default);
+                                     0: by the library's non-temporal copy kernel */
 #define CP_ATTN_OPT_POISON 4      /* 1: fill each receive slot / partial buffer with NaN once consumed */
 #define CP_ATTN_OPT_STEP_TIMING 5 /* 1: time every ring step's attention kernel with HIP events */
-#define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel per tensor (default 256;
-                                     0: one workgroup per 4 KiB); a small grid shares the GPU with the
+#define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel (default 64; 0: one
+                                     workgroup per 16 KiB); a small grid shares the GPU with the
                                      attention kernel it overlaps */
 
 /*
@@ -91,7 +93,8 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
  * sequence are rejected ("Context Parallelism for Long-Context Training",
  * section "Sweep the smallest useful degree").
  * Returns EINVAL for non-positive sizes, a bad flag or layout, or a
- * non-dividing length; EUNSUPPORTED for another head_dim or cp_size > 256.
+ * non-dividing length; EUNSUPPORTED for another head_dim, cp_size > 256, or
+ * seq_len * heads * head_dim * 4 >= 2^32 (device offsets are 32-bit).
  * On success *out owns the plan; free it with cp_attn_plan_destroy.
  */
 int cp_attn_plan(int64_t seq_len, int cp_size, int heads, int head_dim, int causal, int layout,

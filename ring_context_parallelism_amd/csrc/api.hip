@@ -149,46 +149,46 @@ int ensure_device(Plan& p) {
   return CP_ATTN_OK;
 }
 
-// Copy the K and V rows of ring source `src` (its local order) into slot b.
+// Copy the K and V rows of ring source `src` (its local order) into slot b:
+// its one or two chunks are contiguous token ranges of the natural-order
+// tensors, so the receive is four (zigzag) or two (contiguous) linear copies.
 int recv_kv(Plan& p, const void* k, const void* v, int src, int b, hipStream_t s) {
   DeviceState& d = *p.dev;
   const WsLayout w = ws_layout(p);
   char* ws = static_cast<char*>(d.ws);
-  void* dk = ws + w.slot_k[b];
-  void* dv = ws + w.slot_v[b];
+  char* dk = ws + w.slot_k[b];
+  char* dv = ws + w.slot_v[b];
   const int64_t row_bytes = int64_t(p.heads) * p.head_dim * p.elem_bytes();
+  const int nch = p.layout == 1 ? 2 : 1;
+  const int64_t ch_bytes = p.chunk * row_bytes;
   if (p.opt_recv == 1) {
-    const int nch = p.layout == 1 ? 2 : 1;
-    const int64_t ch_bytes = p.chunk * row_bytes;
     for (int c = 0; c < nch; ++c) {
       const int64_t g = p.chunk_of(src, c) * ch_bytes;
-      CPA_HIP(hipMemcpyAsync(static_cast<char*>(dk) + c * ch_bytes, static_cast<const char*>(k) + g, size_t(ch_bytes),
+      CPA_HIP(hipMemcpyAsync(dk + c * ch_bytes, static_cast<const char*>(k) + g, size_t(ch_bytes),
                              hipMemcpyDeviceToDevice, s));
-      CPA_HIP(hipMemcpyAsync(static_cast<char*>(dv) + c * ch_bytes, static_cast<const char*>(v) + g, size_t(ch_bytes),
+      CPA_HIP(hipMemcpyAsync(dv + c * ch_bytes, static_cast<const char*>(v) + g, size_t(ch_bytes),
                              hipMemcpyDeviceToDevice, s));
     }
     return CP_ATTN_OK;
   }
-  LayoutArgs la{};
-  la.src[0] = k;
-  la.src[1] = v;
-  la.dst[0] = dk;
-  la.dst[1] = dv;
-  la.ntensors = 2;
-  la.rank_begin = src;
-  la.rank_count = 1;
-  la.cp = p.cp;
-  la.zigzag = p.layout == 1;
-  la.to_local = 1;
-  la.chunk = p.chunk;
-  la.n_loc = p.n_loc;
-  la.row_vec = row_bytes / 16;
-  la.dst_rank0 = src;
-  CPA_HIP(launch_layout(la, p.opt_recv_blocks, s));
+  RecvArgs ra{};
+  for (int c = 0; c < nch; ++c) {
+    const int64_t g = p.chunk_of(src, c) * ch_bytes;
+    ra.src[ra.n] = static_cast<const char*>(k) + g;
+    ra.dst[ra.n] = dk + c * ch_bytes;
+    ra.vec[ra.n++] = ch_bytes / 16;
+    ra.src[ra.n] = static_cast<const char*>(v) + g;
+    ra.dst[ra.n] = dv + c * ch_bytes;
+    ra.vec[ra.n++] = ch_bytes / 16;
+  }
+  CPA_HIP(launch_recv(ra, p.opt_recv_blocks, s));
   return CP_ATTN_OK;
 }
 
-int launch_step(Plan& p, const void* q, void* out, float* lse, int r, int s, int b, hipStream_t st) {
+// Step 0 reads the rank's own K/V in place (the rank holds them; nothing is
+// received); later steps read receive slot b.
+int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out, float* lse, int r, int s, int b,
+                hipStream_t st) {
   DeviceState& d = *p.dev;
   const WsLayout w = ws_layout(p);
   char* ws = static_cast<char*>(d.ws);
@@ -198,8 +198,22 @@ int launch_step(Plan& p, const void* q, void* out, float* lse, int r, int s, int
   const int bm = bf16 ? attn_bf16_block_m() : attn_f32_block_m();
   StepArgs a{};
   a.q = q;
-  a.k = ws + w.slot_k[b];
-  a.v = ws + w.slot_v[b];
+  const int32_t split = int32_t(p.layout == 1 ? p.chunk : p.n_loc);
+  if (s == 0) {
+    a.k = k;
+    a.v = v;
+    a.kv_bytes = p.seq_len * p.heads * p.head_dim * p.elem_bytes();
+    a.kv_lo = int32_t(p.chunk_of(r, 0) * p.chunk);
+    a.kv_hi = p.layout == 1 ? int32_t(p.chunk_of(r, 1) * p.chunk) : 0;
+    a.kv_split = split;
+  } else {
+    a.k = ws + w.slot_k[b];
+    a.v = ws + w.slot_v[b];
+    a.kv_bytes = w.kv_bytes;
+    a.kv_lo = 0;
+    a.kv_hi = split;
+    a.kv_split = split;
+  }
   a.acc_o = reinterpret_cast<float*>(ws + w.acc_o);
   a.acc_lse = reinterpret_cast<float*>(ws + w.acc_lse);
   a.part_o = reinterpret_cast<float*>(ws + w.part_o[b]);
@@ -308,9 +322,6 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
     CPA_HIP(hipStreamWaitEvent(cs, d.start, 0));
     if (separate) CPA_HIP(hipStreamWaitEvent(ms, d.start, 0));
   }
-  CPA_TRY(recv_kv(p, k, v, p.step(r, 0).src, 0, cs));
-  if (!serial) CPA_HIP(hipEventRecord(d.recv_done[0], cs));
-
   for (int s = 0; s < P; ++s) {
     const int b = s & 1;
     if (s + 1 < P) {
@@ -319,16 +330,16 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
       CPA_TRY(recv_kv(p, k, v, p.step(r, s + 1).src, nb, cs));
       if (!serial) CPA_HIP(hipEventRecord(d.recv_done[nb], cs));
     }
-    if (!serial) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
+    if (!serial && s >= 1) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
     if (separate && !serial && s >= 2) CPA_HIP(hipStreamWaitEvent(st, d.merge_done[b], 0));
     const size_t ti = size_t(r) * P + s;
     if (p.opt_step_timing) CPA_HIP(hipEventRecord(d.t0[ti], st));
-    CPA_TRY(launch_step(p, q, out, lse, r, s, b, st));
+    CPA_TRY(launch_step(p, q, k, v, out, lse, r, s, b, st));
     if (p.opt_step_timing) {
       CPA_HIP(hipEventRecord(d.t1[ti], st));
       d.timed[ti] = 1;
     }
-    if (p.opt_poison) {
+    if (p.opt_poison && s >= 1) {
       CPA_HIP(launch_poison(ws + w.slot_k[b], w.kv_bytes, st));
       CPA_HIP(launch_poison(ws + w.slot_v[b], w.kv_bytes, st));
     }

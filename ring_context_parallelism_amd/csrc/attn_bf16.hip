@@ -64,6 +64,23 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return x * q + min(x, r) + slot;
 }
 
+// (head, tile) of workgroup b.  When the heads split evenly over the 8 XCDs,
+// each XCD owns heads/8 whole heads and walks their tiles tile-major (all its
+// heads' first tile, then their second, ...), so the longest tiles of every
+// head start first; otherwise heads are walked one after the other.
+__device__ __forceinline__ void tile_of(int b, int n, int heads, int tiles, int& h, int& t) {
+  if ((heads & 7) == 0) {
+    const int hg = heads >> 3;
+    const int x = b & 7, slot = b >> 3;
+    h = x * hg + slot % hg;
+    t = slot / hg;
+  } else {
+    const int L = xcd_remap(b, n);
+    h = L / tiles;
+    t = L % tiles;
+  }
+}
+
 // Column of key offset k (multiple of 4) inside the V^T tile: within each
 // 16-key group, offsets 8a + 4b + e live at column 8b + 4a + e.
 __device__ __forceinline__ int vt_col(int k) { return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1); }
@@ -93,9 +110,8 @@ void attn_step_bf16(StepArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kBN * KS];
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * VS];
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = L / a.total_tiles;
-  int t = L % a.total_tiles;
+  int h, t;
+  tile_of(blockIdx.x, gridDim.x, a.heads, a.total_tiles, h, t);
   const int si = t < a.seg[0].tiles ? 0 : 1;
   if (si) t -= a.seg[0].tiles;
   const SegArgs& g = a.seg[si];
@@ -139,12 +155,10 @@ void attn_step_bf16(StepArgs a) {
   for (int b = 0; b < NB; ++b) o[b] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  // K/V slot reads go through buffer resources: a key past the slot's last
-  // row is outside num_records and loads as zero (and is masked anyway).
+  // K/V reads go through buffer resources with 32-bit offsets.
   const uint32_t row_bytes = uint32_t(a.heads) * D * 2;
-  const uint32_t slot_bytes = uint32_t(a.n_loc) * row_bytes;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, slot_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, slot_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, uint32_t(a.kv_bytes));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, uint32_t(a.kv_bytes));
   const uint32_t head_off = uint32_t(h) * D * 2;
 
   u32x4 kreg[KCH];
@@ -154,18 +168,19 @@ void attn_step_bf16(StepArgs a) {
   // their 8-byte transposed writes land on sixteen different bank pairs.
   const int vkg = tid & 15, vdg = tid >> 4;
 
+  // keys past the slot are clamped to its last row (and masked)
+  auto src_off = [&](int kk) { return uint32_t(kv_row(a, min(kk, a.n_loc - 1))) * row_bytes + head_off; };
   auto load_tile = [&](int j0) {
-    const uint32_t base = uint32_t(j0) * row_bytes + head_off;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + kThreads * i;
       const int kr = c / CPR, cc = c % CPR;
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + uint32_t(kr) * row_bytes + cc * 16, 0, 0);
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, src_off(j0 + kr) + cc * 16, 0, 0);
     }
     if (tid < VITEMS) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        vreg[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, base + uint32_t(4 * vkg + e) * row_bytes + vdg * 16, 0, 0);
+        vreg[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, src_off(j0 + 4 * vkg + e) + vdg * 16, 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
@@ -293,6 +308,246 @@ void attn_step_bf16(StepArgs a) {
   if (hf == 0) row_epi_store_lse(a, g, e, h, lrow, grow, lse_s);
 }
 
+// ---------------------------------------------------------------------------
+// head_dim 128: pipelined kernel with direct-to-LDS K/V.
+//
+//   * K/V tiles of 64 keys move global -> LDS with buffer_load ... lds (no
+//     register staging); each wave instruction fills four 256-byte rows, and
+//     the 16-byte chunks of a row are XOR-swizzled (swz) so that both the
+//     K operand reads (32 rows, one chunk) and the transposed V reads below
+//     hit distinct LDS banks.
+//   * V stays row-major in LDS and is read with ds_read_b64_tr_b16: within a
+//     16-lane group, lane i receives element i%4 of the 8 bytes addressed by
+//     lane 4j + i/4 as its j-th value, so the 16 lanes that point at 4 key
+//     rows x 4 column pieces receive 4 keys of one head-dim column each --
+//     exactly the A operand of O^T = V^T P^T.
+//   * cross-tile pipelining: K runs one tile ahead of V in LDS, so while the
+//     softmax of tile j runs on the vector ALUs, the scores of tile j+1 are
+//     already issued to the matrix cores; one barrier per tile.
+// ---------------------------------------------------------------------------
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+constexpr int kTileBytes = kBN * 256;  // one 64-key K or V tile of 128 bf16 columns
+
+// Permutation of the 16 chunks of a 256-byte row (linear over GF(2) in the
+// row index): bit0 <- r2, bit1 <- r1^r3, bit2 <- r0, bit3 <- r1.
+__device__ __forceinline__ int swz(int r) {
+  return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1) | ((r & 1) << 2) | (((r >> 1) & 1) << 3);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void attn_step_bf16_d128(StepArgs a) {
+  constexpr int D = 128, NT = 8, NB = 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * kTileBytes];  // K0 K1 V0 V1
+  lds_u8* const lds = (lds_u8*)smem;  // address-space cast of the shared array
+  lds_u8* const kbuf0 = lds;
+  lds_u8* const kbuf1 = lds + kTileBytes;
+  lds_u8* const vbuf0 = lds + 2 * kTileBytes;
+  lds_u8* const vbuf1 = lds + 3 * kTileBytes;
+
+  int h, t;
+  tile_of(blockIdx.x, gridDim.x, a.heads, a.total_tiles, h, t);
+  const int si = t < a.seg[0].tiles ? 0 : 1;
+  if (si) t -= a.seg[0].tiles;
+  const SegArgs& g = a.seg[si];
+  if (g.diag) t = g.tiles - 1 - t;  // longest rows first
+  const int row0 = t * kBM;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep wave-level values scalar
+  const int qc = lane & 31, hf = lane >> 5;
+  const int row = row0 + wv * 32 + qc;
+  const bool ok = row < g.q_len;
+  const int tile_last = min(row0 + kBM, g.q_len);
+  const int kv_end = g.kv_full + (g.diag ? tile_last : 0);
+  const int w_first = row0 + wv * 32;
+  const int w_last = min(w_first + 32, g.q_len);
+  const int w_max = w_last > w_first ? g.kv_full + (g.diag ? w_last : 0) : 0;
+  const int w_min = g.kv_full + (g.diag ? w_first + 1 : 0);
+  const int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : w_max;
+  const int64_t hd = int64_t(a.heads) * D;
+  const int64_t grow = g.q_global + row;
+
+  bf16x8 qf[NT];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + grow * hd + int64_t(h) * D + 8 * hf;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) qf[i] = ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * i) : bf16x8{};
+  }
+  f32x16 o[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) o[b] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  // load mapping: wave wv, instruction n fills tile rows 16 wv + 4 n + lane/16;
+  // the lane's 16 bytes land in physical chunk lane%16 of that row.
+  // swz is linear over GF(2) and 4 n, lane/16 have disjoint bits, so the
+  // chunk of instruction n is (lane%16 ^ swz(lane/16)) ^ swz(4 n).
+  const uint32_t row_bytes = uint32_t(a.heads) * 256;
+  const int lrow0 = 16 * wv + (lane >> 4);
+  const uint32_t hbase = uint32_t(h) * 256 + (((lane & 15) ^ swz(lane >> 4)) << 4);
+  uint32_t vrow[4];  // per-lane byte offset of its chunk within a tile whose rows are contiguous
+#pragma unroll
+  for (int n = 0; n < 4; ++n) vrow[n] = uint32_t(lrow0 + 4 * n) * row_bytes + (hbase ^ (uint32_t(swz(4 * n)) << 4));
+  auto issue = [&](const void* src, int j0, lds_u8* dst) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, uint32_t(a.kv_bytes));
+    // Fast path: the 64 source rows are consecutive and inside the buffer, so
+    // the tile base is one scalar offset.  Otherwise (a tile that crosses the
+    // split between the two chunks, or the ragged last tile) each lane maps
+    // its own row and clamps keys past the buffer to its last row (masked).
+    const bool whole = j0 + kBN <= a.n_loc && (j0 + kBN <= a.kv_split || j0 >= a.kv_split);
+    if (whole) {
+      const uint32_t soff = uint32_t(kv_row(a, j0)) * row_bytes;
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (16 * wv + 4 * n) * 256),
+                                                 16, vrow[n], soff, 0, 0);
+    } else {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int kk = min(j0 + lrow0 + 4 * n, a.n_loc - 1);
+        const uint32_t voff = uint32_t(kv_row(a, kk)) * row_bytes + (hbase ^ (uint32_t(swz(4 * n)) << 4));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (16 * wv + 4 * n) * 256),
+                                                 16, voff, 0, 0, 0);
+      }
+    }
+  };
+  // K operand: row 32 kb + qc, logical chunk 2 i + hf.  The chunk bits of
+  // 2 i and of hf are disjoint, so the swizzled address is kbase ^ (32 i).
+  const uint32_t kbase = qc * 256 + ((hf ^ swz(qc & 15)) << 4);
+  // transposed V reads: lane (group g, index i16) points at row 8 r + 4 hf + i16/4 of a 16-key
+  // group, bytes 64 b + 32 (g & 1) + 8 (i16 & 3) .. +7; the 64 b part only flips chunk bits 2-3,
+  // so the address is vbase[r] ^ (64 b).
+  const int i16 = lane & 15, g1 = (lane >> 4) & 1;
+  uint32_t vbase[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int vr = 8 * r + 4 * hf + (i16 >> 2);
+    const int c0 = 2 * g1 + ((i16 & 3) >> 1);
+    vbase[r] = vr * 256 + ((c0 ^ swz(vr & 15)) << 4) + 8 * (i16 & 1);
+  }
+
+  auto scores = [&](const lds_u8* kt, f32x16 (&s)[2]) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ka = *reinterpret_cast<const lds_bf16x8*>(kt + kb * 32 * 256 + (kbase ^ (32u * i)));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i], s[kb], 0, 0, 0);
+      }
+  };
+  auto softmax = [&](f32x16 (&s)[2], int j0, bf16x8 (&pb)[2][2]) {
+    if (j0 + kBN > w_min) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+          if (key >= prefix) s[kb][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = mx * a.scale_log2;
+    if (__any(mt > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b] *= alpha;
+      m = mn;
+    }
+    const float mref = (m == -INFINITY) ? 0.f : m;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -mref));
+        l += p;
+        pb[kb][i >> 3][i & 7] = static_cast<__bf16>(p);
+      }
+  };
+  auto pv = [&](const lds_u8* vt, const bf16x8 (&pb)[2][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int roff = (32 * kb + 16 * u) * 256;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + roff + (vbase[0] ^ (64u * b))));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + roff + (vbase[1] ^ (64u * b))));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][u], o[b], 0, 0, 0);
+        }
+  };
+
+  // K(j) lives in kbuf[j & 1], V(j) in vbuf[j & 1]; K runs one tile ahead.
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+  if (ntiles > 0) {
+    issue(a.k, 0, kbuf0);
+    issue(a.v, 0, vbuf0);
+  }
+  if (ntiles > 1) issue(a.k, kBN, kbuf1);
+  wait_vmem();
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  if (ntiles > 0 && w_max > 0) scores(kbuf0, sa);
+  __syncthreads();
+
+#define CPATTN_STEP(J, PAR, SC, SN)                                                       \
+  do {                                                                                    \
+    const int j0_ = (J) * kBN;                                                            \
+    if ((J) + 2 < ntiles) issue(a.k, j0_ + 2 * kBN, (PAR) ? kbuf1 : kbuf0);              \
+    if ((J) + 1 < ntiles) issue(a.v, j0_ + kBN, (PAR) ? vbuf0 : vbuf1);                   \
+    const bool act_ = j0_ < w_max;                                                        \
+    bf16x8 pb_[2][2];                                                                     \
+    if (act_) softmax(SC, j0_, pb_);                                                      \
+    if ((J) + 1 < ntiles && j0_ + kBN < w_max) scores((PAR) ? kbuf0 : kbuf1, SN);         \
+    if (act_) pv((PAR) ? vbuf1 : vbuf0, pb_);                                             \
+    wait_vmem();                                                                          \
+    __syncthreads();                                                                      \
+  } while (0)
+
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    CPATTN_STEP(j, 0, sa, sb);
+    CPATTN_STEP(j + 1, 1, sb, sa);
+  }
+  if (j < ntiles) CPATTN_STEP(j, 0, sa, sb);
+#undef CPATTN_STEP
+
+  l += __shfl_xor(l, 32);
+  if (!ok) return;
+  const int lrow_out = g.q_start + row;
+  const float lse_s = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
+  const float inv = 1.f / l;
+  const RowEpi e = row_epi_begin(a, g, h, lrow_out, lse_s);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 v4 = make_float4(o[b][4 * q4] * inv, o[b][4 * q4 + 1] * inv, o[b][4 * q4 + 2] * inv,
+                                    o[b][4 * q4 + 3] * inv);
+      row_epi_store4(a, g, e, h, lrow_out, grow, 32 * b + 8 * q4 + 4 * hf, D, v4);
+    }
+  }
+  if (hf == 0) row_epi_store_lse(a, g, e, h, lrow_out, grow, lse_s);
+}
+
 }  // namespace
 
 int attn_bf16_block_m() { return kBM; }
@@ -300,7 +555,7 @@ int attn_bf16_block_m() { return kBM; }
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid(unsigned(a.total_tiles) * unsigned(a.heads));
   if (head_dim == 128) {
-    attn_step_bf16<128><<<grid, kThreads, 0, stream>>>(a);
+    attn_step_bf16_d128<<<grid, kThreads, 0, stream>>>(a);
   } else {
     attn_step_bf16<64><<<grid, kThreads, 0, stream>>>(a);
   }

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
       const int key = j0 + kr;
       float kx = 0.f, vx = 0.f;
       if (key < a.n_loc) {
-        const int64_t off = (int64_t(key) * a.heads + h) * D + dc;
+        const int64_t off = (int64_t(kv_row(a, key)) * a.heads + h) * D + dc;
         kx = kp[off];
         vx = vp[off];
       }

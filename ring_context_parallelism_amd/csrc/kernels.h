@@ -28,8 +28,16 @@ struct SegArgs {
 
 struct StepArgs {
   const void* q;     // [S][H][D] natural order, plan dtype
-  const void* k;     // receive slot [n_loc][H][D]
+  // K/V source: rows of [H][D] elements.  Local key kk (0 <= kk < n_loc) is
+  // row kv_lo + kk if kk < kv_split, else row kv_hi + (kk - kv_split).  A
+  // receive slot is (0, split, split); the rank's own chunks are read in
+  // place from the natural-order tensors.
+  const void* k;
   const void* v;
+  int64_t kv_bytes;  // bytes addressable from k and from v
+  int32_t kv_lo;
+  int32_t kv_hi;
+  int32_t kv_split;
   float* acc_o;      // [n_loc][H][D] running O (normalised)
   float* acc_lse;    // [H][n_loc] running LSE (natural log)
   float* part_o;     // [n_loc][H][D] partial O (separate merge mode)
@@ -72,6 +80,17 @@ struct LayoutArgs {
 };
 // max_blocks > 0 bounds the grid (per tensor); 0 sizes it to the data.
 hipError_t launch_layout(const LayoutArgs& a, int max_blocks, hipStream_t stream);
+
+// Ring receive: up to four contiguous byte ranges (16-byte multiples),
+// copied with non-temporal accesses by a small grid that shares the GPU with
+// the attention kernel it overlaps.
+struct RecvArgs {
+  const void* src[4];
+  void* dst[4];
+  int64_t vec[4];  // 16-byte vectors per range
+  int32_t n;
+};
+hipError_t launch_recv(const RecvArgs& a, int blocks, hipStream_t stream);
 
 // Fill with NaN (all-ones bytes) -- a kernel, not a memset, so it is safe in captured graphs.
 hipError_t launch_poison(void* ptr, int64_t bytes, hipStream_t stream);

@@ -30,38 +30,56 @@ __device__ __forceinline__ int64_t local_to_global(int64_t r, int64_t li, int64_
   return ch * chunk + (late ? li - chunk : li);
 }
 
-// Walks whole rows; each thread keeps up to four 16-byte loads in flight
-// before storing, so a small grid (co-resident with a running attention
-// kernel) still moves data at a useful rate.
+// One workgroup per row (grid-stride over rows): the row -> token arithmetic
+// is done once per row, then the row's 16-byte vectors are copied.
 __global__ __launch_bounds__(kThreads) void layout_copy(LayoutArgs a) {
   const int tsel = blockIdx.y;
   const uint4* src = static_cast<const uint4*>(a.src[tsel]);
   uint4* dst = static_cast<uint4*>(a.dst[tsel]);
   const int64_t rows = int64_t(a.rank_count) * a.n_loc;
-  const int64_t total = rows * a.row_vec;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const int64_t r = a.rank_begin + row / a.n_loc;
+    const int64_t li = row % a.n_loc;
+    const int64_t g = local_to_global(r, li, a.chunk, a.n_loc, a.cp, a.zigzag);
+    const int64_t lrow = (r - a.dst_rank0) * a.n_loc + li;
+    const int64_t from = (a.to_local ? g : lrow) * a.row_vec;
+    const int64_t to = (a.to_local ? lrow : g) * a.row_vec;
+    for (int64_t c = threadIdx.x; c < a.row_vec; c += kThreads) dst[to + c] = src[from + c];
+  }
+}
+
+// Ring receive: the ranges are walked as one concatenated index space; every
+// thread keeps four non-temporal 16-byte loads in flight before storing, so a
+// grid of a few dozen workgroups reaches a useful rate without crowding the
+// attention kernel or evicting its cached K/V.
+__global__ __launch_bounds__(kThreads) void recv_copy(RecvArgs a) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   constexpr int kIlp = 4;
-  const int64_t step = int64_t(gridDim.x) * kThreads;
-  for (int64_t base = int64_t(blockIdx.x) * kThreads + threadIdx.x; base < total; base += step * kIlp) {
-    uint4 v[kIlp];
-    int64_t to[kIlp];
+  int64_t start[5];
+  start[0] = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) start[i + 1] = start[i] + (i < a.n ? a.vec[i] : 0);
+  const int64_t total = start[4];
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t base = int64_t(blockIdx.x) * kThreads + threadIdx.x; base < total; base += stride * kIlp) {
+    u32x4 v[kIlp];
+    u32x4* to[kIlp];
 #pragma unroll
     for (int u = 0; u < kIlp; ++u) {
-      const int64_t i = base + u * step;
-      to[u] = -1;
+      const int64_t i = base + u * stride;
+      to[u] = nullptr;
       if (i < total) {
-        const int64_t row = i / a.row_vec, c = i - row * a.row_vec;
-        const int64_t r = a.rank_begin + row / a.n_loc;
-        const int64_t li = row % a.n_loc;
-        const int64_t g = local_to_global(r, li, a.chunk, a.n_loc, a.cp, a.zigzag);
-        const int64_t lrow = (r - a.dst_rank0) * a.n_loc + li;
-        const int64_t from = (a.to_local ? g : lrow) * a.row_vec + c;
-        to[u] = (a.to_local ? lrow : g) * a.row_vec + c;
-        v[u] = src[from];
+        int r = 0;
+#pragma unroll
+        for (int q = 1; q < 4; ++q) r += (i >= start[q]) ? 1 : 0;
+        const int64_t off = i - start[r];
+        v[u] = __builtin_nontemporal_load(static_cast<const u32x4*>(a.src[r]) + off);
+        to[u] = static_cast<u32x4*>(a.dst[r]) + off;
       }
     }
 #pragma unroll
     for (int u = 0; u < kIlp; ++u)
-      if (to[u] >= 0) dst[to[u]] = v[u];
+      if (to[u]) __builtin_nontemporal_store(v[u], to[u]);
   }
 }
 
@@ -149,10 +167,19 @@ unsigned grid_for(int64_t work_items, int64_t per_block, unsigned cap) {
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs& a, int max_blocks, hipStream_t stream) {
-  const int64_t total = int64_t(a.rank_count) * a.n_loc * a.row_vec;
+  const int64_t rows = int64_t(a.rank_count) * a.n_loc;
   const unsigned cap = max_blocks > 0 ? unsigned(max_blocks) : 65536u;
-  const dim3 grid(grid_for(total, int64_t(kThreads) * 4, cap), unsigned(a.ntensors));
+  const dim3 grid(grid_for(rows, 1, cap), unsigned(a.ntensors));
   layout_copy<<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_recv(const RecvArgs& a, int blocks, hipStream_t stream) {
+  int64_t total = 0;
+  for (int i = 0; i < a.n; ++i) total += a.vec[i];
+  if (total == 0) return hipSuccess;
+  const unsigned cap = blocks > 0 ? unsigned(blocks) : 65536u;
+  recv_copy<<<grid_for(total, int64_t(kThreads) * 4, cap), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -137,13 +137,9 @@ int make_plan(int64_t seq_len, int cp, int heads, int head_dim, int causal, int 
     *err = "head_dim must be 64 or 128";
     return kUnsupported;
   }
-  if (seq_len * int64_t(heads) * head_dim > (int64_t(1) << 36)) {
-    *err = "seq_len * heads * head_dim too large";
-    return kUnsupported;
-  }
-  // one rank's K/V slot is addressed with 32-bit byte offsets on the device
-  if ((seq_len / cp + 128) * int64_t(heads) * head_dim * 4 >= (int64_t(1) << 32)) {
-    *err = "seq_len / cp_size * heads * head_dim too large for one rank's buffers";
+  // K/V tensors are addressed with 32-bit byte offsets on the device
+  if (seq_len * int64_t(heads) * head_dim * 4 >= (int64_t(1) << 32)) {
+    *err = "seq_len * heads * head_dim * 4 must stay below 2^32 bytes";
     return kUnsupported;
   }
   Plan* p = new Plan;
