@@ -5,9 +5,11 @@
 One timed step = one call of the library's hot path over the workload's share:
 for the default workload, rank 0's share of a causal 32768-token sequence at
 cp 8 (zigzag chunks {0, 15}, 32 heads x 128, bf16): 8 ring steps, each with the
-next K/V received on a side stream, blockwise MFMA attention with the merge in
-the epilogue, and the final scatter of O/LSE to token positions.  Inputs are
-resident in HBM before timing starts.
+next step's K/V received into the other slot while the step computes,
+blockwise MFMA attention with the LSE merge in the epilogue, and the final
+scatter of O/LSE to token positions.  Inputs are resident in HBM before timing
+starts.  Other schedule modes (side-stream receive, separate merge kernel,
+serialized) are timed alongside and reported under "modes_ms".
 
 Prints ONE JSON line.  `value` is effective TFLOP/s over mask-valid FLOPs
 (4 * head_dim per valid (query, key) pair per head).
@@ -38,7 +40,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip imbalance / mode / parity side measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--recv", choices=["kernel", "memcpy"], default=None, help="ring receive path (default: library's)")
+    ap.add_argument("--recv", choices=["kernel", "memcpy", "fused"], default=None, help="ring receive path (default: library's)")
     ap.add_argument("--recv-blocks", type=int, default=None, help="grid bound of the receive copy kernel")
     ap.add_argument("--serialize", action="store_true", help="run the whole schedule on one stream")
     return ap.parse_args()
@@ -235,10 +237,15 @@ def main():
             plan.set_recv_blocks(nb)
             ms_blocks[nb] = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
         plan.set_recv_blocks(512 if args.recv_blocks is None else args.recv_blocks)
-        plan.set_recv(args.recv or "memcpy")
+        recv_ms = {}
+        for mode in ("memcpy", "fused"):
+            plan.set_recv(mode)
+            recv_ms[mode] = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
+        plan.set_recv(args.recv or "fused")
         result["modes_ms"] = {"overlapped_fused_merge": round(ms, 5), "serialized_fused_merge": round(ms_serial, 5),
                               "overlapped_separate_merge": round(ms_sep, 5),
                               "receive_kernel_grid_blocks_ms": ms_blocks,
+                              "receive_mode_ms": recv_ms,
                               "exposed_copy_ms": round(ms_serial - ms, 5)}
         run_call(plan, w, bufs, stream)
         torch.cuda.synchronize()

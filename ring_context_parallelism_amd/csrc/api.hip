@@ -149,10 +149,10 @@ int ensure_device(Plan& p) {
   return CP_ATTN_OK;
 }
 
-// Copy the K and V rows of ring source `src` (its local order) into slot b:
-// its one or two chunks are contiguous token ranges of the natural-order
-// tensors, so the receive is four (zigzag) or two (contiguous) linear copies.
-int recv_kv(Plan& p, const void* k, const void* v, int src, int b, hipStream_t s) {
+// The K and V rows of ring source `src` (its local order) are one (contiguous)
+// or two (zigzag) token ranges of the natural-order tensors; receiving them
+// into slot b is two or four linear copies.
+RecvArgs recv_ranges(Plan& p, const void* k, const void* v, int src, int b) {
   DeviceState& d = *p.dev;
   const WsLayout w = ws_layout(p);
   char* ws = static_cast<char*>(d.ws);
@@ -161,16 +161,6 @@ int recv_kv(Plan& p, const void* k, const void* v, int src, int b, hipStream_t s
   const int64_t row_bytes = int64_t(p.heads) * p.head_dim * p.elem_bytes();
   const int nch = p.layout == 1 ? 2 : 1;
   const int64_t ch_bytes = p.chunk * row_bytes;
-  if (p.opt_recv == 1) {
-    for (int c = 0; c < nch; ++c) {
-      const int64_t g = p.chunk_of(src, c) * ch_bytes;
-      CPA_HIP(hipMemcpyAsync(dk + c * ch_bytes, static_cast<const char*>(k) + g, size_t(ch_bytes),
-                             hipMemcpyDeviceToDevice, s));
-      CPA_HIP(hipMemcpyAsync(dv + c * ch_bytes, static_cast<const char*>(v) + g, size_t(ch_bytes),
-                             hipMemcpyDeviceToDevice, s));
-    }
-    return CP_ATTN_OK;
-  }
   RecvArgs ra{};
   for (int c = 0; c < nch; ++c) {
     const int64_t g = p.chunk_of(src, c) * ch_bytes;
@@ -181,9 +171,22 @@ int recv_kv(Plan& p, const void* k, const void* v, int src, int b, hipStream_t s
     ra.dst[ra.n] = dv + c * ch_bytes;
     ra.vec[ra.n++] = ch_bytes / 16;
   }
+  return ra;
+}
+
+// Side-stream receive of ring source `src` into slot b.
+int recv_kv(Plan& p, const void* k, const void* v, int src, int b, hipStream_t s) {
+  const RecvArgs ra = recv_ranges(p, k, v, src, b);
+  if (p.opt_recv == 1) {
+    for (int i = 0; i < ra.n; ++i)
+      CPA_HIP(hipMemcpyAsync(ra.dst[i], ra.src[i], size_t(ra.vec[i] * 16), hipMemcpyDeviceToDevice, s));
+    return CP_ATTN_OK;
+  }
   CPA_HIP(launch_recv(ra, p.opt_recv_blocks, s));
   return CP_ATTN_OK;
 }
+
+bool fused_recv(const Plan& p) { return p.opt_recv == 2 && attn_does_recv(p.dtype == CP_ATTN_BF16, p.head_dim); }
 
 // Step 0 reads the rank's own K/V in place (the rank holds them; nothing is
 // received); later steps read receive slot b.
@@ -193,8 +196,12 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
   const WsLayout w = ws_layout(p);
   char* ws = static_cast<char*>(d.ws);
   const StepDesc& sd = p.step(r, s);
-  if (sd.nseg == 0) return CP_ATTN_OK;
   const bool bf16 = p.dtype == CP_ATTN_BF16;
+  if (sd.nseg == 0) {
+    // no query row of this rank sees the step's keys; the receive still happens
+    if (fused_recv(p) && s + 1 < p.cp) CPA_HIP(launch_recv(recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1), 0, st));
+    return CP_ATTN_OK;
+  }
   const int bm = bf16 ? attn_bf16_block_m() : attn_f32_block_m();
   StepArgs a{};
   a.q = q;
@@ -246,6 +253,7 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
     a.total_tiles += x.tiles;
   }
   if (sd.nseg == 1) a.seg[1] = SegArgs{};
+  if (fused_recv(p) && s + 1 < p.cp) a.recv = recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
   return CP_ATTN_OK;
@@ -322,15 +330,16 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
     CPA_HIP(hipStreamWaitEvent(cs, d.start, 0));
     if (separate) CPA_HIP(hipStreamWaitEvent(ms, d.start, 0));
   }
+  const bool fused = fused_recv(p);
   for (int s = 0; s < P; ++s) {
     const int b = s & 1;
-    if (s + 1 < P) {
+    if (s + 1 < P && !fused) {
       const int nb = (s + 1) & 1;
       if (!serial && s >= 1) CPA_HIP(hipStreamWaitEvent(cs, d.attn_done[nb], 0));
       CPA_TRY(recv_kv(p, k, v, p.step(r, s + 1).src, nb, cs));
       if (!serial) CPA_HIP(hipEventRecord(d.recv_done[nb], cs));
     }
-    if (!serial && s >= 1) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
+    if (!serial && !fused && s >= 1) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
     if (separate && !serial && s >= 2) CPA_HIP(hipStreamWaitEvent(st, d.merge_done[b], 0));
     const size_t ti = size_t(r) * P + s;
     if (p.opt_step_timing) CPA_HIP(hipEventRecord(d.t0[ti], st));
@@ -471,7 +480,7 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
       p.opt_serialize = value != 0;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_RECV:
-      if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "recv option must be 0 or 1");
+      if (value < 0 || value > 2) return fail(CP_ATTN_EINVAL, "recv option must be 0, 1 or 2");
       p.opt_recv = value;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_POISON:

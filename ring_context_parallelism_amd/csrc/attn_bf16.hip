@@ -495,6 +495,45 @@ void attn_step_bf16_d128(StepArgs a) {
         }
   };
 
+  // In-kernel ring receive (a.recv.n > 0): this workgroup copies its share of
+  // the next step's K/V into the other receive slot, one 16-byte vector per
+  // thread per tile; each vector is loaded at the top of an iteration and
+  // stored at the top of the next, so the load latency hides under a tile of
+  // compute.  Non-temporal accesses keep the copy out of the caches.
+  int64_t rstart[4];
+  int64_t rtot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rstart[i] = rtot;
+    rtot += i < a.recv.n ? a.recv.vec[i] : 0;
+  }
+  const int64_t rshare = (rtot + gridDim.x - 1) / gridDim.x;
+  int64_t rcur = min(rtot, int64_t(blockIdx.x) * rshare);
+  const int64_t rend = min(rtot, rcur + rshare);
+  u32x4 rbuf{};
+  u32x4* rdst = nullptr;
+  auto recv_ptrs = [&](int64_t i, const u32x4*& src, u32x4*& dst) {
+    const int r = int(i >= rstart[1]) + int(i >= rstart[2]) + int(i >= rstart[3]);
+    const int64_t off = i - rstart[r];
+    src = static_cast<const u32x4*>(a.recv.src[r]) + off;
+    dst = static_cast<u32x4*>(a.recv.dst[r]) + off;
+  };
+  auto recv_step = [&]() {
+    if (rdst) {
+      __builtin_nontemporal_store(rbuf, rdst);
+      rdst = nullptr;
+    }
+    if (rcur < rend) {
+      const int64_t i = rcur + tid;
+      if (i < rend) {
+        const u32x4* src;
+        recv_ptrs(i, src, rdst);
+        rbuf = __builtin_nontemporal_load(src);
+      }
+      rcur += kThreads;
+    }
+  };
+
   // K(j) lives in kbuf[j & 1], V(j) in vbuf[j & 1]; K runs one tile ahead.
   const int ntiles = (kv_end + kBN - 1) / kBN;
   if (ntiles > 0) {
@@ -513,6 +552,7 @@ void attn_step_bf16_d128(StepArgs a) {
     const int j0_ = (J) * kBN;                                                            \
     if ((J) + 2 < ntiles) issue(a.k, j0_ + 2 * kBN, (PAR) ? kbuf1 : kbuf0);              \
     if ((J) + 1 < ntiles) issue(a.v, j0_ + kBN, (PAR) ? vbuf0 : vbuf1);                   \
+    recv_step();                                                                          \
     const bool act_ = j0_ < w_max;                                                        \
     bf16x8 pb_[2][2];                                                                     \
     if (act_) softmax(SC, j0_, pb_);                                                      \
@@ -529,6 +569,17 @@ void attn_step_bf16_d128(StepArgs a) {
   }
   if (j < ntiles) CPATTN_STEP(j, 0, sa, sb);
 #undef CPATTN_STEP
+  // rest of the receive share (workgroups with few tiles)
+  if (rdst) __builtin_nontemporal_store(rbuf, rdst);
+  for (; rcur < rend; rcur += kThreads) {
+    const int64_t i = rcur + tid;
+    if (i < rend) {
+      const u32x4* src;
+      u32x4* dst;
+      recv_ptrs(i, src, dst);
+      __builtin_nontemporal_store(__builtin_nontemporal_load(src), dst);
+    }
+  }
 
   l += __shfl_xor(l, 32);
   if (!ok) return;
@@ -551,6 +602,8 @@ void attn_step_bf16_d128(StepArgs a) {
 }  // namespace
 
 int attn_bf16_block_m() { return kBM; }
+
+bool attn_does_recv(int dtype_bf16, int head_dim) { return dtype_bf16 && head_dim == 128; }
 
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid(unsigned(a.total_tiles) * unsigned(a.heads));

@@ -26,6 +26,14 @@ struct SegArgs {
   int32_t tiles;     // ceil(q_len / BM) for the launching kernel
 };
 
+// Ring receive: up to four contiguous byte ranges (16-byte multiples).
+struct RecvArgs {
+  const void* src[4];
+  void* dst[4];
+  int64_t vec[4];  // 16-byte vectors per range
+  int32_t n;
+};
+
 struct StepArgs {
   const void* q;     // [S][H][D] natural order, plan dtype
   // K/V source: rows of [H][D] elements.  Local key kk (0 <= kk < n_loc) is
@@ -53,9 +61,12 @@ struct StepArgs {
   int32_t nseg;
   int32_t total_tiles;  // sum of seg[i].tiles
   SegArgs seg[2];
+  RecvArgs recv;        // next step's receive done by this kernel (recv.n == 0: none)
 };
 
 // attention step kernels: return hipError_t of the launch
+// (only the head_dim 128 bf16 kernel performs StepArgs::recv)
+bool attn_does_recv(int dtype_bf16, int head_dim);
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_f32(const StepArgs& a, int head_dim, hipStream_t stream);
 int attn_bf16_block_m();
@@ -81,15 +92,6 @@ struct LayoutArgs {
 // max_blocks > 0 bounds the grid (per tensor); 0 sizes it to the data.
 hipError_t launch_layout(const LayoutArgs& a, int max_blocks, hipStream_t stream);
 
-// Ring receive: up to four contiguous byte ranges (16-byte multiples),
-// copied with non-temporal accesses by a small grid that shares the GPU with
-// the attention kernel it overlaps.
-struct RecvArgs {
-  const void* src[4];
-  void* dst[4];
-  int64_t vec[4];  // 16-byte vectors per range
-  int32_t n;
-};
 hipError_t launch_recv(const RecvArgs& a, int blocks, hipStream_t stream);
 
 // Fill with NaN (all-ones bytes) -- a kernel, not a memset, so it is safe in captured graphs.

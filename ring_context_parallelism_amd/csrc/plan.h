@@ -43,7 +43,7 @@ struct Plan {
   // options
   int32_t opt_merge = 0;
   int32_t opt_serialize = 0;
-  int32_t opt_recv = 1;
+  int32_t opt_recv = 2;
   int32_t opt_poison = 0;
   int32_t opt_step_timing = 0;
   int32_t opt_recv_blocks = 64;

@@ -174,7 +174,13 @@ def test_schedule_modes_agree(dtype):
     p.set_recv_blocks(3)
     small_grid = _run(p, q, k, v)
     p.set_recv_blocks(256)
-    for o, l in (ser, poi, mem, full_grid, small_grid):
+    p.set_recv("fused")
+    fused = _run(p, q, k, v)
+    p.set_poison(True)
+    fused_poi = _run(p, q, k, v)
+    p.set_poison(False)
+    p.set_recv("memcpy")
+    for o, l in (ser, poi, mem, full_grid, small_grid, fused, fused_poi):
         assert _bitwise_equal(o, base[0]) and _bitwise_equal(l, base[1])
     p.set_merge(True)
     sep = _run(p, q, k, v)
@@ -251,13 +257,15 @@ def _sample_rows(seq, cp, layout, rank, rng, per_chunk=6):
     return np.unique(np.asarray(rows))
 
 
+@pytest.mark.parametrize("recv", ["memcpy", "fused"])
 @pytest.mark.parametrize("name", [n for n in WORKLOADS if "fp32" not in n])
-def test_full_workload_sampled(name):
+def test_full_workload_sampled(name, recv):
     """The configuration the bench times, compared on sampled rows and heads."""
     w = WORKLOADS[name]
-    _say(f"workload {name}")
+    _say(f"workload {name} receive={recv}")
     q, k, v = workload_qkv(w)
     p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout)
+    p.set_recv(recv)
     out, lse = _run(p, q, k, v, rank=w.rank)
     rng = np.random.default_rng(w.seed)
     rows = _sample_rows(w.seq_len, w.cp, w.layout, w.rank, rng)
