@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="keep warming up (untimed calls) until this long has passed, so clocks have ramped")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip imbalance / mode / parity side measurements")
@@ -43,6 +45,9 @@ def parse():
     ap.add_argument("--recv", choices=["kernel", "memcpy", "fused"], default=None, help="ring receive path (default: library's)")
     ap.add_argument("--recv-blocks", type=int, default=None, help="grid bound of the receive copy kernel")
     ap.add_argument("--serialize", action="store_true", help="run the whole schedule on one stream")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one layout gather of q (a plain copy of known size) before timing, "
+                         "as the reference for hardware traffic counters")
     return ap.parse_args()
 
 
@@ -59,9 +64,14 @@ def run_call(plan, w, bufs, stream):
         plan.rank_forward(q, k, v, out, lse, w.rank, stream=stream)
 
 
-def time_calls(plan, w, bufs, stream, steps, warmup):
-    for _ in range(warmup):
+def time_calls(plan, w, bufs, stream, steps, warmup, warmup_seconds=0.0):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < warmup_seconds:
         run_call(plan, w, bufs, stream)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -83,6 +93,33 @@ def step_kernel_times(plan, w, bufs, stream, reps):
         acc = t if acc is None else acc + t
     plan.set_step_timing(False)
     return acc / reps
+
+
+PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                       "attn_step_bf16_d128_causal_s32768_cp8_rank0.md")
+KERNEL_SOURCES = ("attn_bf16.hip", "epilogue.h", "kernels.h")
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the step kernel from the committed rocprofv3 summary,
+    or None when the kernel source has changed since the counters were taken."""
+    if workload != DEFAULT_WORKLOAD or not os.path.exists(PROFILE):
+        return None
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "ring_context_parallelism_amd", "csrc")
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    fields = {}
+    with open(PROFILE) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in fields else None
 
 
 def cpu_baseline(w, q, k, v, target_s):
@@ -193,9 +230,15 @@ def main():
     if args.serialize:
         plan.set_serialize(True)
 
+    if args.copy_probe:
+        probe = torch.empty_like(q)
+        plan.layout_gather(q, probe)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: layout gather of {q.numel() * q.element_size()} bytes", file=sys.stderr)
+        del probe
     pairs = share_pairs(plan, w)
     flops = 4 * w.head_dim * w.heads * pairs
-    ms = time_calls(plan, w, bufs, stream, args.steps, args.warmup)
+    ms = time_calls(plan, w, bufs, stream, args.steps, args.warmup, args.warmup_seconds)
     tflops = flops / (ms * 1e-3) / 1e12
     print(f"[bench] {w.name}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
@@ -208,7 +251,7 @@ def main():
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
     roofline = {"kernel": "attn_step_bf16" if w.dtype == "bf16" else "attn_step_f32", "bound": "mfma",
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(w.name),
                 "avg_launch_ms": round(avg_ms, 5), "launches_per_step": len(launches),
                 "valid_flops_per_launch": flops_per_launch}
 

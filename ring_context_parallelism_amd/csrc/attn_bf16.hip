@@ -497,9 +497,11 @@ void attn_step_bf16_d128(StepArgs a) {
 
   // In-kernel ring receive (a.recv.n > 0): this workgroup copies its share of
   // the next step's K/V into the other receive slot, one 16-byte vector per
-  // thread per tile; each vector is loaded at the top of an iteration and
-  // stored at the top of the next, so the load latency hides under a tile of
-  // compute.  Non-temporal accesses keep the copy out of the caches.
+  // thread per tile.  Right after each end-of-tile wait the vector loaded one
+  // tile earlier is stored and a new one is loaded into the other register
+  // buffer, so neither waits: the load has a whole tile to complete and the
+  // store is covered by the next end-of-tile wait.  Non-temporal accesses keep
+  // the copy out of the caches.
   int64_t rstart[4];
   int64_t rtot = 0;
 #pragma unroll
@@ -510,25 +512,39 @@ void attn_step_bf16_d128(StepArgs a) {
   const int64_t rshare = (rtot + gridDim.x - 1) / gridDim.x;
   int64_t rcur = min(rtot, int64_t(blockIdx.x) * rshare);
   const int64_t rend = min(rtot, rcur + rshare);
-  u32x4 rbuf{};
-  u32x4* rdst = nullptr;
+  u32x4 rbuf[2] = {u32x4{}, u32x4{}};
+  u32x4* rdst[2] = {nullptr, nullptr};
+  // constant-index selects: the pointers stay in scalar registers
   auto recv_ptrs = [&](int64_t i, const u32x4*& src, u32x4*& dst) {
     const int r = int(i >= rstart[1]) + int(i >= rstart[2]) + int(i >= rstart[3]);
-    const int64_t off = i - rstart[r];
-    src = static_cast<const u32x4*>(a.recv.src[r]) + off;
-    dst = static_cast<u32x4*>(a.recv.dst[r]) + off;
+    const int64_t off = i - (r == 0 ? rstart[0] : r == 1 ? rstart[1] : r == 2 ? rstart[2] : rstart[3]);
+    const void* sb = r == 0 ? a.recv.src[0] : r == 1 ? a.recv.src[1] : r == 2 ? a.recv.src[2] : a.recv.src[3];
+    void* db = r == 0 ? a.recv.dst[0] : r == 1 ? a.recv.dst[1] : r == 2 ? a.recv.dst[2] : a.recv.dst[3];
+    src = static_cast<const u32x4*>(sb) + off;
+    dst = static_cast<u32x4*>(db) + off;
   };
-  auto recv_step = [&]() {
-    if (rdst) {
-      __builtin_nontemporal_store(rbuf, rdst);
-      rdst = nullptr;
+  auto recv_flush = [&](int b) {
+    if (rdst[b]) {
+      __builtin_nontemporal_store(rbuf[b], rdst[b]);
+      rdst[b] = nullptr;
     }
+  };
+  auto recv_load = [&](int b) {
     if (rcur < rend) {
       const int64_t i = rcur + tid;
-      if (i < rend) {
+      const int64_t last = min(rend, rcur + kThreads) - 1;
+      const int r0 = int(rcur >= rstart[1]) + int(rcur >= rstart[2]) + int(rcur >= rstart[3]);
+      const int r1 = int(last >= rstart[1]) + int(last >= rstart[2]) + int(last >= rstart[3]);
+      if (r0 == r1) {  // the block of 256 vectors lies in one range: scalar bases
+        const int64_t off = i - rstart[r0];
+        if (i < rend) {
+          rdst[b] = static_cast<u32x4*>(a.recv.dst[r0]) + off;
+          rbuf[b] = __builtin_nontemporal_load(static_cast<const u32x4*>(a.recv.src[r0]) + off);
+        }
+      } else if (i < rend) {
         const u32x4* src;
-        recv_ptrs(i, src, rdst);
-        rbuf = __builtin_nontemporal_load(src);
+        recv_ptrs(i, src, rdst[b]);
+        rbuf[b] = __builtin_nontemporal_load(src);
       }
       rcur += kThreads;
     }
@@ -545,6 +561,7 @@ void attn_step_bf16_d128(StepArgs a) {
   __syncthreads();
   f32x16 sa[2], sb[2];
   if (ntiles > 0 && w_max > 0) scores(kbuf0, sa);
+  recv_load(0);
   __syncthreads();
 
 #define CPATTN_STEP(J, PAR, SC, SN)                                                       \
@@ -552,13 +569,14 @@ void attn_step_bf16_d128(StepArgs a) {
     const int j0_ = (J) * kBN;                                                            \
     if ((J) + 2 < ntiles) issue(a.k, j0_ + 2 * kBN, (PAR) ? kbuf1 : kbuf0);              \
     if ((J) + 1 < ntiles) issue(a.v, j0_ + kBN, (PAR) ? vbuf0 : vbuf1);                   \
-    recv_step();                                                                          \
     const bool act_ = j0_ < w_max;                                                        \
     bf16x8 pb_[2][2];                                                                     \
     if (act_) softmax(SC, j0_, pb_);                                                      \
     if ((J) + 1 < ntiles && j0_ + kBN < w_max) scores((PAR) ? kbuf0 : kbuf1, SN);         \
     if (act_) pv((PAR) ? vbuf1 : vbuf0, pb_);                                             \
     wait_vmem();                                                                          \
+    recv_flush(PAR);                                                                      \
+    recv_load((PAR) ^ 1);                                                                 \
     __syncthreads();                                                                      \
   } while (0)
 
@@ -570,7 +588,8 @@ void attn_step_bf16_d128(StepArgs a) {
   if (j < ntiles) CPATTN_STEP(j, 0, sa, sb);
 #undef CPATTN_STEP
   // rest of the receive share (workgroups with few tiles)
-  if (rdst) __builtin_nontemporal_store(rbuf, rdst);
+  recv_flush(0);
+  recv_flush(1);
   for (; rcur < rend; rcur += kThreads) {
     const int64_t i = rcur + tid;
     if (i < rend) {
