@@ -321,9 +321,9 @@ void attn_step_bf16(StepArgs a) {
 //     lane 4j + i/4 as its j-th value, so the 16 lanes that point at 4 key
 //     rows x 4 column pieces receive 4 keys of one head-dim column each --
 //     exactly the A operand of O^T = V^T P^T.
-//   * cross-tile pipelining: K runs one tile ahead of V in LDS, so while the
-//     softmax of tile j runs on the vector ALUs, the scores of tile j+1 are
-//     already issued to the matrix cores; one barrier per tile.
+//   * double-buffered LDS: tile j+1 is loaded while tile j computes; one
+//     barrier per tile.  Matrix operands are read from LDS in batches ahead
+//     of their MFMAs (all 16 K fragments of a tile; V in groups of four).
 // ---------------------------------------------------------------------------
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -344,12 +344,16 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16_d128(StepArgs a) {
   constexpr int D = 128, NT = 8, NB = 4;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * kTileBytes];  // K0 K1 V0 V1
-  lds_u8* const lds = (lds_u8*)smem;  // address-space cast of the shared array
-  lds_u8* const kbuf0 = lds;
-  lds_u8* const kbuf1 = lds + kTileBytes;
-  lds_u8* const vbuf0 = lds + 2 * kTileBytes;
-  lds_u8* const vbuf1 = lds + 3 * kTileBytes;
+  // four separate LDS objects, so the compiler can tell that reads of one
+  // buffer do not alias the direct-to-LDS loads in flight to another
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_k0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_v0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_v1[kTileBytes];
+  lds_u8* const kbuf0 = (lds_u8*)smem_k0;  // address-space casts of the shared arrays
+  lds_u8* const kbuf1 = (lds_u8*)smem_k1;
+  lds_u8* const vbuf0 = (lds_u8*)smem_v0;
+  lds_u8* const vbuf1 = (lds_u8*)smem_v1;
 
   int h, t;
   tile_of(blockIdx.x, gridDim.x, a.heads, a.total_tiles, h, t);
@@ -434,16 +438,23 @@ void attn_step_bf16_d128(StepArgs a) {
     vbase[r] = vr * 256 + ((c0 ^ swz(vr & 15)) << 4) + 8 * (i16 & 1);
   }
 
+  // Operand reads are issued in batches ahead of the MFMAs that use them
+  // (pinned with scheduling-group barriers), so the matrix cores do not wait
+  // for one LDS round trip per instruction.
   auto scores = [&](const lds_u8* kt, f32x16 (&s)[2]) {
+    bf16x8 kf[2][NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kf[kb][i] = *reinterpret_cast<const lds_bf16x8*>(kt + kb * 32 * 256 + (kbase ^ (32u * i)));
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const lds_bf16x8*>(kt + kb * 32 * 256 + (kbase ^ (32u * i)));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i], s[kb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][i], qf[i], s[kb], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // 16 LDS reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then 16 MFMAs
   };
   auto softmax = [&](f32x16 (&s)[2], int j0, bf16x8 (&pb)[2][2]) {
     if (j0 + kBN > w_min) {
@@ -481,18 +492,30 @@ void attn_step_bf16_d128(StepArgs a) {
       }
   };
   auto pv = [&](const lds_u8* vt, const bf16x8 (&pb)[2][2]) {
+    // four groups (kb, u) of four head-dim blocks; group g+1's transposed
+    // reads are in flight while group g's MFMAs run
+    bf16x8 va[4][NB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int gq = 0; gq < 4; ++gq) {
+      const int kb = gq >> 1, u = gq & 1;
+      const int roff = (32 * kb + 16 * u) * 256;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int b = 0; b < NB; ++b) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + roff + (vbase[0] ^ (64u * b))));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + roff + (vbase[1] ^ (64u * b))));
+        va[gq][b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const int roff = (32 * kb + 16 * u) * 256;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + roff + (vbase[0] ^ (64u * b))));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + roff + (vbase[1] ^ (64u * b))));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][u], o[b], 0, 0, 0);
-        }
+    for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[gq][b], pb[gq >> 1][gq & 1], o[b], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // groups 0 and 1 read
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // group 0 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // group 2 read
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // group 1 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // group 3 read
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // groups 2 and 3 MFMAs
   };
 
   // In-kernel ring receive (a.recv.n > 0): this workgroup copies its share of
@@ -550,30 +573,31 @@ void attn_step_bf16_d128(StepArgs a) {
     }
   };
 
-  // K(j) lives in kbuf[j & 1], V(j) in vbuf[j & 1]; K runs one tile ahead.
+  // K(j), V(j) live in kbuf[j & 1], vbuf[j & 1]; tile j+1 is loaded while
+  // tile j computes; one barrier per tile.
   const int ntiles = (kv_end + kBN - 1) / kBN;
   if (ntiles > 0) {
     issue(a.k, 0, kbuf0);
     issue(a.v, 0, vbuf0);
   }
-  if (ntiles > 1) issue(a.k, kBN, kbuf1);
   wait_vmem();
-  __syncthreads();
-  f32x16 sa[2], sb[2];
-  if (ntiles > 0 && w_max > 0) scores(kbuf0, sa);
   recv_load(0);
   __syncthreads();
 
-#define CPATTN_STEP(J, PAR, SC, SN)                                                       \
+#define CPATTN_STEP(J, PAR)                                                               \
   do {                                                                                    \
     const int j0_ = (J) * kBN;                                                            \
-    if ((J) + 2 < ntiles) issue(a.k, j0_ + 2 * kBN, (PAR) ? kbuf1 : kbuf0);              \
-    if ((J) + 1 < ntiles) issue(a.v, j0_ + kBN, (PAR) ? vbuf0 : vbuf1);                   \
-    const bool act_ = j0_ < w_max;                                                        \
-    bf16x8 pb_[2][2];                                                                     \
-    if (act_) softmax(SC, j0_, pb_);                                                      \
-    if ((J) + 1 < ntiles && j0_ + kBN < w_max) scores((PAR) ? kbuf0 : kbuf1, SN);         \
-    if (act_) pv((PAR) ? vbuf1 : vbuf0, pb_);                                             \
+    if ((J) + 1 < ntiles) {                                                               \
+      issue(a.k, j0_ + kBN, (PAR) ? kbuf0 : kbuf1);                                       \
+      issue(a.v, j0_ + kBN, (PAR) ? vbuf0 : vbuf1);                                       \
+    }                                                                                     \
+    if (j0_ < w_max) {                                                                    \
+      f32x16 s_[2];                                                                       \
+      bf16x8 pb_[2][2];                                                                   \
+      scores((PAR) ? kbuf1 : kbuf0, s_);                                                  \
+      softmax(s_, j0_, pb_);                                                              \
+      pv((PAR) ? vbuf1 : vbuf0, pb_);                                                     \
+    }                                                                                     \
     wait_vmem();                                                                          \
     recv_flush(PAR);                                                                      \
     recv_load((PAR) ^ 1);                                                                 \
@@ -582,10 +606,10 @@ void attn_step_bf16_d128(StepArgs a) {
 
   int j = 0;
   for (; j + 1 < ntiles; j += 2) {
-    CPATTN_STEP(j, 0, sa, sb);
-    CPATTN_STEP(j + 1, 1, sb, sa);
+    CPATTN_STEP(j, 0);
+    CPATTN_STEP(j + 1, 1);
   }
-  if (j < ntiles) CPATTN_STEP(j, 0, sa, sb);
+  if (j < ntiles) CPATTN_STEP(j, 0);
 #undef CPATTN_STEP
   // rest of the receive share (workgroups with few tiles)
   recv_flush(0);
