@@ -64,7 +64,7 @@ int fail(int code, const std::string& msg) {
   } while (0)
 
 struct WsLayout {
-  int64_t slot_k[2], slot_v[2], acc_o, acc_lse, part_o[2], part_lse[2], total;
+  int64_t slot_k[2], slot_v[2], acc_o, acc_lse, part_o[2], part_lse[2], sink, total;
   int64_t kv_bytes, o_bytes, lse_bytes;
 };
 
@@ -91,6 +91,7 @@ WsLayout ws_layout(const Plan& p) {
     w.part_o[b] = take(w.o_bytes);
     w.part_lse[b] = take(w.lse_bytes);
   }
+  w.sink = take(kRecvSinkBytes);
   w.total = off;
   return w;
 }
@@ -254,6 +255,7 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
   }
   if (sd.nseg == 1) a.seg[1] = SegArgs{};
   if (fused_recv(p) && s + 1 < p.cp) a.recv = recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1);
+  a.recv.sink = ws + w.sink;
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
   return CP_ATTN_OK;
@@ -325,12 +327,16 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
   hipStream_t cs = serial ? st : d.copy;
   hipStream_t ms = serial ? st : d.merge;
 
-  if (!serial) {
-    CPA_HIP(hipEventRecord(d.start, st));
-    CPA_HIP(hipStreamWaitEvent(cs, d.start, 0));
-    if (separate) CPA_HIP(hipStreamWaitEvent(ms, d.start, 0));
-  }
   const bool fused = fused_recv(p);
+  // cross-stream events only where another stream waits on them: each
+  // record/wait pair costs microseconds of queue latency per step
+  const bool copy_side = !serial && !fused;
+  const bool merge_side = !serial && separate;
+  if (copy_side || merge_side) {
+    CPA_HIP(hipEventRecord(d.start, st));
+    if (copy_side) CPA_HIP(hipStreamWaitEvent(cs, d.start, 0));
+    if (merge_side) CPA_HIP(hipStreamWaitEvent(ms, d.start, 0));
+  }
   for (int s = 0; s < P; ++s) {
     const int b = s & 1;
     if (s + 1 < P && !fused) {
@@ -352,7 +358,7 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
       CPA_HIP(launch_poison(ws + w.slot_k[b], w.kv_bytes, st));
       CPA_HIP(launch_poison(ws + w.slot_v[b], w.kv_bytes, st));
     }
-    if (!serial) CPA_HIP(hipEventRecord(d.attn_done[b], st));
+    if (copy_side || merge_side) CPA_HIP(hipEventRecord(d.attn_done[b], st));
     if (separate && s > 0) {
       if (!serial) CPA_HIP(hipStreamWaitEvent(ms, d.attn_done[b], 0));
       CPA_TRY(launch_step_merge(p, r, s, b, ms));

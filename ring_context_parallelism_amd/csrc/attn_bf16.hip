@@ -115,6 +115,7 @@ void attn_step_bf16(StepArgs a) {
   const int si = t < a.seg[0].tiles ? 0 : 1;
   if (si) t -= a.seg[0].tiles;
   const SegArgs& g = a.seg[si];
+  const int epi = __builtin_amdgcn_readfirstlane(g.epi);  // scalar: the epilogue branches on it
   if (g.diag) t = g.tiles - 1 - t;  // longest rows first
   const int row0 = t * kBM;
 
@@ -295,17 +296,22 @@ void attn_step_bf16(StepArgs a) {
   const int lrow = g.q_start + row;
   const float lse_s = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
   const float inv = 1.f / l;
-  const RowEpi e = row_epi_begin(a, g, h, lrow, lse_s);
+  float4 c[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) c[b][q4] = row_epi_load4(a, epi, h, lrow, 32 * b + 8 * q4 + 4 * hf, D);
+  const RowEpi e = row_epi_begin(a, epi, h, lrow, lse_s);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const float4 v4 = make_float4(o[b][4 * q4] * inv, o[b][4 * q4 + 1] * inv, o[b][4 * q4 + 2] * inv,
                                     o[b][4 * q4 + 3] * inv);
-      row_epi_store4(a, g, e, h, lrow, grow, 32 * b + 8 * q4 + 4 * hf, D, v4);
+      row_epi_store4(a, epi, e, h, lrow, grow, 32 * b + 8 * q4 + 4 * hf, D, v4, c[b][q4]);
     }
   }
-  if (hf == 0) row_epi_store_lse(a, g, e, h, lrow, grow, lse_s);
+  if (hf == 0) row_epi_store_lse(a, epi, e, h, lrow, grow, lse_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -341,6 +347,16 @@ __device__ __forceinline__ int swz(int r) {
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// Workgroup barrier ordering LDS only.  __syncthreads() also orders global
+// memory, which makes every wave wait for all of its global loads and stores
+// in flight (the ring copy included); LDS written by direct-to-LDS loads is
+// covered by each wave's own vmcnt wait before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no compiler reordering of memory accesses across
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16_d128(StepArgs a) {
   constexpr int D = 128, NT = 8, NB = 4;
@@ -360,6 +376,7 @@ void attn_step_bf16_d128(StepArgs a) {
   const int si = t < a.seg[0].tiles ? 0 : 1;
   if (si) t -= a.seg[0].tiles;
   const SegArgs& g = a.seg[si];
+  const int epi = __builtin_amdgcn_readfirstlane(g.epi);  // scalar: the epilogue branches on it
   if (g.diag) t = g.tiles - 1 - t;  // longest rows first
   const int row0 = t * kBM;
 
@@ -522,9 +539,9 @@ void attn_step_bf16_d128(StepArgs a) {
   // the next step's K/V into the other receive slot, one 16-byte vector per
   // thread per tile.  Right after each end-of-tile wait the vector loaded one
   // tile earlier is stored and a new one is loaded into the other register
-  // buffer, so neither waits: the load has a whole tile to complete and the
-  // store is covered by the next end-of-tile wait.  Non-temporal accesses keep
-  // the copy out of the caches.
+  // buffer; the barrier that follows orders LDS only, so neither the store nor
+  // the load is waited for until the next end-of-tile wait.  Non-temporal
+  // accesses keep the copy out of the caches.
   int64_t rstart[4];
   int64_t rtot = 0;
 #pragma unroll
@@ -535,17 +552,36 @@ void attn_step_bf16_d128(StepArgs a) {
   const int64_t rshare = (rtot + gridDim.x - 1) / gridDim.x;
   int64_t rcur = min(rtot, int64_t(blockIdx.x) * rshare);
   const int64_t rend = min(rtot, rcur + rshare);
-  u32x4 rbuf[2] = {u32x4{}, u32x4{}};
-  u32x4* rdst[2] = {nullptr, nullptr};
-  // constant-index selects: the pointers stay in scalar registers
-  auto recv_ptrs = [&](int64_t i, const u32x4*& src, u32x4*& dst) {
-    const int r = int(i >= rstart[1]) + int(i >= rstart[2]) + int(i >= rstart[3]);
-    const int64_t off = i - (r == 0 ? rstart[0] : r == 1 ? rstart[1] : r == 2 ? rstart[2] : rstart[3]);
-    const void* sb = r == 0 ? a.recv.src[0] : r == 1 ? a.recv.src[1] : r == 2 ? a.recv.src[2] : a.recv.src[3];
-    void* db = r == 0 ? a.recv.dst[0] : r == 1 ? a.recv.dst[1] : r == 2 ? a.recv.dst[2] : a.recv.dst[3];
-    src = static_cast<const u32x4*>(sb) + off;
-    dst = static_cast<u32x4*>(db) + off;
+  // The range bases are pinned in scalar registers (an empty asm makes them
+  // opaque), so picking one is a few scalar selects rather than an indexed
+  // load from the argument block.
+  typedef __attribute__((address_space(1))) u32x4 g_u32x4;  // global memory: no flat accesses
+  const g_u32x4* rsb[4];
+  g_u32x4* rdb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rsb[i] = (const g_u32x4*)(a.recv.src[i]);
+    rdb[i] = (g_u32x4*)(a.recv.dst[i]);
+    asm volatile("" : "+s"(rsb[i]), "+s"(rdb[i]));
+  }
+  auto recv_range = [&](int64_t i) { return int(i >= rstart[1]) + int(i >= rstart[2]) + int(i >= rstart[3]); };
+  auto recv_src = [&](int r) { return r == 0 ? rsb[0] : r == 1 ? rsb[1] : r == 2 ? rsb[2] : rsb[3]; };
+  auto recv_dst = [&](int r) { return r == 0 ? rdb[0] : r == 1 ? rdb[1] : r == 2 ? rdb[2] : rdb[3]; };
+  auto recv_base = [&](int r) { return r == 0 ? rstart[0] : r == 1 ? rstart[1] : r == 2 ? rstart[2] : rstart[3]; };
+  // addresses of vector i (< rend) when the range is not known to be uniform
+  auto recv_ptrs = [&](int64_t i, const g_u32x4*& src, g_u32x4*& dst) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t lo = rstart[r];
+      const int64_t hi = r < 3 ? rstart[r + 1] : rtot;
+      if (i >= lo && i < hi) {
+        src = rsb[r] + (i - lo);
+        dst = rdb[r] + (i - lo);
+      }
+    }
   };
+  u32x4 rbuf[2] = {u32x4{}, u32x4{}};
+  g_u32x4* rdst[2] = {nullptr, nullptr};
   auto recv_flush = [&](int b) {
     if (rdst[b]) {
       __builtin_nontemporal_store(rbuf[b], rdst[b]);
@@ -556,17 +592,18 @@ void attn_step_bf16_d128(StepArgs a) {
     if (rcur < rend) {
       const int64_t i = rcur + tid;
       const int64_t last = min(rend, rcur + kThreads) - 1;
-      const int r0 = int(rcur >= rstart[1]) + int(rcur >= rstart[2]) + int(rcur >= rstart[3]);
-      const int r1 = int(last >= rstart[1]) + int(last >= rstart[2]) + int(last >= rstart[3]);
-      if (r0 == r1) {  // the block of 256 vectors lies in one range: scalar bases
-        const int64_t off = i - rstart[r0];
-        if (i < rend) {
-          rdst[b] = static_cast<u32x4*>(a.recv.dst[r0]) + off;
-          rbuf[b] = __builtin_nontemporal_load(static_cast<const u32x4*>(a.recv.src[r0]) + off);
-        }
-      } else if (i < rend) {
-        const u32x4* src;
-        recv_ptrs(i, src, rdst[b]);
+      const int r0 = recv_range(rcur);
+      const g_u32x4* src = nullptr;
+      g_u32x4* dst = nullptr;
+      if (r0 == recv_range(last)) {  // the block of 256 vectors lies in one range: scalar bases
+        const int64_t off = i - recv_base(r0);
+        src = recv_src(r0) + off;
+        dst = recv_dst(r0) + off;
+      } else {
+        recv_ptrs(i, src, dst);
+      }
+      if (i < rend) {
+        rdst[b] = dst;
         rbuf[b] = __builtin_nontemporal_load(src);
       }
       rcur += kThreads;
@@ -582,7 +619,7 @@ void attn_step_bf16_d128(StepArgs a) {
   }
   wait_vmem();
   recv_load(0);
-  __syncthreads();
+  lds_barrier();
 
 #define CPATTN_STEP(J, PAR)                                                               \
   do {                                                                                    \
@@ -601,7 +638,7 @@ void attn_step_bf16_d128(StepArgs a) {
     wait_vmem();                                                                          \
     recv_flush(PAR);                                                                      \
     recv_load((PAR) ^ 1);                                                                 \
-    __syncthreads();                                                                      \
+    lds_barrier();                                                                        \
   } while (0)
 
   int j = 0;
@@ -617,8 +654,8 @@ void attn_step_bf16_d128(StepArgs a) {
   for (; rcur < rend; rcur += kThreads) {
     const int64_t i = rcur + tid;
     if (i < rend) {
-      const u32x4* src;
-      u32x4* dst;
+      const g_u32x4* src = nullptr;
+      g_u32x4* dst = nullptr;
       recv_ptrs(i, src, dst);
       __builtin_nontemporal_store(__builtin_nontemporal_load(src), dst);
     }
@@ -629,17 +666,22 @@ void attn_step_bf16_d128(StepArgs a) {
   const int lrow_out = g.q_start + row;
   const float lse_s = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
   const float inv = 1.f / l;
-  const RowEpi e = row_epi_begin(a, g, h, lrow_out, lse_s);
+  float4 c[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) c[b][q4] = row_epi_load4(a, epi, h, lrow_out, 32 * b + 8 * q4 + 4 * hf, D);
+  const RowEpi e = row_epi_begin(a, epi, h, lrow_out, lse_s);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const float4 v4 = make_float4(o[b][4 * q4] * inv, o[b][4 * q4 + 1] * inv, o[b][4 * q4 + 2] * inv,
                                     o[b][4 * q4 + 3] * inv);
-      row_epi_store4(a, g, e, h, lrow_out, grow, 32 * b + 8 * q4 + 4 * hf, D, v4);
+      row_epi_store4(a, epi, e, h, lrow_out, grow, 32 * b + 8 * q4 + 4 * hf, D, v4, c[b][q4]);
     }
   }
-  if (hf == 0) row_epi_store_lse(a, g, e, h, lrow_out, grow, lse_s);
+  if (hf == 0) row_epi_store_lse(a, epi, e, h, lrow_out, grow, lse_s);
 }
 
 }  // namespace

@@ -38,6 +38,7 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
   const int si = t < a.seg[0].tiles ? 0 : 1;
   if (si) t -= a.seg[0].tiles;
   const SegArgs& g = a.seg[si];
+  const int epi = __builtin_amdgcn_readfirstlane(g.epi);  // scalar: the epilogue branches on it
   const int row0 = t * kBM;
   const int tid = threadIdx.x;
   const int rl = tid / kTPR, sub = tid % kTPR;
@@ -108,13 +109,16 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
   const int lrow = g.q_start + row;
   const float lse_s = m + logf(l);
   const float inv = 1.f / l;
-  const RowEpi e = row_epi_begin(a, g, h, lrow, lse_s);
+  float4 c[DS / 4];
+#pragma unroll
+  for (int i = 0; i < DS; i += 4) c[i / 4] = row_epi_load4(a, epi, h, lrow, sub * DS + i, D);
+  const RowEpi e = row_epi_begin(a, epi, h, lrow, lse_s);
 #pragma unroll
   for (int i = 0; i < DS; i += 4) {
     float4 v4 = make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
-    row_epi_store4(a, g, e, h, lrow, grow, sub * DS + i, D, v4);
+    row_epi_store4(a, epi, e, h, lrow, grow, sub * DS + i, D, v4, c[i / 4]);
   }
-  if (sub == 0) row_epi_store_lse(a, g, e, h, lrow, grow, lse_s);
+  if (sub == 0) row_epi_store_lse(a, epi, e, h, lrow, grow, lse_s);
 }
 
 }  // namespace

@@ -28,10 +28,11 @@ struct RowEpi {
   float L;   // resulting LSE (natural log)
 };
 
-__device__ __forceinline__ RowEpi row_epi_begin(const StepArgs& a, const SegArgs& g, int h, int lrow,
-                                                float lse_s) {
+// epi is the segment's EpiMode flags, wave-uniform (pass it through
+// readfirstlane so the mode tests are scalar branches).
+__device__ __forceinline__ RowEpi row_epi_begin(const StepArgs& a, int epi, int h, int lrow, float lse_s) {
   RowEpi e{0.f, 1.f, lse_s};
-  if ((g.epi & 3) == kEpiMerge) {
+  if ((epi & 3) == kEpiMerge) {
     const float la = a.acc_lse[int64_t(h) * a.n_loc + lrow];
     if (la != -INFINITY) {
       if (lse_s == -INFINITY) {
@@ -50,24 +51,34 @@ __device__ __forceinline__ RowEpi row_epi_begin(const StepArgs& a, const SegArgs
   return e;
 }
 
-// Four consecutive head-dim values d0..d0+3 of local row lrow, head h.
-__device__ __forceinline__ void row_epi_store4(const StepArgs& a, const SegArgs& g, const RowEpi& e, int h,
-                                               int lrow, int64_t grow, int d0, int head_dim, float4 o) {
-  const int mode = g.epi & 3;
+// Running-state O values d0..d0+3 of local row lrow, head h, that a merge
+// reads (zero otherwise).  A row's loads are all issued before its stores
+// (and without waiting for row_epi_begin's LSE read: the values are only used
+// where that weight is nonzero), so they are in flight together instead of
+// one memory round trip per four values.
+__device__ __forceinline__ float4 row_epi_load4(const StepArgs& a, int epi, int h, int lrow, int d0, int head_dim) {
+  if ((epi & 3) != kEpiMerge) return make_float4(0.f, 0.f, 0.f, 0.f);
+  return *reinterpret_cast<const float4*>(a.acc_o + (int64_t(lrow) * a.heads + h) * head_dim + d0);
+}
+
+// Four consecutive head-dim values d0..d0+3 of local row lrow, head h: o is
+// this step's normalised output, c what row_epi_load4 returned for them.
+__device__ __forceinline__ void row_epi_store4(const StepArgs& a, int epi, const RowEpi& e, int h, int lrow,
+                                               int64_t grow, int d0, int head_dim, float4 o, float4 c) {
+  const int mode = epi & 3;
   const int64_t lidx = (int64_t(lrow) * a.heads + h) * head_dim + d0;
   if (mode == kEpiPartial) {
     *reinterpret_cast<float4*>(a.part_o + lidx) = o;
     return;
   }
   float4 r = make_float4(o.x * e.ws, o.y * e.ws, o.z * e.ws, o.w * e.ws);
-  if (mode == kEpiMerge && e.wa != 0.f) {
-    const float4 c = *reinterpret_cast<const float4*>(a.acc_o + lidx);
+  if (e.wa != 0.f) {  // an empty running state (weight 0) may hold anything, even NaN
     r.x += e.wa * c.x;
     r.y += e.wa * c.y;
     r.z += e.wa * c.z;
     r.w += e.wa * c.w;
   }
-  if (g.epi & kEpiFinal) {
+  if (epi & kEpiFinal) {
     const int64_t gidx = (grow * a.heads + h) * head_dim + d0;
     if (a.out_f32) {
       *reinterpret_cast<float4*>(static_cast<float*>(a.out) + gidx) = r;
@@ -86,12 +97,12 @@ __device__ __forceinline__ void row_epi_store4(const StepArgs& a, const SegArgs&
   }
 }
 
-__device__ __forceinline__ void row_epi_store_lse(const StepArgs& a, const SegArgs& g, const RowEpi& e, int h,
-                                                  int lrow, int64_t grow, float lse_s) {
-  const int mode = g.epi & 3;
+__device__ __forceinline__ void row_epi_store_lse(const StepArgs& a, int epi, const RowEpi& e, int h, int lrow,
+                                                  int64_t grow, float lse_s) {
+  const int mode = epi & 3;
   if (mode == kEpiPartial) {
     a.part_lse[int64_t(h) * a.n_loc + lrow] = lse_s;
-  } else if (g.epi & kEpiFinal) {
+  } else if (epi & kEpiFinal) {
     a.lse[int64_t(h) * a.seq_len + grow] = e.L;
   } else {
     a.acc_lse[int64_t(h) * a.n_loc + lrow] = e.L;

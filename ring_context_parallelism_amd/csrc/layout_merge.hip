@@ -48,38 +48,34 @@ __global__ __launch_bounds__(kThreads) void layout_copy(LayoutArgs a) {
   }
 }
 
-// Ring receive: the ranges are walked as one concatenated index space; every
-// thread keeps four non-temporal 16-byte loads in flight before storing, so a
-// grid of a few dozen workgroups reaches a useful rate without crowding the
-// attention kernel or evicting its cached K/V.
-__global__ __launch_bounds__(kThreads) void recv_copy(RecvArgs a) {
+// Ring receive as a kernel of its own on the copy stream: one wave per
+// workgroup and at most 16 VGPRs, so its waves fit in the registers the step
+// kernel leaves free on each SIMD and the copy runs beside the step instead
+// of taking compute units from it (and with its own memory counters, so the
+// step never waits for the copy's stores).  Each lane keeps two non-temporal
+// 16-byte loads in flight; offsets are 32-bit from scalar bases (a range is
+// below 4 GiB: the plan bounds every tensor to 2^32 bytes).
+__global__ __launch_bounds__(64) __attribute__((amdgpu_num_vgpr(16))) void recv_copy(RecvArgs a) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  constexpr int kIlp = 4;
-  int64_t start[5];
-  start[0] = 0;
+  typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+  typedef __attribute__((address_space(1))) const char g_cchar;
+  typedef __attribute__((address_space(1))) char g_char;
+  const uint32_t stride = gridDim.x * 64u * 16u;  // bytes
 #pragma unroll
-  for (int i = 0; i < 4; ++i) start[i + 1] = start[i] + (i < a.n ? a.vec[i] : 0);
-  const int64_t total = start[4];
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
-  for (int64_t base = int64_t(blockIdx.x) * kThreads + threadIdx.x; base < total; base += stride * kIlp) {
-    u32x4 v[kIlp];
-    u32x4* to[kIlp];
-#pragma unroll
-    for (int u = 0; u < kIlp; ++u) {
-      const int64_t i = base + u * stride;
-      to[u] = nullptr;
-      if (i < total) {
-        int r = 0;
-#pragma unroll
-        for (int q = 1; q < 4; ++q) r += (i >= start[q]) ? 1 : 0;
-        const int64_t off = i - start[r];
-        v[u] = __builtin_nontemporal_load(static_cast<const u32x4*>(a.src[r]) + off);
-        to[u] = static_cast<u32x4*>(a.dst[r]) + off;
-      }
+  for (int r = 0; r < 4; ++r) {
+    if (r >= a.n) break;
+    g_cchar* src = (g_cchar*)(a.src[r]);
+    g_char* dst = (g_char*)(a.dst[r]);
+    const uint32_t n = uint32_t(a.vec[r]) * 16u;
+    uint32_t o = (blockIdx.x * 64u + threadIdx.x) * 16u;
+    for (; o + stride < n; o += 2 * stride) {
+      const uint32_t o1 = o + stride;
+      const u32x4 x0 = __builtin_nontemporal_load((const g_u32x4*)(src + o));
+      const u32x4 x1 = __builtin_nontemporal_load((const g_u32x4*)(src + o1));
+      __builtin_nontemporal_store(x0, (g_u32x4*)(dst + o));
+      __builtin_nontemporal_store(x1, (g_u32x4*)(dst + o1));
     }
-#pragma unroll
-    for (int u = 0; u < kIlp; ++u)
-      if (to[u]) __builtin_nontemporal_store(v[u], to[u]);
+    if (o < n) __builtin_nontemporal_store(__builtin_nontemporal_load((const g_u32x4*)(src + o)), (g_u32x4*)(dst + o));
   }
 }
 
@@ -179,7 +175,7 @@ hipError_t launch_recv(const RecvArgs& a, int blocks, hipStream_t stream) {
   for (int i = 0; i < a.n; ++i) total += a.vec[i];
   if (total == 0) return hipSuccess;
   const unsigned cap = blocks > 0 ? unsigned(blocks) : 65536u;
-  recv_copy<<<grid_for(total, int64_t(kThreads) * 4, cap), kThreads, 0, stream>>>(a);
+  recv_copy<<<grid_for(total, 64 * 2, cap), 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
