@@ -115,9 +115,8 @@ int cp_attn_set_dtype(cp_attn_plan_t plan, int dtype);
 int cp_attn_set_option(cp_attn_plan_t plan, int option, int value);
 
 /* Bytes of device workspace a forward call needs: two K/V receive slots, the
- * fp32 running state (O, LSE), two fp32 partial buffers for the separate
- * merge mode and a 1 MiB scratch area for the in-kernel receive copy, each
- * rounded up to 256 bytes. */
+ * fp32 running state (O, LSE) and two fp32 partial buffers for the separate
+ * merge mode, each rounded up to 256 bytes. */
 int cp_attn_workspace_bytes(cp_attn_plan_t plan, int64_t* bytes);
 
 /* Hand the plan caller-owned device memory of at least cp_attn_workspace_bytes

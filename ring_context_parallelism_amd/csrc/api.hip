@@ -64,7 +64,7 @@ int fail(int code, const std::string& msg) {
   } while (0)
 
 struct WsLayout {
-  int64_t slot_k[2], slot_v[2], acc_o, acc_lse, part_o[2], part_lse[2], sink, total;
+  int64_t slot_k[2], slot_v[2], acc_o, acc_lse, part_o[2], part_lse[2], total;
   int64_t kv_bytes, o_bytes, lse_bytes;
 };
 
@@ -91,7 +91,6 @@ WsLayout ws_layout(const Plan& p) {
     w.part_o[b] = take(w.o_bytes);
     w.part_lse[b] = take(w.lse_bytes);
   }
-  w.sink = take(kRecvSinkBytes);
   w.total = off;
   return w;
 }
@@ -255,7 +254,6 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
   }
   if (sd.nseg == 1) a.seg[1] = SegArgs{};
   if (fused_recv(p) && s + 1 < p.cp) a.recv = recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1);
-  a.recv.sink = ws + w.sink;
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
   return CP_ATTN_OK;

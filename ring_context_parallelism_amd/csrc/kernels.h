@@ -32,10 +32,7 @@ struct RecvArgs {
   void* dst[4];
   int64_t vec[4];  // 16-byte vectors per range
   int32_t n;
-  void* sink;      // kRecvSinkBytes of workspace that in-kernel copy loads/stores use when idle
 };
-
-constexpr int64_t kRecvSinkBytes = 1 << 20;
 
 struct StepArgs {
   const void* q;     // [S][H][D] natural order, plan dtype

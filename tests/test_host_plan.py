@@ -187,12 +187,11 @@ def test_call_error_codes_enqueue_nothing():
 
 def test_workspace_size_formula():
     import torch
-    SINK = 1 << 20  # scratch area of the in-kernel receive copy
     p = Plan(32768, 8, 32, 128, True, "zigzag")
     n, hd = 4096, 32 * 128
     kv = n * hd * 2
     o = n * hd * 4
     lse = 32 * n * 4
-    assert p.workspace_bytes() == 4 * kv + o + lse + 2 * (o + lse) + SINK
+    assert p.workspace_bytes() == 4 * kv + o + lse + 2 * (o + lse)
     q = Plan(256, 2, 2, 64, True, "zigzag", dtype=torch.float32)
-    assert q.workspace_bytes() == 4 * (128 * 128 * 4) + 3 * (128 * 128 * 4 + 2 * 128 * 4) + SINK
+    assert q.workspace_bytes() == 4 * (128 * 128 * 4) + 3 * (128 * 128 * 4 + 2 * 128 * 4)
