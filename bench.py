@@ -276,16 +276,17 @@ def main():
         plan.set_merge(False)
         plan.set_recv("kernel")
         ms_blocks = {}
-        for nb in (256, 512, 1024, 2048, 0):
+        for nb in (64, 128, 256, 512, 1024):
             plan.set_recv_blocks(nb)
             ms_blocks[nb] = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
-        plan.set_recv_blocks(512 if args.recv_blocks is None else args.recv_blocks)
+        plan.set_recv_blocks(256 if args.recv_blocks is None else args.recv_blocks)
         recv_ms = {}
-        for mode in ("memcpy", "fused"):
+        for mode in ("memcpy", "fused", "kernel"):
             plan.set_recv(mode)
             recv_ms[mode] = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
-        plan.set_recv(args.recv or "fused")
-        result["modes_ms"] = {"overlapped_fused_merge": round(ms, 5), "serialized_fused_merge": round(ms_serial, 5),
+        plan.set_recv(args.recv or "kernel")
+        result["modes_ms"] = {"default_receive": args.recv or "kernel",
+                              "overlapped_fused_merge": round(ms, 5), "serialized_fused_merge": round(ms_serial, 5),
                               "overlapped_separate_merge": round(ms_sep, 5),
                               "receive_kernel_grid_blocks_ms": ms_blocks,
                               "receive_mode_ms": recv_ms,

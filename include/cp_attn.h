@@ -73,16 +73,17 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      1: separate LSE-merge kernel on the merge stream + finalize kernel */
 #define CP_ATTN_OPT_SERIALIZE 2   /* 0: copy/merge on side streams (default); 1: everything on the caller's stream */
 #define CP_ATTN_OPT_RECV 3        /* ring receive of step s+1 while step s computes:
-                                     2: inside step s's attention kernel, one 16-byte vector per
-                                        thread per tile (default; bf16 with head_dim 128 only,
-                                        otherwise as 1);
+                                     0: the library's copy kernel on the copy stream (default):
+                                        one-wave workgroups of 16 VGPRs that run beside the
+                                        attention kernel in the registers it leaves free;
                                      1: hipMemcpyAsync on the copy stream;
-                                     0: the library's non-temporal copy kernel on the copy stream */
+                                     2: inside step s's attention kernel (bf16 with head_dim
+                                        128 only, otherwise as 0) */
 #define CP_ATTN_OPT_POISON 4      /* 1: fill each receive slot / partial buffer with NaN once consumed */
 #define CP_ATTN_OPT_STEP_TIMING 5 /* 1: time every ring step's attention kernel with HIP events */
-#define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel (default 64; 0: one
-                                     workgroup per 16 KiB); a small grid shares the GPU with the
-                                     attention kernel it overlaps */
+#define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel (default 256; 0: one
+                                     workgroup per 128 vectors of 16 bytes); a small grid shares the
+                                     GPU with the attention kernel it overlaps */
 
 /*
  * Create a plan (host only: no device memory, no HIP call).

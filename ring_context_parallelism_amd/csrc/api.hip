@@ -202,7 +202,7 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
     if (fused_recv(p) && s + 1 < p.cp) CPA_HIP(launch_recv(recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1), 0, st));
     return CP_ATTN_OK;
   }
-  const int bm = bf16 ? attn_bf16_block_m() : attn_f32_block_m();
+  const int bm = bf16 ? attn_bf16_block_m(p.head_dim) : attn_f32_block_m();
   StepArgs a{};
   a.q = q;
   const int32_t split = int32_t(p.layout == 1 ? p.chunk : p.n_loc);

@@ -13,22 +13,23 @@
 // future sub-blocks of the same section.
 //
 // gfx950 mapping:
-//   * workgroup = 4 waves = 128 query rows of one head; wave w owns 32 rows.
+//   * workgroup = 8 waves = 256 query rows of one head for head_dim 128
+//     (4 waves = 128 rows for head_dim 64); wave w owns 32 rows.
 //   * scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: A = K from LDS (row = key), B = Q^T from
 //     registers (column = query).  The 32x32 result leaves every lane with 16
 //     keys of ONE query, so the row max and row sum are per-lane reductions
 //     plus a single exchange with the lane 32 away.
 //   * O^T = V^T P^T with the same instruction: B = P^T straight from the score
-//     registers (converted to bf16, round-to-nearest-even), A = V^T from LDS.
-//     V is transposed on its way into LDS and, within every 16-key group, the
-//     key order is permuted to match the order in which the score registers
-//     hold keys, so P never leaves registers.
-//   * K/V tiles of 64 keys are fetched with buffer loads (hardware range
-//     check: keys past the slot read as zero) two tiles ahead into registers,
-//     then written to a double-buffered LDS tile (K row-major, V transposed);
-//     16-byte padded rows keep the matrix-operand reads bank-conflict free and
-//     the transposed V writes are spread over distinct banks.
+//     registers (converted to bf16, round-to-nearest-even), A = V^T from LDS,
+//     with the keys of every 16-key group in the order in which the score
+//     registers hold them, so P never leaves registers.
+//   * K/V tiles of 64 keys come in with buffer loads (hardware range check:
+//     keys past the slot read as zero).  head_dim 64: into registers two
+//     tiles ahead, then into a double-buffered LDS tile (K row-major, V
+//     transposed; 16-byte padded rows keep the operand reads bank-conflict
+//     free).  head_dim 128: straight into a three-stage LDS ring, V row-major
+//     and read transposed (see the head_dim 128 kernel below).
 //   * softmax in base 2: p = exp2(s * scale * log2 e - m); the reference max m
 //     is only raised when a tile's max exceeds it by more than 8 (p <= 2^8 in
 //     between), which skips most O rescales and is exact for any choice of m.
@@ -315,7 +316,7 @@ void attn_step_bf16(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// head_dim 128: pipelined kernel with direct-to-LDS K/V.
+// head_dim 128: direct-to-LDS K/V, three LDS stages, eight waves.
 //
 //   * K/V tiles of 64 keys move global -> LDS with buffer_load ... lds (no
 //     register staging); each wave instruction fills four 256-byte rows, and
@@ -327,9 +328,9 @@ void attn_step_bf16(StepArgs a) {
 //     lane 4j + i/4 as its j-th value, so the 16 lanes that point at 4 key
 //     rows x 4 column pieces receive 4 keys of one head-dim column each --
 //     exactly the A operand of O^T = V^T P^T.
-//   * double-buffered LDS: tile j+1 is loaded while tile j computes; one
-//     barrier per tile.  Matrix operands are read from LDS in batches ahead
-//     of their MFMAs (all 16 K fragments of a tile; V in groups of four).
+//   * Matrix operands are read from LDS in batches ahead of their MFMAs (all
+//     16 K fragments of a tile; V in groups of four), pinned with
+//     scheduling-group barriers.
 // ---------------------------------------------------------------------------
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -357,19 +358,74 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no compiler reordering of memory accesses across
 }
 
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
-void attn_step_bf16_d128(StepArgs a) {
+// Buffer descriptor (raw, stride 0: offsets >= bytes read as zero) as four
+// scalar words, for the inline-assembly loads below.
+__device__ __forceinline__ u32x4 buffer_desc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  u32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  d[1] = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xffffu);
+  d[2] = __builtin_amdgcn_readfirstlane(bytes);
+  d[3] = 0x00020000u;
+  return d;
+}
+
+// 16 bytes per lane from buffer offset voff + soff straight into LDS at
+// lds + 16 lane (buffer_load_dwordx4 ... lds).  Issued as inline assembly so
+// the compiler neither tracks nor waits for it: the caller orders it with
+// explicit vmcnt waits and LDS barriers.  The memory clobber keeps the
+// compiler from caching LDS contents across it.  The compiler's hazard
+// checks do not look inside the assembly, so it carries its own wait states:
+// a vector-memory instruction must not read an SGPR a VALU instruction wrote
+// (v_readfirstlane, or v_readlane reloading a spilled SGPR) fewer than five
+// wait states earlier, nor M0 right after its write; s_nop 4 covers both.
+__device__ __forceinline__ void dma_lds16(u32x4 desc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const __attribute__((address_space(3))) void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Eight waves: 256 query rows per workgroup, 32 per wave (one workgroup per
+// CU, still two waves per SIMD).  Every K/V tile in LDS serves 256 rows, so
+// the loads per flop are half those of a four-wave workgroup, and the LDS
+// left free holds a third K/V stage: tile j+2 is loaded while tile j
+// computes, two tiles of latency.
+//
+// Ring receive (kRecv): the workgroup's share of the next step's K/V is cut
+// into ntiles + 2 slots; at the start of tile j every wave stores slot j
+// (loaded two tiles earlier) and loads slot j + 2, then issues the tile's K/V
+// loads.  Every wave issues exactly one copy store, one copy load and four
+// K/V loads per tile (lanes with nothing to copy repeat a vector of the share:
+// the same bytes to the same place; the K/V loads past the last tile repeat
+// the last tile), so the end-of-tile wait for tile j + 1 is a fixed count of
+// younger loads, vmcnt(5), and a copy access has two tiles to complete.
+// ---------------------------------------------------------------------------
+
+constexpr int kThreads8 = 512;
+constexpr int kBM8 = 256;
+
+template <bool kRecv>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8), amdgpu_waves_per_eu(2, 2)))
+void attn_step_bf16_d128x8(StepArgs a) {
   constexpr int D = 128, NT = 8, NB = 4;
-  // four separate LDS objects, so the compiler can tell that reads of one
-  // buffer do not alias the direct-to-LDS loads in flight to another
+  // 3 stages x K, V
   __shared__ __attribute__((aligned(1024))) uint8_t smem_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t smem_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_k2[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t smem_v0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t smem_v1[kTileBytes];
-  lds_u8* const kbuf0 = (lds_u8*)smem_k0;  // address-space casts of the shared arrays
-  lds_u8* const kbuf1 = (lds_u8*)smem_k1;
-  lds_u8* const vbuf0 = (lds_u8*)smem_v0;
-  lds_u8* const vbuf1 = (lds_u8*)smem_v1;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_v2[kTileBytes];
+  // ring-copy staging: 3 slots x 8 waves x 1 KiB
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_c[kRecv ? 3 * 8 * 1024 : 16];
+  lds_u8* const kst[3] = {(lds_u8*)smem_k0, (lds_u8*)smem_k1, (lds_u8*)smem_k2};
+  lds_u8* const vst[3] = {(lds_u8*)smem_v0, (lds_u8*)smem_v1, (lds_u8*)smem_v2};
+  lds_u8* const cstage = (lds_u8*)smem_c;
 
   int h, t;
   tile_of(blockIdx.x, gridDim.x, a.heads, a.total_tiles, h, t);
@@ -378,7 +434,7 @@ void attn_step_bf16_d128(StepArgs a) {
   const SegArgs& g = a.seg[si];
   const int epi = __builtin_amdgcn_readfirstlane(g.epi);  // scalar: the epilogue branches on it
   if (g.diag) t = g.tiles - 1 - t;  // longest rows first
-  const int row0 = t * kBM;
+  const int row0 = t * kBM8;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -386,7 +442,7 @@ void attn_step_bf16_d128(StepArgs a) {
   const int qc = lane & 31, hf = lane >> 5;
   const int row = row0 + wv * 32 + qc;
   const bool ok = row < g.q_len;
-  const int tile_last = min(row0 + kBM, g.q_len);
+  const int tile_last = min(row0 + kBM8, g.q_len);
   const int kv_end = g.kv_full + (g.diag ? tile_last : 0);
   const int w_first = row0 + wv * 32;
   const int w_last = min(w_first + 32, g.q_len);
@@ -407,36 +463,34 @@ void attn_step_bf16_d128(StepArgs a) {
   for (int b = 0; b < NB; ++b) o[b] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  // load mapping: wave wv, instruction n fills tile rows 16 wv + 4 n + lane/16;
-  // the lane's 16 bytes land in physical chunk lane%16 of that row.
-  // swz is linear over GF(2) and 4 n, lane/16 have disjoint bits, so the
-  // chunk of instruction n is (lane%16 ^ swz(lane/16)) ^ swz(4 n).
+  // load mapping: wave wv, instruction n fills tile rows 8 wv + 4 n + lane/16;
+  // the lane's 16 bytes land in physical chunk lane%16 of that row.  swz is
+  // linear over GF(2), and lane/16, 4 n and 8 (wv & 1) have disjoint bits, so
+  // the chunk of instruction n is (lane%16 ^ swz(lane/16) ^ swz(8 (wv & 1))) ^ swz(4 n).
   const uint32_t row_bytes = uint32_t(a.heads) * 256;
-  const int lrow0 = 16 * wv + (lane >> 4);
-  const uint32_t hbase = uint32_t(h) * 256 + (((lane & 15) ^ swz(lane >> 4)) << 4);
-  uint32_t vrow[4];  // per-lane byte offset of its chunk within a tile whose rows are contiguous
+  const int lrow0 = 8 * wv + (lane >> 4);
+  const uint32_t hbase = uint32_t(h) * 256 + (((lane & 15) ^ swz(lane >> 4) ^ swz(8 * (wv & 1))) << 4);
+  uint32_t vrow[2];  // per-lane byte offset of its chunk within a tile whose rows are contiguous
 #pragma unroll
-  for (int n = 0; n < 4; ++n) vrow[n] = uint32_t(lrow0 + 4 * n) * row_bytes + (hbase ^ (uint32_t(swz(4 * n)) << 4));
-  auto issue = [&](const void* src, int j0, lds_u8* dst) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, uint32_t(a.kv_bytes));
+  for (int n = 0; n < 2; ++n) vrow[n] = uint32_t(lrow0 + 4 * n) * row_bytes + (hbase ^ (uint32_t(swz(4 * n)) << 4));
+  const u32x4 desc_k = buffer_desc(a.k, uint32_t(a.kv_bytes));
+  const u32x4 desc_v = buffer_desc(a.v, uint32_t(a.kv_bytes));
+  auto issue = [&](const u32x4& desc, int j0, lds_u8* dst) {
     // Fast path: the 64 source rows are consecutive and inside the buffer, so
     // the tile base is one scalar offset.  Otherwise (a tile that crosses the
     // split between the two chunks, or the ragged last tile) each lane maps
     // its own row and clamps keys past the buffer to its last row (masked).
     const bool whole = j0 + kBN <= a.n_loc && (j0 + kBN <= a.kv_split || j0 >= a.kv_split);
     if (whole) {
-      const uint32_t soff = uint32_t(kv_row(a, j0)) * row_bytes;
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(uint32_t(kv_row(a, j0)) * row_bytes);
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (16 * wv + 4 * n) * 256),
-                                                 16, vrow[n], soff, 0, 0);
+      for (int n = 0; n < 2; ++n) dma_lds16(desc, vrow[n], soff, lds_addr(dst + (8 * wv + 4 * n) * 256));
     } else {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
+      for (int n = 0; n < 2; ++n) {
         const int kk = min(j0 + lrow0 + 4 * n, a.n_loc - 1);
         const uint32_t voff = uint32_t(kv_row(a, kk)) * row_bytes + (hbase ^ (uint32_t(swz(4 * n)) << 4));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (16 * wv + 4 * n) * 256),
-                                                 16, voff, 0, 0, 0);
+        dma_lds16(desc, voff, 0u, lds_addr(dst + (8 * wv + 4 * n) * 256));
       }
     }
   };
@@ -535,129 +589,122 @@ void attn_step_bf16_d128(StepArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // groups 2 and 3 MFMAs
   };
 
-  // In-kernel ring receive (a.recv.n > 0): this workgroup copies its share of
-  // the next step's K/V into the other receive slot, one 16-byte vector per
-  // thread per tile.  Right after each end-of-tile wait the vector loaded one
-  // tile earlier is stored and a new one is loaded into the other register
-  // buffer; the barrier that follows orders LDS only, so neither the store nor
-  // the load is waited for until the next end-of-tile wait.  Non-temporal
-  // accesses keep the copy out of the caches.
-  int64_t rstart[4];
-  int64_t rtot = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    rstart[i] = rtot;
-    rtot += i < a.recv.n ? a.recv.vec[i] : 0;
-  }
-  const int64_t rshare = (rtot + gridDim.x - 1) / gridDim.x;
-  int64_t rcur = min(rtot, int64_t(blockIdx.x) * rshare);
-  const int64_t rend = min(rtot, rcur + rshare);
-  // The range bases are pinned in scalar registers (an empty asm makes them
-  // opaque), so picking one is a few scalar selects rather than an indexed
-  // load from the argument block.
+  // ---- ring receive ----
+  // Workgroup b copies from one range, r = b mod n, an even share of that
+  // range among the workgroups assigned to it: the source and destination
+  // bases are then workgroup-uniform, picked once.  A grid with fewer
+  // workgroups than ranges copies whole ranges after the loop instead.
+  const int nr = max(a.recv.n, 1);
+  const bool whole_ranges = int(gridDim.x) < nr;
+  const int rr = int(blockIdx.x) % nr;
+  const int64_t rn = rr == 0 ? a.recv.vec[0] : rr == 1 ? a.recv.vec[1] : rr == 2 ? a.recv.vec[2] : a.recv.vec[3];
+  const int64_t rg = whole_ranges ? 1 : (int64_t(gridDim.x) - rr + nr - 1) / nr;  // workgroups copying range rr
+  const int64_t rsh = (rn + rg - 1) / rg;
+  const int64_t rbeg = whole_ranges ? 0 : min(rn, int64_t(blockIdx.x / nr) * rsh);
+  const int64_t rend = whole_ranges ? 0 : min(rn, rbeg + rsh);
   typedef __attribute__((address_space(1))) u32x4 g_u32x4;  // global memory: no flat accesses
-  const g_u32x4* rsb[4];
-  g_u32x4* rdb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    rsb[i] = (const g_u32x4*)(a.recv.src[i]);
-    rdb[i] = (g_u32x4*)(a.recv.dst[i]);
-    asm volatile("" : "+s"(rsb[i]), "+s"(rdb[i]));
-  }
-  auto recv_range = [&](int64_t i) { return int(i >= rstart[1]) + int(i >= rstart[2]) + int(i >= rstart[3]); };
-  auto recv_src = [&](int r) { return r == 0 ? rsb[0] : r == 1 ? rsb[1] : r == 2 ? rsb[2] : rsb[3]; };
-  auto recv_dst = [&](int r) { return r == 0 ? rdb[0] : r == 1 ? rdb[1] : r == 2 ? rdb[2] : rdb[3]; };
-  auto recv_base = [&](int r) { return r == 0 ? rstart[0] : r == 1 ? rstart[1] : r == 2 ? rstart[2] : rstart[3]; };
-  // addresses of vector i (< rend) when the range is not known to be uniform
-  auto recv_ptrs = [&](int64_t i, const g_u32x4*& src, g_u32x4*& dst) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t lo = rstart[r];
-      const int64_t hi = r < 3 ? rstart[r + 1] : rtot;
-      if (i >= lo && i < hi) {
-        src = rsb[r] + (i - lo);
-        dst = rdb[r] + (i - lo);
-      }
-    }
+  const void* const csrc_p = rr == 0 ? a.recv.src[0] : rr == 1 ? a.recv.src[1] : rr == 2 ? a.recv.src[2] : a.recv.src[3];
+  g_u32x4* const cdst = (g_u32x4*)(rr == 0 ? a.recv.dst[0] : rr == 1 ? a.recv.dst[1] : rr == 2 ? a.recv.dst[2] : a.recv.dst[3]);
+  const u32x4 desc_c = buffer_desc(csrc_p, uint32_t(rn * 16));
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+  // slots of the share: ntiles + 2, at most 512 vectors (one per lane) each;
+  // what does not fit is copied after the loop
+  const int64_t nslot = int64_t(ntiles) + 2;
+  const int64_t sv = min<int64_t>(kThreads8, (rend - rbeg + nslot - 1) / nslot);  // vectors per slot
+  const int64_t wvv = (sv + 7) / 8;                                                // per wave
+  // vector of this lane in slot c: its wave's part of the slot, lanes past it
+  // repeat the part's last vector; an empty part repeats the share's (or, for
+  // an empty share, the range's) last vector
+  auto slot_vec = [&](int64_t c) {
+    const int64_t lo = rbeg + c * sv + int64_t(wv) * wvv;
+    const int64_t hi = min(min(lo + wvv, rbeg + (c + 1) * sv), rend);
+    const int64_t fb = rend > rbeg ? rend - 1 : rn - 1;
+    return uint32_t(hi > lo ? min(lo + int64_t(lane), hi - 1) : fb);
   };
-  u32x4 rbuf[2] = {u32x4{}, u32x4{}};
-  g_u32x4* rdst[2] = {nullptr, nullptr};
-  auto recv_flush = [&](int b) {
-    if (rdst[b]) {
-      __builtin_nontemporal_store(rbuf[b], rdst[b]);
-      rdst[b] = nullptr;
-    }
+  // slot c goes HBM -> this wave's 1 KiB of LDS staging b at tile c - 2, and
+  // staging -> receive slot at tile c
+  auto copy_dma = [&](int64_t c, int b) {
+    dma_lds16(desc_c, slot_vec(c) * 16u, 0u, lds_addr(cstage + b * (8 * 1024) + wv * 1024));
   };
-  auto recv_load = [&](int b) {
-    if (rcur < rend) {
-      const int64_t i = rcur + tid;
-      const int64_t last = min(rend, rcur + kThreads) - 1;
-      const int r0 = recv_range(rcur);
-      const g_u32x4* src = nullptr;
-      g_u32x4* dst = nullptr;
-      if (r0 == recv_range(last)) {  // the block of 256 vectors lies in one range: scalar bases
-        const int64_t off = i - recv_base(r0);
-        src = recv_src(r0) + off;
-        dst = recv_dst(r0) + off;
-      } else {
-        recv_ptrs(i, src, dst);
-      }
-      if (i < rend) {
-        rdst[b] = dst;
-        rbuf[b] = __builtin_nontemporal_load(src);
-      }
-      rcur += kThreads;
-    }
+  auto copy_store = [&](int64_t c, int b) {
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+    const u32x4 x = *reinterpret_cast<lds_u32x4*>(cstage + b * (8 * 1024) + wv * 1024 + lane * 16);
+    __builtin_nontemporal_store(x, cdst + slot_vec(c));
   };
 
-  // K(j), V(j) live in kbuf[j & 1], vbuf[j & 1]; tile j+1 is loaded while
-  // tile j computes; one barrier per tile.
-  const int ntiles = (kv_end + kBN - 1) / kBN;
+  // Tile j's K/V live in stage j % 3.  Every load below is issued by
+  // dma_lds16, so the only waits are these: the prologue waits for all, the
+  // end of tile j for all but the tile's own loads (one copy load and four
+  // K/V loads; four without a receive), so that tile j + 1 and copy slot
+  // j + 1 have landed.  Loads complete in order among themselves, but a store
+  // may complete before older loads, so the count leaves out the tile's copy
+  // store: were it counted, an early store would let the wait pass with an
+  // older load still in flight.
   if (ntiles > 0) {
-    issue(a.k, 0, kbuf0);
-    issue(a.v, 0, vbuf0);
+    issue(desc_k, 0, kst[0]);
+    issue(desc_v, 0, vst[0]);
+    if constexpr (kRecv) {
+      copy_dma(0, 0);
+      copy_dma(1, 1);
+    }
+    issue(desc_k, min(1, ntiles - 1) * kBN, kst[1]);
+    issue(desc_v, min(1, ntiles - 1) * kBN, vst[1]);
   }
   wait_vmem();
-  recv_load(0);
   lds_barrier();
 
-#define CPATTN_STEP(J, PAR)                                                               \
-  do {                                                                                    \
-    const int j0_ = (J) * kBN;                                                            \
-    if ((J) + 1 < ntiles) {                                                               \
-      issue(a.k, j0_ + kBN, (PAR) ? kbuf0 : kbuf1);                                       \
-      issue(a.v, j0_ + kBN, (PAR) ? vbuf0 : vbuf1);                                       \
-    }                                                                                     \
-    if (j0_ < w_max) {                                                                    \
-      f32x16 s_[2];                                                                       \
-      bf16x8 pb_[2][2];                                                                   \
-      scores((PAR) ? kbuf1 : kbuf0, s_);                                                  \
-      softmax(s_, j0_, pb_);                                                              \
-      pv((PAR) ? vbuf1 : vbuf0, pb_);                                                     \
-    }                                                                                     \
-    wait_vmem();                                                                          \
-    recv_flush(PAR);                                                                      \
-    recv_load((PAR) ^ 1);                                                                 \
-    lds_barrier();                                                                        \
+#define CPATTN_X8_TILE(J, S)                                                               \
+  do {                                                                                     \
+    if constexpr (kRecv) {                                                                 \
+      copy_store(J, S);                                                                    \
+      copy_dma((J) + 2, ((S) + 2) % 3);                                                    \
+    }                                                                                      \
+    const int jn_ = min((J) + 2, ntiles - 1) * kBN;                                        \
+    issue(desc_k, jn_, kst[((S) + 2) % 3]);                                                \
+    issue(desc_v, jn_, vst[((S) + 2) % 3]);                                                \
+    const int j0_ = (J) * kBN;                                                             \
+    if (j0_ < w_max) {                                                                     \
+      f32x16 s_[2];                                                                        \
+      bf16x8 pb_[2][2];                                                                    \
+      scores(kst[S], s_);                                                                  \
+      softmax(s_, j0_, pb_);                                                               \
+      pv(vst[S], pb_);                                                                     \
+    }                                                                                      \
+    if constexpr (kRecv)                                                                   \
+      __builtin_amdgcn_s_waitcnt(0x0F75); /* vmcnt(5) */                                   \
+    else                                                                                   \
+      __builtin_amdgcn_s_waitcnt(0x0F74); /* vmcnt(4) */                                   \
+    lds_barrier();                                                                         \
   } while (0)
 
   int j = 0;
-  for (; j + 1 < ntiles; j += 2) {
-    CPATTN_STEP(j, 0);
-    CPATTN_STEP(j + 1, 1);
+  for (; j + 2 < ntiles; j += 3) {
+    CPATTN_X8_TILE(j, 0);
+    CPATTN_X8_TILE(j + 1, 1);
+    CPATTN_X8_TILE(j + 2, 2);
   }
-  if (j < ntiles) CPATTN_STEP(j, 0);
-#undef CPATTN_STEP
-  // rest of the receive share (workgroups with few tiles)
-  recv_flush(0);
-  recv_flush(1);
-  for (; rcur < rend; rcur += kThreads) {
-    const int64_t i = rcur + tid;
-    if (i < rend) {
-      const g_u32x4* src = nullptr;
-      g_u32x4* dst = nullptr;
-      recv_ptrs(i, src, dst);
-      __builtin_nontemporal_store(__builtin_nontemporal_load(src), dst);
+  if (j < ntiles) CPATTN_X8_TILE(j, 0);
+  if (j + 1 < ntiles) CPATTN_X8_TILE(j + 1, 1);
+#undef CPATTN_X8_TILE
+
+  wait_vmem();
+  if constexpr (kRecv) {
+    // the last two slots (loaded at the last two tiles, or in the prologue),
+    // then what did not fit in the slots
+    if (ntiles > 0) {
+      copy_store(ntiles, ntiles % 3);
+      copy_store(ntiles + 1, (ntiles + 1) % 3);
+    }
+    const g_u32x4* const csrc = (const g_u32x4*)csrc_p;
+    for (int64_t i = rbeg + (ntiles > 0 ? nslot : 0) * sv + tid; i < rend; i += kThreads8)
+      __builtin_nontemporal_store(__builtin_nontemporal_load(csrc + i), cdst + i);
+    if (whole_ranges) {
+      for (int r = int(blockIdx.x); r < a.recv.n; r += int(gridDim.x)) {
+        const g_u32x4* const src = (const g_u32x4*)(a.recv.src[r]);
+        g_u32x4* const dst = (g_u32x4*)(a.recv.dst[r]);
+        for (int64_t i = tid; i < a.recv.vec[r]; i += kThreads8)
+          __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+      }
     }
   }
 
@@ -686,14 +733,17 @@ void attn_step_bf16_d128(StepArgs a) {
 
 }  // namespace
 
-int attn_bf16_block_m() { return kBM; }
+int attn_bf16_block_m(int head_dim) { return head_dim == 128 ? kBM8 : kBM; }
 
 bool attn_does_recv(int dtype_bf16, int head_dim) { return dtype_bf16 && head_dim == 128; }
 
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid(unsigned(a.total_tiles) * unsigned(a.heads));
   if (head_dim == 128) {
-    attn_step_bf16_d128<<<grid, kThreads, 0, stream>>>(a);
+    if (a.recv.n > 0)
+      attn_step_bf16_d128x8<true><<<grid, kThreads8, 0, stream>>>(a);
+    else
+      attn_step_bf16_d128x8<false><<<grid, kThreads8, 0, stream>>>(a);
   } else {
     attn_step_bf16<64><<<grid, kThreads, 0, stream>>>(a);
   }

@@ -69,7 +69,7 @@ struct StepArgs {
 bool attn_does_recv(int dtype_bf16, int head_dim);
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_f32(const StepArgs& a, int head_dim, hipStream_t stream);
-int attn_bf16_block_m();
+int attn_bf16_block_m(int head_dim);
 int attn_f32_block_m();
 
 // Row copies between natural order and rank-local order.

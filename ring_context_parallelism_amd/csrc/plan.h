@@ -43,10 +43,10 @@ struct Plan {
   // options
   int32_t opt_merge = 0;
   int32_t opt_serialize = 0;
-  int32_t opt_recv = 2;
+  int32_t opt_recv = 0;
   int32_t opt_poison = 0;
   int32_t opt_step_timing = 0;
-  int32_t opt_recv_blocks = 64;
+  int32_t opt_recv_blocks = 256;
 
   DeviceState* dev = nullptr;
 

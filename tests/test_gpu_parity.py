@@ -257,7 +257,7 @@ def _sample_rows(seq, cp, layout, rank, rng, per_chunk=6):
     return np.unique(np.asarray(rows))
 
 
-@pytest.mark.parametrize("recv", ["memcpy", "fused"])
+@pytest.mark.parametrize("recv", ["kernel", "memcpy", "fused"])
 @pytest.mark.parametrize("name", [n for n in WORKLOADS if "fp32" not in n])
 def test_full_workload_sampled(name, recv):
     """The configuration the bench times, compared on sampled rows and heads."""
