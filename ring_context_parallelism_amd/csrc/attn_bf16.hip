@@ -415,16 +415,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8), amd
 void attn_step_bf16_d128x8(StepArgs a) {
   constexpr int D = 128, NT = 8, NB = 4;
   // 3 stages x K, V
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_k0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_k1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_k2[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_v0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_v1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_v2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_kv[3 * 2 * kTileBytes];
   // ring-copy staging: 3 slots x 8 waves x 1 KiB
   __shared__ __attribute__((aligned(1024))) uint8_t smem_c[kRecv ? 3 * 8 * 1024 : 16];
-  lds_u8* const kst[3] = {(lds_u8*)smem_k0, (lds_u8*)smem_k1, (lds_u8*)smem_k2};
-  lds_u8* const vst[3] = {(lds_u8*)smem_v0, (lds_u8*)smem_v1, (lds_u8*)smem_v2};
+  lds_u8* const kv_lds = (lds_u8*)smem_kv;
+  // stage s: K tile, then V tile
+  auto kst = [&](int st) { return kv_lds + st * (2 * kTileBytes); };
+  auto vst = [&](int st) { return kv_lds + st * (2 * kTileBytes) + kTileBytes; };
   lds_u8* const cstage = (lds_u8*)smem_c;
 
   int h, t;
@@ -537,12 +534,19 @@ void attn_step_bf16_d128x8(StepArgs a) {
           if (key >= prefix) s[kb][i] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // two independent chains (one per 32-key block), then the lane 32 away
+    // through v_permlane32_swap (a VALU exchange, no LDS round trip)
+    float mx0 = s[0][0], mx1 = s[1][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int i = 1; i < 16; ++i) {
+      mx0 = fmaxf(mx0, s[0][i]);
+      mx1 = fmaxf(mx1, s[1][i]);
+    }
+    float mx = fmaxf(mx0, mx1);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float mt = mx * a.scale_log2;
     if (__any(mt > m + kRescaleSlack)) {
       const float mn = fmaxf(m, mt);
@@ -553,14 +557,16 @@ void attn_step_bf16_d128x8(StepArgs a) {
       m = mn;
     }
     const float mref = (m == -INFINITY) ? 0.f : m;
+    float lk[2] = {0.f, 0.f};  // two partial row sums: half the dependent adds
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -mref));
-        l += p;
+        lk[kb] += p;
         pb[kb][i >> 3][i & 7] = static_cast<__bf16>(p);
       }
+    l += lk[0] + lk[1];
   };
   auto pv = [&](const lds_u8* vt, const bf16x8 (&pb)[2][2]) {
     // four groups (kb, u) of four head-dim blocks; group g+1's transposed
@@ -641,51 +647,100 @@ void attn_step_bf16_d128x8(StepArgs a) {
   // store: were it counted, an early store would let the wait pass with an
   // older load still in flight.
   if (ntiles > 0) {
-    issue(desc_k, 0, kst[0]);
-    issue(desc_v, 0, vst[0]);
+    issue(desc_k, 0, kst(0));
+    issue(desc_v, 0, vst(0));
     if constexpr (kRecv) {
       copy_dma(0, 0);
       copy_dma(1, 1);
     }
-    issue(desc_k, min(1, ntiles - 1) * kBN, kst[1]);
-    issue(desc_v, min(1, ntiles - 1) * kBN, vst[1]);
+    issue(desc_k, min(1, ntiles - 1) * kBN, kst(1));
+    issue(desc_v, min(1, ntiles - 1) * kBN, vst(1));
   }
   wait_vmem();
   lds_barrier();
 
-#define CPATTN_X8_TILE(J, S)                                                               \
+  // Ping-pong: the two waves of a SIMD (wave w and wave w + 4) work half a
+  // tile apart, so that one runs its score MFMAs while the other runs its
+  // softmax and product.  A tile has two phases between workgroup barriers:
+  //   waves 0-3: phase 1 scores of tile j;  phase 2 softmax + product of tile j
+  //   waves 4-7: phase 1 softmax + product of tile j - 1;  phase 2 scores of tile j
+  // The loads of tile j + 2 go out after the mid-tile barrier, once the stage
+  // they overwrite (tile j - 1) has been read for the last time.  Each group
+  // runs its own copy of the loop (the barriers pair up by count, not by
+  // address), so each copy's registers follow its own live values.  The stage
+  // index is a loop variable: unrolling by three to make it a constant needs
+  // three sets of stage addresses and spills the Q fragments.
+#define CPATTN_X8_LOADS(J, S)                                                              \
+  do {                                                                                     \
+    const int jn_ = min((J) + 2, ntiles - 1) * kBN;                                        \
+    issue(desc_k, jn_, kst(((S) + 2) % 3));                                                \
+    issue(desc_v, jn_, vst(((S) + 2) % 3));                                                \
+  } while (0)
+#define CPATTN_X8_COPY(J, S)                                                               \
   do {                                                                                     \
     if constexpr (kRecv) {                                                                 \
       copy_store(J, S);                                                                    \
       copy_dma((J) + 2, ((S) + 2) % 3);                                                    \
     }                                                                                      \
-    const int jn_ = min((J) + 2, ntiles - 1) * kBN;                                        \
-    issue(desc_k, jn_, kst[((S) + 2) % 3]);                                                \
-    issue(desc_v, jn_, vst[((S) + 2) % 3]);                                                \
-    const int j0_ = (J) * kBN;                                                             \
-    if (j0_ < w_max) {                                                                     \
-      f32x16 s_[2];                                                                        \
-      bf16x8 pb_[2][2];                                                                    \
-      scores(kst[S], s_);                                                                  \
-      softmax(s_, j0_, pb_);                                                               \
-      pv(vst[S], pb_);                                                                     \
-    }                                                                                      \
+  } while (0)
+#define CPATTN_X8_END()                                                                    \
+  do {                                                                                     \
     if constexpr (kRecv)                                                                   \
       __builtin_amdgcn_s_waitcnt(0x0F75); /* vmcnt(5) */                                   \
     else                                                                                   \
       __builtin_amdgcn_s_waitcnt(0x0F74); /* vmcnt(4) */                                   \
     lds_barrier();                                                                         \
   } while (0)
+#define CPATTN_X8_TILE_A(J, S)                                                             \
+  do {                                                                                     \
+    CPATTN_X8_COPY(J, S);                                                                  \
+    const int j0_ = (J) * kBN;                                                             \
+    f32x16 s_[2];                                                                          \
+    if (j0_ < w_max) scores(kst(S), s_);                                                   \
+    lds_barrier();                                                                         \
+    CPATTN_X8_LOADS(J, S);                                                                 \
+    if (j0_ < w_max) {                                                                     \
+      bf16x8 pb_[2][2];                                                                    \
+      softmax(s_, j0_, pb_);                                                               \
+      pv(vst(S), pb_);                                                                     \
+    }                                                                                      \
+    CPATTN_X8_END();                                                                       \
+  } while (0)
+#define CPATTN_X8_TILE_B(J, S)                                                             \
+  do {                                                                                     \
+    CPATTN_X8_COPY(J, S);                                                                  \
+    const int j0_ = (J) * kBN;                                                             \
+    if ((J) > 0 && j0_ - kBN < w_max) {                                                    \
+      bf16x8 pb_[2][2];                                                                    \
+      softmax(sb_, j0_ - kBN, pb_);                                                        \
+      pv(vst(((S) + 2) % 3), pb_);                                                         \
+    }                                                                                      \
+    lds_barrier();                                                                         \
+    CPATTN_X8_LOADS(J, S);                                                                 \
+    if (j0_ < w_max) scores(kst(S), sb_);                                                  \
+    CPATTN_X8_END();                                                                       \
+  } while (0)
 
-  int j = 0;
-  for (; j + 2 < ntiles; j += 3) {
-    CPATTN_X8_TILE(j, 0);
-    CPATTN_X8_TILE(j + 1, 1);
-    CPATTN_X8_TILE(j + 2, 2);
+  if (wv < 4) {
+    int j = 0;
+    for (int st = 0; j < ntiles; ++j, st = st == 2 ? 0 : st + 1) CPATTN_X8_TILE_A(j, st);
+  } else {
+    f32x16 sb_[2];  // scores of the tile whose softmax comes in the next phase
+    int j = 0;
+    for (int st = 0; j < ntiles; ++j, st = st == 2 ? 0 : st + 1) CPATTN_X8_TILE_B(j, st);
+    // softmax and product of the last tile (its stage is not overwritten: the
+    // loads issued at the last tile went to another stage)
+    if (ntiles > 0 && (ntiles - 1) * kBN < w_max) {
+      bf16x8 pb_[2][2];
+      softmax(sb_, (ntiles - 1) * kBN, pb_);
+      pv(vst((ntiles - 1) % 3), pb_);
+    }
   }
-  if (j < ntiles) CPATTN_X8_TILE(j, 0);
-  if (j + 1 < ntiles) CPATTN_X8_TILE(j + 1, 1);
-#undef CPATTN_X8_TILE
+#undef CPATTN_X8_TILE_B
+#undef CPATTN_X8_TILE_A
+#undef CPATTN_X8_END
+#undef CPATTN_X8_COPY
+#undef CPATTN_X8_LOADS
 
   wait_vmem();
   if constexpr (kRecv) {
