@@ -414,8 +414,8 @@ template <bool kRecv>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8), amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16_d128x8(StepArgs a) {
   constexpr int D = 128, NT = 8, NB = 4;
-  // 3 stages x K, V
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_kv[3 * 2 * kTileBytes];
+  // 4 stages x K, V
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_kv[4 * 2 * kTileBytes];
   // ring-copy staging: 3 slots x 8 waves x 1 KiB
   __shared__ __attribute__((aligned(1024))) uint8_t smem_c[kRecv ? 3 * 8 * 1024 : 16];
   lds_u8* const kv_lds = (lds_u8*)smem_kv;
@@ -460,16 +460,17 @@ void attn_step_bf16_d128x8(StepArgs a) {
   for (int b = 0; b < NB; ++b) o[b] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  // load mapping: wave wv, instruction n fills tile rows 8 wv + 4 n + lane/16;
-  // the lane's 16 bytes land in physical chunk lane%16 of that row.  swz is
-  // linear over GF(2), and lane/16, 4 n and 8 (wv & 1) have disjoint bits, so
-  // the chunk of instruction n is (lane%16 ^ swz(lane/16) ^ swz(8 (wv & 1))) ^ swz(4 n).
+  // load mapping (waves 0-3 load every tile): wave wv, instruction n fills
+  // tile rows 16 wv + 4 n + lane/16; the lane's 16 bytes land in physical
+  // chunk lane%16 of that row.  swz is linear over GF(2) and reads the row's
+  // low four bits only, and lane/16 and 4 n have disjoint bits, so the chunk
+  // of instruction n is (lane%16 ^ swz(lane/16)) ^ swz(4 n).
   const uint32_t row_bytes = uint32_t(a.heads) * 256;
-  const int lrow0 = 8 * wv + (lane >> 4);
-  const uint32_t hbase = uint32_t(h) * 256 + (((lane & 15) ^ swz(lane >> 4) ^ swz(8 * (wv & 1))) << 4);
-  uint32_t vrow[2];  // per-lane byte offset of its chunk within a tile whose rows are contiguous
+  const int lrow0 = 16 * (wv & 3) + (lane >> 4);
+  const uint32_t hbase = uint32_t(h) * 256 + (((lane & 15) ^ swz(lane >> 4)) << 4);
+  uint32_t vrow[4];  // per-lane byte offset of its chunk within a tile whose rows are contiguous
 #pragma unroll
-  for (int n = 0; n < 2; ++n) vrow[n] = uint32_t(lrow0 + 4 * n) * row_bytes + (hbase ^ (uint32_t(swz(4 * n)) << 4));
+  for (int n = 0; n < 4; ++n) vrow[n] = uint32_t(lrow0 + 4 * n) * row_bytes + (hbase ^ (uint32_t(swz(4 * n)) << 4));
   const u32x4 desc_k = buffer_desc(a.k, uint32_t(a.kv_bytes));
   const u32x4 desc_v = buffer_desc(a.v, uint32_t(a.kv_bytes));
   auto issue = [&](const u32x4& desc, int j0, lds_u8* dst) {
@@ -481,13 +482,13 @@ void attn_step_bf16_d128x8(StepArgs a) {
     if (whole) {
       const uint32_t soff = __builtin_amdgcn_readfirstlane(uint32_t(kv_row(a, j0)) * row_bytes);
 #pragma unroll
-      for (int n = 0; n < 2; ++n) dma_lds16(desc, vrow[n], soff, lds_addr(dst + (8 * wv + 4 * n) * 256));
+      for (int n = 0; n < 4; ++n) dma_lds16(desc, vrow[n], soff, lds_addr(dst + (16 * (wv & 3) + 4 * n) * 256));
     } else {
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      for (int n = 0; n < 4; ++n) {
         const int kk = min(j0 + lrow0 + 4 * n, a.n_loc - 1);
         const uint32_t voff = uint32_t(kv_row(a, kk)) * row_bytes + (hbase ^ (uint32_t(swz(4 * n)) << 4));
-        dma_lds16(desc, voff, 0u, lds_addr(dst + (8 * wv + 4 * n) * 256));
+        dma_lds16(desc, voff, 0u, lds_addr(dst + (16 * (wv & 3) + 4 * n) * 256));
       }
     }
   };
@@ -638,23 +639,27 @@ void attn_step_bf16_d128x8(StepArgs a) {
     __builtin_nontemporal_store(x, cdst + slot_vec(c));
   };
 
-  // Tile j's K/V live in stage j % 3.  Every load below is issued by
-  // dma_lds16, so the only waits are these: the prologue waits for all, the
-  // end of tile j for all but the tile's own loads (one copy load and four
-  // K/V loads; four without a receive), so that tile j + 1 and copy slot
-  // j + 1 have landed.  Loads complete in order among themselves, but a store
-  // may complete before older loads, so the count leaves out the tile's copy
+  // Tile j's K/V live in stage j % 4; waves 0-3 load them (issue() above),
+  // tile j + 2 during tile j.  Every load below is issued by dma_lds16, so
+  // the only waits are these: the prologue waits for all, the end of tile j
+  // for all but the loads the wave issued during tile j (waves 0-3: one copy
+  // load and eight K/V loads, eight without a receive; waves 4-7: the copy
+  // load, none without a receive), so that tile j + 1 and copy slot j + 1
+  // have landed.  Loads complete in order among themselves, but a store may
+  // complete before older loads, so the count leaves out the tile's copy
   // store: were it counted, an early store would let the wait pass with an
   // older load still in flight.
   if (ntiles > 0) {
-    issue(desc_k, 0, kst(0));
-    issue(desc_v, 0, vst(0));
     if constexpr (kRecv) {
       copy_dma(0, 0);
       copy_dma(1, 1);
     }
-    issue(desc_k, min(1, ntiles - 1) * kBN, kst(1));
-    issue(desc_v, min(1, ntiles - 1) * kBN, vst(1));
+    if (wv < 4) {
+      issue(desc_k, 0, kst(0));
+      issue(desc_v, 0, vst(0));
+      issue(desc_k, min(1, ntiles - 1) * kBN, kst(1));
+      issue(desc_v, min(1, ntiles - 1) * kBN, vst(1));
+    }
   }
   wait_vmem();
   lds_barrier();
@@ -662,85 +667,81 @@ void attn_step_bf16_d128x8(StepArgs a) {
   // Ping-pong: the two waves of a SIMD (wave w and wave w + 4) work half a
   // tile apart, so that one runs its score MFMAs while the other runs its
   // softmax and product.  A tile has two phases between workgroup barriers:
-  //   waves 0-3: phase 1 scores of tile j;  phase 2 softmax + product of tile j
+  //   waves 0-3: phase 1 scores of tile j, then the loads of tile j + 2;
+  //              phase 2 softmax + product of tile j
   //   waves 4-7: phase 1 softmax + product of tile j - 1;  phase 2 scores of tile j
-  // The loads of tile j + 2 go out after the mid-tile barrier, once the stage
-  // they overwrite (tile j - 1) has been read for the last time.  Each group
-  // runs its own copy of the loop (the barriers pair up by count, not by
-  // address), so each copy's registers follow its own live values.  The stage
-  // index is a loop variable: unrolling by three to make it a constant needs
-  // three sets of stage addresses and spills the Q fragments.
-#define CPATTN_X8_LOADS(J, S)                                                              \
-  do {                                                                                     \
-    const int jn_ = min((J) + 2, ntiles - 1) * kBN;                                        \
-    issue(desc_k, jn_, kst(((S) + 2) % 3));                                                \
-    issue(desc_v, jn_, vst(((S) + 2) % 3));                                                \
-  } while (0)
-#define CPATTN_X8_COPY(J, S)                                                               \
+  // The loads go to stage (j + 2) % 4, whose tile (j - 2) was last read in
+  // phase 1 of tile j - 1.  They are issued by the waves that would otherwise
+  // wait at the mid-tile barrier: a direct-to-LDS load holds its wave at issue
+  // until the CU's address unit takes it, and 32 KiB of them issued at once
+  // from every wave stalled all eight.  Each group runs its own copy of the
+  // loop (the barriers pair up by count, not by address), so each copy's
+  // registers follow its own live values.  Stage and copy-staging indices are
+  // loop variables: unrolling to make them constants needs several sets of
+  // stage addresses and spills the Q fragments.
+#define CPATTN_X8_COPY(J, C)                                                               \
   do {                                                                                     \
     if constexpr (kRecv) {                                                                 \
-      copy_store(J, S);                                                                    \
-      copy_dma((J) + 2, ((S) + 2) % 3);                                                    \
+      copy_store(J, C);                                                                    \
+      copy_dma((J) + 2, (C) == 0 ? 2 : (C) - 1);                                           \
     }                                                                                      \
   } while (0)
-#define CPATTN_X8_END()                                                                    \
+#define CPATTN_X8_TILE_A(J, S, C)                                                          \
   do {                                                                                     \
-    if constexpr (kRecv)                                                                   \
-      __builtin_amdgcn_s_waitcnt(0x0F75); /* vmcnt(5) */                                   \
-    else                                                                                   \
-      __builtin_amdgcn_s_waitcnt(0x0F74); /* vmcnt(4) */                                   \
-    lds_barrier();                                                                         \
-  } while (0)
-#define CPATTN_X8_TILE_A(J, S)                                                             \
-  do {                                                                                     \
-    CPATTN_X8_COPY(J, S);                                                                  \
+    CPATTN_X8_COPY(J, C);                                                                  \
     const int j0_ = (J) * kBN;                                                             \
     f32x16 s_[2];                                                                          \
     if (j0_ < w_max) scores(kst(S), s_);                                                   \
+    {                                                                                      \
+      const int jn_ = min((J) + 2, ntiles - 1) * kBN;                                      \
+      issue(desc_k, jn_, kst(((S) + 2) & 3));                                              \
+      issue(desc_v, jn_, vst(((S) + 2) & 3));                                              \
+    }                                                                                      \
     lds_barrier();                                                                         \
-    CPATTN_X8_LOADS(J, S);                                                                 \
     if (j0_ < w_max) {                                                                     \
       bf16x8 pb_[2][2];                                                                    \
       softmax(s_, j0_, pb_);                                                               \
       pv(vst(S), pb_);                                                                     \
     }                                                                                      \
-    CPATTN_X8_END();                                                                       \
+    if constexpr (kRecv)                                                                   \
+      __builtin_amdgcn_s_waitcnt(0x0F79); /* vmcnt(9) */                                   \
+    else                                                                                   \
+      __builtin_amdgcn_s_waitcnt(0x0F78); /* vmcnt(8) */                                   \
+    lds_barrier();                                                                         \
   } while (0)
-#define CPATTN_X8_TILE_B(J, S)                                                             \
+#define CPATTN_X8_TILE_B(J, S, C)                                                          \
   do {                                                                                     \
-    CPATTN_X8_COPY(J, S);                                                                  \
+    CPATTN_X8_COPY(J, C);                                                                  \
     const int j0_ = (J) * kBN;                                                             \
     if ((J) > 0 && j0_ - kBN < w_max) {                                                    \
       bf16x8 pb_[2][2];                                                                    \
       softmax(sb_, j0_ - kBN, pb_);                                                        \
-      pv(vst(((S) + 2) % 3), pb_);                                                         \
+      pv(vst(((S) + 3) & 3), pb_);                                                         \
     }                                                                                      \
     lds_barrier();                                                                         \
-    CPATTN_X8_LOADS(J, S);                                                                 \
     if (j0_ < w_max) scores(kst(S), sb_);                                                  \
-    CPATTN_X8_END();                                                                       \
+    if constexpr (kRecv) __builtin_amdgcn_s_waitcnt(0x0F71); /* vmcnt(1) */                \
+    lds_barrier();                                                                         \
   } while (0)
 
   if (wv < 4) {
-    int j = 0;
-    for (int st = 0; j < ntiles; ++j, st = st == 2 ? 0 : st + 1) CPATTN_X8_TILE_A(j, st);
+    for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1)
+      CPATTN_X8_TILE_A(j, st, cb);
   } else {
     f32x16 sb_[2];  // scores of the tile whose softmax comes in the next phase
-    int j = 0;
-    for (int st = 0; j < ntiles; ++j, st = st == 2 ? 0 : st + 1) CPATTN_X8_TILE_B(j, st);
+    for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1)
+      CPATTN_X8_TILE_B(j, st, cb);
     // softmax and product of the last tile (its stage is not overwritten: the
-    // loads issued at the last tile went to another stage)
+    // loads issued at the last two tiles went to other stages)
     if (ntiles > 0 && (ntiles - 1) * kBN < w_max) {
       bf16x8 pb_[2][2];
       softmax(sb_, (ntiles - 1) * kBN, pb_);
-      pv(vst((ntiles - 1) % 3), pb_);
+      pv(vst((ntiles - 1) & 3), pb_);
     }
   }
 #undef CPATTN_X8_TILE_B
 #undef CPATTN_X8_TILE_A
-#undef CPATTN_X8_END
 #undef CPATTN_X8_COPY
-#undef CPATTN_X8_LOADS
 
   wait_vmem();
   if constexpr (kRecv) {
