@@ -535,38 +535,53 @@ void attn_step_bf16_d128x8(StepArgs a) {
           if (key >= prefix) s[kb][i] = -INFINITY;
         }
     }
-    // two independent chains (one per 32-key block), then the lane 32 away
-    // through v_permlane32_swap (a VALU exchange, no LDS round trip)
-    float mx0 = s[0][0], mx1 = s[1][0];
+    float lk[2];  // two partial row sums: half the dependent adds
+    auto exps = [&](float mref) {
+      lk[0] = lk[1] = 0.f;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      mx0 = fmaxf(mx0, s[0][i]);
-      mx1 = fmaxf(mx1, s[1][i]);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -mref));
+          lk[kb] += p;
+          pb[kb][i >> 3][i & 7] = static_cast<__bf16>(p);
+        }
+    };
+    // Fast path: exponentiate against the running reference max without
+    // taking the tile's max.  It stands if no probability exceeds
+    // 2^kRescaleSlack, which a lane's tile sum of at most that guarantees
+    // (the terms are not negative; an overflow makes the sum infinite).
+    // Otherwise, and before any reference exists, the tile's max is taken,
+    // the reference moves up to it and the exponentials are redone.
+    bool redo = __any(m == -INFINITY);
+    if (!redo) {
+      exps(m);
+      redo = __any(lk[0] + lk[1] > exp2f(kRescaleSlack));
     }
-    float mx = fmaxf(mx0, mx1);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mt = mx * a.scale_log2;
-    if (__any(mt > m + kRescaleSlack)) {
-      const float mn = fmaxf(m, mt);
-      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-      l *= alpha;
+    if (redo) {
+      // two independent chains (one per 32-key block), then the lane 32 away
+      // through v_permlane32_swap (a VALU exchange, no LDS round trip)
+      float mx0 = s[0][0], mx1 = s[1][0];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) o[b] *= alpha;
-      m = mn;
-    }
-    const float mref = (m == -INFINITY) ? 0.f : m;
-    float lk[2] = {0.f, 0.f};  // two partial row sums: half the dependent adds
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -mref));
-        lk[kb] += p;
-        pb[kb][i >> 3][i & 7] = static_cast<__bf16>(p);
+      for (int i = 1; i < 16; ++i) {
+        mx0 = fmaxf(mx0, s[0][i]);
+        mx1 = fmaxf(mx1, s[1][i]);
       }
+      float mx = fmaxf(mx0, mx1);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float mn = fmaxf(m, mx * a.scale_log2);
+      if (__any(mn > m)) {
+        const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) o[b] *= alpha;
+        m = mn;
+      }
+      exps(m == -INFINITY ? 0.f : m);
+    }
     l += lk[0] + lk[1];
   };
   auto pv = [&](const lds_u8* vt, const bf16x8 (&pb)[2][2]) {
@@ -639,46 +654,45 @@ void attn_step_bf16_d128x8(StepArgs a) {
     __builtin_nontemporal_store(x, cdst + slot_vec(c));
   };
 
-  // Tile j's K/V live in stage j % 4; waves 0-3 load them (issue() above),
-  // tile j + 2 during tile j.  Every load below is issued by dma_lds16, so
-  // the only waits are these: the prologue waits for all, the end of tile j
-  // for all but the loads the wave issued during tile j (waves 0-3: one copy
-  // load and eight K/V loads, eight without a receive; waves 4-7: the copy
-  // load, none without a receive), so that tile j + 1 and copy slot j + 1
-  // have landed.  Loads complete in order among themselves, but a store may
-  // complete before older loads, so the count leaves out the tile's copy
-  // store: were it counted, an early store would let the wait pass with an
-  // older load still in flight.
+  // Tile j's K/V live in stage j % 4; waves 0-3 load the K tiles and waves
+  // 4-7 the V tiles (issue() above), tile j + 2 during tile j.  Every load
+  // below is issued by dma_lds16, so the only waits are these: the prologue
+  // waits for all, the end of tile j for all but the loads the wave issued
+  // during tile j (one copy load and four tile loads; four without a
+  // receive), so that tile j + 1 and copy slot j + 1 have landed.  Loads
+  // complete in order among themselves, but a store may complete before
+  // older loads, so the count leaves out the tile's copy store: were it
+  // counted, an early store would let the wait pass with an older load still
+  // in flight.
   if (ntiles > 0) {
     if constexpr (kRecv) {
       copy_dma(0, 0);
       copy_dma(1, 1);
     }
-    if (wv < 4) {
-      issue(desc_k, 0, kst(0));
-      issue(desc_v, 0, vst(0));
-      issue(desc_k, min(1, ntiles - 1) * kBN, kst(1));
-      issue(desc_v, min(1, ntiles - 1) * kBN, vst(1));
-    }
+    const u32x4& desc = wv < 4 ? desc_k : desc_v;
+    issue(desc, 0, wv < 4 ? kst(0) : vst(0));
+    issue(desc, min(1, ntiles - 1) * kBN, wv < 4 ? kst(1) : vst(1));
   }
   wait_vmem();
   lds_barrier();
 
-  // Ping-pong: the two waves of a SIMD (wave w and wave w + 4) work half a
-  // tile apart, so that one runs its score MFMAs while the other runs its
-  // softmax and product.  A tile has two phases between workgroup barriers:
-  //   waves 0-3: phase 1 scores of tile j, then the loads of tile j + 2;
-  //              phase 2 softmax + product of tile j
-  //   waves 4-7: phase 1 softmax + product of tile j - 1;  phase 2 scores of tile j
-  // The loads go to stage (j + 2) % 4, whose tile (j - 2) was last read in
-  // phase 1 of tile j - 1.  They are issued by the waves that would otherwise
-  // wait at the mid-tile barrier: a direct-to-LDS load holds its wave at issue
-  // until the CU's address unit takes it, and 32 KiB of them issued at once
-  // from every wave stalled all eight.  Each group runs its own copy of the
-  // loop (the barriers pair up by count, not by address), so each copy's
-  // registers follow its own live values.  Stage and copy-staging indices are
-  // loop variables: unrolling to make them constants needs several sets of
-  // stage addresses and spills the Q fragments.
+  // Ping-pong: the two waves of a SIMD (wave w and wave w + 4) run half a
+  // tile apart, so that one runs its MFMAs while the other runs its softmax.
+  // A tile has two phases between workgroup barriers:
+  //   waves 0-3: phase 1 product of tile j - 1 and scores of tile j;
+  //              phase 2 softmax of tile j, loads of K tile j + 2
+  //   waves 4-7: phase 1 softmax of tile j - 1, loads of V tile j + 2;
+  //              phase 2 product of tile j - 1 and scores of tile j
+  // so each phase holds one group's 32 MFMAs and the other's softmax.  The
+  // loads go to stage (j + 2) % 4: its K tile (j - 2) was last read in tile
+  // j - 2 and its V tile in tile j - 1.  A direct-to-LDS load holds its wave
+  // at issue until the CU's address unit takes it, so the loads come from
+  // the group that runs the softmax, which finishes before the other group's
+  // MFMAs.  Each group runs its own copy of the loop (the barriers pair up by
+  // count, not by address), so each copy's registers follow its own live
+  // values.  Stage and copy-staging indices are loop variables: unrolling to
+  // make them constants needs several sets of stage addresses and spills the
+  // Q fragments.
 #define CPATTN_X8_COPY(J, C)                                                               \
   do {                                                                                     \
     if constexpr (kRecv) {                                                                 \
@@ -686,61 +700,54 @@ void attn_step_bf16_d128x8(StepArgs a) {
       copy_dma((J) + 2, (C) == 0 ? 2 : (C) - 1);                                           \
     }                                                                                      \
   } while (0)
-#define CPATTN_X8_TILE_A(J, S, C)                                                          \
+  // the MFMA phase of tile J: product of tile J - 1 (probabilities pb_),
+  // scores of tile J into s_
+#define CPATTN_X8_GEMMS(J, S, s_, pb_)                                                     \
   do {                                                                                     \
-    CPATTN_X8_COPY(J, C);                                                                  \
-    const int j0_ = (J) * kBN;                                                             \
-    f32x16 s_[2];                                                                          \
-    if (j0_ < w_max) scores(kst(S), s_);                                                   \
-    {                                                                                      \
-      const int jn_ = min((J) + 2, ntiles - 1) * kBN;                                      \
-      issue(desc_k, jn_, kst(((S) + 2) & 3));                                              \
-      issue(desc_v, jn_, vst(((S) + 2) & 3));                                              \
-    }                                                                                      \
-    lds_barrier();                                                                         \
-    if (j0_ < w_max) {                                                                     \
-      bf16x8 pb_[2][2];                                                                    \
-      softmax(s_, j0_, pb_);                                                               \
-      pv(vst(S), pb_);                                                                     \
-    }                                                                                      \
-    if constexpr (kRecv)                                                                   \
-      __builtin_amdgcn_s_waitcnt(0x0F79); /* vmcnt(9) */                                   \
-    else                                                                                   \
-      __builtin_amdgcn_s_waitcnt(0x0F78); /* vmcnt(8) */                                   \
-    lds_barrier();                                                                         \
+    const bool sc_ = (J) * kBN < w_max;                                                    \
+    const bool pv_ = (J) > 0 && ((J) - 1) * kBN < w_max;                                   \
+    if (pv_) pv(vst(((S) + 3) & 3), pb_);                                                  \
+    if (sc_) scores(kst(S), s_);                                                           \
   } while (0)
-#define CPATTN_X8_TILE_B(J, S, C)                                                          \
+#define CPATTN_X8_END()                                                                    \
   do {                                                                                     \
-    CPATTN_X8_COPY(J, C);                                                                  \
-    const int j0_ = (J) * kBN;                                                             \
-    if ((J) > 0 && j0_ - kBN < w_max) {                                                    \
-      bf16x8 pb_[2][2];                                                                    \
-      softmax(sb_, j0_ - kBN, pb_);                                                        \
-      pv(vst(((S) + 3) & 3), pb_);                                                         \
-    }                                                                                      \
-    lds_barrier();                                                                         \
-    if (j0_ < w_max) scores(kst(S), sb_);                                                  \
-    if constexpr (kRecv) __builtin_amdgcn_s_waitcnt(0x0F71); /* vmcnt(1) */                \
+    if constexpr (kRecv)                                                                   \
+      __builtin_amdgcn_s_waitcnt(0x0F75); /* vmcnt(5) */                                   \
+    else                                                                                   \
+      __builtin_amdgcn_s_waitcnt(0x0F74); /* vmcnt(4) */                                   \
     lds_barrier();                                                                         \
   } while (0)
 
+  bf16x8 pb_[2][2];  // probabilities of the last softmaxed tile
+  f32x16 s_[2];      // scores of the last scored tile
   if (wv < 4) {
-    for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1)
-      CPATTN_X8_TILE_A(j, st, cb);
+    for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
+      CPATTN_X8_COPY(j, cb);
+      CPATTN_X8_GEMMS(j, st, s_, pb_);
+      lds_barrier();
+      if (j * kBN < w_max) softmax(s_, j * kBN, pb_);
+      issue(desc_k, min(j + 2, ntiles - 1) * kBN, kst((st + 2) & 3));
+      CPATTN_X8_END();
+    }
+    // product of the last tile (its stage is not overwritten: the loads
+    // issued at the last two tiles went to other stages)
+    if (ntiles > 0 && (ntiles - 1) * kBN < w_max) pv(vst((ntiles - 1) & 3), pb_);
   } else {
-    f32x16 sb_[2];  // scores of the tile whose softmax comes in the next phase
-    for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1)
-      CPATTN_X8_TILE_B(j, st, cb);
-    // softmax and product of the last tile (its stage is not overwritten: the
-    // loads issued at the last two tiles went to other stages)
+    for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
+      CPATTN_X8_COPY(j, cb);
+      if (j > 0 && (j - 1) * kBN < w_max) softmax(s_, (j - 1) * kBN, pb_);
+      issue(desc_v, min(j + 2, ntiles - 1) * kBN, vst((st + 2) & 3));
+      lds_barrier();
+      CPATTN_X8_GEMMS(j, st, s_, pb_);
+      CPATTN_X8_END();
+    }
     if (ntiles > 0 && (ntiles - 1) * kBN < w_max) {
-      bf16x8 pb_[2][2];
-      softmax(sb_, (ntiles - 1) * kBN, pb_);
+      softmax(s_, (ntiles - 1) * kBN, pb_);
       pv(vst((ntiles - 1) & 3), pb_);
     }
   }
-#undef CPATTN_X8_TILE_B
-#undef CPATTN_X8_TILE_A
+#undef CPATTN_X8_END
+#undef CPATTN_X8_GEMMS
 #undef CPATTN_X8_COPY
 
   wait_vmem();
