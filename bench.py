@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip imbalance / mode / parity side measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--recv", choices=["kernel", "memcpy", "fused"], default=None, help="ring receive path (default: library's)")
+    ap.add_argument("--recv", choices=["kernel", "memcpy", "fused", "hybrid"], default=None, help="ring receive path (default: library's)")
     ap.add_argument("--recv-blocks", type=int, default=None, help="grid bound of the receive copy kernel")
     ap.add_argument("--serialize", action="store_true", help="run the whole schedule on one stream")
     ap.add_argument("--copy-probe", action="store_true",
@@ -281,7 +281,7 @@ def main():
             ms_blocks[nb] = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
         plan.set_recv_blocks(256 if args.recv_blocks is None else args.recv_blocks)
         recv_ms = {}
-        for mode in ("memcpy", "fused", "kernel"):
+        for mode in ("memcpy", "fused", "hybrid", "kernel"):
             plan.set_recv(mode)
             recv_ms[mode] = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
         plan.set_recv(args.recv or "kernel")

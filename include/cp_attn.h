@@ -78,7 +78,9 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                         attention kernel in the registers it leaves free;
                                      1: hipMemcpyAsync on the copy stream;
                                      2: inside step s's attention kernel (bf16 with head_dim
-                                        128 only, otherwise as 0) */
+                                        128 only, otherwise as 0);
+                                     3: as 0 for step 0 (receive of step 1), then as 2: no
+                                        cross-stream event after step 1 */
 #define CP_ATTN_OPT_POISON 4      /* 1: fill each receive slot / partial buffer with NaN once consumed */
 #define CP_ATTN_OPT_STEP_TIMING 5 /* 1: time every ring step's attention kernel with HIP events */
 #define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel (default 256; 0: one

@@ -69,7 +69,7 @@ class Plan:
         self.set_option(N.OPT_SERIALIZE, int(bool(on)))
 
     def set_recv(self, mode):
-        self.set_option(N.OPT_RECV, {"kernel": 0, "memcpy": 1, "fused": 2}[mode])
+        self.set_option(N.OPT_RECV, {"kernel": 0, "memcpy": 1, "fused": 2, "hybrid": 3}[mode])
 
     def set_recv_blocks(self, n):
         self.set_option(N.OPT_RECV_BLOCKS, int(n))

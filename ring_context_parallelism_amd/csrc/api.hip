@@ -186,7 +186,14 @@ int recv_kv(Plan& p, const void* k, const void* v, int src, int b, hipStream_t s
   return CP_ATTN_OK;
 }
 
-bool fused_recv(const Plan& p) { return p.opt_recv == 2 && attn_does_recv(p.dtype == CP_ATTN_BF16, p.head_dim); }
+// Whether step s's attention kernel itself receives step s+1's K/V (mode 2
+// at every step; mode 3 from step 1 on, step 0's receive going through the
+// copy stream), and whether step s's receive runs on the copy stream.
+bool kernel_recv(const Plan& p, int s) {
+  if (s + 1 >= p.cp || !attn_does_recv(p.dtype == CP_ATTN_BF16, p.head_dim)) return false;
+  return p.opt_recv == 2 || (p.opt_recv == 3 && s >= 1);
+}
+bool side_recv(const Plan& p, int s) { return s + 1 < p.cp && !kernel_recv(p, s); }
 
 // Step 0 reads the rank's own K/V in place (the rank holds them; nothing is
 // received); later steps read receive slot b.
@@ -199,7 +206,7 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
   const bool bf16 = p.dtype == CP_ATTN_BF16;
   if (sd.nseg == 0) {
     // no query row of this rank sees the step's keys; the receive still happens
-    if (fused_recv(p) && s + 1 < p.cp) CPA_HIP(launch_recv(recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1), 0, st));
+    if (kernel_recv(p, s)) CPA_HIP(launch_recv(recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1), 0, st));
     return CP_ATTN_OK;
   }
   const int bm = bf16 ? attn_bf16_block_m(p.head_dim) : attn_f32_block_m();
@@ -253,7 +260,7 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
     a.total_tiles += x.tiles;
   }
   if (sd.nseg == 1) a.seg[1] = SegArgs{};
-  if (fused_recv(p) && s + 1 < p.cp) a.recv = recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1);
+  if (kernel_recv(p, s)) a.recv = recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
   return CP_ATTN_OK;
@@ -325,10 +332,11 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
   hipStream_t cs = serial ? st : d.copy;
   hipStream_t ms = serial ? st : d.merge;
 
-  const bool fused = fused_recv(p);
   // cross-stream events only where another stream waits on them: each
   // record/wait pair costs microseconds of queue latency per step
-  const bool copy_side = !serial && !fused;
+  bool any_side = false;
+  for (int s = 0; s < P; ++s) any_side = any_side || side_recv(p, s);
+  const bool copy_side = !serial && any_side;
   const bool merge_side = !serial && separate;
   if (copy_side || merge_side) {
     CPA_HIP(hipEventRecord(d.start, st));
@@ -337,13 +345,14 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
   }
   for (int s = 0; s < P; ++s) {
     const int b = s & 1;
-    if (s + 1 < P && !fused) {
+    if (side_recv(p, s)) {
+      // slot nb was last read by step s-1
       const int nb = (s + 1) & 1;
       if (!serial && s >= 1) CPA_HIP(hipStreamWaitEvent(cs, d.attn_done[nb], 0));
       CPA_TRY(recv_kv(p, k, v, p.step(r, s + 1).src, nb, cs));
       if (!serial) CPA_HIP(hipEventRecord(d.recv_done[nb], cs));
     }
-    if (!serial && !fused && s >= 1) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
+    if (!serial && s >= 1 && side_recv(p, s - 1)) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
     if (separate && !serial && s >= 2) CPA_HIP(hipStreamWaitEvent(st, d.merge_done[b], 0));
     const size_t ti = size_t(r) * P + s;
     if (p.opt_step_timing) CPA_HIP(hipEventRecord(d.t0[ti], st));
@@ -356,7 +365,9 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
       CPA_HIP(launch_poison(ws + w.slot_k[b], w.kv_bytes, st));
       CPA_HIP(launch_poison(ws + w.slot_v[b], w.kv_bytes, st));
     }
-    if (copy_side || merge_side) CPA_HIP(hipEventRecord(d.attn_done[b], st));
+    // the copy stream's receive at step s+1 waits for this step; so does the
+    // merge stream
+    if ((!serial && side_recv(p, s + 1)) || merge_side) CPA_HIP(hipEventRecord(d.attn_done[b], st));
     if (separate && s > 0) {
       if (!serial) CPA_HIP(hipStreamWaitEvent(ms, d.attn_done[b], 0));
       CPA_TRY(launch_step_merge(p, r, s, b, ms));
@@ -484,7 +495,7 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
       p.opt_serialize = value != 0;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_RECV:
-      if (value < 0 || value > 2) return fail(CP_ATTN_EINVAL, "recv option must be 0, 1 or 2");
+      if (value < 0 || value > 3) return fail(CP_ATTN_EINVAL, "recv option must be 0, 1, 2 or 3");
       p.opt_recv = value;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_POISON:

@@ -179,8 +179,13 @@ def test_schedule_modes_agree(dtype):
     p.set_poison(True)
     fused_poi = _run(p, q, k, v)
     p.set_poison(False)
+    p.set_recv("hybrid")
+    hybrid = _run(p, q, k, v)
+    p.set_poison(True)
+    hybrid_poi = _run(p, q, k, v)
+    p.set_poison(False)
     p.set_recv("memcpy")
-    for o, l in (ser, poi, mem, full_grid, small_grid, fused, fused_poi):
+    for o, l in (ser, poi, mem, full_grid, small_grid, fused, fused_poi, hybrid, hybrid_poi):
         assert _bitwise_equal(o, base[0]) and _bitwise_equal(l, base[1])
     p.set_merge(True)
     sep = _run(p, q, k, v)
@@ -257,7 +262,7 @@ def _sample_rows(seq, cp, layout, rank, rng, per_chunk=6):
     return np.unique(np.asarray(rows))
 
 
-@pytest.mark.parametrize("recv", ["kernel", "memcpy", "fused"])
+@pytest.mark.parametrize("recv", ["kernel", "memcpy", "fused", "hybrid"])
 @pytest.mark.parametrize("name", [n for n in WORKLOADS if "fp32" not in n])
 def test_full_workload_sampled(name, recv):
     """The configuration the bench times, compared on sampled rows and heads."""
