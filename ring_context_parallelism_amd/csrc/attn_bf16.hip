@@ -678,21 +678,22 @@ void attn_step_bf16_d128x8(StepArgs a) {
 
   // Ping-pong: the two waves of a SIMD (wave w and wave w + 4) run half a
   // tile apart, so that one runs its MFMAs while the other runs its softmax.
-  // A tile has two phases between workgroup barriers:
-  //   waves 0-3: phase 1 product of tile j - 1 and scores of tile j;
-  //              phase 2 softmax of tile j, loads of K tile j + 2
-  //   waves 4-7: phase 1 softmax of tile j - 1, loads of V tile j + 2;
-  //              phase 2 product of tile j - 1 and scores of tile j
-  // so each phase holds one group's 32 MFMAs and the other's softmax.  The
-  // loads go to stage (j + 2) % 4: its K tile (j - 2) was last read in tile
-  // j - 2 and its V tile in tile j - 1.  A direct-to-LDS load holds its wave
-  // at issue until the CU's address unit takes it, so the loads come from
-  // the group that runs the softmax, which finishes before the other group's
-  // MFMAs.  Each group runs its own copy of the loop (the barriers pair up by
-  // count, not by address), so each copy's registers follow its own live
-  // values.  Stage and copy-staging indices are loop variables: unrolling to
-  // make them constants needs several sets of stage addresses and spills the
-  // Q fragments.
+  // Within tile j:
+  //   waves 0-3: product of tile j - 1 and scores of tile j (32 MFMAs), then
+  //              softmax of tile j and the loads of K tile j + 2
+  //   waves 4-7: softmax of tile j - 1 and the loads of V tile j + 2, then
+  //              product of tile j - 1 and scores of tile j
+  // with one workgroup barrier per tile, at its end (a second one between
+  // the halves only forced the alignment and measured slower).  The loads go
+  // to stage (j + 2) % 4: its K tile (j - 2) was last read in tile j - 2 and
+  // its V tile in tile j - 1, both before the previous end-of-tile barrier.
+  // A direct-to-LDS load holds its wave at issue until the CU's address unit
+  // takes it, so the loads come from the softmax half of each wave's tile.
+  // Each group runs its own copy of the loop (the barriers pair up by count,
+  // not by address), so each copy's registers follow its own live values.
+  // Stage and copy-staging indices are loop variables: unrolling to make them
+  // constants needs several sets of stage addresses and spills the Q
+  // fragments.
 #define CPATTN_X8_COPY(J, C)                                                               \
   do {                                                                                     \
     if constexpr (kRecv) {                                                                 \
@@ -724,7 +725,6 @@ void attn_step_bf16_d128x8(StepArgs a) {
     for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
       CPATTN_X8_COPY(j, cb);
       CPATTN_X8_GEMMS(j, st, s_, pb_);
-      lds_barrier();
       if (j * kBN < w_max) softmax(s_, j * kBN, pb_);
       issue(desc_k, min(j + 2, ntiles - 1) * kBN, kst((st + 2) & 3));
       CPATTN_X8_END();
@@ -737,7 +737,6 @@ void attn_step_bf16_d128x8(StepArgs a) {
       CPATTN_X8_COPY(j, cb);
       if (j > 0 && (j - 1) * kBN < w_max) softmax(s_, (j - 1) * kBN, pb_);
       issue(desc_v, min(j + 2, ntiles - 1) * kBN, vst((st + 2) & 3));
-      lds_barrier();
       CPATTN_X8_GEMMS(j, st, s_, pb_);
       CPATTN_X8_END();
     }
