@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--recv", choices=["kernel", "memcpy", "fused", "hybrid"], default=None, help="ring receive path (default: library's)")
     ap.add_argument("--recv-blocks", type=int, default=None, help="grid bound of the receive copy kernel")
     ap.add_argument("--serialize", action="store_true", help="run the whole schedule on one stream")
+    ap.add_argument("--graph", action="store_true", help="graph mode: each call replays a recorded HIP graph")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one layout gather of q (a plain copy of known size) before timing, "
                          "as the reference for hardware traffic counters")
@@ -83,8 +84,10 @@ def time_calls(plan, w, bufs, stream, steps, warmup, warmup_seconds=0.0):
     return e0.elapsed_time(e1) / steps
 
 
-def step_kernel_times(plan, w, bufs, stream, reps):
-    """Per-(rank, step) attention-kernel ms from the library's own HIP events."""
+def step_kernel_times(plan, w, bufs, stream, reps, graph=False):
+    """Per-(rank, step) attention-kernel ms from the library's own HIP events
+    (recorded by eager calls: graph mode records no step events)."""
+    plan.set_graph(False)
     plan.set_step_timing(True)
     acc = None
     for _ in range(reps):
@@ -92,6 +95,7 @@ def step_kernel_times(plan, w, bufs, stream, reps):
         t = np.array(plan.last_step_times())
         acc = t if acc is None else acc + t
     plan.set_step_timing(False)
+    plan.set_graph(graph)
     return acc / reps
 
 
@@ -229,6 +233,8 @@ def main():
         plan.set_recv_blocks(args.recv_blocks)
     if args.serialize:
         plan.set_serialize(True)
+    if args.graph:
+        plan.set_graph(True)
 
     if args.copy_probe:
         probe = torch.empty_like(q)
@@ -243,7 +249,7 @@ def main():
     print(f"[bench] {w.name}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     # dominant kernel: the attention step kernel, timed with HIP events on its own stream
-    times = step_kernel_times(plan, w, bufs, stream, min(args.steps, 10))
+    times = step_kernel_times(plan, w, bufs, stream, min(args.steps, 10), args.graph)
     ranks = range(w.cp) if w.rank is None else [w.rank]
     launches = [times[r][s] for r in ranks for s in range(w.cp) if times[r][s] > 0]
     avg_ms = float(np.mean(launches))
@@ -285,7 +291,12 @@ def main():
             plan.set_recv(mode)
             recv_ms[mode] = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
         plan.set_recv(args.recv or "kernel")
+        plan.set_graph(not args.graph)
+        ms_graph_other = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
+        plan.set_graph(args.graph)
         result["modes_ms"] = {"default_receive": args.recv or "kernel",
+                              "graph_mode": bool(args.graph),
+                              ("eager_calls" if args.graph else "graph_replay"): ms_graph_other,
                               "overlapped_fused_merge": round(ms, 5), "serialized_fused_merge": round(ms_serial, 5),
                               "overlapped_separate_merge": round(ms_sep, 5),
                               "receive_kernel_grid_blocks_ms": ms_blocks,

@@ -86,6 +86,12 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
 #define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel (default 256; 0: one
                                      workgroup per 128 vectors of 16 bytes); a small grid shares the
                                      GPU with the attention kernel it overlaps */
+#define CP_ATTN_OPT_GRAPH 7       /* 1: graph mode. A forward call is recorded once into a HIP graph
+                                     (stream capture on a library stream) and replayed on the
+                                     caller's stream while its buffers, rank, workspace, side streams
+                                     and options are unchanged; any change records it again. Replays
+                                     read the buffers' current contents. Step timing is not recorded
+                                     in this mode (cp_attn_last_step_times reports -1). */
 
 /*
  * Create a plan (host only: no device memory, no HIP call).

@@ -74,6 +74,9 @@ class Plan:
     def set_recv_blocks(self, n):
         self.set_option(N.OPT_RECV_BLOCKS, int(n))
 
+    def set_graph(self, on):
+        self.set_option(N.OPT_GRAPH, int(bool(on)))
+
     def set_poison(self, on):
         self.set_option(N.OPT_POISON, int(bool(on)))
 

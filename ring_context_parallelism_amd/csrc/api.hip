@@ -46,6 +46,10 @@ struct DeviceState {
   bool own_ws = false;
   std::vector<hipEvent_t> t0, t1;  // per (rank, step) timing events
   std::vector<int> timed;          // 1 if (rank, step) was timed by the last call
+  // graph mode: the last recorded forward and what it was recorded for
+  hipStream_t capture = nullptr;
+  hipGraphExec_t graph = nullptr;
+  std::vector<intptr_t> graph_key;
 };
 
 namespace {
@@ -322,7 +326,8 @@ int launch_rank_finalize(Plan& p, void* out, float* lse, int r, hipStream_t st) 
     if (rc_ != CP_ATTN_OK) return rc_; \
   } while (0)
 
-int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, float* lse, int r, hipStream_t st) {
+int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, float* lse, int r, hipStream_t st,
+             bool capturing = false) {
   DeviceState& d = *p.dev;
   const WsLayout w = ws_layout(p);
   char* ws = static_cast<char*>(d.ws);
@@ -353,11 +358,14 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
       if (!serial) CPA_HIP(hipEventRecord(d.recv_done[nb], cs));
     }
     if (!serial && s >= 1 && side_recv(p, s - 1)) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
-    if (separate && !serial && s >= 2) CPA_HIP(hipStreamWaitEvent(st, d.merge_done[b], 0));
+    // part[b] is free once the merge of step s-2 has read it (step 0 writes
+    // the running state directly and has no merge)
+    if (separate && !serial && s >= 3) CPA_HIP(hipStreamWaitEvent(st, d.merge_done[b], 0));
     const size_t ti = size_t(r) * P + s;
-    if (p.opt_step_timing) CPA_HIP(hipEventRecord(d.t0[ti], st));
+    const bool timing = p.opt_step_timing && !capturing;
+    if (timing) CPA_HIP(hipEventRecord(d.t0[ti], st));
     CPA_TRY(launch_step(p, q, k, v, out, lse, r, s, b, st));
-    if (p.opt_step_timing) {
+    if (timing) {
       CPA_HIP(hipEventRecord(d.t1[ti], st));
       d.timed[ti] = 1;
     }
@@ -408,6 +416,51 @@ void reset_timing(Plan& p) {
   d.timed.assign(size_t(p.cp) * p.cp, 0);
 }
 
+void drop_graph(DeviceState& d) {
+  if (d.graph) (void)hipGraphExecDestroy(d.graph);
+  d.graph = nullptr;
+  d.graph_key.clear();
+}
+
+// Graph mode: the forward of one rank (rank >= 0) or of every rank (-1) is
+// recorded once, by stream capture on the library's capture stream (the copy
+// and merge streams join through their events), and the executable graph is
+// replayed on the caller's stream while the buffers, the workspace, the side
+// streams and the options are the ones it was recorded with; anything else
+// records it again.  Replays read the buffers' current contents.
+int run_graph(Plan& p, const void* q, const void* k, const void* v, void* out, float* lse, int rank,
+              hipStream_t st) {
+  DeviceState& d = *p.dev;
+  const std::vector<intptr_t> key = {
+      intptr_t(q), intptr_t(k), intptr_t(v), intptr_t(out), intptr_t(lse), rank,
+      intptr_t(d.ws), intptr_t(d.copy), intptr_t(d.merge), p.dtype, p.opt_merge, p.opt_serialize,
+      p.opt_recv, p.opt_poison, p.opt_recv_blocks};
+  if (!d.graph || key != d.graph_key) {
+    drop_graph(d);
+    if (!d.capture) CPA_HIP(hipStreamCreateWithFlags(&d.capture, hipStreamNonBlocking));
+    CPA_HIP(hipStreamBeginCapture(d.capture, hipStreamCaptureModeThreadLocal));
+    int rc = CP_ATTN_OK;
+    for (int r = rank < 0 ? 0 : rank; r < (rank < 0 ? p.cp : rank + 1) && rc == CP_ATTN_OK; ++r)
+      rc = run_rank(p, q, k, v, out, lse, r, d.capture, true);
+    hipGraph_t g = nullptr;
+    const hipError_t ec = hipStreamEndCapture(d.capture, &g);
+    if (rc != CP_ATTN_OK) {
+      if (g) (void)hipGraphDestroy(g);
+      return rc;
+    }
+    if (ec != hipSuccess) return fail(CP_ATTN_EHIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(ec));
+    const hipError_t ei = hipGraphInstantiate(&d.graph, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (ei != hipSuccess) {
+      d.graph = nullptr;
+      return fail(CP_ATTN_EHIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(ei));
+    }
+    d.graph_key = key;
+  }
+  CPA_HIP(hipGraphLaunch(d.graph, st));
+  return CP_ATTN_OK;
+}
+
 }  // namespace
 }  // namespace cpattn
 
@@ -452,6 +505,8 @@ int cp_attn_plan_destroy(cp_attn_plan_t h) {
       (void)hipGetDevice(&cur);
       (void)hipSetDevice(d.device);
       if (hipDeviceSynchronize() != hipSuccess) rc = fail(CP_ATTN_EHIP, "hipDeviceSynchronize failed in destroy");
+      drop_graph(d);
+      if (d.capture) (void)hipStreamDestroy(d.capture);
       if (d.own_ws && d.ws) (void)hipFree(d.ws);
       if (d.own_copy && d.copy) (void)hipStreamDestroy(d.copy);
       if (d.own_merge && d.merge) (void)hipStreamDestroy(d.merge);
@@ -508,6 +563,10 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
       if (value < 0) return fail(CP_ATTN_EINVAL, "recv_blocks must be >= 0");
       p.opt_recv_blocks = value;
       return CP_ATTN_OK;
+    case CP_ATTN_OPT_GRAPH:
+      if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "graph option must be 0 or 1");
+      p.opt_graph = value;
+      return CP_ATTN_OK;
     default:
       return fail(CP_ATTN_EINVAL, "unknown option");
   }
@@ -555,6 +614,7 @@ int cp_attn_rank_forward(cp_attn_plan_t h, const void* q, const void* k, const v
   CPA_TRY(check_io(q, k, v, out, lse));
   CPA_TRY(ensure_device(p));
   reset_timing(p);
+  if (p.opt_graph) return run_graph(p, q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
   return run_rank(p, q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
   CPA_GUARD_END
 }
@@ -567,6 +627,7 @@ int cp_attn_full_forward(cp_attn_plan_t h, const void* q, const void* k, const v
   CPA_TRY(check_io(q, k, v, out, lse));
   CPA_TRY(ensure_device(p));
   reset_timing(p);
+  if (p.opt_graph) return run_graph(p, q, k, v, out, lse, -1, static_cast<hipStream_t>(stream));
   for (int r = 0; r < p.cp; ++r) CPA_TRY(run_rank(p, q, k, v, out, lse, r, static_cast<hipStream_t>(stream)));
   return CP_ATTN_OK;
   CPA_GUARD_END
