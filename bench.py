@@ -191,6 +191,29 @@ def imbalance_section(stream):
     return res
 
 
+def rank_step_imbalance(plan, w, bufs, stream, reps=3):
+    """Every rank's share of the timed workload, one rank_forward call each:
+    per-(rank, step) step-kernel ms, per-step max/mean over ranks, and the
+    valid 128x64 tile counts (the plan's balance)."""
+    times = []
+    for r in range(w.cp):
+        plan.set_step_timing(True)
+        acc = None
+        for _ in range(reps):
+            plan.rank_forward(*bufs, r, stream=stream)
+            t = np.array(plan.last_step_times())[r]
+            acc = t if acc is None else acc + t
+        plan.set_step_timing(False)
+        times.append(acc / reps)
+    t = np.asarray(times)
+    per = [round(float(t[:, s].max() / t[:, s].mean()), 4) for s in range(w.cp)]
+    tiles = [[plan.valid_work(r, s, 128, 64)[0] for s in range(w.cp)] for r in range(w.cp)]
+    return {"workload": w.name, "step_ms": [[round(float(x), 4) for x in row] for row in t],
+            "time_imbalance_per_step": per, "max_step_imbalance": max(per),
+            "time_imbalance": round(float(t.max(axis=0).sum() / t.mean(axis=0).sum()), 4),
+            "tiles_128x64": tiles}
+
+
 def sampled_parity(w, q, k, v, out, lse):
     import oracle
     from ring_context_parallelism_amd.inputs import to_numpy_f64
@@ -306,6 +329,10 @@ def main():
         torch.cuda.synchronize()
         result["parity_sampled"] = sampled_parity(w, q_cpu, k_cpu, v_cpu, out, lse)
         result["imbalance"] = imbalance_section(stream)
+        if w.rank is not None:
+            plan.set_graph(False)
+            result["imbalance"]["all_ranks_timed_workload"] = rank_step_imbalance(plan, w, bufs, stream)
+            plan.set_graph(args.graph)
         result["imbalance"]["zigzag_step_time_imbalance"] = result["imbalance"]["zigzag"]["time_imbalance"]
 
     if not args.no_cpu_baseline:
