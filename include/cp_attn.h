@@ -92,6 +92,12 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      and options are unchanged; any change records it again. Replays
                                      read the buffers' current contents. Step timing is not recorded
                                      in this mode (cp_attn_last_step_times reports -1). */
+#define CP_ATTN_OPT_KSPLIT 8      /* 1 (default): when a step's workgroups would fill at most half
+                                     of the GPU (few heads), the bf16 head_dim-128 kernel splits
+                                     each full segment's keys in two halves, one workgroup each;
+                                     the part that finishes second merges the other's result
+                                     (exact LSE merge; no workgroup waits for another).
+                                     0: never split. Not used with the separate merge mode. */
 
 /*
  * Create a plan (host only: no device memory, no HIP call).
@@ -124,8 +130,10 @@ int cp_attn_set_dtype(cp_attn_plan_t plan, int dtype);
 int cp_attn_set_option(cp_attn_plan_t plan, int option, int value);
 
 /* Bytes of device workspace a forward call needs: two K/V receive slots, the
- * fp32 running state (O, LSE) and two fp32 partial buffers for the separate
- * merge mode, each rounded up to 256 bytes. */
+ * fp32 running state (O, LSE), two fp32 partial buffers (separate merge mode,
+ * or the two key halves of a split step) and (n_loc/256 + 2) * heads int32
+ * split counters, each rounded up to 256 bytes.  The library zeroes the
+ * counters once per workspace (synchronously, on the next forward call). */
 int cp_attn_workspace_bytes(cp_attn_plan_t plan, int64_t* bytes);
 
 /* Hand the plan caller-owned device memory of at least cp_attn_workspace_bytes

@@ -31,6 +31,7 @@ OPT_POISON = 4
 OPT_STEP_TIMING = 5
 OPT_RECV_BLOCKS = 6
 OPT_GRAPH = 7
+OPT_KSPLIT = 8
 
 _c_p = ctypes.c_void_p
 _i32 = ctypes.c_int32

@@ -77,6 +77,9 @@ class Plan:
     def set_graph(self, on):
         self.set_option(N.OPT_GRAPH, int(bool(on)))
 
+    def set_key_split(self, on):
+        self.set_option(N.OPT_KSPLIT, int(bool(on)))
+
     def set_poison(self, on):
         self.set_option(N.OPT_POISON, int(bool(on)))
 

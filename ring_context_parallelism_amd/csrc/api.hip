@@ -50,6 +50,8 @@ struct DeviceState {
   hipStream_t capture = nullptr;
   hipGraphExec_t graph = nullptr;
   std::vector<intptr_t> graph_key;
+  bool cnt_ready = false;  // the workspace's key-split counters are zero
+  int cus = 0;             // compute units of the device
 };
 
 namespace {
@@ -68,9 +70,13 @@ int fail(int code, const std::string& msg) {
   } while (0)
 
 struct WsLayout {
-  int64_t slot_k[2], slot_v[2], acc_o, acc_lse, part_o[2], part_lse[2], total;
-  int64_t kv_bytes, o_bytes, lse_bytes;
+  int64_t slot_k[2], slot_v[2], acc_o, acc_lse, part_o[2], part_lse[2], split_cnt, total;
+  int64_t kv_bytes, o_bytes, lse_bytes, cnt_bytes;
 };
+
+// row tiles of the key-split kernel (256 rows) over a step's two segments,
+// one counter per (row tile, head)
+int64_t split_counters(const Plan& p) { return (p.n_loc / 256 + 2) * p.heads; }
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
@@ -95,6 +101,8 @@ WsLayout ws_layout(const Plan& p) {
     w.part_o[b] = take(w.o_bytes);
     w.part_lse[b] = take(w.lse_bytes);
   }
+  w.cnt_bytes = split_counters(p) * 4;
+  w.split_cnt = take(w.cnt_bytes);
   w.total = off;
   return w;
 }
@@ -140,7 +148,16 @@ int ensure_device(Plan& p) {
     }
     d.ws_bytes = w.total;
     d.own_ws = true;
+    d.cnt_ready = false;
   }
+  if (!d.cnt_ready) {
+    // once per workspace: the key-split counters start at zero (the kernel
+    // that uses a counter resets it); synchronous, before any launch
+    CPA_HIP(hipMemset(static_cast<char*>(d.ws) + w.split_cnt, 0, size_t(w.cnt_bytes)));
+    CPA_HIP(hipDeviceSynchronize());
+    d.cnt_ready = true;
+  }
+  if (!d.cus) CPA_HIP(hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev));
   if (p.opt_step_timing && d.t0.empty()) {
     const size_t n = size_t(p.cp) * p.cp;
     d.t0.assign(n, nullptr);
@@ -247,6 +264,17 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
   a.nseg = sd.nseg;
   a.total_tiles = 0;
   const bool separate = p.opt_merge == 1;
+  // Key split: when the step's workgroups would fill at most half the GPU,
+  // each full segment's row tiles take two workgroups, one per half of the
+  // keys (the partial buffers of the separate merge mode hold the parts).
+  int64_t wgs = 0;
+  for (int i = 0; i < sd.nseg; ++i) wgs += (sd.seg[i].q_len + bm - 1) / bm * p.heads;
+  const bool key_split = p.opt_ksplit && !separate && attn_splits_keys(bf16, p.head_dim) && 2 * wgs <= d.cus;
+  for (int b = 0; b < 2; ++b) {
+    a.split_o[b] = reinterpret_cast<float*>(ws + w.part_o[b]);
+    a.split_lse[b] = reinterpret_cast<float*>(ws + w.part_lse[b]);
+  }
+  a.split_cnt = reinterpret_cast<int32_t*>(ws + w.split_cnt);
   for (int i = 0; i < sd.nseg; ++i) {
     const Segment& g = sd.seg[i];
     SegArgs& x = a.seg[i];
@@ -255,7 +283,11 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
     x.q_len = int32_t(g.q_len);
     x.kv_full = int32_t(g.kv_full);
     x.diag = g.diag;
-    x.tiles = int32_t((g.q_len + bm - 1) / bm);
+    const int32_t qt = int32_t((g.q_len + bm - 1) / bm);
+    // the kernel keeps a split row tile's parts in 128 KiB slots of the
+    // partial buffers, one per (256-row tile of the local rows, head)
+    x.ksplit = key_split && !g.diag && g.kv_full >= 16 * 64 && g.q_start % 256 == 0 && p.n_loc % 256 == 0 ? 2 : 1;
+    x.tiles = qt * x.ksplit;
     if (separate) {
       x.epi = g.first ? kEpiInit : kEpiPartial;
     } else {
@@ -434,7 +466,7 @@ int run_graph(Plan& p, const void* q, const void* k, const void* v, void* out, f
   const std::vector<intptr_t> key = {
       intptr_t(q), intptr_t(k), intptr_t(v), intptr_t(out), intptr_t(lse), rank,
       intptr_t(d.ws), intptr_t(d.copy), intptr_t(d.merge), p.dtype, p.opt_merge, p.opt_serialize,
-      p.opt_recv, p.opt_poison, p.opt_recv_blocks};
+      p.opt_recv, p.opt_poison, p.opt_recv_blocks, p.opt_ksplit};
   if (!d.graph || key != d.graph_key) {
     drop_graph(d);
     if (!d.capture) CPA_HIP(hipStreamCreateWithFlags(&d.capture, hipStreamNonBlocking));
@@ -567,6 +599,10 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
       if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "graph option must be 0 or 1");
       p.opt_graph = value;
       return CP_ATTN_OK;
+    case CP_ATTN_OPT_KSPLIT:
+      if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "ksplit option must be 0 or 1");
+      p.opt_ksplit = value;
+      return CP_ATTN_OK;
     default:
       return fail(CP_ATTN_EINVAL, "unknown option");
   }
@@ -591,6 +627,7 @@ int cp_attn_set_workspace(cp_attn_plan_t h, void* ptr, int64_t bytes) {
   d.ws = ptr;
   d.ws_bytes = ptr ? bytes : 0;
   d.own_ws = false;
+  d.cnt_ready = false;
   return CP_ATTN_OK;
 }
 

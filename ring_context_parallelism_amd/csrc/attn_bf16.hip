@@ -430,7 +430,12 @@ void attn_step_bf16_d128x8(StepArgs a) {
   if (si) t -= a.seg[0].tiles;
   const SegArgs& g = a.seg[si];
   const int epi = __builtin_amdgcn_readfirstlane(g.epi);  // scalar: the epilogue branches on it
-  if (g.diag) t = g.tiles - 1 - t;  // longest rows first
+  // key split: a full segment on a grid smaller than the GPU is cut into
+  // g.ksplit = 2 key ranges per row tile, one workgroup each (adjacent ids)
+  const int ks = g.ksplit;
+  const int part = t % ks;
+  t /= ks;
+  if (g.diag) t = g.tiles / ks - 1 - t;  // longest rows first
   const int row0 = t * kBM8;
 
   const int tid = threadIdx.x;
@@ -628,7 +633,12 @@ void attn_step_bf16_d128x8(StepArgs a) {
   const void* const csrc_p = rr == 0 ? a.recv.src[0] : rr == 1 ? a.recv.src[1] : rr == 2 ? a.recv.src[2] : a.recv.src[3];
   g_u32x4* const cdst = (g_u32x4*)(rr == 0 ? a.recv.dst[0] : rr == 1 ? a.recv.dst[1] : rr == 2 ? a.recv.dst[2] : a.recv.dst[3]);
   const u32x4 desc_c = buffer_desc(csrc_p, uint32_t(rn * 16));
-  const int ntiles = (kv_end + kBN - 1) / kBN;
+  // this workgroup's key tiles: jt0 .. jt0 + ntiles - 1 (key kb0 onwards)
+  const int ntiles_all = (kv_end + kBN - 1) / kBN;
+  const int half_tiles = (ntiles_all + 1) >> 1;
+  const int jt0 = part ? half_tiles : 0;
+  const int ntiles = ks == 1 ? ntiles_all : (part ? ntiles_all - half_tiles : half_tiles);
+  const int kb0 = jt0 * kBN;
   // slots of the share: ntiles + 2, at most 512 vectors (one per lane) each;
   // what does not fit is copied after the loop
   const int64_t nslot = int64_t(ntiles) + 2;
@@ -670,8 +680,8 @@ void attn_step_bf16_d128x8(StepArgs a) {
       copy_dma(1, 1);
     }
     const u32x4& desc = wv < 4 ? desc_k : desc_v;
-    issue(desc, 0, wv < 4 ? kst(0) : vst(0));
-    issue(desc, min(1, ntiles - 1) * kBN, wv < 4 ? kst(1) : vst(1));
+    issue(desc, kb0, wv < 4 ? kst(0) : vst(0));
+    issue(desc, kb0 + min(1, ntiles - 1) * kBN, wv < 4 ? kst(1) : vst(1));
   }
   wait_vmem();
   lds_barrier();
@@ -705,8 +715,8 @@ void attn_step_bf16_d128x8(StepArgs a) {
   // scores of tile J into s_
 #define CPATTN_X8_GEMMS(J, S, s_, pb_)                                                     \
   do {                                                                                     \
-    const bool sc_ = (J) * kBN < w_max;                                                    \
-    const bool pv_ = (J) > 0 && ((J) - 1) * kBN < w_max;                                   \
+    const bool sc_ = kb0 + (J) * kBN < w_max;                                              \
+    const bool pv_ = (J) > 0 && kb0 + ((J) - 1) * kBN < w_max;                             \
     if (pv_) pv(vst(((S) + 3) & 3), pb_);                                                  \
     if (sc_) scores(kst(S), s_);                                                           \
   } while (0)
@@ -725,23 +735,23 @@ void attn_step_bf16_d128x8(StepArgs a) {
     for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
       CPATTN_X8_COPY(j, cb);
       CPATTN_X8_GEMMS(j, st, s_, pb_);
-      if (j * kBN < w_max) softmax(s_, j * kBN, pb_);
-      issue(desc_k, min(j + 2, ntiles - 1) * kBN, kst((st + 2) & 3));
+      if (kb0 + j * kBN < w_max) softmax(s_, kb0 + j * kBN, pb_);
+      issue(desc_k, kb0 + min(j + 2, ntiles - 1) * kBN, kst((st + 2) & 3));
       CPATTN_X8_END();
     }
     // product of the last tile (its stage is not overwritten: the loads
     // issued at the last two tiles went to other stages)
-    if (ntiles > 0 && (ntiles - 1) * kBN < w_max) pv(vst((ntiles - 1) & 3), pb_);
+    if (ntiles > 0 && kb0 + (ntiles - 1) * kBN < w_max) pv(vst((ntiles - 1) & 3), pb_);
   } else {
     for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
       CPATTN_X8_COPY(j, cb);
-      if (j > 0 && (j - 1) * kBN < w_max) softmax(s_, (j - 1) * kBN, pb_);
-      issue(desc_v, min(j + 2, ntiles - 1) * kBN, vst((st + 2) & 3));
+      if (j > 0 && kb0 + (j - 1) * kBN < w_max) softmax(s_, kb0 + (j - 1) * kBN, pb_);
+      issue(desc_v, kb0 + min(j + 2, ntiles - 1) * kBN, vst((st + 2) & 3));
       CPATTN_X8_GEMMS(j, st, s_, pb_);
       CPATTN_X8_END();
     }
-    if (ntiles > 0 && (ntiles - 1) * kBN < w_max) {
-      softmax(s_, (ntiles - 1) * kBN, pb_);
+    if (ntiles > 0 && kb0 + (ntiles - 1) * kBN < w_max) {
+      softmax(s_, kb0 + (ntiles - 1) * kBN, pb_);
       pv(vst((ntiles - 1) & 3), pb_);
     }
   }
@@ -771,10 +781,101 @@ void attn_step_bf16_d128x8(StepArgs a) {
   }
 
   l += __shfl_xor(l, 32);
-  if (!ok) return;
   const int lrow_out = g.q_start + row;
-  const float lse_s = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
-  const float inv = 1.f / l;
+  float lse_s = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
+  float inv = 1.f / l;
+  if (ks > 1) {
+    // Key split: the part that finishes first leaves its normalised output
+    // and LSE in split buffer [part] and exits; the second reads them, folds
+    // them into its own by the exact LSE merge and runs the epilogue.  No
+    // workgroup waits for another.  The parts travel as device-scope relaxed
+    // atomic stores and loads (written through to, and read from, the
+    // device's coherence point): a device-scope fence would write back or
+    // invalidate the whole L2 of the XCD, under the K/V tiles the other
+    // workgroups are still streaming.  The writer's stores have completed
+    // (vmcnt 0) before its counter increment; the reader loads only after its
+    // increment returned 1.  The merge is symmetric in the two parts, so the
+    // result does not depend on which finishes first.
+    // Slot of this (row tile, head): the split segments start at a multiple
+    // of 256 local rows.  A wave's 16 KiB of the slot hold its lanes' values
+    // in register order, chunk k (16 bytes per lane) at k KiB, so every access
+    // is a coalesced 1 KiB; the other part's workgroup maps lanes to the same
+    // rows and reads the same layout back.  sc1 on the 16-byte buffer
+    // accesses: written through to, and read from, device coherence.
+    const int64_t slot = int64_t((g.q_start + row0) >> 8) * a.heads + h;
+    auto part_rsrc = [&](int pp) {
+      return __builtin_amdgcn_make_buffer_rsrc(a.split_o[pp] + (slot * 8 + wv) * 4096, short(0), 16384, 0x00020000);
+    };
+    constexpr int kSc1 = 16;  // cache-policy operand: sc1 (device scope)
+    {
+      const __amdgpu_buffer_rsrc_t r = part_rsrc(part);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x4 v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = __float_as_uint(__fmul_rn(o[b][4 * q4 + u], inv));
+          __builtin_amdgcn_raw_buffer_store_b128(v, r, (4 * b + q4) * 1024 + lane * 16, 0, kSc1);
+        }
+      if (hf == 0)
+        __hip_atomic_store(a.split_lse[part] + slot * 256 + wv * 32 + qc, lse_s, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vmem();
+    __syncthreads();
+    int* const flag = reinterpret_cast<int*>(smem_kv);  // the K/V stages are free by now
+    if (tid == 0) {
+      int* const cnt = a.split_cnt + slot;
+      const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old != 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next launch
+      *flag = old;
+    }
+    __syncthreads();
+    if (*flag == 0) return;
+    if (!ok) return;
+    const float lo =
+        __hip_atomic_load(a.split_lse[part ^ 1] + slot * 256 + wv * 32 + qc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float c[NB][16];
+    {
+      const __amdgpu_buffer_rsrc_t r = part_rsrc(part ^ 1);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (4 * b + q4) * 1024 + lane * 16, 0, kSc1);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) c[b][4 * q4 + u] = __uint_as_float(v[u]);
+        }
+    }
+    float w1 = 1.f, w2 = 0.f, L = lse_s;
+    if (lo != -INFINITY) {
+      if (lse_s == -INFINITY) {
+        w1 = 0.f;
+        w2 = 1.f;
+        L = lo;
+      } else {
+        L = fmaxf(lse_s, lo) + log1pf(expf(-fabsf(lse_s - lo)));
+        w1 = expf(lse_s - L);
+        w2 = expf(lo - L);
+      }
+    }
+    // both terms exactly as the other order would form them: own value
+    // rounded as it would have been stored, products and sum rounded one by
+    // one (no contraction), a term of weight 0 left out
+    auto mix = [&](float own, float other) {
+      const float t1 = w1 != 0.f ? __fmul_rn(w1, __fmul_rn(own, inv)) : 0.f;
+      const float t2 = w2 != 0.f ? __fmul_rn(w2, other) : 0.f;
+      return __fadd_rn(t1, t2);
+    };
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[b][e] = mix(o[b][e], c[b][e]);
+    lse_s = L;
+    inv = 1.f;
+  }
+  if (!ok) return;
   float4 c[NB][4];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -798,6 +899,8 @@ void attn_step_bf16_d128x8(StepArgs a) {
 int attn_bf16_block_m(int head_dim) { return head_dim == 128 ? kBM8 : kBM; }
 
 bool attn_does_recv(int dtype_bf16, int head_dim) { return dtype_bf16 && head_dim == 128; }
+
+bool attn_splits_keys(int dtype_bf16, int head_dim) { return dtype_bf16 && head_dim == 128; }
 
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid(unsigned(a.total_tiles) * unsigned(a.heads));

@@ -23,7 +23,9 @@ struct SegArgs {
   int32_t kv_full;   // keys every row sees
   int32_t diag;      // 1: row t also sees keys kv_full .. kv_full + t
   int32_t epi;       // EpiMode | kEpiFinal
-  int32_t tiles;     // ceil(q_len / BM) for the launching kernel
+  int32_t tiles;     // workgroups of the segment: ceil(q_len / BM) * ksplit
+  int32_t ksplit;    // 1, or 2: each row tile's keys in two halves, one workgroup each (full segments
+                     // starting at a multiple of 256 local rows only)
 };
 
 // Ring receive: up to four contiguous byte ranges (16-byte multiples).
@@ -62,11 +64,20 @@ struct StepArgs {
   int32_t total_tiles;  // sum of seg[i].tiles
   SegArgs seg[2];
   RecvArgs recv;        // next step's receive done by this kernel (recv.n == 0: none)
+  // key split (segments with ksplit 2): part p of the 256-row tile r (of the
+  // local rows) and head h leaves its normalised output in the 128 KiB slot
+  // r * heads + h of split_o[p] (n_loc * H * D floats, n_loc a multiple of
+  // 256) and its LSE in split_lse[p]; split_cnt holds one counter per slot,
+  // zero between launches
+  float* split_o[2];
+  float* split_lse[2];
+  int32_t* split_cnt;
 };
 
 // attention step kernels: return hipError_t of the launch
 // (only the head_dim 128 bf16 kernel performs StepArgs::recv)
 bool attn_does_recv(int dtype_bf16, int head_dim);
+bool attn_splits_keys(int dtype_bf16, int head_dim);  // kernel honours SegArgs::ksplit
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_f32(const StepArgs& a, int head_dim, hipStream_t stream);
 int attn_bf16_block_m(int head_dim);

@@ -47,6 +47,7 @@ struct Plan {
   int32_t opt_poison = 0;
   int32_t opt_step_timing = 0;
   int32_t opt_graph = 0;
+  int32_t opt_ksplit = 1;
   int32_t opt_recv_blocks = 256;
 
   DeviceState* dev = nullptr;

@@ -284,3 +284,44 @@ def test_full_workload_sampled(name, recv):
     assert torch.isfinite(lse[:, torch.from_numpy(mine)]).all()
     if w.causal and (w.rank is None or w.rank == 0):
         assert torch.equal(out[0], v[0])
+
+
+# ------------------------------------------------------------- key split ----
+
+@pytest.mark.parametrize("layout,seq,cp,heads,causal", [("zigzag", 8192, 4, 4, True),
+                                                        ("contiguous", 8192, 4, 4, False),
+                                                        ("contiguous", 6144, 3, 2, True)])
+def test_key_split_matches_oracle(layout, seq, cp, heads, causal):
+    """Few heads: the steps' full segments split their keys over two
+    workgroups.  Repeated calls are bit-identical (the per-tile counters are
+    back at zero after every launch) and both the split and the unsplit
+    schedule match the oracle on sampled rows."""
+    _say(f"key split {layout} seq={seq} cp={cp} heads={heads} causal={causal}")
+    q, k, v = make_qkv(seq, heads, 128, "bf16", 41)
+    p = Plan(seq, cp, heads, 128, causal, layout)
+    runs = [_run(p, q, k, v) for _ in range(3)]
+    for o, l in runs[1:]:
+        assert _bitwise_equal(o, runs[0][0]) and _bitwise_equal(l, runs[0][1])
+    rng = np.random.default_rng(seq + cp)
+    rows = np.unique(np.concatenate([[0, seq - 1], rng.choice(seq, 48, replace=False)]))
+    tol_o, tol_l = TOL[torch.bfloat16]
+    d_o, d_l = _compare(runs[0][0], runs[0][1], q, k, v, causal, torch.bfloat16, rows=rows)
+    _say(f"  split: max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= tol_o and d_l <= tol_l
+    p.set_key_split(False)
+    o2, l2 = _run(p, q, k, v)
+    d_o, d_l = _compare(o2, l2, q, k, v, causal, torch.bfloat16, rows=rows)
+    _say(f"  unsplit: max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= tol_o and d_l <= tol_l
+    p.set_key_split(True)
+    p.set_graph(True)
+    dev = _dev()
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    out = torch.empty_like(qd)
+    lse = torch.empty((heads, seq), device=dev)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        p.full_forward(qd, kd, vd, out, lse)
+        torch.cuda.synchronize()
+        assert _bitwise_equal(out.cpu(), runs[0][0]) and _bitwise_equal(lse.cpu(), runs[0][1])
+    p.close()

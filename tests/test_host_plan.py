@@ -181,6 +181,9 @@ def test_call_error_codes_enqueue_nothing():
     assert lib.cp_attn_set_option(h, N.OPT_GRAPH, 2) == N.EINVAL
     assert lib.cp_attn_set_option(h, N.OPT_GRAPH, 1) == N.OK
     assert lib.cp_attn_set_option(h, N.OPT_GRAPH, 0) == N.OK
+    assert lib.cp_attn_set_option(h, N.OPT_KSPLIT, 2) == N.EINVAL
+    assert lib.cp_attn_set_option(h, N.OPT_KSPLIT, 0) == N.OK
+    assert lib.cp_attn_set_option(h, N.OPT_KSPLIT, 1) == N.OK
     assert lib.cp_attn_set_workspace(h, ctypes.c_void_p(256), 16) == N.ENOWORKSPACE
     assert lib.cp_attn_set_workspace(h, ctypes.c_void_p(100), 1 << 30) == N.EINVAL
     assert lib.cp_attn_step_source(h, 0, 5, ctypes.byref(ctypes.c_int32())) == N.EINVAL
@@ -198,6 +201,7 @@ def test_workspace_size_formula():
     kv = n * hd * 2
     o = n * hd * 4
     lse = 32 * n * 4
-    assert p.workspace_bytes() == 4 * kv + o + lse + 2 * (o + lse)
+    cnt = -(-((n // 256 + 2) * 32 * 4) // 256) * 256
+    assert p.workspace_bytes() == 4 * kv + o + lse + 2 * (o + lse) + cnt
     q = Plan(256, 2, 2, 64, True, "zigzag", dtype=torch.float32)
-    assert q.workspace_bytes() == 4 * (128 * 128 * 4) + 3 * (128 * 128 * 4 + 2 * 128 * 4)
+    assert q.workspace_bytes() == 4 * (128 * 128 * 4) + 3 * (128 * 128 * 4 + 2 * 128 * 4) + 256
