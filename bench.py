@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip imbalance / mode / parity side measurements")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--recv", choices=["kernel", "memcpy", "fused", "hybrid"], default=None, help="ring receive path (default: library's)")
     ap.add_argument("--recv-blocks", type=int, default=None, help="grid bound of the receive copy kernel")
     ap.add_argument("--serialize", action="store_true", help="run the whole schedule on one stream")
@@ -137,7 +137,7 @@ def cpu_baseline(w, q, k, v, target_s):
         threads = 1
     ranks = range(w.cp) if w.rank is None else [w.rank]
     rows = np.concatenate([oracle.rank_positions(w.seq_len, w.cp, r, w.layout) for r in ranks])
-    rows = rows[:: max(1, rows.size // 1024)][:1024]
+    rows = rows[:: max(1, rows.size // 2048)][:2048]
     kpos = np.arange(w.seq_len)
     flops = 0
     heads_done = 0
