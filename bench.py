@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--recv-blocks", type=int, default=None, help="grid bound of the receive copy kernel")
     ap.add_argument("--serialize", action="store_true", help="run the whole schedule on one stream")
     ap.add_argument("--graph", action="store_true", help="graph mode: each call replays a recorded HIP graph")
+    ap.add_argument("--merge", choices=["fused", "separate"], default="fused",
+                    help="LSE merge in the attention epilogue (default) or in the separate merge/finalize kernels")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one layout gather of q (a plain copy of known size) before timing, "
                          "as the reference for hardware traffic counters")
@@ -258,6 +260,8 @@ def main():
         plan.set_serialize(True)
     if args.graph:
         plan.set_graph(True)
+    if args.merge == "separate":
+        plan.set_merge(True)
 
     if args.copy_probe:
         probe = torch.empty_like(q)
