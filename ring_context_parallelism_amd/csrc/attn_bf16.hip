@@ -28,11 +28,12 @@
 //     keys past the slot read as zero).  head_dim 64: into registers two
 //     tiles ahead, then into a double-buffered LDS tile (K row-major, V
 //     transposed; 16-byte padded rows keep the operand reads bank-conflict
-//     free).  head_dim 128: straight into a three-stage LDS ring, V row-major
+//     free).  head_dim 128: straight into a four-stage LDS ring, V row-major
 //     and read transposed (see the head_dim 128 kernel below).
 //   * softmax in base 2: p = exp2(s * scale * log2 e - m); the reference max m
-//     is only raised when a tile's max exceeds it by more than 8 (p <= 2^8 in
-//     between), which skips most O rescales and is exact for any choice of m.
+//     may lag the true max by up to 8 (p <= 2^8), which skips most O rescales
+//     and is exact for any choice of m.  The head_dim 128 kernel does not even
+//     take a tile's max unless a lane's tile sum exceeds 2^8.
 //   * workgroup ids are remapped so consecutive logical tiles (same head, same
 //     K/V) share an XCD and its L2; the logical order puts the longest rows of
 //     a diagonal segment first.
@@ -316,7 +317,7 @@ void attn_step_bf16(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// head_dim 128: direct-to-LDS K/V, three LDS stages, eight waves.
+// head_dim 128: direct-to-LDS K/V, four LDS stages, eight waves.
 //
 //   * K/V tiles of 64 keys move global -> LDS with buffer_load ... lds (no
 //     register staging); each wave instruction fills four 256-byte rows, and
@@ -393,18 +394,17 @@ __device__ __forceinline__ uint32_t lds_addr(const __attribute__((address_space(
 // ---------------------------------------------------------------------------
 // Eight waves: 256 query rows per workgroup, 32 per wave (one workgroup per
 // CU, still two waves per SIMD).  Every K/V tile in LDS serves 256 rows, so
-// the loads per flop are half those of a four-wave workgroup, and the LDS
-// left free holds a third K/V stage: tile j+2 is loaded while tile j
-// computes, two tiles of latency.
+// the loads per flop are half those of a four-wave workgroup; four K/V
+// stages: tile j+2 is loaded while tile j computes, two tiles of latency.
 //
 // Ring receive (kRecv): the workgroup's share of the next step's K/V is cut
 // into ntiles + 2 slots; at the start of tile j every wave stores slot j
-// (loaded two tiles earlier) and loads slot j + 2, then issues the tile's K/V
-// loads.  Every wave issues exactly one copy store, one copy load and four
-// K/V loads per tile (lanes with nothing to copy repeat a vector of the share:
-// the same bytes to the same place; the K/V loads past the last tile repeat
-// the last tile), so the end-of-tile wait for tile j + 1 is a fixed count of
-// younger loads, vmcnt(5), and a copy access has two tiles to complete.
+// (loaded two tiles earlier) and loads slot j + 2.  Every wave issues exactly
+// one copy store, one copy load and four tile loads per tile (lanes with
+// nothing to copy repeat a vector of the share: the same bytes to the same
+// place; the tile loads past the last tile repeat the last tile), so the
+// end-of-tile wait for tile j + 1 is a fixed count of younger loads,
+// vmcnt(5), and a copy access has two tiles to complete.
 // ---------------------------------------------------------------------------
 
 constexpr int kThreads8 = 512;
