@@ -98,6 +98,8 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      the part that finishes second merges the other's result
                                      (exact LSE merge; no workgroup waits for another).
                                      0: never split. Not used with the separate merge mode. */
+#define CP_ATTN_OPT_COUNTERS 9    /* 1: the step kernels count the key tiles they compute per (rank,
+                                     step) on the device (cp_attn_last_tile_counts) */
 
 /*
  * Create a plan (host only: no device memory, no HIP call).
@@ -216,6 +218,16 @@ int cp_attn_layout_scatter(cp_attn_plan_t plan, const void* src, void* dst, void
  */
 int cp_attn_lse_merge(float* o_acc, float* lse_acc, const float* o_s, const float* lse_s, int64_t rows,
                       int heads, int head_dim, void* stream);
+
+/* Work counters (CP_ATTN_OPT_COUNTERS = 1): counts[rank * cp + step] (n >=
+ * cp*cp) = key tiles the step kernels computed for (rank, step) in the last
+ * forward call, over all heads, or -1 for pairs that call did not run.  A tile
+ * is *tile_rows query rows x *tile_keys keys (32 x 64 for bf16: one wave's
+ * rows; the workgroup tile for fp32), laid from each segment's first row and
+ * key 0, counted when the kernel computed its scores: with segments starting
+ * at multiples of *tile_rows this equals heads x cp_attn_valid_work(rank,
+ * step, *tile_rows, *tile_keys).  Waits for the device. */
+int cp_attn_last_tile_counts(cp_attn_plan_t plan, int64_t* counts, int n, int32_t* tile_rows, int32_t* tile_keys);
 
 /* Per (rank, step) attention-kernel milliseconds of the last forward call
  * made with CP_ATTN_OPT_STEP_TIMING = 1, row-major [cp][cp]; entries of ranks

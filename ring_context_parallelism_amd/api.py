@@ -181,6 +181,19 @@ class Plan:
         N.check(self.lib.cp_attn_last_step_times(self._h, buf, n), "cp_attn_last_step_times")
         return [[buf[r * self.cp_size + s] for s in range(self.cp_size)] for r in range(self.cp_size)]
 
+    def set_counters(self, on):
+        self.set_option(N.OPT_COUNTERS, int(bool(on)))
+
+    def last_tile_counts(self):
+        """([cp][cp] key tiles computed per (rank, step) by the last call, -1 where not run),
+        (tile rows, tile keys))."""
+        n = self.cp_size * self.cp_size
+        buf = (ctypes.c_int64 * n)()
+        tr, tk = ctypes.c_int32(), ctypes.c_int32()
+        N.check(self.lib.cp_attn_last_tile_counts(self._h, buf, n, ctypes.byref(tr), ctypes.byref(tk)),
+                "cp_attn_last_tile_counts")
+        return [[buf[r * self.cp_size + s] for s in range(self.cp_size)] for r in range(self.cp_size)], (tr.value, tk.value)
+
 
 def lse_merge(o_acc, lse_acc, o_s, lse_s, stream=None):
     """In-place exact LSE merge: o_* ``[rows, H, D]`` fp32, lse_* ``[H, rows]`` fp32."""

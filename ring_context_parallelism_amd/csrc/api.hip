@@ -52,6 +52,9 @@ struct DeviceState {
   std::vector<intptr_t> graph_key;
   bool cnt_ready = false;  // the workspace's key-split counters are zero
   int cus = 0;             // compute units of the device
+  // work counters (CP_ATTN_OPT_COUNTERS): key tiles computed per (rank, step)
+  unsigned long long* tile_cnt = nullptr;
+  std::vector<int> counted;  // 1 if (rank, step) was counted by the last call
 };
 
 namespace {
@@ -158,6 +161,8 @@ int ensure_device(Plan& p) {
     d.cnt_ready = true;
   }
   if (!d.cus) CPA_HIP(hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev));
+  if (p.opt_counters && !d.tile_cnt)
+    CPA_HIP(hipMalloc(&d.tile_cnt, size_t(p.cp) * p.cp * sizeof(unsigned long long)));
   if (p.opt_step_timing && d.t0.empty()) {
     const size_t n = size_t(p.cp) * p.cp;
     d.t0.assign(n, nullptr);
@@ -297,6 +302,7 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
   }
   if (sd.nseg == 1) a.seg[1] = SegArgs{};
   if (kernel_recv(p, s)) a.recv = recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1);
+  if (p.opt_counters) a.tile_cnt = d.tile_cnt + size_t(r) * p.cp + s;
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
   return CP_ATTN_OK;
@@ -369,6 +375,11 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
   hipStream_t cs = serial ? st : d.copy;
   hipStream_t ms = serial ? st : d.merge;
 
+  if (p.opt_counters) {
+    // this rank's work counters start at zero (a kernel: graph-safe)
+    CPA_HIP(launch_fill_words(d.tile_cnt + size_t(r) * P, int64_t(P) * 2, 0u, st));
+    for (int s = 0; s < P; ++s) d.counted[size_t(r) * P + s] = 1;
+  }
   // cross-stream events only where another stream waits on them: each
   // record/wait pair costs microseconds of queue latency per step
   bool any_side = false;
@@ -446,6 +457,7 @@ int check_io(const void* q, const void* k, const void* v, const void* out, const
 void reset_timing(Plan& p) {
   DeviceState& d = *p.dev;
   d.timed.assign(size_t(p.cp) * p.cp, 0);
+  d.counted.assign(size_t(p.cp) * p.cp, 0);
 }
 
 void drop_graph(DeviceState& d) {
@@ -466,7 +478,7 @@ int run_graph(Plan& p, const void* q, const void* k, const void* v, void* out, f
   const std::vector<intptr_t> key = {
       intptr_t(q), intptr_t(k), intptr_t(v), intptr_t(out), intptr_t(lse), rank,
       intptr_t(d.ws), intptr_t(d.copy), intptr_t(d.merge), p.dtype, p.opt_merge, p.opt_serialize,
-      p.opt_recv, p.opt_poison, p.opt_recv_blocks, p.opt_ksplit};
+      p.opt_recv, p.opt_poison, p.opt_recv_blocks, p.opt_ksplit, p.opt_counters};
   if (!d.graph || key != d.graph_key) {
     drop_graph(d);
     if (!d.capture) CPA_HIP(hipStreamCreateWithFlags(&d.capture, hipStreamNonBlocking));
@@ -490,6 +502,9 @@ int run_graph(Plan& p, const void* q, const void* k, const void* v, void* out, f
     d.graph_key = key;
   }
   CPA_HIP(hipGraphLaunch(d.graph, st));
+  if (p.opt_counters)  // the graph zeroes and fills the counters of the ranks it holds
+    for (int r = rank < 0 ? 0 : rank; r < (rank < 0 ? p.cp : rank + 1); ++r)
+      for (int s = 0; s < p.cp; ++s) d.counted[size_t(r) * p.cp + s] = 1;
   return CP_ATTN_OK;
 }
 
@@ -539,6 +554,7 @@ int cp_attn_plan_destroy(cp_attn_plan_t h) {
       if (hipDeviceSynchronize() != hipSuccess) rc = fail(CP_ATTN_EHIP, "hipDeviceSynchronize failed in destroy");
       drop_graph(d);
       if (d.capture) (void)hipStreamDestroy(d.capture);
+      if (d.tile_cnt) (void)hipFree(d.tile_cnt);
       if (d.own_ws && d.ws) (void)hipFree(d.ws);
       if (d.own_copy && d.copy) (void)hipStreamDestroy(d.copy);
       if (d.own_merge && d.merge) (void)hipStreamDestroy(d.merge);
@@ -602,6 +618,10 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
     case CP_ATTN_OPT_KSPLIT:
       if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "ksplit option must be 0 or 1");
       p.opt_ksplit = value;
+      return CP_ATTN_OK;
+    case CP_ATTN_OPT_COUNTERS:
+      if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "counters option must be 0 or 1");
+      p.opt_counters = value;
       return CP_ATTN_OK;
     default:
       return fail(CP_ATTN_EINVAL, "unknown option");
@@ -777,6 +797,26 @@ int cp_attn_lse_merge(float* o_acc, float* lse_acc, const float* o_s, const floa
   m.seg_start[0] = 0;
   m.seg_len[0] = int32_t(rows);
   CPA_HIP(launch_merge(m, static_cast<hipStream_t>(stream)));
+  return CP_ATTN_OK;
+}
+
+int cp_attn_last_tile_counts(cp_attn_plan_t h, int64_t* counts, int n, int32_t* tile_rows, int32_t* tile_keys) {
+  CPA_TRY(check_plan(h));
+  const Plan& p = *h->p;
+  if (!counts) return fail(CP_ATTN_EINVAL, "counts is null");
+  const size_t nn = size_t(p.cp) * p.cp;
+  if (n < 0 || size_t(n) < nn) return fail(CP_ATTN_EINVAL, "n < cp_size * cp_size");
+  const bool bf16 = p.dtype == CP_ATTN_BF16;
+  if (tile_rows) *tile_rows = bf16 ? 32 : attn_f32_block_m();
+  if (tile_keys) *tile_keys = bf16 ? 64 : attn_f32_block_n();
+  DeviceState& d = *p.dev;
+  for (size_t i = 0; i < nn; ++i) counts[i] = -1;
+  if (!d.tile_cnt) return CP_ATTN_OK;
+  std::vector<unsigned long long> c(nn);
+  CPA_HIP(hipDeviceSynchronize());
+  CPA_HIP(hipMemcpy(c.data(), d.tile_cnt, nn * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+  for (size_t i = 0; i < nn; ++i)
+    if (i < d.counted.size() && d.counted[i]) counts[i] = int64_t(c[i]);
   return CP_ATTN_OK;
 }
 

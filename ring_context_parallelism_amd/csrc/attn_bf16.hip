@@ -218,10 +218,12 @@ void attn_step_bf16(StepArgs a) {
   }
   if (ntiles > 1) load_tile(kBN);
   __syncthreads();
+  int done = 0;  // key tiles this wave scored (work counter)
   for (int it = 0; it < ntiles; ++it) {
     const int j0 = it * kBN;
     const int buf = it & 1;
     if (j0 < w_max) {
+      ++done;
       const uint16_t* skb = sk[buf];
       const uint16_t* svb = sv[buf];
       // S^T tile: s[kb][i] = score(key j0 + 32 kb + 8 (i/4) + 4 hf + i%4, query row)
@@ -293,6 +295,8 @@ void attn_step_bf16(StepArgs a) {
     __syncthreads();
   }
 
+  if (a.tile_cnt && lane == 0)
+    __hip_atomic_fetch_add(a.tile_cnt, (unsigned long long)done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   l += __shfl_xor(l, 32);
   if (!ok) return;
   const int lrow = g.q_start + row;
@@ -717,6 +721,7 @@ void attn_step_bf16_d128x8(StepArgs a) {
   do {                                                                                     \
     const bool sc_ = kb0 + (J) * kBN < w_max;                                              \
     const bool pv_ = (J) > 0 && kb0 + ((J) - 1) * kBN < w_max;                             \
+    done += sc_;                                                                           \
     if (pv_) pv(vst(((S) + 3) & 3), pb_);                                                  \
     if (sc_) scores(kst(S), s_);                                                           \
   } while (0)
@@ -731,6 +736,7 @@ void attn_step_bf16_d128x8(StepArgs a) {
 
   bf16x8 pb_[2][2];  // probabilities of the last softmaxed tile
   f32x16 s_[2];      // scores of the last scored tile
+  int done = 0;      // key tiles this wave scored (work counter)
   if (wv < 4) {
     for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
       CPATTN_X8_COPY(j, cb);
@@ -759,6 +765,8 @@ void attn_step_bf16_d128x8(StepArgs a) {
 #undef CPATTN_X8_GEMMS
 #undef CPATTN_X8_COPY
 
+  if (a.tile_cnt && lane == 0)
+    __hip_atomic_fetch_add(a.tile_cnt, (unsigned long long)done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   wait_vmem();
   if constexpr (kRecv) {
     // the last two slots (loaded at the last two tiles, or in the prologue),

@@ -61,6 +61,9 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
     o[i] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
+  if (a.tile_cnt && tid == 0)  // work counter: the workgroup computes every key tile below kv_end
+    __hip_atomic_fetch_add(a.tile_cnt, (unsigned long long)((kv_end + kBN - 1) / kBN), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 
   for (int j0 = 0; j0 < kv_end; j0 += kBN) {
     __syncthreads();
@@ -124,6 +127,7 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
 }  // namespace
 
 int attn_f32_block_m() { return kBM; }
+int attn_f32_block_n() { return kBN; }
 
 hipError_t launch_attn_f32(const StepArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid(unsigned(a.total_tiles) * unsigned(a.heads));

@@ -72,6 +72,9 @@ struct StepArgs {
   float* split_o[2];
   float* split_lse[2];
   int32_t* split_cnt;
+  // work counter (null: off): the kernel adds the key tiles it computed, per
+  // wave of 32 rows x 64 keys (bf16 kernels) or per workgroup tile (fp32)
+  unsigned long long* tile_cnt;
 };
 
 // attention step kernels: return hipError_t of the launch
@@ -82,6 +85,7 @@ hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream)
 hipError_t launch_attn_f32(const StepArgs& a, int head_dim, hipStream_t stream);
 int attn_bf16_block_m(int head_dim);
 int attn_f32_block_m();
+int attn_f32_block_n();
 
 // Row copies between natural order and rank-local order.
 //   gather (to_local=1): dst row (rank_begin+i)*n_loc + li  <-  src global_row(rank, li)
@@ -107,6 +111,7 @@ hipError_t launch_recv(const RecvArgs& a, int blocks, hipStream_t stream);
 
 // Fill with NaN (all-ones bytes) -- a kernel, not a memset, so it is safe in captured graphs.
 hipError_t launch_poison(void* ptr, int64_t bytes, hipStream_t stream);
+hipError_t launch_fill_words(void* ptr, int64_t words, uint32_t value, hipStream_t stream);
 
 // Separate LSE merge (part -> acc) for up to two row segments, optionally
 // writing the final output.  rows_* are local rows.

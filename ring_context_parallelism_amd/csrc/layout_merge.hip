@@ -153,6 +153,10 @@ __global__ __launch_bounds__(kThreads) void finalize_rows(FinalizeArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kThreads) void fill_words(uint32_t* p, int64_t n, uint32_t value) {
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads) p[i] = value;
+}
+
 unsigned grid_for(int64_t work_items, int64_t per_block, unsigned cap) {
   int64_t g = (work_items + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -176,6 +180,13 @@ hipError_t launch_recv(const RecvArgs& a, int blocks, hipStream_t stream) {
   if (total == 0) return hipSuccess;
   const unsigned cap = blocks > 0 ? unsigned(blocks) : 65536u;
   recv_copy<<<grid_for(total, 64 * 2, cap), 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// Fill words with a value (a kernel, so that it may sit in a captured graph).
+hipError_t launch_fill_words(void* ptr, int64_t words, uint32_t value, hipStream_t stream) {
+  if (words <= 0) return hipSuccess;
+  fill_words<<<grid_for(words, kThreads, 1024u), kThreads, 0, stream>>>(static_cast<uint32_t*>(ptr), words, value);
   return hipGetLastError();
 }
 

@@ -325,3 +325,35 @@ def test_key_split_matches_oracle(layout, seq, cp, heads, causal):
         torch.cuda.synchronize()
         assert _bitwise_equal(out.cpu(), runs[0][0]) and _bitwise_equal(lse.cpu(), runs[0][1])
     p.close()
+
+
+# --------------------------------------------------------- work counters ----
+
+@pytest.mark.parametrize("dtype,layout,seq,cp,heads", [(torch.bfloat16, "zigzag", 4096, 4, 2),
+                                                       (torch.bfloat16, "contiguous", 4096, 4, 2),
+                                                       (torch.bfloat16, "zigzag", 16384, 4, 16),
+                                                       (torch.float32, "zigzag", 256, 2, 2)])
+def test_device_tile_counts_match_plan(dtype, layout, seq, cp, heads):
+    """The key tiles the step kernels computed, counted on the device per
+    (rank, step), equal heads x the plan's valid tiles at the kernel's tile
+    shape (the imbalance cross-check)."""
+    _say(f"tile counters {dtype} {layout} seq={seq} cp={cp} heads={heads}")
+    dim = 128 if dtype == torch.bfloat16 else 64
+    q, k, v = make_qkv(seq, heads, dim, "bf16" if dtype == torch.bfloat16 else "fp32", 51)
+    p = Plan(seq, cp, heads, dim, True, layout, dtype=dtype)
+    p.set_counters(True)
+    _run(p, q, k, v)
+    counts, (tr, tk) = p.last_tile_counts()
+    for r in range(cp):
+        for s in range(cp):
+            assert counts[r][s] == heads * p.valid_work(r, s, tr, tk)[0], (r, s, counts[r][s])
+    # a rank call counts only that rank
+    dev = _dev()
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    out = torch.empty_like(qd)
+    lse = torch.empty((heads, seq), device=dev)
+    p.rank_forward(qd, kd, vd, out, lse, cp - 1)
+    counts2, _ = p.last_tile_counts()
+    assert counts2[cp - 1] == counts[cp - 1]
+    assert all(c == -1 for r in range(cp - 1) for c in counts2[r])
+    p.close()

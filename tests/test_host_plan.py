@@ -184,6 +184,9 @@ def test_call_error_codes_enqueue_nothing():
     assert lib.cp_attn_set_option(h, N.OPT_KSPLIT, 2) == N.EINVAL
     assert lib.cp_attn_set_option(h, N.OPT_KSPLIT, 0) == N.OK
     assert lib.cp_attn_set_option(h, N.OPT_KSPLIT, 1) == N.OK
+    assert lib.cp_attn_set_option(h, N.OPT_COUNTERS, 2) == N.EINVAL
+    assert lib.cp_attn_set_option(h, N.OPT_COUNTERS, 0) == N.OK
+    assert lib.cp_attn_last_tile_counts(h, None, 4, None, None) == N.EINVAL
     assert lib.cp_attn_set_workspace(h, ctypes.c_void_p(256), 16) == N.ENOWORKSPACE
     assert lib.cp_attn_set_workspace(h, ctypes.c_void_p(100), 1 << 30) == N.EINVAL
     assert lib.cp_attn_step_source(h, 0, 5, ctypes.byref(ctypes.c_int32())) == N.EINVAL
