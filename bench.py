@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip imbalance / mode / parity side measurements")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=40.0,
+                    help="bound on the oracle's CPU time (the 32k/cp8 rank-0 share takes about 25 s)")
     ap.add_argument("--recv", choices=["kernel", "memcpy", "fused", "hybrid"], default=None, help="ring receive path (default: library's)")
     ap.add_argument("--recv-blocks", type=int, default=None, help="grid bound of the receive copy kernel")
     ap.add_argument("--serialize", action="store_true", help="run the whole schedule on one stream")
@@ -76,14 +77,15 @@ def time_calls(plan, w, bufs, stream, steps, warmup, warmup_seconds=0.0):
         if n % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         run_call(plan, w, bufs, stream)
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    time_calls.last = {"median": float(np.median(per)), "min": float(np.min(per))}
+    return ev[0].elapsed_time(ev[steps]) / steps
 
 
 def step_kernel_times(plan, w, bufs, stream, reps, graph=False):
@@ -128,8 +130,11 @@ def recorded_traffic(workload):
     return int(fields["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in fields else None
 
 
-def cpu_baseline(w, q, k, v, target_s):
-    """The fp64 oracle on a bounded sample of the same share, timed on the host."""
+def cpu_baseline(w, q, k, v, out, lse, target_s):
+    """The fp64 oracle on the same share, timed on the host: every row of the
+    share (at most 4096) and heads until target_s has passed; its results are
+    also compared with the GPU's output of the timed call (parity over the
+    rows and heads it covered)."""
     import oracle
     from ring_context_parallelism_amd.inputs import to_numpy_f64
     try:
@@ -139,25 +144,35 @@ def cpu_baseline(w, q, k, v, target_s):
         threads = 1
     ranks = range(w.cp) if w.rank is None else [w.rank]
     rows = np.concatenate([oracle.rank_positions(w.seq_len, w.cp, r, w.layout) for r in ranks])
-    rows = rows[:: max(1, rows.size // 2048)][:2048]
+    rows = rows[:: max(1, rows.size // 4096)][:4096]
     kpos = np.arange(w.seq_len)
+    out_c = out.cpu()
+    lse_c = lse.cpu()
     flops = 0
     heads_done = 0
-    t0 = time.perf_counter()
+    d_o = d_l = 0.0
+    t_cpu = 0.0
     for h in range(w.heads):
         qh = to_numpy_f64(q[torch.from_numpy(rows), h:h + 1])
         kh = to_numpy_f64(k[:, h:h + 1])
         vh = to_numpy_f64(v[:, h:h + 1])
-        oracle.attention(qh, kh, vh, causal=w.causal, q_pos=rows, k_pos=kpos)
+        t0 = time.perf_counter()
+        o_ref, l_ref = oracle.attention(qh, kh, vh, causal=w.causal, q_pos=rows, k_pos=kpos)
+        t_cpu += time.perf_counter() - t0
         pairs = int((rows + 1).sum()) if w.causal else rows.size * w.seq_len
         flops += oracle.valid_flops(pairs, 1, w.head_dim)
         heads_done += 1
-        if time.perf_counter() - t0 >= target_s:
+        o_got = out_c[torch.from_numpy(rows), h:h + 1].to(torch.float64).numpy()
+        l_got = lse_c[h, torch.from_numpy(rows)].to(torch.float64).numpy()
+        d_o = max(d_o, float(np.max(np.abs(o_got - o_ref))))
+        d_l = max(d_l, float(np.max(np.abs(l_got - l_ref[0]))))
+        if t_cpu >= target_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows.size} of the share's rows (evenly spaced) x {heads_done} head(s), every valid key, "
-                      f"fp64 numpy; {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
+    whole = rows.size == sum(oracle.rank_positions(w.seq_len, w.cp, r, w.layout).size for r in ranks)
+    return {"value": flops / t_cpu / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{'the whole share: ' if whole else ''}{rows.size} rows x {heads_done} of {w.heads} heads, "
+                       f"every valid key, fp64 numpy; {flops / 1e9:.1f} GFLOP in {t_cpu:.1f} s"),
+            "parity": {"rows": int(rows.size), "heads": heads_done, "max_abs_dO": d_o, "max_abs_dLSE": d_l}}
 
 
 def imbalance_section(stream):
@@ -173,7 +188,11 @@ def imbalance_section(stream):
         out = torch.empty_like(q)
         lse = torch.empty(w.heads, w.seq_len, device="cuda")
         bufs = (q, k, v, out, lse)
+        p.set_counters(True)
         run_call(p, w, bufs, stream)
+        dev_tiles, (tr, tk) = p.last_tile_counts()
+        p.set_counters(False)
+        plan_fine = [[w.heads * p.valid_work(r, s, tr, tk)[0] for s in range(w.cp)] for r in range(w.cp)]
         times = step_kernel_times(p, w, bufs, stream, 3)
         ms = time_calls(p, w, bufs, stream, 5, 1)
         def imb(tab):
@@ -184,6 +203,8 @@ def imbalance_section(stream):
         per_t, agg_t = imb(tiles)
         per_m, agg_m = imb(times)
         res[layout] = {"tiles_128x64": tiles, "tile_imbalance_per_step": per_t, "tile_imbalance": agg_t,
+                       f"device_tiles_{tr}x{tk}_all_heads": dev_tiles,
+                       "device_tiles_match_plan": dev_tiles == plan_fine,
                        "step_ms": [[round(float(x), 4) for x in row] for row in times],
                        "time_imbalance_per_step": per_m, "time_imbalance": agg_m,
                        "full_forward_ms": round(ms, 4)}
@@ -272,6 +293,7 @@ def main():
     pairs = share_pairs(plan, w)
     flops = 4 * w.head_dim * w.heads * pairs
     ms = time_calls(plan, w, bufs, stream, args.steps, args.warmup, args.warmup_seconds)
+    call_stats = dict(time_calls.last)
     tflops = flops / (ms * 1e-3) / 1e12
     print(f"[bench] {w.name}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
@@ -298,6 +320,8 @@ def main():
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
     }
+    result["ms_per_call_median"] = round(call_stats["median"], 5)
+    result["ms_per_call_min"] = round(call_stats["min"], 5)
 
     if not args.no_extras:
         # same share, other schedule modes (exposed copy / merge cost)
@@ -340,7 +364,10 @@ def main():
         result["imbalance"]["zigzag_step_time_imbalance"] = result["imbalance"]["zigzag"]["time_imbalance"]
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, args.cpu_seconds)
+        run_call(plan, w, bufs, stream)
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, out, lse, args.cpu_seconds)
+        result["parity_oracle_share"] = result["cpu_baseline"].pop("parity")
 
     props = torch.cuda.get_device_properties(0)
     result["env"] = {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,

@@ -721,7 +721,6 @@ void attn_step_bf16_d128x8(StepArgs a) {
   do {                                                                                     \
     const bool sc_ = kb0 + (J) * kBN < w_max;                                              \
     const bool pv_ = (J) > 0 && kb0 + ((J) - 1) * kBN < w_max;                             \
-    done += sc_;                                                                           \
     if (pv_) pv(vst(((S) + 3) & 3), pb_);                                                  \
     if (sc_) scores(kst(S), s_);                                                           \
   } while (0)
@@ -736,7 +735,6 @@ void attn_step_bf16_d128x8(StepArgs a) {
 
   bf16x8 pb_[2][2];  // probabilities of the last softmaxed tile
   f32x16 s_[2];      // scores of the last scored tile
-  int done = 0;      // key tiles this wave scored (work counter)
   if (wv < 4) {
     for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
       CPATTN_X8_COPY(j, cb);
@@ -765,8 +763,13 @@ void attn_step_bf16_d128x8(StepArgs a) {
 #undef CPATTN_X8_GEMMS
 #undef CPATTN_X8_COPY
 
-  if (a.tile_cnt && lane == 0)
+  if (a.tile_cnt && lane == 0) {
+    // work counter: the tiles whose scores the loops computed (their condition,
+    // kb0 + j kBN < w_max, over j < ntiles); kept out of the loop, where a
+    // counter would cost registers the receive kernel beside this one needs
+    const int done = min(ntiles, max(0, (w_max - kb0 + kBN - 1) / kBN));
     __hip_atomic_fetch_add(a.tile_cnt, (unsigned long long)done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   wait_vmem();
   if constexpr (kRecv) {
     // the last two slots (loaded at the last two tiles, or in the prologue),

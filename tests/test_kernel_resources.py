@@ -1,0 +1,56 @@
+"""Register budget of the head_dim-128 step kernel (CPU only: compiles the
+kernel source for gfx950 and reads the resources the compiler assigns).
+
+Two waves of the step kernel share each SIMD's 512 VGPRs.  The ring-receive
+copy kernel (one wave per workgroup, 16 VGPRs) runs beside it on the copy
+stream only while each step-kernel wave leaves room for it, i.e. takes at
+most 240 VGPRs (allocation granule 8); above that the copy waits for the
+step kernel and the whole call slows down by about a third.  No variant may
+spill to scratch (a scratch reload waits for every load in flight, which
+would collapse the direct-to-LDS pipeline).
+"""
+
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from ring_context_parallelism_amd import build as B
+
+
+def _resources():
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "attn_bf16.s")
+        flags = [f for f in B.COMMON if f != "-fPIC"]
+        cmd = [B.hipcc(), "-x", "hip", *B.HIP_FLAGS, *flags, "--cuda-device-only", "-S",
+               os.path.join(B.CSRC, "attn_bf16.hip"), "-o", out]
+        subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+        text = open(out).read()
+    res = {}
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, re.S):
+        body = m.group(2)
+        get = lambda key: int(re.search(rf"\.amdhsa_{key} (\d+)", body).group(1))
+        res[m.group(1)] = {"vgpr": get("next_free_vgpr"), "scratch": get("private_segment_fixed_size")}
+    return res
+
+
+@pytest.fixture(scope="module")
+def resources():
+    try:
+        B.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    return _resources()
+
+
+def test_step_kernel_leaves_room_for_the_receive_kernel(resources):
+    plain = [v for k, v in resources.items() if "attn_step_bf16_d128x8ILb0E" in k]
+    assert len(plain) == 1, sorted(resources)
+    assert plain[0]["vgpr"] <= 240, plain[0]
+
+
+def test_no_kernel_spills_to_scratch(resources):
+    for name, r in resources.items():
+        assert r["scratch"] == 0, (name, r)
