@@ -345,9 +345,23 @@ def main():
         plan.set_graph(not args.graph)
         ms_graph_other = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
         plan.set_graph(args.graph)
+        ms_allgather = None
+        if w.rank is not None:
+            # the same share in one launch against the whole K/V (no ring steps, no merge)
+            ag_calls = max(3, args.steps // 4)
+            plan.allgather_forward(*bufs, w.rank, stream=stream)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(ag_calls):
+                plan.allgather_forward(*bufs, w.rank, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_allgather = round(e0.elapsed_time(e1) / ag_calls, 5)
         result["modes_ms"] = {"default_receive": args.recv or "kernel",
                               "graph_mode": bool(args.graph),
                               ("eager_calls" if args.graph else "graph_replay"): ms_graph_other,
+                              "allgather_single_launch": ms_allgather,
                               "overlapped_fused_merge": round(ms, 5), "serialized_fused_merge": round(ms_serial, 5),
                               "overlapped_separate_merge": round(ms_sep, 5),
                               "receive_kernel_grid_blocks_ms": ms_blocks,

@@ -163,6 +163,16 @@ int cp_attn_set_streams(cp_attn_plan_t plan, void* copy_stream, void* merge_stre
 int cp_attn_rank_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
                          float* lse, int rank, void* stream);
 
+/* All-gather variant of one rank's share: the rank's rows against the whole
+ * natural-order K/V in a single launch of the step kernel (the K/V of every
+ * rank at once, as after an all-gather), with no ring steps, no receive and no
+ * merge; each owned chunk sees the keys before it (causal) or all keys
+ * (bidirectional).  Same result as cp_attn_rank_forward up to rounding order.
+ * Same arguments and errors as cp_attn_rank_forward, and EUNSUPPORTED when
+ * the K/V tensors exceed 4 GiB.  Uses no workspace. */
+int cp_attn_allgather_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
+                              float* lse, int rank, void* stream);
+
 /* Every rank's share back to back on `stream` (ranks 0..cp_size-1); fills all
  * rows of out and lse.  Same arguments and errors as cp_attn_rank_forward. */
 int cp_attn_full_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,

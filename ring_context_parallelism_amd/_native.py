@@ -61,6 +61,7 @@ SIGNATURES = {
     "cp_attn_layout_scatter": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p]),
     "cp_attn_lse_merge": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i64, ctypes.c_int, ctypes.c_int, _c_p]),
     "cp_attn_last_step_times": (ctypes.c_int, [_c_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int]),
+    "cp_attn_allgather_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_p]),
     "cp_attn_last_tile_counts": (ctypes.c_int, [_c_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
                                                 ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
     "cp_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -121,6 +121,11 @@ class Plan:
         N.check(self.lib.cp_attn_rank_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(rank),
                                               _stream_ptr(stream)), "cp_attn_rank_forward")
 
+    def allgather_forward(self, q, k, v, out, lse, rank, stream=None):
+        self._check_io(q, k, v, out, lse)
+        N.check(self.lib.cp_attn_allgather_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(rank),
+                                                   _stream_ptr(stream)), "cp_attn_allgather_forward")
+
     def full_forward(self, q, k, v, out, lse, stream=None):
         self._check_io(q, k, v, out, lse)
         N.check(self.lib.cp_attn_full_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),

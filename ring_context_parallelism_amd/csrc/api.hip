@@ -676,6 +676,61 @@ int cp_attn_rank_forward(cp_attn_plan_t h, const void* q, const void* k, const v
   CPA_GUARD_END
 }
 
+// All-gather variant: rank r's rows against the whole natural-order K/V in one
+// launch of the step kernel.  Each owned chunk is one segment whose keys are
+// the global prefix before the chunk (every row sees it) plus the causal
+// diagonal inside the chunk (all keys when bidirectional); the key map is the
+// identity, and the epilogue writes O and LSE straight to the global rows.
+int cp_attn_allgather_forward(cp_attn_plan_t h, const void* q, const void* k, const void* v, void* out, float* lse,
+                              int rank, void* stream) {
+  CPA_GUARD_BEGIN
+  CPA_TRY(check_plan(h));
+  Plan& p = *h->p;
+  if (rank < 0 || rank >= p.cp) return fail(CP_ATTN_EINVAL, "rank outside [0, cp_size)");
+  CPA_TRY(check_io(q, k, v, out, lse));
+  CPA_TRY(ensure_device(p));
+  const bool bf16 = p.dtype == CP_ATTN_BF16;
+  const int bm = bf16 ? attn_bf16_block_m(p.head_dim) : attn_f32_block_m();
+  if (p.seq_len * p.heads * p.head_dim * p.elem_bytes() > int64_t(UINT32_MAX))
+    return fail(CP_ATTN_EUNSUPPORTED, "K/V beyond 4 GiB: too large for the all-gather launch");
+  StepArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_bytes = p.seq_len * p.heads * p.head_dim * p.elem_bytes();
+  a.kv_lo = 0;
+  a.kv_hi = 0;
+  a.kv_split = int32_t(p.seq_len);
+  a.out = out;
+  a.lse = lse;
+  a.seq_len = p.seq_len;
+  a.n_loc = int32_t(p.seq_len);  // keys addressable through the identity map
+  a.heads = p.heads;
+  a.scale = 1.0f / std::sqrt(float(p.head_dim));
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.out_f32 = p.dtype == CP_ATTN_FP32;
+  const int nch = p.layout == 1 ? 2 : 1;
+  a.nseg = nch;
+  for (int c = 0; c < nch; ++c) {
+    const int64_t g0 = p.global_row(rank, c * p.chunk);
+    SegArgs& x = a.seg[c];
+    x.q_global = g0;
+    x.q_start = int32_t(c * p.chunk);
+    x.q_len = int32_t(p.chunk);
+    x.kv_full = int32_t(p.causal ? g0 : p.seq_len);
+    x.diag = p.causal ? 1 : 0;
+    x.ksplit = 1;
+    x.tiles = int32_t((p.chunk + bm - 1) / bm);
+    x.epi = kEpiInit | kEpiFinal;
+    a.total_tiles += x.tiles;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
+  if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
+  return CP_ATTN_OK;
+  CPA_GUARD_END
+}
+
 int cp_attn_full_forward(cp_attn_plan_t h, const void* q, const void* k, const void* v, void* out, float* lse,
                          void* stream) {
   CPA_GUARD_BEGIN

@@ -357,3 +357,41 @@ def test_device_tile_counts_match_plan(dtype, layout, seq, cp, heads):
     assert counts2[cp - 1] == counts[cp - 1]
     assert all(c == -1 for r in range(cp - 1) for c in counts2[r])
     p.close()
+
+
+# ------------------------------------------------------ all-gather variant ----
+
+@pytest.mark.parametrize("dtype,layout,causal,seq,cp,heads", [(torch.bfloat16, "zigzag", True, 8192, 4, 2),
+                                                              (torch.bfloat16, "contiguous", True, 6144, 3, 2),
+                                                              (torch.bfloat16, "contiguous", False, 4096, 4, 2),
+                                                              (torch.float32, "zigzag", True, 256, 2, 2)])
+def test_allgather_forward_matches_oracle_and_ring(dtype, layout, causal, seq, cp, heads):
+    """One launch of the rank's rows against the whole K/V: the oracle's
+    result on every row of the rank, and the ring forward's within the
+    tolerance (the two differ only in rounding order)."""
+    _say(f"all-gather {dtype} {layout} causal={causal} seq={seq} cp={cp}")
+    dim = 128 if dtype == torch.bfloat16 else 64
+    q, k, v = make_qkv(seq, heads, dim, "bf16" if dtype == torch.bfloat16 else "fp32", 61)
+    p = Plan(seq, cp, heads, dim, causal, layout, dtype=dtype)
+    dev = _dev()
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    tol_o, tol_l = TOL[dtype]
+    for r in range(cp):
+        out = torch.full_like(qd, float("nan"))
+        lse = torch.full((heads, seq), float("nan"), device=dev)
+        p.allgather_forward(qd, kd, vd, out, lse, r)
+        out_ring = torch.full_like(qd, float("nan"))
+        lse_ring = torch.full((heads, seq), float("nan"), device=dev)
+        p.rank_forward(qd, kd, vd, out_ring, lse_ring, r)
+        torch.cuda.synchronize()
+        rows = oracle.rank_positions(seq, cp, r, layout)
+        sub = rows[:: max(1, rows.size // 96)]
+        d_o, d_l = _compare(out.cpu(), lse.cpu(), q, k, v, causal, dtype, rows=sub)
+        assert d_o <= tol_o and d_l <= tol_l, (r, d_o, d_l)
+        o_a, o_r = out.cpu()[rows].float(), out_ring.cpu()[rows].float()
+        assert float((o_a - o_r).abs().max()) <= tol_o
+        assert float((lse.cpu()[:, rows] - lse_ring.cpu()[:, rows]).abs().max()) <= tol_l
+        # rows of other ranks are untouched
+        others = np.setdiff1d(np.arange(seq), rows)
+        assert torch.isnan(out.cpu()[others].float()).all()
+    p.close()
