@@ -20,8 +20,9 @@ Sources (pages, cited by title and section):
   (section "Sequence Partitioning Across GPUs").
 * "Context Parallelism for Long-Context Training" (jpcasabianca.com) --
   equivalence against the unsharded reference (section "Prove attention
-  equivalence") and shard coverage (section "Test sequence divisibility and
-  padding").
+  equivalence"), shard coverage and padding of awkward lengths (section "Test
+  sequence divisibility and padding": pad ownership, masked pad keys and
+  queries, real outputs unchanged by the padding).
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, invariants, brute force or an independent library
@@ -31,6 +32,7 @@ routine; none is "parity unpinned".
 from .attention import attention, attention_probabilities, valid_mask
 from .cp_reference import (
     chunk_size,
+    padded_length,
     rank_chunks,
     rank_positions,
     ring_source,
@@ -48,6 +50,7 @@ __all__ = [
     "attention_probabilities",
     "valid_mask",
     "chunk_size",
+    "padded_length",
     "rank_chunks",
     "rank_positions",
     "ring_source",

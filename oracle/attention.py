@@ -38,24 +38,30 @@ def _as_f64(x):
     return a
 
 
-def valid_mask(q_pos, k_pos, causal):
+def valid_mask(q_pos, k_pos, causal, k_valid=None):
     """Boolean ``[len(q_pos), len(k_pos)]`` mask of valid (query, key) pairs.
 
     Causal: a key is valid when its global position is not after the query's.
-    Bidirectional: every pair is valid.
+    Bidirectional: every pair is valid.  ``k_valid`` (optional, per key) masks
+    keys out entirely, as padded keys are.
     """
     q_pos = np.asarray(q_pos, dtype=np.int64)
     k_pos = np.asarray(k_pos, dtype=np.int64)
     if not causal:
-        return np.ones((q_pos.size, k_pos.size), dtype=bool)
-    return k_pos[None, :] <= q_pos[:, None]
+        m = np.ones((q_pos.size, k_pos.size), dtype=bool)
+    else:
+        m = k_pos[None, :] <= q_pos[:, None]
+    if k_valid is not None:
+        m = m & np.asarray(k_valid, dtype=bool)[None, :]
+    return m
 
 
-def attention(q, k, v, *, causal, scale=None, q_pos=None, k_pos=None, block=1024):
+def attention(q, k, v, *, causal, scale=None, q_pos=None, k_pos=None, k_valid=None, block=1024):
     """Unsplit softmax attention.
 
     q: ``[Sq, H, D]``; k, v: ``[Sk, H, D]`` (any real dtype; upcast to fp64).
     q_pos, k_pos: global token positions of the rows (default ``arange``).
+    k_valid: optional per-key flags; False keys are masked out (padding).
     Returns ``(O [Sq, H, D] fp64, LSE [H, Sq] fp64)``.
     """
     q = _as_f64(q)
@@ -80,7 +86,7 @@ def attention(q, k, v, *, causal, scale=None, q_pos=None, k_pos=None, block=1024
         for i0 in range(0, sq, block):
             i1 = min(sq, i0 + block)
             s = scale * (q[i0:i1, h, :] @ kh.T)
-            valid = valid_mask(q_pos[i0:i1], k_pos, causal)
+            valid = valid_mask(q_pos[i0:i1], k_pos, causal, k_valid)
             s = np.where(valid, s, -np.inf)
             m = s.max(axis=1)
             has = np.isfinite(m)

@@ -22,6 +22,14 @@ This module has its own chunk map; it does not use the HIP library's plan.
 * Exact merge (section 4): each step yields a partial ``(O_s, lse_s)`` over the
   keys present; partials are folded with log-sum-exp weights, which reproduces
   the unsplit softmax exactly up to rounding.
+* Padding ("Context Parallelism for Long-Context Training", section "Test
+  sequence divisibility and padding": define pad ownership, mask padded keys
+  and queries; masked padding must not alter real-token outputs).  A length
+  that does not divide into the chunks is padded at the end to the next
+  multiple; the pad positions belong to the rank that owns their chunk, are
+  never attended as keys and produce no output.  ``rank_positions`` lists the
+  real positions only; for any chunk the real positions are a prefix of it,
+  so a rank's real rows keep their local indices.
 * Work counts (section 3): per ring iteration, the number of valid (q, k)
   pairs and of BMxBN tiles holding at least one valid pair, per rank; the
   imbalance of an iteration is max over ranks / mean over ranks, and the
@@ -39,20 +47,26 @@ CONTIGUOUS = "contiguous"
 def _check(seq_len, cp, layout):
     if cp < 1:
         raise ValueError("cp must be >= 1")
-    if layout == ZIGZAG:
-        if seq_len % (2 * cp):
-            raise ValueError("zigzag needs seq_len divisible by 2*cp")
-    elif layout == CONTIGUOUS:
-        if seq_len % cp:
-            raise ValueError("contiguous needs seq_len divisible by cp")
-    else:
+    if seq_len < 1:
+        raise ValueError("seq_len must be >= 1")
+    if layout not in (ZIGZAG, CONTIGUOUS):
         raise ValueError(f"unknown layout {layout!r}")
 
 
-def chunk_size(seq_len, cp, layout):
-    """Length of one chunk: ``S/(2cp)`` for zigzag, ``S/cp`` for contiguous."""
+def _parts(cp, layout):
+    return 2 * cp if layout == ZIGZAG else cp
+
+
+def padded_length(seq_len, cp, layout):
+    """``seq_len`` rounded up to a multiple of the number of chunks."""
     _check(seq_len, cp, layout)
-    return seq_len // (2 * cp) if layout == ZIGZAG else seq_len // cp
+    n = _parts(cp, layout)
+    return -(-seq_len // n) * n
+
+
+def chunk_size(seq_len, cp, layout):
+    """Length of one chunk of the padded sequence: ``S_pad/(2cp)`` (zigzag) or ``S_pad/cp``."""
+    return padded_length(seq_len, cp, layout) // _parts(cp, layout)
 
 
 def rank_chunks(cp, layout):
@@ -65,9 +79,10 @@ def rank_chunks(cp, layout):
 
 
 def rank_positions(seq_len, cp, rank, layout):
-    """Global token positions of rank ``rank``'s local rows, in local order."""
+    """Global token positions of rank ``rank``'s real local rows, in local order
+    (pad positions, at or past ``seq_len``, are left out)."""
     c = chunk_size(seq_len, cp, layout)
-    parts = [np.arange(ch * c, (ch + 1) * c, dtype=np.int64) for ch in rank_chunks(cp, layout)[rank]]
+    parts = [np.arange(ch * c, min((ch + 1) * c, seq_len), dtype=np.int64) for ch in rank_chunks(cp, layout)[rank]]
     return np.concatenate(parts)
 
 

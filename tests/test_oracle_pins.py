@@ -222,11 +222,87 @@ def test_ring_sources_visit_every_rank_once(cp):
             assert oracle.ring_source(r, s + 1, cp) == oracle.ring_source((r - 1) % cp, s, cp)
 
 
-def test_bad_divisibility_rejected():
-    with pytest.raises(ValueError):
-        oracle.rank_positions(100, 3, 0, "zigzag")
-    with pytest.raises(ValueError):
-        oracle.rank_positions(10, 4, 0, "contiguous")
+def test_bad_arguments_rejected():
+    for args in ((0, 2, 0, "zigzag"), (10, 0, 0, "zigzag"), (10, 2, 0, "diagonal")):
+        with pytest.raises(ValueError):
+            oracle.rank_positions(*args)
+
+
+# --------------------------------------------------------------------------
+# Awkward lengths: padding ("Context Parallelism for Long-Context Training",
+# section "Test sequence divisibility and padding")
+# --------------------------------------------------------------------------
+
+AWKWARD = [1, 2, 5, 7, 13, 31, 47, 100, 101, 1003]
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
+def test_padded_map_is_the_divisible_map_without_the_tail(layout, cp):
+    """Pad ownership: rank r's positions at length S are those it owns at the
+    padded length (a multiple of the chunk count, where the map is the page's)
+    that fall below S, in the same order; and every real token is owned once."""
+    parts = 2 * cp if layout == "zigzag" else cp
+    for seq in AWKWARD:
+        pad = oracle.padded_length(seq, cp, layout)
+        assert pad % parts == 0 and seq <= pad < seq + parts  # the smallest multiple of parts >= S
+        assert oracle.chunk_size(seq, cp, layout) == -(-seq // parts)
+        flat = []
+        for r in range(cp):
+            full = oracle.rank_positions(pad, cp, r, layout)
+            got = oracle.rank_positions(seq, cp, r, layout)
+            assert full.size == pad // cp
+            assert got.tolist() == [x for x in full.tolist() if x < seq]
+            # the real rows are a prefix of the rank's local buffer
+            assert got.tolist() == full[:got.size].tolist()
+            flat += got.tolist()
+        assert sorted(flat) == list(range(seq))
+
+
+def test_padded_map_small_case_by_hand():
+    """S = 5, cp = 2, zigzag: 4 chunks of 2 over 8 padded positions; rank 0
+    owns chunks 0 and 3 = {0, 1} + {6, 7} (pad), rank 1 chunks 1 and 2 =
+    {2, 3} + {4, 5} (5 is pad)."""
+    assert oracle.rank_positions(5, 2, 0, "zigzag").tolist() == [0, 1]
+    assert oracle.rank_positions(5, 2, 1, "zigzag").tolist() == [2, 3, 4]
+    # contiguous, S = 5, cp = 4: chunks of 2 -> {0,1}, {2,3}, {4}, {}
+    assert [oracle.rank_positions(5, 4, r, "contiguous").tolist() for r in range(4)] == [[0, 1], [2, 3], [4], []]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_masked_padding_leaves_real_outputs_unchanged(causal):
+    """The page's decision rule: appending masked pad tokens (with arbitrary,
+    even huge, values) must not change any real token's output or LSE."""
+    seq, pad, heads, dim = 11, 5, 2, 4
+    q, k, v = (_rand((seq + pad, heads, dim), 70 + i) for i in range(3))
+    k[seq:] *= 1e3
+    v[seq:] = 1e6
+    valid = np.arange(seq + pad) < seq
+    o_ref, lse_ref = _brute_force(q[:seq], k[:seq], v[:seq], causal, 1 / math.sqrt(dim))
+    o, lse = oracle.attention(q, k, v, causal=causal, k_valid=valid)
+    assert np.max(np.abs(o[:seq] - o_ref)) <= 1e-12
+    assert np.max(np.abs(lse[:, :seq] - lse_ref)) <= 1e-12
+    if not causal:  # pad queries see only the real keys as well
+        assert np.all(np.isfinite(o[seq:]))
+
+
+def test_planted_unmasked_padding_is_caught():
+    """Without the key mask the pad keys change the real outputs."""
+    seq, pad, heads, dim = 11, 5, 2, 4
+    q, k, v = (_rand((seq + pad, heads, dim), 70 + i) for i in range(3))
+    v[seq:] = 1e6
+    o_ref, _ = _brute_force(q[:seq], k[:seq], v[:seq], False, 1 / math.sqrt(dim))
+    o, _ = oracle.attention(q, k, v, causal=False)
+    assert np.max(np.abs(o[:seq] - o_ref)) > 1.0
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+def test_pairs_sum_to_causal_triangle_at_awkward_lengths(layout):
+    for seq, cp in ((100, 3), (1003, 4), (5, 4), (47, 8)):
+        tot = sum(oracle.step_valid_pairs(seq, cp, layout, True, r, s) for r in range(cp) for s in range(cp))
+        assert tot == seq * (seq + 1) // 2
+        tot = sum(oracle.step_valid_pairs(seq, cp, layout, False, r, s) for r in range(cp) for s in range(cp))
+        assert tot == seq * seq
 
 
 # --------------------------------------------------------------------------
@@ -264,7 +340,10 @@ def test_merge_of_key_split_equals_whole():
 
 CASES = [(256, 2, "zigzag", True), (96, 3, "zigzag", True), (64, 4, "contiguous", True),
          (64, 4, "zigzag", False), (48, 1, "zigzag", True), (80, 5, "contiguous", False),
-         (128, 8, "zigzag", True)]
+         (128, 8, "zigzag", True),
+         # awkward lengths (padded): tail chunks partly or wholly pad, ranks with no real row
+         (100, 3, "zigzag", True), (101, 4, "zigzag", False), (5, 4, "zigzag", True),
+         (10, 4, "contiguous", True), (13, 3, "contiguous", False), (47, 8, "zigzag", True)]
 
 
 @pytest.mark.parametrize("seq,cp,layout,causal", CASES)
@@ -377,7 +456,7 @@ def test_golden_hashes_and_oracle_summary():
 
 def test_planted_mask_off_by_one_is_caught(monkeypatch):
     """A mask that drops the diagonal breaks the zero-query closed form."""
-    def strict(q_pos, k_pos, causal):
+    def strict(q_pos, k_pos, causal, k_valid=None):
         q_pos = np.asarray(q_pos)
         k_pos = np.asarray(k_pos)
         return k_pos[None, :] < q_pos[:, None] if causal else np.ones((q_pos.size, k_pos.size), bool)
