@@ -61,8 +61,8 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
 #define CP_ATTN_EHIP (-4)         /* a HIP runtime call or kernel launch failed */
 
 /* Chunk placement. */
-#define CP_ATTN_CONTIGUOUS 0 /* rank r owns tokens [r*S/cp, (r+1)*S/cp) */
-#define CP_ATTN_ZIGZAG 1     /* rank r owns chunks r and 2*cp-1-r of S/(2*cp) tokens, early chunk first */
+#define CP_ATTN_CONTIGUOUS 0 /* rank r owns tokens [r*L, (r+1)*L), L = ceil(S/cp) */
+#define CP_ATTN_ZIGZAG 1     /* rank r owns chunks r and 2*cp-1-r of C = ceil(S/(2*cp)) tokens, early chunk first */
 
 /* Element types of q, k, v and out (lse is always fp32). */
 #define CP_ATTN_BF16 0
@@ -108,14 +108,21 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
  *   heads    > 0 (K/V heads equal query heads);
  *   head_dim 64 or 128;
  *   causal   1 causal, 0 bidirectional;
- *   layout   CP_ATTN_ZIGZAG (S % (2*cp_size) == 0) or CP_ATTN_CONTIGUOUS (S % cp_size == 0).
+ *   layout   CP_ATTN_ZIGZAG or CP_ATTN_CONTIGUOUS.
  * Per-rank length is S / cp_size ("Context Parallelism in MegaDLMs", section
- * "Sequence Partitioning Across GPUs").  Degrees that do not divide the
- * sequence are rejected ("Context Parallelism for Long-Context Training",
- * section "Sweep the smallest useful degree").
- * Returns EINVAL for non-positive sizes, a bad flag or layout, or a
- * non-dividing length; EUNSUPPORTED for another head_dim, cp_size > 256, or
- * seq_len * heads * head_dim * 4 >= 2^32 (device offsets are 32-bit).
+ * "Sequence Partitioning Across GPUs").  A length that does not divide into
+ * the 2*cp_size (zigzag) or cp_size (contiguous) chunks is padded at the end
+ * to the next multiple, S_pad ("Context Parallelism for Long-Context
+ * Training", section "Test sequence divisibility and padding"): chunk c holds
+ * positions [c*C, (c+1)*C) of the padded sequence, of which those below S are
+ * real.  A pad position belongs to the rank owning its chunk; pad keys are
+ * never attended and pad queries produce no output, so every real token's
+ * result equals that of unpadded attention.  A rank's real rows are the first
+ * cp_attn_rank_valid_rows of its local buffer.  The natural-order tensors
+ * still hold S rows: pad rows exist only in the local layout.
+ * Returns EINVAL for non-positive sizes or a bad flag or layout; EUNSUPPORTED
+ * for another head_dim, cp_size > 256, or S_pad * heads * head_dim * 4 >=
+ * 2^32 (device offsets are 32-bit).
  * On success *out owns the plan; free it with cp_attn_plan_destroy.
  */
 int cp_attn_plan(int64_t seq_len, int cp_size, int heads, int head_dim, int causal, int layout,
@@ -180,8 +187,13 @@ int cp_attn_full_forward(cp_attn_plan_t plan, const void* q, const void* k, cons
 
 /* ---- host-only introspection (no HIP calls; CPU-testable) ---- */
 
-/* Rows (tokens) each rank owns: 2*S/(2*cp) zigzag, S/cp contiguous. */
+/* Rows of each rank's local buffer, pad rows included: S_pad/cp. */
 int cp_attn_local_rows(cp_attn_plan_t plan, int64_t* rows);
+
+/* Real (non-pad) rows of `rank`: the first *rows rows of its local buffer
+ * (S_pad/cp for every rank when S divides; fewer for the ranks owning the
+ * tail chunks otherwise, possibly 0).  EINVAL for a bad rank or null rows. */
+int cp_attn_rank_valid_rows(cp_attn_plan_t plan, int rank, int64_t* rows);
 
 /* Chunk indices owned by `rank`, local order; *count = 2 (zigzag) or 1
  * (contiguous, where the chunk index equals the rank). */
@@ -211,10 +223,11 @@ int cp_attn_valid_work(cp_attn_plan_t plan, int rank, int step, int bm, int bn, 
 /* ---- layout kernels (zigzag / contiguous reordering) ---- */
 
 /* src: [S][heads][head_dim] natural order -> dst: [cp][local_rows][heads][head_dim],
- * each rank's rows in its local order.  Plan dtype, bit-exact copy. */
+ * each rank's rows in its local order.  Plan dtype, bit-exact copy; pad rows
+ * (positions >= S of a padded plan) are written as zeros. */
 int cp_attn_layout_gather(cp_attn_plan_t plan, const void* src, void* dst, void* stream);
 
-/* Inverse of cp_attn_layout_gather. */
+/* Inverse of cp_attn_layout_gather; pad rows of src are not read. */
 int cp_attn_layout_scatter(cp_attn_plan_t plan, const void* src, void* dst, void* stream);
 
 /*

@@ -137,6 +137,11 @@ class Plan:
         N.check(self.lib.cp_attn_local_rows(self._h, ctypes.byref(n)), "cp_attn_local_rows")
         return n.value
 
+    def rank_valid_rows(self, rank):
+        n = ctypes.c_int64()
+        N.check(self.lib.cp_attn_rank_valid_rows(self._h, int(rank), ctypes.byref(n)), "cp_attn_rank_valid_rows")
+        return n.value
+
     def rank_chunks(self, rank):
         ch = (ctypes.c_int32 * 2)()
         cnt = ctypes.c_int32()
@@ -165,20 +170,23 @@ class Plan:
 
     # -- layout -----------------------------------------------------------
     def layout_gather(self, src, dst, stream=None):
-        self._check_layout(src, dst)
+        """natural order ``[S, H, D]`` -> local order ``[cp * local_rows, H, D]`` (pad rows zero)."""
+        self._check_layout(natural=src, local=dst)
         N.check(self.lib.cp_attn_layout_gather(self._h, _ptr(src), _ptr(dst), _stream_ptr(stream)),
                 "cp_attn_layout_gather")
 
     def layout_scatter(self, src, dst, stream=None):
-        self._check_layout(src, dst)
+        """local order ``[cp * local_rows, H, D]`` -> natural order ``[S, H, D]``."""
+        self._check_layout(natural=dst, local=src)
         N.check(self.lib.cp_attn_layout_scatter(self._h, _ptr(src), _ptr(dst), _stream_ptr(stream)),
                 "cp_attn_layout_scatter")
 
-    def _check_layout(self, src, dst):
-        n = self.seq_len * self.heads * self.head_dim
-        for name, t in (("src", src), ("dst", dst)):
+    def _check_layout(self, natural, local):
+        row = self.heads * self.head_dim
+        for name, t, rows in (("natural", natural, self.seq_len), ("local", local, self.cp_size * self.local_rows())):
+            n = rows * row
             if t.numel() != n or t.dtype != self.dtype or not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous {self.dtype} CUDA tensor with {n} elements")
+                raise ValueError(f"{name}-order tensor must be a contiguous {self.dtype} CUDA tensor with {n} elements")
 
     def last_step_times(self):
         n = self.cp_size * self.cp_size

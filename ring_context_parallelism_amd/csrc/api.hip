@@ -177,7 +177,9 @@ int ensure_device(Plan& p) {
 
 // The K and V rows of ring source `src` (its local order) are one (contiguous)
 // or two (zigzag) token ranges of the natural-order tensors; receiving them
-// into slot b is two or four linear copies.
+// into slot b is two or four linear copies.  Only real rows are received: a
+// chunk's pad rows (and a chunk of pad only) are not copied, and the kernels
+// never read past the source's real keys.
 RecvArgs recv_ranges(Plan& p, const void* k, const void* v, int src, int b) {
   DeviceState& d = *p.dev;
   const WsLayout w = ws_layout(p);
@@ -190,12 +192,14 @@ RecvArgs recv_ranges(Plan& p, const void* k, const void* v, int src, int b) {
   RecvArgs ra{};
   for (int c = 0; c < nch; ++c) {
     const int64_t g = p.chunk_of(src, c) * ch_bytes;
+    const int64_t bytes = p.valid_in_chunk(p.chunk_of(src, c)) * row_bytes;
+    if (bytes == 0) continue;
     ra.src[ra.n] = static_cast<const char*>(k) + g;
     ra.dst[ra.n] = dk + c * ch_bytes;
-    ra.vec[ra.n++] = ch_bytes / 16;
+    ra.vec[ra.n++] = bytes / 16;
     ra.src[ra.n] = static_cast<const char*>(v) + g;
     ra.dst[ra.n] = dv + c * ch_bytes;
-    ra.vec[ra.n++] = ch_bytes / 16;
+    ra.vec[ra.n++] = bytes / 16;
   }
   return ra;
 }
@@ -262,6 +266,7 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
   a.lse = lse;
   a.seq_len = p.seq_len;
   a.n_loc = int32_t(p.n_loc);
+  a.kv_valid = int32_t(p.valid_rows(sd.src));
   a.heads = p.heads;
   a.scale = 1.0f / std::sqrt(float(p.head_dim));
   a.scale_log2 = a.scale * 1.4426950408889634f;
@@ -348,12 +353,15 @@ int launch_rank_finalize(Plan& p, void* out, float* lse, int r, hipStream_t st) 
   f.head_dim = p.head_dim;
   f.out_f32 = p.dtype == CP_ATTN_FP32;
   const int nch = p.layout == 1 ? 2 : 1;
-  f.nseg = nch;
-  for (int c = 0; c < nch; ++c) {
-    f.seg_start[c] = int32_t(c * p.chunk);
-    f.seg_len[c] = int32_t(p.chunk);
-    f.seg_global[c] = p.global_row(r, c * p.chunk);
+  for (int c = 0; c < nch; ++c) {  // real rows only
+    const int64_t len = p.valid_in_chunk(p.chunk_of(r, c));
+    if (len == 0) continue;
+    f.seg_start[f.nseg] = int32_t(c * p.chunk);
+    f.seg_len[f.nseg] = int32_t(len);
+    f.seg_global[f.nseg] = p.global_row(r, c * p.chunk);
+    ++f.nseg;
   }
+  if (f.nseg == 0) return CP_ATTN_OK;
   CPA_HIP(launch_finalize(f, st));
   return CP_ATTN_OK;
 }
@@ -380,6 +388,7 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
     CPA_HIP(launch_fill_words(d.tile_cnt + size_t(r) * P, int64_t(P) * 2, 0u, st));
     for (int s = 0; s < P; ++s) d.counted[size_t(r) * P + s] = 1;
   }
+  if (p.valid_rows(r) == 0) return CP_ATTN_OK;  // a rank of pad tokens only: nothing to compute or write
   // cross-stream events only where another stream waits on them: each
   // record/wait pair costs microseconds of queue latency per step
   bool any_side = false;
@@ -671,7 +680,8 @@ int cp_attn_rank_forward(cp_attn_plan_t h, const void* q, const void* k, const v
   CPA_TRY(check_io(q, k, v, out, lse));
   CPA_TRY(ensure_device(p));
   reset_timing(p);
-  if (p.opt_graph) return run_graph(p, q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
+  // (a rank of pad tokens only has nothing to record)
+  if (p.opt_graph && p.valid_rows(rank) > 0) return run_graph(p, q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
   return run_rank(p, q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
   CPA_GUARD_END
 }
@@ -705,25 +715,28 @@ int cp_attn_allgather_forward(cp_attn_plan_t h, const void* q, const void* k, co
   a.lse = lse;
   a.seq_len = p.seq_len;
   a.n_loc = int32_t(p.seq_len);  // keys addressable through the identity map
+  a.kv_valid = int32_t(p.seq_len);
   a.heads = p.heads;
   a.scale = 1.0f / std::sqrt(float(p.head_dim));
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.out_f32 = p.dtype == CP_ATTN_FP32;
   const int nch = p.layout == 1 ? 2 : 1;
-  a.nseg = nch;
-  for (int c = 0; c < nch; ++c) {
+  for (int c = 0; c < nch; ++c) {  // real rows of each owned chunk
+    const int64_t len = p.valid_in_chunk(p.chunk_of(rank, c));
+    if (len == 0) continue;
     const int64_t g0 = p.global_row(rank, c * p.chunk);
-    SegArgs& x = a.seg[c];
+    SegArgs& x = a.seg[a.nseg++];
     x.q_global = g0;
     x.q_start = int32_t(c * p.chunk);
-    x.q_len = int32_t(p.chunk);
+    x.q_len = int32_t(len);
     x.kv_full = int32_t(p.causal ? g0 : p.seq_len);
     x.diag = p.causal ? 1 : 0;
     x.ksplit = 1;
-    x.tiles = int32_t((p.chunk + bm - 1) / bm);
+    x.tiles = int32_t((len + bm - 1) / bm);
     x.epi = kEpiInit | kEpiFinal;
     a.total_tiles += x.tiles;
   }
+  if (a.nseg == 0) return CP_ATTN_OK;  // a rank of pad only
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
@@ -749,6 +762,15 @@ int cp_attn_local_rows(cp_attn_plan_t h, int64_t* rows) {
   CPA_TRY(check_plan(h));
   if (!rows) return fail(CP_ATTN_EINVAL, "rows is null");
   *rows = h->p->n_loc;
+  return CP_ATTN_OK;
+}
+
+int cp_attn_rank_valid_rows(cp_attn_plan_t h, int rank, int64_t* rows) {
+  CPA_TRY(check_plan(h));
+  const Plan& p = *h->p;
+  if (rank < 0 || rank >= p.cp) return fail(CP_ATTN_EINVAL, "rank outside [0, cp_size)");
+  if (!rows) return fail(CP_ATTN_EINVAL, "rows is null");
+  *rows = p.valid_rows(rank);
   return CP_ATTN_OK;
 }
 
@@ -820,6 +842,7 @@ static int layout_all(cp_attn_plan_t h, const void* src, void* dst, void* stream
   la.chunk = p.chunk;
   la.n_loc = p.n_loc;
   la.row_vec = int64_t(p.heads) * p.head_dim * p.elem_bytes() / 16;
+  la.seq_len = p.seq_len;
   la.dst_rank0 = 0;
   CPA_HIP(launch_layout(la, 0, static_cast<hipStream_t>(stream)));
   return CP_ATTN_OK;

@@ -171,8 +171,8 @@ void attn_step_bf16(StepArgs a) {
   // their 8-byte transposed writes land on sixteen different bank pairs.
   const int vkg = tid & 15, vdg = tid >> 4;
 
-  // keys past the slot are clamped to its last row (and masked)
-  auto src_off = [&](int kk) { return uint32_t(kv_row(a, min(kk, a.n_loc - 1))) * row_bytes + head_off; };
+  // keys past the source's real keys are clamped to its last real row (and masked)
+  auto src_off = [&](int kk) { return uint32_t(kv_row(a, min(kk, a.kv_valid - 1))) * row_bytes + head_off; };
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
@@ -486,8 +486,9 @@ void attn_step_bf16_d128x8(StepArgs a) {
     // Fast path: the 64 source rows are consecutive and inside the buffer, so
     // the tile base is one scalar offset.  Otherwise (a tile that crosses the
     // split between the two chunks, or the ragged last tile) each lane maps
-    // its own row and clamps keys past the buffer to its last row (masked).
-    const bool whole = j0 + kBN <= a.n_loc && (j0 + kBN <= a.kv_split || j0 >= a.kv_split);
+    // its own row and clamps keys past the source's real keys to its last
+    // real row (masked).
+    const bool whole = j0 + kBN <= a.kv_valid && (j0 + kBN <= a.kv_split || j0 >= a.kv_split);
     if (whole) {
       const uint32_t soff = __builtin_amdgcn_readfirstlane(uint32_t(kv_row(a, j0)) * row_bytes);
 #pragma unroll
@@ -495,7 +496,7 @@ void attn_step_bf16_d128x8(StepArgs a) {
     } else {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int kk = min(j0 + lrow0 + 4 * n, a.n_loc - 1);
+        const int kk = min(j0 + lrow0 + 4 * n, a.kv_valid - 1);
         const uint32_t voff = uint32_t(kv_row(a, kk)) * row_bytes + (hbase ^ (uint32_t(swz(4 * n)) << 4));
         dma_lds16(desc, voff, 0u, lds_addr(dst + (16 * (wv & 3) + 4 * n) * 256));
       }

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
       const int kr = e / D, dc = e % D;
       const int key = j0 + kr;
       float kx = 0.f, vx = 0.f;
-      if (key < a.n_loc) {
+      if (key < a.kv_valid) {  // keys past the real ones stay zero (and masked)
         const int64_t off = (int64_t(kv_row(a, key)) * a.heads + h) * D + dc;
         kx = kp[off];
         vx = vp[off];

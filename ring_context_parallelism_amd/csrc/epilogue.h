@@ -17,7 +17,7 @@
 
 namespace cpattn {
 
-// Source row of local key kk (0 <= kk < n_loc) in the step's K/V tensors.
+// Source row of local key kk (0 <= kk < kv_valid) in the step's K/V tensors.
 __device__ __forceinline__ int kv_row(const StepArgs& a, int kk) {
   return kk < a.kv_split ? a.kv_lo + kk : a.kv_hi + (kk - a.kv_split);
 }

@@ -56,6 +56,7 @@ struct StepArgs {
   float* lse;        // [H][S]
   int64_t seq_len;
   int32_t n_loc;
+  int32_t kv_valid;  // real keys of the source: local keys [0, kv_valid); loads never go past them
   int32_t heads;
   float scale_log2;  // softmax scale * log2(e)
   float scale;       // softmax scale 1/sqrt(D)
@@ -102,6 +103,7 @@ struct LayoutArgs {
   int64_t chunk;       // rows per chunk
   int64_t n_loc;       // rows per rank
   int64_t row_vec;     // 16-byte vectors per row
+  int64_t seq_len;     // real tokens: pad rows (token >= seq_len) are zero-filled by gather, skipped by scatter
   int64_t dst_rank0;   // rank whose local buffer starts at dst (gather) / src (scatter) row 0
 };
 // max_blocks > 0 bounds the grid (per tensor); 0 sizes it to the data.

@@ -42,6 +42,11 @@ __global__ __launch_bounds__(kThreads) void layout_copy(LayoutArgs a) {
     const int64_t li = row % a.n_loc;
     const int64_t g = local_to_global(r, li, a.chunk, a.n_loc, a.cp, a.zigzag);
     const int64_t lrow = (r - a.dst_rank0) * a.n_loc + li;
+    if (g >= a.seq_len) {  // pad row: zero in the local layout, absent from the natural one
+      if (a.to_local)
+        for (int64_t c = threadIdx.x; c < a.row_vec; c += kThreads) dst[lrow * a.row_vec + c] = uint4{0u, 0u, 0u, 0u};
+      continue;
+    }
     const int64_t from = (a.to_local ? g : lrow) * a.row_vec;
     const int64_t to = (a.to_local ? lrow : g) * a.row_vec;
     for (int64_t c = threadIdx.x; c < a.row_vec; c += kThreads) dst[to + c] = src[from + c];

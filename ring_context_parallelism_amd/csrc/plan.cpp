@@ -19,6 +19,18 @@
 //   j >  r : query chunk r sees nothing; chunk 2cp-1-r sees both key chunks.
 // In every case a local row's valid keys form a prefix of the source's local
 // buffer, which is what a Segment records.
+//
+// Awkward lengths ("Context Parallelism for Long-Context Training", section
+// "Test sequence divisibility and padding": pad ownership, masked pad keys and
+// queries, local offsets).  A length that does not divide into the chunks is
+// padded at the end to the next multiple; pad token c*chunk + i belongs to the
+// owner of chunk c like any other.  Chunk c holds vl(c) = clamp(S - c*chunk, 0,
+// chunk) real tokens, first.  A chunk with a real token has only real chunks
+// before it, so a rank's real rows are a prefix of its local buffer (its early
+// chunk is full whenever its late chunk holds anything), and so are a
+// source's real keys.  Segments keep only real rows; causal rows only ever
+// see keys before them, which are real; bidirectional rows see the source's
+// real prefix.  Pad rows appear in no segment and pad keys in no prefix.
 #include "plan.h"
 
 #include <algorithm>
@@ -40,16 +52,28 @@ int64_t Plan::global_row(int r, int64_t i) const {
   return chunk_of(r, which) * chunk + (i - which * chunk);
 }
 
+int64_t Plan::valid_in_chunk(int64_t c) const { return std::min(chunk, std::max<int64_t>(0, seq_len - c * chunk)); }
+
+int64_t Plan::valid_rows(int r) const {
+  if (layout == 0) return valid_in_chunk(r);
+  return valid_in_chunk(chunk_of(r, 0)) + valid_in_chunk(chunk_of(r, 1));
+}
+
 static void build_steps(Plan& p) {
   const int P = p.cp;
   const int64_t C = p.chunk;
   p.steps.assign(size_t(P) * P, StepDesc{});
   for (int r = 0; r < P; ++r) {
+    // real rows of the rank's early / late chunk
+    const int64_t q0 = p.valid_in_chunk(p.chunk_of(r, 0));
+    const int64_t q1 = p.layout == 1 ? p.valid_in_chunk(p.chunk_of(r, 1)) : 0;
     for (int s = 0; s < P; ++s) {
       StepDesc& d = p.steps[size_t(r) * P + s];
       const int j = ((r - s) % P + P) % P;
       d.src = j;
+      // a segment with no real row, or whose rows see no key, is dropped
       auto add = [&](int64_t q_start, int64_t q_len, int64_t kv_full, int diag) {
+        if (q_len <= 0 || (kv_full <= 0 && !diag)) return;
         Segment& g = d.seg[d.nseg++];
         g.q_start = q_start;
         g.q_len = q_len;
@@ -59,24 +83,25 @@ static void build_steps(Plan& p) {
       };
       if (p.layout == 1) {  // zigzag: local rows [0,C) chunk r, [C,2C) chunk 2P-1-r
         if (!p.causal) {
-          add(0, C, 2 * C, 0);
-          add(C, C, 2 * C, 0);
+          const int64_t kv = p.valid_rows(j);  // the source's real keys
+          add(0, q0, kv, 0);
+          add(C, q1, kv, 0);
         } else if (j == r) {
-          add(C, C, C, 1);  // late chunk first: the longer rows (longest-first order)
-          add(0, C, 0, 1);
+          add(C, q1, C, 1);  // late chunk first: the longer rows (longest-first order)
+          add(0, q0, 0, 1);
         } else if (j < r) {
-          add(0, C, C, 0);
-          add(C, C, C, 0);
+          add(0, q0, C, 0);
+          add(C, q1, C, 0);
         } else {
-          add(C, C, 2 * C, 0);
+          add(C, q1, 2 * C, 0);
         }
       } else {  // contiguous: local rows [0,L) chunk r
         if (!p.causal) {
-          add(0, C, C, 0);
+          add(0, q0, p.valid_rows(j), 0);
         } else if (j == r) {
-          add(0, C, 0, 1);
+          add(0, q0, 0, 1);
         } else if (j < r) {
-          add(0, C, C, 0);
+          add(0, q0, C, 0);
         }
       }
     }
@@ -128,18 +153,14 @@ int make_plan(int64_t seq_len, int cp, int heads, int head_dim, int causal, int 
     return kUnsupported;
   }
   const int64_t parts = layout == 1 ? 2 * int64_t(cp) : int64_t(cp);
-  if (seq_len % parts != 0) {
-    *err = layout == 1 ? "zigzag needs seq_len divisible by 2*cp_size"
-                       : "contiguous needs seq_len divisible by cp_size";
-    return kInval;
-  }
+  const int64_t padded = (seq_len + parts - 1) / parts * parts;
   if (head_dim != 64 && head_dim != 128) {
     *err = "head_dim must be 64 or 128";
     return kUnsupported;
   }
   // K/V tensors are addressed with 32-bit byte offsets on the device
-  if (seq_len * int64_t(heads) * head_dim * 4 >= (int64_t(1) << 32)) {
-    *err = "seq_len * heads * head_dim * 4 must stay below 2^32 bytes";
+  if (padded * int64_t(heads) * head_dim * 4 >= (int64_t(1) << 32)) {
+    *err = "padded seq_len * heads * head_dim * 4 must stay below 2^32 bytes";
     return kUnsupported;
   }
   Plan* p = new Plan;
@@ -149,8 +170,9 @@ int make_plan(int64_t seq_len, int cp, int heads, int head_dim, int causal, int 
   p->head_dim = head_dim;
   p->causal = causal;
   p->layout = layout;
-  p->chunk = seq_len / parts;
-  p->n_loc = seq_len / cp;
+  p->padded_len = padded;
+  p->chunk = padded / parts;
+  p->n_loc = padded / cp;
   build_steps(*p);
   *out = p;
   return kOk;

@@ -36,8 +36,9 @@ struct Plan {
   int32_t causal = 1;
   int32_t layout = 1;
   int32_t dtype = 0;
-  int64_t chunk = 0;   // S/(2cp) zigzag, S/cp contiguous
-  int64_t n_loc = 0;   // rows per rank
+  int64_t padded_len = 0;  // seq_len rounded up to a multiple of the chunk count
+  int64_t chunk = 0;   // padded_len/(2cp) zigzag, padded_len/cp contiguous
+  int64_t n_loc = 0;   // rows of a rank's local buffer (pad rows included)
   std::vector<StepDesc> steps;  // [rank * cp + step]
 
   // options
@@ -58,6 +59,10 @@ struct Plan {
   // global token position of local row i of rank r
   int64_t global_row(int r, int64_t i) const;
   int64_t chunk_of(int r, int which) const;  // which in {0, 1}
+  // real (non-pad) tokens of chunk c: the first valid_in_chunk(c) rows
+  int64_t valid_in_chunk(int64_t c) const;
+  // real rows of rank r's local buffer; they are its first valid_rows(r) rows
+  int64_t valid_rows(int r) const;
 };
 
 // Returns a status code; on success *out is a new plan.
