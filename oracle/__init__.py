@@ -19,8 +19,8 @@ Sources (pages, cited by title and section):
   (instagit.com) -- per-GPU length ``seq_length // context_parallel_size``
   (section "Sequence Partitioning Across GPUs").
 * "Context Parallelism for Long-Context Training" (jpcasabianca.com) --
-  equivalence against the unsharded reference (section "Prove attention
-  equivalence"), shard coverage and padding of awkward lengths (section "Test
+  equivalence against the unsharded reference for outputs and gradients
+  (section "Prove attention equivalence"; the gradients in ``backward``), shard coverage and padding of awkward lengths (section "Test
   sequence divisibility and padding": pad ownership, masked pad keys and
   queries, real outputs unchanged by the padding).
 
@@ -30,6 +30,7 @@ routine; none is "parity unpinned".
 """
 
 from .attention import attention, attention_probabilities, valid_mask
+from .backward import attention_backward, rank_backward, full_backward
 from .cp_reference import (
     chunk_size,
     padded_length,
@@ -49,6 +50,9 @@ __all__ = [
     "attention",
     "attention_probabilities",
     "valid_mask",
+    "attention_backward",
+    "rank_backward",
+    "full_backward",
     "chunk_size",
     "padded_length",
     "rank_chunks",
