@@ -185,6 +185,32 @@ int cp_attn_allgather_forward(cp_attn_plan_t plan, const void* q, const void* k,
 int cp_attn_full_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
                          float* lse, void* stream);
 
+/*
+ * Backward of one rank's share, asynchronous on `stream` ("Context
+ * Parallelism for Long-Context Training", section "Prove attention
+ * equivalence": gradients must match the unsharded reference).  With the
+ * complete forward's out and lse, every step knows the exact softmax of its
+ * valid pairs, P_ij = exp(s_ij - lse_i), and adds, over the same ring steps
+ * and valid pairs as the forward:
+ *   dV_j += P_ij dO_i;  dS_ij = P_ij (<dO_i, v_j> - <dO_i, O_i>);
+ *   dQ_i += dS_ij k_j / sqrt(head_dim);  dK_j += dS_ij q_i / sqrt(head_dim).
+ * q, k, v, out, dout: [S][heads][head_dim] plan dtype (out and lse as written
+ * by a forward call of the same plan); dq, dk, dv: [S][heads][head_dim] fp32.
+ * Writes dq at the rank's real rows; ADDS the rank's terms to dk and dv at
+ * the rows of every source it sees (on a ring these partial sums travel
+ * with the K/V chunks back to their owner), so zero dk and dv before the
+ * first rank.  Uses the plan's workspace; ignores the schedule options.
+ * Errors as cp_attn_rank_forward.
+ */
+int cp_attn_rank_backward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, float* dq, float* dk, float* dv, int rank,
+                          void* stream);
+
+/* Every rank's backward on `stream`: zeroes dk and dv, then runs ranks
+ * 0..cp_size-1; dq, dk, dv end as the complete gradients. */
+int cp_attn_full_backward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, float* dq, float* dk, float* dv, void* stream);
+
 /* ---- host-only introspection (no HIP calls; CPU-testable) ---- */
 
 /* Rows of each rank's local buffer, pad rows included: S_pad/cp. */

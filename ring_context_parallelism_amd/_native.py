@@ -50,6 +50,9 @@ SIGNATURES = {
     "cp_attn_set_streams": (ctypes.c_int, [_c_p, _c_p, _c_p]),
     "cp_attn_rank_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_p]),
     "cp_attn_full_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
+    "cp_attn_rank_backward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int,
+                                             _c_p]),
+    "cp_attn_full_backward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "cp_attn_local_rows": (ctypes.c_int, [_c_p, ctypes.POINTER(_i64)]),
     "cp_attn_rank_chunks": (ctypes.c_int, [_c_p, ctypes.c_int, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "cp_attn_rank_valid_rows": (ctypes.c_int, [_c_p, ctypes.c_int, ctypes.POINTER(_i64)]),

@@ -131,6 +131,30 @@ class Plan:
         N.check(self.lib.cp_attn_full_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                               _stream_ptr(stream)), "cp_attn_full_forward")
 
+    # -- backward -------------------------------------------------------
+    def _check_bwd(self, dout, dq, dk, dv):
+        shape = (self.seq_len, self.heads, self.head_dim)
+        if tuple(dout.shape) != shape or dout.dtype != self.dtype or not dout.is_cuda or not dout.is_contiguous():
+            raise ValueError(f"dout must be a contiguous {self.dtype} CUDA tensor of shape {shape}")
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape {shape}")
+
+    def rank_backward(self, q, k, v, out, lse, dout, dq, dk, dv, rank, stream=None):
+        """dq at the rank's rows; the rank's terms ADDED to dk, dv."""
+        self._check_io(q, k, v, out, lse)
+        self._check_bwd(dout, dq, dk, dv)
+        N.check(self.lib.cp_attn_rank_backward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                               _ptr(dq), _ptr(dk), _ptr(dv), int(rank), _stream_ptr(stream)),
+                "cp_attn_rank_backward")
+
+    def full_backward(self, q, k, v, out, lse, dout, dq, dk, dv, stream=None):
+        self._check_io(q, k, v, out, lse)
+        self._check_bwd(dout, dq, dk, dv)
+        N.check(self.lib.cp_attn_full_backward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                               _ptr(dq), _ptr(dk), _ptr(dv), _stream_ptr(stream)),
+                "cp_attn_full_backward")
+
     # -- host-only introspection -----------------------------------------
     def local_rows(self):
         n = ctypes.c_int64()

@@ -517,6 +517,93 @@ int run_graph(Plan& p, const void* q, const void* k, const void* v, void* out, f
   return CP_ATTN_OK;
 }
 
+// ---- backward ----
+
+// Rows and keys per workgroup of the backward kernels the plan uses.
+void bwd_tile_sizes(const Plan& p, int* rows, int* keys) {
+  *rows = bwd_generic_tile();
+  *keys = bwd_generic_tile();
+}
+
+// Rank r's share of the backward on one stream: D_i of its rows, then per
+// ring step the key-major (dK, dV) and row-major (dQ) kernels of the step's
+// segments.  K and V are read in place at the source's natural rows, and the
+// source's dK, dV are accumulated there: on a real ring those partial sums
+// travel with the K/V chunks and arrive home complete after cp steps.
+int run_rank_backward(Plan& p, const void* q, const void* k, const void* v, const void* out, const float* lse,
+                      const void* dout, float* dq, float* dk, float* dv, int r, hipStream_t st) {
+  if (p.valid_rows(r) == 0) return CP_ATTN_OK;  // a rank of pad tokens only
+  DeviceState& d = *p.dev;
+  const WsLayout w = ws_layout(p);
+  char* ws = static_cast<char*>(d.ws);
+  const bool bf16 = p.dtype == CP_ATTN_BF16;
+  int bt_rows = 0, bt_keys = 0;
+  bwd_tile_sizes(p, &bt_rows, &bt_keys);
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = reinterpret_cast<float*>(ws + w.acc_lse);  // the forward's running-LSE region, [H][n_loc]
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.seq_len = p.seq_len;
+  a.n_loc = int32_t(p.n_loc);
+  a.heads = p.heads;
+  a.scale = 1.0f / std::sqrt(float(p.head_dim));
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  const int64_t split = p.layout == 1 ? p.chunk : p.n_loc;
+  a.delta_rows = p.valid_rows(r);
+  a.delta_lo = p.chunk_of(r, 0) * p.chunk;
+  a.delta_hi = p.layout == 1 ? p.chunk_of(r, 1) * p.chunk : 0;
+  a.delta_split = split;
+  CPA_HIP(launch_bwd_delta(a, bf16, p.head_dim, st));
+  for (int s = 0; s < p.cp; ++s) {
+    const StepDesc& sd = p.step(r, s);
+    if (sd.nseg == 0) continue;
+    const int j = sd.src;
+    a.kv_lo = int32_t(p.chunk_of(j, 0) * p.chunk);
+    a.kv_hi = p.layout == 1 ? int32_t(p.chunk_of(j, 1) * p.chunk) : 0;
+    a.kv_split = int32_t(split);
+    a.kv_valid = int32_t(p.valid_rows(j));
+    a.nseg = sd.nseg;
+    a.total_tiles = 0;
+    a.seg[1] = SegArgs{};
+    int64_t maxpre = 0;  // longest key prefix of the step's rows
+    for (int i = 0; i < sd.nseg; ++i) {
+      const Segment& g = sd.seg[i];
+      SegArgs& x = a.seg[i];
+      x.q_global = g.q_global;
+      x.q_start = int32_t(g.q_start);
+      x.q_len = int32_t(g.q_len);
+      x.kv_full = int32_t(g.kv_full);
+      x.diag = g.diag;
+      x.epi = g.first;
+      x.ksplit = 1;
+      x.tiles = int32_t((g.q_len + bt_rows - 1) / bt_rows);
+      a.total_tiles += x.tiles;
+      maxpre = std::max<int64_t>(maxpre, g.kv_full + (g.diag ? g.q_len : 0));
+    }
+    a.key_tiles = int32_t((maxpre + bt_keys - 1) / bt_keys);
+    const hipError_t e = launch_bwd_generic(a, bf16, p.head_dim, st);
+    if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("backward launch: ") + hipGetErrorString(e));
+  }
+  return CP_ATTN_OK;
+}
+
+int check_bwd_io(const void* dout, const void* dq, const void* dk, const void* dv) {
+  const void* ptrs[4] = {dout, dq, dk, dv};
+  const char* names[4] = {"dout", "dq", "dk", "dv"};
+  for (int i = 0; i < 4; ++i) {
+    if (!ptrs[i]) return fail(CP_ATTN_EINVAL, std::string(names[i]) + " is null");
+    if (!aligned16(ptrs[i])) return fail(CP_ATTN_EINVAL, std::string(names[i]) + " is not 16-byte aligned");
+  }
+  return CP_ATTN_OK;
+}
+
 }  // namespace
 }  // namespace cpattn
 
@@ -754,6 +841,37 @@ int cp_attn_full_forward(cp_attn_plan_t h, const void* q, const void* k, const v
   reset_timing(p);
   if (p.opt_graph) return run_graph(p, q, k, v, out, lse, -1, static_cast<hipStream_t>(stream));
   for (int r = 0; r < p.cp; ++r) CPA_TRY(run_rank(p, q, k, v, out, lse, r, static_cast<hipStream_t>(stream)));
+  return CP_ATTN_OK;
+  CPA_GUARD_END
+}
+
+int cp_attn_rank_backward(cp_attn_plan_t h, const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, float* dq, float* dk, float* dv, int rank,
+                          void* stream) {
+  CPA_GUARD_BEGIN
+  CPA_TRY(check_plan(h));
+  Plan& p = *h->p;
+  if (rank < 0 || rank >= p.cp) return fail(CP_ATTN_EINVAL, "rank outside [0, cp_size)");
+  CPA_TRY(check_io(q, k, v, out, lse));
+  CPA_TRY(check_bwd_io(dout, dq, dk, dv));
+  CPA_TRY(ensure_device(p));
+  return run_rank_backward(p, q, k, v, out, lse, dout, dq, dk, dv, rank, static_cast<hipStream_t>(stream));
+  CPA_GUARD_END
+}
+
+int cp_attn_full_backward(cp_attn_plan_t h, const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, float* dq, float* dk, float* dv, void* stream) {
+  CPA_GUARD_BEGIN
+  CPA_TRY(check_plan(h));
+  Plan& p = *h->p;
+  CPA_TRY(check_io(q, k, v, out, lse));
+  CPA_TRY(check_bwd_io(dout, dq, dk, dv));
+  CPA_TRY(ensure_device(p));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t words = p.seq_len * p.heads * p.head_dim;
+  CPA_HIP(launch_fill_words(dk, words, 0u, st));
+  CPA_HIP(launch_fill_words(dv, words, 0u, st));
+  for (int r = 0; r < p.cp; ++r) CPA_TRY(run_rank_backward(p, q, k, v, out, lse, dout, dq, dk, dv, r, st));
   return CP_ATTN_OK;
   CPA_GUARD_END
 }

@@ -78,6 +78,44 @@ struct StepArgs {
   unsigned long long* tile_cnt;
 };
 
+// Backward of one ring step (attn_bwd.hip, attn_bwd_bf16.hip).  Q, dO, O are
+// read at the natural rows of the segments, K and V of the source in place
+// through the two-run map (local key kk -> row kv_lo + kk below kv_split, else
+// kv_hi + kk - kv_split); gradients are fp32 [S][H][D] at natural rows.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;   // forward output (delta kernel)
+  const void* dout;
+  const float* lse;  // [H][S] forward LSE, natural log
+  float* delta;      // [H][n_loc] D_i = <dO_i, O_i> of local row i
+  float* dq;         // written at a row run's first step (SegArgs::epi != 0), added to later
+  float* dk;         // added to
+  float* dv;         // added to
+  int64_t seq_len;
+  int32_t n_loc;
+  int32_t heads;
+  int32_t kv_valid;
+  int32_t kv_lo;
+  int32_t kv_hi;
+  int32_t kv_split;
+  float scale;
+  float scale_log2;
+  int32_t nseg;
+  int32_t total_tiles;  // row-major workgroups per head (sum of seg[i].tiles)
+  int32_t key_tiles;    // key-major workgroups per head
+  SegArgs seg[2];       // epi: 1 = first active step of the row run
+  // delta kernel: the rank's real local rows, local row -> natural row map
+  int64_t delta_rows;
+  int64_t delta_lo;
+  int64_t delta_hi;
+  int64_t delta_split;
+};
+int bwd_generic_tile();  // rows and keys per workgroup of the generic kernels
+hipError_t launch_bwd_delta(const BwdArgs& a, int dtype_bf16, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_generic(const BwdArgs& a, int dtype_bf16, int head_dim, hipStream_t stream);
+
 // attention step kernels: return hipError_t of the launch
 // (only the head_dim 128 bf16 kernel performs StepArgs::recv)
 bool attn_does_recv(int dtype_bf16, int head_dim);

@@ -1,0 +1,136 @@
+"""GPU parity of the backward (through the C ABI) against the fp64 oracle.
+
+The GPU forward of the same plan supplies out and lse (as a training step
+would); the oracle differentiates its own fp64 forward.  Tolerances, per
+gradient tensor, relative to that tensor's largest reference magnitude:
+bf16 inputs max|d| <= 2e-2 * max|ref|, fp32 inputs <= 1e-4 * max|ref|.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_context_parallelism_amd import Plan
+from ring_context_parallelism_amd.inputs import make_qkv, to_numpy_f64
+
+pytestmark = pytest.mark.gpu
+
+REL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+
+
+def _dev():
+    assert torch.cuda.is_available(), "no GPU"
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _inputs(seq, heads, dim, dtype, seed):
+    kind = "bf16" if dtype == torch.bfloat16 else "fp32"
+    q, k, v = make_qkv(seq, heads, dim, kind, seed)
+    dout = make_qkv(seq, heads, dim, kind, seed + 1)[0]
+    return q, k, v, dout
+
+
+def _forward(p, qd, kd, vd):
+    out = torch.empty_like(qd)
+    lse = torch.empty((p.heads, p.seq_len), device=qd.device)
+    p.full_forward(qd, kd, vd, out, lse)
+    return out, lse
+
+
+def _rel_err(got, ref, rows=None):
+    g = got.double().cpu().numpy()
+    if rows is not None:
+        g, ref = g[rows], ref[rows]
+    assert np.all(np.isfinite(g))
+    return float(np.max(np.abs(g - ref)) / max(1e-30, np.max(np.abs(ref))))
+
+
+CASES = [
+    (1536, 2, "zigzag", True, 2, 128, torch.bfloat16),
+    (1003, 4, "zigzag", True, 2, 128, torch.bfloat16),   # padded
+    (768, 3, "contiguous", True, 2, 128, torch.bfloat16),
+    (1024, 4, "zigzag", False, 2, 128, torch.bfloat16),
+    (520, 2, "zigzag", True, 2, 64, torch.bfloat16),
+    (256, 2, "zigzag", True, 2, 64, torch.float32),
+    (299, 3, "contiguous", False, 2, 128, torch.float32),
+    (21, 8, "zigzag", True, 1, 128, torch.bfloat16),     # ranks with no real row
+]
+
+
+def _ids(c):
+    return f"s{c[0]}_cp{c[1]}_{c[2]}_{'causal' if c[3] else 'bidir'}_h{c[4]}_d{c[5]}_{str(c[6])[6:]}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
+def test_full_backward_matches_oracle(case):
+    seq, cp, layout, causal, heads, dim, dtype = case
+    _say(f"backward {_ids(case)}")
+    q, k, v, dout = _inputs(seq, heads, dim, dtype, 91)
+    p = Plan(seq, cp, heads, dim, causal, layout, dtype=dtype)
+    dev = _dev()
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+    out, lse = _forward(p, qd, kd, vd)
+    dq, dk, dv = (torch.full((seq, heads, dim), float("nan"), device=dev) for _ in range(3))
+    p.full_backward(qd, kd, vd, out, lse, dod, dq, dk, dv)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(*(to_numpy_f64(t) for t in (q, k, v, dout)), causal=causal)
+    errs = [_rel_err(g, r) for g, r in zip((dq, dk, dv), ref)]
+    _say(f"  rel err dq={errs[0]:.2e} dk={errs[1]:.2e} dv={errs[2]:.2e}")
+    assert max(errs) <= REL[dtype], errs
+    p.close()
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+def test_rank_backward_rows_and_travelling_terms(layout):
+    """Each rank writes dq at its own rows only and adds exactly its terms to
+    dk and dv (the oracle's per-rank contributions)."""
+    seq, cp, heads, dim, dtype = 1024, 4, 2, 128, torch.bfloat16
+    _say(f"rank backward {layout}")
+    q, k, v, dout = _inputs(seq, heads, dim, dtype, 92)
+    p = Plan(seq, cp, heads, dim, True, layout, dtype=dtype)
+    dev = _dev()
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+    out, lse = _forward(p, qd, kd, vd)
+    qn, kn, vn, don = (to_numpy_f64(t) for t in (q, k, v, dout))
+    for r in (0, cp - 1):
+        dq = torch.full((seq, heads, dim), float("nan"), device=dev)
+        dk = torch.zeros((seq, heads, dim), device=dev)
+        dv = torch.zeros((seq, heads, dim), device=dev)
+        p.rank_backward(qd, kd, vd, out, lse, dod, dq, dk, dv, r)
+        torch.cuda.synchronize()
+        rdq, rdk, rdv, pos = oracle.rank_backward(qn, kn, vn, don, cp, r, layout=layout, causal=True)
+        others = np.setdiff1d(np.arange(seq), pos)
+        assert torch.isnan(dq.cpu()[others]).all()
+        full = np.zeros((seq, heads, dim))
+        full[pos] = rdq
+        assert _rel_err(dq, full, rows=pos) <= REL[dtype]
+        for g, rf in ((dk, rdk), (dv, rdv)):
+            assert _rel_err(g, rf) <= REL[dtype]
+            untouched = np.all(rf == 0, axis=(1, 2))  # sources this rank never sees
+            assert torch.all(g.cpu()[torch.from_numpy(untouched)] == 0)
+    p.close()
+
+
+def test_backward_is_deterministic():
+    """No atomics: two runs give the same bits."""
+    seq, cp, heads, dim = 1536, 3, 2, 128
+    _say("backward determinism")
+    q, k, v, dout = _inputs(seq, heads, dim, torch.bfloat16, 93)
+    p = Plan(seq, cp, heads, dim, True, "zigzag")
+    dev = _dev()
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+    out, lse = _forward(p, qd, kd, vd)
+    runs = []
+    for _ in range(2):
+        g = [torch.empty((seq, heads, dim), device=dev) for _ in range(3)]
+        p.full_backward(qd, kd, vd, out, lse, dod, *g)
+        torch.cuda.synchronize()
+        runs.append([t.cpu() for t in g])
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    p.close()
