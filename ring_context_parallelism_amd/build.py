@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
 
-SOURCES = ["plan.cpp", "api.hip", "attn_bf16.hip", "attn_f32.hip", "attn_bwd.hip", "layout_merge.hip"]
+SOURCES = ["plan.cpp", "api.hip", "attn_bf16.hip", "attn_f32.hip", "attn_bwd.hip", "attn_bwd_bf16.hip", "layout_merge.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -521,8 +521,13 @@ int run_graph(Plan& p, const void* q, const void* k, const void* v, void* out, f
 
 // Rows and keys per workgroup of the backward kernels the plan uses.
 void bwd_tile_sizes(const Plan& p, int* rows, int* keys) {
-  *rows = bwd_generic_tile();
-  *keys = bwd_generic_tile();
+  if (bwd_mfma(p.dtype == CP_ATTN_BF16, p.head_dim)) {
+    *rows = bwd_mfma_rows();
+    *keys = bwd_mfma_keys();
+  } else {
+    *rows = bwd_generic_tile();
+    *keys = bwd_generic_tile();
+  }
 }
 
 // Rank r's share of the backward on one stream: D_i of its rows, then per
@@ -588,7 +593,8 @@ int run_rank_backward(Plan& p, const void* q, const void* k, const void* v, cons
       maxpre = std::max<int64_t>(maxpre, g.kv_full + (g.diag ? g.q_len : 0));
     }
     a.key_tiles = int32_t((maxpre + bt_keys - 1) / bt_keys);
-    const hipError_t e = launch_bwd_generic(a, bf16, p.head_dim, st);
+    const hipError_t e = bwd_mfma(bf16, p.head_dim) ? launch_bwd_bf16_d128(a, st)
+                                                    : launch_bwd_generic(a, bf16, p.head_dim, st);
     if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("backward launch: ") + hipGetErrorString(e));
   }
   return CP_ATTN_OK;

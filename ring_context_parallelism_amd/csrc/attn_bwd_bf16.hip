@@ -1,0 +1,379 @@
+// Backward of one ring step on gfx950 matrix cores: bf16, head_dim 128.
+//
+// The same step and the same terms as the generic kernels in attn_bwd.hip
+// (gradients of the step's valid pairs with the complete forward's LSE and
+// D_i = <dO_i, O_i>; "Context Parallelism for Long-Context Training", section
+// "Prove attention equivalence"; valid pairs and skipped future sub-blocks as
+// in "Sequence Parallelism IV: Megatron Context Parallel and Load-Balanced
+// Rings", section 4), with every product on v_mfma_f32_32x32x16_bf16:
+//
+// Key-major kernel (dK, dV): a workgroup of 4 waves owns 128 keys of one head,
+// 32 per wave, whose K and V rows stay in registers as the B operand
+// (column = key).  Tiles of 64 of the rank's rows (Q and dO, row-major with
+// the XOR swizzle of the forward's K/V tiles) are staged in LDS:
+//   S = Q K^T and dP = dO V^T   (A = Q / dO rows from LDS; lane = one key)
+//   P = exp2(S scale log2e - LSE log2e), dS = P (dP - D)   (per element)
+//   dV^T += dO^T P and dK^T += Q^T dS   (A = dO^T / Q^T read transposed
+//   from the same tiles with ds_read_b64_tr_b16; B = P / dS straight from
+//   the registers of S, rounded to bf16, rows in register order)
+// Row-major kernel (dQ): a workgroup of 4 waves owns 128 rows, 32 per wave,
+// whose Q and dO stay in registers; K/V tiles of 64 keys in LDS:
+//   S^T = K Q^T, dP^T = V dO^T, dS^T as above, dQ^T += K^T dS^T.
+// Rows past a segment's end carry LSE = +inf, so their P is exactly zero;
+// keys past the source's real keys are clamped to its last real row and
+// masked.  Tiles are loaded to registers one tile ahead and stored to LDS
+// after the barrier that ends the previous tile.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace cpattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+constexpr int D = 128;
+constexpr int NT = D / 16;     // k-steps over the head dimension
+constexpr int NB = D / 32;     // 32-row blocks of a transposed gradient
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kRows = 128;     // rows per row-major workgroup (32 per wave)
+constexpr int kKeys = 128;     // keys per key-major workgroup (32 per wave)
+constexpr int kTileRows = 64;  // rows of an LDS tile (Q/dO rows or K/V keys)
+constexpr int kTileBytes = kTileRows * 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Permutation of the 16 16-byte chunks of a 256-byte tile row (linear over
+// GF(2) in the row's low four bits); logical chunk c of row r is stored at
+// chunk c ^ swz(r & 15), so that the operand reads below hit distinct banks.
+__device__ __forceinline__ int swz(int r) {
+  return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1) | ((r & 1) << 2) | (((r >> 1) & 1) << 3);
+}
+
+__device__ __forceinline__ int kv_row(const BwdArgs& a, int kk) {
+  return kk < a.kv_split ? a.kv_lo + kk : a.kv_hi + (kk - a.kv_split);
+}
+
+// Per-lane LDS offsets of the operand reads (see the forward's tiles):
+//   row reads: lane (row qc, half hf) takes logical chunk 2 i + hf of row qc
+//   transposed reads: lane (group g1, index i16) points at row 8 r + 4 hf +
+//   i16/4 of a 16-row group, bytes 32 g1 + 8 (i16 & 3) .. + 7 of a 64-byte block
+struct Bases {
+  uint32_t row;
+  uint32_t tr[2];
+};
+
+__device__ __forceinline__ Bases make_bases(int lane) {
+  const int qc = lane & 31, hf = lane >> 5;
+  Bases b;
+  b.row = qc * 256 + ((hf ^ swz(qc & 15)) << 4);
+  const int i16 = lane & 15, g1 = (lane >> 4) & 1;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int vr = 8 * r + 4 * hf + (i16 >> 2);
+    const int c0 = 2 * g1 + ((i16 & 3) >> 1);
+    b.tr[r] = vr * 256 + ((c0 ^ swz(vr & 15)) << 4) + 8 * (i16 & 1);
+  }
+  return b;
+}
+
+// C[row][col] over two 32-row blocks of a 64-row tile: A = tile rows (LDS),
+// B = the lane's resident column operand (8 k-steps over the head dimension).
+__device__ __forceinline__ void mm_rows(const lds_u8* tile, uint32_t base, const bf16x8 (&b)[NT], f32x16 (&c)[2]) {
+  c[0] = f32x16{};
+  c[1] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const bf16x8 a0 = *reinterpret_cast<const lds_bf16x8*>(tile + (base ^ (32u * i)));
+    const bf16x8 a1 = *reinterpret_cast<const lds_bf16x8*>(tile + 32 * 256 + (base ^ (32u * i)));
+    c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[i], c[0], 0, 0, 0);
+    c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[i], c[1], 0, 0, 0);
+  }
+}
+
+// acc^T[d][col] += sum over the tile's 64 rows of tile[row][d] * w[row][col]:
+// A = the tile read transposed, B = w from registers (rows in register order).
+__device__ __forceinline__ void mm_tr(const lds_u8* tile, const uint32_t (&tr)[2], const bf16x8 (&w)[2][2],
+                                      f32x16 (&acc)[NB]) {
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    const int kb = gq >> 1, u = gq & 1;
+    const int roff = (32 * kb + 16 * u) * 256;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + roff + (tr[0] ^ (64u * b))));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + roff + (tr[1] ^ (64u * b))));
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, w[kb][u], acc[b], 0, 0, 0);
+    }
+  }
+}
+
+// 64 rows x 256 bytes from global (row r at src_row(r) * row_bytes + hoff)
+// into registers, four 16-byte chunks per thread; then into a swizzled tile.
+struct TileRegs {
+  u32x4 x[4];
+};
+
+template <typename RowFn>
+__device__ __forceinline__ void tile_load(TileRegs& t, const void* base, uint32_t row_bytes, uint32_t hoff, int tid,
+                                          RowFn src_row) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = c >> 4, ch = c & 15;
+    const char* p = static_cast<const char*>(base) + uint64_t(src_row(r)) * row_bytes + hoff + ch * 16;
+    t.x[i] = *reinterpret_cast<const u32x4*>(p);
+  }
+}
+
+__device__ __forceinline__ void tile_store(const TileRegs& t, lds_u8* tile, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = c >> 4, ch = c & 15;
+    *reinterpret_cast<lds_u32x4*>(tile + r * 256 + ((ch ^ swz(r & 15)) << 4)) = t.x[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key-major: dK and dV of 128 keys.
+// ---------------------------------------------------------------------------
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_bf16_d128(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) float s_lse[kTileRows];
+  __shared__ __attribute__((aligned(16))) float s_del[kTileRows];
+  lds_u8* const tq = (lds_u8*)smem;
+  lds_u8* const tdo = tq + kTileBytes;
+
+  const int h = blockIdx.x % a.heads;
+  const int k0 = (blockIdx.x / a.heads) * kKeys;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qc = lane & 31, hf = lane >> 5;
+  const int key = k0 + 32 * wv + qc;
+  const bool kok = key < a.kv_valid;
+  const int krow = kv_row(a, min(key, a.kv_valid - 1));
+  const uint32_t row_bytes = uint32_t(a.heads) * 256;
+  const uint32_t hoff = uint32_t(h) * 256;
+
+  bf16x8 kf[NT], vf[NT];
+  {
+    const __bf16* kp = static_cast<const __bf16*>(a.k) + (int64_t(krow) * a.heads + h) * D + 8 * hf;
+    const __bf16* vp = static_cast<const __bf16*>(a.v) + (int64_t(krow) * a.heads + h) * D + 8 * hf;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      kf[i] = *reinterpret_cast<const bf16x8*>(kp + 16 * i);
+      vf[i] = *reinterpret_cast<const bf16x8*>(vp + 16 * i);
+    }
+  }
+  f32x16 dk[NB], dv[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    dk[b] = f32x16{};
+    dv[b] = f32x16{};
+  }
+  const Bases bs = make_bases(lane);
+  const int w_key0 = k0 + 32 * wv;  // the wave's smallest key
+
+  for (int si = 0; si < a.nseg; ++si) {
+    const SegArgs& g = a.seg[si];
+    int t0;
+    if (k0 < g.kv_full) t0 = 0;
+    else if (g.diag) t0 = k0 - g.kv_full;  // row t sees keys < kv_full + t + 1
+    else continue;
+    if (t0 >= g.q_len) continue;
+    auto qrow = [&](int r) { return g.q_global + min(r, g.q_len - 1); };
+    TileRegs rq, rdo;
+    tile_load(rq, a.q, row_bytes, hoff, tid, [&](int r) { return qrow(t0 + r); });
+    tile_load(rdo, a.dout, row_bytes, hoff, tid, [&](int r) { return qrow(t0 + r); });
+    for (int r0 = t0; r0 < g.q_len; r0 += kTileRows) {
+      __syncthreads();  // the previous tile's reads are done
+      tile_store(rq, tq, tid);
+      tile_store(rdo, tdo, tid);
+      if (tid < kTileRows) {
+        const int t = r0 + tid;
+        const bool ok = t < g.q_len;
+        s_lse[tid] = ok ? a.lse[int64_t(h) * a.seq_len + g.q_global + t] * kLog2e : INFINITY;
+        s_del[tid] = ok ? a.delta[int64_t(h) * a.n_loc + g.q_start + t] : 0.f;
+      }
+      __syncthreads();
+      if (r0 + kTileRows < g.q_len) {  // next tile in flight during this one
+        tile_load(rq, a.q, row_bytes, hoff, tid, [&](int r) { return qrow(r0 + kTileRows + r); });
+        tile_load(rdo, a.dout, row_bytes, hoff, tid, [&](int r) { return qrow(r0 + kTileRows + r); });
+      }
+      // the wave's keys against the tile's longest prefix
+      const int tile_pre = g.kv_full + (g.diag ? min(r0 + kTileRows, g.q_len) : 0);
+      if (w_key0 >= tile_pre) continue;
+      f32x16 s[2], dp[2];
+      mm_rows(tq, bs.row, kf, s);
+      mm_rows(tdo, bs.row, vf, dp);
+      bf16x8 wp[2][2], ws[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int rl = 32 * qb + 8 * m + 4 * hf;  // tile row of register 4 m
+          const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[rl]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&s_del[rl]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * m + c;
+            const int t = r0 + rl + c;
+            const int pre = g.kv_full + (g.diag ? t + 1 : 0);
+            const float p = key < pre ? __builtin_amdgcn_exp2f(fmaf(s[qb][e], a.scale_log2, -lv[c])) : 0.f;
+            const float ds = p * (dp[qb][e] - dl[c]);
+            wp[qb][e >> 3][e & 7] = static_cast<__bf16>(p);
+            ws[qb][e >> 3][e & 7] = static_cast<__bf16>(ds);
+          }
+        }
+      }
+      mm_tr(tdo, bs.tr, wp, dv);
+      mm_tr(tq, bs.tr, ws, dk);
+    }
+  }
+  if (!kok) return;
+  // lane (key, hf) holds d = 32 b + 8 m + 4 hf + c of its key
+  float* dkp = a.dk + (int64_t(krow) * a.heads + h) * D;
+  float* dvp = a.dv + (int64_t(krow) * a.heads + h) * D;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int d0 = 32 * b + 8 * m + 4 * hf;
+      float4 x = *reinterpret_cast<float4*>(dkp + d0);
+      float4 y = *reinterpret_cast<float4*>(dvp + d0);
+      x.x += a.scale * dk[b][4 * m + 0];
+      x.y += a.scale * dk[b][4 * m + 1];
+      x.z += a.scale * dk[b][4 * m + 2];
+      x.w += a.scale * dk[b][4 * m + 3];
+      y.x += dv[b][4 * m + 0];
+      y.y += dv[b][4 * m + 1];
+      y.z += dv[b][4 * m + 2];
+      y.w += dv[b][4 * m + 3];
+      *reinterpret_cast<float4*>(dkp + d0) = x;
+      *reinterpret_cast<float4*>(dvp + d0) = y;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row-major: dQ of 128 rows.
+// ---------------------------------------------------------------------------
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_bf16_d128(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileBytes];
+  lds_u8* const tk = (lds_u8*)smem;
+  lds_u8* const tv = tk + kTileBytes;
+
+  const int h = blockIdx.x / a.total_tiles;
+  int t = blockIdx.x % a.total_tiles;
+  const int si = t < a.seg[0].tiles ? 0 : 1;
+  if (si) t -= a.seg[0].tiles;
+  const SegArgs& g = a.seg[si];
+  if (g.diag) t = g.tiles - 1 - t;  // longest rows first
+  const int row0 = t * kRows;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qc = lane & 31, hf = lane >> 5;
+  const int row = row0 + 32 * wv + qc;
+  const bool ok = row < g.q_len;
+  const int64_t grow = g.q_global + row;
+  const int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : 0;
+  const int w_first = row0 + 32 * wv;
+  const int w_last = min(w_first + 32, g.q_len);
+  const int w_max = w_last > w_first ? g.kv_full + (g.diag ? w_last : 0) : 0;
+  const int kv_end = g.kv_full + (g.diag ? min(row0 + kRows, g.q_len) : 0);
+  const uint32_t row_bytes = uint32_t(a.heads) * 256;
+  const uint32_t hoff = uint32_t(h) * 256;
+
+  bf16x8 qf[NT], dof[NT];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + (grow * a.heads + h) * D + 8 * hf;
+    const __bf16* dp = static_cast<const __bf16*>(a.dout) + (grow * a.heads + h) * D + 8 * hf;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      qf[i] = ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * i) : bf16x8{};
+      dof[i] = ok ? *reinterpret_cast<const bf16x8*>(dp + 16 * i) : bf16x8{};
+    }
+  }
+  const float lse2 = ok ? a.lse[int64_t(h) * a.seq_len + grow] * kLog2e : INFINITY;
+  const float del = ok ? a.delta[int64_t(h) * a.n_loc + g.q_start + row] : 0.f;
+  f32x16 dq[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
+  const Bases bs = make_bases(lane);
+
+  auto krow_of = [&](int kk) { return kv_row(a, min(kk, a.kv_valid - 1)); };
+  TileRegs rk, rv;
+  if (kv_end > 0) {
+    tile_load(rk, a.k, row_bytes, hoff, tid, [&](int r) { return krow_of(r); });
+    tile_load(rv, a.v, row_bytes, hoff, tid, [&](int r) { return krow_of(r); });
+  }
+  for (int j0 = 0; j0 < kv_end; j0 += kTileRows) {
+    __syncthreads();
+    tile_store(rk, tk, tid);
+    tile_store(rv, tv, tid);
+    __syncthreads();
+    if (j0 + kTileRows < kv_end) {
+      tile_load(rk, a.k, row_bytes, hoff, tid, [&](int r) { return krow_of(j0 + kTileRows + r); });
+      tile_load(rv, a.v, row_bytes, hoff, tid, [&](int r) { return krow_of(j0 + kTileRows + r); });
+    }
+    if (j0 >= w_max) continue;
+    f32x16 s[2], dp[2];
+    mm_rows(tk, bs.row, qf, s);
+    mm_rows(tv, bs.row, dof, dp);
+    bf16x8 ws[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kk = j0 + 32 * kb + 8 * (e >> 2) + 4 * hf + (e & 3);
+        const float p = kk < prefix ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], a.scale_log2, -lse2)) : 0.f;
+        ws[kb][e >> 3][e & 7] = static_cast<__bf16>(p * (dp[kb][e] - del));
+      }
+    mm_tr(tk, bs.tr, ws, dq);
+  }
+  if (!ok) return;
+  float* dqp = a.dq + (grow * a.heads + h) * D;
+  const bool first = g.epi != 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int d0 = 32 * b + 8 * m + 4 * hf;
+      float4 x = first ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<float4*>(dqp + d0);
+      x.x += a.scale * dq[b][4 * m + 0];
+      x.y += a.scale * dq[b][4 * m + 1];
+      x.z += a.scale * dq[b][4 * m + 2];
+      x.w += a.scale * dq[b][4 * m + 3];
+      *reinterpret_cast<float4*>(dqp + d0) = x;
+    }
+  }
+}
+
+}  // namespace
+
+bool bwd_mfma(int dtype_bf16, int head_dim) { return dtype_bf16 && head_dim == 128; }
+int bwd_mfma_rows() { return kRows; }
+int bwd_mfma_keys() { return kKeys; }
+
+hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t st) {
+  if (a.key_tiles > 0) bwd_dkdv_bf16_d128<<<unsigned(a.key_tiles) * unsigned(a.heads), kThreads, 0, st>>>(a);
+  if (a.total_tiles > 0) bwd_dq_bf16_d128<<<unsigned(a.total_tiles) * unsigned(a.heads), kThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn
