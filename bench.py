@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="graph mode: each call replays a recorded HIP graph")
     ap.add_argument("--merge", choices=["fused", "separate"], default="fused",
                     help="LSE merge in the attention epilogue (default) or in the separate merge/finalize kernels")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the share's backward (on by default with the extras)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one layout gather of q (a plain copy of known size) before timing, "
                          "as the reference for hardware traffic counters")
@@ -255,6 +257,45 @@ def sampled_parity(w, q, k, v, out, lse):
     return {"rows": int(rows.size), "heads": 2, "max_abs_dO": d_o, "max_abs_dLSE": d_l}
 
 
+def backward_section(plan, w, bufs, stream, reps):
+    """One rank's backward on the timed workload: time per call, TFLOP/s at the
+    usual 2.5x of the forward's valid FLOPs (five products of 2 head_dim flops
+    per valid pair), and dQ of sampled rows against the fp64 oracle."""
+    import oracle
+    from ring_context_parallelism_amd.inputs import make_qkv, to_numpy_f64
+    q, k, v, out, lse = bufs
+    dout_cpu = make_qkv(w.seq_len, w.heads, w.head_dim, w.dtype, w.seed + 7)[0]
+    dout = dout_cpu.cuda()
+    run_call(plan, w, bufs, stream)  # out and lse of the share
+    shape = (w.seq_len, w.heads, w.head_dim)
+    dq = torch.zeros(shape, device="cuda", dtype=torch.float32)
+    dk = torch.zeros(shape, device="cuda", dtype=torch.float32)
+    dv = torch.zeros(shape, device="cuda", dtype=torch.float32)
+    args = (q, k, v, out, lse, dout, dq, dk, dv, w.rank)
+    plan.rank_backward(*args, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        plan.rank_backward(*args, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.5 * 4 * w.head_dim * w.heads * share_pairs(plan, w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    # dQ of sampled rows of the share (written by the last call in full)
+    rows = oracle.rank_positions(w.seq_len, w.cp, w.rank, w.layout)
+    sample = rows[np.linspace(0, rows.size - 1, 8).astype(np.int64)]
+    q_cpu, k_cpu, v_cpu = (t.cpu() for t in (q, k, v))
+    ref = oracle.query_gradients(*(to_numpy_f64(t) for t in (q_cpu, k_cpu, v_cpu, dout_cpu)), sample, causal=w.causal)
+    got = dq.cpu().double().numpy()[sample]
+    rel = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    return {"ms_per_call": round(ms, 5), "tflops": round(tflops, 2),
+            "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "valid_flops": flops,
+            "flop_convention": "2.5 x forward valid flops",
+            "parity_dq_sampled_rows": {"rows": sample.tolist(), "max_rel_err": rel, "tol": 2e-2, "ok": rel <= 2e-2}}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -376,6 +417,13 @@ def main():
             result["imbalance"]["all_ranks_timed_workload"] = rank_step_imbalance(plan, w, bufs, stream)
             plan.set_graph(args.graph)
         result["imbalance"]["zigzag_step_time_imbalance"] = result["imbalance"]["zigzag"]["time_imbalance"]
+
+    if (args.backward or not args.no_extras) and w.rank is not None:
+        plan.set_graph(False)
+        result["backward"] = backward_section(plan, w, bufs, stream, max(3, args.steps // 4))
+        plan.set_graph(args.graph)
+        print(f"[bench] backward: {result['backward']['ms_per_call']} ms/call, "
+              f"{result['backward']['tflops']} TFLOP/s", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
         run_call(plan, w, bufs, stream)

@@ -30,7 +30,7 @@ routine; none is "parity unpinned".
 """
 
 from .attention import attention, attention_probabilities, valid_mask
-from .backward import attention_backward, rank_backward, full_backward
+from .backward import attention_backward, query_gradients, rank_backward, full_backward
 from .cp_reference import (
     chunk_size,
     padded_length,
@@ -51,6 +51,7 @@ __all__ = [
     "attention_probabilities",
     "valid_mask",
     "attention_backward",
+    "query_gradients",
     "rank_backward",
     "full_backward",
     "chunk_size",

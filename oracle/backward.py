@@ -65,6 +65,18 @@ def attention_backward(q, k, v, dout, *, causal, scale=None):
     return _pair_terms(q, k, v, dout, o, lse, pos, pos, causal, scale)
 
 
+def query_gradients(q, k, v, dout, rows, *, causal, scale=None):
+    """dQ of the natural-order rows ``rows`` only (all keys; cost linear in
+    ``len(rows)``): the same terms as ``attention_backward`` for those rows."""
+    q, k, v, dout = (_f64(x) for x in (q, k, v, dout))
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[2])
+    rows = np.asarray(rows, dtype=np.int64)
+    o, lse = attention(q[rows], k, v, causal=causal, scale=scale, q_pos=rows)
+    dq, _, _ = _pair_terms(q[rows], k, v, dout[rows], o, lse, rows, np.arange(k.shape[0]), causal, scale)
+    return dq
+
+
 def rank_backward(q, k, v, dout, cp, rank, *, layout=ZIGZAG, causal=True, scale=None):
     """One rank's share of the backward, one ring step at a time.
 

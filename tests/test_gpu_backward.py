@@ -134,3 +134,34 @@ def test_backward_is_deterministic():
     for a, b in zip(*runs):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     p.close()
+
+
+def test_full_size_backward_sampled_rows_and_gradient_sums():
+    """The 32k-token, cp 8 zigzag workload (32 heads x 128, bf16): dQ of sampled
+    rows against the oracle, and two properties of the complete key/value
+    gradients that hold at any size: sum_j dV_j = sum_i dO_i, sum_j dK_j = 0."""
+    from ring_context_parallelism_amd.inputs import WORKLOADS, workload_qkv
+    w = WORKLOADS["causal_s32768_cp8_zigzag_h32_d128_bf16_rank0"]
+    _say(f"full-size backward {w.name}")
+    q, k, v = workload_qkv(w)
+    dout = make_qkv(w.seq_len, w.heads, w.head_dim, "bf16", w.seed + 7)[0]
+    p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, True, w.layout)
+    dev = _dev()
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+    out, lse = _forward(p, qd, kd, vd)
+    dq, dk, dv = (torch.empty((w.seq_len, w.heads, w.head_dim), device=dev) for _ in range(3))
+    p.full_backward(qd, kd, vd, out, lse, dod, dq, dk, dv)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 2047, 2048, 9000, 16383, 16384, 30000, 32767])
+    ref = oracle.query_gradients(*(to_numpy_f64(t) for t in (q, k, v, dout)), rows, causal=True)
+    rel = float(np.max(np.abs(dq.cpu().double().numpy()[rows] - ref)) / np.max(np.abs(ref)))
+    _say(f"  sampled dq rel err {rel:.2e}")
+    assert rel <= REL[torch.bfloat16]
+    sdv = dv.double().sum(dim=0).cpu()
+    sdo = dod.double().sum(dim=0).cpu()
+    assert float((sdv - sdo).abs().max()) <= 1e-2 * float(sdo.abs().max())
+    sdk = dk.double().sum(dim=0).abs().max().cpu()
+    adk = dk.double().abs().sum(dim=0).max().cpu()
+    _say(f"  |sum dV - sum dO| {float((sdv - sdo).abs().max()):.3e}  |sum dK| {float(sdk):.3e} of {float(adk):.3e}")
+    assert float(sdk) <= 1e-2 * float(adk)
+    p.close()

@@ -76,6 +76,16 @@ def test_single_key_row_has_no_query_gradient():
     assert np.max(np.abs(dq[0])) == 0.0
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_query_gradients_equal_rows_of_the_whole(causal):
+    sq, heads, dim = 40, 2, 8
+    q, k, v, dout = (_rand((sq, heads, dim), 125 + i) for i in range(4))
+    dq, _, _ = oracle.attention_backward(q, k, v, dout, causal=causal)
+    rows = [0, 7, 19, 39]
+    got = oracle.query_gradients(q, k, v, dout, rows, causal=causal)
+    assert np.max(np.abs(got - dq[rows])) <= 1e-13
+
+
 CASES = [(64, 2, "zigzag", True), (96, 3, "zigzag", False), (64, 4, "contiguous", True),
          (80, 5, "contiguous", False), (101, 4, "zigzag", True), (13, 3, "contiguous", True),
          (21, 8, "zigzag", True)]
