@@ -40,6 +40,9 @@ from .cp_reference import (
     merge_partial,
     rank_forward,
     full_forward,
+    sequence_shards,
+    head_shards,
+    ulysses_forward,
     step_valid_pairs,
     step_valid_tiles,
     imbalance,
@@ -62,6 +65,9 @@ __all__ = [
     "merge_partial",
     "rank_forward",
     "full_forward",
+    "sequence_shards",
+    "head_shards",
+    "ulysses_forward",
     "step_valid_pairs",
     "step_valid_tiles",
     "imbalance",

@@ -160,6 +160,46 @@ def full_forward(q, k, v, cp, *, layout=ZIGZAG, causal=True, scale=None, step_or
     return out, lse
 
 
+def sequence_shards(x, cp, layout):
+    """Sequence ownership: ``[cp, S_pad/cp, H, D]``, rank ``r``'s rows in its
+    local order (its real rows first; pad rows zero)."""
+    x = np.asarray(x)
+    seq_len = x.shape[0]
+    n_loc = padded_length(seq_len, cp, layout) // cp
+    out = np.zeros((cp, n_loc) + x.shape[1:], dtype=x.dtype)
+    for r in range(cp):
+        pos = rank_positions(seq_len, cp, r, layout)
+        out[r, :pos.size] = x[pos]
+    return out
+
+
+def head_shards(x, cp):
+    """Head ownership after the Ulysses all-to-all ("Sequence Parallelism IV",
+    section 7 "CP vs Ulysses": a rank ends with every token of a head slice):
+    ``[cp, S, H/cp, D]``, rank ``r`` holding heads ``[r H/cp, (r+1) H/cp)``."""
+    x = np.asarray(x)
+    heads = x.shape[1]
+    if heads % cp:
+        raise ValueError("the head count must divide by cp (Ulysses is bounded by the heads)")
+    g = heads // cp
+    return np.stack([x[:, r * g:(r + 1) * g] for r in range(cp)])
+
+
+def ulysses_forward(q, k, v, cp, *, causal=True, scale=None):
+    """Every rank's attention over all tokens of its head slice, assembled to
+    natural order ``(O [S, H, D], LSE [H, S])``."""
+    qs, ks, vs = (head_shards(x, cp) for x in (q, k, v))
+    seq_len, heads, dim = np.shape(q)
+    g = heads // cp
+    out = np.zeros((seq_len, heads, dim))
+    lse = np.zeros((heads, seq_len))
+    for r in range(cp):
+        o, l = attention(qs[r], ks[r], vs[r], causal=causal, scale=scale)
+        out[:, r * g:(r + 1) * g] = o
+        lse[r * g:(r + 1) * g] = l
+    return out, lse
+
+
 def step_valid_pairs(seq_len, cp, layout, causal, rank, step):
     """Valid (q, k) pairs of one head in ring step ``step`` of rank ``rank``."""
     qpos = rank_positions(seq_len, cp, rank, layout)

@@ -499,3 +499,50 @@ def test_planted_transposed_operand_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "attention", swapped)
     with pytest.raises(AssertionError):
         test_o1_constant_values_are_reproduced(True)
+
+
+# --------------------------------------------------------------------------
+# Ulysses (sequence -> head ownership; "Sequence Parallelism IV", section 7)
+# --------------------------------------------------------------------------
+
+def test_head_shards_partition_heads_and_keep_every_token():
+    x = _rand((10, 6, 3), 150)
+    sh = oracle.head_shards(x, 3)
+    assert sh.shape == (3, 10, 2, 3)                        # every token, a third of the heads
+    assert np.array_equal(np.concatenate(list(sh), axis=1), x)  # heads in rank order rebuild x
+    one = oracle.head_shards(x, 6)                          # cp = heads: one head per rank
+    assert all(np.array_equal(one[h, :, 0], x[:, h]) for h in range(6))
+    with pytest.raises(ValueError):
+        oracle.head_shards(x, 4)
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+def test_sequence_shards_follow_the_chunk_map(layout):
+    x = _rand((13, 2, 4), 151)
+    sh = oracle.sequence_shards(x, 3, layout)
+    n_loc = oracle.padded_length(13, 3, layout) // 3
+    assert sh.shape == (3, n_loc, 2, 4)
+    seen = []
+    for r in range(3):
+        pos = oracle.rank_positions(13, 3, r, layout)
+        assert np.array_equal(sh[r, :pos.size], x[pos]) and not np.any(sh[r, pos.size:])
+        seen += pos.tolist()
+    assert sorted(seen) == list(range(13))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_ulysses_forward_equals_unsplit(causal):
+    q, k, v = (_rand((40, 8, 8), 152 + i) for i in range(3))
+    o, lse = oracle.attention(q, k, v, causal=causal)
+    o2, lse2 = oracle.ulysses_forward(q, k, v, 4, causal=causal)
+    assert np.max(np.abs(o2 - o)) <= 1e-12 and np.max(np.abs(lse2 - lse)) <= 1e-12
+
+
+def test_planted_head_slice_shift_is_caught(monkeypatch):
+    real = cp_reference.head_shards
+
+    def shifted(x, cp):
+        return real(np.roll(np.asarray(x), 1, axis=1), cp)
+    monkeypatch.setattr(cp_reference, "head_shards", shifted)
+    with pytest.raises(AssertionError):
+        test_ulysses_forward_equals_unsplit(True)
