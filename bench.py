@@ -296,6 +296,60 @@ def backward_section(plan, w, bufs, stream, reps):
             "parity_dq_sampled_rows": {"rows": sample.tolist(), "max_rel_err": rel, "tol": 2e-2, "ok": rel <= 2e-2}}
 
 
+def ulysses_section(plan, w, bufs, stream, reps):
+    """Ulysses variant on the timed workload: the all-to-all of Q, K, V to head
+    ownership (every rank at once on one GPU), rank 0's attention over all
+    tokens of its head slice, the all-to-all of O back."""
+    q, k, v, out, lse = bufs
+    cp, heads, dim = w.cp, w.heads, w.head_dim
+    if heads % cp:
+        return None
+    g = heads // cp
+    n_seq = cp * plan.local_rows()
+    seq_l = [torch.empty((n_seq, heads, dim), device="cuda", dtype=q.dtype) for _ in range(3)]
+    for src, dst in zip((q, k, v), seq_l):
+        plan.layout_gather(src, dst, stream=stream)
+    head_l = [torch.empty((cp, w.seq_len, g, dim), device="cuda", dtype=q.dtype) for _ in range(3)]
+    out_h = torch.empty((cp, w.seq_len, g, dim), device="cuda", dtype=q.dtype)
+    lse_h = torch.empty((heads, w.seq_len), device="cuda", dtype=torch.float32)
+    out_s = torch.empty((n_seq, heads, dim), device="cuda", dtype=q.dtype)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def a2a_in():
+        for s_l, h_l in zip(seq_l, head_l):
+            plan.ulysses_a2a(s_l, h_l, True, stream=stream)
+
+    ms_in = timed(a2a_in)
+    ms_rank0 = timed(lambda: plan.ulysses_forward(head_l[0][0], head_l[1][0], head_l[2][0], out_h[0], lse_h[:g],
+                                                  stream=stream))
+
+    def all_ranks():
+        for r in range(cp):
+            plan.ulysses_forward(head_l[0][r], head_l[1][r], head_l[2][r], out_h[r], lse_h[r * g:(r + 1) * g],
+                                 stream=stream)
+    ms_all = timed(all_ranks)
+    ms_out = timed(lambda: plan.ulysses_a2a(out_h, out_s, False, stream=stream))
+    pairs = w.seq_len * (w.seq_len + 1) // 2 if w.causal else w.seq_len * w.seq_len
+    rank_flops = 4 * dim * g * pairs
+    tensor_bytes = w.seq_len * heads * dim * q.element_size()
+    return {"heads_per_rank": g, "a2a_qkv_ms": round(ms_in, 5), "a2a_out_ms": round(ms_out, 5),
+            "a2a_gbps": round(2 * tensor_bytes / (ms_out * 1e-3) / 1e9, 1),
+            "rank0_attention_ms": round(ms_rank0, 5),
+            "rank0_attention_tflops": round(rank_flops / (ms_rank0 * 1e-3) / 1e12, 2),
+            "all_ranks_attention_ms": round(ms_all, 5),
+            "note": "one GPU: each all-to-all moves every rank's data (a rank's part is 1/cp of it)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -417,6 +471,9 @@ def main():
             result["imbalance"]["all_ranks_timed_workload"] = rank_step_imbalance(plan, w, bufs, stream)
             plan.set_graph(args.graph)
         result["imbalance"]["zigzag_step_time_imbalance"] = result["imbalance"]["zigzag"]["time_imbalance"]
+
+    if not args.no_extras:
+        result["ulysses"] = ulysses_section(plan, w, bufs, stream, max(3, args.steps // 4))
 
     if (args.backward or not args.no_extras) and w.rank is not None:
         plan.set_graph(False)

@@ -180,6 +180,33 @@ int cp_attn_rank_forward(cp_attn_plan_t plan, const void* q, const void* k, cons
 int cp_attn_allgather_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
                               float* lse, int rank, void* stream);
 
+/*
+ * Ulysses variant ("Sequence Parallelism IV: Megatron Context Parallel and
+ * Load-Balanced Rings", section 7 "CP vs Ulysses"): an all-to-all moves the
+ * ranks from sequence ownership to head ownership, after which a rank holds
+ * every token of a slice of heads_per_rank = heads / cp_size heads and runs
+ * plain attention on it; a second all-to-all moves the output back.  The
+ * head count bounds the degree: both calls return EUNSUPPORTED unless
+ * heads % cp_size == 0.
+ *
+ * cp_attn_ulysses_a2a: the all-to-all of every rank at once, plan dtype,
+ * bit-exact copies.  to_heads = 1: src is the sequence layout
+ * [cp][local_rows][heads][head_dim] (as cp_attn_layout_gather writes it),
+ * dst the head layout [cp][S][heads_per_rank][head_dim] (rank r: heads
+ * r*heads_per_rank .. (r+1)*heads_per_rank-1 of every token, natural order).
+ * to_heads = 0: the reverse (pad rows of the sequence layout are not
+ * written).  EINVAL for null/misaligned pointers or to_heads outside {0, 1}.
+ */
+int cp_attn_ulysses_a2a(cp_attn_plan_t plan, const void* src, void* dst, int to_heads, void* stream);
+
+/* One rank's Ulysses attention: q, k, v, out [S][heads_per_rank][head_dim]
+ * (that rank's slice of the head layout), lse [heads_per_rank][S] fp32 (4-byte
+ * alignment suffices: it may be rows r*heads_per_rank.. of a [heads][S]
+ * array); the plan's mask (causal or bidirectional) over all S tokens, one
+ * launch of the step kernel.  EUNSUPPORTED also when a slice exceeds 4 GiB. */
+int cp_attn_ulysses_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out, float* lse,
+                            void* stream);
+
 /* Every rank's share back to back on `stream` (ranks 0..cp_size-1); fills all
  * rows of out and lse.  Same arguments and errors as cp_attn_rank_forward. */
 int cp_attn_full_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,

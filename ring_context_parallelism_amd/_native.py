@@ -50,6 +50,8 @@ SIGNATURES = {
     "cp_attn_set_streams": (ctypes.c_int, [_c_p, _c_p, _c_p]),
     "cp_attn_rank_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_p]),
     "cp_attn_full_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
+    "cp_attn_ulysses_a2a": (ctypes.c_int, [_c_p, _c_p, _c_p, ctypes.c_int, _c_p]),
+    "cp_attn_ulysses_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "cp_attn_rank_backward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int,
                                              _c_p]),
     "cp_attn_full_backward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),

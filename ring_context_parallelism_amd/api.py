@@ -131,6 +131,33 @@ class Plan:
         N.check(self.lib.cp_attn_full_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                               _stream_ptr(stream)), "cp_attn_full_forward")
 
+    # -- Ulysses ----------------------------------------------------------
+    def heads_per_rank(self):
+        return self.heads // self.cp_size
+
+    def ulysses_a2a(self, src, dst, to_heads, stream=None):
+        """sequence layout ``[cp * local_rows, H, D]`` <-> head layout ``[cp, S, H/cp, D]``."""
+        seq_n = self.cp_size * self.local_rows() * self.heads * self.head_dim
+        head_n = self.seq_len * self.heads * self.head_dim
+        want = {"src": head_n if not to_heads else seq_n, "dst": head_n if to_heads else seq_n}
+        for name, t in (("src", src), ("dst", dst)):
+            if t.numel() != want[name] or t.dtype != self.dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {self.dtype} CUDA tensor with {want[name]} elements")
+        N.check(self.lib.cp_attn_ulysses_a2a(self._h, _ptr(src), _ptr(dst), int(bool(to_heads)), _stream_ptr(stream)),
+                "cp_attn_ulysses_a2a")
+
+    def ulysses_forward(self, q, k, v, out, lse, stream=None):
+        """One rank's head slice: q, k, v, out ``[S, H/cp, D]``, lse ``[H/cp, S]``."""
+        g = self.heads // self.cp_size
+        shape = (self.seq_len, g, self.head_dim)
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+            if tuple(t.shape) != shape or t.dtype != self.dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {self.dtype} CUDA tensor of shape {shape}")
+        if tuple(lse.shape) != (g, self.seq_len) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError(f"lse must be a contiguous float32 CUDA tensor of shape {(g, self.seq_len)}")
+        N.check(self.lib.cp_attn_ulysses_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                                 _stream_ptr(stream)), "cp_attn_ulysses_forward")
+
     # -- backward -------------------------------------------------------
     def _check_bwd(self, dout, dq, dk, dv):
         shape = (self.seq_len, self.heads, self.head_dim)

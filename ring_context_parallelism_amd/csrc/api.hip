@@ -453,12 +453,16 @@ int check_plan(cp_attn_plan_t h) {
   return CP_ATTN_OK;
 }
 
-int check_io(const void* q, const void* k, const void* v, const void* out, const void* lse) {
+// lse_align: the alignment demanded of lse (it is only ever written with
+// 4-byte stores; entry points that document 4 pass 4)
+int check_io(const void* q, const void* k, const void* v, const void* out, const void* lse, int lse_align = 16) {
   const void* ptrs[5] = {q, k, v, out, lse};
   const char* names[5] = {"q", "k", "v", "out", "lse"};
   for (int i = 0; i < 5; ++i) {
     if (!ptrs[i]) return fail(CP_ATTN_EINVAL, std::string(names[i]) + " is null");
-    if (!aligned16(ptrs[i])) return fail(CP_ATTN_EINVAL, std::string(names[i]) + " is not 16-byte aligned");
+    const uintptr_t al = i == 4 ? uintptr_t(lse_align) : 16u;
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % al != 0)
+      return fail(CP_ATTN_EINVAL, std::string(names[i]) + " is not " + std::to_string(al) + "-byte aligned");
   }
   return CP_ATTN_OK;
 }
@@ -830,6 +834,82 @@ int cp_attn_allgather_forward(cp_attn_plan_t h, const void* q, const void* k, co
     a.total_tiles += x.tiles;
   }
   if (a.nseg == 0) return CP_ATTN_OK;  // a rank of pad only
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
+  if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
+  return CP_ATTN_OK;
+  CPA_GUARD_END
+}
+
+// Ulysses: the all-to-all of every rank at once, and one rank's attention over
+// every token of its head slice (one launch of the step kernel, identity key
+// map, the whole sequence as one segment).
+int cp_attn_ulysses_a2a(cp_attn_plan_t h, const void* src, void* dst, int to_heads, void* stream) {
+  CPA_GUARD_BEGIN
+  CPA_TRY(check_plan(h));
+  Plan& p = *h->p;
+  if (p.heads % p.cp != 0) return fail(CP_ATTN_EUNSUPPORTED, "Ulysses needs heads divisible by cp_size");
+  if (!src || !dst) return fail(CP_ATTN_EINVAL, "src or dst is null");
+  if (!aligned16(src) || !aligned16(dst)) return fail(CP_ATTN_EINVAL, "src or dst not 16-byte aligned");
+  if (to_heads != 0 && to_heads != 1) return fail(CP_ATTN_EINVAL, "to_heads must be 0 or 1");
+  CPA_TRY(ensure_device(p));
+  UlyssesArgs u{};
+  u.src = src;
+  u.dst = dst;
+  u.to_heads = to_heads;
+  u.cp = p.cp;
+  u.zigzag = p.layout == 1;
+  u.seq_len = p.seq_len;
+  u.chunk = p.chunk;
+  u.n_loc = p.n_loc;
+  u.heads = p.heads;
+  u.head_vec = int64_t(p.head_dim) * p.elem_bytes() / 16;
+  CPA_HIP(launch_ulysses(u, static_cast<hipStream_t>(stream)));
+  return CP_ATTN_OK;
+  CPA_GUARD_END
+}
+
+int cp_attn_ulysses_forward(cp_attn_plan_t h, const void* q, const void* k, const void* v, void* out, float* lse,
+                            void* stream) {
+  CPA_GUARD_BEGIN
+  CPA_TRY(check_plan(h));
+  Plan& p = *h->p;
+  if (p.heads % p.cp != 0) return fail(CP_ATTN_EUNSUPPORTED, "Ulysses needs heads divisible by cp_size");
+  CPA_TRY(check_io(q, k, v, out, lse, 4));  // lse may be a row slice of a [heads][S] array
+  const int32_t group = p.heads / p.cp;
+  if (p.seq_len * group * p.head_dim * p.elem_bytes() > int64_t(UINT32_MAX))
+    return fail(CP_ATTN_EUNSUPPORTED, "a head slice beyond 4 GiB");
+  CPA_TRY(ensure_device(p));
+  const bool bf16 = p.dtype == CP_ATTN_BF16;
+  const int bm = bf16 ? attn_bf16_block_m(p.head_dim) : attn_f32_block_m();
+  StepArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_bytes = p.seq_len * group * p.head_dim * p.elem_bytes();
+  a.kv_lo = 0;
+  a.kv_hi = 0;
+  a.kv_split = int32_t(p.seq_len);
+  a.out = out;
+  a.lse = lse;
+  a.seq_len = p.seq_len;
+  a.n_loc = int32_t(p.seq_len);
+  a.kv_valid = int32_t(p.seq_len);
+  a.heads = group;
+  a.scale = 1.0f / std::sqrt(float(p.head_dim));
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.out_f32 = p.dtype == CP_ATTN_FP32;
+  a.nseg = 1;
+  SegArgs& x = a.seg[0];
+  x.q_global = 0;
+  x.q_start = 0;
+  x.q_len = int32_t(p.seq_len);
+  x.kv_full = p.causal ? 0 : int32_t(p.seq_len);
+  x.diag = p.causal ? 1 : 0;
+  x.ksplit = 1;
+  x.tiles = int32_t((p.seq_len + bm - 1) / bm);
+  x.epi = kEpiInit | kEpiFinal;
+  a.total_tiles = x.tiles;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));

@@ -153,6 +153,23 @@ hipError_t launch_layout(const LayoutArgs& a, int max_blocks, hipStream_t stream
 
 hipError_t launch_recv(const RecvArgs& a, int blocks, hipStream_t stream);
 
+// Ulysses all-to-all of every rank at once (one GPU): sequence ownership
+// [cp][n_loc][H][D] (each rank's rows in its local order) <-> head ownership
+// [cp][S][H/cp][D] (rank r: every token of heads r H/cp .. (r+1) H/cp - 1).
+struct UlyssesArgs {
+  const void* src;
+  void* dst;
+  int32_t to_heads;  // 1: sequence -> head ownership, 0: back (pad rows of the sequence layout untouched)
+  int32_t cp;
+  int32_t zigzag;
+  int64_t seq_len;   // real tokens
+  int64_t chunk;     // rows per chunk
+  int64_t n_loc;     // rows per rank in the sequence layout
+  int64_t heads;
+  int64_t head_vec;  // 16-byte vectors per head row (head_dim * element size / 16)
+};
+hipError_t launch_ulysses(const UlyssesArgs& a, hipStream_t stream);
+
 // Fill with NaN (all-ones bytes) -- a kernel, not a memset, so it is safe in captured graphs.
 hipError_t launch_poison(void* ptr, int64_t bytes, hipStream_t stream);
 hipError_t launch_fill_words(void* ptr, int64_t words, uint32_t value, hipStream_t stream);

@@ -53,6 +53,37 @@ __global__ __launch_bounds__(kThreads) void layout_copy(LayoutArgs a) {
   }
 }
 
+// Ulysses all-to-all ("Sequence Parallelism IV: Megatron Context Parallel and
+// Load-Balanced Rings", section 7 "CP vs Ulysses": the transpose from
+// sequence ownership to head ownership).  One workgroup per (head owner r',
+// token t) row of the head layout: the H/cp heads of token t that r' receives
+// are one contiguous run in the sequence owner's local row, so both sides
+// move whole 16-byte vectors.
+__global__ __launch_bounds__(kThreads) void ulysses_copy(UlyssesArgs a) {
+  const uint4* src = static_cast<const uint4*>(a.src);
+  uint4* dst = static_cast<uint4*>(a.dst);
+  const int64_t group = a.heads / a.cp;
+  const int64_t run = group * a.head_vec;  // vectors per (r', t)
+  const int64_t rows = int64_t(a.cp) * a.seq_len;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const int64_t rh = row / a.seq_len, t = row % a.seq_len;
+    const int64_t c = t / a.chunk;
+    int64_t owner, li;
+    if (a.zigzag) {
+      owner = c < a.cp ? c : 2 * int64_t(a.cp) - 1 - c;
+      li = (c < a.cp ? 0 : a.chunk) + t % a.chunk;
+    } else {
+      owner = c;
+      li = t % a.chunk;
+    }
+    const int64_t hs = row * run;                                                  // head layout
+    const int64_t sq = ((owner * a.n_loc + li) * a.heads + rh * group) * a.head_vec;  // sequence layout
+    const int64_t from = a.to_heads ? sq : hs;
+    const int64_t to = a.to_heads ? hs : sq;
+    for (int64_t v = threadIdx.x; v < run; v += kThreads) dst[to + v] = src[from + v];
+  }
+}
+
 // Ring receive as a kernel of its own on the copy stream: one wave per
 // workgroup and at most 16 VGPRs, so its waves fit in the registers the step
 // kernel leaves free on each SIMD and the copy runs beside the step instead
@@ -176,6 +207,12 @@ hipError_t launch_layout(const LayoutArgs& a, int max_blocks, hipStream_t stream
   const unsigned cap = max_blocks > 0 ? unsigned(max_blocks) : 65536u;
   const dim3 grid(grid_for(rows, 1, cap), unsigned(a.ntensors));
   layout_copy<<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ulysses(const UlyssesArgs& a, hipStream_t stream) {
+  const int64_t rows = int64_t(a.cp) * a.seq_len;
+  ulysses_copy<<<grid_for(rows, 1, 65536u), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

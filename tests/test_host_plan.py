@@ -217,3 +217,17 @@ def test_workspace_size_formula():
     assert p.workspace_bytes() == 4 * kv + o + lse + 2 * (o + lse) + cnt
     q = Plan(256, 2, 2, 64, True, "zigzag", dtype=torch.float32)
     assert q.workspace_bytes() == 4 * (128 * 128 * 4) + 3 * (128 * 128 * 4 + 2 * 128 * 4) + 256
+
+
+def test_ulysses_argument_errors_enqueue_nothing():
+    """Ulysses is bounded by the head count: heads % cp != 0 is unsupported;
+    bad flags are rejected before any device work."""
+    lib = N.lib()
+    dummy = ctypes.c_void_p(1 << 20)  # never dereferenced
+    with Plan(96, 3, 2, 64, True, "zigzag") as p:
+        assert lib.cp_attn_ulysses_a2a(p._h, dummy, dummy, 1, None) == N.EUNSUPPORTED
+        assert lib.cp_attn_ulysses_forward(p._h, dummy, dummy, dummy, dummy, dummy, None) == N.EUNSUPPORTED
+    with Plan(96, 2, 4, 64, True, "zigzag") as p:
+        assert lib.cp_attn_ulysses_a2a(p._h, dummy, dummy, 2, None) == N.EINVAL
+        assert lib.cp_attn_ulysses_a2a(p._h, None, dummy, 1, None) == N.EINVAL
+        assert lib.cp_attn_ulysses_forward(p._h, None, dummy, dummy, dummy, dummy, None) == N.EINVAL
