@@ -29,7 +29,7 @@ against closed forms, invariants, brute force or an independent library
 routine; none is "parity unpinned".
 """
 
-from .attention import attention, attention_probabilities, valid_mask
+from .attention import attention, attention_probabilities, document_of, valid_mask
 from .backward import attention_backward, query_gradients, rank_backward, full_backward
 from .cp_reference import (
     chunk_size,
@@ -53,6 +53,7 @@ __all__ = [
     "attention",
     "attention_probabilities",
     "valid_mask",
+    "document_of",
     "attention_backward",
     "query_gradients",
     "rank_backward",

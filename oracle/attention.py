@@ -38,12 +38,21 @@ def _as_f64(x):
     return a
 
 
-def valid_mask(q_pos, k_pos, causal, k_valid=None):
+def document_of(pos, doc_starts):
+    """Index of the document holding each global position; documents are the
+    runs ``[doc_starts[d], doc_starts[d + 1])`` (the first starts at 0)."""
+    return np.searchsorted(np.asarray(doc_starts, dtype=np.int64), np.asarray(pos, dtype=np.int64), side="right") - 1
+
+
+def valid_mask(q_pos, k_pos, causal, k_valid=None, doc_starts=None):
     """Boolean ``[len(q_pos), len(k_pos)]`` mask of valid (query, key) pairs.
 
     Causal: a key is valid when its global position is not after the query's.
     Bidirectional: every pair is valid.  ``k_valid`` (optional, per key) masks
-    keys out entirely, as padded keys are.
+    keys out entirely, as padded keys are.  ``doc_starts`` (optional; the
+    document masks of "Context Parallelism for Long-Context Training",
+    section "Prove attention equivalence") keeps only pairs whose query and
+    key lie in the same document.
     """
     q_pos = np.asarray(q_pos, dtype=np.int64)
     k_pos = np.asarray(k_pos, dtype=np.int64)
@@ -53,15 +62,19 @@ def valid_mask(q_pos, k_pos, causal, k_valid=None):
         m = k_pos[None, :] <= q_pos[:, None]
     if k_valid is not None:
         m = m & np.asarray(k_valid, dtype=bool)[None, :]
+    if doc_starts is not None:
+        m = m & (document_of(q_pos, doc_starts)[:, None] == document_of(k_pos, doc_starts)[None, :])
     return m
 
 
-def attention(q, k, v, *, causal, scale=None, q_pos=None, k_pos=None, k_valid=None, block=1024):
+def attention(q, k, v, *, causal, scale=None, q_pos=None, k_pos=None, k_valid=None, doc_starts=None, block=1024):
     """Unsplit softmax attention.
 
     q: ``[Sq, H, D]``; k, v: ``[Sk, H, D]`` (any real dtype; upcast to fp64).
     q_pos, k_pos: global token positions of the rows (default ``arange``).
     k_valid: optional per-key flags; False keys are masked out (padding).
+    doc_starts: optional sorted document starts (first 0); pairs across
+    documents are masked out.
     Returns ``(O [Sq, H, D] fp64, LSE [H, Sq] fp64)``.
     """
     q = _as_f64(q)
@@ -86,7 +99,7 @@ def attention(q, k, v, *, causal, scale=None, q_pos=None, k_pos=None, k_valid=No
         for i0 in range(0, sq, block):
             i1 = min(sq, i0 + block)
             s = scale * (q[i0:i1, h, :] @ kh.T)
-            valid = valid_mask(q_pos[i0:i1], k_pos, causal, k_valid)
+            valid = valid_mask(q_pos[i0:i1], k_pos, causal, k_valid, doc_starts=doc_starts)
             s = np.where(valid, s, -np.inf)
             m = s.max(axis=1)
             has = np.isfinite(m)

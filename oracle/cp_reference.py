@@ -38,7 +38,7 @@ This module has its own chunk map; it does not use the HIP library's plan.
 
 import numpy as np
 
-from .attention import attention
+from .attention import attention, valid_mask
 
 ZIGZAG = "zigzag"
 CONTIGUOUS = "contiguous"
@@ -122,7 +122,7 @@ def merge_partial(o_acc, lse_acc, o_s, lse_s):
     return o_new, new.T.copy()
 
 
-def rank_forward(q, k, v, cp, rank, *, layout=ZIGZAG, causal=True, scale=None, step_order=None):
+def rank_forward(q, k, v, cp, rank, *, layout=ZIGZAG, causal=True, scale=None, step_order=None, doc_starts=None):
     """One rank's share: its Q rows against every rank's K/V, one ring step at a time.
 
     q, k, v: natural-order ``[S, H, D]``.  Returns ``(O_loc [n, H, D],
@@ -139,12 +139,12 @@ def rank_forward(q, k, v, cp, rank, *, layout=ZIGZAG, causal=True, scale=None, s
         j = ring_source(rank, s, cp)
         kpos = rank_positions(seq_len, cp, j, layout)
         o_s, lse_s = attention(qloc, np.asarray(k)[kpos], np.asarray(v)[kpos],
-                               causal=causal, scale=scale, q_pos=qpos, k_pos=kpos)
+                               causal=causal, scale=scale, q_pos=qpos, k_pos=kpos, doc_starts=doc_starts)
         o_acc, lse_acc = merge_partial(o_acc, lse_acc, o_s, lse_s)
     return o_acc, lse_acc, qpos
 
 
-def full_forward(q, k, v, cp, *, layout=ZIGZAG, causal=True, scale=None, step_orders=None):
+def full_forward(q, k, v, cp, *, layout=ZIGZAG, causal=True, scale=None, step_orders=None, doc_starts=None):
     """Every rank's share, assembled back to natural token order.
 
     Returns ``(O [S, H, D], LSE [H, S])``.
@@ -154,7 +154,8 @@ def full_forward(q, k, v, cp, *, layout=ZIGZAG, causal=True, scale=None, step_or
     lse = np.full((heads, seq_len), -np.inf, dtype=np.float64)
     for r in range(cp):
         order = None if step_orders is None else step_orders[r]
-        o, l, pos = rank_forward(q, k, v, cp, r, layout=layout, causal=causal, scale=scale, step_order=order)
+        o, l, pos = rank_forward(q, k, v, cp, r, layout=layout, causal=causal, scale=scale, step_order=order,
+                                 doc_starts=doc_starts)
         out[pos] = o
         lse[:, pos] = l
     return out, lse
@@ -200,10 +201,12 @@ def ulysses_forward(q, k, v, cp, *, causal=True, scale=None):
     return out, lse
 
 
-def step_valid_pairs(seq_len, cp, layout, causal, rank, step):
+def step_valid_pairs(seq_len, cp, layout, causal, rank, step, doc_starts=None):
     """Valid (q, k) pairs of one head in ring step ``step`` of rank ``rank``."""
     qpos = rank_positions(seq_len, cp, rank, layout)
     kpos = rank_positions(seq_len, cp, ring_source(rank, step, cp), layout)
+    if doc_starts is not None:
+        return int(valid_mask(qpos, kpos, causal, doc_starts=doc_starts).sum())
     if not causal:
         return int(qpos.size * kpos.size)
     ks = np.sort(kpos)

@@ -456,7 +456,7 @@ def test_golden_hashes_and_oracle_summary():
 
 def test_planted_mask_off_by_one_is_caught(monkeypatch):
     """A mask that drops the diagonal breaks the zero-query closed form."""
-    def strict(q_pos, k_pos, causal, k_valid=None):
+    def strict(q_pos, k_pos, causal, k_valid=None, doc_starts=None):
         q_pos = np.asarray(q_pos)
         k_pos = np.asarray(k_pos)
         return k_pos[None, :] < q_pos[:, None] if causal else np.ones((q_pos.size, k_pos.size), bool)
@@ -546,3 +546,46 @@ def test_planted_head_slice_shift_is_caught(monkeypatch):
     monkeypatch.setattr(cp_reference, "head_shards", shifted)
     with pytest.raises(AssertionError):
         test_ulysses_forward_equals_unsplit(True)
+
+
+# --------------------------------------------------------------------------
+# Document masks ("Context Parallelism for Long-Context Training", section
+# "Prove attention equivalence": test causal and document masks)
+# --------------------------------------------------------------------------
+
+DOCS = [0, 5, 6, 17, 30]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_document_mask_equals_separate_documents(causal):
+    """Masked attention over packed documents equals attention run on each
+    document alone (positions restart per document), concatenated."""
+    seq = 41
+    q, k, v = (_rand((seq, 2, 4), 160 + i) for i in range(3))
+    o, lse = oracle.attention(q, k, v, causal=causal, doc_starts=DOCS)
+    ends = DOCS[1:] + [seq]
+    for a, b in zip(DOCS, ends):
+        oa, la = _brute_force(q[a:b], k[a:b], v[a:b], causal, 0.5)
+        assert np.max(np.abs(o[a:b] - oa)) <= 1e-12 and np.max(np.abs(lse[:, a:b] - la)) <= 1e-12
+
+
+def test_document_of_by_hand():
+    assert oracle.document_of([0, 4, 5, 6, 16, 17, 29, 30, 40], DOCS).tolist() == [0, 0, 1, 2, 2, 3, 3, 4, 4]
+
+
+@pytest.mark.parametrize("seq,cp,layout,causal", [(64, 4, "zigzag", True), (41, 3, "zigzag", False),
+                                                  (41, 4, "contiguous", True), (64, 2, "contiguous", False)])
+def test_cp_decomposition_with_documents_equals_unsplit(seq, cp, layout, causal):
+    q, k, v = (_rand((seq, 2, 8), 170 + i) for i in range(3))
+    o, lse = oracle.attention(q, k, v, causal=causal, doc_starts=DOCS)
+    o2, lse2 = oracle.full_forward(q, k, v, cp, layout=layout, causal=causal, doc_starts=DOCS)
+    assert np.max(np.abs(o2 - o)) <= 1e-12 and np.max(np.abs(lse2 - lse)) <= 1e-12
+
+
+def test_document_pairs_sum_to_per_document_triangles():
+    seq, cp = 41, 3
+    ends = DOCS[1:] + [seq]
+    for layout in ("zigzag", "contiguous"):
+        tot = sum(oracle.step_valid_pairs(seq, cp, layout, True, r, s, doc_starts=DOCS)
+                  for r in range(cp) for s in range(cp))
+        assert tot == sum((b - a) * (b - a + 1) // 2 for a, b in zip(DOCS, ends))
