@@ -140,8 +140,9 @@ int cp_attn_set_option(cp_attn_plan_t plan, int option, int value);
 
 /* Bytes of device workspace a forward call needs: two K/V receive slots, the
  * fp32 running state (O, LSE), two fp32 partial buffers (separate merge mode,
- * or the two key halves of a split step) and (n_loc/256 + 2) * heads int32
- * split counters, each rounded up to 256 bytes.  The library zeroes the
+ * or the two key halves of a split step), (n_loc/256 + 2) * heads int32
+ * split counters and the document table (2 int32 per token), each rounded
+ * up to 256 bytes.  The library zeroes the
  * counters once per workspace (synchronously, on the next forward call). */
 int cp_attn_workspace_bytes(cp_attn_plan_t plan, int64_t* bytes);
 
@@ -156,6 +157,25 @@ int cp_attn_set_workspace(cp_attn_plan_t plan, void* device_ptr, int64_t bytes);
  * as void*).  NULL lets the library create and own non-blocking streams of
  * default priority on first use. */
 int cp_attn_set_streams(cp_attn_plan_t plan, void* copy_stream, void* merge_stream);
+
+/*
+ * Document masks ("Context Parallelism for Long-Context Training", section
+ * "Prove attention equivalence": causal and document masks).  The S tokens
+ * are cut into `count` documents; document d holds the positions
+ * [starts[d], starts[d+1]) and the last one runs to S.  A query then attends
+ * only to keys of its own document, on top of the plan's causal or
+ * bidirectional mask.  starts: host array, strictly increasing, starts[0] =
+ * 0, every entry below S; the plan keeps a copy.  count = 0 removes the
+ * documents.  The forward calls (ring, all-gather, Ulysses) honour them; the
+ * backward calls return EUNSUPPORTED while documents are set.  The device
+ * table (two int32 per token, in the workspace) is written by the next
+ * forward call, which first waits for the device.  A query row that sees no
+ * key of a ring step takes nothing from that step; the key split
+ * (CP_ATTN_OPT_KSPLIT) is not used while documents are set.
+ * EINVAL for an unsorted list, a first start other than 0, a start >= S, a
+ * negative count or a null starts with count > 0.  Host-only.
+ */
+int cp_attn_set_documents(cp_attn_plan_t plan, const int64_t* starts, int64_t count);
 
 /*
  * One rank's share, asynchronous on `stream`: for s = 0..cp_size-1 the rank's
@@ -269,7 +289,8 @@ int cp_attn_step_segments(cp_attn_plan_t plan, int rank, int step, int64_t out[1
 
 /* Valid (query, key) pairs of one head in (rank, step), and tiles of
  * bm local rows x bn local keys holding at least one valid pair (tiles laid
- * from local index 0, last tile of each axis clipped). */
+ * from local index 0, last tile of each axis clipped); document masks
+ * included when set. */
 int cp_attn_valid_work(cp_attn_plan_t plan, int rank, int step, int bm, int bn, int64_t* tiles,
                        int64_t* pairs);
 

@@ -48,6 +48,7 @@ SIGNATURES = {
     "cp_attn_workspace_bytes": (ctypes.c_int, [_c_p, ctypes.POINTER(_i64)]),
     "cp_attn_set_workspace": (ctypes.c_int, [_c_p, _c_p, _i64]),
     "cp_attn_set_streams": (ctypes.c_int, [_c_p, _c_p, _c_p]),
+    "cp_attn_set_documents": (ctypes.c_int, [_c_p, ctypes.POINTER(_i64), _i64]),
     "cp_attn_rank_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_p]),
     "cp_attn_full_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "cp_attn_ulysses_a2a": (ctypes.c_int, [_c_p, _c_p, _c_p, ctypes.c_int, _c_p]),

@@ -37,6 +37,7 @@ class Plan:
         self.causal, self.layout = bool(causal), layout
         self.dtype = dtype
         self._workspace = None
+        self.documents = None
         N.check(self.lib.cp_attn_set_dtype(self._h, _DTYPES[dtype]), "cp_attn_set_dtype")
 
     # -- lifetime -------------------------------------------------------
@@ -105,6 +106,14 @@ class Plan:
         m = ctypes.c_void_p(merge_stream.cuda_stream) if merge_stream is not None else None
         N.check(self.lib.cp_attn_set_streams(self._h, c, m), "cp_attn_set_streams")
         self._streams = (copy_stream, merge_stream)
+
+    def set_documents(self, starts):
+        """Document masks: document d holds positions [starts[d], starts[d+1]) (the
+        last runs to seq_len); starts increases strictly from 0.  None or [] clears."""
+        starts = [] if starts is None else [int(x) for x in starts]
+        arr = (ctypes.c_int64 * max(1, len(starts)))(*starts)
+        N.check(self.lib.cp_attn_set_documents(self._h, arr, len(starts)), "cp_attn_set_documents")
+        self.documents = tuple(starts) if starts else None
 
     # -- forward --------------------------------------------------------
     def _check_io(self, q, k, v, out, lse):

@@ -51,6 +51,7 @@ struct DeviceState {
   hipGraphExec_t graph = nullptr;
   std::vector<intptr_t> graph_key;
   bool cnt_ready = false;  // the workspace's key-split counters are zero
+  int64_t doc_uploaded = -1;  // plan doc_version whose document table the workspace holds
   int cus = 0;             // compute units of the device
   // work counters (CP_ATTN_OPT_COUNTERS): key tiles computed per (rank, step)
   unsigned long long* tile_cnt = nullptr;
@@ -73,8 +74,8 @@ int fail(int code, const std::string& msg) {
   } while (0)
 
 struct WsLayout {
-  int64_t slot_k[2], slot_v[2], acc_o, acc_lse, part_o[2], part_lse[2], split_cnt, total;
-  int64_t kv_bytes, o_bytes, lse_bytes, cnt_bytes;
+  int64_t slot_k[2], slot_v[2], acc_o, acc_lse, part_o[2], part_lse[2], split_cnt, doc, total;
+  int64_t kv_bytes, o_bytes, lse_bytes, cnt_bytes, doc_bytes;
 };
 
 // row tiles of the key-split kernel (256 rows) over a step's two segments,
@@ -106,6 +107,8 @@ WsLayout ws_layout(const Plan& p) {
   }
   w.cnt_bytes = split_counters(p) * 4;
   w.split_cnt = take(w.cnt_bytes);
+  w.doc_bytes = p.seq_len * 8;  // document table: [start, end) per position, int32
+  w.doc = take(w.doc_bytes);
   w.total = off;
   return w;
 }
@@ -152,6 +155,7 @@ int ensure_device(Plan& p) {
     d.ws_bytes = w.total;
     d.own_ws = true;
     d.cnt_ready = false;
+    d.doc_uploaded = -1;
   }
   if (!d.cnt_ready) {
     // once per workspace: the key-split counters start at zero (the kernel
@@ -159,6 +163,21 @@ int ensure_device(Plan& p) {
     CPA_HIP(hipMemset(static_cast<char*>(d.ws) + w.split_cnt, 0, size_t(w.cnt_bytes)));
     CPA_HIP(hipDeviceSynchronize());
     d.cnt_ready = true;
+  }
+  if (!p.doc_starts.empty() && d.doc_uploaded != p.doc_version) {
+    // the document table of the current list: once per list and workspace,
+    // synchronously (kernels still queued may read the old table)
+    std::vector<int32_t> tab(size_t(p.seq_len) * 2);
+    for (size_t dd = 0; dd < p.doc_starts.size(); ++dd) {
+      const int64_t b = p.doc_starts[dd], e = dd + 1 < p.doc_starts.size() ? p.doc_starts[dd + 1] : p.seq_len;
+      for (int64_t i = b; i < e; ++i) {
+        tab[size_t(i) * 2] = int32_t(b);
+        tab[size_t(i) * 2 + 1] = int32_t(e);
+      }
+    }
+    CPA_HIP(hipDeviceSynchronize());
+    CPA_HIP(hipMemcpy(static_cast<char*>(d.ws) + w.doc, tab.data(), size_t(w.doc_bytes), hipMemcpyHostToDevice));
+    d.doc_uploaded = p.doc_version;
   }
   if (!d.cus) CPA_HIP(hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev));
   if (p.opt_counters && !d.tile_cnt)
@@ -225,6 +244,22 @@ bool kernel_recv(const Plan& p, int s) {
 }
 bool side_recv(const Plan& p, int s) { return s + 1 < p.cp && !kernel_recv(p, s); }
 
+// Document masks of a launch whose keys are source j's local buffer (j < 0:
+// the identity map, keys at their own positions).
+void set_doc(const Plan& p, StepArgs& a, int j) {
+  if (p.doc_starts.empty()) return;
+  a.doc = reinterpret_cast<const int32_t*>(static_cast<const char*>(p.dev->ws) + ws_layout(p).doc);
+  if (j < 0) {
+    a.kpos_lo = 0;
+    a.kpos_hi = 0;
+    a.kpos_split = a.n_loc;
+  } else {
+    a.kpos_lo = int32_t(p.chunk_of(j, 0) * p.chunk);
+    a.kpos_hi = p.layout == 1 ? int32_t(p.chunk_of(j, 1) * p.chunk) : 0;
+    a.kpos_split = int32_t(p.layout == 1 ? p.chunk : p.n_loc);
+  }
+}
+
 // Step 0 reads the rank's own K/V in place (the rank holds them; nothing is
 // received); later steps read receive slot b.
 int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out, float* lse, int r, int s, int b,
@@ -279,7 +314,8 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
   // keys (the partial buffers of the separate merge mode hold the parts).
   int64_t wgs = 0;
   for (int i = 0; i < sd.nseg; ++i) wgs += (sd.seg[i].q_len + bm - 1) / bm * p.heads;
-  const bool key_split = p.opt_ksplit && !separate && attn_splits_keys(bf16, p.head_dim) && 2 * wgs <= d.cus;
+  const bool key_split = p.opt_ksplit && !separate && p.doc_starts.empty() && attn_splits_keys(bf16, p.head_dim) &&
+                         2 * wgs <= d.cus;
   for (int b = 0; b < 2; ++b) {
     a.split_o[b] = reinterpret_cast<float*>(ws + w.part_o[b]);
     a.split_lse[b] = reinterpret_cast<float*>(ws + w.part_lse[b]);
@@ -308,6 +344,7 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
   if (sd.nseg == 1) a.seg[1] = SegArgs{};
   if (kernel_recv(p, s)) a.recv = recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1);
   if (p.opt_counters) a.tile_cnt = d.tile_cnt + size_t(r) * p.cp + s;
+  set_doc(p, a, sd.src);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
   return CP_ATTN_OK;
@@ -491,7 +528,7 @@ int run_graph(Plan& p, const void* q, const void* k, const void* v, void* out, f
   const std::vector<intptr_t> key = {
       intptr_t(q), intptr_t(k), intptr_t(v), intptr_t(out), intptr_t(lse), rank,
       intptr_t(d.ws), intptr_t(d.copy), intptr_t(d.merge), p.dtype, p.opt_merge, p.opt_serialize,
-      p.opt_recv, p.opt_poison, p.opt_recv_blocks, p.opt_ksplit, p.opt_counters};
+      p.opt_recv, p.opt_poison, p.opt_recv_blocks, p.opt_ksplit, p.opt_counters, intptr_t(p.doc_version)};
   if (!d.graph || key != d.graph_key) {
     drop_graph(d);
     if (!d.capture) CPA_HIP(hipStreamCreateWithFlags(&d.capture, hipStreamNonBlocking));
@@ -754,7 +791,20 @@ int cp_attn_set_workspace(cp_attn_plan_t h, void* ptr, int64_t bytes) {
   d.ws_bytes = ptr ? bytes : 0;
   d.own_ws = false;
   d.cnt_ready = false;
+  d.doc_uploaded = -1;
   return CP_ATTN_OK;
+}
+
+int cp_attn_set_documents(cp_attn_plan_t h, const int64_t* starts, int64_t count) {
+  CPA_GUARD_BEGIN
+  CPA_TRY(check_plan(h));
+  Plan& p = *h->p;
+  std::string err;
+  const int rc = set_documents(p, starts, count, &err);
+  if (rc != CP_ATTN_OK) return fail(rc, err);
+  drop_graph(*p.dev);
+  return CP_ATTN_OK;
+  CPA_GUARD_END
 }
 
 int cp_attn_set_streams(cp_attn_plan_t h, void* copy_stream, void* merge_stream) {
@@ -834,6 +884,7 @@ int cp_attn_allgather_forward(cp_attn_plan_t h, const void* q, const void* k, co
     a.total_tiles += x.tiles;
   }
   if (a.nseg == 0) return CP_ATTN_OK;  // a rank of pad only
+  set_doc(p, a, -1);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
@@ -910,6 +961,7 @@ int cp_attn_ulysses_forward(cp_attn_plan_t h, const void* q, const void* k, cons
   x.tiles = int32_t((p.seq_len + bm - 1) / bm);
   x.epi = kEpiInit | kEpiFinal;
   a.total_tiles = x.tiles;
+  set_doc(p, a, -1);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
@@ -936,6 +988,7 @@ int cp_attn_rank_backward(cp_attn_plan_t h, const void* q, const void* k, const 
                           void* stream) {
   CPA_GUARD_BEGIN
   CPA_TRY(check_plan(h));
+  if (!h->p->doc_starts.empty()) return fail(CP_ATTN_EUNSUPPORTED, "backward with document masks");
   Plan& p = *h->p;
   if (rank < 0 || rank >= p.cp) return fail(CP_ATTN_EINVAL, "rank outside [0, cp_size)");
   CPA_TRY(check_io(q, k, v, out, lse));
@@ -949,6 +1002,7 @@ int cp_attn_full_backward(cp_attn_plan_t h, const void* q, const void* k, const 
                           const float* lse, const void* dout, float* dq, float* dk, float* dv, void* stream) {
   CPA_GUARD_BEGIN
   CPA_TRY(check_plan(h));
+  if (!h->p->doc_starts.empty()) return fail(CP_ATTN_EUNSUPPORTED, "backward with document masks");
   Plan& p = *h->p;
   CPA_TRY(check_io(q, k, v, out, lse));
   CPA_TRY(check_bwd_io(dout, dq, dk, dv));

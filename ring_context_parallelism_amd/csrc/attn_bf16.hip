@@ -128,16 +128,35 @@ void attn_step_bf16(StepArgs a) {
   const bool ok = row < g.q_len;
 
   const int tile_last = min(row0 + kBM, g.q_len);
-  const int kv_end = g.kv_full + (g.diag ? tile_last : 0);
+  int kv_end = g.kv_full + (g.diag ? tile_last : 0);
   const int w_first = row0 + wv * 32;
   const int w_last = min(w_first + 32, g.q_len);
   const bool w_active = w_last > w_first;
-  const int w_max = w_active ? g.kv_full + (g.diag ? w_last : 0) : 0;      // longest prefix in the wave
-  const int w_min = g.kv_full + (g.diag ? w_first + 1 : 0);                // shortest prefix in the wave
-  const int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : w_max;
+  int w_max = w_active ? g.kv_full + (g.diag ? w_last : 0) : 0;      // longest prefix in the wave
+  int w_min = g.kv_full + (g.diag ? w_first + 1 : 0);                // shortest prefix in the wave
+  int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : w_max;
 
   const int64_t hd = int64_t(a.heads) * D;
   const int64_t grow = g.q_global + row;
+  // document masks (as in the head_dim 128 kernel below): this row's first
+  // key, the wave's smallest and largest first key, the workgroup's first key
+  const bool doc = a.doc != nullptr;
+  int klo = 0, w_lo = 0, w_lo_last = 0, wg_lo = 0;
+  if (doc) {
+    int lo, hi;
+    doc_row_keys(a, g.q_global + min(row, g.q_len - 1), lo, hi);
+    klo = lo;
+    prefix = min(prefix, hi);
+    doc_row_keys(a, g.q_global + row0, wg_lo, hi);
+    doc_row_keys(a, g.q_global + tile_last - 1, lo, hi);
+    kv_end = min(kv_end, hi);
+    if (w_active) {
+      doc_row_keys(a, g.q_global + w_first, w_lo, hi);
+      w_min = min(w_min, hi);
+      doc_row_keys(a, g.q_global + w_last - 1, w_lo_last, hi);
+      w_max = min(w_max, hi);
+    }
+  }
 
   // Q^T operand: lane holds Q[row][16 t + 8 hf + 0..7].
   bf16x8 qf[NT];
@@ -211,18 +230,19 @@ void attn_step_bf16(StepArgs a) {
   // Double-buffered LDS: tile it is read from buffer it&1 while tile it+1 is
   // written to the other buffer and tile it+2 is in flight in registers; one
   // barrier per tile.
-  const int ntiles = (kv_end + kBN - 1) / kBN;
+  const int kb0 = (doc ? wg_lo / kBN : 0) * kBN;  // first key tile of the workgroup
+  const int ntiles = max(0, (kv_end + kBN - 1) / kBN - kb0 / kBN);
   if (ntiles > 0) {
-    load_tile(0);
+    load_tile(kb0);
     store_tile(0);
   }
-  if (ntiles > 1) load_tile(kBN);
+  if (ntiles > 1) load_tile(kb0 + kBN);
   __syncthreads();
   int done = 0;  // key tiles this wave scored (work counter)
   for (int it = 0; it < ntiles; ++it) {
-    const int j0 = it * kBN;
+    const int j0 = kb0 + it * kBN;
     const int buf = it & 1;
-    if (j0 < w_max) {
+    if (j0 < w_max && (!doc || j0 + kBN > w_lo)) {
       ++done;
       const uint16_t* skb = sk[buf];
       const uint16_t* svb = sv[buf];
@@ -237,13 +257,13 @@ void attn_step_bf16(StepArgs a) {
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i], s[kb], 0, 0, 0);
         }
       }
-      if (j0 + kBN > w_min) {
+      if (j0 + kBN > w_min || (doc && j0 < w_lo_last)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (key >= prefix) s[kb][i] = -INFINITY;
+            if (key >= prefix || (doc && key < klo)) s[kb][i] = -INFINITY;
           }
         }
       }
@@ -290,7 +310,7 @@ void attn_step_bf16(StepArgs a) {
     }
     if (it + 1 < ntiles) {
       store_tile(buf ^ 1);
-      if (it + 2 < ntiles) load_tile((it + 2) * kBN);
+      if (it + 2 < ntiles) load_tile(kb0 + (it + 2) * kBN);
     }
     __syncthreads();
   }
@@ -301,7 +321,7 @@ void attn_step_bf16(StepArgs a) {
   if (!ok) return;
   const int lrow = g.q_start + row;
   const float lse_s = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;  // a row that saw no key (document masks): O_s = 0, lse_s = -inf
   float4 c[NB][4];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -409,12 +429,20 @@ __device__ __forceinline__ uint32_t lds_addr(const __attribute__((address_space(
 // place; the tile loads past the last tile repeat the last tile), so the
 // end-of-tile wait for tile j + 1 is a fixed count of younger loads,
 // vmcnt(5), and a copy access has two tiles to complete.
+//
+// Document masks (kDoc): a row sees only the run of the source's keys that
+// holds its own document, [klo, khi), clipped to its prefix.  The rows of a
+// segment are consecutive positions, so klo and khi grow with the row: a
+// run of rows takes its first key from its first row and its last from its
+// last row.  The workgroup starts at the 64-key tile of its first row's klo,
+// a wave skips the tiles below its first row's klo, and tiles that reach
+// below its last row's klo are masked.
 // ---------------------------------------------------------------------------
 
 constexpr int kThreads8 = 512;
 constexpr int kBM8 = 256;
 
-template <bool kRecv>
+template <bool kRecv, bool kDoc>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8), amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16_d128x8(StepArgs a) {
   constexpr int D = 128, NT = 8, NB = 4;
@@ -449,14 +477,34 @@ void attn_step_bf16_d128x8(StepArgs a) {
   const int row = row0 + wv * 32 + qc;
   const bool ok = row < g.q_len;
   const int tile_last = min(row0 + kBM8, g.q_len);
-  const int kv_end = g.kv_full + (g.diag ? tile_last : 0);
+  int kv_end = g.kv_full + (g.diag ? tile_last : 0);
   const int w_first = row0 + wv * 32;
   const int w_last = min(w_first + 32, g.q_len);
-  const int w_max = w_last > w_first ? g.kv_full + (g.diag ? w_last : 0) : 0;
-  const int w_min = g.kv_full + (g.diag ? w_first + 1 : 0);
-  const int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : w_max;
+  int w_max = w_last > w_first ? g.kv_full + (g.diag ? w_last : 0) : 0;
+  int w_min = g.kv_full + (g.diag ? w_first + 1 : 0);
+  int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : w_max;
   const int64_t hd = int64_t(a.heads) * D;
   const int64_t grow = g.q_global + row;
+  // document masks: this row's first key, the wave's smallest and largest
+  // first key, the workgroup's first key
+  int klo = 0, w_lo = 0, w_lo_last = 0, wg_lo = 0;
+  if constexpr (kDoc) {
+    int lo, hi;
+    doc_row_keys(a, g.q_global + min(row, g.q_len - 1), lo, hi);
+    klo = lo;
+    prefix = min(prefix, hi);
+    doc_row_keys(a, g.q_global + row0, wg_lo, hi);
+    doc_row_keys(a, g.q_global + tile_last - 1, lo, hi);
+    kv_end = min(kv_end, hi);
+    if (w_last > w_first) {
+      doc_row_keys(a, g.q_global + w_first, w_lo, hi);
+      w_min = min(w_min, hi);
+      doc_row_keys(a, g.q_global + w_last - 1, w_lo_last, hi);
+      w_max = min(w_max, hi);
+    }
+  }
+  // whether the wave computes the key tile at j0
+  auto live = [&](int j0) { return j0 < w_max && (!kDoc || j0 + kBN > w_lo); };
 
   bf16x8 qf[NT];
   {
@@ -536,13 +584,13 @@ void attn_step_bf16_d128x8(StepArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then 16 MFMAs
   };
   auto softmax = [&](f32x16 (&s)[2], int j0, bf16x8 (&pb)[2][2]) {
-    if (j0 + kBN > w_min) {
+    if (j0 + kBN > w_min || (kDoc && j0 < w_lo_last)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if (key >= prefix) s[kb][i] = -INFINITY;
+          if (key >= prefix || (kDoc && key < klo)) s[kb][i] = -INFINITY;
         }
     }
     float lk[2];  // two partial row sums: half the dependent adds
@@ -639,10 +687,11 @@ void attn_step_bf16_d128x8(StepArgs a) {
   g_u32x4* const cdst = (g_u32x4*)(rr == 0 ? a.recv.dst[0] : rr == 1 ? a.recv.dst[1] : rr == 2 ? a.recv.dst[2] : a.recv.dst[3]);
   const u32x4 desc_c = buffer_desc(csrc_p, uint32_t(rn * 16));
   // this workgroup's key tiles: jt0 .. jt0 + ntiles - 1 (key kb0 onwards)
+  // (document masks: from the tile of the workgroup's first key, never split)
   const int ntiles_all = (kv_end + kBN - 1) / kBN;
   const int half_tiles = (ntiles_all + 1) >> 1;
-  const int jt0 = part ? half_tiles : 0;
-  const int ntiles = ks == 1 ? ntiles_all : (part ? ntiles_all - half_tiles : half_tiles);
+  const int jt0 = kDoc ? wg_lo / kBN : part ? half_tiles : 0;
+  const int ntiles = kDoc ? max(0, ntiles_all - jt0) : ks == 1 ? ntiles_all : (part ? ntiles_all - half_tiles : half_tiles);
   const int kb0 = jt0 * kBN;
   // slots of the share: ntiles + 2, at most 512 vectors (one per lane) each;
   // what does not fit is copied after the loop
@@ -720,8 +769,8 @@ void attn_step_bf16_d128x8(StepArgs a) {
   // scores of tile J into s_
 #define CPATTN_X8_GEMMS(J, S, s_, pb_)                                                     \
   do {                                                                                     \
-    const bool sc_ = kb0 + (J) * kBN < w_max;                                              \
-    const bool pv_ = (J) > 0 && kb0 + ((J) - 1) * kBN < w_max;                             \
+    const bool sc_ = live(kb0 + (J) * kBN);                                                \
+    const bool pv_ = (J) > 0 && live(kb0 + ((J) - 1) * kBN);                               \
     if (pv_) pv(vst(((S) + 3) & 3), pb_);                                                  \
     if (sc_) scores(kst(S), s_);                                                           \
   } while (0)
@@ -740,22 +789,22 @@ void attn_step_bf16_d128x8(StepArgs a) {
     for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
       CPATTN_X8_COPY(j, cb);
       CPATTN_X8_GEMMS(j, st, s_, pb_);
-      if (kb0 + j * kBN < w_max) softmax(s_, kb0 + j * kBN, pb_);
+      if (live(kb0 + j * kBN)) softmax(s_, kb0 + j * kBN, pb_);
       issue(desc_k, kb0 + min(j + 2, ntiles - 1) * kBN, kst((st + 2) & 3));
       CPATTN_X8_END();
     }
     // product of the last tile (its stage is not overwritten: the loads
     // issued at the last two tiles went to other stages)
-    if (ntiles > 0 && kb0 + (ntiles - 1) * kBN < w_max) pv(vst((ntiles - 1) & 3), pb_);
+    if (ntiles > 0 && live(kb0 + (ntiles - 1) * kBN)) pv(vst((ntiles - 1) & 3), pb_);
   } else {
     for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
       CPATTN_X8_COPY(j, cb);
-      if (j > 0 && kb0 + (j - 1) * kBN < w_max) softmax(s_, kb0 + (j - 1) * kBN, pb_);
+      if (j > 0 && live(kb0 + (j - 1) * kBN)) softmax(s_, kb0 + (j - 1) * kBN, pb_);
       issue(desc_v, kb0 + min(j + 2, ntiles - 1) * kBN, vst((st + 2) & 3));
       CPATTN_X8_GEMMS(j, st, s_, pb_);
       CPATTN_X8_END();
     }
-    if (ntiles > 0 && kb0 + (ntiles - 1) * kBN < w_max) {
+    if (ntiles > 0 && live(kb0 + (ntiles - 1) * kBN)) {
       softmax(s_, kb0 + (ntiles - 1) * kBN, pb_);
       pv(vst((ntiles - 1) & 3), pb_);
     }
@@ -765,10 +814,12 @@ void attn_step_bf16_d128x8(StepArgs a) {
 #undef CPATTN_X8_COPY
 
   if (a.tile_cnt && lane == 0) {
-    // work counter: the tiles whose scores the loops computed (their condition,
-    // kb0 + j kBN < w_max, over j < ntiles); kept out of the loop, where a
-    // counter would cost registers the receive kernel beside this one needs
-    const int done = min(ntiles, max(0, (w_max - kb0 + kBN - 1) / kBN));
+    // work counter: the tiles whose scores the loops computed (their
+    // condition, live(kb0 + j kBN), over j < ntiles); kept out of the loop,
+    // where a counter would cost registers the receive kernel beside this one
+    // needs.  kb0 <= w_lo for a wave with rows under document masks.
+    const int skipped = kDoc ? max(0, w_lo - kb0) / kBN : 0;
+    const int done = max(0, min(ntiles, max(0, (w_max - kb0 + kBN - 1) / kBN)) - skipped);
     __hip_atomic_fetch_add(a.tile_cnt, (unsigned long long)done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   wait_vmem();
@@ -795,7 +846,8 @@ void attn_step_bf16_d128x8(StepArgs a) {
   l += __shfl_xor(l, 32);
   const int lrow_out = g.q_start + row;
   float lse_s = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
-  float inv = 1.f / l;
+  // a row that saw no key (document masks) leaves O_s = 0 and lse_s = -inf
+  float inv = kDoc ? (l > 0.f ? 1.f / l : 0.f) : 1.f / l;
   if (ks > 1) {
     // Key split: the part that finishes first leaves its normalised output
     // and LSE in split buffer [part] and exits; the second reads them, folds
@@ -917,10 +969,16 @@ bool attn_splits_keys(int dtype_bf16, int head_dim) { return dtype_bf16 && head_
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid(unsigned(a.total_tiles) * unsigned(a.heads));
   if (head_dim == 128) {
-    if (a.recv.n > 0)
-      attn_step_bf16_d128x8<true><<<grid, kThreads8, 0, stream>>>(a);
-    else
-      attn_step_bf16_d128x8<false><<<grid, kThreads8, 0, stream>>>(a);
+    if (a.doc) {
+      if (a.recv.n > 0)
+        attn_step_bf16_d128x8<true, true><<<grid, kThreads8, 0, stream>>>(a);
+      else
+        attn_step_bf16_d128x8<false, true><<<grid, kThreads8, 0, stream>>>(a);
+    } else if (a.recv.n > 0) {
+      attn_step_bf16_d128x8<true, false><<<grid, kThreads8, 0, stream>>>(a);
+    } else {
+      attn_step_bf16_d128x8<false, false><<<grid, kThreads8, 0, stream>>>(a);
+    }
   } else {
     attn_step_bf16<64><<<grid, kThreads, 0, stream>>>(a);
   }

@@ -44,9 +44,23 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
   const int rl = tid / kTPR, sub = tid % kTPR;
   const int row = row0 + rl;  // row within the segment
   const bool ok = row < g.q_len;
-  const int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : 0;
+  int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : 0;
   const int last = min(row0 + kBM, g.q_len);
-  const int kv_end = g.kv_full + (g.diag ? last : 0);
+  int kv_end = g.kv_full + (g.diag ? last : 0);
+  // document masks: a row sees only its document's run of the source's keys,
+  // [klo, khi); the rows are consecutive positions, so the workgroup's keys
+  // run from its first row's klo to its last row's khi
+  int klo = 0, kb0 = 0;
+  if (a.doc) {
+    int lo, hi;
+    doc_row_keys(a, g.q_global + min(row, g.q_len - 1), lo, hi);
+    klo = lo;
+    prefix = min(prefix, hi);
+    doc_row_keys(a, g.q_global + row0, lo, hi);
+    kb0 = lo / kBN * kBN;
+    doc_row_keys(a, g.q_global + last - 1, lo, hi);
+    kv_end = min(kv_end, hi);
+  }
 
   const float* q = static_cast<const float*>(a.q);
   const float* kp = static_cast<const float*>(a.k);
@@ -61,11 +75,11 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
     o[i] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  if (a.tile_cnt && tid == 0)  // work counter: the workgroup computes every key tile below kv_end
-    __hip_atomic_fetch_add(a.tile_cnt, (unsigned long long)((kv_end + kBN - 1) / kBN), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  if (a.tile_cnt && tid == 0)  // work counter: the workgroup computes every key tile from kb0 below kv_end
+    __hip_atomic_fetch_add(a.tile_cnt, (unsigned long long)max(0, (kv_end + kBN - 1) / kBN - kb0 / kBN),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  for (int j0 = 0; j0 < kv_end; j0 += kBN) {
+  for (int j0 = kb0; j0 < kv_end; j0 += kBN) {
     __syncthreads();
     for (int e = tid; e < kBN * D; e += kThreads) {
       const int kr = e / D, dc = e % D;
@@ -90,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
       for (int i = 0; i < DS; ++i) part = fmaf(qv[i], sk[kk * LS + sub * DS + i], part);
       part += __shfl_xor(part, 1);
       part += __shfl_xor(part, 2);
-      sc[kk] = (j0 + kk < prefix) ? part * a.scale : -INFINITY;
+      sc[kk] = (j0 + kk < prefix && j0 + kk >= klo) ? part * a.scale : -INFINITY;
       mt = fmaxf(mt, sc[kk]);
     }
     const float mn = fmaxf(m, mt);
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
   if (!ok) return;
   const int lrow = g.q_start + row;
   const float lse_s = m + logf(l);
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;  // a row that saw no key (document masks): O_s = 0, lse_s = -inf
   float4 c[DS / 4];
 #pragma unroll
   for (int i = 0; i < DS; i += 4) c[i / 4] = row_epi_load4(a, epi, h, lrow, sub * DS + i, D);

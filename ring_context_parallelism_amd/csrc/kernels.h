@@ -76,6 +76,14 @@ struct StepArgs {
   // work counter (null: off): the kernel adds the key tiles it computed, per
   // wave of 32 rows x 64 keys (bf16 kernels) or per workgroup tile (fp32)
   unsigned long long* tile_cnt;
+  // document masks (null: none): doc[2 p], doc[2 p + 1] = [start, end) of the
+  // document holding global position p.  Local key kk of the source sits at
+  // global position kpos_lo + kk below kpos_split, kpos_hi + kk - kpos_split
+  // from there on; a row sees only the keys of its own document.
+  const int32_t* doc;
+  int32_t kpos_lo;
+  int32_t kpos_hi;
+  int32_t kpos_split;
 };
 
 // Backward of one ring step (attn_bwd.hip, attn_bwd_bf16.hip).  Q, dO, O are

@@ -20,6 +20,13 @@
 // In every case a local row's valid keys form a prefix of the source's local
 // buffer, which is what a Segment records.
 //
+// Document masks ("Context Parallelism for Long-Context Training", section
+// "Prove attention equivalence": causal and document masks) leave the
+// descriptors as they are: a document is a run of positions and a source's
+// local keys are in increasing position order, so the keys of a row's
+// document are one run of the source's local buffer, [keys_before(start),
+// keys_before(end)); a row sees that run clipped to its prefix.
+//
 // Awkward lengths ("Context Parallelism for Long-Context Training", section
 // "Test sequence divisibility and padding": pad ownership, masked pad keys and
 // queries, local offsets).  A length that does not divide into the chunks is
@@ -57,6 +64,39 @@ int64_t Plan::valid_in_chunk(int64_t c) const { return std::min(chunk, std::max<
 int64_t Plan::valid_rows(int r) const {
   if (layout == 0) return valid_in_chunk(r);
   return valid_in_chunk(chunk_of(r, 0)) + valid_in_chunk(chunk_of(r, 1));
+}
+
+void Plan::doc_range(int64_t pos, int64_t* start, int64_t* end) const {
+  if (doc_starts.empty()) {
+    *start = 0;
+    *end = seq_len;
+    return;
+  }
+  const auto it = std::upper_bound(doc_starts.begin(), doc_starts.end(), pos);  // first start after pos
+  *start = *(it - 1);
+  *end = it == doc_starts.end() ? seq_len : *it;
+}
+
+int64_t Plan::keys_before(int j, int64_t pos) const {
+  auto run = [&](int64_t first, int64_t len) { return std::min(len, std::max<int64_t>(0, pos - first)); };
+  if (layout == 0) return run(int64_t(j) * chunk, chunk);
+  return run(chunk_of(j, 0) * chunk, chunk) + run(chunk_of(j, 1) * chunk, chunk);
+}
+
+int set_documents(Plan& p, const int64_t* starts, int64_t count, std::string* err) {
+  if (count < 0 || (count > 0 && !starts)) {
+    *err = "documents: count < 0, or starts is null";
+    return kInval;
+  }
+  for (int64_t d = 0; d < count; ++d) {
+    if ((d == 0 && starts[0] != 0) || (d > 0 && starts[d] <= starts[d - 1]) || starts[d] >= p.seq_len) {
+      *err = "documents: starts must increase strictly from 0 and stay below seq_len";
+      return kInval;
+    }
+  }
+  p.doc_starts.assign(starts, starts + count);
+  ++p.doc_version;
+  return kOk;
 }
 
 static void build_steps(Plan& p) {
@@ -178,9 +218,30 @@ int make_plan(int64_t seq_len, int cp, int heads, int head_dim, int causal, int 
   return kOk;
 }
 
+namespace {
+// Local key run [lo, hi) that segment row t sees in step (r, s) under the
+// document mask: its prefix clipped to its document's run of the source.
+void row_keys(const Plan& p, const StepDesc& d, const Segment& g, int64_t t, int64_t* lo, int64_t* hi) {
+  int64_t ds = 0, de = 0;
+  p.doc_range(g.q_global + t, &ds, &de);
+  *lo = p.keys_before(d.src, ds);
+  *hi = std::min(g.kv_full + (g.diag ? t + 1 : 0), p.keys_before(d.src, de));
+}
+}  // namespace
+
 int64_t step_pairs(const Plan& p, int r, int s) {
   const StepDesc& d = p.step(r, s);
   int64_t n = 0;
+  if (!p.doc_starts.empty()) {
+    for (int i = 0; i < d.nseg; ++i) {
+      for (int64_t t = 0; t < d.seg[i].q_len; ++t) {
+        int64_t lo = 0, hi = 0;
+        row_keys(p, d, d.seg[i], t, &lo, &hi);
+        n += std::max<int64_t>(0, hi - lo);
+      }
+    }
+    return n;
+  }
   for (int i = 0; i < d.nseg; ++i) {
     const Segment& g = d.seg[i];
     n += g.q_len * g.kv_full;
@@ -192,6 +253,32 @@ int64_t step_pairs(const Plan& p, int r, int s) {
 int64_t step_tiles(const Plan& p, int r, int s, int bm, int bn) {
   const StepDesc& d = p.step(r, s);
   int64_t tiles = 0;
+  if (!p.doc_starts.empty()) {
+    // per row tile, the key tiles that some row's run reaches (a difference
+    // array over key tiles)
+    const int64_t nk = (p.n_loc + bn - 1) / bn;
+    std::vector<int64_t> cover(size_t(nk) + 1);
+    for (int64_t i0 = 0; i0 < p.n_loc; i0 += bm) {
+      std::fill(cover.begin(), cover.end(), 0);
+      const int64_t i1 = std::min<int64_t>(p.n_loc, i0 + bm);
+      for (int k = 0; k < d.nseg; ++k) {
+        const Segment& g = d.seg[k];
+        for (int64_t i = std::max(i0, g.q_start); i < std::min(i1, g.q_start + g.q_len); ++i) {
+          int64_t lo = 0, hi = 0;
+          row_keys(p, d, g, i - g.q_start, &lo, &hi);
+          if (hi <= lo) continue;
+          ++cover[size_t(lo / bn)];
+          --cover[size_t((hi + bn - 1) / bn)];
+        }
+      }
+      int64_t run = 0;
+      for (int64_t kt = 0; kt < nk; ++kt) {
+        run += cover[size_t(kt)];
+        tiles += run > 0;
+      }
+    }
+    return tiles;
+  }
   for (int64_t i0 = 0; i0 < p.n_loc; i0 += bm) {
     const int64_t i1 = std::min<int64_t>(p.n_loc, i0 + bm);
     int64_t maxpre = 0;  // longest valid key prefix among the tile's rows

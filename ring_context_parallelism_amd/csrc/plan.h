@@ -40,6 +40,10 @@ struct Plan {
   int64_t chunk = 0;   // padded_len/(2cp) zigzag, padded_len/cp contiguous
   int64_t n_loc = 0;   // rows of a rank's local buffer (pad rows included)
   std::vector<StepDesc> steps;  // [rank * cp + step]
+  // document masks: document d holds positions [doc_starts[d], doc_starts[d+1])
+  // (the last runs to seq_len); empty = one document (no document mask)
+  std::vector<int64_t> doc_starts;
+  int64_t doc_version = 0;  // bumped by every change of doc_starts
 
   // options
   int32_t opt_merge = 0;
@@ -63,11 +67,20 @@ struct Plan {
   int64_t valid_in_chunk(int64_t c) const;
   // real rows of rank r's local buffer; they are its first valid_rows(r) rows
   int64_t valid_rows(int r) const;
+  // [start, end) of the document holding global position pos (the whole
+  // sequence when no documents are set)
+  void doc_range(int64_t pos, int64_t* start, int64_t* end) const;
+  // local keys of source j whose global position is below pos
+  int64_t keys_before(int j, int64_t pos) const;
 };
 
 // Returns a status code; on success *out is a new plan.
 int make_plan(int64_t seq_len, int cp, int heads, int head_dim, int causal, int layout, Plan** out,
               std::string* err);
+
+// Checks and stores a document list (strictly increasing, first 0, all below
+// seq_len; count 0 clears it).
+int set_documents(Plan& p, const int64_t* starts, int64_t count, std::string* err);
 
 int64_t step_pairs(const Plan& p, int r, int s);
 int64_t step_tiles(const Plan& p, int r, int s, int bm, int bn);

@@ -80,3 +80,18 @@ def sha256_of(*tensors):
 def to_numpy_f64(t):
     """Exact fp64 copy of a CPU fp32/bf16 tensor (both embed exactly in fp64)."""
     return t.to(torch.float64).numpy()
+
+
+def make_documents(seq_len, mean_len, seed):
+    """Seeded document starts for document masks: lengths i.i.d. uniform on
+    ``[1, 2 mean_len - 1]`` (a mix of short and long documents, mean about
+    ``mean_len``), laid end to end from position 0; the last document is cut
+    at ``seq_len``.  Returns a sorted list whose first entry is 0."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    starts, pos = [], 0
+    hi = max(1, 2 * int(mean_len) - 1)
+    while pos < seq_len:
+        starts.append(pos)
+        pos += int(torch.randint(1, hi + 1, (1,), generator=g))
+    return starts

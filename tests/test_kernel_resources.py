@@ -46,7 +46,7 @@ def resources():
 
 
 def test_step_kernel_leaves_room_for_the_receive_kernel(resources):
-    plain = [v for k, v in resources.items() if "attn_step_bf16_d128x8ILb0E" in k]
+    plain = [v for k, v in resources.items() if "attn_step_bf16_d128x8ILb0ELb0E" in k]
     assert len(plain) == 1, sorted(resources)
     assert plain[0]["vgpr"] <= 240, plain[0]
 
