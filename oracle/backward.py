@@ -23,6 +23,11 @@ with ``P`` and ``D`` taken from the complete forward (its LSE and O), to its
 own ``dQ`` and to the source's ``dK``, ``dV``.  The valid pairs of all steps
 partition those of the whole sequence, so the sums equal the unsplit
 gradients.
+
+Document masks (the same section: "Test causal and document masks") enter
+only through the valid pairs: ``doc_starts`` drops the pairs whose query and
+key lie in different documents, in the forward that gives ``P`` and in the
+pair terms alike.
 """
 
 import numpy as np
@@ -35,13 +40,13 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _pair_terms(q, k, v, dout, o, lse, q_pos, k_pos, causal, scale):
+def _pair_terms(q, k, v, dout, o, lse, q_pos, k_pos, causal, scale, doc_starts=None):
     """dQ, dK, dV contributions of the valid pairs between rows ``q`` and keys ``k``."""
     sq, heads, dim = q.shape
     dq = np.zeros((sq, heads, dim))
     dk = np.zeros((k.shape[0], heads, dim))
     dv = np.zeros((k.shape[0], heads, dim))
-    valid = valid_mask(q_pos, k_pos, causal)
+    valid = valid_mask(q_pos, k_pos, causal, doc_starts=doc_starts)
     for h in range(heads):
         s = scale * (q[:, h] @ k[:, h].T)
         lse_h = np.where(np.isfinite(lse[h]), lse[h], 0.0)[:, None]  # -inf only for rows with no valid key
@@ -55,29 +60,30 @@ def _pair_terms(q, k, v, dout, o, lse, q_pos, k_pos, causal, scale):
     return dq, dk, dv
 
 
-def attention_backward(q, k, v, dout, *, causal, scale=None):
+def attention_backward(q, k, v, dout, *, causal, scale=None, doc_starts=None):
     """Unsplit gradients ``(dQ, dK, dV)`` of natural-order ``[S, H, D]`` inputs."""
     q, k, v, dout = (_f64(x) for x in (q, k, v, dout))
     if scale is None:
         scale = 1.0 / np.sqrt(q.shape[2])
-    o, lse = attention(q, k, v, causal=causal, scale=scale)
+    o, lse = attention(q, k, v, causal=causal, scale=scale, doc_starts=doc_starts)
     pos = np.arange(q.shape[0])
-    return _pair_terms(q, k, v, dout, o, lse, pos, pos, causal, scale)
+    return _pair_terms(q, k, v, dout, o, lse, pos, pos, causal, scale, doc_starts=doc_starts)
 
 
-def query_gradients(q, k, v, dout, rows, *, causal, scale=None):
+def query_gradients(q, k, v, dout, rows, *, causal, scale=None, doc_starts=None):
     """dQ of the natural-order rows ``rows`` only (all keys; cost linear in
     ``len(rows)``): the same terms as ``attention_backward`` for those rows."""
     q, k, v, dout = (_f64(x) for x in (q, k, v, dout))
     if scale is None:
         scale = 1.0 / np.sqrt(q.shape[2])
     rows = np.asarray(rows, dtype=np.int64)
-    o, lse = attention(q[rows], k, v, causal=causal, scale=scale, q_pos=rows)
-    dq, _, _ = _pair_terms(q[rows], k, v, dout[rows], o, lse, rows, np.arange(k.shape[0]), causal, scale)
+    o, lse = attention(q[rows], k, v, causal=causal, scale=scale, q_pos=rows, doc_starts=doc_starts)
+    dq, _, _ = _pair_terms(q[rows], k, v, dout[rows], o, lse, rows, np.arange(k.shape[0]), causal, scale,
+                           doc_starts=doc_starts)
     return dq
 
 
-def rank_backward(q, k, v, dout, cp, rank, *, layout=ZIGZAG, causal=True, scale=None):
+def rank_backward(q, k, v, dout, cp, rank, *, layout=ZIGZAG, causal=True, scale=None, doc_starts=None):
     """One rank's share of the backward, one ring step at a time.
 
     Returns ``(dQ_loc [n, H, D], dK [S, H, D], dV [S, H, D], positions [n])``:
@@ -88,7 +94,7 @@ def rank_backward(q, k, v, dout, cp, rank, *, layout=ZIGZAG, causal=True, scale=
     seq_len, heads, dim = q.shape
     if scale is None:
         scale = 1.0 / np.sqrt(dim)
-    o, lse = attention(q, k, v, causal=causal, scale=scale)  # the complete forward
+    o, lse = attention(q, k, v, causal=causal, scale=scale, doc_starts=doc_starts)  # the complete forward
     qpos = rank_positions(seq_len, cp, rank, layout)
     dq = np.zeros((qpos.size, heads, dim))
     dk = np.zeros((seq_len, heads, dim))
@@ -96,21 +102,22 @@ def rank_backward(q, k, v, dout, cp, rank, *, layout=ZIGZAG, causal=True, scale=
     for s in range(cp):
         kpos = rank_positions(seq_len, cp, ring_source(rank, s, cp), layout)
         a, b, c = _pair_terms(q[qpos], k[kpos], v[kpos], dout[qpos], o[qpos], lse[:, qpos], qpos, kpos, causal,
-                              scale)
+                              scale, doc_starts=doc_starts)
         dq += a
         dk[kpos] += b
         dv[kpos] += c
     return dq, dk, dv, qpos
 
 
-def full_backward(q, k, v, dout, cp, *, layout=ZIGZAG, causal=True, scale=None):
+def full_backward(q, k, v, dout, cp, *, layout=ZIGZAG, causal=True, scale=None, doc_starts=None):
     """Every rank's share; ``(dQ, dK, dV)`` in natural order."""
     q = _f64(q)
     dq = np.zeros(q.shape)
     dk = np.zeros(q.shape)
     dv = np.zeros(q.shape)
     for r in range(cp):
-        a, b, c, pos = rank_backward(q, k, v, dout, cp, r, layout=layout, causal=causal, scale=scale)
+        a, b, c, pos = rank_backward(q, k, v, dout, cp, r, layout=layout, causal=causal, scale=scale,
+                                     doc_starts=doc_starts)
         dq[pos] = a
         dk += b
         dv += c

@@ -112,14 +112,80 @@ def test_rank_share_touches_only_visible_sources():
 
 
 # ----------------------------------------------------------------------------
+# Document masks ("Context Parallelism for Long-Context Training", section
+# "Prove attention equivalence": causal and document masks)
+# ----------------------------------------------------------------------------
+
+DOCS = [0, 1, 9, 10, 23]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_document_gradients_equal_each_document_alone(causal):
+    """With document masks no pair crosses a boundary, so the gradients are
+    those of every document run through the plain (maskless) backward alone."""
+    seq, heads, dim = 31, 2, 4
+    q, k, v, dout = (_rand((seq, heads, dim), 150 + i) for i in range(4))
+    got = oracle.attention_backward(q, k, v, dout, causal=causal, doc_starts=DOCS)
+    bounds = DOCS + [seq]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        ref = oracle.attention_backward(q[a:b], k[a:b], v[a:b], dout[a:b], causal=causal)
+        for g, r in zip(got, ref):
+            assert np.max(np.abs(g[a:b] - r)) <= 1e-13
+
+
+def test_document_gradients_match_central_differences():
+    seq, heads, dim = 7, 1, 2
+    docs = [0, 3, 4]
+    q, k, v, dout = (_rand((seq, heads, dim), 160 + i) for i in range(4))
+    dq, dk, dv = oracle.attention_backward(q, k, v, dout, causal=True, doc_starts=docs)
+
+    def loss():
+        o, _ = oracle.attention(q, k, v, causal=True, doc_starts=docs)
+        return float(np.sum(o * dout))
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            up = loss()
+            x[idx] = keep - eps
+            down = loss()
+            x[idx] = keep
+            num[idx] = (up - down) / (2 * eps)
+        assert np.max(np.abs(num - g)) <= 1e-7
+
+
+@pytest.mark.parametrize("seq,cp,layout,causal", [(64, 2, "zigzag", True), (101, 4, "zigzag", True),
+                                                  (80, 5, "contiguous", False), (21, 8, "zigzag", True)])
+def test_document_ring_decomposition_equals_unsplit(seq, cp, layout, causal):
+    heads, dim = 2, 4
+    docs = sorted({0, 1, 5, seq // 3, seq // 2 + 1, seq - 2})
+    q, k, v, dout = (_rand((seq, heads, dim), 170 + i) for i in range(4))
+    ref = oracle.attention_backward(q, k, v, dout, causal=causal, doc_starts=docs)
+    got = oracle.full_backward(q, k, v, dout, cp, layout=layout, causal=causal, doc_starts=docs)
+    for a, b in zip(got, ref):
+        assert np.max(np.abs(a - b)) <= 1e-12
+    rows = [0, 5, seq - 1]
+    dq = oracle.query_gradients(q, k, v, dout, rows, causal=causal, doc_starts=docs)
+    assert np.max(np.abs(dq - ref[0][rows])) <= 1e-13
+
+
+# ----------------------------------------------------------------------------
 # Planted mistakes
 # ----------------------------------------------------------------------------
+
+def test_planted_documents_ignored_in_the_pair_terms_are_caught(monkeypatch):
+    real = backward_mod._pair_terms
+    monkeypatch.setattr(backward_mod, "_pair_terms", lambda *a, **kw: real(*a))
+    with pytest.raises(AssertionError):
+        test_document_gradients_equal_each_document_alone(True)
 
 def test_planted_missing_delta_term_is_caught(monkeypatch):
     real = backward_mod._pair_terms
 
-    def no_delta(q, k, v, dout, o, lse, *rest):
-        return real(q, k, v, dout, np.zeros_like(o), lse, *rest)
+    def no_delta(q, k, v, dout, o, lse, *rest, **kw):
+        return real(q, k, v, dout, np.zeros_like(o), lse, *rest, **kw)
     monkeypatch.setattr(backward_mod, "_pair_terms", no_delta)
     with pytest.raises(AssertionError):
         test_gradients_match_central_differences(True)
@@ -128,9 +194,9 @@ def test_planted_missing_delta_term_is_caught(monkeypatch):
 def test_planted_unscaled_key_gradient_is_caught(monkeypatch):
     real = backward_mod._pair_terms
 
-    def unscaled(*args):
-        dq, dk, dv = real(*args)
-        return dq, dk / args[-1], dv
+    def unscaled(*args, **kw):
+        dq, dk, dv = real(*args, **kw)
+        return dq, dk / args[9], dv
     monkeypatch.setattr(backward_mod, "_pair_terms", unscaled)
     with pytest.raises(AssertionError):
         test_gradients_match_torch_autograd_fp64(False)
