@@ -296,6 +296,45 @@ def backward_section(plan, w, bufs, stream, reps):
             "parity_dq_sampled_rows": {"rows": sample.tolist(), "max_rel_err": rel, "tol": 2e-2, "ok": rel <= 2e-2}}
 
 
+def documents_section(w, bufs, stream, reps):
+    """Document masks on the timed workload's share (seeded document lengths,
+    uniform on [1, 2 mean - 1]): time per call, TFLOP/s of the valid pairs
+    (same document and causal), and sampled rows against the fp64 oracle."""
+    import oracle
+    import ring_context_parallelism_amd as R
+    from ring_context_parallelism_amd.inputs import make_documents, to_numpy_f64
+    q, k, v, out, lse = bufs
+    rows = oracle.rank_positions(w.seq_len, w.cp, w.rank, w.layout)
+    sample = rows[np.linspace(0, rows.size - 1, 12).astype(np.int64)]
+    qn, kn, vn = (to_numpy_f64(t.cpu()) for t in (q, k, v))
+    res = {}
+    for mean in (8192, 1024):
+        docs = make_documents(w.seq_len, mean, seed=w.seed + mean)
+        p = R.Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout, dtype=w.torch_dtype)
+        p.set_documents(docs)
+        pairs = sum(p.valid_work(w.rank, s, 128, 64)[1] for s in range(w.cp))
+        p.rank_forward(q, k, v, out, lse, w.rank, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            p.rank_forward(q, k, v, out, lse, w.rank, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = 4 * w.head_dim * w.heads * pairs
+        o_ref, l_ref = oracle.attention(qn[sample], kn, vn, causal=w.causal, q_pos=sample, doc_starts=docs)
+        d_o = float(np.max(np.abs(out.cpu()[sample].double().numpy() - o_ref)))
+        d_l = float(np.max(np.abs(lse.cpu()[:, sample].double().numpy() - l_ref)))
+        res[f"mean_doc_len_{mean}"] = {
+            "documents": len(docs), "valid_pairs_per_head": pairs, "ms_per_call": round(ms, 5),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "parity_sampled": {"rows": sample.tolist(), "max_abs_dO": d_o, "max_abs_dLSE": d_l,
+                               "ok": d_o <= 2e-2 and d_l <= 1e-3}}
+        p.close()
+    return res
+
+
 def ulysses_section(plan, w, bufs, stream, reps):
     """Ulysses variant on the timed workload: the all-to-all of Q, K, V to head
     ownership (every rank at once on one GPU), rank 0's attention over all
@@ -474,6 +513,8 @@ def main():
 
     if not args.no_extras:
         result["ulysses"] = ulysses_section(plan, w, bufs, stream, max(3, args.steps // 4))
+        if w.rank is not None and w.causal:
+            result["documents"] = documents_section(w, bufs, stream, max(3, args.steps // 4))
 
     if (args.backward or not args.no_extras) and w.rank is not None:
         plan.set_graph(False)

@@ -166,10 +166,10 @@ int cp_attn_set_streams(cp_attn_plan_t plan, void* copy_stream, void* merge_stre
  * only to keys of its own document, on top of the plan's causal or
  * bidirectional mask.  starts: host array, strictly increasing, starts[0] =
  * 0, every entry below S; the plan keeps a copy.  count = 0 removes the
- * documents.  The forward calls (ring, all-gather, Ulysses) honour them; the
- * backward calls return EUNSUPPORTED while documents are set.  The device
- * table (two int32 per token, in the workspace) is written by the next
- * forward call, which first waits for the device.  A query row that sees no
+ * documents.  Every forward call (ring, all-gather, Ulysses) and the
+ * backward calls honour them.  The device table (two int32 per token, in
+ * the workspace) is written by the next forward or backward call, which
+ * first waits for the device.  A query row that sees no
  * key of a ring step takes nothing from that step; the key split
  * (CP_ATTN_OPT_KSPLIT) is not used while documents are set.
  * EINVAL for an unsorted list, a first start other than 0, a start >= S, a

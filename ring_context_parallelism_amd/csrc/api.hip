@@ -245,8 +245,9 @@ bool kernel_recv(const Plan& p, int s) {
 bool side_recv(const Plan& p, int s) { return s + 1 < p.cp && !kernel_recv(p, s); }
 
 // Document masks of a launch whose keys are source j's local buffer (j < 0:
-// the identity map, keys at their own positions).
-void set_doc(const Plan& p, StepArgs& a, int j) {
+// the identity map, keys at their own positions).  A is StepArgs or BwdArgs.
+template <typename A>
+void set_doc(const Plan& p, A& a, int j) {
   if (p.doc_starts.empty()) return;
   a.doc = reinterpret_cast<const int32_t*>(static_cast<const char*>(p.dev->ws) + ws_layout(p).doc);
   if (j < 0) {
@@ -634,6 +635,7 @@ int run_rank_backward(Plan& p, const void* q, const void* k, const void* v, cons
       maxpre = std::max<int64_t>(maxpre, g.kv_full + (g.diag ? g.q_len : 0));
     }
     a.key_tiles = int32_t((maxpre + bt_keys - 1) / bt_keys);
+    set_doc(p, a, j);
     const hipError_t e = bwd_mfma(bf16, p.head_dim) ? launch_bwd_bf16_d128(a, st)
                                                     : launch_bwd_generic(a, bf16, p.head_dim, st);
     if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("backward launch: ") + hipGetErrorString(e));
@@ -988,7 +990,6 @@ int cp_attn_rank_backward(cp_attn_plan_t h, const void* q, const void* k, const 
                           void* stream) {
   CPA_GUARD_BEGIN
   CPA_TRY(check_plan(h));
-  if (!h->p->doc_starts.empty()) return fail(CP_ATTN_EUNSUPPORTED, "backward with document masks");
   Plan& p = *h->p;
   if (rank < 0 || rank >= p.cp) return fail(CP_ATTN_EINVAL, "rank outside [0, cp_size)");
   CPA_TRY(check_io(q, k, v, out, lse));
@@ -1002,7 +1003,6 @@ int cp_attn_full_backward(cp_attn_plan_t h, const void* q, const void* k, const 
                           const float* lse, const void* dout, float* dq, float* dk, float* dv, void* stream) {
   CPA_GUARD_BEGIN
   CPA_TRY(check_plan(h));
-  if (!h->p->doc_starts.empty()) return fail(CP_ATTN_EUNSUPPORTED, "backward with document masks");
   Plan& p = *h->p;
   CPA_TRY(check_io(q, k, v, out, lse));
   CPA_TRY(check_bwd_io(dout, dq, dk, dv));

@@ -21,7 +21,9 @@
 //   * row-major: a workgroup owns a tile of the rank's rows and walks the
 //     keys they see, accumulating dQ (written at the row run's first step,
 //     added to afterwards).
-// Plus a per-rank kernel for D_i.  This file holds the generic kernels (any
+// Document masks clip every row's keys to its document's run of the source,
+// [klo, khi) (rows of a segment are consecutive positions, so both grow with
+// the row).  Plus a per-rank kernel for D_i.  This file holds the generic kernels (any
 // element type, fp32 arithmetic on the vector ALUs); the bf16 head_dim 128
 // kernels on the matrix cores are in attn_bwd_bf16.hip.
 #include <hip/hip_runtime.h>
@@ -83,6 +85,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_generic(BwdArgs a) {
   __shared__ float sdo[kTile * D];
   __shared__ float slse[kTile];
   __shared__ float sdel[kTile];
+  __shared__ int sklo[kTile];  // document masks: the rows' key runs
+  __shared__ int skhi[kTile];
 
   const int h = blockIdx.x % a.heads;
   const int k0 = (blockIdx.x / a.heads) * kTile;
@@ -133,6 +137,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_generic(BwdArgs a) {
         const bool ok = t < g.q_len;
         slse[tid] = ok ? a.lse[int64_t(h) * a.seq_len + g.q_global + t] * kLog2e : 0.f;
         sdel[tid] = ok ? a.delta[int64_t(h) * a.n_loc + g.q_start + t] : 0.f;
+        int lo = 0, hi = a.n_loc;
+        if (a.doc && ok) doc_row_keys(a, g.q_global + t, lo, hi);
+        sklo[tid] = lo;
+        skhi[tid] = hi;
       }
       __syncthreads();
       const int rn = min(kTile, g.q_len - r0);
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_generic(BwdArgs a) {
         }
         s = sum_sub(s);
         dp = sum_sub(dp);
-        const bool valid = kok && key < g.kv_full + (g.diag ? t + 1 : 0);
+        const bool valid = kok && key < g.kv_full + (g.diag ? t + 1 : 0) && key >= sklo[rr] && key < skhi[rr];
         const float p = valid ? exp2f(s * a.scale_log2 - slse[rr]) : 0.f;
         const float ds = p * (dp - sdel[rr]);
 #pragma unroll
@@ -184,9 +192,20 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_generic(BwdArgs a) {
   const int rl = tid / kSub, sub = tid % kSub;
   const int row = row0 + rl;
   const bool ok = row < g.q_len;
-  const int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : 0;
-  const int kv_end = g.kv_full + (g.diag ? min(row0 + kTile, g.q_len) : 0);
+  int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : 0;
+  int kv_end = g.kv_full + (g.diag ? min(row0 + kTile, g.q_len) : 0);
   const int64_t grow = g.q_global + row;
+  int klo = 0, kb0 = 0;  // document masks: the row's first key, the workgroup's first key tile
+  if (a.doc) {
+    int lo, hi;
+    doc_row_keys(a, g.q_global + min(row, g.q_len - 1), lo, hi);
+    klo = lo;
+    prefix = min(prefix, hi);
+    doc_row_keys(a, g.q_global + row0, lo, hi);
+    kb0 = lo / kTile * kTile;
+    doc_row_keys(a, g.q_global + min(row0 + kTile, g.q_len) - 1, lo, hi);
+    kv_end = min(kv_end, hi);
+  }
 
   const T* qp = static_cast<const T*>(a.q);
   const T* dop = static_cast<const T*>(a.dout);
@@ -202,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_generic(BwdArgs a) {
 
   const T* kp = static_cast<const T*>(a.k);
   const T* vp = static_cast<const T*>(a.v);
-  for (int j0 = 0; j0 < kv_end; j0 += kTile) {
+  for (int j0 = kb0; j0 < kv_end; j0 += kTile) {
     __syncthreads();
     for (int e = tid; e < kTile * D; e += kThreads) {
       const int kr = e / D, c = e % D;
@@ -227,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_generic(BwdArgs a) {
       }
       s = sum_sub(s);
       dp = sum_sub(dp);
-      const float p = (j0 + kk < prefix) ? exp2f(s * a.scale_log2 - lse2) : 0.f;
+      const float p = (j0 + kk < prefix && j0 + kk >= klo) ? exp2f(s * a.scale_log2 - lse2) : 0.f;
       const float ds = p * (dp - del);
 #pragma unroll
       for (int i = 0; i < DS; ++i) dq[i] = fmaf(ds, sk[kk * D + i * kSub + sub], dq[i]);

@@ -23,11 +23,18 @@
 // keys past the source's real keys are clamped to its last real row and
 // masked.  Tiles are loaded to registers one tile ahead and stored to LDS
 // after the barrier that ends the previous tile.
+//
+// Document masks: every row sees only its document's run of the source's
+// keys, [klo, khi).  The rows of a segment are consecutive positions, so klo
+// and khi grow with the row: the key-major kernel skips a row tile whose runs
+// miss the wave's keys and stops at the first tile that starts past its
+// keys; the row-major kernel starts at its first row's run.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 
+#include "epilogue.h"
 #include "kernels.h"
 
 namespace cpattn {
@@ -148,11 +155,14 @@ __device__ __forceinline__ void tile_store(const TileRegs& t, lds_u8* tile, int 
 // ---------------------------------------------------------------------------
 // Key-major: dK and dV of 128 keys.
 // ---------------------------------------------------------------------------
+template <bool kDoc>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_bf16_d128(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileBytes];
   __shared__ __attribute__((aligned(16))) float s_lse[kTileRows];
   __shared__ __attribute__((aligned(16))) float s_del[kTileRows];
+  __shared__ __attribute__((aligned(16))) int s_klo[kTileRows];  // document masks: the rows' key runs
+  __shared__ __attribute__((aligned(16))) int s_khi[kTileRows];
   lds_u8* const tq = (lds_u8*)smem;
   lds_u8* const tdo = tq + kTileBytes;
 
@@ -206,15 +216,30 @@ void bwd_dkdv_bf16_d128(BwdArgs a) {
         const bool ok = t < g.q_len;
         s_lse[tid] = ok ? a.lse[int64_t(h) * a.seq_len + g.q_global + t] * kLog2e : INFINITY;
         s_del[tid] = ok ? a.delta[int64_t(h) * a.n_loc + g.q_start + t] : 0.f;
+        if constexpr (kDoc) {
+          int lo, hi;
+          doc_row_keys(a, qrow(t), lo, hi);
+          s_klo[tid] = lo;
+          s_khi[tid] = hi;
+        }
       }
       __syncthreads();
+      // document masks: runs start no earlier than the tile's first row's, end
+      // no later than its last row's; no later tile reaches these keys once
+      // a tile's first run starts past them
+      int tile_klo = 0, tile_khi = a.n_loc;
+      if constexpr (kDoc) {
+        tile_klo = s_klo[0];
+        tile_khi = s_khi[min(kTileRows, g.q_len - r0) - 1];
+        if (tile_klo >= k0 + kKeys) break;
+      }
       if (r0 + kTileRows < g.q_len) {  // next tile in flight during this one
         tile_load(rq, a.q, row_bytes, hoff, tid, [&](int r) { return qrow(r0 + kTileRows + r); });
         tile_load(rdo, a.dout, row_bytes, hoff, tid, [&](int r) { return qrow(r0 + kTileRows + r); });
       }
       // the wave's keys against the tile's longest prefix
       const int tile_pre = g.kv_full + (g.diag ? min(r0 + kTileRows, g.q_len) : 0);
-      if (w_key0 >= tile_pre) continue;
+      if (w_key0 >= min(tile_pre, tile_khi) || (kDoc && w_key0 + 32 <= tile_klo)) continue;
       f32x16 s[2], dp[2];
       mm_rows(tq, bs.row, kf, s);
       mm_rows(tdo, bs.row, vf, dp);
@@ -228,12 +253,21 @@ void bwd_dkdv_bf16_d128(BwdArgs a) {
           const float4 d4 = *reinterpret_cast<const float4*>(&s_del[rl]);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+          int klo[4] = {0, 0, 0, 0}, khi[4] = {a.n_loc, a.n_loc, a.n_loc, a.n_loc};
+          if constexpr (kDoc) {
+            const int4 lo4 = *reinterpret_cast<const int4*>(&s_klo[rl]);
+            const int4 hi4 = *reinterpret_cast<const int4*>(&s_khi[rl]);
+            klo[0] = lo4.x, klo[1] = lo4.y, klo[2] = lo4.z, klo[3] = lo4.w;
+            khi[0] = hi4.x, khi[1] = hi4.y, khi[2] = hi4.z, khi[3] = hi4.w;
+          }
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int e = 4 * m + c;
             const int t = r0 + rl + c;
-            const int pre = g.kv_full + (g.diag ? t + 1 : 0);
-            const float p = key < pre ? __builtin_amdgcn_exp2f(fmaf(s[qb][e], a.scale_log2, -lv[c])) : 0.f;
+            const int pre = kDoc ? min(g.kv_full + (g.diag ? t + 1 : 0), khi[c]) : g.kv_full + (g.diag ? t + 1 : 0);
+            const float p = key < pre && (!kDoc || key >= klo[c])
+                                ? __builtin_amdgcn_exp2f(fmaf(s[qb][e], a.scale_log2, -lv[c]))
+                                : 0.f;
             const float ds = p * (dp[qb][e] - dl[c]);
             wp[qb][e >> 3][e & 7] = static_cast<__bf16>(p);
             ws[qb][e >> 3][e & 7] = static_cast<__bf16>(ds);
@@ -272,6 +306,7 @@ void bwd_dkdv_bf16_d128(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Row-major: dQ of 128 rows.
 // ---------------------------------------------------------------------------
+template <bool kDoc>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_bf16_d128(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileBytes];
@@ -291,11 +326,29 @@ void bwd_dq_bf16_d128(BwdArgs a) {
   const int row = row0 + 32 * wv + qc;
   const bool ok = row < g.q_len;
   const int64_t grow = g.q_global + row;
-  const int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : 0;
+  int prefix = ok ? g.kv_full + (g.diag ? row + 1 : 0) : 0;
   const int w_first = row0 + 32 * wv;
   const int w_last = min(w_first + 32, g.q_len);
-  const int w_max = w_last > w_first ? g.kv_full + (g.diag ? w_last : 0) : 0;
-  const int kv_end = g.kv_full + (g.diag ? min(row0 + kRows, g.q_len) : 0);
+  int w_max = w_last > w_first ? g.kv_full + (g.diag ? w_last : 0) : 0;
+  int kv_end = g.kv_full + (g.diag ? min(row0 + kRows, g.q_len) : 0);
+  // document masks: the row's first key, the wave's smallest first key, the
+  // workgroup's first key tile
+  int klo = 0, w_lo = 0, kb0 = 0;
+  if constexpr (kDoc) {
+    int lo, hi;
+    doc_row_keys(a, g.q_global + min(row, g.q_len - 1), lo, hi);
+    klo = lo;
+    prefix = min(prefix, hi);
+    doc_row_keys(a, g.q_global + row0, lo, hi);
+    kb0 = lo / kTileRows * kTileRows;
+    doc_row_keys(a, g.q_global + min(row0 + kRows, g.q_len) - 1, lo, hi);
+    kv_end = min(kv_end, hi);
+    if (w_last > w_first) {
+      doc_row_keys(a, g.q_global + w_first, w_lo, hi);
+      doc_row_keys(a, g.q_global + w_last - 1, lo, hi);
+      w_max = min(w_max, hi);
+    }
+  }
   const uint32_t row_bytes = uint32_t(a.heads) * 256;
   const uint32_t hoff = uint32_t(h) * 256;
 
@@ -318,11 +371,11 @@ void bwd_dq_bf16_d128(BwdArgs a) {
 
   auto krow_of = [&](int kk) { return kv_row(a, min(kk, a.kv_valid - 1)); };
   TileRegs rk, rv;
-  if (kv_end > 0) {
-    tile_load(rk, a.k, row_bytes, hoff, tid, [&](int r) { return krow_of(r); });
-    tile_load(rv, a.v, row_bytes, hoff, tid, [&](int r) { return krow_of(r); });
+  if (kv_end > kb0) {
+    tile_load(rk, a.k, row_bytes, hoff, tid, [&](int r) { return krow_of(kb0 + r); });
+    tile_load(rv, a.v, row_bytes, hoff, tid, [&](int r) { return krow_of(kb0 + r); });
   }
-  for (int j0 = 0; j0 < kv_end; j0 += kTileRows) {
+  for (int j0 = kb0; j0 < kv_end; j0 += kTileRows) {
     __syncthreads();
     tile_store(rk, tk, tid);
     tile_store(rv, tv, tid);
@@ -331,7 +384,7 @@ void bwd_dq_bf16_d128(BwdArgs a) {
       tile_load(rk, a.k, row_bytes, hoff, tid, [&](int r) { return krow_of(j0 + kTileRows + r); });
       tile_load(rv, a.v, row_bytes, hoff, tid, [&](int r) { return krow_of(j0 + kTileRows + r); });
     }
-    if (j0 >= w_max) continue;
+    if (j0 >= w_max || (kDoc && j0 + kTileRows <= w_lo)) continue;
     f32x16 s[2], dp[2];
     mm_rows(tk, bs.row, qf, s);
     mm_rows(tv, bs.row, dof, dp);
@@ -341,7 +394,9 @@ void bwd_dq_bf16_d128(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kk = j0 + 32 * kb + 8 * (e >> 2) + 4 * hf + (e & 3);
-        const float p = kk < prefix ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], a.scale_log2, -lse2)) : 0.f;
+        const float p = kk < prefix && (!kDoc || kk >= klo)
+                            ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], a.scale_log2, -lse2))
+                            : 0.f;
         ws[kb][e >> 3][e & 7] = static_cast<__bf16>(p * (dp[kb][e] - del));
       }
     mm_tr(tk, bs.tr, ws, dq);
@@ -370,10 +425,15 @@ bool bwd_mfma(int dtype_bf16, int head_dim) { return dtype_bf16 && head_dim == 1
 int bwd_mfma_rows() { return kRows; }
 int bwd_mfma_keys() { return kKeys; }
 
-hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t st) {
-  if (a.key_tiles > 0) bwd_dkdv_bf16_d128<<<unsigned(a.key_tiles) * unsigned(a.heads), kThreads, 0, st>>>(a);
-  if (a.total_tiles > 0) bwd_dq_bf16_d128<<<unsigned(a.total_tiles) * unsigned(a.heads), kThreads, 0, st>>>(a);
+template <bool kDoc>
+hipError_t launch_bf16_d128(const BwdArgs& a, hipStream_t st) {
+  if (a.key_tiles > 0) bwd_dkdv_bf16_d128<kDoc><<<unsigned(a.key_tiles) * unsigned(a.heads), kThreads, 0, st>>>(a);
+  if (a.total_tiles > 0) bwd_dq_bf16_d128<kDoc><<<unsigned(a.total_tiles) * unsigned(a.heads), kThreads, 0, st>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t st) {
+  return a.doc ? launch_bf16_d128<true>(a, st) : launch_bf16_d128<false>(a, st);
 }
 
 }  // namespace cpattn

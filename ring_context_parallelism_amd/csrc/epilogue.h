@@ -23,13 +23,16 @@ __device__ __forceinline__ int kv_row(const StepArgs& a, int kk) {
 }
 
 // Document masks: local keys of the step's source below global position x
-// (the source's local keys are in increasing position order).
-__device__ __forceinline__ int doc_keys_before(const StepArgs& a, int x) {
+// (the source's local keys are in increasing position order).  A is StepArgs
+// or BwdArgs.
+template <typename A>
+__device__ __forceinline__ int doc_keys_before(const A& a, int x) {
   return min(max(x - a.kpos_lo, 0), a.kpos_split) + min(max(x - a.kpos_hi, 0), a.n_loc - a.kpos_split);
 }
 
 // The run of local keys [lo, hi) of the document holding global position grow.
-__device__ __forceinline__ void doc_row_keys(const StepArgs& a, int64_t grow, int& lo, int& hi) {
+template <typename A>
+__device__ __forceinline__ void doc_row_keys(const A& a, int64_t grow, int& lo, int& hi) {
   const int2 d = reinterpret_cast<const int2*>(a.doc)[grow];
   lo = doc_keys_before(a, d.x);
   hi = doc_keys_before(a, d.y);

@@ -119,6 +119,11 @@ struct BwdArgs {
   int64_t delta_lo;
   int64_t delta_hi;
   int64_t delta_split;
+  // document masks, as in StepArgs (null: none)
+  const int32_t* doc;
+  int32_t kpos_lo;
+  int32_t kpos_hi;
+  int32_t kpos_split;
 };
 int bwd_generic_tile();  // rows and keys per workgroup of the generic kernels
 hipError_t launch_bwd_delta(const BwdArgs& a, int dtype_bf16, int head_dim, hipStream_t stream);

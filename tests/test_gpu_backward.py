@@ -165,3 +165,37 @@ def test_full_size_backward_sampled_rows_and_gradient_sums():
     _say(f"  |sum dV - sum dO| {float((sdv - sdo).abs().max()):.3e}  |sum dK| {float(sdk):.3e} of {float(adk):.3e}")
     assert float(sdk) <= 1e-2 * float(adk)
     p.close()
+
+
+# Document masks ("Context Parallelism for Long-Context Training", section
+# "Prove attention equivalence": causal and document masks): single-token
+# documents, boundaries on 64- and 128-token tile edges and inside chunks.
+DOC_CASES = [
+    (1536, 2, "zigzag", True, 2, 128, torch.bfloat16, [0, 1, 2, 64, 128, 129, 500, 777, 1535]),
+    (1003, 4, "zigzag", True, 2, 128, torch.bfloat16, [0, 100, 101, 383, 640]),
+    (1024, 4, "zigzag", False, 2, 128, torch.bfloat16, [0, 256, 300, 900]),
+    (768, 3, "contiguous", True, 2, 128, torch.bfloat16, [0, 5, 260, 511, 512]),
+    (520, 2, "zigzag", True, 2, 64, torch.bfloat16, [0, 33, 130, 131]),
+    (256, 2, "zigzag", True, 2, 64, torch.float32, [0, 1, 64, 100, 200]),
+    (299, 3, "contiguous", False, 2, 128, torch.float32, [0, 50, 51, 250]),
+]
+
+
+@pytest.mark.parametrize("case", DOC_CASES, ids=[_ids(c[:7]) for c in DOC_CASES])
+def test_full_backward_with_documents_matches_oracle(case):
+    seq, cp, layout, causal, heads, dim, dtype, docs = case
+    _say(f"backward with documents {_ids(case[:7])} {docs}")
+    q, k, v, dout = _inputs(seq, heads, dim, dtype, 93)
+    p = Plan(seq, cp, heads, dim, causal, layout, dtype=dtype)
+    p.set_documents(docs)
+    dev = _dev()
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+    out, lse = _forward(p, qd, kd, vd)
+    dq, dk, dv = (torch.full((seq, heads, dim), float("nan"), device=dev) for _ in range(3))
+    p.full_backward(qd, kd, vd, out, lse, dod, dq, dk, dv)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(*(to_numpy_f64(t) for t in (q, k, v, dout)), causal=causal, doc_starts=docs)
+    errs = [_rel_err(g, r) for g, r in zip((dq, dk, dv), ref)]
+    _say(f"  rel err dq={errs[0]:.2e} dk={errs[1]:.2e} dv={errs[2]:.2e}")
+    assert max(errs) <= REL[dtype], errs
+    p.close()

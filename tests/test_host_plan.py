@@ -254,17 +254,6 @@ def test_document_list_errors():
         assert lib.cp_attn_set_documents(None, None, 0) == N.EINVAL
 
 
-def test_backward_with_documents_is_unsupported():
-    lib = N.lib()
-    dummy = ctypes.c_void_p(1 << 20)  # never dereferenced
-    with Plan(128, 2, 1, 64, True, "zigzag") as p:
-        p.set_documents([0, 40])
-        f = ctypes.c_void_p(1 << 20)
-        assert lib.cp_attn_rank_backward(p._h, dummy, dummy, dummy, dummy, f, dummy, f, f, f, 0, None) == \
-            N.EUNSUPPORTED
-        assert lib.cp_attn_full_backward(p._h, dummy, dummy, dummy, dummy, f, dummy, f, f, f, None) == N.EUNSUPPORTED
-
-
 def _tiles_brute(seq, cp, layout, causal, r, s, bm, bn, docs):
     qpos = oracle.rank_positions(seq, cp, r, layout)
     kpos = oracle.rank_positions(seq, cp, oracle.ring_source(r, s, cp), layout)
