@@ -322,6 +322,7 @@ void attn_step_bf16(StepArgs a) {
   const int lrow = g.q_start + row;
   const float lse_s = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
   const float inv = l > 0.f ? 1.f / l : 0.f;  // a row that saw no key (document masks): O_s = 0, lse_s = -inf
+  if (doc && l == 0.f && epi == kEpiMerge) return;  // ... and leaves a merge-only step's running state as it is
   float4 c[NB][4];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -940,6 +941,9 @@ void attn_step_bf16_d128x8(StepArgs a) {
     inv = 1.f;
   }
   if (!ok) return;
+  // document masks: a row that saw no key leaves a merge-only step's running
+  // state as it is
+  if (kDoc && l == 0.f && epi == kEpiMerge) return;
   float4 c[NB][4];
 #pragma unroll
   for (int b = 0; b < NB; ++b)

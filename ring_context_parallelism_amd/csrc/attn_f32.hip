@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kThreads) void attn_step_f32(StepArgs a) {
   const int lrow = g.q_start + row;
   const float lse_s = m + logf(l);
   const float inv = l > 0.f ? 1.f / l : 0.f;  // a row that saw no key (document masks): O_s = 0, lse_s = -inf
+  if (a.doc && l == 0.f && epi == kEpiMerge) return;  // ... and leaves a merge-only step's running state as it is
   float4 c[DS / 4];
 #pragma unroll
   for (int i = 0; i < DS; i += 4) c[i / 4] = row_epi_load4(a, epi, h, lrow, sub * DS + i, D);

@@ -83,6 +83,12 @@ int64_t Plan::keys_before(int j, int64_t pos) const {
   return run(chunk_of(j, 0) * chunk, chunk) + run(chunk_of(j, 1) * chunk, chunk);
 }
 
+namespace {
+void row_keys(const Plan& p, const StepDesc& d, const Segment& g, int64_t t, int64_t* lo, int64_t* hi);
+}
+static void build_steps(Plan& p);
+static void mark_first_last(Plan& p);
+
 int set_documents(Plan& p, const int64_t* starts, int64_t count, std::string* err) {
   if (count < 0 || (count > 0 && !starts)) {
     *err = "documents: count < 0, or starts is null";
@@ -96,6 +102,25 @@ int set_documents(Plan& p, const int64_t* starts, int64_t count, std::string* er
   }
   p.doc_starts.assign(starts, starts + count);
   ++p.doc_version;
+  build_steps(p);
+  if (!p.doc_starts.empty()) {
+    // a segment none of whose rows sees a key of the step's source under the
+    // documents is dropped, and the first / last steps of the row runs follow
+    for (auto& d : p.steps) {
+      int kept = 0;
+      for (int i = 0; i < d.nseg; ++i) {
+        bool any = false;
+        for (int64_t t = 0; t < d.seg[i].q_len && !any; ++t) {
+          int64_t lo = 0, hi = 0;
+          row_keys(p, d, d.seg[i], t, &lo, &hi);
+          any = hi > lo;
+        }
+        if (any) d.seg[kept++] = d.seg[i];
+      }
+      d.nseg = kept;
+    }
+    mark_first_last(p);
+  }
   return kOk;
 }
 
@@ -146,7 +171,12 @@ static void build_steps(Plan& p) {
       }
     }
   }
-  // first / last active step of each row run (identified by q_start)
+  mark_first_last(p);
+}
+
+// first / last active step of each row run (identified by q_start)
+static void mark_first_last(Plan& p) {
+  const int P = p.cp;
   for (int r = 0; r < P; ++r) {
     for (int s = 0; s < P; ++s) {
       StepDesc& d = p.steps[size_t(r) * P + s];

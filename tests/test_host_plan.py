@@ -292,3 +292,34 @@ def test_document_work_counts_match_oracle(seq, cp, layout, causal, bm, bn, docs
     p.set_documents(None)
     for r in range(cp):
         assert p.valid_work(r, 0, bm, bn)[1] == oracle.step_valid_pairs(seq, cp, layout, causal, r, 0)
+
+
+@pytest.mark.parametrize("seq,cp,layout,causal", [(1003, 4, "zigzag", True), (1000, 3, "contiguous", True),
+                                                  (999, 7, "contiguous", False), (4096, 8, "zigzag", True)])
+def test_document_plan_drops_empty_segments(seq, cp, layout, causal):
+    """Under document masks every kept segment holds a valid pair, step 0
+    keeps every real row (a row sees itself), and each row run's first and last
+    flags sit on the first and last steps that still hold it."""
+    from ring_context_parallelism_amd.inputs import make_documents
+    docs = make_documents(seq, 60, seed=seq)
+    p = Plan(seq, cp, 1, 128, causal, layout)
+    p.set_documents(docs)
+    for r in range(cp):
+        steps_of = {}
+        for s in range(cp):
+            segs = p.step_segments(r, s)
+            for g in segs:
+                qpos = oracle.rank_positions(seq, cp, r, layout)[g["q_start"]:g["q_start"] + g["q_len"]]
+                kpos = oracle.rank_positions(seq, cp, oracle.ring_source(r, s, cp), layout)
+                assert oracle.valid_mask(qpos, kpos, causal, doc_starts=docs).any(), (r, s, g)
+                steps_of.setdefault(g["q_start"], []).append((s, g["first"], g["last"]))
+        assert sum(g["q_len"] for g in p.step_segments(r, 0)) == p.rank_valid_rows(r)
+        for run in steps_of.values():
+            ss = [x[0] for x in run]
+            for s, first, last in run:
+                assert bool(first) == (s == min(ss)) and bool(last) == (s == max(ss))
+    p.set_documents(None)
+    q = Plan(seq, cp, 1, 128, causal, layout)
+    for r in range(cp):
+        for s in range(cp):
+            assert p.step_segments(r, s) == q.step_segments(r, s)
