@@ -452,9 +452,20 @@ void attn_step_bf16_d128x8(StepArgs a) {
   // ring-copy staging: 3 slots x 8 waves x 1 KiB
   __shared__ __attribute__((aligned(1024))) uint8_t smem_c[kRecv ? 3 * 8 * 1024 : 16];
   lds_u8* const kv_lds = (lds_u8*)smem_kv;
-  // stage s: K tile, then V tile
-  auto kst = [&](int st) { return kv_lds + st * (2 * kTileBytes); };
-  auto vst = [&](int st) { return kv_lds + st * (2 * kTileBytes) + kTileBytes; };
+  // the four K stages fill the first 64 KiB, the four V stages the second:
+  // with a constant stage every operand read addresses a per-lane base plus
+  // an offset below 64 KiB, which the read instruction carries itself
+  auto kst = [&](int st) { return kv_lds + st * kTileBytes; };
+  auto vst = [&](int st) { return kv_lds + (4 + st) * kTileBytes; };
+  // The transposed V reads take no offset from the compiler: a constant V
+  // stage would only make it keep every stage's eight addresses in VGPRs.
+  // The stage base goes through an SGPR the compiler cannot see into (an
+  // empty assembly statement), so each read adds it, as with a loop index.
+  auto vst_rt = [&](int st) {
+    int o = (4 + st) * kTileBytes;
+    asm volatile("" : "+s"(o));
+    return kv_lds + o;
+  };
   lds_u8* const cstage = (lds_u8*)smem_c;
 
   int h, t;
@@ -772,7 +783,7 @@ void attn_step_bf16_d128x8(StepArgs a) {
   do {                                                                                     \
     const bool sc_ = live(kb0 + (J) * kBN);                                                \
     const bool pv_ = (J) > 0 && live(kb0 + ((J) - 1) * kBN);                               \
-    if (pv_) pv(vst(((S) + 3) & 3), pb_);                                                  \
+    if (pv_) pv(vst_rt(((S) + 3) & 3), pb_);                                               \
     if (sc_) scores(kst(S), s_);                                                           \
   } while (0)
 #define CPATTN_X8_END()                                                                    \
@@ -784,32 +795,66 @@ void attn_step_bf16_d128x8(StepArgs a) {
     lds_barrier();                                                                         \
   } while (0)
 
+  // Without the ring copy the loops run four tiles per iteration, one per
+  // stage, so that each tile's stage is a constant (the copy's registers
+  // leave no room for that; its loops take the stage as a variable).
   bf16x8 pb_[2][2];  // probabilities of the last softmaxed tile
   f32x16 s_[2];      // scores of the last scored tile
+  int cb = 0;        // copy staging slot of the tile
+#define CPATTN_X8_TILE_A(J, ST)                                                            \
+  do {                                                                                     \
+    if ((J) < ntiles) {                                                                    \
+      CPATTN_X8_COPY(J, cb);                                                               \
+      CPATTN_X8_GEMMS(J, ST, s_, pb_);                                                     \
+      if (live(kb0 + (J) * kBN)) softmax(s_, kb0 + (J) * kBN, pb_);                        \
+      issue(desc_k, kb0 + min((J) + 2, ntiles - 1) * kBN, kst(((ST) + 2) & 3));            \
+      CPATTN_X8_END();                                                                     \
+      cb = cb == 2 ? 0 : cb + 1;                                                           \
+    }                                                                                      \
+  } while (0)
+#define CPATTN_X8_TILE_B(J, ST)                                                            \
+  do {                                                                                     \
+    if ((J) < ntiles) {                                                                    \
+      CPATTN_X8_COPY(J, cb);                                                               \
+      if ((J) > 0 && live(kb0 + ((J) - 1) * kBN)) softmax(s_, kb0 + ((J) - 1) * kBN, pb_); \
+      issue(desc_v, kb0 + min((J) + 2, ntiles - 1) * kBN, vst(((ST) + 2) & 3));            \
+      CPATTN_X8_GEMMS(J, ST, s_, pb_);                                                     \
+      CPATTN_X8_END();                                                                     \
+      cb = cb == 2 ? 0 : cb + 1;                                                           \
+    }                                                                                      \
+  } while (0)
   if (wv < 4) {
-    for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
-      CPATTN_X8_COPY(j, cb);
-      CPATTN_X8_GEMMS(j, st, s_, pb_);
-      if (live(kb0 + j * kBN)) softmax(s_, kb0 + j * kBN, pb_);
-      issue(desc_k, kb0 + min(j + 2, ntiles - 1) * kBN, kst((st + 2) & 3));
-      CPATTN_X8_END();
+    if constexpr (kRecv) {
+      for (int j = 0, st = 0; j < ntiles; ++j, st = (st + 1) & 3) CPATTN_X8_TILE_A(j, st);
+    } else {
+      for (int j = 0; j < ntiles; j += 4) {
+        CPATTN_X8_TILE_A(j, 0);
+        CPATTN_X8_TILE_A(j + 1, 1);
+        CPATTN_X8_TILE_A(j + 2, 2);
+        CPATTN_X8_TILE_A(j + 3, 3);
+      }
     }
     // product of the last tile (its stage is not overwritten: the loads
     // issued at the last two tiles went to other stages)
     if (ntiles > 0 && live(kb0 + (ntiles - 1) * kBN)) pv(vst((ntiles - 1) & 3), pb_);
   } else {
-    for (int j = 0, st = 0, cb = 0; j < ntiles; ++j, st = (st + 1) & 3, cb = cb == 2 ? 0 : cb + 1) {
-      CPATTN_X8_COPY(j, cb);
-      if (j > 0 && live(kb0 + (j - 1) * kBN)) softmax(s_, kb0 + (j - 1) * kBN, pb_);
-      issue(desc_v, kb0 + min(j + 2, ntiles - 1) * kBN, vst((st + 2) & 3));
-      CPATTN_X8_GEMMS(j, st, s_, pb_);
-      CPATTN_X8_END();
+    if constexpr (kRecv) {
+      for (int j = 0, st = 0; j < ntiles; ++j, st = (st + 1) & 3) CPATTN_X8_TILE_B(j, st);
+    } else {
+      for (int j = 0; j < ntiles; j += 4) {
+        CPATTN_X8_TILE_B(j, 0);
+        CPATTN_X8_TILE_B(j + 1, 1);
+        CPATTN_X8_TILE_B(j + 2, 2);
+        CPATTN_X8_TILE_B(j + 3, 3);
+      }
     }
     if (ntiles > 0 && live(kb0 + (ntiles - 1) * kBN)) {
       softmax(s_, kb0 + (ntiles - 1) * kBN, pb_);
       pv(vst((ntiles - 1) & 3), pb_);
     }
   }
+#undef CPATTN_X8_TILE_B
+#undef CPATTN_X8_TILE_A
 #undef CPATTN_X8_END
 #undef CPATTN_X8_GEMMS
 #undef CPATTN_X8_COPY
