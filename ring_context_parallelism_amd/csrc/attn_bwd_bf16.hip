@@ -19,10 +19,13 @@
 // Row-major kernel (dQ): a workgroup of 4 waves owns 128 rows, 32 per wave,
 // whose Q and dO stay in registers; K/V tiles of 64 keys in LDS:
 //   S^T = K Q^T, dP^T = V dO^T, dS^T as above, dQ^T += K^T dS^T.
+// It loads each tile when it needs it (no register prefetch), which keeps it
+// within 256 VGPRs: two workgroups share a CU and one computes while the
+// other waits for its tile.
 // Rows past a segment's end carry LSE = +inf, so their P is exactly zero;
 // keys past the source's real keys are clamped to its last real row and
-// masked.  Tiles are loaded to registers one tile ahead and stored to LDS
-// after the barrier that ends the previous tile.
+// masked.  The key-major kernel loads its tiles to registers one tile ahead
+// and stores them to LDS after the barrier that ends the previous tile.
 //
 // Document masks: every row sees only its document's run of the source's
 // keys, [klo, khi).  The rows of a segment are consecutive positions, so klo
@@ -307,7 +310,7 @@ void bwd_dkdv_bf16_d128(BwdArgs a) {
 // Row-major: dQ of 128 rows.
 // ---------------------------------------------------------------------------
 template <bool kDoc>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_bf16_d128(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileBytes];
   lds_u8* const tk = (lds_u8*)smem;
@@ -370,20 +373,16 @@ void bwd_dq_bf16_d128(BwdArgs a) {
   const Bases bs = make_bases(lane);
 
   auto krow_of = [&](int kk) { return kv_row(a, min(kk, a.kv_valid - 1)); };
-  TileRegs rk, rv;
-  if (kv_end > kb0) {
-    tile_load(rk, a.k, row_bytes, hoff, tid, [&](int r) { return krow_of(kb0 + r); });
-    tile_load(rv, a.v, row_bytes, hoff, tid, [&](int r) { return krow_of(kb0 + r); });
-  }
   for (int j0 = kb0; j0 < kv_end; j0 += kTileRows) {
-    __syncthreads();
-    tile_store(rk, tk, tid);
-    tile_store(rv, tv, tid);
-    __syncthreads();
-    if (j0 + kTileRows < kv_end) {
-      tile_load(rk, a.k, row_bytes, hoff, tid, [&](int r) { return krow_of(j0 + kTileRows + r); });
-      tile_load(rv, a.v, row_bytes, hoff, tid, [&](int r) { return krow_of(j0 + kTileRows + r); });
+    {
+      TileRegs rk, rv;
+      tile_load(rk, a.k, row_bytes, hoff, tid, [&](int r) { return krow_of(j0 + r); });
+      tile_load(rv, a.v, row_bytes, hoff, tid, [&](int r) { return krow_of(j0 + r); });
+      __syncthreads();
+      tile_store(rk, tk, tid);
+      tile_store(rv, tv, tid);
     }
+    __syncthreads();
     if (j0 >= w_max || (kDoc && j0 + kTileRows <= w_lo)) continue;
     f32x16 s[2], dp[2];
     mm_rows(tk, bs.row, qf, s);
