@@ -20,12 +20,12 @@ import pytest
 from ring_context_parallelism_amd import build as B
 
 
-def _resources():
+def _resources(source="attn_bf16.hip"):
     with tempfile.TemporaryDirectory() as d:
-        out = os.path.join(d, "attn_bf16.s")
+        out = os.path.join(d, "kernels.s")
         flags = [f for f in B.COMMON if f != "-fPIC"]
         cmd = [B.hipcc(), "-x", "hip", *B.HIP_FLAGS, *flags, "--cuda-device-only", "-S",
-               os.path.join(B.CSRC, "attn_bf16.hip"), "-o", out]
+               os.path.join(B.CSRC, source), "-o", out]
         subprocess.run(cmd, check=True, capture_output=True, timeout=600)
         text = open(out).read()
     res = {}
@@ -54,3 +54,18 @@ def test_step_kernel_leaves_room_for_the_receive_kernel(resources):
 def test_no_kernel_spills_to_scratch(resources):
     for name, r in resources.items():
         assert r["scratch"] == 0, (name, r)
+
+
+def test_backward_kernels_do_not_spill():
+    """The matrix-core backward kernels keep every value in registers; the
+    row-major dQ kernel stays within 256 VGPRs, so two workgroups share a CU."""
+    try:
+        B.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    res = _resources("attn_bwd_bf16.hip")
+    assert res
+    for name, r in res.items():
+        assert r["scratch"] == 0, (name, r)
+    dq = [v for k, v in res.items() if "bwd_dq_bf16_d128ILb0E" in k]
+    assert len(dq) == 1 and dq[0]["vgpr"] <= 256, dq
