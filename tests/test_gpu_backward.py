@@ -199,3 +199,34 @@ def test_full_backward_with_documents_matches_oracle(case):
     _say(f"  rel err dq={errs[0]:.2e} dk={errs[1]:.2e} dv={errs[2]:.2e}")
     assert max(errs) <= REL[dtype], errs
     p.close()
+
+
+def test_full_size_backward_with_documents_sampled_rows():
+    """The 32k-token, cp 8 zigzag workload with seeded documents (mean length
+    2048): dQ of sampled rows against the oracle's document gradients, and the
+    per-document closed form sum_j dV_j = sum_i dO_i over each document."""
+    from ring_context_parallelism_amd.inputs import WORKLOADS, make_documents, workload_qkv
+    w = WORKLOADS["causal_s32768_cp8_zigzag_h32_d128_bf16_rank0"]
+    docs = make_documents(w.seq_len, 2048, seed=w.seed + 11)
+    _say(f"full-size backward with {len(docs)} documents {w.name}")
+    q, k, v = workload_qkv(w)
+    dout = make_qkv(w.seq_len, w.heads, w.head_dim, "bf16", w.seed + 7)[0]
+    p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, True, w.layout)
+    p.set_documents(docs)
+    dev = _dev()
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+    out, lse = _forward(p, qd, kd, vd)
+    dq, dk, dv = (torch.empty((w.seq_len, w.heads, w.head_dim), device=dev) for _ in range(3))
+    p.full_backward(qd, kd, vd, out, lse, dod, dq, dk, dv)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 1, 2047, 2048, 16383, 16384, 32767} | {d for d in docs[1:4]} | {docs[-1] - 1}))
+    ref = oracle.query_gradients(*(to_numpy_f64(t) for t in (q, k, v, dout)), rows, causal=True, doc_starts=docs)
+    rel = float(np.max(np.abs(dq.cpu().double().numpy()[rows] - ref)) / np.max(np.abs(ref)))
+    _say(f"  sampled dq rel err {rel:.2e}")
+    assert rel <= REL[torch.bfloat16]
+    bounds = list(docs) + [w.seq_len]
+    dv64, do64 = dv.double().cpu(), dod.double().cpu()
+    for a, b in list(zip(bounds[:-1], bounds[1:]))[:6]:
+        sdv, sdo = dv64[a:b].sum(dim=0), do64[a:b].sum(dim=0)
+        assert float((sdv - sdo).abs().max()) <= 1e-2 * max(1.0, float(sdo.abs().max())), (a, b)
+    p.close()

@@ -238,3 +238,28 @@ def test_padding_invariance_with_documents():
     _check(got[0], got[1], *(t[:seq] for t in (q, k, v)), True, docs, torch.bfloat16)
     long.close()
     short.close()
+
+
+def test_full_size_rank0_with_documents_sampled_rows():
+    """The bench's workload and launch configuration (32k tokens, cp 8,
+    zigzag, 32 heads x 128, bf16, rank 0's share, default schedule) with seeded
+    documents: sampled rows of the share against the oracle."""
+    from ring_context_parallelism_amd.inputs import WORKLOADS, workload_qkv
+    w = WORKLOADS["causal_s32768_cp8_zigzag_h32_d128_bf16_rank0"]
+    q, k, v = workload_qkv(w)
+    rows = oracle.rank_positions(w.seq_len, w.cp, w.rank, w.layout)
+    sample = rows[np.linspace(0, rows.size - 1, 16).astype(np.int64)]
+    for mean in (8192, 1024):
+        docs = make_documents(w.seq_len, mean, seed=w.seed + mean)
+        _say(f"documents full size: {len(docs)} documents (mean {mean})")
+        p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, True, w.layout, dtype=torch.bfloat16)
+        p.set_documents(docs)
+        qd, kd, vd, out, lse = _bufs(p, q, k, v)
+        p.rank_forward(qd, kd, vd, out, lse, w.rank)
+        torch.cuda.synchronize()
+        out_c, lse_c = out.cpu(), lse.cpu()
+        _check(out_c, lse_c, q, k, v, True, docs, torch.bfloat16, rows=sample)
+        # the rank writes only its own rows
+        others = np.setdiff1d(np.arange(w.seq_len), rows)[::997]
+        assert torch.isnan(out_c[others].float()).all() and torch.isnan(lse_c[:, others]).all()
+        p.close()
