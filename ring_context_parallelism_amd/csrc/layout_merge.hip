@@ -55,32 +55,40 @@ __global__ __launch_bounds__(kThreads) void layout_copy(LayoutArgs a) {
 
 // Ulysses all-to-all ("Sequence Parallelism IV: Megatron Context Parallel and
 // Load-Balanced Rings", section 7 "CP vs Ulysses": the transpose from
-// sequence ownership to head ownership).  One workgroup per (head owner r',
-// token t) row of the head layout: the H/cp heads of token t that r' receives
-// are one contiguous run in the sequence owner's local row, so both sides
-// move whole 16-byte vectors.
+// sequence ownership to head ownership).  A (head owner r', token t) row of
+// the head layout -- the H/cp heads of token t that r' receives -- is one
+// contiguous run of `run` 16-byte vectors in the sequence owner's local row,
+// so both sides move whole vectors.  Each thread moves one vector of a row
+// (a workgroup covers kThreads / run rows when a run is shorter than the
+// workgroup); the row arithmetic is 32-bit (the plan keeps every tensor below
+// 2^32 bytes, so rows and vector indices fit).
 __global__ __launch_bounds__(kThreads) void ulysses_copy(UlyssesArgs a) {
   const uint4* src = static_cast<const uint4*>(a.src);
   uint4* dst = static_cast<uint4*>(a.dst);
-  const int64_t group = a.heads / a.cp;
-  const int64_t run = group * a.head_vec;  // vectors per (r', t)
-  const int64_t rows = int64_t(a.cp) * a.seq_len;
-  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-    const int64_t rh = row / a.seq_len, t = row % a.seq_len;
-    const int64_t c = t / a.chunk;
-    int64_t owner, li;
+  const uint32_t group = uint32_t(a.heads / a.cp);
+  const uint32_t run = group * uint32_t(a.head_vec);     // vectors per (r', t)
+  const uint32_t tpr = run < uint32_t(kThreads) ? run : uint32_t(kThreads);  // threads per row
+  const uint32_t rpw = uint32_t(kThreads) / tpr;          // rows per workgroup pass
+  const uint32_t sub = threadIdx.x / tpr, lv = threadIdx.x % tpr;
+  if (sub >= rpw) return;
+  const uint32_t seq = uint32_t(a.seq_len), chunk = uint32_t(a.chunk), cp = uint32_t(a.cp);
+  const uint32_t rows = cp * seq;
+  for (uint32_t row = blockIdx.x * rpw + sub; row < rows; row += gridDim.x * rpw) {
+    const uint32_t rh = row / seq, t = row - rh * seq;
+    const uint32_t c = t / chunk, tc = t - c * chunk;
+    uint32_t owner, li;
     if (a.zigzag) {
-      owner = c < a.cp ? c : 2 * int64_t(a.cp) - 1 - c;
-      li = (c < a.cp ? 0 : a.chunk) + t % a.chunk;
+      owner = c < cp ? c : 2 * cp - 1 - c;
+      li = (c < cp ? 0 : chunk) + tc;
     } else {
       owner = c;
-      li = t % a.chunk;
+      li = tc;
     }
-    const int64_t hs = row * run;                                                  // head layout
-    const int64_t sq = ((owner * a.n_loc + li) * a.heads + rh * group) * a.head_vec;  // sequence layout
-    const int64_t from = a.to_heads ? sq : hs;
-    const int64_t to = a.to_heads ? hs : sq;
-    for (int64_t v = threadIdx.x; v < run; v += kThreads) dst[to + v] = src[from + v];
+    const uint32_t hs = row * run;                                                                  // head layout
+    const uint32_t sq = ((owner * uint32_t(a.n_loc) + li) * uint32_t(a.heads) + rh * group) * uint32_t(a.head_vec);
+    const uint32_t from = a.to_heads ? sq : hs;
+    const uint32_t to = a.to_heads ? hs : sq;
+    for (uint32_t v = lv; v < run; v += tpr) dst[to + v] = src[from + v];
   }
 }
 
@@ -212,7 +220,9 @@ hipError_t launch_layout(const LayoutArgs& a, int max_blocks, hipStream_t stream
 
 hipError_t launch_ulysses(const UlyssesArgs& a, hipStream_t stream) {
   const int64_t rows = int64_t(a.cp) * a.seq_len;
-  ulysses_copy<<<grid_for(rows, 1, 65536u), kThreads, 0, stream>>>(a);
+  const int64_t run = a.heads / a.cp * a.head_vec;
+  const int64_t rpw = run < kThreads ? kThreads / run : 1;  // rows per workgroup pass
+  ulysses_copy<<<grid_for(rows, rpw, 65536u), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
