@@ -169,12 +169,13 @@ def test_allgather_with_documents_matches_oracle(layout, causal, dtype):
     p.close()
 
 
-def test_ulysses_forward_with_documents_matches_oracle():
+@pytest.mark.parametrize("causal", [True, False])
+def test_ulysses_forward_with_documents_matches_oracle(causal):
     seq, cp, heads, dim = 2048, 2, 4, 128
-    _say("documents ulysses")
+    _say(f"documents ulysses causal={causal}")
     docs = _docs("300", seq)
     q, k, v = make_qkv(seq, heads, dim, "bf16", 82)
-    p = Plan(seq, cp, heads, dim, True, "zigzag", dtype=torch.bfloat16)
+    p = Plan(seq, cp, heads, dim, causal, "zigzag", dtype=torch.bfloat16)
     p.set_documents(docs)
     dev = _dev()
     g = heads // cp
@@ -189,7 +190,7 @@ def test_ulysses_forward_with_documents_matches_oracle():
         torch.cuda.synchronize()
         out[:, sl] = o.cpu()
         lse[sl] = l.cpu()
-    _check(out, lse, q, k, v, True, docs, torch.bfloat16)
+    _check(out, lse, q, k, v, causal, docs, torch.bfloat16)
     p.close()
 
 

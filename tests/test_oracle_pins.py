@@ -589,3 +589,17 @@ def test_document_pairs_sum_to_per_document_triangles():
         tot = sum(oracle.step_valid_pairs(seq, cp, layout, True, r, s, doc_starts=DOCS)
                   for r in range(cp) for s in range(cp))
         assert tot == sum((b - a) * (b - a + 1) // 2 for a, b in zip(DOCS, ends))
+
+
+def test_planted_document_boundary_shift_is_caught(monkeypatch):
+    """A document lookup that puts each start token in the previous document
+    (a boundary off by one) breaks the per-document equality."""
+    attention_mod = importlib.import_module("oracle.attention")  # the module, not the function of that name
+    real = attention_mod.document_of
+
+    def shifted(pos, doc_starts):
+        return np.searchsorted(np.asarray(doc_starts, dtype=np.int64), np.asarray(pos, dtype=np.int64), side="left") - 1
+    monkeypatch.setattr(attention_mod, "document_of", shifted)
+    assert real(DOCS, DOCS).tolist() != shifted(DOCS, DOCS).tolist()
+    with pytest.raises(AssertionError):
+        test_document_mask_equals_separate_documents(True)
