@@ -222,3 +222,28 @@ def test_padded_device_tile_counts_match_plan():
         for s in range(cp):
             assert counts[r][s] == heads * p.valid_work(r, s, tr, tk)[0], (r, s, counts[r][s])
     p.close()
+
+
+@pytest.mark.parametrize("dtype,dim", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_tiny_sequences_every_row(dtype, dim):
+    """The smallest inputs: 1, 2 and 3 tokens at cp 1 and 2, both placements,
+    causal and bidirectional (a single token is its own whole context: its
+    output is its value row exactly and its LSE its own scaled score)."""
+    for seq in (1, 2, 3):
+        for cp in (1, 2):
+            for layout in ("zigzag", "contiguous"):
+                for causal in (True, False):
+                    _say(f"tiny seq={seq} cp={cp} {layout} causal={causal} {dtype}")
+                    q, k, v = make_qkv(seq, 2, dim, "bf16" if dtype == torch.bfloat16 else "fp32", 90 + seq)
+                    p = Plan(seq, cp, 2, dim, causal, layout, dtype=dtype)
+                    dev = _dev()
+                    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+                    out = torch.full_like(qd, float("nan"))
+                    lse = torch.full((2, seq), float("nan"), device=dev)
+                    p.full_forward(qd, kd, vd, out, lse)
+                    torch.cuda.synchronize()
+                    out, lse = out.cpu(), lse.cpu()
+                    _check(out, lse, q, k, v, causal, dtype, np.arange(seq))
+                    if causal or seq == 1:
+                        assert torch.equal(out[0], v[0])
+                    p.close()
