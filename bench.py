@@ -396,7 +396,7 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import ring_context_parallelism_amd as R
-    from ring_context_parallelism_amd.inputs import WORKLOADS, workload_qkv
+    from ring_context_parallelism_amd.inputs import WORKLOADS, sha256_of, workload_qkv
 
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
@@ -450,7 +450,8 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic: i.i.d. N(0,1) Q/K/V, seeded, CPU-drawn",
         "config": {"workload": w.name, "seq_len": w.seq_len, "cp_size": w.cp, "layout": w.layout,
                    "causal": w.causal, "rank": w.rank, "heads": w.heads, "head_dim": w.head_dim,
-                   "ring_steps": w.cp, "valid_flops": flops},
+                   "ring_steps": w.cp, "valid_flops": flops, "seed": w.seed,
+                   "inputs_sha256": sha256_of(q_cpu, k_cpu, v_cpu)},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
     }
