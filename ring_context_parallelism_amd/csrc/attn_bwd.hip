@@ -53,24 +53,35 @@ __device__ __forceinline__ float sum_sub(float x) {  // over the kSub lanes of a
   return x;
 }
 
-// D_i = <dO_i, O_i> of the rank's real local rows: one wave per (row, head).
+// D_i = <dO_i, O_i> of the rank's real local rows.  One item = (head, row):
+// D / kVec lanes per item, each with one 16-byte vector of O and of dO, then
+// a shuffle reduction within the item's lanes (an aligned power-of-two group
+// of a wave).
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_delta(BwdArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t item = int64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  constexpr int kVec = 16 / int(sizeof(T));  // elements per 16-byte vector
+  constexpr int kLanes = D / kVec;           // lanes per item: 8 to 32
+  static_assert(kLanes >= 1 && kLanes <= 64 && (kLanes & (kLanes - 1)) == 0, "lanes per item");
+  const int64_t gtid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t item = gtid / kLanes;
+  const int sub = int(gtid % kLanes);
   const int64_t rows = a.delta_rows;
-  if (item >= rows * a.heads) return;
-  const int h = int(item / rows);
-  const int lrow = int(item % rows);
-  const int64_t grow = lrow < a.delta_split ? a.delta_lo + lrow : a.delta_hi + (lrow - a.delta_split);
-  const T* o = static_cast<const T*>(a.out) + (grow * a.heads + h) * D;
-  const T* d = static_cast<const T*>(a.dout) + (grow * a.heads + h) * D;
+  const bool ok = item < rows * a.heads;  // lanes past the end still join the shuffles
+  const int h = ok ? int(item / rows) : 0;
+  const int lrow = ok ? int(item % rows) : 0;
   float s = 0.f;
+  if (ok) {
+    const int64_t grow = lrow < a.delta_split ? a.delta_lo + lrow : a.delta_hi + (lrow - a.delta_split);
+    const int64_t off = (grow * a.heads + h) * D + sub * kVec;
+    typedef T tv __attribute__((ext_vector_type(kVec)));
+    const tv o = *reinterpret_cast<const tv*>(static_cast<const T*>(a.out) + off);
+    const tv d = *reinterpret_cast<const tv*>(static_cast<const T*>(a.dout) + off);
 #pragma unroll
-  for (int i = lane; i < D; i += 64) s += ld(o + i) * ld(d + i);
+    for (int i = 0; i < kVec; ++i) s = fmaf(static_cast<float>(o[i]), static_cast<float>(d[i]), s);
+  }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-  if (lane == 0) a.delta[int64_t(h) * a.n_loc + lrow] = s;
+  for (int m = kLanes / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if (ok && sub == 0) a.delta[int64_t(h) * a.n_loc + lrow] = s;
 }
 
 __device__ __forceinline__ int bwd_kv_row(const BwdArgs& a, int kk) {
@@ -271,9 +282,10 @@ hipError_t launch_generic(const BwdArgs& a, hipStream_t st) {
 
 template <typename T, int D>
 hipError_t launch_delta_t(const BwdArgs& a, hipStream_t st) {
-  const int64_t waves = a.delta_rows * a.heads;
-  if (waves == 0) return hipSuccess;
-  bwd_delta<T, D><<<unsigned((waves + 3) / 4), kThreads, 0, st>>>(a);
+  const int64_t items = a.delta_rows * a.heads;
+  if (items == 0) return hipSuccess;
+  const int64_t threads = items * (D / (16 / int64_t(sizeof(T))));
+  bwd_delta<T, D><<<unsigned((threads + kThreads - 1) / kThreads), kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
