@@ -85,7 +85,10 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
 #define CP_ATTN_OPT_STEP_TIMING 5 /* 1: time every ring step's attention kernel with HIP events */
 #define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel (default 256; 0: one
                                      workgroup per 128 vectors of 16 bytes); a small grid shares the
-                                     GPU with the attention kernel it overlaps */
+                                     GPU with the attention kernel it overlaps.  A receive that
+                                     overlaps no attention kernel (serial order, or a ring step
+                                     with no valid pair, e.g. under document masks) always takes
+                                     the full grid */
 #define CP_ATTN_OPT_GRAPH 7       /* 1: graph mode. A forward call is recorded once into a HIP graph
                                      (stream capture on a library stream) and replayed on the
                                      caller's stream while its buffers, rank, workspace, side streams

@@ -223,15 +223,18 @@ RecvArgs recv_ranges(Plan& p, const void* k, const void* v, int src, int b) {
   return ra;
 }
 
-// Side-stream receive of ring source `src` into slot b.
-int recv_kv(Plan& p, const void* k, const void* v, int src, int b, hipStream_t s) {
+// Side-stream receive of ring source `src` into slot b.  `alone`: no step
+// kernel runs beside it (serial order, or a step that launches nothing), so
+// the copy takes the whole chip instead of the few workgroups that leave the
+// step kernel its compute units.
+int recv_kv(Plan& p, const void* k, const void* v, int src, int b, bool alone, hipStream_t s) {
   const RecvArgs ra = recv_ranges(p, k, v, src, b);
   if (p.opt_recv == 1) {
     for (int i = 0; i < ra.n; ++i)
       CPA_HIP(hipMemcpyAsync(ra.dst[i], ra.src[i], size_t(ra.vec[i] * 16), hipMemcpyDeviceToDevice, s));
     return CP_ATTN_OK;
   }
-  CPA_HIP(launch_recv(ra, p.opt_recv_blocks, s));
+  CPA_HIP(launch_recv(ra, alone ? 0 : p.opt_recv_blocks, s));
   return CP_ATTN_OK;
 }
 
@@ -444,7 +447,7 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
       // slot nb was last read by step s-1
       const int nb = (s + 1) & 1;
       if (!serial && s >= 1) CPA_HIP(hipStreamWaitEvent(cs, d.attn_done[nb], 0));
-      CPA_TRY(recv_kv(p, k, v, p.step(r, s + 1).src, nb, cs));
+      CPA_TRY(recv_kv(p, k, v, p.step(r, s + 1).src, nb, serial || p.step(r, s).nseg == 0, cs));
       if (!serial) CPA_HIP(hipEventRecord(d.recv_done[nb], cs));
     }
     if (!serial && s >= 1 && side_recv(p, s - 1)) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
