@@ -13,7 +13,7 @@
  *   - the rank's queries stay resident while the K/V chunks of every rank pass
  *     by, one source rank per ring step (section 4 "What Actually Moves");
  *   - each step's partial result is folded into a running (O, LSE) state by
- *     log-sum-exp correction, which keeps the result exact (section 4);
+ *     log-sum-exp correction, which reproduces the unsplit result (section 4);
  *   - sub-blocks that the causal mask puts entirely in the future are skipped
  *     (section 4);
  *   - the next step's K/V is received while the current step computes
@@ -145,8 +145,12 @@ int cp_attn_set_option(cp_attn_plan_t plan, int option, int value);
  * fp32 running state (O, LSE), two fp32 partial buffers (separate merge mode,
  * or the two key halves of a split step), (n_loc/256 + 2) * heads int32
  * split counters and the document table (2 int32 per token), each rounded
- * up to 256 bytes.  The library zeroes the
- * counters once per workspace (synchronously, on the next forward call). */
+ * up to 256 bytes.  Everything but the document table is scratch: a call
+ * clears what must start at zero (the split counters, with a fill kernel on
+ * its own stream before the first step that splits), so the caller may reuse
+ * the memory between calls.  The document table is written once per
+ * document list (and again after cp_attn_set_workspace); while documents are
+ * set, the caller must not write that region between calls. */
 int cp_attn_workspace_bytes(cp_attn_plan_t plan, int64_t* bytes);
 
 /* Hand the plan caller-owned device memory of at least cp_attn_workspace_bytes
@@ -193,23 +197,26 @@ int cp_attn_set_documents(cp_attn_plan_t plan, const int64_t* starts, int64_t co
 int cp_attn_rank_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
                          float* lse, int rank, void* stream);
 
-/* All-gather variant of one rank's share: the rank's rows against the whole
- * natural-order K/V in a single launch of the step kernel (the K/V of every
- * rank at once, as after an all-gather), with no ring steps, no receive and no
- * merge; each owned chunk sees the keys before it (causal) or all keys
- * (bidirectional).  Same result as cp_attn_rank_forward up to rounding order.
- * Same arguments and errors as cp_attn_rank_forward, and EUNSUPPORTED when
- * the K/V tensors exceed 4 GiB.  Uses no workspace. */
+/* All-gather variant of one rank's share ("Context Parallelism in MegaDLMs",
+ * section "Key-Value Communication Patterns": the all_gather communication
+ * type, where every rank first collects the K/V of the whole sequence): the
+ * rank's rows against the whole natural-order K/V in a single launch of the
+ * step kernel, with no ring steps, no receive and no merge; each owned chunk
+ * sees the keys before it (causal) or all keys (bidirectional).  Same result
+ * as cp_attn_rank_forward up to rounding order.  Same arguments and errors as
+ * cp_attn_rank_forward, and EUNSUPPORTED when the K/V tensors exceed 4 GiB.
+ * Uses the workspace only for the document table, when documents are set
+ * (allocating it on first use unless the caller gave one). */
 int cp_attn_allgather_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
                               float* lse, int rank, void* stream);
 
 /*
  * Ulysses variant ("Sequence Parallelism IV: Megatron Context Parallel and
- * Load-Balanced Rings", section 7 "CP vs Ulysses"): an all-to-all moves the
- * ranks from sequence ownership to head ownership, after which a rank holds
- * every token of a slice of heads_per_rank = heads / cp_size heads and runs
- * plain attention on it; a second all-to-all moves the output back.  The
- * head count bounds the degree: both calls return EUNSUPPORTED unless
+ * Load-Balanced Rings", section 7 "CP vs Ulysses"): one all-to-all trades
+ * token slices for head slices, so that a rank holds all S tokens of
+ * heads_per_rank = heads / cp_size heads and runs plain attention on them;
+ * a second all-to-all returns the output to the token owners.  The degree
+ * cannot exceed the head count: both calls return EUNSUPPORTED unless
  * heads % cp_size == 0.
  *
  * cp_attn_ulysses_a2a: the all-to-all of every rank at once, plan dtype,
@@ -312,8 +319,10 @@ int cp_attn_layout_scatter(cp_attn_plan_t plan, const void* src, void* dst, void
  * o_acc, o_s: [rows][heads][head_dim]; lse_acc, lse_s: [heads][rows].
  * Per (row, head): lse_s = -inf leaves the state; lse_acc = -inf takes the
  * partial; otherwise lse' = max + log1p(exp(-|lse_acc - lse_s|)) and
- * O' = exp(lse_acc - lse') O_acc + exp(lse_s - lse') O_s.  Section 4 of the
- * same page: the online softmax state keeps the result exact.
+ * O' = exp(lse_acc - lse') O_acc + exp(lse_s - lse') O_s: two partials over
+ * disjoint key sets combine into the softmax over their union, so the split
+ * result equals the unsplit one ("Sequence Parallelism IV: Megatron Context
+ * Parallel and Load-Balanced Rings", section 4 "What Actually Moves").
  * head_dim must be a multiple of 4; pointers 16-byte aligned.
  */
 int cp_attn_lse_merge(float* o_acc, float* lse_acc, const float* o_s, const float* lse_s, int64_t rows,

@@ -23,8 +23,9 @@ This module has its own chunk map; it does not use the HIP library's plan.
   keys present; partials are folded with log-sum-exp weights, which reproduces
   the unsplit softmax exactly up to rounding.
 * Padding ("Context Parallelism for Long-Context Training", section "Test
-  sequence divisibility and padding": define pad ownership, mask padded keys
-  and queries; masked padding must not alter real-token outputs).  A length
+  sequence divisibility and padding": the page asks which rank holds each pad
+  token, that pad keys and pad queries be masked, and that adding them leave
+  every real token's output as it was).  A length
   that does not divide into the chunks is padded at the end to the next
   multiple; the pad positions belong to the rank that owns their chunk, are
   never attended as keys and produce no output.  ``rank_positions`` lists the

@@ -26,7 +26,7 @@ ARCH = "gfx950"
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 # gfx950 device code: no packed-fp32 instructions anywhere.
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-fno-gpu-rdc", "-munsafe-fp-atomics"]
+             "-fno-gpu-rdc"]
 
 
 def hipcc():

@@ -50,7 +50,6 @@ struct DeviceState {
   hipStream_t capture = nullptr;
   hipGraphExec_t graph = nullptr;
   std::vector<intptr_t> graph_key;
-  bool cnt_ready = false;  // the workspace's key-split counters are zero
   int64_t doc_uploaded = -1;  // plan doc_version whose document table the workspace holds
   int cus = 0;             // compute units of the device
   // work counters (CP_ATTN_OPT_COUNTERS): key tiles computed per (rank, step)
@@ -115,7 +114,11 @@ WsLayout ws_layout(const Plan& p) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int ensure_device(Plan& p) {
+// Device, streams and events of the plan; with need_ws also the workspace
+// (allocated on first use unless the caller gave one) and the document table
+// in it.  The single-launch forwards (all-gather, Ulysses) need the workspace
+// only for the document table.
+int ensure_device(Plan& p, bool need_ws = true) {
   DeviceState& d = *p.dev;
   int dev = 0;
   CPA_HIP(hipGetDevice(&dev));
@@ -140,6 +143,8 @@ int ensure_device(Plan& p) {
     CPA_HIP(hipStreamCreateWithFlags(&d.merge, hipStreamNonBlocking));
     d.own_merge = true;
   }
+  if (!d.cus) CPA_HIP(hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev));
+  if (!need_ws) return CP_ATTN_OK;
   const WsLayout w = ws_layout(p);
   if (d.ws && d.ws_bytes < w.total) {
     if (!d.own_ws) return fail(CP_ATTN_ENOWORKSPACE, "caller workspace smaller than cp_attn_workspace_bytes");
@@ -154,15 +159,7 @@ int ensure_device(Plan& p) {
     }
     d.ws_bytes = w.total;
     d.own_ws = true;
-    d.cnt_ready = false;
     d.doc_uploaded = -1;
-  }
-  if (!d.cnt_ready) {
-    // once per workspace: the key-split counters start at zero (the kernel
-    // that uses a counter resets it); synchronous, before any launch
-    CPA_HIP(hipMemset(static_cast<char*>(d.ws) + w.split_cnt, 0, size_t(w.cnt_bytes)));
-    CPA_HIP(hipDeviceSynchronize());
-    d.cnt_ready = true;
   }
   if (!p.doc_starts.empty() && d.doc_uploaded != p.doc_version) {
     // the document table of the current list: once per list and workspace,
@@ -179,7 +176,6 @@ int ensure_device(Plan& p) {
     CPA_HIP(hipMemcpy(static_cast<char*>(d.ws) + w.doc, tab.data(), size_t(w.doc_bytes), hipMemcpyHostToDevice));
     d.doc_uploaded = p.doc_version;
   }
-  if (!d.cus) CPA_HIP(hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev));
   if (p.opt_counters && !d.tile_cnt)
     CPA_HIP(hipMalloc(&d.tile_cnt, size_t(p.cp) * p.cp * sizeof(unsigned long long)));
   if (p.opt_step_timing && d.t0.empty()) {
@@ -264,6 +260,31 @@ void set_doc(const Plan& p, A& a, int j) {
   }
 }
 
+// Key split: when a step's workgroups would fill at most half the GPU, each
+// full segment's row tiles take two workgroups, one per half of the keys (the
+// partial buffers of the separate merge mode hold the parts).  Returns the
+// ksplit factor (1 or 2) of segment i of (r, s).
+int seg_ksplit(const Plan& p, int r, int s, int i) {
+  const StepDesc& sd = p.step(r, s);
+  const bool bf16 = p.dtype == CP_ATTN_BF16;
+  if (!p.opt_ksplit || p.opt_merge == 1 || !p.doc_starts.empty() || !attn_splits_keys(bf16, p.head_dim)) return 1;
+  const int bm = attn_bf16_block_m(p.head_dim);
+  int64_t wgs = 0;
+  for (int t = 0; t < sd.nseg; ++t) wgs += (sd.seg[t].q_len + bm - 1) / bm * p.heads;
+  if (2 * wgs > p.dev->cus) return 1;
+  const Segment& g = sd.seg[i];
+  // the kernel keeps a split row tile's parts in 128 KiB slots of the
+  // partial buffers, one per (256-row tile of the local rows, head)
+  return !g.diag && g.kv_full >= 16 * 64 && g.q_start % 256 == 0 && p.n_loc % 256 == 0 ? 2 : 1;
+}
+
+bool rank_splits(const Plan& p, int r) {
+  for (int s = 0; s < p.cp; ++s)
+    for (int i = 0; i < p.step(r, s).nseg; ++i)
+      if (seg_ksplit(p, r, s, i) > 1) return true;
+  return false;
+}
+
 // Step 0 reads the rank's own K/V in place (the rank holds them; nothing is
 // received); later steps read receive slot b.
 int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out, float* lse, int r, int s, int b,
@@ -313,13 +334,6 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
   a.nseg = sd.nseg;
   a.total_tiles = 0;
   const bool separate = p.opt_merge == 1;
-  // Key split: when the step's workgroups would fill at most half the GPU,
-  // each full segment's row tiles take two workgroups, one per half of the
-  // keys (the partial buffers of the separate merge mode hold the parts).
-  int64_t wgs = 0;
-  for (int i = 0; i < sd.nseg; ++i) wgs += (sd.seg[i].q_len + bm - 1) / bm * p.heads;
-  const bool key_split = p.opt_ksplit && !separate && p.doc_starts.empty() && attn_splits_keys(bf16, p.head_dim) &&
-                         2 * wgs <= d.cus;
   for (int b = 0; b < 2; ++b) {
     a.split_o[b] = reinterpret_cast<float*>(ws + w.part_o[b]);
     a.split_lse[b] = reinterpret_cast<float*>(ws + w.part_lse[b]);
@@ -334,9 +348,7 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
     x.kv_full = int32_t(g.kv_full);
     x.diag = g.diag;
     const int32_t qt = int32_t((g.q_len + bm - 1) / bm);
-    // the kernel keeps a split row tile's parts in 128 KiB slots of the
-    // partial buffers, one per (256-row tile of the local rows, head)
-    x.ksplit = key_split && !g.diag && g.kv_full >= 16 * 64 && g.q_start % 256 == 0 && p.n_loc % 256 == 0 ? 2 : 1;
+    x.ksplit = seg_ksplit(p, r, s, i);
     x.tiles = qt * x.ksplit;
     if (separate) {
       x.epi = g.first ? kEpiInit : kEpiPartial;
@@ -430,6 +442,13 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
     for (int s = 0; s < P; ++s) d.counted[size_t(r) * P + s] = 1;
   }
   if (p.valid_rows(r) == 0) return CP_ATTN_OK;  // a rank of pad tokens only: nothing to compute or write
+  if (rank_splits(p, r)) {
+    // The key split's per-tile counters: the kernels leave every counter they
+    // use at zero, but nothing stops a caller from writing its workspace
+    // between calls, so they are cleared (a kernel, so graph-safe) before any
+    // step of a rank that splits.
+    CPA_HIP(launch_fill_words(ws + w.split_cnt, split_counters(p), 0u, st));
+  }
   // cross-stream events only where another stream waits on them: each
   // record/wait pair costs microseconds of queue latency per step
   bool any_side = false;
@@ -795,7 +814,6 @@ int cp_attn_set_workspace(cp_attn_plan_t h, void* ptr, int64_t bytes) {
   d.ws = ptr;
   d.ws_bytes = ptr ? bytes : 0;
   d.own_ws = false;
-  d.cnt_ready = false;
   d.doc_uploaded = -1;
   return CP_ATTN_OK;
 }
@@ -850,7 +868,7 @@ int cp_attn_allgather_forward(cp_attn_plan_t h, const void* q, const void* k, co
   Plan& p = *h->p;
   if (rank < 0 || rank >= p.cp) return fail(CP_ATTN_EINVAL, "rank outside [0, cp_size)");
   CPA_TRY(check_io(q, k, v, out, lse));
-  CPA_TRY(ensure_device(p));
+  CPA_TRY(ensure_device(p, !p.doc_starts.empty()));
   const bool bf16 = p.dtype == CP_ATTN_BF16;
   const int bm = bf16 ? attn_bf16_block_m(p.head_dim) : attn_f32_block_m();
   if (p.seq_len * p.heads * p.head_dim * p.elem_bytes() > int64_t(UINT32_MAX))
@@ -908,7 +926,7 @@ int cp_attn_ulysses_a2a(cp_attn_plan_t h, const void* src, void* dst, int to_hea
   if (!src || !dst) return fail(CP_ATTN_EINVAL, "src or dst is null");
   if (!aligned16(src) || !aligned16(dst)) return fail(CP_ATTN_EINVAL, "src or dst not 16-byte aligned");
   if (to_heads != 0 && to_heads != 1) return fail(CP_ATTN_EINVAL, "to_heads must be 0 or 1");
-  CPA_TRY(ensure_device(p));
+  CPA_TRY(ensure_device(p, false));
   UlyssesArgs u{};
   u.src = src;
   u.dst = dst;
@@ -935,7 +953,7 @@ int cp_attn_ulysses_forward(cp_attn_plan_t h, const void* q, const void* k, cons
   const int32_t group = p.heads / p.cp;
   if (p.seq_len * group * p.head_dim * p.elem_bytes() > int64_t(UINT32_MAX))
     return fail(CP_ATTN_EUNSUPPORTED, "a head slice beyond 4 GiB");
-  CPA_TRY(ensure_device(p));
+  CPA_TRY(ensure_device(p, !p.doc_starts.empty()));
   const bool bf16 = p.dtype == CP_ATTN_BF16;
   const int bm = bf16 ? attn_bf16_block_m(p.head_dim) : attn_f32_block_m();
   StepArgs a{};

@@ -2,8 +2,9 @@
 // (normalised O_s, lse_s) into the running state, a partial, or the output.
 //
 // Exact merge ("Sequence Parallelism IV: Megatron Context Parallel and
-// Load-Balanced Rings", section 4 "What Actually Moves": the online softmax
-// state keeps the result exact across block updates).  In (O, LSE) form:
+// Load-Balanced Rings", section 4 "What Actually Moves": carrying the running
+// max and sum from block to block makes the split computation equal the
+// unsplit softmax).  In (O, LSE) form:
 //   lse' = max(a, b) + log1p(exp(-|a - b|)),
 //   O'   = exp(a - lse') O_acc + exp(b - lse') O_s,
 // where a = lse_acc, b = lse_s; an empty state (a = -inf) takes the partial.

@@ -54,8 +54,8 @@ __global__ __launch_bounds__(kThreads) void layout_copy(LayoutArgs a) {
 }
 
 // Ulysses all-to-all ("Sequence Parallelism IV: Megatron Context Parallel and
-// Load-Balanced Rings", section 7 "CP vs Ulysses": the transpose from
-// sequence ownership to head ownership).  A (head owner r', token t) row of
+// Load-Balanced Rings", section 7 "CP vs Ulysses": ranks trade their token
+// slices so that each ends up with all tokens of a subset of heads).  A (head owner r', token t) row of
 // the head layout -- the H/cp heads of token t that r' receives -- is one
 // contiguous run of `run` 16-byte vectors in the sequence owner's local row,
 // so both sides move whole vectors.  Each thread moves one vector of a row

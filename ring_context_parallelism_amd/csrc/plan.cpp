@@ -8,9 +8,9 @@
 // moves K/V to a neighbour each step; rank r receives from r-1, so at step s
 // it holds the K/V of source j = (r - s) mod cp.
 //
-// Causal step descriptors (section 4: the mask must know which local query
-// positions and remote key positions are valid; future sub-blocks are
-// skipped).  For a query chunk a and key chunk b of equal length, the pair is
+// Causal step descriptors (section 4: a step's mask is decided by the global
+// positions of the rank's own queries and of the visiting keys, and key
+// blocks wholly in a query block's future are not computed).  For a query chunk a and key chunk b of equal length, the pair is
 // fully visible if b < a, causal on the diagonal if b == a, and skipped if
 // b > a.  With a in {r, 2cp-1-r} and b in {j, 2cp-1-j}:
 //   j == r : (r, r) diagonal; (2cp-1-r, r) full; (2cp-1-r, 2cp-1-r) diagonal;

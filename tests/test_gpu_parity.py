@@ -286,6 +286,87 @@ def test_full_workload_sampled(name, recv):
         assert torch.equal(out[0], v[0])
 
 
+# ------------------------------------------------- full workloads (whole) --
+
+def _compare_heads(out, lse, q, k, v, causal, rows, heads):
+    """max |dO|, max |dLSE| over the given rows of the given heads, upcasting
+    one head at a time (the full tensors would take gigabytes in fp64)."""
+    rows_t = torch.from_numpy(rows)
+    d_o = d_l = 0.0
+    for h in heads:
+        o_ref, l_ref = oracle.attention(to_numpy_f64(q[rows_t, h:h + 1]), to_numpy_f64(k[:, h:h + 1]),
+                                        to_numpy_f64(v[:, h:h + 1]), causal=causal, q_pos=rows)
+        o_got = out[rows_t, h:h + 1].to(torch.float64).numpy()
+        l_got = lse[h, rows_t].to(torch.float64).numpy()
+        assert np.all(np.isfinite(o_got)) and np.all(np.isfinite(l_got))
+        d_o = max(d_o, float(np.max(np.abs(o_got - o_ref))))
+        d_l = max(d_l, float(np.max(np.abs(l_got - l_ref[0]))))
+    return d_o, d_l
+
+
+@pytest.mark.parametrize("name", ["causal_s8192_cp4_zigzag_h32_d128_bf16",
+                                  "causal_s32768_cp8_zigzag_h32_d128_bf16_rank0",
+                                  "bidir_s65536_cp16_contiguous_h8_d128_bf16_rank0"])
+def test_whole_share_first_and_last_head(name):
+    """Every row of the share (all ranks of the 8192-token workload; rank 0's
+    4096 rows of the 32768- and 65536-token ones) on the first and the last
+    head, in the launch configuration the bench times."""
+    w = WORKLOADS[name]
+    _say(f"whole share {name}")
+    q, k, v = workload_qkv(w)
+    p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout)
+    out, lse = _run(p, q, k, v, rank=w.rank)
+    p.close()
+    ranks = range(w.cp) if w.rank is None else [w.rank]
+    rows = np.sort(np.concatenate([oracle.rank_positions(w.seq_len, w.cp, r, w.layout) for r in ranks]))
+    d_o, d_l = _compare_heads(out, lse, q, k, v, w.causal, rows, [0, w.heads - 1])
+    _say(f"  rows={rows.size} heads=[0, {w.heads - 1}] max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= 2e-2 and d_l <= 1e-3
+    if w.causal:
+        assert torch.equal(out[0], v[0])
+
+
+def test_key_split_full_size_bit_identical():
+    """The 16384-token, cp 4, 16-head workload: its steps of C rows x 2C keys
+    fill half the GPU, so they split their keys over two workgroups.  Three
+    calls agree bit for bit whichever half finishes first, and every row of
+    the first and last head matches the oracle."""
+    w = WORKLOADS["causal_s16384_cp4_zigzag_h16_d128_bf16"]
+    _say(f"key split, full size: {w.name}")
+    q, k, v = workload_qkv(w)
+    p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout)
+    p.set_counters(True)
+    runs = [_run(p, q, k, v) for _ in range(3)]
+    counts, (tr, tk) = p.last_tile_counts()
+    for r in range(w.cp):
+        for s in range(w.cp):
+            assert counts[r][s] == w.heads * p.valid_work(r, s, tr, tk)[0]
+    p.close()
+    for o, l in runs[1:]:
+        assert _bitwise_equal(o, runs[0][0]) and _bitwise_equal(l, runs[0][1])
+    d_o, d_l = _compare_heads(runs[0][0], runs[0][1], q, k, v, True, np.arange(w.seq_len), [0, w.heads - 1])
+    _say(f"  max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= 2e-2 and d_l <= 1e-3
+
+
+def test_workspace_overwritten_between_calls():
+    """A caller-owned workspace is scratch between calls: filling it with
+    garbage (the key-split counters included) between two calls leaves the
+    result bit-identical."""
+    seq, cp, heads = 8192, 4, 4
+    _say(f"workspace overwritten between calls seq={seq} cp={cp} heads={heads}")
+    q, k, v = make_qkv(seq, heads, 128, "bf16", 42)
+    p = Plan(seq, cp, heads, 128, True, "zigzag")
+    ws = torch.empty(p.workspace_bytes(), dtype=torch.uint8, device=_dev())
+    p.set_workspace(ws)
+    first = _run(p, q, k, v)
+    for fill in (0xFF, 0x01):
+        ws.fill_(fill)
+        again = _run(p, q, k, v)
+        assert _bitwise_equal(again[0], first[0]) and _bitwise_equal(again[1], first[1])
+    p.close()
+
+
 # ------------------------------------------------------------- key split ----
 
 @pytest.mark.parametrize("layout,seq,cp,heads,causal", [("zigzag", 8192, 4, 4, True),

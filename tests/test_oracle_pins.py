@@ -427,6 +427,70 @@ def test_imbalance_contiguous_cp4_and_zigzag_at_16k_tile128():
     assert oracle.imbalance(pz) == ([1.0] * cp, 1.0)
 
 
+def _tiles_brute(seq, cp, layout, causal, rank, step, bm, bn):
+    """Pure-Python tile count: every bm x bn tile of the local row and key
+    indices (laid from 0, the last one clipped), kept when one of its pairs is
+    valid (key position not after the query's, or any pair when bidirectional)."""
+    qpos = [int(x) for x in oracle.rank_positions(seq, cp, rank, layout)]
+    kpos = [int(x) for x in oracle.rank_positions(seq, cp, oracle.ring_source(rank, step, cp), layout)]
+    n = 0
+    for i0 in range(0, len(qpos), bm):
+        for j0 in range(0, len(kpos), bn):
+            if any((not causal) or kk <= qq for qq in qpos[i0:i0 + bm] for kk in kpos[j0:j0 + bn]):
+                n += 1
+    return n
+
+
+# Bidirectional tiles at lengths that divide neither the chunks nor the tiles,
+# worked out by hand: (seq, cp, layout, bm, bn) -> {(rank, step): tiles}.
+#   100 tokens, cp 3 contiguous: padded to 102, chunks of 34; real rows 34, 34, 32;
+#     3 x 3 row/key tiles of 16 for a 34-row rank against a 34-key source, 3 x 2
+#     against the 32-key one, 2 x 3 and 2 x 2 for the 32-row rank.
+#   50 tokens, cp 2 zigzag: padded to 52, chunks of 13; rank 0 holds 0..12 and
+#     39..49 (24 real rows), rank 1 holds 13..38 (26 rows); tiles of 8:
+#     ceil(24/8) = 3, ceil(26/8) = 4.
+BIDIR_TILES = {
+    (100, 3, "contiguous", 16, 16): {(0, 0): 9, (0, 1): 6, (0, 2): 9, (2, 0): 4, (2, 1): 6, (2, 2): 6},
+    (50, 2, "zigzag", 8, 8): {(0, 0): 9, (0, 1): 12, (1, 0): 16, (1, 1): 12},
+}
+
+
+@pytest.mark.parametrize("key", list(BIDIR_TILES))
+def test_bidirectional_tiles_by_hand(key):
+    """The bidirectional branch of step_valid_tiles (a product of tile counts
+    per axis) against hand-counted tiles at ragged sizes, where a floor in
+    place of a ceiling drops the clipped last tile."""
+    seq, cp, layout, bm, bn = key
+    for (r, s), want in BIDIR_TILES[key].items():
+        assert oracle.step_valid_tiles(seq, cp, layout, False, r, s, bm, bn) == want, (r, s)
+        assert _tiles_brute(seq, cp, layout, False, r, s, bm, bn) == want, (r, s)
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_tiles_equal_brute_force_at_awkward_lengths(layout, causal):
+    for seq, cp, bm, bn in [(37, 3, 4, 8), (50, 2, 8, 8), (61, 4, 3, 5), (100, 3, 16, 16), (24, 2, 32, 32)]:
+        for r in range(cp):
+            for s in range(cp):
+                want = _tiles_brute(seq, cp, layout, causal, r, s, bm, bn)
+                assert oracle.step_valid_tiles(seq, cp, layout, causal, r, s, bm, bn) == want, (seq, cp, r, s)
+
+
+def test_planted_floor_in_bidirectional_tiles_is_caught(monkeypatch):
+    """Counting only whole tiles (floor for ceiling) fails the hand-counted table."""
+    real = cp_reference.step_valid_tiles
+
+    def floored(seq_len, cp, layout, causal, rank, step, bm, bn):
+        if causal:
+            return real(seq_len, cp, layout, causal, rank, step, bm, bn)
+        nq = cp_reference.rank_positions(seq_len, cp, rank, layout).size
+        nk = cp_reference.rank_positions(seq_len, cp, cp_reference.ring_source(rank, step, cp), layout).size
+        return (nq // bm) * (nk // bn)
+    monkeypatch.setattr(oracle, "step_valid_tiles", floored)
+    with pytest.raises(AssertionError):
+        test_bidirectional_tiles_by_hand((100, 3, "contiguous", 16, 16))
+
+
 def test_valid_flops_formula():
     assert oracle.valid_flops(1, 1, 128) == 512
     c = 2048  # rank 0 of the 32k, cp 8 share: 16 C^2 + C pairs per head
