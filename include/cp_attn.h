@@ -237,6 +237,28 @@ int cp_attn_ulysses_a2a(cp_attn_plan_t plan, const void* src, void* dst, int to_
 int cp_attn_ulysses_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out, float* lse,
                             void* stream);
 
+/*
+ * cp_attn_rank_forward without any allocation, for callers that cannot
+ * allocate device memory or create streams: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * result (bit for bit) and errors as cp_attn_rank_forward, but the workspace
+ * is a static device array of the library, CP_ATTN_NOALLOC_SCRATCH_BYTES per
+ * GPU, held on every GPU the library runs on until the process ends.  The
+ * plan's workspace, side streams, events, graph mode, step timing and work
+ * counters are not used: every kernel runs on `stream` (the next ring
+ * step's K/V is received inside the step kernel where it supports that,
+ * otherwise by a copy kernel before the step), so the call can be captured
+ * into a HIP graph.  The array keeps the last call's contents; what must
+ * start at zero is cleared by the call itself.  All calls on one GPU share
+ * the array: calls in flight on that GPU at the same time (any plan, any
+ * stream) race, so the caller must order them.
+ * ENOWORKSPACE when cp_attn_workspace_bytes exceeds the array; EUNSUPPORTED
+ * while document masks are set; otherwise as cp_attn_rank_forward.
+ */
+#define CP_ATTN_NOALLOC_SCRATCH_BYTES (128LL << 20)
+int cp_attn_rank_forward_noalloc(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
+                                 float* lse, int rank, void* stream);
+
 /* Every rank's share back to back on `stream` (ranks 0..cp_size-1); fills all
  * rows of out and lse.  Same arguments and errors as cp_attn_rank_forward. */
 int cp_attn_full_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,

@@ -34,6 +34,8 @@ OPT_GRAPH = 7
 OPT_KSPLIT = 8
 OPT_COUNTERS = 9
 
+NOALLOC_SCRATCH_BYTES = 128 << 20  # CP_ATTN_NOALLOC_SCRATCH_BYTES
+
 _c_p = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -50,6 +52,7 @@ SIGNATURES = {
     "cp_attn_set_streams": (ctypes.c_int, [_c_p, _c_p, _c_p]),
     "cp_attn_set_documents": (ctypes.c_int, [_c_p, ctypes.POINTER(_i64), _i64]),
     "cp_attn_rank_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_p]),
+    "cp_attn_rank_forward_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_p]),
     "cp_attn_full_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "cp_attn_ulysses_a2a": (ctypes.c_int, [_c_p, _c_p, _c_p, ctypes.c_int, _c_p]),
     "cp_attn_ulysses_forward": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),

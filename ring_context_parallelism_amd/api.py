@@ -130,6 +130,14 @@ class Plan:
         N.check(self.lib.cp_attn_rank_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(rank),
                                               _stream_ptr(stream)), "cp_attn_rank_forward")
 
+    def rank_forward_noalloc(self, q, k, v, out, lse, rank, stream=None):
+        """rank_forward on the library's static device scratch: no allocation,
+        every kernel on ``stream`` (graph-capturable).  Calls on one GPU share
+        the scratch, so calls in flight at the same time race."""
+        self._check_io(q, k, v, out, lse)
+        N.check(self.lib.cp_attn_rank_forward_noalloc(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                                      int(rank), _stream_ptr(stream)), "cp_attn_rank_forward_noalloc")
+
     def allgather_forward(self, q, k, v, out, lse, rank, stream=None):
         self._check_io(q, k, v, out, lse)
         N.check(self.lib.cp_attn_allgather_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(rank),

@@ -15,8 +15,10 @@
 //   merge(s)                   waits attn_done[s&1]
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -190,15 +192,38 @@ int ensure_device(Plan& p, bool need_ws = true) {
   return CP_ATTN_OK;
 }
 
+// What one forward call runs with: the workspace base and the schedule.  A
+// plain call takes both from the plan; the no-allocation entry point runs the
+// same steps on the library's static scratch, on the caller's stream only.
+struct RunCfg {
+  char* ws = nullptr;      // workspace base (ws_layout offsets apply)
+  bool serial = false;     // every step on the caller's stream, no events
+  int recv = 0;            // CP_ATTN_OPT_RECV in effect
+  int recv_blocks = 256;   // CP_ATTN_OPT_RECV_BLOCKS in effect
+  bool counters = false;   // device work counters (plan-owned buffer)
+  bool timing = false;     // per-step timing events
+  bool poison = false;     // NaN-fill consumed buffers
+};
+
+RunCfg plan_cfg(const Plan& p, bool capturing) {
+  RunCfg c;
+  c.ws = static_cast<char*>(p.dev->ws);
+  c.serial = p.opt_serialize != 0;
+  c.recv = p.opt_recv;
+  c.recv_blocks = p.opt_recv_blocks;
+  c.counters = p.opt_counters != 0;
+  c.timing = p.opt_step_timing != 0 && !capturing;
+  c.poison = p.opt_poison != 0;
+  return c;
+}
+
 // The K and V rows of ring source `src` (its local order) are one (contiguous)
 // or two (zigzag) token ranges of the natural-order tensors; receiving them
 // into slot b is two or four linear copies.  Only real rows are received: a
 // chunk's pad rows (and a chunk of pad only) are not copied, and the kernels
 // never read past the source's real keys.
-RecvArgs recv_ranges(Plan& p, const void* k, const void* v, int src, int b) {
-  DeviceState& d = *p.dev;
+RecvArgs recv_ranges(const Plan& p, char* ws, const void* k, const void* v, int src, int b) {
   const WsLayout w = ws_layout(p);
-  char* ws = static_cast<char*>(d.ws);
   char* dk = ws + w.slot_k[b];
   char* dv = ws + w.slot_v[b];
   const int64_t row_bytes = int64_t(p.heads) * p.head_dim * p.elem_bytes();
@@ -223,32 +248,33 @@ RecvArgs recv_ranges(Plan& p, const void* k, const void* v, int src, int b) {
 // kernel runs beside it (serial order, or a step that launches nothing), so
 // the copy takes the whole chip instead of the few workgroups that leave the
 // step kernel its compute units.
-int recv_kv(Plan& p, const void* k, const void* v, int src, int b, bool alone, hipStream_t s) {
-  const RecvArgs ra = recv_ranges(p, k, v, src, b);
-  if (p.opt_recv == 1) {
+int recv_kv(const Plan& p, const RunCfg& c, const void* k, const void* v, int src, int b, bool alone,
+            hipStream_t s) {
+  const RecvArgs ra = recv_ranges(p, c.ws, k, v, src, b);
+  if (c.recv == 1) {
     for (int i = 0; i < ra.n; ++i)
       CPA_HIP(hipMemcpyAsync(ra.dst[i], ra.src[i], size_t(ra.vec[i] * 16), hipMemcpyDeviceToDevice, s));
     return CP_ATTN_OK;
   }
-  CPA_HIP(launch_recv(ra, alone ? 0 : p.opt_recv_blocks, s));
+  CPA_HIP(launch_recv(ra, alone ? 0 : c.recv_blocks, s));
   return CP_ATTN_OK;
 }
 
 // Whether step s's attention kernel itself receives step s+1's K/V (mode 2
 // at every step; mode 3 from step 1 on, step 0's receive going through the
 // copy stream), and whether step s's receive runs on the copy stream.
-bool kernel_recv(const Plan& p, int s) {
+bool kernel_recv(const Plan& p, const RunCfg& c, int s) {
   if (s + 1 >= p.cp || !attn_does_recv(p.dtype == CP_ATTN_BF16, p.head_dim)) return false;
-  return p.opt_recv == 2 || (p.opt_recv == 3 && s >= 1);
+  return c.recv == 2 || (c.recv == 3 && s >= 1);
 }
-bool side_recv(const Plan& p, int s) { return s + 1 < p.cp && !kernel_recv(p, s); }
+bool side_recv(const Plan& p, const RunCfg& c, int s) { return s + 1 < p.cp && !kernel_recv(p, c, s); }
 
 // Document masks of a launch whose keys are source j's local buffer (j < 0:
 // the identity map, keys at their own positions).  A is StepArgs or BwdArgs.
 template <typename A>
-void set_doc(const Plan& p, A& a, int j) {
+void set_doc(const Plan& p, const char* ws, A& a, int j) {
   if (p.doc_starts.empty()) return;
-  a.doc = reinterpret_cast<const int32_t*>(static_cast<const char*>(p.dev->ws) + ws_layout(p).doc);
+  a.doc = reinterpret_cast<const int32_t*>(ws + ws_layout(p).doc);
   if (j < 0) {
     a.kpos_lo = 0;
     a.kpos_hi = 0;
@@ -287,16 +313,16 @@ bool rank_splits(const Plan& p, int r) {
 
 // Step 0 reads the rank's own K/V in place (the rank holds them; nothing is
 // received); later steps read receive slot b.
-int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out, float* lse, int r, int s, int b,
-                hipStream_t st) {
+int launch_step(Plan& p, const RunCfg& c, const void* q, const void* k, const void* v, void* out, float* lse, int r,
+                int s, int b, hipStream_t st) {
   DeviceState& d = *p.dev;
   const WsLayout w = ws_layout(p);
-  char* ws = static_cast<char*>(d.ws);
+  char* ws = c.ws;
   const StepDesc& sd = p.step(r, s);
   const bool bf16 = p.dtype == CP_ATTN_BF16;
   if (sd.nseg == 0) {
     // no query row of this rank sees the step's keys; the receive still happens
-    if (kernel_recv(p, s)) CPA_HIP(launch_recv(recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1), 0, st));
+    if (kernel_recv(p, c, s)) CPA_HIP(launch_recv(recv_ranges(p, ws, k, v, p.step(r, s + 1).src, (s + 1) & 1), 0, st));
     return CP_ATTN_OK;
   }
   const int bm = bf16 ? attn_bf16_block_m(p.head_dim) : attn_f32_block_m();
@@ -358,19 +384,17 @@ int launch_step(Plan& p, const void* q, const void* k, const void* v, void* out,
     a.total_tiles += x.tiles;
   }
   if (sd.nseg == 1) a.seg[1] = SegArgs{};
-  if (kernel_recv(p, s)) a.recv = recv_ranges(p, k, v, p.step(r, s + 1).src, (s + 1) & 1);
-  if (p.opt_counters) a.tile_cnt = d.tile_cnt + size_t(r) * p.cp + s;
-  set_doc(p, a, sd.src);
+  if (kernel_recv(p, c, s)) a.recv = recv_ranges(p, ws, k, v, p.step(r, s + 1).src, (s + 1) & 1);
+  if (c.counters) a.tile_cnt = d.tile_cnt + size_t(r) * p.cp + s;
+  set_doc(p, ws, a, sd.src);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
   return CP_ATTN_OK;
 }
 
 // Separate-merge mode: fold part[b] of step (r, s) into the running state.
-int launch_step_merge(Plan& p, int r, int s, int b, hipStream_t ms) {
-  DeviceState& d = *p.dev;
+int launch_step_merge(Plan& p, char* ws, int r, int s, int b, hipStream_t ms) {
   const WsLayout w = ws_layout(p);
-  char* ws = static_cast<char*>(d.ws);
   const StepDesc& sd = p.step(r, s);
   MergeArgs m{};
   m.o_s = reinterpret_cast<const float*>(ws + w.part_o[b]);
@@ -391,10 +415,8 @@ int launch_step_merge(Plan& p, int r, int s, int b, hipStream_t ms) {
   return CP_ATTN_OK;
 }
 
-int launch_rank_finalize(Plan& p, void* out, float* lse, int r, hipStream_t st) {
-  DeviceState& d = *p.dev;
+int launch_rank_finalize(Plan& p, const char* ws, void* out, float* lse, int r, hipStream_t st) {
   const WsLayout w = ws_layout(p);
-  char* ws = static_cast<char*>(d.ws);
   FinalizeArgs f{};
   f.acc_o = reinterpret_cast<const float*>(ws + w.acc_o);
   f.acc_lse = reinterpret_cast<const float*>(ws + w.acc_lse);
@@ -425,18 +447,18 @@ int launch_rank_finalize(Plan& p, void* out, float* lse, int r, hipStream_t st) 
     if (rc_ != CP_ATTN_OK) return rc_; \
   } while (0)
 
-int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, float* lse, int r, hipStream_t st,
-             bool capturing = false) {
+int run_rank(Plan& p, const RunCfg& c, const void* q, const void* k, const void* v, void* out, float* lse, int r,
+             hipStream_t st) {
   DeviceState& d = *p.dev;
   const WsLayout w = ws_layout(p);
-  char* ws = static_cast<char*>(d.ws);
+  char* ws = c.ws;
   const int P = p.cp;
-  const bool serial = p.opt_serialize != 0;
+  const bool serial = c.serial;
   const bool separate = p.opt_merge == 1;
   hipStream_t cs = serial ? st : d.copy;
   hipStream_t ms = serial ? st : d.merge;
 
-  if (p.opt_counters) {
+  if (c.counters) {
     // this rank's work counters start at zero (a kernel: graph-safe)
     CPA_HIP(launch_fill_words(d.tile_cnt + size_t(r) * P, int64_t(P) * 2, 0u, st));
     for (int s = 0; s < P; ++s) d.counted[size_t(r) * P + s] = 1;
@@ -452,7 +474,7 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
   // cross-stream events only where another stream waits on them: each
   // record/wait pair costs microseconds of queue latency per step
   bool any_side = false;
-  for (int s = 0; s < P; ++s) any_side = any_side || side_recv(p, s);
+  for (int s = 0; s < P; ++s) any_side = any_side || side_recv(p, c, s);
   const bool copy_side = !serial && any_side;
   const bool merge_side = !serial && separate;
   if (copy_side || merge_side) {
@@ -462,36 +484,35 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
   }
   for (int s = 0; s < P; ++s) {
     const int b = s & 1;
-    if (side_recv(p, s)) {
+    if (side_recv(p, c, s)) {
       // slot nb was last read by step s-1
       const int nb = (s + 1) & 1;
       if (!serial && s >= 1) CPA_HIP(hipStreamWaitEvent(cs, d.attn_done[nb], 0));
-      CPA_TRY(recv_kv(p, k, v, p.step(r, s + 1).src, nb, serial || p.step(r, s).nseg == 0, cs));
+      CPA_TRY(recv_kv(p, c, k, v, p.step(r, s + 1).src, nb, serial || p.step(r, s).nseg == 0, cs));
       if (!serial) CPA_HIP(hipEventRecord(d.recv_done[nb], cs));
     }
-    if (!serial && s >= 1 && side_recv(p, s - 1)) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
+    if (!serial && s >= 1 && side_recv(p, c, s - 1)) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
     // part[b] is free once the merge of step s-2 has read it (step 0 writes
     // the running state directly and has no merge)
     if (separate && !serial && s >= 3) CPA_HIP(hipStreamWaitEvent(st, d.merge_done[b], 0));
     const size_t ti = size_t(r) * P + s;
-    const bool timing = p.opt_step_timing && !capturing;
-    if (timing) CPA_HIP(hipEventRecord(d.t0[ti], st));
-    CPA_TRY(launch_step(p, q, k, v, out, lse, r, s, b, st));
-    if (timing) {
+    if (c.timing) CPA_HIP(hipEventRecord(d.t0[ti], st));
+    CPA_TRY(launch_step(p, c, q, k, v, out, lse, r, s, b, st));
+    if (c.timing) {
       CPA_HIP(hipEventRecord(d.t1[ti], st));
       d.timed[ti] = 1;
     }
-    if (p.opt_poison && s >= 1) {
+    if (c.poison && s >= 1) {
       CPA_HIP(launch_poison(ws + w.slot_k[b], w.kv_bytes, st));
       CPA_HIP(launch_poison(ws + w.slot_v[b], w.kv_bytes, st));
     }
     // the copy stream's receive at step s+1 waits for this step; so does the
     // merge stream
-    if ((!serial && side_recv(p, s + 1)) || merge_side) CPA_HIP(hipEventRecord(d.attn_done[b], st));
+    if ((!serial && side_recv(p, c, s + 1)) || merge_side) CPA_HIP(hipEventRecord(d.attn_done[b], st));
     if (separate && s > 0) {
       if (!serial) CPA_HIP(hipStreamWaitEvent(ms, d.attn_done[b], 0));
-      CPA_TRY(launch_step_merge(p, r, s, b, ms));
-      if (p.opt_poison) {
+      CPA_TRY(launch_step_merge(p, ws, r, s, b, ms));
+      if (c.poison) {
         CPA_HIP(launch_poison(ws + w.part_o[b], w.o_bytes, ms));
         CPA_HIP(launch_poison(ws + w.part_lse[b], w.lse_bytes, ms));
       }
@@ -503,7 +524,7 @@ int run_rank(Plan& p, const void* q, const void* k, const void* v, void* out, fl
       CPA_HIP(hipEventRecord(d.merge_join, ms));
       CPA_HIP(hipStreamWaitEvent(st, d.merge_join, 0));
     }
-    CPA_TRY(launch_rank_finalize(p, out, lse, r, st));
+    CPA_TRY(launch_rank_finalize(p, ws, out, lse, r, st));
   }
   return CP_ATTN_OK;
 }
@@ -533,6 +554,34 @@ void reset_timing(Plan& p) {
   d.counted.assign(size_t(p.cp) * p.cp, 0);
 }
 
+// ---- the no-allocation forward ----
+// The workspace of cp_attn_rank_forward_noalloc: a file-scope device array.
+// Each GPU the library runs on holds its own copy, at its own address, until
+// the process ends.  On the host, `scratch` names a host-side stand-in, not
+// device memory: host code uses only the address hipGetSymbolAddress returns
+// for the current device (scratch_base), never the array's name.
+constexpr int64_t kScratchBytes = CP_ATTN_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on device `dev` (the current device), looked up
+// once per device and kept.
+int scratch_base(int dev, char** out) {
+  static std::mutex mu;
+  static void* base[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return fail(CP_ATTN_EUNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!base[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(CP_ATTN_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    base[dev] = ptr;
+  }
+  *out = static_cast<char*>(base[dev]);
+  return CP_ATTN_OK;
+}
+
 void drop_graph(DeviceState& d) {
   if (d.graph) (void)hipGraphExecDestroy(d.graph);
   d.graph = nullptr;
@@ -558,7 +607,7 @@ int run_graph(Plan& p, const void* q, const void* k, const void* v, void* out, f
     CPA_HIP(hipStreamBeginCapture(d.capture, hipStreamCaptureModeThreadLocal));
     int rc = CP_ATTN_OK;
     for (int r = rank < 0 ? 0 : rank; r < (rank < 0 ? p.cp : rank + 1) && rc == CP_ATTN_OK; ++r)
-      rc = run_rank(p, q, k, v, out, lse, r, d.capture, true);
+      rc = run_rank(p, plan_cfg(p, true), q, k, v, out, lse, r, d.capture);
     hipGraph_t g = nullptr;
     const hipError_t ec = hipStreamEndCapture(d.capture, &g);
     if (rc != CP_ATTN_OK) {
@@ -657,7 +706,7 @@ int run_rank_backward(Plan& p, const void* q, const void* k, const void* v, cons
       maxpre = std::max<int64_t>(maxpre, g.kv_full + (g.diag ? g.q_len : 0));
     }
     a.key_tiles = int32_t((maxpre + bt_keys - 1) / bt_keys);
-    set_doc(p, a, j);
+    set_doc(p, ws, a, j);
     const hipError_t e = bwd_mfma(bf16, p.head_dim) ? launch_bwd_bf16_d128(a, st)
                                                     : launch_bwd_generic(a, bf16, p.head_dim, st);
     if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("backward launch: ") + hipGetErrorString(e));
@@ -852,7 +901,7 @@ int cp_attn_rank_forward(cp_attn_plan_t h, const void* q, const void* k, const v
   reset_timing(p);
   // (a rank of pad tokens only has nothing to record)
   if (p.opt_graph && p.valid_rows(rank) > 0) return run_graph(p, q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
-  return run_rank(p, q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
+  return run_rank(p, plan_cfg(p, false), q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
   CPA_GUARD_END
 }
 
@@ -907,7 +956,7 @@ int cp_attn_allgather_forward(cp_attn_plan_t h, const void* q, const void* k, co
     a.total_tiles += x.tiles;
   }
   if (a.nseg == 0) return CP_ATTN_OK;  // a rank of pad only
-  set_doc(p, a, -1);
+  set_doc(p, static_cast<const char*>(p.dev->ws), a, -1);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
@@ -984,11 +1033,50 @@ int cp_attn_ulysses_forward(cp_attn_plan_t h, const void* q, const void* k, cons
   x.tiles = int32_t((p.seq_len + bm - 1) / bm);
   x.epi = kEpiInit | kEpiFinal;
   a.total_tiles = x.tiles;
-  set_doc(p, a, -1);
+  set_doc(p, static_cast<const char*>(p.dev->ws), a, -1);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
   return CP_ATTN_OK;
+  CPA_GUARD_END
+}
+
+// The same steps as cp_attn_rank_forward on the static scratch, without any
+// allocation: no plan workspace, no side streams or events (every kernel on
+// the caller's stream, the ring receive inside the step kernels where they
+// support it, else a full-grid copy kernel before the step), no step timing
+// or work counters.  The key-split counters are cleared by run_rank's fill
+// kernel; every other scratch region is written before it is read.
+int cp_attn_rank_forward_noalloc(cp_attn_plan_t h, const void* q, const void* k, const void* v, void* out,
+                                 float* lse, int rank, void* stream) {
+  CPA_GUARD_BEGIN
+  CPA_TRY(check_plan(h));
+  Plan& p = *h->p;
+  if (rank < 0 || rank >= p.cp) return fail(CP_ATTN_EINVAL, "rank outside [0, cp_size)");
+  CPA_TRY(check_io(q, k, v, out, lse));
+  if (!p.doc_starts.empty())
+    return fail(CP_ATTN_EUNSUPPORTED, "document masks need the plan's workspace (cp_attn_rank_forward)");
+  const int64_t need = ws_layout(p).total;
+  if (need > kScratchBytes)
+    return fail(CP_ATTN_ENOWORKSPACE, "the plan needs " + std::to_string(need) + " bytes of workspace; the " +
+                                          "no-allocation forward holds " + std::to_string(kScratchBytes));
+  DeviceState& d = *p.dev;
+  int dev = 0;
+  CPA_HIP(hipGetDevice(&dev));
+  if (d.device >= 0 && d.device != dev) return fail(CP_ATTN_EINVAL, "plan was first used on another device");
+  if (!d.cus) CPA_HIP(hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev));
+  char* base = nullptr;
+  CPA_TRY(scratch_base(dev, &base));
+  d.device = dev;
+  std::fill(d.timed.begin(), d.timed.end(), 0);  // this call records no step times or counts
+  std::fill(d.counted.begin(), d.counted.end(), 0);
+  RunCfg c;
+  c.ws = base;
+  c.serial = true;
+  c.recv = 2;
+  c.recv_blocks = p.opt_recv_blocks;
+  c.poison = p.opt_poison != 0;
+  return run_rank(p, c, q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
   CPA_GUARD_END
 }
 
@@ -1001,7 +1089,8 @@ int cp_attn_full_forward(cp_attn_plan_t h, const void* q, const void* k, const v
   CPA_TRY(ensure_device(p));
   reset_timing(p);
   if (p.opt_graph) return run_graph(p, q, k, v, out, lse, -1, static_cast<hipStream_t>(stream));
-  for (int r = 0; r < p.cp; ++r) CPA_TRY(run_rank(p, q, k, v, out, lse, r, static_cast<hipStream_t>(stream)));
+  const RunCfg c = plan_cfg(p, false);
+  for (int r = 0; r < p.cp; ++r) CPA_TRY(run_rank(p, c, q, k, v, out, lse, r, static_cast<hipStream_t>(stream)));
   return CP_ATTN_OK;
   CPA_GUARD_END
 }
