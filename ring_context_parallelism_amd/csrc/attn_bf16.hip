@@ -423,13 +423,17 @@ __device__ __forceinline__ uint32_t lds_addr(const __attribute__((address_space(
 // stages: tile j+2 is loaded while tile j computes, two tiles of latency.
 //
 // Ring receive (kRecv): the workgroup's share of the next step's K/V is cut
-// into ntiles + 2 slots; at the start of tile j every wave stores slot j
-// (loaded two tiles earlier) and loads slot j + 2.  Every wave issues exactly
-// one copy store, one copy load and four tile loads per tile (lanes with
-// nothing to copy repeat a vector of the share: the same bytes to the same
-// place; the tile loads past the last tile repeat the last tile), so the
-// end-of-tile wait for tile j + 1 is a fixed count of younger loads,
-// vmcnt(5), and a copy access has two tiles to complete.
+// into ntiles chunks of at most 256 16-byte vectors.  The waves of group A
+// (0-3) copy one chunk per tile through registers, at the start of tile j:
+// chunk j - 1 (loaded at the start of tile j - 1, a whole tile earlier, so
+// the wait before its store finds it landed) is stored and chunk j loaded.
+// Every A wave issues exactly one copy store and one copy load per tile
+// (lanes with nothing to copy repeat a vector of the share: the same bytes
+// to the same place), so its end-of-tile wait for tile j + 1 stays a fixed
+// count of younger loads, vmcnt(5).  Group B copies nothing.  What does not
+// fit in the chunks is copied after the loop.  (An earlier form staged the
+// copy through LDS with direct-to-LDS loads in every wave; each such load
+// holds its wave at issue for about 50 clocks, and the copy cost more.)
 //
 // Document masks (kDoc): a row sees only the run of the source's keys that
 // holds its own document, [klo, khi), clipped to its prefix.  The rows of a
@@ -449,8 +453,6 @@ void attn_step_bf16_d128x8(StepArgs a) {
   constexpr int D = 128, NT = 8, NB = 4;
   // 4 stages x K, V
   __shared__ __attribute__((aligned(1024))) uint8_t smem_kv[4 * 2 * kTileBytes];
-  // ring-copy staging: 3 slots x 8 waves x 1 KiB
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_c[kRecv ? 3 * 8 * 1024 : 16];
   lds_u8* const kv_lds = (lds_u8*)smem_kv;
   // the four K stages fill the first 64 KiB, the four V stages the second:
   // with a constant stage every operand read addresses a per-lane base plus
@@ -466,7 +468,6 @@ void attn_step_bf16_d128x8(StepArgs a) {
     asm volatile("" : "+s"(o));
     return kv_lds + o;
   };
-  lds_u8* const cstage = (lds_u8*)smem_c;
 
   int h, t;
   tile_of(blockIdx.x, gridDim.x, a.heads, a.total_tiles, h, t);
@@ -697,7 +698,7 @@ void attn_step_bf16_d128x8(StepArgs a) {
   typedef __attribute__((address_space(1))) u32x4 g_u32x4;  // global memory: no flat accesses
   const void* const csrc_p = rr == 0 ? a.recv.src[0] : rr == 1 ? a.recv.src[1] : rr == 2 ? a.recv.src[2] : a.recv.src[3];
   g_u32x4* const cdst = (g_u32x4*)(rr == 0 ? a.recv.dst[0] : rr == 1 ? a.recv.dst[1] : rr == 2 ? a.recv.dst[2] : a.recv.dst[3]);
-  const u32x4 desc_c = buffer_desc(csrc_p, uint32_t(rn * 16));
+  const g_u32x4* const csrc = (const g_u32x4*)csrc_p;
   // this workgroup's key tiles: jt0 .. jt0 + ntiles - 1 (key kb0 onwards)
   // (document masks: from the tile of the workgroup's first key, never split)
   const int ntiles_all = (kv_end + kBN - 1) / kBN;
@@ -705,46 +706,36 @@ void attn_step_bf16_d128x8(StepArgs a) {
   const int jt0 = kDoc ? wg_lo / kBN : part ? half_tiles : 0;
   const int ntiles = kDoc ? max(0, ntiles_all - jt0) : ks == 1 ? ntiles_all : (part ? ntiles_all - half_tiles : half_tiles);
   const int kb0 = jt0 * kBN;
-  // slots of the share: ntiles + 2, at most 512 vectors (one per lane) each;
-  // what does not fit is copied after the loop
-  const int64_t nslot = int64_t(ntiles) + 2;
-  const int64_t sv = min<int64_t>(kThreads8, (rend - rbeg + nslot - 1) / nslot);  // vectors per slot
-  const int64_t wvv = (sv + 7) / 8;                                                // per wave
-  // vector of this lane in slot c: its wave's part of the slot, lanes past it
-  // repeat the part's last vector; an empty part repeats the share's (or, for
-  // an empty share, the range's) last vector
-  auto slot_vec = [&](int64_t c) {
-    const int64_t lo = rbeg + c * sv + int64_t(wv) * wvv;
-    const int64_t hi = min(min(lo + wvv, rbeg + (c + 1) * sv), rend);
+  // chunks of the share: ntiles, at most 256 vectors (one per lane of group
+  // A) each; what does not fit is copied after the loop
+  const int64_t cv = ntiles > 0 ? min<int64_t>(256, (rend - rbeg + ntiles - 1) / ntiles) : 0;  // vectors per chunk
+  // vector of lane a (0..255 over group A) in chunk c: lanes past the chunk
+  // repeat its last vector; an empty chunk repeats the share's (or, for an
+  // empty share, the range's) last vector
+  auto chunk_vec = [&](int64_t c) {
+    const int64_t lo = rbeg + c * cv;
+    const int64_t hi = min(lo + cv, rend);
     const int64_t fb = rend > rbeg ? rend - 1 : rn - 1;
-    return uint32_t(hi > lo ? min(lo + int64_t(lane), hi - 1) : fb);
+    return hi > lo ? min(lo + int64_t(wv * 64 + lane), hi - 1) : fb;
   };
-  // slot c goes HBM -> this wave's 1 KiB of LDS staging b at tile c - 2, and
-  // staging -> receive slot at tile c
-  auto copy_dma = [&](int64_t c, int b) {
-    dma_lds16(desc_c, slot_vec(c) * 16u, 0u, lds_addr(cstage + b * (8 * 1024) + wv * 1024));
-  };
-  auto copy_store = [&](int64_t c, int b) {
-    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-    const u32x4 x = *reinterpret_cast<lds_u32x4*>(cstage + b * (8 * 1024) + wv * 1024 + lane * 16);
-    __builtin_nontemporal_store(x, cdst + slot_vec(c));
+  u32x4 creg = {};  // group A: the chunk loaded at the end of the previous tile
+  auto copy_step = [&](int j) {
+    if (j > 0) __builtin_nontemporal_store(creg, cdst + chunk_vec(j - 1));
+    creg = __builtin_nontemporal_load(csrc + chunk_vec(j));
   };
 
   // Tile j's K/V live in stage j % 4; waves 0-3 load the K tiles and waves
-  // 4-7 the V tiles (issue() above), tile j + 2 during tile j.  Every load
-  // below is issued by dma_lds16, so the only waits are these: the prologue
+  // 4-7 the V tiles (issue() above), tile j + 2 during tile j.  Every tile
+  // load is issued by dma_lds16, so the only waits are these: the prologue
   // waits for all, the end of tile j for all but the loads the wave issued
-  // during tile j (one copy load and four tile loads; four without a
-  // receive), so that tile j + 1 and copy slot j + 1 have landed.  Loads
-  // complete in order among themselves, but a store may complete before
-  // older loads, so the count leaves out the tile's copy store: were it
-  // counted, an early store would let the wait pass with an older load still
-  // in flight.
+  // during tile j (four tile loads; with a receive, group A also issued one
+  // copy store and one copy load at the start of the tile), so that tile
+  // j + 1 has landed.  Loads complete in order among themselves, and a store
+  // may complete before older loads: the count 5 of group A with a receive
+  // holds back only loads younger than the tile loads of tile j - 1 (the
+  // copy load and the four tile loads of tile j; with one of tile j - 1's
+  // loads still in flight those five would be too, six or seven in all).
   if (ntiles > 0) {
-    if constexpr (kRecv) {
-      copy_dma(0, 0);
-      copy_dma(1, 1);
-    }
     const u32x4& desc = wv < 4 ? desc_k : desc_v;
     issue(desc, kb0, wv < 4 ? kst(0) : vst(0));
     issue(desc, kb0 + min(1, ntiles - 1) * kBN, wv < 4 ? kst(1) : vst(1));
@@ -770,13 +761,6 @@ void attn_step_bf16_d128x8(StepArgs a) {
   // Stage and copy-staging indices are loop variables: unrolling to make them
   // constants needs several sets of stage addresses and spills the Q
   // fragments.
-#define CPATTN_X8_COPY(J, C)                                                               \
-  do {                                                                                     \
-    if constexpr (kRecv) {                                                                 \
-      copy_store(J, C);                                                                    \
-      copy_dma((J) + 2, (C) == 0 ? 2 : (C) - 1);                                           \
-    }                                                                                      \
-  } while (0)
   // the MFMA phase of tile J: product of tile J - 1 (probabilities pb_),
   // scores of tile J into s_
 #define CPATTN_X8_GEMMS(J, S, s_, pb_)                                                     \
@@ -786,7 +770,7 @@ void attn_step_bf16_d128x8(StepArgs a) {
     if (pv_) pv(vst_rt(((S) + 3) & 3), pb_);                                               \
     if (sc_) scores(kst(S), s_);                                                           \
   } while (0)
-#define CPATTN_X8_END()                                                                    \
+#define CPATTN_X8_END_A(J)                                                                 \
   do {                                                                                     \
     if constexpr (kRecv)                                                                   \
       __builtin_amdgcn_s_waitcnt(0x0F75); /* vmcnt(5) */                                   \
@@ -794,59 +778,54 @@ void attn_step_bf16_d128x8(StepArgs a) {
       __builtin_amdgcn_s_waitcnt(0x0F74); /* vmcnt(4) */                                   \
     lds_barrier();                                                                         \
   } while (0)
+#define CPATTN_X8_END_B()                                                                  \
+  do {                                                                                     \
+    __builtin_amdgcn_s_waitcnt(0x0F74); /* vmcnt(4) */                                     \
+    lds_barrier();                                                                         \
+  } while (0)
 
-  // Without the ring copy the loops run four tiles per iteration, one per
-  // stage, so that each tile's stage is a constant (the copy's registers
-  // leave no room for that; its loops take the stage as a variable).
+  // The loops run four tiles per iteration, one per stage, so that each
+  // tile's stage is a constant.
   bf16x8 pb_[2][2];  // probabilities of the last softmaxed tile
   f32x16 s_[2];      // scores of the last scored tile
-  int cb = 0;        // copy staging slot of the tile
 #define CPATTN_X8_TILE_A(J, ST)                                                            \
   do {                                                                                     \
     if ((J) < ntiles) {                                                                    \
-      CPATTN_X8_COPY(J, cb);                                                               \
+      if constexpr (kRecv) copy_step(J);                                                   \
       CPATTN_X8_GEMMS(J, ST, s_, pb_);                                                     \
       if (live(kb0 + (J) * kBN)) softmax(s_, kb0 + (J) * kBN, pb_);                        \
       issue(desc_k, kb0 + min((J) + 2, ntiles - 1) * kBN, kst(((ST) + 2) & 3));            \
-      CPATTN_X8_END();                                                                     \
-      cb = cb == 2 ? 0 : cb + 1;                                                           \
+      CPATTN_X8_END_A(J);                                                                  \
     }                                                                                      \
   } while (0)
 #define CPATTN_X8_TILE_B(J, ST)                                                            \
   do {                                                                                     \
     if ((J) < ntiles) {                                                                    \
-      CPATTN_X8_COPY(J, cb);                                                               \
       if ((J) > 0 && live(kb0 + ((J) - 1) * kBN)) softmax(s_, kb0 + ((J) - 1) * kBN, pb_); \
       issue(desc_v, kb0 + min((J) + 2, ntiles - 1) * kBN, vst(((ST) + 2) & 3));            \
       CPATTN_X8_GEMMS(J, ST, s_, pb_);                                                     \
-      CPATTN_X8_END();                                                                     \
-      cb = cb == 2 ? 0 : cb + 1;                                                           \
+      CPATTN_X8_END_B();                                                                   \
     }                                                                                      \
   } while (0)
   if (wv < 4) {
-    if constexpr (kRecv) {
-      for (int j = 0, st = 0; j < ntiles; ++j, st = (st + 1) & 3) CPATTN_X8_TILE_A(j, st);
-    } else {
-      for (int j = 0; j < ntiles; j += 4) {
-        CPATTN_X8_TILE_A(j, 0);
-        CPATTN_X8_TILE_A(j + 1, 1);
-        CPATTN_X8_TILE_A(j + 2, 2);
-        CPATTN_X8_TILE_A(j + 3, 3);
-      }
+    for (int j = 0; j < ntiles; j += 4) {
+      CPATTN_X8_TILE_A(j, 0);
+      CPATTN_X8_TILE_A(j + 1, 1);
+      CPATTN_X8_TILE_A(j + 2, 2);
+      CPATTN_X8_TILE_A(j + 3, 3);
     }
     // product of the last tile (its stage is not overwritten: the loads
     // issued at the last two tiles went to other stages)
     if (ntiles > 0 && live(kb0 + (ntiles - 1) * kBN)) pv(vst((ntiles - 1) & 3), pb_);
+    // the last chunk of the receive
+    if constexpr (kRecv)
+      if (ntiles > 0) __builtin_nontemporal_store(creg, cdst + chunk_vec(ntiles - 1));
   } else {
-    if constexpr (kRecv) {
-      for (int j = 0, st = 0; j < ntiles; ++j, st = (st + 1) & 3) CPATTN_X8_TILE_B(j, st);
-    } else {
-      for (int j = 0; j < ntiles; j += 4) {
-        CPATTN_X8_TILE_B(j, 0);
-        CPATTN_X8_TILE_B(j + 1, 1);
-        CPATTN_X8_TILE_B(j + 2, 2);
-        CPATTN_X8_TILE_B(j + 3, 3);
-      }
+    for (int j = 0; j < ntiles; j += 4) {
+      CPATTN_X8_TILE_B(j, 0);
+      CPATTN_X8_TILE_B(j + 1, 1);
+      CPATTN_X8_TILE_B(j + 2, 2);
+      CPATTN_X8_TILE_B(j + 3, 3);
     }
     if (ntiles > 0 && live(kb0 + (ntiles - 1) * kBN)) {
       softmax(s_, kb0 + (ntiles - 1) * kBN, pb_);
@@ -855,9 +834,9 @@ void attn_step_bf16_d128x8(StepArgs a) {
   }
 #undef CPATTN_X8_TILE_B
 #undef CPATTN_X8_TILE_A
-#undef CPATTN_X8_END
+#undef CPATTN_X8_END_A
+#undef CPATTN_X8_END_B
 #undef CPATTN_X8_GEMMS
-#undef CPATTN_X8_COPY
 
   if (a.tile_cnt && lane == 0) {
     // work counter: the tiles whose scores the loops computed (their
@@ -870,14 +849,8 @@ void attn_step_bf16_d128x8(StepArgs a) {
   }
   wait_vmem();
   if constexpr (kRecv) {
-    // the last two slots (loaded at the last two tiles, or in the prologue),
-    // then what did not fit in the slots
-    if (ntiles > 0) {
-      copy_store(ntiles, ntiles % 3);
-      copy_store(ntiles + 1, (ntiles + 1) % 3);
-    }
-    const g_u32x4* const csrc = (const g_u32x4*)csrc_p;
-    for (int64_t i = rbeg + (ntiles > 0 ? nslot : 0) * sv + tid; i < rend; i += kThreads8)
+    // what did not fit in the chunks
+    for (int64_t i = rbeg + int64_t(ntiles) * cv + tid; i < rend; i += kThreads8)
       __builtin_nontemporal_store(__builtin_nontemporal_load(csrc + i), cdst + i);
     if (whole_ranges) {
       for (int r = int(blockIdx.x); r < a.recv.n; r += int(gridDim.x)) {
