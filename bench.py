@@ -229,6 +229,45 @@ def imbalance_section(stream):
     return res
 
 
+def workload_section(name, stream, steps, graph_too=False):
+    """One of the other workloads, timed like the headline: calls per second
+    over its share, effective TFLOP/s of the valid pairs, the step kernel's
+    mean launch time from the library's step events and its fraction of the
+    bf16 peak, and (graph_too) the same calls replayed from a HIP graph."""
+    import ring_context_parallelism_amd as R
+    from ring_context_parallelism_amd.inputs import WORKLOADS, workload_qkv
+    w = WORKLOADS[name]
+    p = R.Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout, dtype=w.torch_dtype)
+    q, k, v = (t.cuda() for t in workload_qkv(w))
+    out = torch.empty_like(q)
+    lse = torch.empty(w.heads, w.seq_len, device="cuda")
+    bufs = (q, k, v, out, lse)
+    pairs = share_pairs(p, w)
+    flops = 4 * w.head_dim * w.heads * pairs
+    ms = time_calls(p, w, bufs, stream, steps, 3, 0.3)
+    med = time_calls.last["median"]
+    times = step_kernel_times(p, w, bufs, stream, 3)
+    ranks = range(w.cp) if w.rank is None else [w.rank]
+    launches = [times[r][s] for r in ranks for s in range(w.cp) if times[r][s] > 0]
+    avg = float(np.mean(launches))
+    kern = flops / len(launches) / (avg * 1e-3) / 1e12
+    res = {"workload": name, "share": "all ranks" if w.rank is None else f"rank {w.rank}", "valid_flops": flops,
+           "ms_per_call": round(ms, 5), "ms_per_call_median": round(med, 5),
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "step_kernel": {"launches_per_call": len(launches), "avg_launch_ms": round(avg, 5),
+                           "tflops": round(kern, 2), "frac_bf16_peak": round(kern / PEAK_BF16_TFLOPS, 4)}}
+    if graph_too:
+        p.set_graph(True)
+        gms = time_calls(p, w, bufs, stream, steps, 3, 0.3)
+        p.set_graph(False)
+        res["graph_replay_ms_per_call"] = round(gms, 5)
+        res["graph_replay_median_ms"] = round(time_calls.last["median"], 5)
+    p.close()
+    del q, k, v, out, lse, bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def rank_step_imbalance(plan, w, bufs, stream, reps=3):
     """Every rank's share of the timed workload, one rank_forward call each:
     per-(rank, step) step-kernel ms, per-step max/mean over ranks, and the
@@ -246,7 +285,18 @@ def rank_step_imbalance(plan, w, bufs, stream, reps=3):
     t = np.asarray(times)
     per = [round(float(t[:, s].max() / t[:, s].mean()), 4) for s in range(w.cp)]
     tiles = [[plan.valid_work(r, s, 128, 64)[0] for s in range(w.cp)] for r in range(w.cp)]
+    # A ring runs in lockstep: step s of the job takes the slowest rank's
+    # step s.  Per GPU, the job's valid FLOPs (all ranks, divided by cp) over
+    # the sum of those maxima of the step kernels' times.
+    all_pairs = sum(plan.valid_work(r, s, 128, 64)[1] for r in range(w.cp) for s in range(w.cp))
+    lockstep_ms = float(t.max(axis=0).sum())
+    lockstep_tflops = 4 * w.head_dim * w.heads * all_pairs / w.cp / (lockstep_ms * 1e-3) / 1e12
+    rank0_ms = float(t[0].sum())
     return {"workload": w.name, "step_ms": [[round(float(x), 4) for x in row] for row in t],
+            "lockstep_step_kernel_ms": round(lockstep_ms, 5), "rank0_step_kernel_ms": round(rank0_ms, 5),
+            "lockstep_over_rank0": round(lockstep_ms / rank0_ms, 4),
+            "lockstep_tflops_per_gpu": round(lockstep_tflops, 2),
+            "lockstep_frac_bf16_peak": round(lockstep_tflops / PEAK_BF16_TFLOPS, 4),
             "time_imbalance_per_step": per, "max_step_imbalance": max(per),
             "time_imbalance": round(float(t.max(axis=0).sum() / t.mean(axis=0).sum()), 4),
             "tiles_128x64": tiles}
@@ -514,7 +564,10 @@ def main():
                               "overlapped_separate_merge": round(ms_sep, 5),
                               "receive_kernel_grid_blocks_ms": ms_blocks,
                               "receive_mode_ms": recv_ms,
-                              "exposed_copy_ms": round(ms_serial - ms, 5)}
+                              # serial order also gives each receive the full copy grid (it overlaps
+                              # no step kernel there), so this difference is not the copy time that
+                              # the overlap hides; it is what the overlapped schedule saves
+                              "serial_minus_overlapped_ms": round(ms_serial - ms, 5)}
         run_call(plan, w, bufs, stream)
         torch.cuda.synchronize()
         result["parity_sampled"] = sampled_parity(w, q_cpu, k_cpu, v_cpu, out, lse)
@@ -526,6 +579,12 @@ def main():
         result["imbalance"]["zigzag_step_time_imbalance"] = result["imbalance"]["zigzag"]["time_imbalance"]
 
     if not args.no_extras:
+        result["other_workloads"] = [
+            workload_section("causal_s8192_cp4_zigzag_h32_d128_bf16", stream, max(5, args.steps // 2), graph_too=True),
+            workload_section("bidir_s65536_cp16_contiguous_h8_d128_bf16_rank0", stream, max(5, args.steps // 2)),
+        ]
+        print("[bench] other workloads: " + "; ".join(f"{o['workload']}: {o['ms_per_call']} ms, {o['tflops']} TFLOP/s"
+                                                    for o in result["other_workloads"]), file=sys.stderr, flush=True)
         result["ulysses"] = ulysses_section(plan, w, bufs, stream, max(3, args.steps // 4))
         if w.rank is not None and w.causal:
             result["documents"] = documents_section(w, bufs, stream, max(3, args.steps // 4))

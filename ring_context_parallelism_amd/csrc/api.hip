@@ -384,6 +384,15 @@ int launch_step(Plan& p, const RunCfg& c, const void* q, const void* k, const vo
     a.total_tiles += x.tiles;
   }
   if (sd.nseg == 1) a.seg[1] = SegArgs{};
+  // Workgroups are dispatched in segment order: the segment with the longer
+  // rows goes first, so that (each segment already ordered longest row tile
+  // first) the short tiles of the other fill in behind the long ones.  On a
+  // rank's first step this pairs the long row tiles of the late chunk with
+  // the short diagonal tiles of the early one on the same compute unit.
+  if (sd.nseg == 2) {
+    auto work = [](const SegArgs& x) { return int64_t(x.q_len) * (2 * int64_t(x.kv_full) + (x.diag ? x.q_len : 0)); };
+    if (work(a.seg[1]) > work(a.seg[0])) std::swap(a.seg[0], a.seg[1]);
+  }
   if (kernel_recv(p, c, s)) a.recv = recv_ranges(p, ws, k, v, p.step(r, s + 1).src, (s + 1) & 1);
   if (c.counters) a.tile_cnt = d.tile_cnt + size_t(r) * p.cp + s;
   set_doc(p, ws, a, sd.src);
