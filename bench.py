@@ -51,6 +51,7 @@ def parse():
                     help="LSE merge in the attention epilogue (default) or in the separate merge/finalize kernels")
     ap.add_argument("--backward", action="store_true",
                     help="also time the share's backward (on by default with the extras)")
+    ap.add_argument("--no-key-split", action="store_true", help="never split a step's keys over two workgroups")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one layout gather of q (a plain copy of known size) before timing, "
                          "as the reference for hardware traffic counters")
@@ -480,6 +481,8 @@ def main():
         plan.set_graph(True)
     if args.merge == "separate":
         plan.set_merge(True)
+    if args.no_key_split:
+        plan.set_key_split(False)
 
     if args.copy_probe:
         probe = torch.empty_like(q)
