@@ -339,12 +339,21 @@ def backward_section(plan, w, bufs, stream, reps):
     plan.rank_backward(*args, stream=stream)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        plan.rank_backward(*args, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+
+    def timed():
+        e0.record(stream)
+        for _ in range(reps):
+            plan.rank_backward(*args, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    plan.set_backward_key_kernel("four")  # one wave per 32-key column, for comparison
+    plan.rank_backward(*args, stream=stream)
+    ms_four = timed()
+    plan.set_backward_key_kernel("eight")  # the default; its call writes dq last
+    plan.rank_backward(*args, stream=stream)
+    ms = timed()
     flops = 2.5 * 4 * w.head_dim * w.heads * share_pairs(plan, w)
     tflops = flops / (ms * 1e-3) / 1e12
     # dQ of sampled rows of the share (written by the last call in full)
@@ -356,6 +365,7 @@ def backward_section(plan, w, bufs, stream, reps):
     rel = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
     return {"ms_per_call": round(ms, 5), "tflops": round(tflops, 2),
             "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "valid_flops": flops,
+            "four_wave_key_kernel_ms_per_call": round(ms_four, 5),
             "flop_convention": "2.5 x forward valid flops",
             "parity_dq_sampled_rows": {"rows": sample.tolist(), "max_rel_err": rel, "tol": 2e-2, "ok": rel <= 2e-2}}
 

@@ -103,6 +103,10 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      0: never split. Not used with the separate merge mode. */
 #define CP_ATTN_OPT_COUNTERS 9    /* 1: the step kernels count the key tiles they compute per (rank,
                                      step) on the device (cp_attn_last_tile_counts) */
+#define CP_ATTN_OPT_BWD_KEYS 10   /* backward dK/dV kernel (bf16, head_dim 128): 0 (default): eight
+                                     waves, each 32-key column's products split between two waves;
+                                     1: four waves, one wave per 32-key column. dK and dV are
+                                     bit-identical either way. */
 
 /*
  * Create a plan (host only: no device memory, no HIP call).

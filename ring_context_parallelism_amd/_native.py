@@ -33,6 +33,7 @@ OPT_RECV_BLOCKS = 6
 OPT_GRAPH = 7
 OPT_KSPLIT = 8
 OPT_COUNTERS = 9
+OPT_BWD_KEYS = 10
 
 NOALLOC_SCRATCH_BYTES = 128 << 20  # CP_ATTN_NOALLOC_SCRATCH_BYTES
 

@@ -81,6 +81,11 @@ class Plan:
     def set_key_split(self, on):
         self.set_option(N.OPT_KSPLIT, int(bool(on)))
 
+    def set_backward_key_kernel(self, kind):
+        """dK/dV kernel of the bf16, head_dim-128 backward: "eight" (default,
+        two waves per 32-key column) or "four" (one wave per column)."""
+        self.set_option(N.OPT_BWD_KEYS, {"eight": 0, "four": 1}[kind])
+
     def set_poison(self, on):
         self.set_option(N.OPT_POISON, int(bool(on)))
 

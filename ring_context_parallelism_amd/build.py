@@ -28,6 +28,14 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{IN
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-fno-gpu-rdc"]
 
+# Per-file device flags.  The eight-wave key-major backward kernel branches
+# on a wave-uniform role into two loops; by default the control-flow
+# structurizer sequences the two branches one after the other behind flags,
+# and the wait-count insertion then treats one role's loads as in flight in
+# the other's loop (stalling its matrix work on them).  Keeping uniform
+# regions as they are avoids that.
+TU_FLAGS = {"attn_bwd_bf16.hip": ["-mllvm", "-structurizecfg-skip-uniform-regions=true"]}
+
 
 def hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -40,7 +48,7 @@ def _compile(src, verbose):
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     if src.endswith(".hip"):
-        cmd = [hipcc(), "-x", "hip", *HIP_FLAGS, *COMMON, "-c", path, "-o", obj]
+        cmd = [hipcc(), "-x", "hip", *HIP_FLAGS, *TU_FLAGS.get(src, []), *COMMON, "-c", path, "-o", obj]
     else:
         cmd = [hipcc(), *COMMON, "-c", path, "-o", obj]
     if verbose:

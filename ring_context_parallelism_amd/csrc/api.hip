@@ -716,7 +716,7 @@ int run_rank_backward(Plan& p, const void* q, const void* k, const void* v, cons
     }
     a.key_tiles = int32_t((maxpre + bt_keys - 1) / bt_keys);
     set_doc(p, ws, a, j);
-    const hipError_t e = bwd_mfma(bf16, p.head_dim) ? launch_bwd_bf16_d128(a, st)
+    const hipError_t e = bwd_mfma(bf16, p.head_dim) ? launch_bwd_bf16_d128(a, p.opt_bwd_keys == 0, st)
                                                     : launch_bwd_generic(a, bf16, p.head_dim, st);
     if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("backward launch: ") + hipGetErrorString(e));
   }
@@ -843,6 +843,10 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
     case CP_ATTN_OPT_KSPLIT:
       if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "ksplit option must be 0 or 1");
       p.opt_ksplit = value;
+      return CP_ATTN_OK;
+    case CP_ATTN_OPT_BWD_KEYS:
+      if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "CP_ATTN_OPT_BWD_KEYS must be 0 or 1");
+      p.opt_bwd_keys = value;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_COUNTERS:
       if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "counters option must be 0 or 1");

@@ -307,6 +307,362 @@ void bwd_dkdv_bf16_d128(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Key-major, eight waves: the same products as above with the work of a
+// 32-key column split between two waves of one SIMD.
+// ---------------------------------------------------------------------------
+// Waves w and w + 4 (on one SIMD) own keys 32 (w & 3) .. + 31 of the
+// workgroup's 128.  Wave w (S role) holds K, computes S = Q K^T and P and
+// accumulates dV; wave w + 4 (dP role) holds V, computes dP = dO V^T, takes
+// P (fp32) through LDS, forms dS and accumulates dK.  Each wave then needs
+// one K or V operand and one 32x128 accumulator, half the registers of the
+// one-pass kernel, so two waves share a SIMD.  The dP role runs one tile
+// behind: with tiles T_0 .. T_{n-1}, phase p is
+//   [X_p .. Y_p]   S role: dV += dO(T_{p-1})^T P, S(T_p)     (32 MFMAs)
+//                  dP role: dS(T_{p-1}) = P (dP - D)        (vector ALU)
+//   [Y_p .. X_p+1] S role: P(T_p) from S(T_p), to LDS       (vector ALU)
+//                  dP role: dK += Q(T_{p-1})^T dS, dP(T_p)  (32 MFMAs)
+// between workgroup barriers X and Y, so on every SIMD one wave's matrix
+// work runs while the other's elementwise work does.  Phase p reads the tile
+// stages of T_p and T_{p-1} and fills the third with T_{p+1}, loaded to
+// registers at the phase's start.  Per wave the products, their operands and
+// the order over tiles are those of the one-pass kernel: dK and dV are
+// bit-identical to it.
+constexpr int kThreads8 = 512;
+constexpr int kStages = 3;
+
+// mm_rows with the operand reads two k-steps ahead of the MFMAs (pinned by
+// scheduling-group barriers): one wave issues the reads and MFMAs of a
+// product alone, so the LDS latency has to hide behind its own MFMAs.
+__device__ __forceinline__ void mm_rows_p(const lds_u8* tile, uint32_t base, const bf16x8 (&b)[NT], f32x16 (&c)[2]) {
+  bf16x8 a0[NT], a1[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    a0[i] = *reinterpret_cast<const lds_bf16x8*>(tile + (base ^ (32u * i)));
+    a1[i] = *reinterpret_cast<const lds_bf16x8*>(tile + 32 * 256 + (base ^ (32u * i)));
+  }
+  c[0] = f32x16{};
+  c[1] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b[i], c[0], 0, 0, 0);
+    c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b[i], c[1], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // k-steps 0, 1 read
+#pragma unroll
+  for (int i = 0; i < NT - 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // k-step i
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // k-step i + 2 read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // k-steps NT - 2, NT - 1
+}
+
+// mm_tr with the transposed reads one group of four MFMAs ahead.
+__device__ __forceinline__ void mm_tr_p(const lds_u8* tile, const uint32_t (&tr)[2], const bf16x8 (&w)[2][2],
+                                        f32x16 (&acc)[NB]) {
+  bf16x8 va[4][NB];
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    const int roff = (32 * (gq >> 1) + 16 * (gq & 1)) * 256;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + roff + (tr[0] ^ (64u * b))));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + roff + (tr[1] ^ (64u * b))));
+      va[gq][b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[gq][b], w[gq >> 1][gq & 1], acc[b], 0, 0, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // groups 0 and 1 read
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // group 0 MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // group 2 read
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // group 1 MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // group 3 read
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // groups 2 and 3 MFMAs
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// (the next tile's prefetch) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The next 64-row tile of a key-major workgroup's walk (keys k0 .. k0 + 127):
+// the search starts at row r0 of segment si (r0 < 0: the segment's first
+// tile).  Rows before a segment's first tile see none of the keys; with
+// document masks the walk leaves a segment at the first tile whose first
+// row's run starts past them.  Leaves si = nseg when no tile is left.
+template <bool kDoc>
+__device__ __forceinline__ void km_seek(const BwdArgs& a, int k0, int& si, int& r0) {
+  // one exit, at the loop's end (with early exits the compiler linearizes
+  // the two role branches of the kernel below, see there)
+  bool found = false;
+  while (!found && si < a.nseg) {
+    const SegArgs& g = a.seg[si];
+    // row t sees keys < kv_full + t + 1 on a diagonal segment
+    const int t0 = k0 < g.kv_full ? 0 : (g.diag ? k0 - g.kv_full : g.q_len);
+    if (r0 < 0) r0 = t0;
+    found = r0 < g.q_len;
+    if constexpr (kDoc) {
+      if (found) {
+        int lo, hi;
+        doc_row_keys(a, g.q_global + r0, lo, hi);
+        found = lo < k0 + kKeys;
+      }
+    }
+    if (!found) {
+      ++si;
+      r0 = -1;
+    }
+  }
+}
+
+// One tile's prefetch: two 16-byte chunks of Q and of dO per thread, and
+// (threads 0..63) the row's log2-scaled LSE, D and document run.
+struct KmRegs {
+  u32x4 q[2], o[2];
+  float lse, del;  // raw; rows at or past `rows` are replaced at the store
+  int rows;        // valid rows of the tile
+  int klo, khi;
+};
+
+template <bool kDoc>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8), amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_bf16_d128x8(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * 2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) float s_p[4 * 2 * 4 * 64 * 4];  // P of each wave pair, fp32
+  __shared__ __attribute__((aligned(16))) float s_lse[kStages][kTileRows];
+  __shared__ __attribute__((aligned(16))) float s_del[kStages][kTileRows];
+  __shared__ __attribute__((aligned(16))) int s_klo[kStages][kTileRows];
+  __shared__ __attribute__((aligned(16))) int s_khi[kStages][kTileRows];
+
+  const int h = blockIdx.x % a.heads;
+  const int k0 = (blockIdx.x / a.heads) * kKeys;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wv >> 2, pw = wv & 3;  // role 0: S, P, dV; role 1: dP, dS, dK
+  const int qc = lane & 31, hf = lane >> 5;
+  const int w_key0 = k0 + 32 * pw;  // the pair's smallest key
+  const int key = w_key0 + qc;
+  const bool kok = key < a.kv_valid;
+  const int krow = kv_row(a, min(key, a.kv_valid - 1));
+  const uint32_t row_bytes = uint32_t(a.heads) * 256;
+  const uint32_t hoff = uint32_t(h) * 256;
+  const Bases bs = make_bases(lane);
+  float* const pbuf = s_p + pw * (2 * 4 * 64 * 4) + lane * 4;  // + (4 qb + m) * 256: float4 of the lane
+
+  auto stage_q = [&](int st) { return (lds_u8*)smem + st * 2 * kTileBytes; };
+  auto stage_o = [&](int st) { return (lds_u8*)smem + st * 2 * kTileBytes + kTileBytes; };
+
+  auto load_tile = [&](int si, int r0, KmRegs& rg) {
+    const SegArgs& g = a.seg[si];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kThreads8 * i;
+      const int r = c >> 4, ch = c & 15;
+      const uint64_t off = uint64_t(g.q_global + min(r0 + r, g.q_len - 1)) * row_bytes + hoff + ch * 16;
+      rg.q[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + off);
+      rg.o[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.dout) + off);
+    }
+    if (wv == 0) {  // the tile's rows, one per lane (clamped loads, then selects: no lane branches)
+      const int tc = min(r0 + lane, g.q_len - 1);
+      rg.lse = a.lse[int64_t(h) * a.seq_len + g.q_global + tc];
+      rg.del = a.delta[int64_t(h) * a.n_loc + g.q_start + tc];
+      rg.rows = g.q_len - r0;
+      if constexpr (kDoc) doc_row_keys(a, g.q_global + tc, rg.klo, rg.khi);
+    }
+  };
+  auto store_tile = [&](int st, const KmRegs& rg) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kThreads8 * i;
+      const int r = c >> 4, ch = c & 15;
+      const uint32_t o = r * 256 + ((ch ^ swz(r & 15)) << 4);
+      *reinterpret_cast<lds_u32x4*>(stage_q(st) + o) = rg.q[i];
+      *reinterpret_cast<lds_u32x4*>(stage_o(st) + o) = rg.o[i];
+    }
+    if (wv == 0) {  // rows past the segment: LSE = +inf (P = 0), D = 0
+      const bool ok = lane < rg.rows;
+      s_lse[st][lane] = ok ? rg.lse * kLog2e : INFINITY;
+      s_del[st][lane] = ok ? rg.del : 0.f;
+      if constexpr (kDoc) {
+        s_klo[st][lane] = rg.klo;
+        s_khi[st][lane] = rg.khi;
+      }
+    }
+  };
+  // does the pair have a valid pair in tile (si, r0), held in stage st?
+  auto pair_active = [&](int si, int r0, int st) {
+    const SegArgs& g = a.seg[si];
+    const int tile_pre = g.kv_full + (g.diag ? min(r0 + kTileRows, g.q_len) : 0);
+    if constexpr (kDoc) {
+      const int tile_klo = s_klo[st][0];
+      const int tile_khi = s_khi[st][min(kTileRows, g.q_len - r0) - 1];
+      return !(w_key0 >= min(tile_pre, tile_khi) || w_key0 + 32 <= tile_klo);
+    }
+    return w_key0 < tile_pre;
+  };
+
+  bf16x8 kv[NT];  // K (S role) or V (dP role) of the lane's key
+  {
+    const void* src = role == 0 ? a.k : a.v;
+    const __bf16* p = static_cast<const __bf16*>(src) + (int64_t(krow) * a.heads + h) * D + 8 * hf;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) kv[i] = *reinterpret_cast<const bf16x8*>(p + 16 * i);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no wait for these inside the loop
+  f32x16 acc[NB];  // dV^T (S role) or dK^T (dP role)
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
+
+  int c_si = 0, c_r0 = -1;
+  km_seek<kDoc>(a, k0, c_si, c_r0);
+  bool c_ok = c_si < a.nseg;  // T_p exists
+  KmRegs rg;
+  if (c_ok) {
+    load_tile(c_si, c_r0, rg);
+    store_tile(0, rg);
+  }
+  lds_barrier();  // X_0
+  bool p_act = false;  // T_{p-1} exists and has work for the pair
+  int st = 0;          // stage of T_p; T_{p-1} in (st + 2) % 3, T_{p+1} goes to (st + 1) % 3
+  // Next tile: its place in the walk, and its prefetch into rg
+  auto next_tile = [&](int& n_si, int& n_r0, bool& n_ok) {
+    n_si = c_si;
+    n_r0 = c_r0 + kTileRows;
+    n_ok = false;
+    if (c_ok) {
+      km_seek<kDoc>(a, k0, n_si, n_r0);
+      n_ok = n_si < a.nseg;
+      if (n_ok) load_tile(n_si, n_r0, rg);
+    }
+  };
+  // End of phase p: the next tile to its stage, barrier X_{p+1}, advance.
+  // Returns false after phase n (T_{n-1} was the last tile).
+  auto end_phase = [&](int n_si, int n_r0, bool n_ok, bool c_act) {
+    const bool last = !c_ok;
+    if (!last) {
+      if (n_ok) store_tile(st == 2 ? 0 : st + 1, rg);
+      lds_barrier();  // X_{p+1}
+    }
+    p_act = c_act;
+    c_si = n_si;
+    c_r0 = n_r0;
+    c_ok = n_ok;
+    st = st == 2 ? 0 : st + 1;
+    return !last;
+  };
+  // The two roles run separate loops under a wave-uniform branch (the
+  // kernel is built with the structurizer skipping uniform regions: by
+  // default it would sequence the two loops behind flags, and the
+  // wait-count insertion would then see one role's loads in flight in the
+  // other's loop and stall its matrix work on them).
+  if (role == 0) {
+    f32x16 s[2];
+    bf16x8 wp[2][2];
+    for (bool more = c_ok; more;) {  // phases 0 .. n (none without a tile)
+      int n_si, n_r0;
+      bool n_ok;
+      next_tile(n_si, n_r0, n_ok);
+      const int ps = st == 0 ? 2 : st - 1;
+      const bool c_act = c_ok && pair_active(c_si, c_r0, st);
+      if (p_act) mm_tr_p(stage_o(ps), bs.tr, wp, acc);    // dV += dO(T_{p-1})^T P
+      if (c_act) mm_rows_p(stage_q(st), bs.row, kv, s);  // S(T_p)
+      lds_barrier();                                     // Y_p
+      if (c_act) {  // P(T_p): bf16 for dV, fp32 to the dP role through LDS
+        const SegArgs& g = a.seg[c_si];
+        // without document masks, element (qb, m, c) is valid iff
+        // 32 qb + 8 m + c >= thr: on a diagonal segment row t sees the key
+        // iff t >= key - kv_full, elsewhere every row sees it or none does
+        const int thr = g.diag ? key - g.kv_full - c_r0 - 4 * hf : (key < g.kv_full ? -1 : kTileRows);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int rl = 32 * qb + 8 * m + 4 * hf;  // tile row of register 4 m
+            const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[st][rl]);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            int klo[4] = {0, 0, 0, 0}, khi[4] = {a.n_loc, a.n_loc, a.n_loc, a.n_loc};
+            if constexpr (kDoc) {
+              const int4 lo4 = *reinterpret_cast<const int4*>(&s_klo[st][rl]);
+              const int4 hi4 = *reinterpret_cast<const int4*>(&s_khi[st][rl]);
+              klo[0] = lo4.x, klo[1] = lo4.y, klo[2] = lo4.z, klo[3] = lo4.w;
+              khi[0] = hi4.x, khi[1] = hi4.y, khi[2] = hi4.z, khi[3] = hi4.w;
+            }
+            float pv[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int e = 4 * m + c;
+              const int t = c_r0 + rl + c;
+              bool ok;
+              if constexpr (kDoc) ok = key < min(g.kv_full + (g.diag ? t + 1 : 0), khi[c]) && key >= klo[c];
+              else ok = 32 * qb + 8 * m + c >= thr;
+              const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][e], a.scale_log2, -lv[c]));
+              pv[c] = ok ? x : 0.f;
+              wp[qb][e >> 3][e & 7] = static_cast<__bf16>(pv[c]);
+            }
+            *reinterpret_cast<float4*>(pbuf + (4 * qb + m) * 256) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+          }
+        }
+      }
+      more = end_phase(n_si, n_r0, n_ok, c_act);
+    }
+  } else {
+    f32x16 dp[2];
+    bf16x8 ws[2][2];
+    for (bool more = c_ok; more;) {
+      int n_si, n_r0;
+      bool n_ok;
+      next_tile(n_si, n_r0, n_ok);
+      const int ps = st == 0 ? 2 : st - 1;
+      const bool c_act = c_ok && pair_active(c_si, c_r0, st);
+      if (p_act) {  // dS(T_{p-1}) = P (dP - D)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int rl = 32 * qb + 8 * m + 4 * hf;
+            const float4 d4 = *reinterpret_cast<const float4*>(&s_del[ps][rl]);
+            const float4 p4 = *reinterpret_cast<const float4*>(pbuf + (4 * qb + m) * 256);
+            const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+            const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int e = 4 * m + c;
+              ws[qb][e >> 3][e & 7] = static_cast<__bf16>(pv[c] * (dp[qb][e] - dl[c]));
+            }
+          }
+        }
+      }
+      lds_barrier();                                      // Y_p
+      if (p_act) mm_tr_p(stage_q(ps), bs.tr, ws, acc);    // dK += Q(T_{p-1})^T dS
+      if (c_act) mm_rows_p(stage_o(st), bs.row, kv, dp);  // dP(T_p)
+      more = end_phase(n_si, n_r0, n_ok, c_act);
+    }
+  }
+  if (!kok) return;
+  // lane (key, hf) holds d = 32 b + 8 m + 4 hf + c of its key
+  float* dst = (role == 0 ? a.dv : a.dk) + (int64_t(krow) * a.heads + h) * D;
+  const float f = role == 0 ? 1.f : a.scale;  // f * x is exactly x for dV
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int d0 = 32 * b + 8 * m + 4 * hf;
+      float4 x = *reinterpret_cast<float4*>(dst + d0);
+      x.x += f * acc[b][4 * m + 0];
+      x.y += f * acc[b][4 * m + 1];
+      x.z += f * acc[b][4 * m + 2];
+      x.w += f * acc[b][4 * m + 3];
+      *reinterpret_cast<float4*>(dst + d0) = x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Row-major: dQ of 128 rows.
 // ---------------------------------------------------------------------------
 template <bool kDoc>
@@ -425,14 +781,18 @@ int bwd_mfma_rows() { return kRows; }
 int bwd_mfma_keys() { return kKeys; }
 
 template <bool kDoc>
-hipError_t launch_bf16_d128(const BwdArgs& a, hipStream_t st) {
-  if (a.key_tiles > 0) bwd_dkdv_bf16_d128<kDoc><<<unsigned(a.key_tiles) * unsigned(a.heads), kThreads, 0, st>>>(a);
+hipError_t launch_bf16_d128(const BwdArgs& a, bool eight, hipStream_t st) {
+  if (a.key_tiles > 0) {
+    const unsigned grid = unsigned(a.key_tiles) * unsigned(a.heads);
+    if (eight) bwd_dkdv_bf16_d128x8<kDoc><<<grid, kThreads8, 0, st>>>(a);
+    else bwd_dkdv_bf16_d128<kDoc><<<grid, kThreads, 0, st>>>(a);
+  }
   if (a.total_tiles > 0) bwd_dq_bf16_d128<kDoc><<<unsigned(a.total_tiles) * unsigned(a.heads), kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t st) {
-  return a.doc ? launch_bf16_d128<true>(a, st) : launch_bf16_d128<false>(a, st);
+hipError_t launch_bwd_bf16_d128(const BwdArgs& a, bool eight_wave_keys, hipStream_t st) {
+  return a.doc ? launch_bf16_d128<true>(a, eight_wave_keys, st) : launch_bf16_d128<false>(a, eight_wave_keys, st);
 }
 
 }  // namespace cpattn

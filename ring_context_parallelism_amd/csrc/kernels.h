@@ -131,7 +131,7 @@ hipError_t launch_bwd_generic(const BwdArgs& a, int dtype_bf16, int head_dim, hi
 bool bwd_mfma(int dtype_bf16, int head_dim);  // the matrix-core kernels serve this configuration
 int bwd_mfma_rows();                          // rows per row-major workgroup
 int bwd_mfma_keys();                          // keys per key-major workgroup
-hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_bf16_d128(const BwdArgs& a, bool eight_wave_keys, hipStream_t stream);
 
 // attention step kernels: return hipError_t of the launch
 // (only the head_dim 128 bf16 kernel performs StepArgs::recv)

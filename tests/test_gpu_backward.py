@@ -136,6 +136,66 @@ def test_backward_is_deterministic():
     p.close()
 
 
+KEY_KERNEL_CASES = [c for c in CASES if c[6] == torch.bfloat16 and c[5] == 128]
+
+
+def _backward_with(p, kind, qd, kd, vd, out, lse, dod):
+    p.set_backward_key_kernel(kind)
+    g = [torch.full(qd.shape, float("nan"), dtype=torch.float32, device=qd.device) for _ in range(3)]
+    p.full_backward(qd, kd, vd, out, lse, dod, *g)
+    torch.cuda.synchronize()
+    return [t.cpu() for t in g]
+
+
+def _assert_same_bits(a, b, what):
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32)), (what, name)
+
+
+@pytest.mark.parametrize("case", KEY_KERNEL_CASES, ids=[_ids(c) for c in KEY_KERNEL_CASES])
+def test_eight_wave_key_kernel_matches_four_wave_bits(case):
+    """The eight-wave dK/dV kernel issues the same products in the same order
+    per key as the four-wave one: every gradient bit-identical."""
+    seq, cp, layout, causal, heads, dim, dtype = case
+    _say(f"key-major kernels, same bits: {_ids(case)}")
+    q, k, v, dout = _inputs(seq, heads, dim, dtype, 94)
+    p = Plan(seq, cp, heads, dim, causal, layout, dtype=dtype)
+    dev = _dev()
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+    out, lse = _forward(p, qd, kd, vd)
+    four = _backward_with(p, "four", qd, kd, vd, out, lse, dod)
+    eight = _backward_with(p, "eight", qd, kd, vd, out, lse, dod)
+    _assert_same_bits(four, eight, _ids(case))
+    p.close()
+
+
+def test_eight_wave_key_kernel_documents_and_full_size_bits():
+    """Same check with document masks (boundaries inside and on the edges of
+    64-row tiles) and on the 32k-token, cp 8 workload (32 heads x 128)."""
+    from ring_context_parallelism_amd.inputs import WORKLOADS, workload_qkv
+    dev = _dev()
+    seq, cp, heads, dim = 1536, 2, 2, 128
+    _say("key-major kernels, same bits: documents s1536 cp2")
+    q, k, v, dout = _inputs(seq, heads, dim, torch.bfloat16, 95)
+    p = Plan(seq, cp, heads, dim, True, "zigzag")
+    p.set_documents([0, 1, 2, 64, 128, 129, 500, 777, 1535])
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+    out, lse = _forward(p, qd, kd, vd)
+    _assert_same_bits(_backward_with(p, "four", qd, kd, vd, out, lse, dod),
+                      _backward_with(p, "eight", qd, kd, vd, out, lse, dod), "documents")
+    p.close()
+    w = WORKLOADS["causal_s32768_cp8_zigzag_h32_d128_bf16_rank0"]
+    _say(f"key-major kernels, same bits: {w.name}")
+    q, k, v = workload_qkv(w)
+    dout = make_qkv(w.seq_len, w.heads, w.head_dim, "bf16", w.seed + 7)[0]
+    p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, True, w.layout)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+    out, lse = _forward(p, qd, kd, vd)
+    _assert_same_bits(_backward_with(p, "four", qd, kd, vd, out, lse, dod),
+                      _backward_with(p, "eight", qd, kd, vd, out, lse, dod), w.name)
+    p.close()
+
+
 def test_full_size_backward_sampled_rows_and_gradient_sums():
     """The 32k-token, cp 8 zigzag workload (32 heads x 128, bf16): dQ of sampled
     rows against the oracle, and two properties of the complete key/value

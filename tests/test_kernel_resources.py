@@ -24,7 +24,7 @@ def _resources(source="attn_bf16.hip"):
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "kernels.s")
         flags = [f for f in B.COMMON if f != "-fPIC"]
-        cmd = [B.hipcc(), "-x", "hip", *B.HIP_FLAGS, *flags, "--cuda-device-only", "-S",
+        cmd = [B.hipcc(), "-x", "hip", *B.HIP_FLAGS, *B.TU_FLAGS.get(source, []), *flags, "--cuda-device-only", "-S",
                os.path.join(B.CSRC, source), "-o", out]
         subprocess.run(cmd, check=True, capture_output=True, timeout=600)
         text = open(out).read()
@@ -58,7 +58,8 @@ def test_no_kernel_spills_to_scratch(resources):
 
 def test_backward_kernels_do_not_spill():
     """The matrix-core backward kernels keep every value in registers; the
-    row-major dQ kernel stays within 256 VGPRs, so two workgroups share a CU."""
+    row-major dQ kernel stays within 256 VGPRs, so two workgroups share a CU,
+    and so does the eight-wave key-major kernel (two of its waves per SIMD)."""
     try:
         B.hipcc()
     except RuntimeError:
@@ -69,3 +70,5 @@ def test_backward_kernels_do_not_spill():
         assert r["scratch"] == 0, (name, r)
     dq = [v for k, v in res.items() if "bwd_dq_bf16_d128ILb0E" in k]
     assert len(dq) == 1 and dq[0]["vgpr"] <= 256, dq
+    x8 = [v for k, v in res.items() if "bwd_dkdv_bf16_d128x8" in k]
+    assert len(x8) == 2 and all(v["vgpr"] <= 256 for v in x8), x8
