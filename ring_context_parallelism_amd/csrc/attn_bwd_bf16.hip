@@ -36,9 +36,11 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "epilogue.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace cpattn {
 namespace {
@@ -382,26 +384,43 @@ __device__ __forceinline__ void mm_tr_p(const lds_u8* tile, const uint32_t (&tr)
   __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // groups 2 and 3 MFMAs
 }
 
-// Workgroup barrier that orders LDS accesses only: global loads in flight
-// (the next tile's prefetch) stay in flight across it.
+// Workgroup barrier that orders LDS accesses only: global and direct-to-LDS
+// loads in flight stay in flight across it (a wave waits for its own
+// direct-to-LDS loads with vmcnt before the barrier that publishes them).
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Segment si of the step (0 or 1) by field-wise selection from two copies
+// held in scalar registers: no indexed load of the kernel arguments inside
+// the tile loop (a chain of dependent scalar loads each phase).
+__device__ __forceinline__ SegArgs seg_pick(const SegArgs& x, const SegArgs& y, int si) {
+  SegArgs r;
+  r.q_global = si ? y.q_global : x.q_global;
+  r.q_start = si ? y.q_start : x.q_start;
+  r.q_len = si ? y.q_len : x.q_len;
+  r.kv_full = si ? y.kv_full : x.kv_full;
+  r.diag = si ? y.diag : x.diag;
+  r.epi = si ? y.epi : x.epi;
+  r.tiles = si ? y.tiles : x.tiles;
+  r.ksplit = si ? y.ksplit : x.ksplit;
+  return r;
+}
+
 // The next 64-row tile of a key-major workgroup's walk (keys k0 .. k0 + 127):
 // the search starts at row r0 of segment si (r0 < 0: the segment's first
 // tile).  Rows before a segment's first tile see none of the keys; with
 // document masks the walk leaves a segment at the first tile whose first
-// row's run starts past them.  Leaves si = nseg when no tile is left.
+// row's run starts past them.  Leaves si = nseg when no tile is left.  One
+// exit, at the loop's end.
 template <bool kDoc>
-__device__ __forceinline__ void km_seek(const BwdArgs& a, int k0, int& si, int& r0) {
-  // one exit, at the loop's end (with early exits the compiler linearizes
-  // the two role branches of the kernel below, see there)
+__device__ __forceinline__ void km_seek(const BwdArgs& a, const SegArgs& s0, const SegArgs& s1, int k0, int& si,
+                                        int& r0) {
   bool found = false;
   while (!found && si < a.nseg) {
-    const SegArgs& g = a.seg[si];
+    const SegArgs g = seg_pick(s0, s1, si);
     // row t sees keys < kv_full + t + 1 on a diagonal segment
     const int t0 = k0 < g.kv_full ? 0 : (g.diag ? k0 - g.kv_full : g.q_len);
     if (r0 < 0) r0 = t0;
@@ -420,12 +439,12 @@ __device__ __forceinline__ void km_seek(const BwdArgs& a, int k0, int& si, int& 
   }
 }
 
-// One tile's prefetch: two 16-byte chunks of Q and of dO per thread, and
-// (threads 0..63) the row's log2-scaled LSE, D and document run.
-struct KmRegs {
-  u32x4 q[2], o[2];
-  float lse, del;  // raw; rows at or past `rows` are replaced at the store
-  int rows;        // valid rows of the tile
+// Per-row tables of one tile, loaded by wave 0 (a lane per row) one phase
+// ahead: raw LSE and D (rows at or past `rows` are replaced when stored),
+// and the rows' document runs.
+struct KmRows {
+  float lse, del;
+  int rows;
   int klo, khi;
 };
 
@@ -453,50 +472,61 @@ void bwd_dkdv_bf16_d128x8(BwdArgs a) {
   const uint32_t hoff = uint32_t(h) * 256;
   const Bases bs = make_bases(lane);
   float* const pbuf = s_p + pw * (2 * 4 * 64 * 4) + lane * 4;  // + (4 qb + m) * 256: float4 of the lane
+  const SegArgs sg0 = a.seg[0], sg1 = a.seg[1];
 
   auto stage_q = [&](int st) { return (lds_u8*)smem + st * 2 * kTileBytes; };
   auto stage_o = [&](int st) { return (lds_u8*)smem + st * 2 * kTileBytes + kTileBytes; };
 
-  auto load_tile = [&](int si, int r0, KmRegs& rg) {
-    const SegArgs& g = a.seg[si];
+  // Tile loads straight into LDS: 32 loads of 1 KiB per tile (Q, then dO,
+  // four rows each: lane = row 4 b + lane / 16 of block b, physical chunk
+  // lane % 16, which holds logical chunk (lane % 16) ^ swz(row)).  Pair pw
+  // issues loads 8 pw .. 8 pw + 7 (Q for pairs 0-1, dO for pairs 2-3): its
+  // S-role wave the first two, during its P work, its dP-role wave the other
+  // six, during its dS work (which is shorter than the other wave's matrix
+  // work, while P is not).  Offsets are 32-bit: the plan keeps every tensor
+  // below 4 GiB.
+  const dma_u32x4 desc = buffer_desc(pw < 2 ? a.q : a.dout, uint32_t(a.seq_len) * row_bytes);
+  const int dma_r = 32 * (pw & 1) + (lane >> 4);  // + 4 j: the lane's tile row for load 8 pw + j
+  uint32_t dma_c[4];  // + row * row_bytes: the lane's global byte offset (depends on j mod 4)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kThreads8 * i;
-      const int r = c >> 4, ch = c & 15;
-      const uint64_t off = uint64_t(g.q_global + min(r0 + r, g.q_len - 1)) * row_bytes + hoff + ch * 16;
-      rg.q[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + off);
-      rg.o[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.dout) + off);
-    }
-    if (wv == 0) {  // the tile's rows, one per lane (clamped loads, then selects: no lane branches)
-      const int tc = min(r0 + lane, g.q_len - 1);
-      rg.lse = a.lse[int64_t(h) * a.seq_len + g.q_global + tc];
-      rg.del = a.delta[int64_t(h) * a.n_loc + g.q_start + tc];
-      rg.rows = g.q_len - r0;
-      if constexpr (kDoc) doc_row_keys(a, g.q_global + tc, rg.klo, rg.khi);
+  for (int j = 0; j < 4; ++j) dma_c[j] = uint32_t(((lane & 15) ^ swz((dma_r + 4 * j) & 15)) << 4) + hoff;
+  auto issue_loads = [&](int si, int r0, int st, auto j0, auto j1) {
+    const SegArgs g = seg_pick(sg0, sg1, si);
+    const uint32_t dst = lds_addr((pw < 2 ? stage_q(st) : stage_o(st)) + 32 * (pw & 1) * 256);
+#pragma unroll
+    for (int j = decltype(j0)::value; j < decltype(j1)::value; ++j) {
+      const int row = int(g.q_global) + min(r0 + dma_r + 4 * j, g.q_len - 1);
+      // 24-bit multiply: row and row_bytes are below 2^24 and their product
+      // below 2^32 (a 64-bit multiply-add here reads an undefined high half
+      // that can alias a register with a load in flight, and then waits for it)
+      dma_lds16(desc, __umul24(uint32_t(row), row_bytes) + dma_c[j & 3], 0u, dst + j * 1024);
     }
   };
-  auto store_tile = [&](int st, const KmRegs& rg) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kThreads8 * i;
-      const int r = c >> 4, ch = c & 15;
-      const uint32_t o = r * 256 + ((ch ^ swz(r & 15)) << 4);
-      *reinterpret_cast<lds_u32x4*>(stage_q(st) + o) = rg.q[i];
-      *reinterpret_cast<lds_u32x4*>(stage_o(st) + o) = rg.o[i];
-    }
-    if (wv == 0) {  // rows past the segment: LSE = +inf (P = 0), D = 0
-      const bool ok = lane < rg.rows;
-      s_lse[st][lane] = ok ? rg.lse * kLog2e : INFINITY;
-      s_del[st][lane] = ok ? rg.del : 0.f;
-      if constexpr (kDoc) {
-        s_klo[st][lane] = rg.klo;
-        s_khi[st][lane] = rg.khi;
-      }
+  using I0 = std::integral_constant<int, 0>;
+  using I2 = std::integral_constant<int, 2>;
+  using I8 = std::integral_constant<int, 8>;
+  auto issue_tile = [&](int si, int r0, int st) { issue_loads(si, r0, st, I0{}, I8{}); };  // prologue
+  auto load_rows = [&](int si, int r0, KmRows& rg) {  // wave 0
+    const SegArgs g = seg_pick(sg0, sg1, si);
+    const int tc = min(r0 + lane, g.q_len - 1);
+    rg.lse = a.lse[int64_t(h) * a.seq_len + g.q_global + tc];
+    rg.del = a.delta[int64_t(h) * a.n_loc + g.q_start + tc];
+    rg.rows = g.q_len - r0;
+    if constexpr (kDoc) doc_row_keys(a, g.q_global + tc, rg.klo, rg.khi);
+  };
+  // wave 0; rows past the segment: LSE = +inf (P = 0), D = 0
+  auto store_rows = [&](int st, const KmRows& rg) {
+    const bool ok = lane < rg.rows;
+    s_lse[st][lane] = ok ? rg.lse * kLog2e : INFINITY;
+    s_del[st][lane] = ok ? rg.del : 0.f;
+    if constexpr (kDoc) {
+      s_klo[st][lane] = rg.klo;
+      s_khi[st][lane] = rg.khi;
     }
   };
   // does the pair have a valid pair in tile (si, r0), held in stage st?
   auto pair_active = [&](int si, int r0, int st) {
-    const SegArgs& g = a.seg[si];
+    const SegArgs g = seg_pick(sg0, sg1, si);
     const int tile_pre = g.kv_full + (g.diag ? min(r0 + kTileRows, g.q_len) : 0);
     if constexpr (kDoc) {
       const int tile_klo = s_klo[st][0];
@@ -513,40 +543,44 @@ void bwd_dkdv_bf16_d128x8(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) kv[i] = *reinterpret_cast<const bf16x8*>(p + 16 * i);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no wait for these inside the loop
   f32x16 acc[NB];  // dV^T (S role) or dK^T (dP role)
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
 
   int c_si = 0, c_r0 = -1;
-  km_seek<kDoc>(a, k0, c_si, c_r0);
+  km_seek<kDoc>(a, sg0, sg1, k0, c_si, c_r0);
   bool c_ok = c_si < a.nseg;  // T_p exists
-  KmRegs rg;
+  KmRows rg{};
   if (c_ok) {
-    load_tile(c_si, c_r0, rg);
-    store_tile(0, rg);
+    if (role == 0) issue_tile(c_si, c_r0, 0);  // the S-role waves load T_0 alone
+    if (wv == 0) {
+      load_rows(c_si, c_r0, rg);
+      store_rows(0, rg);
+    }
   }
-  lds_barrier();  // X_0
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the K/V rows above and this wave's tile loads
+  lds_barrier();                       // X_0
   bool p_act = false;  // T_{p-1} exists and has work for the pair
   int st = 0;          // stage of T_p; T_{p-1} in (st + 2) % 3, T_{p+1} goes to (st + 1) % 3
-  // Next tile: its place in the walk, and its prefetch into rg
   auto next_tile = [&](int& n_si, int& n_r0, bool& n_ok) {
     n_si = c_si;
     n_r0 = c_r0 + kTileRows;
     n_ok = false;
     if (c_ok) {
-      km_seek<kDoc>(a, k0, n_si, n_r0);
+      km_seek<kDoc>(a, sg0, sg1, k0, n_si, n_r0);
       n_ok = n_si < a.nseg;
-      if (n_ok) load_tile(n_si, n_r0, rg);
+      if (n_ok && wv == 0) load_rows(n_si, n_r0, rg);
     }
   };
-  // End of phase p: the next tile to its stage, barrier X_{p+1}, advance.
-  // Returns false after phase n (T_{n-1} was the last tile).
+  // End of phase p: the next tile's row tables, wait for this wave's loads
+  // of T_{p+1}, barrier X_{p+1}, advance.  Returns false after phase n
+  // (T_{n-1} was the last tile).
   auto end_phase = [&](int n_si, int n_r0, bool n_ok, bool c_act) {
     const bool last = !c_ok;
     if (!last) {
-      if (n_ok) store_tile(st == 2 ? 0 : st + 1, rg);
-      lds_barrier();  // X_{p+1}
+      if (n_ok && wv == 0) store_rows(st == 2 ? 0 : st + 1, rg);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      lds_barrier();                       // X_{p+1}
     }
     p_act = c_act;
     c_si = n_si;
@@ -572,41 +606,59 @@ void bwd_dkdv_bf16_d128x8(BwdArgs a) {
       if (p_act) mm_tr_p(stage_o(ps), bs.tr, wp, acc);    // dV += dO(T_{p-1})^T P
       if (c_act) mm_rows_p(stage_q(st), bs.row, kv, s);  // S(T_p)
       lds_barrier();                                     // Y_p
+      float4 l4[2][4];
+      if (c_act) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            l4[qb][m] = *reinterpret_cast<const float4*>(&s_lse[st][32 * qb + 8 * m + 4 * hf]);
+      }
+      if (n_ok) issue_loads(n_si, n_r0, st == 2 ? 0 : st + 1, I0{}, I2{});  // two loads of T_{p+1}
       if (c_act) {  // P(T_p): bf16 for dV, fp32 to the dP role through LDS
-        const SegArgs& g = a.seg[c_si];
+        const SegArgs g = seg_pick(sg0, sg1, c_si);
         // without document masks, element (qb, m, c) is valid iff
         // 32 qb + 8 m + c >= thr: on a diagonal segment row t sees the key
         // iff t >= key - kv_full, elsewhere every row sees it or none does
         const int thr = g.diag ? key - g.kv_full - c_r0 - 4 * hf : (key < g.kv_full ? -1 : kTileRows);
+        // every element valid (wave-uniform): no mask work at all
+        const bool dense = !kDoc && __all(thr <= 0);
+        auto p_tile = [&](auto masked) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+          for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int rl = 32 * qb + 8 * m + 4 * hf;  // tile row of register 4 m
-            const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[st][rl]);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            int klo[4] = {0, 0, 0, 0}, khi[4] = {a.n_loc, a.n_loc, a.n_loc, a.n_loc};
-            if constexpr (kDoc) {
-              const int4 lo4 = *reinterpret_cast<const int4*>(&s_klo[st][rl]);
-              const int4 hi4 = *reinterpret_cast<const int4*>(&s_khi[st][rl]);
-              klo[0] = lo4.x, klo[1] = lo4.y, klo[2] = lo4.z, klo[3] = lo4.w;
-              khi[0] = hi4.x, khi[1] = hi4.y, khi[2] = hi4.z, khi[3] = hi4.w;
+            for (int m = 0; m < 4; ++m) {
+              const int rl = 32 * qb + 8 * m + 4 * hf;  // tile row of register 4 m
+              const float lv[4] = {l4[qb][m].x, l4[qb][m].y, l4[qb][m].z, l4[qb][m].w};
+              int klo[4] = {0, 0, 0, 0}, khi[4] = {a.n_loc, a.n_loc, a.n_loc, a.n_loc};
+              if constexpr (kDoc) {
+                const int4 lo4 = *reinterpret_cast<const int4*>(&s_klo[st][rl]);
+                const int4 hi4 = *reinterpret_cast<const int4*>(&s_khi[st][rl]);
+                klo[0] = lo4.x, klo[1] = lo4.y, klo[2] = lo4.z, klo[3] = lo4.w;
+                khi[0] = hi4.x, khi[1] = hi4.y, khi[2] = hi4.z, khi[3] = hi4.w;
+              }
+              float pv[4];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const int e = 4 * m + c;
+                const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][e], a.scale_log2, -lv[c]));
+                if constexpr (decltype(masked)::value) {
+                  const int t = c_r0 + rl + c;
+                  bool ok;
+                  if constexpr (kDoc) ok = key < min(g.kv_full + (g.diag ? t + 1 : 0), khi[c]) && key >= klo[c];
+                  else ok = 32 * qb + 8 * m + c >= thr;
+                  pv[c] = ok ? x : 0.f;
+                } else {
+                  pv[c] = x;
+                }
+                wp[qb][e >> 3][e & 7] = static_cast<__bf16>(pv[c]);
+              }
+              *reinterpret_cast<float4*>(pbuf + (4 * qb + m) * 256) = make_float4(pv[0], pv[1], pv[2], pv[3]);
             }
-            float pv[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int e = 4 * m + c;
-              const int t = c_r0 + rl + c;
-              bool ok;
-              if constexpr (kDoc) ok = key < min(g.kv_full + (g.diag ? t + 1 : 0), khi[c]) && key >= klo[c];
-              else ok = 32 * qb + 8 * m + c >= thr;
-              const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][e], a.scale_log2, -lv[c]));
-              pv[c] = ok ? x : 0.f;
-              wp[qb][e >> 3][e & 7] = static_cast<__bf16>(pv[c]);
-            }
-            *reinterpret_cast<float4*>(pbuf + (4 * qb + m) * 256) = make_float4(pv[0], pv[1], pv[2], pv[3]);
           }
-        }
+        };
+        if (dense) p_tile(std::false_type{});
+        else p_tile(std::true_type{});
       }
       more = end_phase(n_si, n_r0, n_ok, c_act);
     }
@@ -619,16 +671,22 @@ void bwd_dkdv_bf16_d128x8(BwdArgs a) {
       next_tile(n_si, n_r0, n_ok);
       const int ps = st == 0 ? 2 : st - 1;
       const bool c_act = c_ok && pair_active(c_si, c_r0, st);
+      float4 p4[2][4];
+      if (p_act) {  // P of T_{p-1}: these reads first
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) p4[qb][m] = *reinterpret_cast<const float4*>(pbuf + (4 * qb + m) * 256);
+      }
+      if (n_ok) issue_loads(n_si, n_r0, st == 2 ? 0 : st + 1, I2{}, I8{});  // six loads of T_{p+1}
       if (p_act) {  // dS(T_{p-1}) = P (dP - D)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const int rl = 32 * qb + 8 * m + 4 * hf;
-            const float4 d4 = *reinterpret_cast<const float4*>(&s_del[ps][rl]);
-            const float4 p4 = *reinterpret_cast<const float4*>(pbuf + (4 * qb + m) * 256);
+            const float4 d4 = *reinterpret_cast<const float4*>(&s_del[ps][32 * qb + 8 * m + 4 * hf]);
             const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
-            const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+            const float pv[4] = {p4[qb][m].x, p4[qb][m].y, p4[qb][m].z, p4[qb][m].w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const int e = 4 * m + c;
@@ -672,12 +730,18 @@ void bwd_dq_bf16_d128(BwdArgs a) {
   lds_u8* const tk = (lds_u8*)smem;
   lds_u8* const tv = tk + kTileBytes;
 
-  const int h = blockIdx.x / a.total_tiles;
-  int t = blockIdx.x % a.total_tiles;
-  const int si = t < a.seg[0].tiles ? 0 : 1;
-  if (si) t -= a.seg[0].tiles;
+  // Dispatch order, longest workgroups first: tile-major over the heads,
+  // the segment whose rows see more keys first, and on a diagonal segment
+  // its last (longest) rows first.  Each workgroup's result does not
+  // depend on the order.
+  const int h = blockIdx.x % a.heads;
+  int t = blockIdx.x / a.heads;
+  auto keys_of = [](const SegArgs& x) { return int64_t(x.kv_full) + (x.diag ? x.q_len : 0); };
+  const int s0 = a.nseg == 2 && keys_of(a.seg[1]) > keys_of(a.seg[0]) ? 1 : 0;
+  const int si = t < a.seg[s0].tiles ? s0 : 1 - s0;
+  if (si != s0) t -= a.seg[s0].tiles;
   const SegArgs& g = a.seg[si];
-  if (g.diag) t = g.tiles - 1 - t;  // longest rows first
+  if (g.diag) t = g.tiles - 1 - t;
   const int row0 = t * kRows;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
