@@ -108,7 +108,7 @@ def step_kernel_times(plan, w, bufs, stream, reps, graph=False):
 
 PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                        "attn_step_bf16_d128_causal_s32768_cp8_rank0.md")
-KERNEL_SOURCES = ("attn_bf16.hip", "epilogue.h", "kernels.h")
+KERNEL_SOURCES = ("attn_bf16.hip", "epilogue.h", "kernels.h", "lds_dma.h")
 
 
 def recorded_traffic(workload):

@@ -807,17 +807,27 @@ void bwd_dq_bf16_d128(BwdArgs a) {
     f32x16 s[2], dp[2];
     mm_rows(tk, bs.row, qf, s);
     mm_rows(tv, bs.row, dof, dp);
+    // P in place of S; the mask is a pass of its own, taken only when some
+    // row of the wave does not see every key of the tile (rows past the
+    // segment have LSE = +inf, so their P is 0 either way)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = __builtin_amdgcn_exp2f(fmaf(s[kb][e], a.scale_log2, -lse2));
+    if (kDoc || !__all(!ok || j0 + kTileRows <= prefix)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kk = j0 + 32 * kb + 8 * (e >> 2) + 4 * hf + (e & 3);
+          if (!(kk < prefix && (!kDoc || kk >= klo))) s[kb][e] = 0.f;
+        }
+    }
     bf16x8 ws[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kk = j0 + 32 * kb + 8 * (e >> 2) + 4 * hf + (e & 3);
-        const float p = kk < prefix && (!kDoc || kk >= klo)
-                            ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], a.scale_log2, -lse2))
-                            : 0.f;
-        ws[kb][e >> 3][e & 7] = static_cast<__bf16>(p * (dp[kb][e] - del));
-      }
+      for (int e = 0; e < 16; ++e) ws[kb][e >> 3][e & 7] = static_cast<__bf16>(s[kb][e] * (dp[kb][e] - del));
     mm_tr(tk, bs.tr, ws, dq);
   }
   if (!ok) return;
