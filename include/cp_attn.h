@@ -128,8 +128,11 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
  * cp_attn_rank_valid_rows of its local buffer.  The natural-order tensors
  * still hold S rows: pad rows exist only in the local layout.
  * Returns EINVAL for non-positive sizes or a bad flag or layout; EUNSUPPORTED
- * for another head_dim, cp_size > 256, or S_pad * heads * head_dim * 4 >=
- * 2^32 (device offsets are 32-bit).
+ * for another head_dim, cp_size > 256, (S_pad / cp_size) * heads * head_dim
+ * * 4 >= 2^32 (one rank's rows are addressed with 32-bit offsets), or
+ * S_pad >= 2^31.  The natural-order tensors may exceed 4 GiB (beyond that,
+ * each rank's first ring step reads its own K/V chunks from a receive slot
+ * filled by one extra copy instead of in place).
  * On success *out owns the plan; free it with cp_attn_plan_destroy.
  */
 int cp_attn_plan(int64_t seq_len, int cp_size, int heads, int head_dim, int causal, int layout,

@@ -222,6 +222,14 @@ RunCfg plan_cfg(const Plan& p, bool capturing) {
 // into slot b is two or four linear copies.  Only real rows are received: a
 // chunk's pad rows (and a chunk of pad only) are not copied, and the kernels
 // never read past the source's real keys.
+// The step kernels address K/V with 32-bit byte offsets from one base.  The
+// natural-order tensors are read in place at step 0 only while they span at
+// most 4 GiB; beyond that step 0, like every later step, reads the rank's own
+// chunks from receive slot 0, filled by one copy before it.
+bool kv_beyond_32bit(const Plan& p) {
+  return p.seq_len * p.heads * p.head_dim * p.elem_bytes() > int64_t(UINT32_MAX);
+}
+
 RecvArgs recv_ranges(const Plan& p, char* ws, const void* k, const void* v, int src, int b) {
   const WsLayout w = ws_layout(p);
   char* dk = ws + w.slot_k[b];
@@ -329,7 +337,7 @@ int launch_step(Plan& p, const RunCfg& c, const void* q, const void* k, const vo
   StepArgs a{};
   a.q = q;
   const int32_t split = int32_t(p.layout == 1 ? p.chunk : p.n_loc);
-  if (s == 0) {
+  if (s == 0 && !kv_beyond_32bit(p)) {  // the rank's own chunks, read in place
     a.k = k;
     a.v = v;
     a.kv_bytes = p.seq_len * p.heads * p.head_dim * p.elem_bytes();
@@ -491,6 +499,8 @@ int run_rank(Plan& p, const RunCfg& c, const void* q, const void* k, const void*
     if (copy_side) CPA_HIP(hipStreamWaitEvent(cs, d.start, 0));
     if (merge_side) CPA_HIP(hipStreamWaitEvent(ms, d.start, 0));
   }
+  const bool self_copy = kv_beyond_32bit(p);
+  if (self_copy) CPA_HIP(launch_recv(recv_ranges(p, ws, k, v, r, 0), 0, st));  // own chunks into slot 0
   for (int s = 0; s < P; ++s) {
     const int b = s & 1;
     if (side_recv(p, c, s)) {
@@ -511,7 +521,7 @@ int run_rank(Plan& p, const RunCfg& c, const void* q, const void* k, const void*
       CPA_HIP(hipEventRecord(d.t1[ti], st));
       d.timed[ti] = 1;
     }
-    if (c.poison && s >= 1) {
+    if (c.poison && (s >= 1 || self_copy)) {
       CPA_HIP(launch_poison(ws + w.slot_k[b], w.kv_bytes, st));
       CPA_HIP(launch_poison(ws + w.slot_v[b], w.kv_bytes, st));
     }

@@ -483,19 +483,23 @@ void bwd_dkdv_bf16_d128x8(BwdArgs a) {
   // issues loads 8 pw .. 8 pw + 7 (Q for pairs 0-1, dO for pairs 2-3): its
   // S-role wave the first two, during its P work, its dP-role wave the other
   // six, during its dS work (which is shorter than the other wave's matrix
-  // work, while P is not).  Offsets are 32-bit: the plan keeps every tensor
-  // below 4 GiB.
-  const dma_u32x4 desc = buffer_desc(pw < 2 ? a.q : a.dout, uint32_t(a.seq_len) * row_bytes);
+  // work, while P is not).  Offsets are 32-bit, from a base at each
+  // segment's first row (a segment spans at most the rank's rows, which the
+  // plan keeps below 4 GiB).
+  const char* const dma_src = static_cast<const char*>(pw < 2 ? a.q : a.dout);
+  const dma_u32x4 desc0 = buffer_desc(dma_src + uint64_t(sg0.q_global) * row_bytes, uint32_t(sg0.q_len) * row_bytes);
+  const dma_u32x4 desc1 = buffer_desc(dma_src + uint64_t(sg1.q_global) * row_bytes, uint32_t(sg1.q_len) * row_bytes);
   const int dma_r = 32 * (pw & 1) + (lane >> 4);  // + 4 j: the lane's tile row for load 8 pw + j
   uint32_t dma_c[4];  // + row * row_bytes: the lane's global byte offset (depends on j mod 4)
 #pragma unroll
   for (int j = 0; j < 4; ++j) dma_c[j] = uint32_t(((lane & 15) ^ swz((dma_r + 4 * j) & 15)) << 4) + hoff;
   auto issue_loads = [&](int si, int r0, int st, auto j0, auto j1) {
     const SegArgs g = seg_pick(sg0, sg1, si);
+    const dma_u32x4 desc = si ? desc1 : desc0;
     const uint32_t dst = lds_addr((pw < 2 ? stage_q(st) : stage_o(st)) + 32 * (pw & 1) * 256);
 #pragma unroll
     for (int j = decltype(j0)::value; j < decltype(j1)::value; ++j) {
-      const int row = int(g.q_global) + min(r0 + dma_r + 4 * j, g.q_len - 1);
+      const int row = min(r0 + dma_r + 4 * j, g.q_len - 1);  // of the segment
       // 24-bit multiply: row and row_bytes are below 2^24 and their product
       // below 2^32 (a 64-bit multiply-add here reads an undefined high half
       // that can alias a register with a load in flight, and then waits for it)

@@ -228,9 +228,17 @@ int make_plan(int64_t seq_len, int cp, int heads, int head_dim, int causal, int 
     *err = "head_dim must be 64 or 128";
     return kUnsupported;
   }
-  // K/V tensors are addressed with 32-bit byte offsets on the device
-  if (padded * int64_t(heads) * head_dim * 4 >= (int64_t(1) << 32)) {
-    *err = "padded seq_len * heads * head_dim * 4 must stay below 2^32 bytes";
+  // The kernels address one rank's rows (a receive slot, a segment, the
+  // fp32 running state) with 32-bit byte offsets from a base, and token rows
+  // with 32-bit integers; natural-order tensors are otherwise addressed with
+  // 64-bit offsets (beyond 4 GiB of K/V, step 0 reads the rank's own chunks
+  // from a receive slot rather than in place).
+  if (padded / cp * int64_t(heads) * head_dim * 4 >= (int64_t(1) << 32)) {
+    *err = "(padded seq_len / cp_size) * heads * head_dim * 4 must stay below 2^32 bytes";
+    return kUnsupported;
+  }
+  if (padded >= (int64_t(1) << 31)) {
+    *err = "padded seq_len must stay below 2^31";
     return kUnsupported;
   }
   Plan* p = new Plan;

@@ -160,12 +160,18 @@ def test_plan_error_codes():
         ((64, 2, 2, 128, 1, 7), N.EINVAL),               # layout
         ((64, 2, 2, 96, 1, N.ZIGZAG), N.EUNSUPPORTED),   # head_dim
         ((1024, 512, 2, 128, 1, N.ZIGZAG), N.EUNSUPPORTED),  # cp > 256
+        ((1 << 20, 1, 32, 128, 1, N.ZIGZAG), N.EUNSUPPORTED),  # one rank's fp32 rows reach 2^32 bytes
+        ((1 << 31, 256, 1, 64, 1, N.ZIGZAG), N.EUNSUPPORTED),  # 2^31 tokens
     ]
     for args, want in cases:
         assert lib.cp_attn_plan(*args, ctypes.byref(h)) == want, args
         assert not h.value
         assert lib.cp_attn_last_error()
     assert lib.cp_attn_plan(64, 2, 2, 128, 1, N.ZIGZAG, None) == N.EINVAL
+    # natural-order tensors beyond 4 GiB are fine while one rank's rows stay below it
+    for args in ((1 << 19, 16, 32, 128, 1, N.ZIGZAG), ((1 << 20) - 5, 8, 16, 128, 1, N.CONTIGUOUS)):
+        assert lib.cp_attn_plan(*args, ctypes.byref(h)) == N.OK, args
+        assert lib.cp_attn_plan_destroy(h) == N.OK
     for s in (N.OK, N.EINVAL, N.EUNSUPPORTED, N.ENOWORKSPACE, N.EHIP, 12345):
         assert lib.cp_attn_status_string(s)
 
