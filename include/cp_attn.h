@@ -307,8 +307,12 @@ int cp_attn_local_rows(cp_attn_plan_t plan, int64_t* rows);
  * tail chunks otherwise, possibly 0).  EINVAL for a bad rank or null rows. */
 int cp_attn_rank_valid_rows(cp_attn_plan_t plan, int rank, int64_t* rows);
 
-/* Chunk indices owned by `rank`, local order; *count = 2 (zigzag) or 1
- * (contiguous, where the chunk index equals the rank). */
+/* Chunk indices owned by `rank`, local order ("Sequence Parallelism IV:
+ * Megatron Context Parallel and Load-Balanced Rings", section 3: rank r holds
+ * chunks r and 2cp-1-r under zigzag); *count = 2 (zigzag) or 1 (contiguous,
+ * where the chunk index equals the rank).  `count` is an addition to the
+ * plain (rank) -> chunk pair: a contiguous plan owns one chunk, and the
+ * caller is told so instead of reading an unused second entry. */
 int cp_attn_rank_chunks(cp_attn_plan_t plan, int rank, int32_t chunks[2], int32_t* count);
 
 /* Ring source of (rank, step): (rank - step) mod cp_size. */
