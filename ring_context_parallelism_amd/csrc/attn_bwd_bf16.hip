@@ -16,12 +16,9 @@
 //   dV^T += dO^T P and dK^T += Q^T dS   (A = dO^T / Q^T read transposed
 //   from the same tiles with ds_read_b64_tr_b16; B = P / dS straight from
 //   the registers of S, rounded to bf16, rows in register order)
-// Row-major kernel (dQ): a workgroup of 4 waves owns 128 rows, 32 per wave,
-// whose Q and dO stay in registers; K/V tiles of 64 keys in LDS:
+// Row-major kernel (dQ): a workgroup of 8 waves owns 256 rows, 32 per wave,
+// whose Q and dO stay in registers; K/V tiles of 64 keys stream into LDS:
 //   S^T = K Q^T, dP^T = V dO^T, dS^T as above, dQ^T += K^T dS^T.
-// It loads each tile when it needs it (no register prefetch), which keeps it
-// within 256 VGPRs: two workgroups share a CU and one computes while the
-// other waits for its tile.
 // Rows past a segment's end carry LSE = +inf, so their P is exactly zero;
 // keys past the source's real keys are clamped to its last real row and
 // masked.  The key-major kernel loads its tiles to registers one tile ahead
@@ -58,7 +55,6 @@ constexpr int D = 128;
 constexpr int NT = D / 16;     // k-steps over the head dimension
 constexpr int NB = D / 32;     // 32-row blocks of a transposed gradient
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kRows = 128;     // rows per row-major workgroup (32 per wave)
 constexpr int kKeys = 128;     // keys per key-major workgroup (32 per wave)
 constexpr int kTileRows = 64;  // rows of an LDS tile (Q/dO rows or K/V keys)
 constexpr int kTileBytes = kTileRows * 256;
@@ -725,28 +721,50 @@ void bwd_dkdv_bf16_d128x8(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Row-major: dQ of 128 rows.
+// Row-major, eight waves: dQ of 256 rows with K/V tiles streamed into LDS.
 // ---------------------------------------------------------------------------
+// A workgroup of 8 waves owns 256 rows, 32 per wave, whose Q and dO stay in
+// registers as the B operand (column = row); per 64-key tile:
+//   S^T = K Q^T and dP^T = V dO^T   (A = K / V rows from LDS)
+//   P = exp2(S scale log2e - LSE log2e), masked; dS = P (dP - D)
+//   dQ^T += K^T dS^T   (A = K read transposed, B = dS^T in register order)
+// P is formed in place of S, and the mask is a pass of its own, taken only
+// when some row of the wave does not see every key of the tile.  The K/V
+// tiles stream through a three-stage direct-to-LDS ring two tiles ahead (a
+// tile serves 256 rows): waves 0-3 load the K tile, waves 4-7 the V tile,
+// four 1 KiB loads each (tile row 16 (wv & 3) + 4 n + lane / 16, physical
+// chunk lane % 16 holding logical chunk (lane % 16) ^ swz(row)).  Keys come
+// from the source's two chunks through two buffer bases, so the 32-bit
+// offsets stay within one chunk; a tile across the two chunks, or the
+// ragged last tile, takes each lane's chunk (at least four loads per wave
+// and tile either way).  (Running the two waves of a SIMD half a tile apart,
+// as the forward step kernel does, measured slower here: 48 MFMAs per tile
+// against little elementwise work leave nothing to overlap.)  A workgroup
+// that loaded each tile when it needed it, four waves and 128 rows, took
+// 218-220 us per 32k/cp8 rank-0 step against 196-197.
+constexpr int kDqRows8 = 256;
+constexpr int kDqStages8 = 3;
+
 template <bool kDoc>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_bf16_d128(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileBytes];
-  lds_u8* const tk = (lds_u8*)smem;
-  lds_u8* const tv = tk + kTileBytes;
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8), amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_bf16_d128x8(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDqStages8 * 2 * kTileBytes];
+  auto kst = [&](int st) { return (lds_u8*)smem + st * 2 * kTileBytes; };
+  auto vst = [&](int st) { return (lds_u8*)smem + st * 2 * kTileBytes + kTileBytes; };
 
   // Dispatch order, longest workgroups first: tile-major over the heads,
   // the segment whose rows see more keys first, and on a diagonal segment
-  // its last (longest) rows first.  Each workgroup's result does not
-  // depend on the order.
+  // its last (longest) rows first.  Each workgroup's result does not depend
+  // on the order.
   const int h = blockIdx.x % a.heads;
   int t = blockIdx.x / a.heads;
   auto keys_of = [](const SegArgs& x) { return int64_t(x.kv_full) + (x.diag ? x.q_len : 0); };
   const int s0 = a.nseg == 2 && keys_of(a.seg[1]) > keys_of(a.seg[0]) ? 1 : 0;
   const int si = t < a.seg[s0].tiles ? s0 : 1 - s0;
   if (si != s0) t -= a.seg[s0].tiles;
-  const SegArgs& g = a.seg[si];
+  const SegArgs g = seg_pick(a.seg[0], a.seg[1], si);
   if (g.diag) t = g.tiles - 1 - t;
-  const int row0 = t * kRows;
+  const int row0 = t * kDqRows8;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qc = lane & 31, hf = lane >> 5;
@@ -757,7 +775,7 @@ void bwd_dq_bf16_d128(BwdArgs a) {
   const int w_first = row0 + 32 * wv;
   const int w_last = min(w_first + 32, g.q_len);
   int w_max = w_last > w_first ? g.kv_full + (g.diag ? w_last : 0) : 0;
-  int kv_end = g.kv_full + (g.diag ? min(row0 + kRows, g.q_len) : 0);
+  int kv_end = g.kv_full + (g.diag ? min(row0 + kDqRows8, g.q_len) : 0);
   // document masks: the row's first key, the wave's smallest first key, the
   // workgroup's first key tile
   int klo = 0, w_lo = 0, kb0 = 0;
@@ -768,7 +786,7 @@ void bwd_dq_bf16_d128(BwdArgs a) {
     prefix = min(prefix, hi);
     doc_row_keys(a, g.q_global + row0, lo, hi);
     kb0 = lo / kTileRows * kTileRows;
-    doc_row_keys(a, g.q_global + min(row0 + kRows, g.q_len) - 1, lo, hi);
+    doc_row_keys(a, g.q_global + min(row0 + kDqRows8, g.q_len) - 1, lo, hi);
     kv_end = min(kv_end, hi);
     if (w_last > w_first) {
       doc_row_keys(a, g.q_global + w_first, w_lo, hi);
@@ -776,6 +794,7 @@ void bwd_dq_bf16_d128(BwdArgs a) {
       w_max = min(w_max, hi);
     }
   }
+  const int ntiles = kv_end > kb0 ? (kv_end - kb0 + kTileRows - 1) / kTileRows : 0;
   const uint32_t row_bytes = uint32_t(a.heads) * 256;
   const uint32_t hoff = uint32_t(h) * 256;
 
@@ -796,44 +815,83 @@ void bwd_dq_bf16_d128(BwdArgs a) {
   for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
   const Bases bs = make_bases(lane);
 
-  auto krow_of = [&](int kk) { return kv_row(a, min(kk, a.kv_valid - 1)); };
-  for (int j0 = kb0; j0 < kv_end; j0 += kTileRows) {
-    {
-      TileRegs rk, rv;
-      tile_load(rk, a.k, row_bytes, hoff, tid, [&](int r) { return krow_of(j0 + r); });
-      tile_load(rv, a.v, row_bytes, hoff, tid, [&](int r) { return krow_of(j0 + r); });
-      __syncthreads();
-      tile_store(rk, tk, tid);
-      tile_store(rv, tv, tid);
+  // tile loads
+  const char* const src = static_cast<const char*>(wv < 4 ? a.k : a.v);
+  const dma_u32x4 desc_lo = buffer_desc(src + int64_t(a.kv_lo) * row_bytes, uint32_t(a.kv_split) * row_bytes);
+  const dma_u32x4 desc_hi =
+      buffer_desc(src + int64_t(a.kv_hi) * row_bytes, uint32_t(max(0, a.kv_valid - a.kv_split)) * row_bytes);
+  const int lrow0 = 16 * (wv & 3) + (lane >> 4);  // + 4 n: the lane's tile row for load n
+  uint32_t c16[4];                                 // its chunk's byte offset within a row (head included)
+#pragma unroll
+  for (int n = 0; n < 4; ++n) c16[n] = (uint32_t((lane & 15) ^ swz((lrow0 + 4 * n) & 15)) << 4) + hoff;
+  auto issue = [&](int j0, int st) {
+    const uint32_t dst = lds_addr((wv < 4 ? kst(st) : vst(st)) + 16 * (wv & 3) * 256);
+    const bool whole = j0 + kTileRows <= a.kv_valid && (j0 + kTileRows <= a.kv_split || j0 >= a.kv_split);
+    if (whole) {
+      const bool lo = j0 < a.kv_split;
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(uint32_t(lo ? j0 : j0 - a.kv_split) * row_bytes);
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        dma_lds16(lo ? desc_lo : desc_hi, __umul24(uint32_t(lrow0 + 4 * n), row_bytes) + c16[n], soff, dst + n * 1024);
+    } else {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int kk = min(j0 + lrow0 + 4 * n, a.kv_valid - 1);
+        if (kk < a.kv_split)
+          dma_lds16(desc_lo, __umul24(uint32_t(kk), row_bytes) + c16[n], 0u, dst + n * 1024);
+        else
+          dma_lds16(desc_hi, __umul24(uint32_t(kk - a.kv_split), row_bytes) + c16[n], 0u, dst + n * 1024);
+      }
     }
-    __syncthreads();
-    if (j0 >= w_max || (kDoc && j0 + kTileRows <= w_lo)) continue;
-    f32x16 s[2], dp[2];
-    mm_rows(tk, bs.row, qf, s);
-    mm_rows(tv, bs.row, dof, dp);
-    // P in place of S; the mask is a pass of its own, taken only when some
-    // row of the wave does not see every key of the tile (rows past the
-    // segment have LSE = +inf, so their P is 0 either way)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = __builtin_amdgcn_exp2f(fmaf(s[kb][e], a.scale_log2, -lse2));
-    if (kDoc || !__all(!ok || j0 + kTileRows <= prefix)) {
+  };
+
+  if (ntiles > 0) {
+    issue(kb0, 0);
+    issue(kb0 + min(1, ntiles - 1) * kTileRows, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the rows above and this wave's first tile loads
+  lds_barrier();
+  int st = 0;
+  for (int j = 0; j < ntiles; ++j) {
+    const int j0 = kb0 + j * kTileRows;
+    // tile j + 2 into the stage tile j - 1 left (its reads ended before the
+    // last barrier)
+    issue(kb0 + min(j + 2, ntiles - 1) * kTileRows, st == 0 ? 2 : st - 1);
+    if (j0 < w_max && !(kDoc && j0 + kTileRows <= w_lo)) {
+      const lds_u8* const tk = kst(st);
+      const lds_u8* const tv = vst(st);
+      f32x16 s[2], dp[2];
+      mm_rows(tk, bs.row, qf, s);
+      mm_rows(tv, bs.row, dof, dp);
+      // P in place of S; the mask is a pass of its own, taken only when some
+      // row of the wave does not see every key of the tile
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kk = j0 + 32 * kb + 8 * (e >> 2) + 4 * hf + (e & 3);
-          if (!(kk < prefix && (!kDoc || kk >= klo))) s[kb][e] = 0.f;
-        }
+        for (int e = 0; e < 16; ++e) s[kb][e] = __builtin_amdgcn_exp2f(fmaf(s[kb][e], a.scale_log2, -lse2));
+      if (kDoc || !__all(!ok || j0 + kTileRows <= prefix)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int kk = j0 + 32 * kb + 8 * (e >> 2) + 4 * hf + (e & 3);
+            if (!(kk < prefix && (!kDoc || kk >= klo))) s[kb][e] = 0.f;
+          }
+      }
+      bf16x8 ws[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ws[kb][e >> 3][e & 7] = static_cast<__bf16>(s[kb][e] * (dp[kb][e] - del));
+      mm_tr(tk, bs.tr, ws, dq);
     }
-    bf16x8 ws[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) ws[kb][e >> 3][e & 7] = static_cast<__bf16>(s[kb][e] * (dp[kb][e] - del));
-    mm_tr(tk, bs.tr, ws, dq);
+    // tile j + 1 has landed (loads complete in order; at least four loads,
+    // those of tile j + 2, were issued since)
+    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    lds_barrier();
+    st = st == 2 ? 0 : st + 1;
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load in flight at exit
   if (!ok) return;
   float* dqp = a.dq + (grow * a.heads + h) * D;
   const bool first = g.epi != 0;
@@ -855,7 +913,7 @@ void bwd_dq_bf16_d128(BwdArgs a) {
 }  // namespace
 
 bool bwd_mfma(int dtype_bf16, int head_dim) { return dtype_bf16 && head_dim == 128; }
-int bwd_mfma_rows() { return kRows; }
+int bwd_mfma_rows() { return kDqRows8; }
 int bwd_mfma_keys() { return kKeys; }
 
 template <bool kDoc>
@@ -865,7 +923,7 @@ hipError_t launch_bf16_d128(const BwdArgs& a, bool eight, hipStream_t st) {
     if (eight) bwd_dkdv_bf16_d128x8<kDoc><<<grid, kThreads8, 0, st>>>(a);
     else bwd_dkdv_bf16_d128<kDoc><<<grid, kThreads, 0, st>>>(a);
   }
-  if (a.total_tiles > 0) bwd_dq_bf16_d128<kDoc><<<unsigned(a.total_tiles) * unsigned(a.heads), kThreads, 0, st>>>(a);
+  if (a.total_tiles > 0) bwd_dq_bf16_d128x8<kDoc><<<unsigned(a.total_tiles) * unsigned(a.heads), kThreads8, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -58,8 +58,8 @@ def test_no_kernel_spills_to_scratch(resources):
 
 def test_backward_kernels_do_not_spill():
     """The matrix-core backward kernels keep every value in registers; the
-    row-major dQ kernel stays within 256 VGPRs, so two workgroups share a CU,
-    and so does the eight-wave key-major kernel (two of its waves per SIMD)."""
+    eight-wave row-major dQ kernel and the eight-wave key-major kernel stay
+    within 256 VGPRs (two of their waves per SIMD)."""
     try:
         B.hipcc()
     except RuntimeError:
@@ -68,7 +68,7 @@ def test_backward_kernels_do_not_spill():
     assert res
     for name, r in res.items():
         assert r["scratch"] == 0, (name, r)
-    dq = [v for k, v in res.items() if "bwd_dq_bf16_d128ILb0E" in k]
-    assert len(dq) == 1 and dq[0]["vgpr"] <= 256, dq
+    dq = [v for k, v in res.items() if "bwd_dq_bf16_d128x8" in k]
+    assert len(dq) == 2 and all(v["vgpr"] <= 256 for v in dq), dq
     x8 = [v for k, v in res.items() if "bwd_dkdv_bf16_d128x8" in k]
     assert len(x8) == 2 and all(v["vgpr"] <= 256 for v in x8), x8
