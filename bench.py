@@ -234,7 +234,9 @@ def workload_section(name, stream, steps, graph_too=False):
     """One of the other workloads, timed like the headline: calls per second
     over its share, effective TFLOP/s of the valid pairs, the step kernel's
     mean launch time from the library's step events and its fraction of the
-    bf16 peak, and (graph_too) the same calls replayed from a HIP graph."""
+    bf16 peak, (graph_too) the same calls replayed from a HIP graph, and, for
+    a share of every rank, the ranks in lockstep (every rank's ring step in
+    one launch, CP_ATTN_OPT_LOCKSTEP)."""
     import ring_context_parallelism_amd as R
     from ring_context_parallelism_amd.inputs import WORKLOADS, workload_qkv
     w = WORKLOADS[name]
@@ -263,6 +265,14 @@ def workload_section(name, stream, steps, graph_too=False):
         p.set_graph(False)
         res["graph_replay_ms_per_call"] = round(gms, 5)
         res["graph_replay_median_ms"] = round(time_calls.last["median"], 5)
+    if w.rank is None:
+        p.set_lockstep(True)
+        lms = time_calls(p, w, bufs, stream, steps, 3, 0.3)
+        p.set_lockstep(False)
+        res["lockstep"] = {"ms_per_call": round(lms, 5), "ms_per_call_median": round(time_calls.last["median"], 5),
+                           "tflops": round(flops / (lms * 1e-3) / 1e12, 2),
+                           "frac_bf16_peak": round(flops / (lms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "launches_per_call": w.cp}
     p.close()
     del q, k, v, out, lse, bufs
     torch.cuda.empty_cache()
@@ -293,7 +303,30 @@ def rank_step_imbalance(plan, w, bufs, stream, reps=3):
     lockstep_ms = float(t.max(axis=0).sum())
     lockstep_tflops = 4 * w.head_dim * w.heads * all_pairs / w.cp / (lockstep_ms * 1e-3) / 1e12
     rank0_ms = float(t[0].sum())
+    # measured: every rank's share on this GPU, back to back and in lockstep
+    # (every rank's ring step in one launch), whole calls
+    flops_all = 4 * w.head_dim * w.heads * all_pairs
+    full = {}
+    for mode in (False, True):
+        plan.set_lockstep(mode)
+        for _ in range(2):
+            plan.full_forward(*bufs, stream=stream)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            plan.full_forward(*bufs, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        full[mode] = ev[0].elapsed_time(ev[1]) / reps
+    plan.set_lockstep(False)
+    measured = {"all_ranks_back_to_back_ms": round(full[False], 5), "all_ranks_lockstep_ms": round(full[True], 5),
+                "lockstep_ms_per_rank": round(full[True] / w.cp, 5),
+                "lockstep_tflops_per_gpu": round(flops_all / (full[True] * 1e-3) / 1e12, 2),
+                "lockstep_frac_bf16_peak": round(flops_all / (full[True] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "note": "one GPU runs every rank; per GPU of a cp-GPU ring, the same rate"}
     return {"workload": w.name, "step_ms": [[round(float(x), 4) for x in row] for row in t],
+            "measured_lockstep": measured,
             "lockstep_step_kernel_ms": round(lockstep_ms, 5), "rank0_step_kernel_ms": round(rank0_ms, 5),
             "lockstep_over_rank0": round(lockstep_ms / rank0_ms, 4),
             "lockstep_tflops_per_gpu": round(lockstep_tflops, 2),

@@ -107,6 +107,20 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      waves, each 32-key column's products split between two waves;
                                      1: four waves, one wave per 32-key column. dK and dV are
                                      bit-identical either way. */
+#define CP_ATTN_OPT_LOCKSTEP 12   /* cp_attn_full_forward: 0 (default): the ranks' shares back to
+                                     back; 1: the ranks in lockstep, as a CP group runs a ring
+                                     step together: per step, every rank's receive on the copy
+                                     stream and one launch of the step kernel over every rank's
+                                     tiles (no key split).  Each rank gets its own receive slots
+                                     and running state in a library-owned buffer (about
+                                     cp x (4 x n_loc x H x D x 2 + n_loc x H x (D + 1) x 4) bytes,
+                                     allocated by the first such call, freed with the plan;
+                                     ENOWORKSPACE if that allocation fails).  Each rank's result is
+                                     bit-identical to its back-to-back result without the key
+                                     split.  Served for bf16 head_dim 128 with the fused merge,
+                                     the copy-kernel or memcpy receive, and no serial, poison or
+                                     step-timing mode (and while K/V span at most 4 GiB);
+                                     otherwise, and in graph mode, the ranks run back to back. */
 
 /*
  * Create a plan (host only: no device memory, no HIP call).
@@ -266,8 +280,9 @@ int cp_attn_ulysses_forward(cp_attn_plan_t plan, const void* q, const void* k, c
 int cp_attn_rank_forward_noalloc(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
                                  float* lse, int rank, void* stream);
 
-/* Every rank's share back to back on `stream` (ranks 0..cp_size-1); fills all
- * rows of out and lse.  Same arguments and errors as cp_attn_rank_forward. */
+/* Every rank's share on `stream` (ranks 0..cp_size-1), back to back, or with
+ * CP_ATTN_OPT_LOCKSTEP all ranks' ring step s in one launch; fills all rows
+ * of out and lse.  Same arguments and errors as cp_attn_rank_forward. */
 int cp_attn_full_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
                          float* lse, void* stream);
 

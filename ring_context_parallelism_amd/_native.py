@@ -34,6 +34,7 @@ OPT_GRAPH = 7
 OPT_KSPLIT = 8
 OPT_COUNTERS = 9
 OPT_BWD_KEYS = 10
+OPT_LOCKSTEP = 12
 
 NOALLOC_SCRATCH_BYTES = 128 << 20  # CP_ATTN_NOALLOC_SCRATCH_BYTES
 

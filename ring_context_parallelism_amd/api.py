@@ -86,6 +86,11 @@ class Plan:
         two waves per 32-key column) or "four" (one wave per column)."""
         self.set_option(N.OPT_BWD_KEYS, {"eight": 0, "four": 1}[kind])
 
+    def set_lockstep(self, on):
+        """full_forward: every rank's ring step in one launch (on) or the ranks
+        one after another (off, the default)."""
+        self.set_option(N.OPT_LOCKSTEP, int(bool(on)))
+
     def set_poison(self, on):
         self.set_option(N.OPT_POISON, int(bool(on)))
 

@@ -57,6 +57,13 @@ struct DeviceState {
   // work counters (CP_ATTN_OPT_COUNTERS): key tiles computed per (rank, step)
   unsigned long long* tile_cnt = nullptr;
   std::vector<int> counted;  // 1 if (rank, step) was counted by the last call
+  // lockstep full forward (CP_ATTN_OPT_LOCKSTEP): every rank's receive slots
+  // and running state, the step-argument table and its workgroup ranges
+  char* ls_ws = nullptr;
+  int64_t ls_bytes = 0;
+  void* ls_host = nullptr;         // pinned staging of the table
+  hipEvent_t ls_uploaded = nullptr;
+  std::vector<intptr_t> ls_key;    // what the uploaded table was built for
 };
 
 namespace {
@@ -298,7 +305,8 @@ void set_doc(const Plan& p, const char* ws, A& a, int j) {
 // full segment's row tiles take two workgroups, one per half of the keys (the
 // partial buffers of the separate merge mode hold the parts).  Returns the
 // ksplit factor (1 or 2) of segment i of (r, s).
-int seg_ksplit(const Plan& p, int r, int s, int i) {
+int seg_ksplit(const Plan& p, int r, int s, int i, bool lockstep = false) {
+  if (lockstep) return 1;  // every rank's step fills the GPU together, and the split buffers are per rank
   const StepDesc& sd = p.step(r, s);
   const bool bf16 = p.dtype == CP_ATTN_BF16;
   if (!p.opt_ksplit || p.opt_merge == 1 || !p.doc_starts.empty() || !attn_splits_keys(bf16, p.head_dim)) return 1;
@@ -319,20 +327,17 @@ bool rank_splits(const Plan& p, int r) {
   return false;
 }
 
-// Step 0 reads the rank's own K/V in place (the rank holds them; nothing is
-// received); later steps read receive slot b.
-int launch_step(Plan& p, const RunCfg& c, const void* q, const void* k, const void* v, void* out, float* lse, int r,
-                int s, int b, hipStream_t st) {
+// The arguments of step (r, s).  Step 0 reads the rank's own K/V in place
+// (the rank holds them; nothing is received); later steps read receive slot
+// b.  ws: the workspace holding the rank's slots and running state; the
+// document table is always the plan's (dws).  lockstep: every rank's step in
+// one launch (no key split, no in-kernel receive).
+StepArgs make_step_args(Plan& p, const RunCfg& c, const void* q, const void* k, const void* v, void* out, float* lse,
+                        int r, int s, int b, char* ws, const char* dws, bool lockstep) {
   DeviceState& d = *p.dev;
   const WsLayout w = ws_layout(p);
-  char* ws = c.ws;
   const StepDesc& sd = p.step(r, s);
   const bool bf16 = p.dtype == CP_ATTN_BF16;
-  if (sd.nseg == 0) {
-    // no query row of this rank sees the step's keys; the receive still happens
-    if (kernel_recv(p, c, s)) CPA_HIP(launch_recv(recv_ranges(p, ws, k, v, p.step(r, s + 1).src, (s + 1) & 1), 0, st));
-    return CP_ATTN_OK;
-  }
   const int bm = bf16 ? attn_bf16_block_m(p.head_dim) : attn_f32_block_m();
   StepArgs a{};
   a.q = q;
@@ -382,7 +387,7 @@ int launch_step(Plan& p, const RunCfg& c, const void* q, const void* k, const vo
     x.kv_full = int32_t(g.kv_full);
     x.diag = g.diag;
     const int32_t qt = int32_t((g.q_len + bm - 1) / bm);
-    x.ksplit = seg_ksplit(p, r, s, i);
+    x.ksplit = seg_ksplit(p, r, s, i, lockstep);
     x.tiles = qt * x.ksplit;
     if (separate) {
       x.epi = g.first ? kEpiInit : kEpiPartial;
@@ -401,9 +406,23 @@ int launch_step(Plan& p, const RunCfg& c, const void* q, const void* k, const vo
     auto work = [](const SegArgs& x) { return int64_t(x.q_len) * (2 * int64_t(x.kv_full) + (x.diag ? x.q_len : 0)); };
     if (work(a.seg[1]) > work(a.seg[0])) std::swap(a.seg[0], a.seg[1]);
   }
-  if (kernel_recv(p, c, s)) a.recv = recv_ranges(p, ws, k, v, p.step(r, s + 1).src, (s + 1) & 1);
+  if (!lockstep && kernel_recv(p, c, s)) a.recv = recv_ranges(p, ws, k, v, p.step(r, s + 1).src, (s + 1) & 1);
   if (c.counters) a.tile_cnt = d.tile_cnt + size_t(r) * p.cp + s;
-  set_doc(p, ws, a, sd.src);
+  set_doc(p, dws, a, sd.src);
+  return a;
+}
+
+int launch_step(Plan& p, const RunCfg& c, const void* q, const void* k, const void* v, void* out, float* lse, int r,
+                int s, int b, hipStream_t st) {
+  char* ws = c.ws;
+  const StepDesc& sd = p.step(r, s);
+  const bool bf16 = p.dtype == CP_ATTN_BF16;
+  if (sd.nseg == 0) {
+    // no query row of this rank sees the step's keys; the receive still happens
+    if (kernel_recv(p, c, s)) CPA_HIP(launch_recv(recv_ranges(p, ws, k, v, p.step(r, s + 1).src, (s + 1) & 1), 0, st));
+    return CP_ATTN_OK;
+  }
+  const StepArgs a = make_step_args(p, c, q, k, v, out, lse, r, s, b, ws, ws, false);
   const hipError_t e = bf16 ? launch_attn_bf16(a, p.head_dim, st) : launch_attn_f32(a, p.head_dim, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("attention launch: ") + hipGetErrorString(e));
   return CP_ATTN_OK;
@@ -544,6 +563,119 @@ int run_rank(Plan& p, const RunCfg& c, const void* q, const void* k, const void*
       CPA_HIP(hipStreamWaitEvent(st, d.merge_join, 0));
     }
     CPA_TRY(launch_rank_finalize(p, ws, out, lse, r, st));
+  }
+  return CP_ATTN_OK;
+}
+
+// ---- lockstep full forward ----
+// Every rank's step s in one launch, as the ranks of a CP group run step s
+// together: per step, the receives of all ranks on the copy stream, then one
+// launch of the step kernel over every rank's tiles.  Each rank has its own
+// receive slots and running state (a library-owned workspace); the document
+// table stays the plan's.  Served for bf16 head_dim 128 with the fused merge
+// and the side-stream receive (copy kernel or memcpy), without the serial,
+// poison or step-timing modes and while step 0 reads K/V in place; otherwise
+// the ranks run back to back.
+bool lockstep_served(const Plan& p, const RunCfg& c) {
+  return p.opt_lockstep && p.dtype == CP_ATTN_BF16 && p.head_dim == 128 && p.opt_merge == 0 &&
+         (c.recv == 0 || c.recv == 1) && !c.serial && !c.poison && !c.timing && !kv_beyond_32bit(p) && p.cp > 1;
+}
+
+// bytes of one rank's slots and running state (the leading part of ws_layout)
+int64_t lockstep_rank_bytes(const Plan& p) { return ws_layout(p).part_o[0]; }
+
+int run_lockstep(Plan& p, const RunCfg& c0, const void* q, const void* k, const void* v, void* out, float* lse,
+                 hipStream_t st) {
+  DeviceState& d = *p.dev;
+  const int P = p.cp;
+  const int64_t rb = lockstep_rank_bytes(p);
+  const int64_t tbl_bytes = int64_t(P) * P * int64_t(sizeof(StepArgs));
+  const int64_t wgb_bytes = int64_t(P) * (P + 1) * 4;
+  const int64_t need = rb * P + align256(tbl_bytes + wgb_bytes);
+  if (d.ls_bytes < need) {
+    if (d.ls_ws) {  // earlier calls may still use it
+      CPA_HIP(hipDeviceSynchronize());
+      CPA_HIP(hipFree(d.ls_ws));
+      d.ls_ws = nullptr;
+      d.ls_bytes = 0;
+    }
+    if (d.ls_host) {
+      CPA_HIP(hipHostFree(d.ls_host));
+      d.ls_host = nullptr;
+    }
+    if (hipMalloc(reinterpret_cast<void**>(&d.ls_ws), size_t(need)) != hipSuccess) {
+      (void)hipGetLastError();
+      d.ls_ws = nullptr;
+      return fail(CP_ATTN_ENOWORKSPACE, "lockstep workspace allocation failed");
+    }
+    d.ls_bytes = need;
+    CPA_HIP(hipHostMalloc(&d.ls_host, size_t(tbl_bytes + wgb_bytes), hipHostMallocDefault));
+    if (!d.ls_uploaded) CPA_HIP(hipEventCreateWithFlags(&d.ls_uploaded, hipEventDisableTiming));
+    d.ls_key.clear();
+  }
+  StepArgs* const tbl_dev = reinterpret_cast<StepArgs*>(d.ls_ws + rb * P);
+  // the table and the ranges lie one after the other, as in the staging buffer
+  int32_t* const wgb_dev = reinterpret_cast<int32_t*>(d.ls_ws + rb * P + tbl_bytes);
+  auto rank_ws = [&](int r) { return d.ls_ws + rb * r; };
+  // the table: every (rank, step)'s arguments and each step's workgroup ranges
+  std::vector<int32_t> total(P, 0);
+  const std::vector<intptr_t> key = {reinterpret_cast<intptr_t>(q), reinterpret_cast<intptr_t>(k),
+                                     reinterpret_cast<intptr_t>(v), reinterpret_cast<intptr_t>(out),
+                                     reinterpret_cast<intptr_t>(lse), intptr_t(c0.counters), intptr_t(p.doc_version),
+                                     reinterpret_cast<intptr_t>(c0.ws)};
+  {
+    StepArgs* const tbl = static_cast<StepArgs*>(d.ls_host);
+    int32_t* const wgb = reinterpret_cast<int32_t*>(static_cast<char*>(d.ls_host) + tbl_bytes);
+    const bool fresh = d.ls_key == key;
+    if (!fresh) CPA_HIP(hipEventSynchronize(d.ls_uploaded));  // the staging buffer's last upload has been read
+    for (int s = 0; s < P; ++s) {
+      int32_t* const w = wgb + int64_t(s) * (P + 1);
+      w[0] = 0;
+      for (int r = 0; r < P; ++r) {
+        StepArgs& a = tbl[int64_t(s) * P + r];
+        int32_t n = 0;
+        if (p.step(r, s).nseg > 0 && p.valid_rows(r) > 0) {
+          if (!fresh) a = make_step_args(p, c0, q, k, v, out, lse, r, s, s & 1, rank_ws(r), c0.ws, true);
+          n = (a.total_tiles * a.heads + 7) / 8 * 8;
+        } else if (!fresh) {
+          a = StepArgs{};
+        }
+        w[r + 1] = w[r] + n;
+      }
+      total[s] = w[P];
+    }
+    if (!fresh) {
+      CPA_HIP(hipMemcpyAsync(tbl_dev, d.ls_host, size_t(tbl_bytes + wgb_bytes), hipMemcpyHostToDevice, st));
+      CPA_HIP(hipEventRecord(d.ls_uploaded, st));
+      d.ls_key = key;
+    }
+  }
+  if (c0.counters) {
+    CPA_HIP(launch_fill_words(d.tile_cnt, int64_t(P) * P * 2, 0u, st));
+    for (int i = 0; i < P * P; ++i) d.counted[size_t(i)] = 1;
+  }
+  hipStream_t cs = d.copy;
+  CPA_HIP(hipEventRecord(d.start, st));
+  CPA_HIP(hipStreamWaitEvent(cs, d.start, 0));
+  for (int s = 0; s < P; ++s) {
+    const int b = s & 1;
+    if (s + 1 < P) {
+      // every rank's receive of step s + 1 into its slot nb, last read by step s - 1
+      const int nb = (s + 1) & 1;
+      if (s >= 1) CPA_HIP(hipStreamWaitEvent(cs, d.attn_done[nb], 0));
+      for (int r = 0; r < P; ++r) {
+        if (p.valid_rows(r) == 0) continue;
+        RunCfg cr = c0;
+        cr.ws = rank_ws(r);
+        CPA_TRY(recv_kv(p, cr, k, v, p.step(r, s + 1).src, nb, false, cs));
+      }
+      CPA_HIP(hipEventRecord(d.recv_done[nb], cs));
+    }
+    if (s >= 1) CPA_HIP(hipStreamWaitEvent(st, d.recv_done[b], 0));
+    const hipError_t e = launch_attn_bf16_ranks(tbl_dev + int64_t(s) * P, wgb_dev + int64_t(s) * (P + 1), P, total[s],
+                                                !p.doc_starts.empty(), st);
+    if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("lockstep attention launch: ") + hipGetErrorString(e));
+    if (s + 2 < P) CPA_HIP(hipEventRecord(d.attn_done[b], st));
   }
   return CP_ATTN_OK;
 }
@@ -790,6 +922,9 @@ int cp_attn_plan_destroy(cp_attn_plan_t h) {
       drop_graph(d);
       if (d.capture) (void)hipStreamDestroy(d.capture);
       if (d.tile_cnt) (void)hipFree(d.tile_cnt);
+      if (d.ls_ws) (void)hipFree(d.ls_ws);
+      if (d.ls_host) (void)hipHostFree(d.ls_host);
+      if (d.ls_uploaded) (void)hipEventDestroy(d.ls_uploaded);
       if (d.own_ws && d.ws) (void)hipFree(d.ws);
       if (d.own_copy && d.copy) (void)hipStreamDestroy(d.copy);
       if (d.own_merge && d.merge) (void)hipStreamDestroy(d.merge);
@@ -857,6 +992,10 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
     case CP_ATTN_OPT_BWD_KEYS:
       if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "CP_ATTN_OPT_BWD_KEYS must be 0 or 1");
       p.opt_bwd_keys = value;
+      return CP_ATTN_OK;
+    case CP_ATTN_OPT_LOCKSTEP:
+      if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "CP_ATTN_OPT_LOCKSTEP must be 0 or 1");
+      p.opt_lockstep = value;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_COUNTERS:
       if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "counters option must be 0 or 1");
@@ -1113,6 +1252,7 @@ int cp_attn_full_forward(cp_attn_plan_t h, const void* q, const void* k, const v
   reset_timing(p);
   if (p.opt_graph) return run_graph(p, q, k, v, out, lse, -1, static_cast<hipStream_t>(stream));
   const RunCfg c = plan_cfg(p, false);
+  if (lockstep_served(p, c)) return run_lockstep(p, c, q, k, v, out, lse, static_cast<hipStream_t>(stream));
   for (int r = 0; r < p.cp; ++r) CPA_TRY(run_rank(p, c, q, k, v, out, lse, r, static_cast<hipStream_t>(stream)));
   return CP_ATTN_OK;
   CPA_GUARD_END

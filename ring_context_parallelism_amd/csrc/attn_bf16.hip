@@ -416,10 +416,31 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kThreads8 = 512;
 constexpr int kBM8 = 256;
 
-template <bool kRecv, bool kDoc>
+// kRanks: every rank's step of one ring step in one launch (a CP group in
+// lockstep on one GPU): rank r's workgroups are wgb[r] .. wgb[r + 1] - 1
+// (ranges that start at multiples of 8, so a rank's workgroups keep their
+// XCD mapping), its arguments tbl[r] (device memory); a workgroup past its
+// rank's tiles (padding of the range) does nothing.  Otherwise the launch is
+// one rank's step, with arguments a0.
+template <bool kRecv, bool kDoc, bool kRanks>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8), amdgpu_waves_per_eu(2, 2)))
-void attn_step_bf16_d128x8(StepArgs a) {
+void attn_step_bf16_d128x8(StepArgs a0, const StepArgs* __restrict__ tbl, const int32_t* __restrict__ wgb, int nranks) {
   constexpr int D = 128, NT = 8, NB = 4;
+  static_assert(!(kRanks && kRecv), "the in-kernel receive is per rank");
+  int bid = int(blockIdx.x), nblk = int(gridDim.x), rank = 0;
+  if constexpr (kRanks) {
+    int lo = 0, hi = nranks;  // the rank: wgb[lo] <= blockIdx.x < wgb[lo + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (wgb[mid] <= bid) lo = mid;
+      else hi = mid;
+    }
+    rank = lo;
+    bid -= wgb[lo];
+    nblk = tbl[lo].total_tiles * tbl[lo].heads;
+    if (bid >= nblk) return;
+  }
+  const StepArgs& a = kRanks ? tbl[rank] : a0;
   // 4 stages x K, V
   __shared__ __attribute__((aligned(1024))) uint8_t smem_kv[4 * 2 * kTileBytes];
   lds_u8* const kv_lds = (lds_u8*)smem_kv;
@@ -439,7 +460,7 @@ void attn_step_bf16_d128x8(StepArgs a) {
   };
 
   int h, t;
-  tile_of(blockIdx.x, gridDim.x, a.heads, a.total_tiles, h, t);
+  tile_of(bid, nblk, a.heads, a.total_tiles, h, t);
   const int si = t < a.seg[0].tiles ? 0 : 1;
   if (si) t -= a.seg[0].tiles;
   const SegArgs& g = a.seg[si];
@@ -957,18 +978,29 @@ bool attn_does_recv(int dtype_bf16, int head_dim) { return dtype_bf16 && head_di
 
 bool attn_splits_keys(int dtype_bf16, int head_dim) { return dtype_bf16 && head_dim == 128; }
 
+hipError_t launch_attn_bf16_ranks(const StepArgs* tbl, const int32_t* wgb, int nranks, int total_wgs, bool doc,
+                                  hipStream_t stream) {
+  if (total_wgs <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(total_wgs));
+  if (doc)
+    attn_step_bf16_d128x8<false, true, true><<<grid, kThreads8, 0, stream>>>(StepArgs{}, tbl, wgb, nranks);
+  else
+    attn_step_bf16_d128x8<false, false, true><<<grid, kThreads8, 0, stream>>>(StepArgs{}, tbl, wgb, nranks);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid(unsigned(a.total_tiles) * unsigned(a.heads));
   if (head_dim == 128) {
     if (a.doc) {
       if (a.recv.n > 0)
-        attn_step_bf16_d128x8<true, true><<<grid, kThreads8, 0, stream>>>(a);
+        attn_step_bf16_d128x8<true, true, false><<<grid, kThreads8, 0, stream>>>(a, nullptr, nullptr, 0);
       else
-        attn_step_bf16_d128x8<false, true><<<grid, kThreads8, 0, stream>>>(a);
+        attn_step_bf16_d128x8<false, true, false><<<grid, kThreads8, 0, stream>>>(a, nullptr, nullptr, 0);
     } else if (a.recv.n > 0) {
-      attn_step_bf16_d128x8<true, false><<<grid, kThreads8, 0, stream>>>(a);
+      attn_step_bf16_d128x8<true, false, false><<<grid, kThreads8, 0, stream>>>(a, nullptr, nullptr, 0);
     } else {
-      attn_step_bf16_d128x8<false, false><<<grid, kThreads8, 0, stream>>>(a);
+      attn_step_bf16_d128x8<false, false, false><<<grid, kThreads8, 0, stream>>>(a, nullptr, nullptr, 0);
     }
   } else {
     attn_step_bf16<64><<<grid, kThreads, 0, stream>>>(a);

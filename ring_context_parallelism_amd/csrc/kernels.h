@@ -138,6 +138,12 @@ hipError_t launch_bwd_bf16_d128(const BwdArgs& a, bool eight_wave_keys, hipStrea
 bool attn_does_recv(int dtype_bf16, int head_dim);
 bool attn_splits_keys(int dtype_bf16, int head_dim);  // kernel honours SegArgs::ksplit
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream);
+// Every rank's step of one ring step in one launch (bf16, head_dim 128, no
+// in-kernel receive): tbl[r] (device memory) are rank r's arguments, its
+// workgroups wgb[r] .. wgb[r + 1] - 1 (wgb[nranks] = total_wgs; each range
+// starts at a multiple of 8 and holds at least tbl[r].total_tiles * heads).
+hipError_t launch_attn_bf16_ranks(const StepArgs* tbl, const int32_t* wgb, int nranks, int total_wgs, bool doc,
+                                  hipStream_t stream);
 hipError_t launch_attn_f32(const StepArgs& a, int head_dim, hipStream_t stream);
 int attn_bf16_block_m(int head_dim);
 int attn_f32_block_m();

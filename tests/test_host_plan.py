@@ -203,6 +203,9 @@ def test_call_error_codes_enqueue_nothing():
     assert lib.cp_attn_set_option(h, N.OPT_BWD_KEYS, -1) == N.EINVAL
     assert lib.cp_attn_set_option(h, N.OPT_BWD_KEYS, 1) == N.OK
     assert lib.cp_attn_set_option(h, N.OPT_BWD_KEYS, 0) == N.OK
+    assert lib.cp_attn_set_option(h, N.OPT_LOCKSTEP, 2) == N.EINVAL
+    assert lib.cp_attn_set_option(h, N.OPT_LOCKSTEP, 1) == N.OK
+    assert lib.cp_attn_set_option(h, N.OPT_LOCKSTEP, 0) == N.OK
     assert lib.cp_attn_set_option(h, N.OPT_COUNTERS, 2) == N.EINVAL
     assert lib.cp_attn_set_option(h, N.OPT_COUNTERS, 0) == N.OK
     assert lib.cp_attn_last_tile_counts(h, None, 4, None, None) == N.EINVAL

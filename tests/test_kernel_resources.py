@@ -46,9 +46,10 @@ def resources():
 
 
 def test_step_kernel_leaves_room_for_the_receive_kernel(resources):
-    plain = [v for k, v in resources.items() if "attn_step_bf16_d128x8ILb0ELb0E" in k]
-    assert len(plain) == 1, sorted(resources)
-    assert plain[0]["vgpr"] <= 240, plain[0]
+    # <no in-kernel receive, no documents>, one rank's step and every rank's step in one launch
+    plain = [v for k, v in resources.items() if "attn_step_bf16_d128x8ILb0ELb0EL" in k]
+    assert len(plain) == 2, sorted(resources)
+    assert all(v["vgpr"] <= 240 for v in plain), plain
 
 
 def test_no_kernel_spills_to_scratch(resources):
