@@ -121,6 +121,33 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      the copy-kernel or memcpy receive, and no serial, poison or
                                      step-timing mode (and while K/V span at most 4 GiB);
                                      otherwise, and in graph mode, the ranks run back to back. */
+#define CP_ATTN_OPT_FUSED_RING 13 /* 0: one launch of the step kernel per ring step, the running
+                                     state stored between them; 1 (default): every ring step of a
+                                     rank in one launch, where served (cp_attn_fused_ring_active
+                                     tells whether the last call was).  Each row tile takes the keys of all its
+                                     steps in turn with its running max and sum in registers (the
+                                     exact merge of "Sequence Parallelism IV", section 4, carried
+                                     across steps) and writes its output once.  The receives of
+                                     steps 1 .. cp-1 still go one by one on the copy stream (section
+                                     5, "Overlap: More Than One Stream"), each into a slot of its
+                                     own, followed by a one-thread kernel that stores the call's
+                                     epoch to the step's device flag; a workgroup polls that flag
+                                     (a fraction of a second at most) before it loads any key of the step.
+                                     The slots (2 x (cp-1) x n_loc x H x D x 2 bytes), flags and
+                                     key-run table are a library-owned allocation made by the first
+                                     such call and freed with the plan (ENOWORKSPACE if it fails).
+                                     A wait that runs out sets a word that
+                                     cp_attn_ring_wait_timeouts reports; that call's results are not
+                                     valid.  Results agree with mode 0 to rounding (the merge order
+                                     differs).  Served for bf16 head_dim 128, the zigzag causal
+                                     layout without padding with chunks of whole 64-key tiles, the
+                                     fused merge and the copy-kernel receive (CP_ATTN_OPT_RECV 0),
+                                     without documents and the serial, step-timing, counter and
+                                     poison modes, while K/V span at most 4 GiB; otherwise, while a
+                                     graph is recorded and in the no-allocation forward, mode 0.
+                                     2: as 1, but every wait looks for an epoch no signal stores and
+                                     gives up after 16 polls: a test of the time-out path (results
+                                     not valid). */
 
 /*
  * Create a plan (host only: no device memory, no HIP call).
@@ -173,6 +200,19 @@ int cp_attn_set_option(cp_attn_plan_t plan, int option, int value);
  * document list (and again after cp_attn_set_workspace); while documents are
  * set, the caller must not write that region between calls. */
 int cp_attn_workspace_bytes(cp_attn_plan_t plan, int64_t* bytes);
+
+/* Whether a receive wait of the fused ring (CP_ATTN_OPT_FUSED_RING) ran out
+ * of polls since the last query: *timed_out = 1 if so (the results of the
+ * calls since then are not valid), else 0; the word is cleared.  The step
+ * kernel sets it in host-visible memory: query after synchronizing the
+ * calls' stream.  No device call; EINVAL for a null timed_out. */
+int cp_attn_ring_wait_timeouts(cp_attn_plan_t plan, int32_t* timed_out);
+
+/* Whether the plan's last forward call (rank or full) ran each rank it
+ * computed as one fused launch (CP_ATTN_OPT_FUSED_RING served): *active = 1,
+ * else 0 (one launch per ring step, or no call yet).  Host only; EINVAL for a
+ * null active. */
+int cp_attn_fused_ring_active(cp_attn_plan_t plan, int32_t* active);
 
 /* Hand the plan caller-owned device memory of at least cp_attn_workspace_bytes
  * bytes (256-byte aligned); the caller keeps ownership and must keep it alive
@@ -261,8 +301,10 @@ int cp_attn_ulysses_forward(cp_attn_plan_t plan, const void* q, const void* k, c
 /*
  * cp_attn_rank_forward without any allocation, for callers that cannot
  * allocate device memory or create streams: code under HIP graph capture,
- * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
- * result (bit for bit) and errors as cp_attn_rank_forward, but the workspace
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * errors as cp_attn_rank_forward, and its result bit for bit with
+ * CP_ATTN_OPT_FUSED_RING 0 (this call runs one launch per ring step; the
+ * fused launch agrees with that to rounding), but the workspace
  * is a static device array of the library, CP_ATTN_NOALLOC_SCRATCH_BYTES per
  * GPU, held on every GPU the library runs on until the process ends.  The
  * plan's workspace, side streams, events, graph mode, step timing and work

@@ -35,6 +35,7 @@ OPT_KSPLIT = 8
 OPT_COUNTERS = 9
 OPT_BWD_KEYS = 10
 OPT_LOCKSTEP = 12
+OPT_FUSED_RING = 13
 
 NOALLOC_SCRATCH_BYTES = 128 << 20  # CP_ATTN_NOALLOC_SCRATCH_BYTES
 
@@ -50,6 +51,8 @@ SIGNATURES = {
     "cp_attn_set_dtype": (ctypes.c_int, [_c_p, ctypes.c_int]),
     "cp_attn_set_option": (ctypes.c_int, [_c_p, ctypes.c_int, ctypes.c_int]),
     "cp_attn_workspace_bytes": (ctypes.c_int, [_c_p, ctypes.POINTER(_i64)]),
+    "cp_attn_ring_wait_timeouts": (ctypes.c_int, [_c_p, ctypes.POINTER(_i32)]),
+    "cp_attn_fused_ring_active": (ctypes.c_int, [_c_p, ctypes.POINTER(_i32)]),
     "cp_attn_set_workspace": (ctypes.c_int, [_c_p, _c_p, _i64]),
     "cp_attn_set_streams": (ctypes.c_int, [_c_p, _c_p, _c_p]),
     "cp_attn_set_documents": (ctypes.c_int, [_c_p, ctypes.POINTER(_i64), _i64]),

@@ -91,6 +91,26 @@ class Plan:
         one after another (off, the default)."""
         self.set_option(N.OPT_LOCKSTEP, int(bool(on)))
 
+    def set_fused_ring(self, mode):
+        """Every ring step of a rank in one launch where served: True / 1 (the
+        default), False / 0 (one launch per step) or "timeout_test" (2: every
+        receive wait gives up at once; results not valid)."""
+        value = 2 if mode == "timeout_test" else int(bool(mode))
+        self.set_option(N.OPT_FUSED_RING, value)
+
+    def fused_ring_active(self):
+        """True if the last forward call ran each rank as one fused launch."""
+        t = ctypes.c_int32()
+        N.check(self.lib.cp_attn_fused_ring_active(self._h, ctypes.byref(t)), "cp_attn_fused_ring_active")
+        return bool(t.value)
+
+    def ring_wait_timeouts(self):
+        """True if a fused-ring receive wait ran out since the last query
+        (cleared); query after synchronizing the stream of the calls."""
+        t = ctypes.c_int32()
+        N.check(self.lib.cp_attn_ring_wait_timeouts(self._h, ctypes.byref(t)), "cp_attn_ring_wait_timeouts")
+        return bool(t.value)
+
     def set_poison(self, on):
         self.set_option(N.OPT_POISON, int(bool(on)))
 

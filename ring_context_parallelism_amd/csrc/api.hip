@@ -64,6 +64,21 @@ struct DeviceState {
   void* ls_host = nullptr;         // pinned staging of the table
   hipEvent_t ls_uploaded = nullptr;
   std::vector<intptr_t> ls_key;    // what the uploaded table was built for
+  // fused ring (CP_ATTN_OPT_FUSED_RING): receive slots of steps 1 .. P-1 (all
+  // the K slots, then all the V slots), a flag per step (zeroed once), every
+  // rank's key runs (uploaded once) with each rank's two row ranges, the
+  // epoch of the last call and the host-visible time-out word
+  char* fr_slots = nullptr;
+  int64_t fr_slots_bytes = 0;
+  uint32_t* fr_flags = nullptr;
+  RingRun* fr_runs = nullptr;
+  std::vector<SegArgs> fr_segs;  // [rank * 2 + i]: late rows, then early rows (run0 set)
+  bool fr_ok = false;            // the plan's runs are whole tiles (built once)
+  bool fr_built = false;
+  uint32_t* fr_err = nullptr;
+  uint32_t* fr_err_dev = nullptr;
+  uint32_t fr_epoch = 0;
+  int fr_last = 0;  // the last forward call ran every rank it computed as one fused launch
 };
 
 namespace {
@@ -207,6 +222,7 @@ struct RunCfg {
   bool serial = false;     // every step on the caller's stream, no events
   int recv = 0;            // CP_ATTN_OPT_RECV in effect
   int recv_blocks = 256;   // CP_ATTN_OPT_RECV_BLOCKS in effect
+  int fused_ring = 0;      // CP_ATTN_OPT_FUSED_RING in effect (0 while capturing a graph)
   bool counters = false;   // device work counters (plan-owned buffer)
   bool timing = false;     // per-step timing events
   bool poison = false;     // NaN-fill consumed buffers
@@ -221,6 +237,7 @@ RunCfg plan_cfg(const Plan& p, bool capturing) {
   c.counters = p.opt_counters != 0;
   c.timing = p.opt_step_timing != 0 && !capturing;
   c.poison = p.opt_poison != 0;
+  c.fused_ring = capturing ? 0 : p.opt_fused_ring;
   return c;
 }
 
@@ -237,10 +254,7 @@ bool kv_beyond_32bit(const Plan& p) {
   return p.seq_len * p.heads * p.head_dim * p.elem_bytes() > int64_t(UINT32_MAX);
 }
 
-RecvArgs recv_ranges(const Plan& p, char* ws, const void* k, const void* v, int src, int b) {
-  const WsLayout w = ws_layout(p);
-  char* dk = ws + w.slot_k[b];
-  char* dv = ws + w.slot_v[b];
+RecvArgs recv_ranges_to(const Plan& p, char* dk, char* dv, const void* k, const void* v, int src) {
   const int64_t row_bytes = int64_t(p.heads) * p.head_dim * p.elem_bytes();
   const int nch = p.layout == 1 ? 2 : 1;
   const int64_t ch_bytes = p.chunk * row_bytes;
@@ -257,6 +271,11 @@ RecvArgs recv_ranges(const Plan& p, char* ws, const void* k, const void* v, int 
     ra.vec[ra.n++] = bytes / 16;
   }
   return ra;
+}
+
+RecvArgs recv_ranges(const Plan& p, char* ws, const void* k, const void* v, int src, int b) {
+  const WsLayout w = ws_layout(p);
+  return recv_ranges_to(p, ws + w.slot_k[b], ws + w.slot_v[b], k, v, src);
 }
 
 // Side-stream receive of ring source `src` into slot b.  `alone`: no step
@@ -483,6 +502,191 @@ int launch_rank_finalize(Plan& p, const char* ws, void* out, float* lse, int r, 
     if (rc_ != CP_ATTN_OK) return rc_; \
   } while (0)
 
+// ---- fused ring ----
+// Every ring step of a rank in one launch of the step kernel: each row tile
+// takes the keys of all its steps in turn with the running max and sum in
+// registers (the exact merge of "Sequence Parallelism IV: Megatron Context
+// Parallel and Load-Balanced Rings", section 4, carried across steps instead
+// of stored between launches) and writes its output once.  The receives of
+// steps 1 .. P-1 still arrive one by one on the copy stream ("Sequence
+// Parallelism IV", section 5, "Overlap: More Than One Stream"), each into a
+// slot of its own and followed by a one-thread kernel that stores the call's
+// epoch to the step's flag; a workgroup waits for that flag before loading
+// any key of the step.  Served for bf16 head_dim 128, the zigzag causal
+// layout without padding, chunks of whole 64-key tiles, the fused merge and
+// the copy-kernel receive, outside graph capture and the serial, timing,
+// counter and poison modes, without document masks, while the own K/V and
+// the slots each span at most 4 GiB.
+
+constexpr int kRingPolls = 1 << 18;  // polls (each a coherent load and a short sleep, ~0.2-2 us) before a wait gives up
+
+bool fused_ring_served(const Plan& p, const RunCfg& c) {
+  if (!c.fused_ring || c.serial || c.recv != 0 || c.timing || c.counters || c.poison) return false;
+  if (p.dtype != CP_ATTN_BF16 || p.head_dim != 128 || p.layout != 1 || !p.causal || p.opt_merge != 0) return false;
+  if (!p.doc_starts.empty() || p.cp < 2 || kv_beyond_32bit(p) || p.padded_len != p.seq_len) return false;
+  if (int64_t(p.cp - 1) * ws_layout(p).kv_bytes > int64_t(UINT32_MAX)) return false;
+  return p.dev->fr_ok || !p.dev->fr_built;  // (the run check needs the table: built at the first call)
+}
+
+// The key runs of rank r's row range [R0, R0 + chunk): the keys its
+// segments see at each step, in step order (the rank's own chunks read in
+// place at step 0, slot s at step s >= 1), then its causal diagonal (step 0).
+// Returns false if a run is not a whole number of 64-key tiles or a step's
+// segments do not cover the range whole.
+bool ring_runs(const Plan& p, int r, int64_t R0, std::vector<RingRun>& runs, SegArgs& sa) {
+  const int64_t C = p.chunk;
+  int64_t key = 0, diag_lo = -1;
+  auto own_row = [&](int64_t kk) { return kk < C ? p.chunk_of(r, 0) * C + kk : p.chunk_of(r, 1) * C + (kk - C); };
+  auto add = [&](int64_t n, int64_t row, int buf, int step) {
+    if (n <= 0) return true;
+    if (n % 64) return false;
+    runs.push_back(RingRun{int32_t(key + n), int32_t(row - key), buf, step});
+    key += n;
+    return true;
+  };
+  for (int s = 0; s < p.cp; ++s) {
+    const StepDesc& sd = p.step(r, s);
+    for (int i = 0; i < sd.nseg; ++i) {
+      const Segment& g = sd.seg[i];
+      if (g.q_start + g.q_len <= R0 || g.q_start >= R0 + C) continue;  // not these rows
+      if (g.q_start > R0 || g.q_start + g.q_len < R0 + C) return false;  // part of them
+      if (s == 0) {
+        // the own buffer's two chunks are apart in the natural order
+        if (!add(std::min(g.kv_full, C), own_row(0), 0, -1)) return false;
+        if (!add(g.kv_full - C, own_row(C), 0, -1)) return false;
+      } else if (!add(g.kv_full, int64_t(s - 1) * p.n_loc, 1, s)) {
+        return false;
+      }
+      if (g.diag) {
+        if (s != 0 || g.q_start != R0) return false;
+        diag_lo = g.kv_full;
+      }
+    }
+  }
+  sa = SegArgs{};
+  sa.q_start = int32_t(R0);
+  sa.q_len = int32_t(C);
+  sa.q_global = p.global_row(r, R0);
+  sa.kv_full = int32_t(key);
+  sa.diag = diag_lo >= 0 ? 1 : 0;
+  if (sa.diag && !add(C, own_row(diag_lo), 0, -1)) return false;
+  sa.epi = kEpiInit | kEpiFinal;
+  const int bm = attn_bf16_block_m(128);
+  sa.tiles = int32_t((C + bm - 1) / bm);
+  sa.ksplit = 1;
+  return !runs.empty();
+}
+
+// The run table of every rank, uploaded once per plan (set-up, synchronous).
+int ensure_fused_ring(Plan& p) {
+  DeviceState& d = *p.dev;
+  if (!d.fr_built) {
+    d.fr_built = true;
+    d.fr_ok = false;
+    std::vector<RingRun> all;
+    d.fr_segs.assign(size_t(p.cp) * 2, SegArgs{});
+    bool ok = true;
+    for (int r = 0; r < p.cp && ok; ++r) {
+      const int64_t R0[2] = {p.chunk, 0};  // late rows first: they see more keys
+      for (int i = 0; i < 2 && ok; ++i) {
+        std::vector<RingRun> runs;
+        SegArgs sa;
+        ok = ring_runs(p, r, R0[i], runs, sa);
+        sa.run0 = int32_t(all.size());
+        all.insert(all.end(), runs.begin(), runs.end());
+        d.fr_segs[size_t(r) * 2 + i] = sa;
+      }
+    }
+    if (!ok) return CP_ATTN_OK;  // served no more: the per-step launches take over
+    void* m = nullptr;
+    CPA_HIP(hipMalloc(&m, all.size() * sizeof(RingRun)));
+    d.fr_runs = static_cast<RingRun*>(m);
+    CPA_HIP(hipMemcpy(d.fr_runs, all.data(), all.size() * sizeof(RingRun), hipMemcpyHostToDevice));
+    CPA_HIP(hipMalloc(&m, size_t(p.cp) * sizeof(uint32_t)));
+    d.fr_flags = static_cast<uint32_t*>(m);
+    CPA_HIP(hipMemset(d.fr_flags, 0, size_t(p.cp) * sizeof(uint32_t)));
+    CPA_HIP(hipDeviceSynchronize());  // zero before any stream of the plan reads them
+    void* h = nullptr;
+    CPA_HIP(hipHostMalloc(&h, sizeof(uint32_t), hipHostMallocCoherent | hipHostMallocMapped));
+    d.fr_err = static_cast<uint32_t*>(h);
+    *d.fr_err = 0;
+    CPA_HIP(hipHostGetDevicePointer(&m, h, 0));
+    d.fr_err_dev = static_cast<uint32_t*>(m);
+    d.fr_ok = true;
+  }
+  if (!d.fr_ok) return CP_ATTN_OK;
+  const int64_t need = 2 * align256(int64_t(p.cp - 1) * ws_layout(p).kv_bytes);
+  if (d.fr_slots_bytes < need) {
+    if (d.fr_slots) {  // earlier calls may still use it
+      CPA_HIP(hipDeviceSynchronize());
+      CPA_HIP(hipFree(d.fr_slots));
+      d.fr_slots = nullptr;
+      d.fr_slots_bytes = 0;
+    }
+    void* m = nullptr;
+    if (hipMalloc(&m, size_t(need)) != hipSuccess) return fail(CP_ATTN_ENOWORKSPACE, "hipMalloc of the fused-ring slots failed");
+    d.fr_slots = static_cast<char*>(m);
+    d.fr_slots_bytes = need;
+  }
+  return CP_ATTN_OK;
+}
+
+int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const void* v, void* out, float* lse,
+                   int r, hipStream_t st) {
+  DeviceState& d = *p.dev;
+  const WsLayout w = ws_layout(p);
+  const int P = p.cp;
+  if (++d.fr_epoch == 0) d.fr_epoch = 1;  // a zeroed flag never reads as done
+  const uint32_t epoch = d.fr_epoch;
+  const int64_t kvs = w.kv_bytes;  // one slot of K (or V): the source's n_loc rows
+  char* const k2 = d.fr_slots;
+  char* const v2 = d.fr_slots + align256(int64_t(P - 1) * kvs);
+  // the copy stream starts behind everything queued on st before this call
+  // (an earlier call's kernel may still read the slots)
+  CPA_HIP(hipEventRecord(d.start, st));
+  CPA_HIP(hipStreamWaitEvent(d.copy, d.start, 0));
+  for (int s = 1; s < P; ++s) {
+    const RecvArgs ra = recv_ranges_to(p, k2 + int64_t(s - 1) * kvs, v2 + int64_t(s - 1) * kvs, k, v, p.step(r, s).src);
+    // the first receive is needed soonest: the full grid; then the narrow one
+    CPA_HIP(launch_recv(ra, s == 1 ? 0 : c.recv_blocks, d.copy));
+    CPA_HIP(launch_ring_signal(d.fr_flags + s, epoch, d.copy));
+  }
+  StepArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_bytes = p.seq_len * p.heads * p.head_dim * p.elem_bytes();
+  a.k2 = k2;
+  a.v2 = v2;
+  a.kv2_bytes = int64_t(P - 1) * kvs;
+  a.acc_o = reinterpret_cast<float*>(c.ws + w.acc_o);
+  a.acc_lse = reinterpret_cast<float*>(c.ws + w.acc_lse);
+  a.out = out;
+  a.lse = lse;
+  a.seq_len = p.seq_len;
+  a.n_loc = int32_t(p.n_loc);
+  a.kv_valid = int32_t(p.n_loc);
+  a.heads = p.heads;
+  a.scale = 1.0f / std::sqrt(float(p.head_dim));
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.out_f32 = 0;
+  a.nseg = 2;
+  for (int i = 0; i < 2; ++i) {
+    a.seg[i] = d.fr_segs[size_t(r) * 2 + i];
+    a.total_tiles += a.seg[i].tiles;
+  }
+  a.runs = d.fr_runs;
+  a.ring_flags = d.fr_flags;
+  a.ring_err = d.fr_err_dev;
+  // test mode: an epoch no signal ever stores, and few polls
+  a.ring_epoch = c.fused_ring == 2 ? epoch + 0x40000000u : epoch;
+  a.ring_polls = c.fused_ring == 2 ? 16 : kRingPolls;
+  const hipError_t e = launch_attn_bf16_ring(a, st);
+  if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("fused ring launch: ") + hipGetErrorString(e));
+  d.fr_last = 1;
+  return CP_ATTN_OK;
+}
+
 int run_rank(Plan& p, const RunCfg& c, const void* q, const void* k, const void* v, void* out, float* lse, int r,
              hipStream_t st) {
   DeviceState& d = *p.dev;
@@ -500,6 +704,11 @@ int run_rank(Plan& p, const RunCfg& c, const void* q, const void* k, const void*
     for (int s = 0; s < P; ++s) d.counted[size_t(r) * P + s] = 1;
   }
   if (p.valid_rows(r) == 0) return CP_ATTN_OK;  // a rank of pad tokens only: nothing to compute or write
+  if (fused_ring_served(p, c)) {
+    CPA_TRY(ensure_fused_ring(p));
+    if (p.dev->fr_ok) return run_rank_fused(p, c, q, k, v, out, lse, r, st);
+  }
+  p.dev->fr_last = 0;
   if (rank_splits(p, r)) {
     // The key split's per-tile counters: the kernels leave every counter they
     // use at zero, but nothing stops a caller from writing its workspace
@@ -587,6 +796,7 @@ int64_t lockstep_rank_bytes(const Plan& p) { return ws_layout(p).part_o[0]; }
 int run_lockstep(Plan& p, const RunCfg& c0, const void* q, const void* k, const void* v, void* out, float* lse,
                  hipStream_t st) {
   DeviceState& d = *p.dev;
+  d.fr_last = 0;
   const int P = p.cp;
   const int64_t rb = lockstep_rank_bytes(p);
   const int64_t tbl_bytes = int64_t(P) * P * int64_t(sizeof(StepArgs));
@@ -925,6 +1135,10 @@ int cp_attn_plan_destroy(cp_attn_plan_t h) {
       if (d.ls_ws) (void)hipFree(d.ls_ws);
       if (d.ls_host) (void)hipHostFree(d.ls_host);
       if (d.ls_uploaded) (void)hipEventDestroy(d.ls_uploaded);
+      if (d.fr_slots) (void)hipFree(d.fr_slots);
+      if (d.fr_flags) (void)hipFree(d.fr_flags);
+      if (d.fr_runs) (void)hipFree(d.fr_runs);
+      if (d.fr_err) (void)hipHostFree(d.fr_err);
       if (d.own_ws && d.ws) (void)hipFree(d.ws);
       if (d.own_copy && d.copy) (void)hipStreamDestroy(d.copy);
       if (d.own_merge && d.merge) (void)hipStreamDestroy(d.merge);
@@ -997,6 +1211,10 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
       if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "CP_ATTN_OPT_LOCKSTEP must be 0 or 1");
       p.opt_lockstep = value;
       return CP_ATTN_OK;
+    case CP_ATTN_OPT_FUSED_RING:
+      if (value < 0 || value > 2) return fail(CP_ATTN_EINVAL, "CP_ATTN_OPT_FUSED_RING must be 0, 1 or 2");
+      p.opt_fused_ring = value;
+      return CP_ATTN_OK;
     case CP_ATTN_OPT_COUNTERS:
       if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "counters option must be 0 or 1");
       p.opt_counters = value;
@@ -1004,6 +1222,21 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
     default:
       return fail(CP_ATTN_EINVAL, "unknown option");
   }
+}
+
+int cp_attn_fused_ring_active(cp_attn_plan_t h, int32_t* active) {
+  CPA_TRY(check_plan(h));
+  if (!active) return fail(CP_ATTN_EINVAL, "active is null");
+  *active = h->p->dev->fr_last;
+  return CP_ATTN_OK;
+}
+
+int cp_attn_ring_wait_timeouts(cp_attn_plan_t h, int32_t* timed_out) {
+  CPA_TRY(check_plan(h));
+  if (!timed_out) return fail(CP_ATTN_EINVAL, "timed_out is null");
+  DeviceState& d = *h->p->dev;
+  *timed_out = d.fr_err ? int32_t(__atomic_exchange_n(d.fr_err, 0u, __ATOMIC_SEQ_CST) != 0) : 0;
+  return CP_ATTN_OK;
 }
 
 int cp_attn_workspace_bytes(cp_attn_plan_t h, int64_t* bytes) {

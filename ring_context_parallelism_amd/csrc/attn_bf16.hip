@@ -416,17 +416,50 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kThreads8 = 512;
 constexpr int kBM8 = 256;
 
+// Fused-ring receive wait: poll flag `step` of the call until it reaches the
+// call's epoch (wrap-aware), sleeping between polls; after ring_polls polls
+// the wave's first lane records the time-out in the host-visible word and
+// the wave goes on.  The relaxed agent-scope load reads the flag through to
+// device coherence (sc1), never from an older copy in this XCD's L2.  Every
+// lane of the calling wave takes the same path.
+__device__ __forceinline__ void ring_wait(const StepArgs& a, int step) {
+  const uint32_t* const f = a.ring_flags + step;
+  for (int n = 0; int32_t(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - a.ring_epoch) < 0; ++n) {
+    if (n >= a.ring_polls) {
+      if ((threadIdx.x & 63) == 0) __hip_atomic_store(a.ring_err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
 // kRanks: every rank's step of one ring step in one launch (a CP group in
 // lockstep on one GPU): rank r's workgroups are wgb[r] .. wgb[r + 1] - 1
 // (ranges that start at multiples of 8, so a rank's workgroups keep their
 // XCD mapping), its arguments tbl[r] (device memory); a workgroup past its
 // rank's tiles (padding of the range) does nothing.  Otherwise the launch is
 // one rank's step, with arguments a0.
-template <bool kRecv, bool kDoc, bool kRanks>
+// kRing: every ring step of one rank in one launch.  A row tile's keys are
+// the runs of its segment (StepArgs::runs): the rank's own chunks in place
+// and the receive slots of steps 1 .. P-1, every run a whole number of
+// 64-key tiles, the causal diagonal last.  The running max and sum stay in
+// registers from the first step to the last, and the epilogue writes the
+// output once.  At the top of tile j (j a multiple of 4) wave 4 holds the
+// workgroup until the receives of the runs up to tile j + 6 have landed
+// (their flags carry the call's epoch); the barrier that ends tile j puts
+// that ahead of every load of tiles j + 3 .. j + 6, which the waves issue in
+// tiles j + 1 .. j + 4.  No cache maintenance
+// is needed: a slot's rows reach a cache of this kernel only through those
+// loads, after the flag; the kernel started with its caches invalidated
+// (kernel-start acquire), and the copy kernel's writes were made visible at
+// agent scope when it completed, before the signal kernel behind it on the
+// copy stream stored the flag.
+template <bool kRecv, bool kDoc, bool kRanks, bool kRing = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8), amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16_d128x8(StepArgs a0, const StepArgs* __restrict__ tbl, const int32_t* __restrict__ wgb, int nranks) {
   constexpr int D = 128, NT = 8, NB = 4;
   static_assert(!(kRanks && kRecv), "the in-kernel receive is per rank");
+  static_assert(!(kRing && (kRecv || kDoc || kRanks)), "the fused ring stands alone");
   int bid = int(blockIdx.x), nblk = int(gridDim.x), rank = 0;
   if constexpr (kRanks) {
     int lo = 0, hi = nranks;  // the rank: wgb[lo] <= blockIdx.x < wgb[lo + 1]
@@ -533,7 +566,46 @@ void attn_step_bf16_d128x8(StepArgs a0, const StepArgs* __restrict__ tbl, const 
   for (int n = 0; n < 4; ++n) vrow[n] = uint32_t(lrow0 + 4 * n) * row_bytes + (hbase ^ (uint32_t(swz(4 * n)) << 4));
   const u32x4 desc_k = buffer_desc(a.k, uint32_t(a.kv_bytes));
   const u32x4 desc_v = buffer_desc(a.v, uint32_t(a.kv_bytes));
+  // fused ring: the wave's position in the segment's key runs and the buffer
+  // of its current run (a wave loads only K or only V: one descriptor); wave
+  // 0 keeps a second position for the receive gate
+  int ld_run = -1, ld_end = 0, ld_delta = 0;
+  u32x4 ld_desc = {};
+  // the run table is written once at set-up and only read here: through the
+  // constant address space its wave-uniform reads are scalar loads
+  typedef const __attribute__((address_space(4))) RingRun c_run;
+  c_run* const runs = (c_run*)(a.runs);
+  int gt_run = -1, gt_end = 0, gt_step = 0;
+  auto gate = [&](int j0) {  // wave 4: the receives of the runs up to the one holding key j0 have landed
+    while (j0 >= gt_end) {
+      ++gt_run;
+      c_run& rr = runs[g.run0 + gt_run];
+      gt_end = __builtin_amdgcn_readfirstlane(rr.end);  // (wave-uniform: keep run fields scalar)
+      const int st = __builtin_amdgcn_readfirstlane(rr.step);
+      if (st > gt_step) {
+        ring_wait(a, st);
+        gt_step = st;
+      }
+    }
+  };
   auto issue = [&](const u32x4& desc, int j0, lds_u8* dst) {
+    if constexpr (kRing) {
+      // runs are whole tiles: the tile's 64 rows are consecutive rows of one buffer
+      while (j0 >= ld_end) {
+        ++ld_run;
+        c_run& rr = runs[g.run0 + ld_run];
+        ld_end = __builtin_amdgcn_readfirstlane(rr.end);
+        ld_delta = __builtin_amdgcn_readfirstlane(rr.delta);
+        if (__builtin_amdgcn_readfirstlane(rr.buf))
+          ld_desc = buffer_desc(wv < 4 ? a.k2 : a.v2, uint32_t(a.kv2_bytes));
+        else
+          ld_desc = buffer_desc(wv < 4 ? a.k : a.v, uint32_t(a.kv_bytes));
+      }
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(uint32_t(j0 + ld_delta) * row_bytes);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) dma_lds16(ld_desc, vrow[n], soff, lds_addr(dst + (16 * (wv & 3) + 4 * n) * 256));
+      return;
+    }
     // Fast path: the 64 source rows are consecutive and inside the buffer, so
     // the tile base is one scalar offset.  Otherwise (a tile that crosses the
     // split between the two chunks, or the ragged last tile) each lane maps
@@ -725,6 +797,12 @@ void attn_step_bf16_d128x8(StepArgs a0, const StepArgs* __restrict__ tbl, const 
   // holds back only loads younger than the tile loads of tile j - 1 (the
   // copy load and the four tile loads of tile j; with one of tile j - 1's
   // loads still in flight those five would be too, six or seven in all).
+  if constexpr (kRing) {
+    // the first three tiles' receives, before the first loads
+    if (wv == 4 && ntiles > 0) gate(kb0 + min(2, ntiles - 1) * kBN);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
   if (ntiles > 0) {
     const u32x4& desc = wv < 4 ? desc_k : desc_v;
     issue(desc, kb0, wv < 4 ? kst(0) : vst(0));
@@ -812,6 +890,12 @@ void attn_step_bf16_d128x8(StepArgs a0, const StepArgs* __restrict__ tbl, const 
       if (ntiles > 0) __builtin_nontemporal_store(creg, cdst + chunk_vec(ntiles - 1));
   } else {
     for (int j = 0; j < ntiles; j += 4) {
+      // fused ring: the receives of tiles j + 3 .. j + 6, whose loads the
+      // waves issue in tiles j + 1 .. j + 4, after the barriers that end
+      // tiles j .. j + 3 (tile j + 2's were gated one iteration earlier).
+      // Wave 4 polls: in wave 0 the gate cost the loops twelve VGPRs.
+      if constexpr (kRing)
+        if (wv == 4) gate(kb0 + min(j + 6, ntiles - 1) * kBN);
       CPATTN_X8_TILE_B(j, 0);
       CPATTN_X8_TILE_B(j + 1, 1);
       CPATTN_X8_TILE_B(j + 2, 2);
@@ -986,6 +1070,12 @@ hipError_t launch_attn_bf16_ranks(const StepArgs* tbl, const int32_t* wgb, int n
     attn_step_bf16_d128x8<false, true, true><<<grid, kThreads8, 0, stream>>>(StepArgs{}, tbl, wgb, nranks);
   else
     attn_step_bf16_d128x8<false, false, true><<<grid, kThreads8, 0, stream>>>(StepArgs{}, tbl, wgb, nranks);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_ring(const StepArgs& a, hipStream_t stream) {
+  const dim3 grid(unsigned(a.total_tiles) * unsigned(a.heads));
+  attn_step_bf16_d128x8<false, false, false, true><<<grid, kThreads8, 0, stream>>>(a, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -26,6 +26,20 @@ struct SegArgs {
   int32_t tiles;     // workgroups of the segment: ceil(q_len / BM) * ksplit
   int32_t ksplit;    // 1, or 2: each row tile's keys in two halves, one workgroup each (full segments
                      // starting at a multiple of 256 local rows only)
+  int32_t run0;      // fused ring: index in StepArgs::runs of the segment's first key run
+};
+
+// Fused ring (every ring step of a rank in one launch): the keys a segment's
+// rows see are a sequence of runs, in the order the workgroup takes them.
+// Run i covers the segment's keys [end of run i-1, end) and key kk of it is
+// source row kk + delta of buffer buf (0: the rank's own natural-order K/V,
+// 1: the receive slots); its rows are there once flag `step` of the call has
+// reached the call's epoch (step < 0: nothing to wait for).
+struct RingRun {
+  int32_t end;
+  int32_t delta;
+  int32_t buf;
+  int32_t step;
 };
 
 // Ring receive: up to four contiguous byte ranges (16-byte multiples).
@@ -84,6 +98,19 @@ struct StepArgs {
   int32_t kpos_lo;
   int32_t kpos_hi;
   int32_t kpos_split;
+  // fused ring (null runs: not fused): the receive slots of steps 1 .. P-1,
+  // K and V each one buffer of rows (kv2_bytes addressable from each), the
+  // segments' key runs, and the per-step receive flags; a workgroup polls
+  // flag s (at most ring_polls times) before it loads any row of a run of
+  // step s, and a wait that runs out stores 1 to *ring_err (host-visible)
+  const void* k2;
+  const void* v2;
+  int64_t kv2_bytes;
+  const RingRun* runs;
+  const uint32_t* ring_flags;
+  uint32_t* ring_err;
+  uint32_t ring_epoch;
+  int32_t ring_polls;
 };
 
 // Backward of one ring step (attn_bwd.hip, attn_bwd_bf16.hip).  Q, dO, O are
@@ -138,6 +165,12 @@ hipError_t launch_bwd_bf16_d128(const BwdArgs& a, bool eight_wave_keys, hipStrea
 bool attn_does_recv(int dtype_bf16, int head_dim);
 bool attn_splits_keys(int dtype_bf16, int head_dim);  // kernel honours SegArgs::ksplit
 hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream);
+// fused ring: one launch of the bf16 head_dim 128 kernel over every ring step
+// of a rank (StepArgs::runs set)
+hipError_t launch_attn_bf16_ring(const StepArgs& a, hipStream_t stream);
+// store epoch to *flag (release, agent scope) from one thread, once every
+// kernel before it on the stream has completed
+hipError_t launch_ring_signal(uint32_t* flag, uint32_t epoch, hipStream_t stream);
 // Every rank's step of one ring step in one launch (bf16, head_dim 128, no
 // in-kernel receive): tbl[r] (device memory) are rank r's arguments, its
 // workgroups wgb[r] .. wgb[r + 1] - 1 (wgb[nranks] = total_wgs; each range

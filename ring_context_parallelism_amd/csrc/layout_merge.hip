@@ -123,6 +123,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_num_vgpr(16))) void recv_
   }
 }
 
+// Fused-ring receive flag: launched behind the copy kernel on its stream, so
+// it runs once that kernel has completed (and its writes are visible at agent
+// scope); the release store then publishes the epoch.
+__global__ __launch_bounds__(64) void ring_signal(uint32_t* flag, uint32_t epoch) {
+  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ __launch_bounds__(kThreads) void poison_fill(uint4* p, int64_t n) {
   const uint4 nan4 = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
   for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads)
@@ -232,6 +239,11 @@ hipError_t launch_recv(const RecvArgs& a, int blocks, hipStream_t stream) {
   if (total == 0) return hipSuccess;
   const unsigned cap = blocks > 0 ? unsigned(blocks) : 65536u;
   recv_copy<<<grid_for(total, 64 * 2, cap), 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_signal(uint32_t* flag, uint32_t epoch, hipStream_t stream) {
+  ring_signal<<<1, 64, 0, stream>>>(flag, epoch);
   return hipGetLastError();
 }
 

@@ -56,6 +56,7 @@ struct Plan {
   int32_t opt_counters = 0;
   int32_t opt_bwd_keys = 0;
   int32_t opt_lockstep = 0;
+  int32_t opt_fused_ring = 1;
   int32_t opt_recv_blocks = 256;
 
   DeviceState* dev = nullptr;

@@ -68,6 +68,7 @@ def test_graph_replays_match_eager(mode, dtype):
     _say(f"graph mode={mode} {dtype} seq={seq} cp={cp} rank={rank}")
     q, k, v = make_qkv(seq, heads, dim, "bf16" if dtype == torch.bfloat16 else "fp32", 31)
     p = Plan(seq, cp, heads, dim, True, "zigzag", dtype=dtype)
+    p.set_fused_ring(False)  # graph mode records the one-launch-per-step schedule
     if mode in ("memcpy", "hybrid"):
         p.set_recv(mode)
     elif mode == "separate":
@@ -110,6 +111,7 @@ def test_graph_full_forward_and_option_change():
     _say(f"graph full_forward seq={seq} cp={cp}")
     q, k, v = make_qkv(seq, heads, dim, "bf16", 33)
     p = Plan(seq, cp, heads, dim, True, "zigzag", dtype=torch.bfloat16)
+    p.set_fused_ring(False)  # graph mode records the one-launch-per-step schedule
     b = _bufs(p, q, k, v)
     ref = _call(p, b, None)
     p.set_graph(True)

@@ -40,6 +40,7 @@ def _same(a, b):
 
 def _both(p, qd, kd, vd):
     p.set_key_split(False)
+    p.set_fused_ring(False)  # lockstep launches each step: compare with one launch per step
     p.set_lockstep(False)
     ref = _full(p, qd, kd, vd)
     p.set_lockstep(True)
@@ -81,6 +82,7 @@ def test_lockstep_repeated_calls_new_buffers_memcpy_receive_documents_counters()
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     p = Plan(seq, cp, heads, 128, True, "zigzag")
     p.set_key_split(False)
+    p.set_fused_ring(False)
     ref = _full(p, qd, kd, vd)
     p.set_lockstep(True)
     _say("lockstep: repeated calls and new buffers")

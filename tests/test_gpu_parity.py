@@ -159,6 +159,7 @@ def test_schedule_modes_agree(dtype):
     _say(f"modes {dtype}")
     q, k, v = make_qkv(seq, heads, dim, "bf16" if dtype == torch.bfloat16 else "fp32", 13)
     p = Plan(seq, cp, heads, dim, True, "zigzag", dtype=dtype)
+    p.set_fused_ring(False)  # the modes of the one-launch-per-step schedule
     base = _run(p, q, k, v)
     p.set_serialize(True)
     ser = _run(p, q, k, v)
@@ -380,6 +381,7 @@ def test_key_split_matches_oracle(layout, seq, cp, heads, causal):
     _say(f"key split {layout} seq={seq} cp={cp} heads={heads} causal={causal}")
     q, k, v = make_qkv(seq, heads, 128, "bf16", 41)
     p = Plan(seq, cp, heads, 128, causal, layout)
+    p.set_fused_ring(False)  # the key split belongs to the one-launch-per-step schedule
     runs = [_run(p, q, k, v) for _ in range(3)]
     for o, l in runs[1:]:
         assert _bitwise_equal(o, runs[0][0]) and _bitwise_equal(l, runs[0][1])

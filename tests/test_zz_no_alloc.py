@@ -37,6 +37,7 @@ def _both(seq, cp, layout, causal, heads, dim, dtype, rank, seed):
     q, k, v = make_qkv(seq, heads, dim, "bf16" if dtype == torch.bfloat16 else "fp32", seed)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     p = Plan(seq, cp, heads, dim, causal, layout, dtype=dtype)
+    p.set_fused_ring(False)  # the no-allocation call runs one launch per step
     res = []
     for fn in (p.rank_forward, p.rank_forward_noalloc):
         out = torch.full_like(qd, float("nan"))
