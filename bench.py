@@ -52,6 +52,11 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="also time the share's backward (on by default with the extras)")
     ap.add_argument("--no-key-split", action="store_true", help="never split a step's keys over two workgroups")
+    ap.add_argument("--no-fused-ring", action="store_true",
+                    help="one launch of the step kernel per ring step instead of one per rank")
+    ap.add_argument("--fused-ring-staged", action="store_true",
+                    help="fused ring with every receive done before the launch (for counter collection, "
+                         "which runs one kernel at a time)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one layout gather of q (a plain copy of known size) before timing, "
                          "as the reference for hardware traffic counters")
@@ -104,6 +109,20 @@ def step_kernel_times(plan, w, bufs, stream, reps, graph=False):
     plan.set_step_timing(False)
     plan.set_graph(graph)
     return acc / reps
+
+
+def kernel_launches(plan, w, bufs, stream, reps):
+    """The attention launches of one call of the plan's default schedule:
+    (kind, per-launch ms list), from the library's HIP step events recorded
+    on the launching stream right around each launch: one per ring step, or
+    one per rank for a call that ran fused (CP_ATTN_OPT_FUSED_RING, reported
+    under step 0)."""
+    run_call(plan, w, bufs, stream)
+    torch.cuda.synchronize()
+    fused = plan.fused_ring_active()
+    times = step_kernel_times(plan, w, bufs, stream, reps)
+    ranks = range(w.cp) if w.rank is None else [w.rank]
+    return ("fused_ring" if fused else "per_step"), [times[r][s] for r in ranks for s in range(w.cp) if times[r][s] > 0]
 
 
 PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -199,6 +218,7 @@ def imbalance_section(stream):
     for layout in ("zigzag", "contiguous"):
         w = WORKLOADS[f"causal_s16384_cp4_{layout}_h16_d128_bf16"]
         p = R.Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout)
+        p.set_fused_ring(False)  # per-step times: the one-launch-per-step schedule
         tiles = [[p.valid_work(r, s, 128, 64)[0] for s in range(w.cp)] for r in range(w.cp)]
         q, k, v = (t.cuda() for t in workload_qkv(w))
         out = torch.empty_like(q)
@@ -249,16 +269,19 @@ def workload_section(name, stream, steps, graph_too=False):
     flops = 4 * w.head_dim * w.heads * pairs
     ms = time_calls(p, w, bufs, stream, steps, 3, 0.3)
     med = time_calls.last["median"]
-    times = step_kernel_times(p, w, bufs, stream, 3)
-    ranks = range(w.cp) if w.rank is None else [w.rank]
-    launches = [times[r][s] for r in ranks for s in range(w.cp) if times[r][s] > 0]
+    kind, launches = kernel_launches(p, w, bufs, stream, 3)
     avg = float(np.mean(launches))
     kern = flops / len(launches) / (avg * 1e-3) / 1e12
     res = {"workload": name, "share": "all ranks" if w.rank is None else f"rank {w.rank}", "valid_flops": flops,
            "ms_per_call": round(ms, 5), "ms_per_call_median": round(med, 5),
            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-           "step_kernel": {"launches_per_call": len(launches), "avg_launch_ms": round(avg, 5),
+           "step_kernel": {"schedule": kind, "launches_per_call": len(launches), "avg_launch_ms": round(avg, 5),
                            "tflops": round(kern, 2), "frac_bf16_peak": round(kern / PEAK_BF16_TFLOPS, 4)}}
+    if kind == "fused_ring":
+        p.set_fused_ring(False)
+        sms = time_calls(p, w, bufs, stream, steps, 3, 0.3)
+        p.set_fused_ring(True)
+        res["one_launch_per_step_ms_per_call"] = round(sms, 5)
     if graph_too:
         p.set_graph(True)
         gms = time_calls(p, w, bufs, stream, steps, 3, 0.3)
@@ -281,8 +304,11 @@ def workload_section(name, stream, steps, graph_too=False):
 
 def rank_step_imbalance(plan, w, bufs, stream, reps=3):
     """Every rank's share of the timed workload, one rank_forward call each:
-    per-(rank, step) step-kernel ms, per-step max/mean over ranks, and the
-    valid 128x64 tile counts (the plan's balance)."""
+    per-(rank, step) step-kernel ms of the one-launch-per-step schedule,
+    per-step max/mean over ranks, and the valid 128x64 tile counts (the
+    plan's balance); then every rank's share measured whole: back to back
+    with the fused ring, back to back one launch per step, and in lockstep."""
+    plan.set_fused_ring(False)
     times = []
     for r in range(w.cp):
         plan.set_step_timing(True)
@@ -307,8 +333,9 @@ def rank_step_imbalance(plan, w, bufs, stream, reps=3):
     # (every rank's ring step in one launch), whole calls
     flops_all = 4 * w.head_dim * w.heads * all_pairs
     full = {}
-    for mode in (False, True):
-        plan.set_lockstep(mode)
+    for mode in ("per_step", "lockstep", "fused"):
+        plan.set_lockstep(mode == "lockstep")
+        plan.set_fused_ring(mode == "fused")
         for _ in range(2):
             plan.full_forward(*bufs, stream=stream)
         torch.cuda.synchronize()
@@ -320,10 +347,13 @@ def rank_step_imbalance(plan, w, bufs, stream, reps=3):
         torch.cuda.synchronize()
         full[mode] = ev[0].elapsed_time(ev[1]) / reps
     plan.set_lockstep(False)
-    measured = {"all_ranks_back_to_back_ms": round(full[False], 5), "all_ranks_lockstep_ms": round(full[True], 5),
-                "lockstep_ms_per_rank": round(full[True] / w.cp, 5),
-                "lockstep_tflops_per_gpu": round(flops_all / (full[True] * 1e-3) / 1e12, 2),
-                "lockstep_frac_bf16_peak": round(flops_all / (full[True] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    plan.set_fused_ring(True)
+    measured = {"all_ranks_fused_ring_ms": round(full["fused"], 5),
+                "fused_ring_tflops_per_gpu": round(flops_all / (full["fused"] * 1e-3) / 1e12, 2),
+                "all_ranks_back_to_back_ms": round(full["per_step"], 5), "all_ranks_lockstep_ms": round(full["lockstep"], 5),
+                "lockstep_ms_per_rank": round(full["lockstep"] / w.cp, 5),
+                "lockstep_tflops_per_gpu": round(flops_all / (full["lockstep"] * 1e-3) / 1e12, 2),
+                "lockstep_frac_bf16_peak": round(flops_all / (full["lockstep"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "note": "one GPU runs every rank; per GPU of a cp-GPU ring, the same rate"}
     return {"workload": w.name, "step_ms": [[round(float(x), 4) for x in row] for row in t],
             "measured_lockstep": measured,
@@ -526,6 +556,10 @@ def main():
         plan.set_merge(True)
     if args.no_key_split:
         plan.set_key_split(False)
+    if args.no_fused_ring:
+        plan.set_fused_ring(False)
+    if args.fused_ring_staged:
+        plan.set_fused_ring("staged")
 
     if args.copy_probe:
         probe = torch.empty_like(q)
@@ -541,13 +575,14 @@ def main():
     print(f"[bench] {w.name}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     # dominant kernel: the attention step kernel, timed with HIP events on its own stream
-    times = step_kernel_times(plan, w, bufs, stream, min(args.steps, 10), args.graph)
-    ranks = range(w.cp) if w.rank is None else [w.rank]
-    launches = [times[r][s] for r in ranks for s in range(w.cp) if times[r][s] > 0]
+    plan.set_graph(False)
+    kind, launches = kernel_launches(plan, w, bufs, stream, min(args.steps, 10))
+    plan.set_graph(args.graph)
     avg_ms = float(np.mean(launches))
     flops_per_launch = flops / len(launches)
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
-    roofline = {"kernel": "attn_step_bf16" if w.dtype == "bf16" else "attn_step_f32", "bound": "mfma",
+    kname = "attn_step_bf16" if w.dtype == "bf16" else "attn_step_f32"
+    roofline = {"kernel": kname + ("_fused_ring" if kind == "fused_ring" else ""), "bound": "mfma",
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(w.name),
                 "avg_launch_ms": round(avg_ms, 5), "launches_per_step": len(launches),
@@ -602,7 +637,12 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             ms_allgather = round(e0.elapsed_time(e1) / ag_calls, 5)
+        plan.set_fused_ring(False)
+        ms_per_step_launches = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
+        plan.set_fused_ring("staged" if args.fused_ring_staged else not args.no_fused_ring)
         result["modes_ms"] = {"default_receive": args.recv or "kernel",
+                              "dominant_launch": kind,
+                              "one_launch_per_step": ms_per_step_launches,
                               "graph_mode": bool(args.graph),
                               ("eager_calls" if args.graph else "graph_replay"): ms_graph_other,
                               "allgather_single_launch": ms_allgather,

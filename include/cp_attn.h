@@ -82,7 +82,8 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      3: as 0 for step 0 (receive of step 1), then as 2: no
                                         cross-stream event after step 1 */
 #define CP_ATTN_OPT_POISON 4      /* 1: fill each receive slot / partial buffer with NaN once consumed */
-#define CP_ATTN_OPT_STEP_TIMING 5 /* 1: time every ring step's attention kernel with HIP events */
+#define CP_ATTN_OPT_STEP_TIMING 5 /* 1: time every ring step's attention kernel with HIP events (a
+                                     fused-ring call's one launch per rank under step 0) */
 #define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel (default 256; 0: one
                                      workgroup per 128 vectors of 16 bytes); a small grid shares the
                                      GPU with the attention kernel it overlaps.  A receive that
@@ -142,12 +143,16 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      differs).  Served for bf16 head_dim 128, the zigzag causal
                                      layout without padding with chunks of whole 64-key tiles, the
                                      fused merge and the copy-kernel receive (CP_ATTN_OPT_RECV 0),
-                                     without documents and the serial, step-timing, counter and
-                                     poison modes, while K/V span at most 4 GiB; otherwise, while a
+                                     without documents and the serial, counter and poison modes,
+                                     while K/V span at most 4 GiB; otherwise, while a
                                      graph is recorded and in the no-allocation forward, mode 0.
                                      2: as 1, but every wait looks for an epoch no signal stores and
                                      gives up after 16 polls: a test of the time-out path (results
-                                     not valid). */
+                                     not valid).  3 (staged): as 1, but the caller's stream waits
+                                     (HIP event) for every receive before the launch, so no wait is
+                                     polled and nothing overlaps: for tools that run one kernel at a
+                                     time (counter collection), under which mode 1's waits can only
+                                     run out.  Results bit-identical to mode 1. */
 
 /*
  * Create a plan (host only: no device memory, no HIP call).
@@ -430,7 +435,9 @@ int cp_attn_last_tile_counts(cp_attn_plan_t plan, int64_t* counts, int n, int32_
 
 /* Per (rank, step) attention-kernel milliseconds of the last forward call
  * made with CP_ATTN_OPT_STEP_TIMING = 1, row-major [cp][cp]; entries of ranks
- * the call did not run are -1.  Blocks until those events complete.
+ * the call did not run are -1, and a rank run as one fused launch
+ * (CP_ATTN_OPT_FUSED_RING) has it under step 0 and -1 for its other steps.
+ * Blocks until those events complete.
  * n must be >= cp_size * cp_size. */
 int cp_attn_last_step_times(cp_attn_plan_t plan, float* ms, int n);
 

@@ -93,9 +93,13 @@ class Plan:
 
     def set_fused_ring(self, mode):
         """Every ring step of a rank in one launch where served: True / 1 (the
-        default), False / 0 (one launch per step) or "timeout_test" (2: every
-        receive wait gives up at once; results not valid)."""
-        value = 2 if mode == "timeout_test" else int(bool(mode))
+        default), False / 0 (one launch per step), "timeout_test" (2: every
+        receive wait gives up at once; results not valid) or "staged" (3: the
+        launch waits for every receive first; for tools that run one kernel
+        at a time)."""
+        value = {"timeout_test": 2, "staged": 3}.get(mode) if isinstance(mode, str) else int(bool(mode))
+        if value is None:
+            raise ValueError(f"fused ring mode must be a bool, 'timeout_test' or 'staged', not {mode!r}")
         self.set_option(N.OPT_FUSED_RING, value)
 
     def fused_ring_active(self):

@@ -514,14 +514,14 @@ int launch_rank_finalize(Plan& p, const char* ws, void* out, float* lse, int r, 
 // epoch to the step's flag; a workgroup waits for that flag before loading
 // any key of the step.  Served for bf16 head_dim 128, the zigzag causal
 // layout without padding, chunks of whole 64-key tiles, the fused merge and
-// the copy-kernel receive, outside graph capture and the serial, timing,
-// counter and poison modes, without document masks, while the own K/V and
-// the slots each span at most 4 GiB.
+// the copy-kernel receive, outside graph capture and the serial, counter and
+// poison modes, without document masks, while the own K/V and the slots each
+// span at most 4 GiB.  Step timing reports the launch under step 0.
 
 constexpr int kRingPolls = 1 << 18;  // polls (each a coherent load and a short sleep, ~0.2-2 us) before a wait gives up
 
 bool fused_ring_served(const Plan& p, const RunCfg& c) {
-  if (!c.fused_ring || c.serial || c.recv != 0 || c.timing || c.counters || c.poison) return false;
+  if (!c.fused_ring || c.serial || c.recv != 0 || c.counters || c.poison) return false;
   if (p.dtype != CP_ATTN_BF16 || p.head_dim != 128 || p.layout != 1 || !p.causal || p.opt_merge != 0) return false;
   if (!p.doc_starts.empty() || p.cp < 2 || kv_beyond_32bit(p) || p.padded_len != p.seq_len) return false;
   if (int64_t(p.cp - 1) * ws_layout(p).kv_bytes > int64_t(UINT32_MAX)) return false;
@@ -651,6 +651,11 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
     CPA_HIP(launch_recv(ra, s == 1 ? 0 : c.recv_blocks, d.copy));
     CPA_HIP(launch_ring_signal(d.fr_flags + s, epoch, d.copy));
   }
+  if (c.fused_ring == 3) {
+    // staged: every receive done before the launch starts (no wait is polled)
+    CPA_HIP(hipEventRecord(d.recv_done[0], d.copy));
+    CPA_HIP(hipStreamWaitEvent(st, d.recv_done[0], 0));
+  }
   StepArgs a{};
   a.q = q;
   a.k = k;
@@ -681,8 +686,15 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   // test mode: an epoch no signal ever stores, and few polls
   a.ring_epoch = c.fused_ring == 2 ? epoch + 0x40000000u : epoch;
   a.ring_polls = c.fused_ring == 2 ? 16 : kRingPolls;
+  // step timing: the one launch is reported under step 0
+  const size_t ti = size_t(r) * P;
+  if (c.timing) CPA_HIP(hipEventRecord(d.t0[ti], st));
   const hipError_t e = launch_attn_bf16_ring(a, st);
   if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("fused ring launch: ") + hipGetErrorString(e));
+  if (c.timing) {
+    CPA_HIP(hipEventRecord(d.t1[ti], st));
+    d.timed[ti] = 1;
+  }
   d.fr_last = 1;
   return CP_ATTN_OK;
 }
@@ -1212,7 +1224,7 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
       p.opt_lockstep = value;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_FUSED_RING:
-      if (value < 0 || value > 2) return fail(CP_ATTN_EINVAL, "CP_ATTN_OPT_FUSED_RING must be 0, 1 or 2");
+      if (value < 0 || value > 3) return fail(CP_ATTN_EINVAL, "CP_ATTN_OPT_FUSED_RING must be 0, 1, 2 or 3");
       p.opt_fused_ring = value;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_COUNTERS:

@@ -163,14 +163,14 @@ def test_fused_ring_forced_timeout_is_reported():
 def test_fused_ring_falls_back_where_not_served():
     """Padding, the contiguous layout, bidirectional attention, documents,
     fp32, head_dim 64, the separate merge, the serial mode, the memcpy
-    receive, work counters, step timing, poison and graph mode take one
+    receive, work counters, poison and graph mode take one
     launch per step with the option set: the same bits as without it, and
     no wait is polled (the time-out test mode would report one)."""
     dev = _dev()
     setups = [
         dict(seq=1003), dict(layout="contiguous"), dict(causal=False), dict(docs=[0, 100, 700]),
         dict(dtype=torch.float32), dict(dim=64), dict(opt="merge"), dict(opt="serial"), dict(opt="memcpy"),
-        dict(opt="counters"), dict(opt="timing"), dict(opt="poison"), dict(opt="graph"),
+        dict(opt="counters"), dict(opt="poison"), dict(opt="graph"),
     ]
     for st in setups:
         seq, layout, causal = st.get("seq", 1024), st.get("layout", "zigzag"), st.get("causal", True)
@@ -190,8 +190,6 @@ def test_fused_ring_falls_back_where_not_served():
             p.set_recv("memcpy")
         if opt == "counters":
             p.set_counters(True)
-        if opt == "timing":
-            p.set_step_timing(True)
         if opt == "poison":
             p.set_poison(True)
         if opt == "graph":
@@ -231,3 +229,24 @@ def test_fused_ring_full_size(name):
     assert float((o[rt].float() - ref[0][rt].float()).abs().max()) <= 1.6e-2
     assert float((l[:, rt] - ref[1][:, rt]).abs().max()) <= 1e-4
     _check_oracle(o, l, q, k, v, rows, (0, w.heads - 1))
+
+
+def test_fused_ring_staged_equals_overlapped_bits():
+    """Mode 3 waits for every receive before the launch (no wait is polled,
+    nothing overlaps): the same kernel on the same data, so the same bits as
+    mode 1, call after call."""
+    seq, cp, heads = 4096, 8, 4
+    q, k, v = make_qkv(seq, heads, 128, "bf16", 95)
+    dev = _dev()
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    p = Plan(seq, cp, heads, 128, True, "zigzag")
+    _say("fused ring: staged vs overlapped")
+    ref = _full(p, qd, kd, vd)
+    assert p.fused_ring_active()
+    p.set_fused_ring("staged")
+    for _ in range(2):
+        o, l = _full(p, qd, kd, vd)
+        assert p.fused_ring_active()
+        assert _same(o, ref[0]) and _same(l, ref[1])
+    assert not p.ring_wait_timeouts()
+    p.close()

@@ -219,11 +219,20 @@ def test_step_timing_reports_run_steps():
     q, k, v = make_qkv(seq, heads, dim, "bf16", 15)
     p = Plan(seq, cp, heads, dim, True, "zigzag")
     p.set_step_timing(True)
+    p.set_fused_ring(False)
     _run(p, q, k, v, rank=2)
     t = p.last_step_times()
     for r in range(cp):
         for s in range(cp):
             assert (t[r][s] > 0) if r == 2 else (t[r][s] == -1)
+    # fused ring: the rank's one launch under step 0
+    p.set_fused_ring(True)
+    _run(p, q, k, v, rank=1)
+    assert p.fused_ring_active()
+    t = p.last_step_times()
+    for r in range(cp):
+        for s in range(cp):
+            assert (t[r][s] > 0) if (r, s) == (1, 0) else (t[r][s] == -1)
 
 
 def test_lse_merge_kernel_matches_oracle():

@@ -206,9 +206,9 @@ def test_call_error_codes_enqueue_nothing():
     assert lib.cp_attn_set_option(h, N.OPT_LOCKSTEP, 2) == N.EINVAL
     assert lib.cp_attn_set_option(h, N.OPT_LOCKSTEP, 1) == N.OK
     assert lib.cp_attn_set_option(h, N.OPT_LOCKSTEP, 0) == N.OK
-    assert lib.cp_attn_set_option(h, N.OPT_FUSED_RING, 3) == N.EINVAL
+    assert lib.cp_attn_set_option(h, N.OPT_FUSED_RING, 4) == N.EINVAL
     assert lib.cp_attn_set_option(h, N.OPT_FUSED_RING, -1) == N.EINVAL
-    for mode in (2, 1, 0):
+    for mode in (3, 2, 1, 0):
         assert lib.cp_attn_set_option(h, N.OPT_FUSED_RING, mode) == N.OK
     assert lib.cp_attn_ring_wait_timeouts(h, None) == N.EINVAL
     t = ctypes.c_int32(7)
