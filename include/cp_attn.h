@@ -144,8 +144,10 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      layout without padding with chunks of whole 64-key tiles, the
                                      fused merge and the copy-kernel receive (CP_ATTN_OPT_RECV 0),
                                      without documents and the serial, counter and poison modes,
-                                     while K/V span at most 4 GiB; otherwise, while a
-                                     graph is recorded and in the no-allocation forward, mode 0.
+                                     while K/V span at most 4 GiB (graph mode included: each call
+                                     advances its epoch on the device, so every replay waits for its
+                                     own receives); otherwise, and in the no-allocation forward,
+                                     mode 0.
                                      2: as 1, but every wait looks for an epoch no signal stores and
                                      gives up after 16 polls: a test of the time-out path (results
                                      not valid).  3 (staged): as 1, but the caller's stream waits

@@ -77,7 +77,6 @@ struct DeviceState {
   bool fr_built = false;
   uint32_t* fr_err = nullptr;
   uint32_t* fr_err_dev = nullptr;
-  uint32_t fr_epoch = 0;
   int fr_last = 0;  // the last forward call ran every rank it computed as one fused launch
 };
 
@@ -222,7 +221,8 @@ struct RunCfg {
   bool serial = false;     // every step on the caller's stream, no events
   int recv = 0;            // CP_ATTN_OPT_RECV in effect
   int recv_blocks = 256;   // CP_ATTN_OPT_RECV_BLOCKS in effect
-  int fused_ring = 0;      // CP_ATTN_OPT_FUSED_RING in effect (0 while capturing a graph)
+  int fused_ring = 0;      // CP_ATTN_OPT_FUSED_RING in effect
+  bool capturing = false;  // the calls are being recorded into a graph
   bool counters = false;   // device work counters (plan-owned buffer)
   bool timing = false;     // per-step timing events
   bool poison = false;     // NaN-fill consumed buffers
@@ -237,7 +237,8 @@ RunCfg plan_cfg(const Plan& p, bool capturing) {
   c.counters = p.opt_counters != 0;
   c.timing = p.opt_step_timing != 0 && !capturing;
   c.poison = p.opt_poison != 0;
-  c.fused_ring = capturing ? 0 : p.opt_fused_ring;
+  c.fused_ring = p.opt_fused_ring;
+  c.capturing = capturing;
   return c;
 }
 
@@ -514,9 +515,12 @@ int launch_rank_finalize(Plan& p, const char* ws, void* out, float* lse, int r, 
 // epoch to the step's flag; a workgroup waits for that flag before loading
 // any key of the step.  Served for bf16 head_dim 128, the zigzag causal
 // layout without padding, chunks of whole 64-key tiles, the fused merge and
-// the copy-kernel receive, outside graph capture and the serial, counter and
-// poison modes, without document masks, while the own K/V and the slots each
-// span at most 4 GiB.  Step timing reports the launch under step 0.
+// the copy-kernel receive, outside the serial, counter and poison modes,
+// without document masks, while the own K/V and the slots each span at most
+// 4 GiB.  Step timing reports the launch under step 0.  The call's epoch
+// lives in device memory (flag word 0), advanced by a kernel at the start of
+// the call, so that a recorded graph's replays each wait for their own
+// receives.
 
 constexpr int kRingPolls = 1 << 18;  // polls (each a coherent load and a short sleep, ~0.2-2 us) before a wait gives up
 
@@ -636,8 +640,7 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   DeviceState& d = *p.dev;
   const WsLayout w = ws_layout(p);
   const int P = p.cp;
-  if (++d.fr_epoch == 0) d.fr_epoch = 1;  // a zeroed flag never reads as done
-  const uint32_t epoch = d.fr_epoch;
+  CPA_HIP(launch_ring_epoch(d.fr_flags, st));  // this call's epoch, in flag word 0
   const int64_t kvs = w.kv_bytes;  // one slot of K (or V): the source's n_loc rows
   char* const k2 = d.fr_slots;
   char* const v2 = d.fr_slots + align256(int64_t(P - 1) * kvs);
@@ -649,7 +652,7 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
     const RecvArgs ra = recv_ranges_to(p, k2 + int64_t(s - 1) * kvs, v2 + int64_t(s - 1) * kvs, k, v, p.step(r, s).src);
     // the first receive is needed soonest: the full grid; then the narrow one
     CPA_HIP(launch_recv(ra, s == 1 ? 0 : c.recv_blocks, d.copy));
-    CPA_HIP(launch_ring_signal(d.fr_flags + s, epoch, d.copy));
+    CPA_HIP(launch_ring_signal(d.fr_flags + s, d.fr_flags, d.copy));
   }
   if (c.fused_ring == 3) {
     // staged: every receive done before the launch starts (no wait is polled)
@@ -684,7 +687,7 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   a.ring_flags = d.fr_flags;
   a.ring_err = d.fr_err_dev;
   // test mode: an epoch no signal ever stores, and few polls
-  a.ring_epoch = c.fused_ring == 2 ? epoch + 0x40000000u : epoch;
+  a.ring_epoch_add = c.fused_ring == 2 ? 0x40000000u : 0u;
   a.ring_polls = c.fused_ring == 2 ? 16 : kRingPolls;
   // step timing: the one launch is reported under step 0
   const size_t ti = size_t(r) * P;
@@ -694,6 +697,12 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   if (c.timing) {
     CPA_HIP(hipEventRecord(d.t1[ti], st));
     d.timed[ti] = 1;
+  }
+  if (c.capturing) {
+    // a capture must join every stream it forked (the launch itself only
+    // waits on the flags)
+    CPA_HIP(hipEventRecord(d.recv_done[1], d.copy));
+    CPA_HIP(hipStreamWaitEvent(st, d.recv_done[1], 0));
   }
   d.fr_last = 1;
   return CP_ATTN_OK;
@@ -973,9 +982,12 @@ int run_graph(Plan& p, const void* q, const void* k, const void* v, void* out, f
   const std::vector<intptr_t> key = {
       intptr_t(q), intptr_t(k), intptr_t(v), intptr_t(out), intptr_t(lse), rank,
       intptr_t(d.ws), intptr_t(d.copy), intptr_t(d.merge), p.dtype, p.opt_merge, p.opt_serialize,
-      p.opt_recv, p.opt_poison, p.opt_recv_blocks, p.opt_ksplit, p.opt_counters, intptr_t(p.doc_version)};
+      p.opt_recv, p.opt_poison, p.opt_recv_blocks, p.opt_ksplit, p.opt_counters, intptr_t(p.doc_version),
+      p.opt_fused_ring};
   if (!d.graph || key != d.graph_key) {
     drop_graph(d);
+    // the fused ring's buffers and table are made outside the capture
+    if (fused_ring_served(p, plan_cfg(p, true))) CPA_TRY(ensure_fused_ring(p));
     if (!d.capture) CPA_HIP(hipStreamCreateWithFlags(&d.capture, hipStreamNonBlocking));
     CPA_HIP(hipStreamBeginCapture(d.capture, hipStreamCaptureModeThreadLocal));
     int rc = CP_ATTN_OK;

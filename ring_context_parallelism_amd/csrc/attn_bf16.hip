@@ -417,14 +417,14 @@ constexpr int kThreads8 = 512;
 constexpr int kBM8 = 256;
 
 // Fused-ring receive wait: poll flag `step` of the call until it reaches the
-// call's epoch (wrap-aware), sleeping between polls; after ring_polls polls
+// call's epoch `ep` (wrap-aware), sleeping between polls; after ring_polls polls
 // the wave's first lane records the time-out in the host-visible word and
 // the wave goes on.  The relaxed agent-scope load reads the flag through to
 // device coherence (sc1), never from an older copy in this XCD's L2.  Every
 // lane of the calling wave takes the same path.
-__device__ __forceinline__ void ring_wait(const StepArgs& a, int step) {
+__device__ __forceinline__ void ring_wait(const StepArgs& a, int step, uint32_t ep) {
   const uint32_t* const f = a.ring_flags + step;
-  for (int n = 0; int32_t(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - a.ring_epoch) < 0; ++n) {
+  for (int n = 0; int32_t(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - ep) < 0; ++n) {
     if (n >= a.ring_polls) {
       if ((threadIdx.x & 63) == 0) __hip_atomic_store(a.ring_err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       break;
@@ -575,6 +575,7 @@ void attn_step_bf16_d128x8(StepArgs a0, const StepArgs* __restrict__ tbl, const 
   // constant address space its wave-uniform reads are scalar loads
   typedef const __attribute__((address_space(4))) RingRun c_run;
   c_run* const runs = (c_run*)(a.runs);
+  uint32_t gt_epoch = 0;  // (wave 4) the call's epoch, read before the first wait
   int gt_run = -1, gt_end = 0, gt_step = 0;
   auto gate = [&](int j0) {  // wave 4: the receives of the runs up to the one holding key j0 have landed
     while (j0 >= gt_end) {
@@ -583,7 +584,13 @@ void attn_step_bf16_d128x8(StepArgs a0, const StepArgs* __restrict__ tbl, const 
       gt_end = __builtin_amdgcn_readfirstlane(rr.end);  // (wave-uniform: keep run fields scalar)
       const int st = __builtin_amdgcn_readfirstlane(rr.step);
       if (st > gt_step) {
-        ring_wait(a, st);
+        if (gt_step == 0) {
+          // written by the kernel before this launch on its stream: the
+          // constant address space reads it with a scalar load
+          typedef const __attribute__((address_space(4))) uint32_t c_u32;
+          gt_epoch = *(c_u32*)(a.ring_flags) + a.ring_epoch_add;
+        }
+        ring_wait(a, st, gt_epoch);
         gt_step = st;
       }
     }

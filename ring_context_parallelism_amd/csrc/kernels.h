@@ -100,7 +100,9 @@ struct StepArgs {
   int32_t kpos_split;
   // fused ring (null runs: not fused): the receive slots of steps 1 .. P-1,
   // K and V each one buffer of rows (kv2_bytes addressable from each), the
-  // segments' key runs, and the per-step receive flags; a workgroup polls
+  // segments' key runs, and the per-step receive flags; ring_flags[0] holds
+  // the call's epoch (advanced by a kernel before the launch), flag s is
+  // done once it reaches that epoch plus ring_epoch_add; a workgroup polls
   // flag s (at most ring_polls times) before it loads any row of a run of
   // step s, and a wait that runs out stores 1 to *ring_err (host-visible)
   const void* k2;
@@ -109,7 +111,7 @@ struct StepArgs {
   const RingRun* runs;
   const uint32_t* ring_flags;
   uint32_t* ring_err;
-  uint32_t ring_epoch;
+  uint32_t ring_epoch_add;
   int32_t ring_polls;
 };
 
@@ -168,9 +170,11 @@ hipError_t launch_attn_bf16(const StepArgs& a, int head_dim, hipStream_t stream)
 // fused ring: one launch of the bf16 head_dim 128 kernel over every ring step
 // of a rank (StepArgs::runs set)
 hipError_t launch_attn_bf16_ring(const StepArgs& a, hipStream_t stream);
-// store epoch to *flag (release, agent scope) from one thread, once every
+// store *epoch to *flag (release, agent scope) from one thread, once every
 // kernel before it on the stream has completed
-hipError_t launch_ring_signal(uint32_t* flag, uint32_t epoch, hipStream_t stream);
+hipError_t launch_ring_signal(uint32_t* flag, const uint32_t* epoch, hipStream_t stream);
+// advance the epoch word by one (never to zero), one thread
+hipError_t launch_ring_epoch(uint32_t* epoch, hipStream_t stream);
 // Every rank's step of one ring step in one launch (bf16, head_dim 128, no
 // in-kernel receive): tbl[r] (device memory) are rank r's arguments, its
 // workgroups wgb[r] .. wgb[r + 1] - 1 (wgb[nranks] = total_wgs; each range

@@ -125,9 +125,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_num_vgpr(16))) void recv_
 
 // Fused-ring receive flag: launched behind the copy kernel on its stream, so
 // it runs once that kernel has completed (and its writes are visible at agent
-// scope); the release store then publishes the epoch.
-__global__ __launch_bounds__(64) void ring_signal(uint32_t* flag, uint32_t epoch) {
-  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+// scope); the release store then publishes the call's epoch, which a kernel
+// on the caller's stream advanced before the copy stream started (so a
+// replayed graph publishes a new one each time).
+__global__ __launch_bounds__(64) void ring_signal(uint32_t* flag, const uint32_t* epoch) {
+  if (threadIdx.x == 0) __hip_atomic_store(flag, *epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(64) void ring_epoch(uint32_t* epoch) {
+  if (threadIdx.x == 0) {
+    const uint32_t e = *epoch + 1u;
+    *epoch = e ? e : 1u;  // a zeroed flag never reads as done
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void poison_fill(uint4* p, int64_t n) {
@@ -242,8 +251,13 @@ hipError_t launch_recv(const RecvArgs& a, int blocks, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_ring_signal(uint32_t* flag, uint32_t epoch, hipStream_t stream) {
+hipError_t launch_ring_signal(uint32_t* flag, const uint32_t* epoch, hipStream_t stream) {
   ring_signal<<<1, 64, 0, stream>>>(flag, epoch);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_epoch(uint32_t* epoch, hipStream_t stream) {
+  ring_epoch<<<1, 64, 0, stream>>>(epoch);
   return hipGetLastError();
 }
 

@@ -163,14 +163,14 @@ def test_fused_ring_forced_timeout_is_reported():
 def test_fused_ring_falls_back_where_not_served():
     """Padding, the contiguous layout, bidirectional attention, documents,
     fp32, head_dim 64, the separate merge, the serial mode, the memcpy
-    receive, work counters, poison and graph mode take one
+    receive, work counters and poison take one
     launch per step with the option set: the same bits as without it, and
     no wait is polled (the time-out test mode would report one)."""
     dev = _dev()
     setups = [
         dict(seq=1003), dict(layout="contiguous"), dict(causal=False), dict(docs=[0, 100, 700]),
         dict(dtype=torch.float32), dict(dim=64), dict(opt="merge"), dict(opt="serial"), dict(opt="memcpy"),
-        dict(opt="counters"), dict(opt="poison"), dict(opt="graph"),
+        dict(opt="counters"), dict(opt="poison"),
     ]
     for st in setups:
         seq, layout, causal = st.get("seq", 1024), st.get("layout", "zigzag"), st.get("causal", True)
@@ -192,8 +192,6 @@ def test_fused_ring_falls_back_where_not_served():
             p.set_counters(True)
         if opt == "poison":
             p.set_poison(True)
-        if opt == "graph":
-            p.set_graph(True)
         p.set_fused_ring(False)
         ref = _rank(p, qd, kd, vd, 1)
         p.set_fused_ring("timeout_test")
@@ -248,5 +246,44 @@ def test_fused_ring_staged_equals_overlapped_bits():
         o, l = _full(p, qd, kd, vd)
         assert p.fused_ring_active()
         assert _same(o, ref[0]) and _same(l, ref[1])
+    assert not p.ring_wait_timeouts()
+    p.close()
+
+
+def test_fused_ring_graph_replays_match_eager():
+    """Graph mode records the fused launch with its receives, their signals
+    and the kernel that advances the call's epoch in device memory: every
+    replay waits for its own receives, so each equals the eager call bit for
+    bit (eager work and host synchronisation between replays), also after
+    the inputs change in place, for one rank's share and the full forward."""
+    seq, cp, heads = 4096, 4, 8
+    q, k, v = make_qkv(seq, heads, 128, "bf16", 96)
+    dev = _dev()
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    p = Plan(seq, cp, heads, 128, True, "zigzag")
+    for rank in (1, None):
+        _say(f"fused ring graph replays: rank {rank}")
+        call = (lambda: _rank(p, qd, kd, vd, rank)) if rank is not None else (lambda: _full(p, qd, kd, vd))
+        p.set_graph(False)
+        ref = call()
+        assert p.fused_ring_active()
+        p.set_graph(True)
+        for i in range(4):
+            junk = torch.randn(1 << 20, device=dev).sum()  # eager work between replays
+            torch.cuda.synchronize()
+            o, l = call()
+            assert torch.isfinite(junk)
+            assert _same(o, ref[0]) and _same(l, ref[1]), (rank, i)
+        assert p.fused_ring_active()
+        # new contents in the same buffers: the replays receive them
+        kd.mul_(0.75)
+        vd.add_(0.5)
+        p.set_graph(False)
+        ref2 = call()
+        assert not _same(ref2[0], ref[0])
+        p.set_graph(True)
+        for i in range(2):
+            o, l = call()
+            assert _same(o, ref2[0]) and _same(l, ref2[1]), (rank, "changed", i)
     assert not p.ring_wait_timeouts()
     p.close()
