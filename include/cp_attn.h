@@ -101,7 +101,16 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      each full segment's keys in two halves, one workgroup each;
                                      the part that finishes second merges the other's result
                                      (exact LSE merge; no workgroup waits for another).
-                                     0: never split. Not used with the separate merge mode. */
+                                     0: never split. Not used with the separate merge mode.
+                                     In the fused ring (CP_ATTN_OPT_FUSED_RING) the split is
+                                     decided per rank when the plan's run table is built: where
+                                     an estimate of the launch (workgroups in dispatch order, one
+                                     per compute unit, slower per unit as more are busy) comes
+                                     out at least 5 % shorter, a segment's row tiles take two
+                                     workgroups, one the first half of every step's keys, the
+                                     other the second halves and the causal diagonal (chunks of a
+                                     multiple of 256 rows whose key runs split into whole 64-key
+                                     tiles only). */
 #define CP_ATTN_OPT_COUNTERS 9    /* 1: the step kernels count the key tiles they compute per (rank,
                                      step) on the device (cp_attn_last_tile_counts) */
 #define CP_ATTN_OPT_BWD_KEYS 10   /* backward dK/dV kernel (bf16, head_dim 128): 0 (default): eight
@@ -217,8 +226,9 @@ int cp_attn_ring_wait_timeouts(cp_attn_plan_t plan, int32_t* timed_out);
 
 /* Whether the plan's last forward call (rank or full) ran each rank it
  * computed as one fused launch (CP_ATTN_OPT_FUSED_RING served): *active = 1,
- * else 0 (one launch per ring step, or no call yet).  Host only; EINVAL for a
- * null active. */
+ * or 2 if the last rank it computed split its row tiles' keys in that launch
+ * (CP_ATTN_OPT_KSPLIT); 0: one launch per ring step, or no call yet.  Host
+ * only; EINVAL for a null active. */
 int cp_attn_fused_ring_active(cp_attn_plan_t plan, int32_t* active);
 
 /* Hand the plan caller-owned device memory of at least cp_attn_workspace_bytes

@@ -103,10 +103,12 @@ class Plan:
         self.set_option(N.OPT_FUSED_RING, value)
 
     def fused_ring_active(self):
-        """True if the last forward call ran each rank as one fused launch."""
+        """1 if the last forward call ran each rank as one fused launch, 2 if
+        the last rank it computed also split its row tiles' keys in that
+        launch, 0 otherwise."""
         t = ctypes.c_int32()
         N.check(self.lib.cp_attn_fused_ring_active(self._h, ctypes.byref(t)), "cp_attn_fused_ring_active")
-        return bool(t.value)
+        return int(t.value)
 
     def ring_wait_timeouts(self):
         """True if a fused-ring receive wait ran out since the last query

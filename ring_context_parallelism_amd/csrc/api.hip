@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -73,6 +74,10 @@ struct DeviceState {
   uint32_t* fr_flags = nullptr;
   RingRun* fr_runs = nullptr;
   std::vector<SegArgs> fr_segs;  // [rank * 2 + i]: late rows, then early rows (run0 set)
+  // key split of the fused launch: [rank * 4 + i], seg[0..3] of the launch
+  // (part 0 of late and early rows, then their part 1), used where fr_split[rank]
+  std::vector<SegArgs> fr_split_segs;
+  std::vector<uint8_t> fr_split;
   bool fr_ok = false;            // the plan's runs are whole tiles (built once)
   bool fr_built = false;
   uint32_t* fr_err = nullptr;
@@ -581,6 +586,71 @@ bool ring_runs(const Plan& p, int r, int64_t R0, std::vector<RingRun>& runs, Seg
   return !runs.empty();
 }
 
+// Key split of a segment's run list: part 0 takes the first half of every
+// full run, part 1 the second halves and then the diagonal run (the last run
+// when sa.diag), each in a key space of its own from 0.  The halves keep the
+// step order, so each part waits for the receives in the order they land.
+// Returns false if a full run's half is not a whole number of 64-key tiles.
+bool split_ring_runs(const std::vector<RingRun>& runs, const SegArgs& sa, std::vector<RingRun> part[2]) {
+  int64_t beg = 0, key[2] = {0, 0};
+  const size_t nfull = runs.size() - (sa.diag ? 1 : 0);
+  for (size_t i = 0; i < runs.size(); ++i) {
+    const RingRun& u = runs[i];
+    const int64_t n = u.end - beg;
+    if (i < nfull) {
+      if (n % 128) return false;
+      for (int pp = 0; pp < 2; ++pp) {
+        const int64_t first = beg + pp * (n / 2);  // the half's first key in the segment's key space
+        part[pp].push_back(RingRun{int32_t(key[pp] + n / 2), int32_t(first + u.delta - key[pp]), u.buf, u.step});
+        key[pp] += n / 2;
+      }
+    } else {
+      part[1].push_back(RingRun{int32_t(key[1] + n), int32_t(beg + u.delta - key[1]), u.buf, u.step});
+    }
+    beg = u.end;
+  }
+  return !part[0].empty();
+}
+
+// Estimated length, in 64-key tiles, of a fused launch whose segments have
+// row tiles of the given key-tile counts (full and diagonal keys apart).
+// Workgroups start in dispatch order (segment by segment, longest row tiles
+// first, a split tile's parts side by side, every head of a tile together),
+// one per compute unit.  The chip's clock is bound by its power: measured,
+// every compute unit busy gives only about 1.4 times the throughput of half
+// of them, so a workgroup runs at full speed while at most half the compute
+// units are busy and at (half / busy)^0.5 of it beyond.  A workgroup adds a
+// fixed cost of 16 tiles (prologue, first receive, epilogue), a split part 2
+// more for the fold.  (Fitted to the rank calls of the 8192-token cp 4
+// 32-head and the 16384-token cp 4 16-head workloads, within 4 %.)
+double ring_launch_tiles(const std::vector<std::array<int64_t, 2>> tiles[2], const int split[2], int heads, int cus) {
+  constexpr double kWg = 16.0, kFold = 2.0;
+  std::vector<double> queue;
+  for (int i = 0; i < 2; ++i)
+    for (const auto& rt : tiles[i])
+      for (int pp = 0; pp < split[i]; ++pp) {
+        const double c = split[i] == 1 ? kWg + double(rt[0] + rt[1])
+                                        : kWg + kFold + double(rt[0] / 2 + (pp ? rt[1] : 0));
+        for (int h = 0; h < heads; ++h) queue.push_back(c);
+      }
+  std::vector<double> busy;  // work left of the running workgroups
+  size_t next = 0;
+  double t = 0.0;
+  const double half = std::max(1, cus / 2);
+  while (next < queue.size() || !busy.empty()) {
+    while (next < queue.size() && int(busy.size()) < cus) busy.push_back(queue[next++]);
+    const double n = double(busy.size());
+    const double rate = n <= half ? 1.0 : std::sqrt(half / n);
+    const double m = *std::min_element(busy.begin(), busy.end());
+    t += m / rate;
+    size_t k = 0;
+    for (double b : busy)
+      if (b - m > 1e-9) busy[k++] = b - m;
+    busy.resize(k);
+  }
+  return t;
+}
+
 // The run table of every rank, uploaded once per plan (set-up, synchronous).
 int ensure_fused_ring(Plan& p) {
   DeviceState& d = *p.dev;
@@ -589,16 +659,67 @@ int ensure_fused_ring(Plan& p) {
     d.fr_ok = false;
     std::vector<RingRun> all;
     d.fr_segs.assign(size_t(p.cp) * 2, SegArgs{});
+    d.fr_split_segs.assign(size_t(p.cp) * 4, SegArgs{});
+    d.fr_split.assign(size_t(p.cp), 0);
     bool ok = true;
+    const int bm = attn_bf16_block_m(128);
     for (int r = 0; r < p.cp && ok; ++r) {
       const int64_t R0[2] = {p.chunk, 0};  // late rows first: they see more keys
+      std::vector<RingRun> runs[2];
       for (int i = 0; i < 2 && ok; ++i) {
-        std::vector<RingRun> runs;
-        SegArgs sa;
-        ok = ring_runs(p, r, R0[i], runs, sa);
+        SegArgs& sa = d.fr_segs[size_t(r) * 2 + i];
+        ok = ring_runs(p, r, R0[i], runs[i], sa);
         sa.run0 = int32_t(all.size());
-        all.insert(all.end(), runs.begin(), runs.end());
-        d.fr_segs[size_t(r) * 2 + i] = sa;
+        all.insert(all.end(), runs[i].begin(), runs[i].end());
+      }
+      if (!ok) break;
+      // key split: where the launch would leave compute units idle (few
+      // heads, or one segment's rows seeing most of the keys), a segment's
+      // row tiles may take two workgroups each.  The split's fold keeps a
+      // part in a 128 KiB slot per (256-row tile, head) of the workspace.
+      if (bm != 256 || p.chunk % 256 || p.n_loc % 256) continue;
+      // (a segment whose rows see only the diagonal, rank 0's early rows,
+      // has nothing to split)
+      std::vector<RingRun> halves[2][2];
+      bool can[2];
+      std::vector<std::array<int64_t, 2>> rt[2];
+      for (int i = 0; i < 2; ++i) {
+        const SegArgs& sa = d.fr_segs[size_t(r) * 2 + i];
+        can[i] = split_ring_runs(runs[i], sa, halves[i]);
+        for (int64_t t = sa.tiles - 1; t >= 0; --t)  // longest first
+          rt[i].push_back({sa.kv_full / 64, sa.diag ? (t + 1) * bm / 64 : 0});
+      }
+      int best[2] = {1, 1};
+      const int none[2] = {1, 1};
+      const double base = ring_launch_tiles(rt, none, p.heads, d.cus);
+      double best_len = base;
+      for (int o = 1; o < 4; ++o) {
+        const int sp[2] = {1 + (o & 1), 1 + (o >> 1)};
+        if ((sp[0] > 1 && !can[0]) || (sp[1] > 1 && !can[1])) continue;
+        const double len = ring_launch_tiles(rt, sp, p.heads, d.cus);
+        if (len < best_len) {
+          best_len = len;
+          best[0] = sp[0];
+          best[1] = sp[1];
+        }
+      }
+      if (best_len > 0.95 * base) continue;  // within the estimate's error
+      d.fr_split[r] = 1;
+      for (int i = 0; i < 2; ++i) {
+        const SegArgs& sa = d.fr_segs[size_t(r) * 2 + i];
+        SegArgs& s0 = d.fr_split_segs[size_t(r) * 4 + i];
+        SegArgs& s1 = d.fr_split_segs[size_t(r) * 4 + 2 + i];
+        s0 = sa;
+        s1 = sa;
+        if (best[i] == 1) continue;
+        s0.ksplit = s1.ksplit = 2;
+        s0.tiles = s1.tiles = sa.tiles * 2;
+        s0.diag = 0;
+        s0.kv_full = s1.kv_full = int32_t(halves[i][0].back().end);
+        s0.run0 = int32_t(all.size());
+        all.insert(all.end(), halves[i][0].begin(), halves[i][0].end());
+        s1.run0 = int32_t(all.size());
+        all.insert(all.end(), halves[i][1].begin(), halves[i][1].end());
       }
     }
     if (!ok) return CP_ATTN_OK;  // served no more: the per-step launches take over
@@ -679,9 +800,21 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.out_f32 = 0;
   a.nseg = 2;
+  const bool split = p.opt_ksplit && d.fr_split[size_t(r)];
   for (int i = 0; i < 2; ++i) {
-    a.seg[i] = d.fr_segs[size_t(r) * 2 + i];
+    a.seg[i] = split ? d.fr_split_segs[size_t(r) * 4 + i] : d.fr_segs[size_t(r) * 2 + i];
+    if (split) a.seg[2 + i] = d.fr_split_segs[size_t(r) * 4 + 2 + i];
     a.total_tiles += a.seg[i].tiles;
+  }
+  if (split) {
+    for (int b = 0; b < 2; ++b) {
+      a.split_o[b] = reinterpret_cast<float*>(c.ws + w.part_o[b]);
+      a.split_lse[b] = reinterpret_cast<float*>(c.ws + w.part_lse[b]);
+    }
+    a.split_cnt = reinterpret_cast<int32_t*>(c.ws + w.split_cnt);
+    // (the kernel leaves its counters at zero; a caller may have written the
+    // workspace since: cleared by a kernel, which a graph may hold)
+    CPA_HIP(launch_fill_words(c.ws + w.split_cnt, split_counters(p), 0u, st));
   }
   a.runs = d.fr_runs;
   a.ring_flags = d.fr_flags;
@@ -704,7 +837,7 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
     CPA_HIP(hipEventRecord(d.recv_done[1], d.copy));
     CPA_HIP(hipStreamWaitEvent(st, d.recv_done[1], 0));
   }
-  d.fr_last = 1;
+  d.fr_last = split ? 2 : 1;
   return CP_ATTN_OK;
 }
 

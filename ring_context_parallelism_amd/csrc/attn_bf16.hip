@@ -496,14 +496,16 @@ void attn_step_bf16_d128x8(StepArgs a0, const StepArgs* __restrict__ tbl, const 
   tile_of(bid, nblk, a.heads, a.total_tiles, h, t);
   const int si = t < a.seg[0].tiles ? 0 : 1;
   if (si) t -= a.seg[0].tiles;
-  const SegArgs& g = a.seg[si];
-  const int epi = __builtin_amdgcn_readfirstlane(g.epi);  // scalar: the epilogue branches on it
+  const SegArgs& g0 = a.seg[si];
   // key split: a full segment on a grid smaller than the GPU is cut into
-  // g.ksplit = 2 key ranges per row tile, one workgroup each (adjacent ids)
-  const int ks = g.ksplit;
+  // ksplit = 2 key ranges per row tile, one workgroup each (adjacent ids);
+  // in the fused ring each part has its own run list, part 1's in seg[si + 2]
+  const int ks = g0.ksplit;
   const int part = t % ks;
   t /= ks;
-  if (g.diag) t = g.tiles / ks - 1 - t;  // longest rows first
+  if (g0.diag || (kRing && ks > 1)) t = g0.tiles / ks - 1 - t;  // longest rows first
+  const SegArgs& g = (kRing && part) ? a.seg[si + 2] : g0;
+  const int epi = __builtin_amdgcn_readfirstlane(g.epi);  // scalar: the epilogue branches on it
   const int row0 = t * kBM8;
 
   const int tid = threadIdx.x;
@@ -772,8 +774,13 @@ void attn_step_bf16_d128x8(StepArgs a0, const StepArgs* __restrict__ tbl, const 
   // (document masks: from the tile of the workgroup's first key, never split)
   const int ntiles_all = (kv_end + kBN - 1) / kBN;
   const int half_tiles = (ntiles_all + 1) >> 1;
-  const int jt0 = kDoc ? wg_lo / kBN : part ? half_tiles : 0;
-  const int ntiles = kDoc ? max(0, ntiles_all - jt0) : ks == 1 ? ntiles_all : (part ? ntiles_all - half_tiles : half_tiles);
+  // (fused ring: each part has its own run list and key space, from key 0;
+  // the zero stays opaque to the compiler, which otherwise keeps more load
+  // addresses live and goes past the register budget)
+  int jt0 = kDoc ? wg_lo / kBN : (part && !kRing) ? half_tiles : 0;
+  if constexpr (kRing) asm volatile("" : "+s"(jt0));
+  const int ntiles = kDoc ? max(0, ntiles_all - jt0)
+                          : (ks == 1 || kRing) ? ntiles_all : (part ? ntiles_all - half_tiles : half_tiles);
   const int kb0 = jt0 * kBN;
   // chunks of the share: ntiles, at most 256 vectors (one per lane of group
   // A) each; what does not fit is copied after the loop

@@ -76,8 +76,11 @@ struct StepArgs {
   float scale;       // softmax scale 1/sqrt(D)
   int32_t out_f32;   // 1: out is fp32, 0: bf16
   int32_t nseg;
-  int32_t total_tiles;  // sum of seg[i].tiles
-  SegArgs seg[2];
+  int32_t total_tiles;  // sum of seg[i].tiles, i < nseg
+  // seg[2], seg[3]: fused ring only, part 1 of a key-split seg[0], seg[1]
+  // (the same rows; its own run list and kv_full, the diagonal if any);
+  // seg[0], seg[1] then describe part 0 (the first half of every full run)
+  SegArgs seg[4];
   RecvArgs recv;        // next step's receive done by this kernel (recv.n == 0: none)
   // key split (segments with ksplit 2): part p of the 256-row tile r (of the
   // local rows) and head h leaves its normalised output in the 128 KiB slot

@@ -229,6 +229,69 @@ def test_fused_ring_full_size(name):
     _check_oracle(o, l, q, k, v, rows, (0, w.heads - 1))
 
 
+SPLIT_CASES = [
+    (6144, 4, 5),     # three row tiles per chunk, heads not a multiple of 8
+    (2048, 4, 4),     # one row tile per chunk; the last rank splits both row ranges
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"s{c[0]}_cp{c[1]}_h{c[2]}" for c in SPLIT_CASES])
+def test_fused_ring_key_split_every_row(case):
+    """With few workgroups the fused launch splits a row tile's keys in two
+    parts (the first half of every step's keys, then the second halves and
+    the diagonal), merged by the part that ends last: every row of every
+    head of every rank against the oracle, within rounding of the unsplit
+    fused launch, and the same bits call after call."""
+    seq, cp, heads = case
+    _say(f"fused ring key split: {case}")
+    q, k, v = make_qkv(seq, heads, 128, "bf16", 97)
+    dev = _dev()
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    p = Plan(seq, cp, heads, 128, True, "zigzag")
+    for r in range(cp):
+        p.set_key_split(False)
+        ref = _rank(p, qd, kd, vd, r)
+        assert p.fused_ring_active() == 1, r
+        p.set_key_split(True)
+        o, l = _rank(p, qd, kd, vd, r)
+        assert p.fused_ring_active() == 2, r
+        rows = _rows_of(p, r)
+        rt = torch.as_tensor(rows)
+        assert float((o[rt].float() - ref[0][rt].float()).abs().max()) <= 1.6e-2, r
+        assert float((l[:, rt] - ref[1][:, rt]).abs().max()) <= 1e-4, r
+        _check_oracle(o, l, q, k, v, rows, range(heads))
+        o2, l2 = _rank(p, qd, kd, vd, r)
+        assert _same(o2, o) and _same(l2, l), r
+    assert not p.ring_wait_timeouts()
+    p.close()
+
+
+@pytest.mark.parametrize("rank", [0, 1, 3])
+def test_fused_ring_key_split_full_size_16_heads(rank):
+    """The 16384-token cp 4 workload with 16 heads: ranks 0 and 1 split
+    (their launches alone would leave compute units idle), rank 3 does not;
+    rows of the first and last head against the oracle, every row of every
+    head within rounding of one launch per step."""
+    w = WORKLOADS["causal_s16384_cp4_zigzag_h16_d128_bf16"]
+    _say(f"fused ring key split, full size: {w.name} rank {rank}")
+    q, k, v = workload_qkv(w)
+    dev = _dev()
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout)
+    p.set_fused_ring(False)
+    ref = _rank(p, qd, kd, vd, rank)
+    p.set_fused_ring(True)
+    o, l = _rank(p, qd, kd, vd, rank)
+    assert p.fused_ring_active() == (1 if rank == 3 else 2)
+    assert not p.ring_wait_timeouts()
+    p.close()
+    rows = _rows_of(p, rank)
+    rt = torch.as_tensor(rows)
+    assert float((o[rt].float() - ref[0][rt].float()).abs().max()) <= 1.6e-2
+    assert float((l[:, rt] - ref[1][:, rt]).abs().max()) <= 1e-4
+    _check_oracle(o, l, q, k, v, rows[::5], (0, w.heads - 1))
+
+
 def test_fused_ring_staged_equals_overlapped_bits():
     """Mode 3 waits for every receive before the launch (no wait is polled,
     nothing overlaps): the same kernel on the same data, so the same bits as
@@ -266,7 +329,7 @@ def test_fused_ring_graph_replays_match_eager():
         call = (lambda: _rank(p, qd, kd, vd, rank)) if rank is not None else (lambda: _full(p, qd, kd, vd))
         p.set_graph(False)
         ref = call()
-        assert p.fused_ring_active()
+        assert p.fused_ring_active() == 2  # (with the key split)
         p.set_graph(True)
         for i in range(4):
             junk = torch.randn(1 << 20, device=dev).sum()  # eager work between replays
