@@ -96,14 +96,18 @@ def time_calls(plan, w, bufs, stream, steps, warmup, warmup_seconds=0.0):
     return ev[0].elapsed_time(ev[steps]) / steps
 
 
-def step_kernel_times(plan, w, bufs, stream, reps, graph=False):
+def step_kernel_times(plan, w, bufs, stream, reps, graph=False, queued=1):
     """Per-(rank, step) attention-kernel ms from the library's own HIP events
-    (recorded by eager calls: graph mode records no step events)."""
+    (recorded by eager calls: graph mode records no step events).  queued > 1:
+    each sample is the last of that many calls queued back to back, so the
+    launch runs as in the timed loop rather than on a GPU left idle by the
+    host's wait for the previous call's events."""
     plan.set_graph(False)
     plan.set_step_timing(True)
     acc = None
     for _ in range(reps):
-        run_call(plan, w, bufs, stream)
+        for _ in range(queued):
+            run_call(plan, w, bufs, stream)
         t = np.array(plan.last_step_times())
         acc = t if acc is None else acc + t
     plan.set_step_timing(False)
@@ -120,7 +124,7 @@ def kernel_launches(plan, w, bufs, stream, reps):
     run_call(plan, w, bufs, stream)
     torch.cuda.synchronize()
     fused = plan.fused_ring_active()
-    times = step_kernel_times(plan, w, bufs, stream, reps)
+    times = step_kernel_times(plan, w, bufs, stream, reps, queued=4)
     ranks = range(w.cp) if w.rank is None else [w.rank]
     return ("fused_ring" if fused else "per_step"), [times[r][s] for r in ranks for s in range(w.cp) if times[r][s] > 0]
 
@@ -307,7 +311,8 @@ def rank_step_imbalance(plan, w, bufs, stream, reps=3):
     per-(rank, step) step-kernel ms of the one-launch-per-step schedule,
     per-step max/mean over ranks, and the valid 128x64 tile counts (the
     plan's balance); then every rank's share measured whole: back to back
-    with the fused ring, back to back one launch per step, and in lockstep."""
+    with the fused ring, back to back one launch per step, and in lockstep;
+    and each rank's fused call alone."""
     plan.set_fused_ring(False)
     times = []
     for r in range(w.cp):
@@ -348,7 +353,26 @@ def rank_step_imbalance(plan, w, bufs, stream, reps=3):
         full[mode] = ev[0].elapsed_time(ev[1]) / reps
     plan.set_lockstep(False)
     plan.set_fused_ring(True)
-    measured = {"all_ranks_fused_ring_ms": round(full["fused"], 5),
+    # each rank's fused call alone: a ring whose ranks each run one fused
+    # launch moves at the slowest rank's call
+    rank_ms = []
+    for r in range(w.cp):
+        for _ in range(2):
+            plan.rank_forward(*bufs, r, stream=stream)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        n = max(reps, 10)
+        ev[0].record(stream)
+        for _ in range(n):
+            plan.rank_forward(*bufs, r, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        rank_ms.append(ev[0].elapsed_time(ev[1]) / n)
+    measured = {"fused_ring_rank_ms": [round(x, 5) for x in rank_ms],
+                "fused_ring_max_over_rank0": round(max(rank_ms) / rank_ms[0], 4),
+                "fused_ring_max_over_mean": round(max(rank_ms) / (sum(rank_ms) / len(rank_ms)), 4),
+                "fused_ring_slowest_rank_tflops_per_gpu": round(flops_all / w.cp / (max(rank_ms) * 1e-3) / 1e12, 2),
+                "all_ranks_fused_ring_ms": round(full["fused"], 5),
                 "fused_ring_tflops_per_gpu": round(flops_all / (full["fused"] * 1e-3) / 1e12, 2),
                 "all_ranks_back_to_back_ms": round(full["per_step"], 5), "all_ranks_lockstep_ms": round(full["lockstep"], 5),
                 "lockstep_ms_per_rank": round(full["lockstep"] / w.cp, 5),
@@ -615,7 +639,7 @@ def main():
         for nb in (64, 128, 256, 512, 1024):
             plan.set_recv_blocks(nb)
             ms_blocks[nb] = round(time_calls(plan, w, bufs, stream, max(3, args.steps // 4), 1), 5)
-        plan.set_recv_blocks(256 if args.recv_blocks is None else args.recv_blocks)
+        plan.set_recv_blocks(-1 if args.recv_blocks is None else args.recv_blocks)
         recv_ms = {}
         for mode in ("memcpy", "fused", "hybrid", "kernel"):
             plan.set_recv(mode)

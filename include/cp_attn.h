@@ -84,9 +84,11 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
 #define CP_ATTN_OPT_POISON 4      /* 1: fill each receive slot / partial buffer with NaN once consumed */
 #define CP_ATTN_OPT_STEP_TIMING 5 /* 1: time every ring step's attention kernel with HIP events (a
                                      fused-ring call's one launch per rank under step 0) */
-#define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel (default 256; 0: one
-                                     workgroup per 128 vectors of 16 bytes); a small grid shares the
-                                     GPU with the attention kernel it overlaps.  A receive that
+#define CP_ATTN_OPT_RECV_BLOCKS 6 /* grid bound of the ring-receive copy kernel (0: one workgroup
+                                     per 128 vectors of 16 bytes); a small grid shares the GPU with
+                                     the attention kernel it overlaps.  -1 (default): automatic,
+                                     256 beside a per-step launch, 1024 beside the fused ring's
+                                     launch (whose later steps wait for the receives).  A receive that
                                      overlaps no attention kernel (serial order, or a ring step
                                      with no valid pair, e.g. under document masks) always takes
                                      the full grid */

@@ -225,7 +225,8 @@ struct RunCfg {
   char* ws = nullptr;      // workspace base (ws_layout offsets apply)
   bool serial = false;     // every step on the caller's stream, no events
   int recv = 0;            // CP_ATTN_OPT_RECV in effect
-  int recv_blocks = 256;   // CP_ATTN_OPT_RECV_BLOCKS in effect
+  int recv_blocks = 256;   // CP_ATTN_OPT_RECV_BLOCKS in effect beside a step launch
+  int recv_blocks_fused = 1024;  // and beside the fused ring's one launch
   int fused_ring = 0;      // CP_ATTN_OPT_FUSED_RING in effect
   bool capturing = false;  // the calls are being recorded into a graph
   bool counters = false;   // device work counters (plan-owned buffer)
@@ -238,7 +239,12 @@ RunCfg plan_cfg(const Plan& p, bool capturing) {
   c.ws = static_cast<char*>(p.dev->ws);
   c.serial = p.opt_serialize != 0;
   c.recv = p.opt_recv;
-  c.recv_blocks = p.opt_recv_blocks;
+  // automatic receive grid: beside one step launch, 256 workgroups leave it
+  // its compute units; the fused launch's later steps wait for the receives,
+  // which then need the wider grid to keep ahead (32k/cp8: the late ranks'
+  // calls 1.10 ms at 256, 0.96 at 1024, as rank 0's)
+  c.recv_blocks = p.opt_recv_blocks < 0 ? 256 : p.opt_recv_blocks;
+  c.recv_blocks_fused = p.opt_recv_blocks < 0 ? 1024 : p.opt_recv_blocks;
   c.counters = p.opt_counters != 0;
   c.timing = p.opt_step_timing != 0 && !capturing;
   c.poison = p.opt_poison != 0;
@@ -772,7 +778,7 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   for (int s = 1; s < P; ++s) {
     const RecvArgs ra = recv_ranges_to(p, k2 + int64_t(s - 1) * kvs, v2 + int64_t(s - 1) * kvs, k, v, p.step(r, s).src);
     // the first receive is needed soonest: the full grid; then the narrow one
-    CPA_HIP(launch_recv(ra, s == 1 ? 0 : c.recv_blocks, d.copy));
+    CPA_HIP(launch_recv(ra, s == 1 ? 0 : c.recv_blocks_fused, d.copy));
     CPA_HIP(launch_ring_signal(d.fr_flags + s, d.fr_flags, d.copy));
   }
   if (c.fused_ring == 3) {
@@ -1349,7 +1355,7 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
       p.opt_step_timing = value != 0;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_RECV_BLOCKS:
-      if (value < 0) return fail(CP_ATTN_EINVAL, "recv_blocks must be >= 0");
+      if (value < -1) return fail(CP_ATTN_EINVAL, "recv_blocks must be >= -1");
       p.opt_recv_blocks = value;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_GRAPH:
@@ -1626,7 +1632,7 @@ int cp_attn_rank_forward_noalloc(cp_attn_plan_t h, const void* q, const void* k,
   c.ws = base;
   c.serial = true;
   c.recv = 2;
-  c.recv_blocks = p.opt_recv_blocks;
+  c.recv_blocks = p.opt_recv_blocks < 0 ? 256 : p.opt_recv_blocks;
   c.poison = p.opt_poison != 0;
   return run_rank(p, c, q, k, v, out, lse, rank, static_cast<hipStream_t>(stream));
   CPA_GUARD_END

@@ -174,7 +174,7 @@ def test_schedule_modes_agree(dtype):
     full_grid = _run(p, q, k, v)
     p.set_recv_blocks(3)
     small_grid = _run(p, q, k, v)
-    p.set_recv_blocks(256)
+    p.set_recv_blocks(-1)
     p.set_recv("fused")
     fused = _run(p, q, k, v)
     p.set_poison(True)
