@@ -438,10 +438,14 @@ def backward_section(plan, w, bufs, stream, reps):
     plan.set_backward_key_kernel("four")  # one wave per 32-key column, for comparison
     plan.rank_backward(*args, stream=stream)
     ms_four = timed()
-    plan.set_backward_key_kernel("eight")  # the default; its call writes dq last
-    plan.rank_backward(*args, stream=stream)
-    ms = timed()
+    plan.set_backward_key_kernel("eight")
     flops = 2.5 * 4 * w.head_dim * w.heads * share_pairs(plan, w)
+    fused_ms = {}
+    for mode in (0, 2, 1):  # the last one (the default schedule) writes dq last
+        plan.set_backward_fused(mode)
+        plan.rank_backward(*args, stream=stream)
+        fused_ms[mode] = timed()
+    ms = fused_ms[1]
     tflops = flops / (ms * 1e-3) / 1e12
     # dQ of sampled rows of the share (written by the last call in full)
     rows = oracle.rank_positions(w.seq_len, w.cp, w.rank, w.layout)
@@ -453,6 +457,10 @@ def backward_section(plan, w, bufs, stream, reps):
     return {"ms_per_call": round(ms, 5), "tflops": round(tflops, 2),
             "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "valid_flops": flops,
             "four_wave_key_kernel_ms_per_call": round(ms_four, 5),
+            "schedules": {name: {"ms_per_call": round(fused_ms[m], 5),
+                                 "tflops": round(flops / (fused_ms[m] * 1e-3) / 1e12, 2),
+                                 "frac_bf16_peak": round(flops / (fused_ms[m] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                          for name, m in (("per_step", 0), ("fused_dq", 1), ("all_gather_form", 2))},
             "flop_convention": "2.5 x forward valid flops",
             "parity_dq_sampled_rows": {"rows": sample.tolist(), "max_rel_err": rel, "tol": 2e-2, "ok": rel <= 2e-2}}
 

@@ -166,6 +166,18 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      polled and nothing overlaps: for tools that run one kernel at a
                                      time (counter collection), under which mode 1's waits can only
                                      run out.  Results bit-identical to mode 1. */
+#define CP_ATTN_OPT_BWD_FUSED 14  /* backward schedule (bf16, head_dim 128, no documents, no padding,
+                                     S x H x D x 2 bytes below 2 GiB; elsewhere 0).  0: per ring
+                                     step a dK/dV launch and a dQ launch, dQ stored between steps.
+                                     1 (default): dQ of every ring step in one launch: a row's keys
+                                     over all steps are one prefix of the natural order (the keys
+                                     before its chunk, then its chunk's causal part; every key
+                                     without the mask), taken in natural order with dQ in
+                                     registers and written once; dK/dV per step as in 0.  2: dK/dV
+                                     in one launch as well, over the same prefixes: the all-gather
+                                     form of "Context Parallelism in MegaDLMs", "Key-Value
+                                     Communication Patterns" (every source's K/V present at once).
+                                     Results agree with mode 0 to rounding (summation order). */
 
 /*
  * Create a plan (host only: no device memory, no HIP call).

@@ -36,6 +36,7 @@ OPT_COUNTERS = 9
 OPT_BWD_KEYS = 10
 OPT_LOCKSTEP = 12
 OPT_FUSED_RING = 13
+OPT_BWD_FUSED = 14
 
 NOALLOC_SCRATCH_BYTES = 128 << 20  # CP_ATTN_NOALLOC_SCRATCH_BYTES
 

@@ -102,6 +102,13 @@ class Plan:
             raise ValueError(f"fused ring mode must be a bool, 'timeout_test' or 'staged', not {mode!r}")
         self.set_option(N.OPT_FUSED_RING, value)
 
+    def set_backward_fused(self, mode):
+        """Backward schedule: 0 dK/dV and dQ per ring step; 1 (default) dQ of
+        every step in one launch; 2 dK/dV in one launch too (the all-gather
+        form).  Served for bf16 head_dim 128 without documents or padding;
+        elsewhere mode 0."""
+        self.set_option(N.OPT_BWD_FUSED, int(mode))
+
     def fused_ring_active(self):
         """1 if the last forward call ran each rank as one fused launch, 2 if
         the last rank it computed also split its row tiles' keys in that

@@ -1167,9 +1167,64 @@ void bwd_tile_sizes(const Plan& p, int* rows, int* keys) {
   }
 }
 
+// The backward over the natural-order K/V as one source: local row runs of
+// rank r (its chunks) whose key prefix is every key before the chunk
+// (causal, the chunk's own keys as the diagonal) or every key (bidirectional),
+// the run that sees more keys first.  The keys of all ring steps of a row are
+// then one prefix of the natural order, so one launch of each kernel covers
+// every step: the keys each step's source holds, in natural order instead of
+// step order.  Served for the matrix-core kernels without documents or
+// padding while a K/V row offset stays below 2^31 bytes.
+bool bwd_fused_served(const Plan& p) {
+  if (!p.opt_bwd_fused || !bwd_mfma(p.dtype == CP_ATTN_BF16, p.head_dim)) return false;
+  if (!p.doc_starts.empty() || p.padded_len != p.seq_len) return false;
+  return p.seq_len * int64_t(p.heads) * p.head_dim * p.elem_bytes() < (int64_t(1) << 31);
+}
+
+void bwd_fused_args(const Plan& p, int r, int bt_rows, int bt_keys, BwdArgs& a) {
+  const int64_t C = p.layout == 1 ? p.chunk : p.n_loc;
+  const int nch = p.layout == 1 ? 2 : 1;
+  Segment segs[2];
+  for (int c = 0; c < nch; ++c) {
+    Segment& g = segs[c];
+    g.q_start = c * C;
+    g.q_len = C;
+    g.q_global = p.global_row(r, c * C);
+    g.kv_full = p.causal ? g.q_global : p.seq_len;
+    g.diag = p.causal ? 1 : 0;
+  }
+  if (nch == 2 && segs[1].kv_full > segs[0].kv_full) std::swap(segs[0], segs[1]);
+  a.kv_lo = 0;
+  a.kv_hi = 0;
+  a.kv_split = int32_t(p.seq_len);
+  a.kv_valid = int32_t(p.seq_len);
+  a.nseg = nch;
+  a.total_tiles = 0;
+  a.seg[1] = SegArgs{};
+  int64_t maxpre = 0;
+  for (int i = 0; i < nch; ++i) {
+    const Segment& g = segs[i];
+    SegArgs& x = a.seg[i];
+    x = SegArgs{};
+    x.q_global = g.q_global;
+    x.q_start = int32_t(g.q_start);
+    x.q_len = int32_t(g.q_len);
+    x.kv_full = int32_t(g.kv_full);
+    x.diag = g.diag;
+    x.epi = 1;  // dQ written once
+    x.ksplit = 1;
+    x.tiles = int32_t((g.q_len + bt_rows - 1) / bt_rows);
+    a.total_tiles += x.tiles;
+    maxpre = std::max<int64_t>(maxpre, g.kv_full + (g.diag ? g.q_len : 0));
+  }
+  a.key_tiles = int32_t((maxpre + bt_keys - 1) / bt_keys);
+  a.doc = nullptr;
+}
+
 // Rank r's share of the backward on one stream: D_i of its rows, then per
 // ring step the key-major (dK, dV) and row-major (dQ) kernels of the step's
-// segments.  K and V are read in place at the source's natural rows, and the
+// segments (CP_ATTN_OPT_BWD_FUSED 1: dQ of every step in one launch; 2:
+// dK, dV of every step in one launch too).  K and V are read in place at the source's natural rows, and the
 // source's dK, dV are accumulated there: on a real ring those partial sums
 // travel with the K/V chunks and arrive home complete after cp steps.
 int run_rank_backward(Plan& p, const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -1203,6 +1258,17 @@ int run_rank_backward(Plan& p, const void* q, const void* k, const void* v, cons
   a.delta_hi = p.layout == 1 ? p.chunk_of(r, 1) * p.chunk : 0;
   a.delta_split = split;
   CPA_HIP(launch_bwd_delta(a, bf16, p.head_dim, st));
+  const bool fused = bwd_fused_served(p);
+  // (the one dQ launch of mode 1 on a side stream beside the per-step dK/dV
+  // launches measured slower than in turn: 3.99 against 3.82 ms at 32k/cp8)
+  if (fused) {
+    BwdArgs f = a;
+    bwd_fused_args(p, r, bt_rows, bt_keys, f);
+    if (p.opt_bwd_fused == 1) f.key_tiles = 0;  // dK, dV per step below
+    const hipError_t e = launch_bwd_bf16_d128(f, p.opt_bwd_keys == 0, st);
+    if (e != hipSuccess) return fail(CP_ATTN_EHIP, std::string("backward launch: ") + hipGetErrorString(e));
+    if (p.opt_bwd_fused == 2) return CP_ATTN_OK;
+  }
   for (int s = 0; s < p.cp; ++s) {
     const StepDesc& sd = p.step(r, s);
     if (sd.nseg == 0) continue;
@@ -1230,6 +1296,7 @@ int run_rank_backward(Plan& p, const void* q, const void* k, const void* v, cons
       maxpre = std::max<int64_t>(maxpre, g.kv_full + (g.diag ? g.q_len : 0));
     }
     a.key_tiles = int32_t((maxpre + bt_keys - 1) / bt_keys);
+    if (fused) a.total_tiles = 0;  // dQ done above
     set_doc(p, ws, a, j);
     const hipError_t e = bwd_mfma(bf16, p.head_dim) ? launch_bwd_bf16_d128(a, p.opt_bwd_keys == 0, st)
                                                     : launch_bwd_generic(a, bf16, p.head_dim, st);
@@ -1377,6 +1444,10 @@ int cp_attn_set_option(cp_attn_plan_t h, int option, int value) {
     case CP_ATTN_OPT_FUSED_RING:
       if (value < 0 || value > 3) return fail(CP_ATTN_EINVAL, "CP_ATTN_OPT_FUSED_RING must be 0, 1, 2 or 3");
       p.opt_fused_ring = value;
+      return CP_ATTN_OK;
+    case CP_ATTN_OPT_BWD_FUSED:
+      if (value < 0 || value > 2) return fail(CP_ATTN_EINVAL, "CP_ATTN_OPT_BWD_FUSED must be 0, 1 or 2");
+      p.opt_bwd_fused = value;
       return CP_ATTN_OK;
     case CP_ATTN_OPT_COUNTERS:
       if (value != 0 && value != 1) return fail(CP_ATTN_EINVAL, "counters option must be 0 or 1");

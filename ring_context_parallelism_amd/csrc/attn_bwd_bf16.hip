@@ -228,7 +228,7 @@ void bwd_dkdv_bf16_d128(BwdArgs a) {
       // document masks: runs start no earlier than the tile's first row's, end
       // no later than its last row's; no later tile reaches these keys once
       // a tile's first run starts past them
-      int tile_klo = 0, tile_khi = a.n_loc;
+      int tile_klo = 0, tile_khi = 0x7fffffff;  // (no document bound)
       if constexpr (kDoc) {
         tile_klo = s_klo[0];
         tile_khi = s_khi[min(kTileRows, g.q_len - r0) - 1];

@@ -57,6 +57,7 @@ struct Plan {
   int32_t opt_bwd_keys = 0;
   int32_t opt_lockstep = 0;
   int32_t opt_fused_ring = 1;
+  int32_t opt_bwd_fused = 1;
   int32_t opt_recv_blocks = -1;  // -1: automatic (256 beside a step launch, 1024 beside the fused ring)
 
   DeviceState* dev = nullptr;

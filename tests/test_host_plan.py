@@ -210,6 +210,10 @@ def test_call_error_codes_enqueue_nothing():
     assert lib.cp_attn_set_option(h, N.OPT_FUSED_RING, -1) == N.EINVAL
     for mode in (3, 2, 1, 0):
         assert lib.cp_attn_set_option(h, N.OPT_FUSED_RING, mode) == N.OK
+    assert lib.cp_attn_set_option(h, N.OPT_BWD_FUSED, 3) == N.EINVAL
+    assert lib.cp_attn_set_option(h, N.OPT_BWD_FUSED, -1) == N.EINVAL
+    for mode in (0, 2, 1):
+        assert lib.cp_attn_set_option(h, N.OPT_BWD_FUSED, mode) == N.OK
     assert lib.cp_attn_set_option(h, N.OPT_RECV_BLOCKS, -2) == N.EINVAL
     for nb in (0, 3, 1024, -1):  # -1: the automatic grid
         assert lib.cp_attn_set_option(h, N.OPT_RECV_BLOCKS, nb) == N.OK
