@@ -151,8 +151,10 @@ typedef struct cp_attn_plan_s* cp_attn_plan_t;
                                      A wait that runs out sets a word that
                                      cp_attn_ring_wait_timeouts reports; that call's results are not
                                      valid.  Results agree with mode 0 to rounding (the merge order
-                                     differs).  Served for bf16 head_dim 128, the zigzag causal
-                                     layout without padding with chunks of whole 64-key tiles, the
+                                     differs).  Served for bf16 head_dim 128, the zigzag and the
+                                     contiguous layouts, causal or bidirectional, without padding,
+                                     with chunks of whole 64-key tiles (a receive no row of the
+                                     rank needs is not made), the
                                      fused merge and the copy-kernel receive (CP_ATTN_OPT_RECV 0),
                                      without documents and the serial, counter and poison modes,
                                      while K/V span at most 4 GiB (graph mode included: each call

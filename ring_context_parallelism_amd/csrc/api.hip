@@ -78,6 +78,8 @@ struct DeviceState {
   // (part 0 of late and early rows, then their part 1), used where fr_split[rank]
   std::vector<SegArgs> fr_split_segs;
   std::vector<uint8_t> fr_split;
+  std::vector<uint8_t> fr_need;  // [rank * cp + step]: a run of the rank reads step's slot
+  int fr_nseg = 2;               // row ranges per rank: 2 zigzag (late, early), 1 contiguous
   bool fr_ok = false;            // the plan's runs are whole tiles (built once)
   bool fr_built = false;
   uint32_t* fr_err = nullptr;
@@ -524,8 +526,9 @@ int launch_rank_finalize(Plan& p, const char* ws, void* out, float* lse, int r, 
 // Parallelism IV", section 5, "Overlap: More Than One Stream"), each into a
 // slot of its own and followed by a one-thread kernel that stores the call's
 // epoch to the step's flag; a workgroup waits for that flag before loading
-// any key of the step.  Served for bf16 head_dim 128, the zigzag causal
-// layout without padding, chunks of whole 64-key tiles, the fused merge and
+// any key of the step.  Served for bf16 head_dim 128, zigzag (two row ranges)
+// and contiguous (one) layouts, causal or bidirectional, without padding,
+// chunks of whole 64-key tiles, the fused merge and
 // the copy-kernel receive, outside the serial, counter and poison modes,
 // without document masks, while the own K/V and the slots each span at most
 // 4 GiB.  Step timing reports the launch under step 0.  The call's epoch
@@ -537,7 +540,7 @@ constexpr int kRingPolls = 1 << 18;  // polls (each a coherent load and a short 
 
 bool fused_ring_served(const Plan& p, const RunCfg& c) {
   if (!c.fused_ring || c.serial || c.recv != 0 || c.counters || c.poison) return false;
-  if (p.dtype != CP_ATTN_BF16 || p.head_dim != 128 || p.layout != 1 || !p.causal || p.opt_merge != 0) return false;
+  if (p.dtype != CP_ATTN_BF16 || p.head_dim != 128 || p.opt_merge != 0) return false;
   if (!p.doc_starts.empty() || p.cp < 2 || kv_beyond_32bit(p) || p.padded_len != p.seq_len) return false;
   if (int64_t(p.cp - 1) * ws_layout(p).kv_bytes > int64_t(UINT32_MAX)) return false;
   return p.dev->fr_ok || !p.dev->fr_built;  // (the run check needs the table: built at the first call)
@@ -667,16 +670,23 @@ int ensure_fused_ring(Plan& p) {
     d.fr_segs.assign(size_t(p.cp) * 2, SegArgs{});
     d.fr_split_segs.assign(size_t(p.cp) * 4, SegArgs{});
     d.fr_split.assign(size_t(p.cp), 0);
+    d.fr_need.assign(size_t(p.cp) * p.cp, 0);
     bool ok = true;
     const int bm = attn_bf16_block_m(128);
+    // zigzag: the late rows first (causal: they see more keys), then the
+    // early rows; contiguous: the rank's one chunk
+    const int nr = p.layout == 1 ? 2 : 1;
+    d.fr_nseg = nr;
     for (int r = 0; r < p.cp && ok; ++r) {
-      const int64_t R0[2] = {p.chunk, 0};  // late rows first: they see more keys
+      const int64_t R0[2] = {nr == 2 ? p.chunk : 0, 0};
       std::vector<RingRun> runs[2];
-      for (int i = 0; i < 2 && ok; ++i) {
+      for (int i = 0; i < nr && ok; ++i) {
         SegArgs& sa = d.fr_segs[size_t(r) * 2 + i];
         ok = ring_runs(p, r, R0[i], runs[i], sa);
         sa.run0 = int32_t(all.size());
         all.insert(all.end(), runs[i].begin(), runs[i].end());
+        for (const RingRun& u : runs[i])
+          if (u.step > 0) d.fr_need[size_t(r) * p.cp + u.step] = 1;
       }
       if (!ok) break;
       // key split: where the launch would leave compute units idle (few
@@ -776,6 +786,7 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   CPA_HIP(hipEventRecord(d.start, st));
   CPA_HIP(hipStreamWaitEvent(d.copy, d.start, 0));
   for (int s = 1; s < P; ++s) {
+    if (!d.fr_need[size_t(r) * P + s]) continue;  // no row of the rank sees that source (causal, contiguous)
     const RecvArgs ra = recv_ranges_to(p, k2 + int64_t(s - 1) * kvs, v2 + int64_t(s - 1) * kvs, k, v, p.step(r, s).src);
     // the first receive is needed soonest: the full grid; then the narrow one
     CPA_HIP(launch_recv(ra, s == 1 ? 0 : c.recv_blocks_fused, d.copy));
@@ -805,7 +816,7 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   a.scale = 1.0f / std::sqrt(float(p.head_dim));
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.out_f32 = 0;
-  a.nseg = 2;
+  a.nseg = d.fr_nseg;
   const bool split = p.opt_ksplit && d.fr_split[size_t(r)];
   for (int i = 0; i < 2; ++i) {
     a.seg[i] = split ? d.fr_split_segs[size_t(r) * 4 + i] : d.fr_segs[size_t(r) * 2 + i];

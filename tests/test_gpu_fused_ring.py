@@ -70,6 +70,14 @@ CASES = [
     (1536, 4, 2),     # chunks of 192 keys: runs of three tiles
 ]
 
+# other layouts and masks: (seq, cp, heads, layout, causal)
+LAYOUT_CASES = [
+    (2048, 4, 3, "contiguous", True),    # a rank sees only the sources before it
+    (2048, 4, 3, "contiguous", False),
+    (2048, 4, 2, "zigzag", False),
+    (4096, 8, 2, "contiguous", False),   # chunks of 512 keys, seven receives, key split
+]
+
 
 @pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}_cp{c[1]}_h{c[2]}" for c in CASES])
 def test_fused_ring_every_row_against_oracle_and_step_launches(case):
@@ -102,6 +110,78 @@ def test_fused_ring_every_row_against_oracle_and_step_launches(case):
         assert torch.isnan(o_r[others].float()).all(), r
     assert not p.ring_wait_timeouts()
     p.close()
+
+
+def _rows_any(p, layout, r):
+    if layout == "zigzag":
+        return _rows_of(p, r)
+    n = p.seq_len // p.cp_size
+    return np.arange(r * n, (r + 1) * n)
+
+
+@pytest.mark.parametrize("case", LAYOUT_CASES, ids=[f"s{c[0]}_cp{c[1]}_h{c[2]}_{c[3]}_{'causal' if c[4] else 'bidir'}" for c in LAYOUT_CASES])
+def test_fused_ring_layouts_and_bidirectional(case):
+    """The contiguous layout (one row range per rank) and bidirectional
+    attention in the fused launch: every row of every head against the
+    oracle, within rounding of one launch per step, each rank's call
+    writing its rows only."""
+    seq, cp, heads, layout, causal = case
+    _say(f"fused ring, layout/mask: {case}")
+    q, k, v = make_qkv(seq, heads, 128, "bf16", 98)
+    dev = _dev()
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    p = Plan(seq, cp, heads, 128, causal, layout)
+    p.set_fused_ring(False)
+    ref = _full(p, qd, kd, vd)
+    p.set_fused_ring(True)
+    o, l = _full(p, qd, kd, vd)
+    assert p.fused_ring_active()
+    assert not p.ring_wait_timeouts()
+    qn, kn, vn = (to_numpy_f64(t) for t in (q, k, v))
+    for h in range(heads):
+        o_r, l_r = oracle.attention(qn[:, h:h + 1], kn[:, h:h + 1], vn[:, h:h + 1], causal=causal)
+        assert float(np.max(np.abs(o[:, h:h + 1].double().numpy() - o_r))) <= 2e-2, h
+        assert float(np.max(np.abs(l[h].double().numpy() - l_r[0]))) <= 1e-3, h
+    assert float((o.float() - ref[0].float()).abs().max()) <= 1.6e-2
+    assert float((l - ref[1]).abs().max()) <= 1e-4
+    for r in (0, cp - 1):
+        o_r, l_r = _rank(p, qd, kd, vd, r)
+        rows = torch.as_tensor(_rows_any(p, layout, r))
+        assert _same(o_r[rows], o[rows]) and _same(l_r[:, rows], l[:, rows]), r
+        others = torch.ones(seq, dtype=torch.bool)
+        others[rows] = False
+        assert torch.isnan(o_r[others].float()).all(), r
+    assert not p.ring_wait_timeouts()
+    p.close()
+
+
+def test_fused_ring_full_size_bidirectional_contiguous_rank0():
+    """The 65536-token cp 16 bidirectional contiguous rank-0 share (8 heads):
+    fused (key-split) launch within rounding of one launch per step on every
+    row, sampled rows of the first and last head against the oracle."""
+    w = WORKLOADS["bidir_s65536_cp16_contiguous_h8_d128_bf16_rank0"]
+    _say(f"fused ring, full size: {w.name}")
+    q, k, v = workload_qkv(w)
+    dev = _dev()
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    p = Plan(w.seq_len, w.cp, w.heads, w.head_dim, w.causal, w.layout)
+    p.set_fused_ring(False)
+    ref = _rank(p, qd, kd, vd, 0)
+    p.set_fused_ring(True)
+    o, l = _rank(p, qd, kd, vd, 0)
+    assert p.fused_ring_active()
+    assert not p.ring_wait_timeouts()
+    p.close()
+    rows = np.arange(w.seq_len // w.cp)
+    rt = torch.as_tensor(rows)
+    assert float((o[rt].float() - ref[0][rt].float()).abs().max()) <= 1.6e-2
+    assert float((l[:, rt] - ref[1][:, rt]).abs().max()) <= 1e-4
+    qn, kn, vn = (to_numpy_f64(t) for t in (q, k, v))
+    sample = rows[::97]
+    for h in (0, w.heads - 1):
+        o_r, l_r = oracle.attention(qn[sample][:, h:h + 1], kn[:, h:h + 1], vn[:, h:h + 1], causal=False)
+        assert float(np.max(np.abs(o[sample, h:h + 1].double().numpy() - o_r))) <= 2e-2, h
+        assert float(np.max(np.abs(l[h, sample].double().numpy() - l_r[0]))) <= 1e-3, h
 
 
 def test_fused_ring_calls_back_to_back_and_new_buffers():
@@ -161,14 +241,14 @@ def test_fused_ring_forced_timeout_is_reported():
 
 
 def test_fused_ring_falls_back_where_not_served():
-    """Padding, the contiguous layout, bidirectional attention, documents,
+    """Padding, documents,
     fp32, head_dim 64, the separate merge, the serial mode, the memcpy
     receive, work counters and poison take one
     launch per step with the option set: the same bits as without it, and
     no wait is polled (the time-out test mode would report one)."""
     dev = _dev()
     setups = [
-        dict(seq=1003), dict(layout="contiguous"), dict(causal=False), dict(docs=[0, 100, 700]),
+        dict(seq=1003), dict(docs=[0, 100, 700]),
         dict(dtype=torch.float32), dict(dim=64), dict(opt="merge"), dict(opt="serial"), dict(opt="memcpy"),
         dict(opt="counters"), dict(opt="poison"),
     ]
