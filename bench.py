@@ -172,7 +172,7 @@ def cpu_baseline(w, q, k, v, out, lse, target_s):
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count() or 1
-    workers = max(1, min(avail, 16))  # a one-GPU machine's share of the host is 16 cores
+    workers = max(1, min(avail, 16))  # at most 16 worker threads
     ranks = range(w.cp) if w.rank is None else [w.rank]
     rows = np.concatenate([oracle.rank_positions(w.seq_len, w.cp, r, w.layout) for r in ranks])
     rows = rows[:: max(1, rows.size // 4096)][:4096]
