@@ -79,7 +79,17 @@ struct DeviceState {
   std::vector<SegArgs> fr_split_segs;
   std::vector<uint8_t> fr_split;
   std::vector<uint8_t> fr_need;  // [rank * cp + step]: a run of the rank reads step's slot
+  // second lane of cp_attn_full_forward's fused ranks (odd ranks): its own
+  // compute and copy streams, slots, flags and events, so that one rank's
+  // launch runs beside the next one's
+  hipStream_t fl_comp = nullptr, fl_copy = nullptr;
+  char* fl_slots = nullptr;
+  int64_t fl_slots_bytes = 0;
+  uint32_t* fl_flags = nullptr;
+  char* fl_split = nullptr;  // key split's partial outputs, LSEs and counters of the second lane
+  hipEvent_t fl_enter = nullptr, fl_join = nullptr, fl_start = nullptr, fl_recv[2] = {nullptr, nullptr};
   int fr_nseg = 2;               // row ranges per rank: 2 zigzag (late, early), 1 contiguous
+  bool fr_lanes = false;         // full forward: two lanes (short launches only)
   bool fr_ok = false;            // the plan's runs are whole tiles (built once)
   bool fr_built = false;
   uint32_t* fr_err = nullptr;
@@ -739,6 +749,13 @@ int ensure_fused_ring(Plan& p) {
       }
     }
     if (!ok) return CP_ATTN_OK;  // served no more: the per-step launches take over
+    // Two lanes pay off for short launches only: 8k/cp4/32 heads (at most
+    // 128 key tiles per row tile) 0.62 against 0.71 ms per full forward;
+    // 16k/cp4/16 heads (256) 1.14 against 1.13; 32k/cp8/32 heads (512) 8.56
+    // against 7.65 (the two launches' waits and working sets collide)
+    int64_t most = 0;
+    for (const SegArgs& sa : d.fr_segs) most = std::max<int64_t>(most, sa.kv_full + (sa.diag ? sa.q_len : 0));
+    d.fr_lanes = most <= 192 * 64;
     void* m = nullptr;
     CPA_HIP(hipMalloc(&m, all.size() * sizeof(RingRun)));
     d.fr_runs = static_cast<RingRun*>(m);
@@ -772,30 +789,80 @@ int ensure_fused_ring(Plan& p) {
   return CP_ATTN_OK;
 }
 
+// The second lane's streams, events, slots and flags (made once; the slots
+// grow with the plan's need like the first lane's).
+int ensure_fused_lane(Plan& p) {
+  DeviceState& d = *p.dev;
+  if (!d.fl_comp) {
+    CPA_HIP(hipStreamCreateWithFlags(&d.fl_comp, hipStreamNonBlocking));
+    CPA_HIP(hipStreamCreateWithFlags(&d.fl_copy, hipStreamNonBlocking));
+    for (hipEvent_t* e : {&d.fl_enter, &d.fl_join, &d.fl_start, &d.fl_recv[0], &d.fl_recv[1]})
+      CPA_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
+    void* m = nullptr;
+    CPA_HIP(hipMalloc(&m, size_t(p.cp) * sizeof(uint32_t)));
+    d.fl_flags = static_cast<uint32_t*>(m);
+    CPA_HIP(hipMemset(d.fl_flags, 0, size_t(p.cp) * sizeof(uint32_t)));
+    CPA_HIP(hipDeviceSynchronize());
+  }
+  bool odd_split = false;
+  for (int r = 1; r < p.cp; r += 2) odd_split = odd_split || d.fr_split[size_t(r)];
+  if (odd_split && !d.fl_split) {
+    const WsLayout w = ws_layout(p);
+    void* m = nullptr;
+    const int64_t bytes = 2 * align256(w.o_bytes) + 2 * align256(w.lse_bytes) + align256(w.cnt_bytes);
+    if (hipMalloc(&m, size_t(bytes)) != hipSuccess)
+      return fail(CP_ATTN_ENOWORKSPACE, "hipMalloc of the second lane's key-split buffers failed");
+    d.fl_split = static_cast<char*>(m);
+  }
+  if (d.fl_slots_bytes < d.fr_slots_bytes) {
+    if (d.fl_slots) {
+      CPA_HIP(hipDeviceSynchronize());
+      CPA_HIP(hipFree(d.fl_slots));
+      d.fl_slots = nullptr;
+      d.fl_slots_bytes = 0;
+    }
+    void* m = nullptr;
+    if (hipMalloc(&m, size_t(d.fr_slots_bytes)) != hipSuccess)
+      return fail(CP_ATTN_ENOWORKSPACE, "hipMalloc of the second lane's fused-ring slots failed");
+    d.fl_slots = static_cast<char*>(m);
+    d.fl_slots_bytes = d.fr_slots_bytes;
+  }
+  return CP_ATTN_OK;
+}
+
+// lane 0: the caller's stream st, the copy stream and the first slots; lane
+// 1 (odd ranks of a full forward): st is the second lane's compute stream,
+// with its own copy stream, slots, flags and key-split buffers
 int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const void* v, void* out, float* lse,
-                   int r, hipStream_t st) {
+                   int r, hipStream_t st, int lane = 0) {
   DeviceState& d = *p.dev;
   const WsLayout w = ws_layout(p);
   const int P = p.cp;
-  CPA_HIP(launch_ring_epoch(d.fr_flags, st));  // this call's epoch, in flag word 0
+  const bool l1 = lane == 1;
+  hipStream_t const cps = l1 ? d.fl_copy : d.copy;
+  char* const slots = l1 ? d.fl_slots : d.fr_slots;
+  uint32_t* const flags = l1 ? d.fl_flags : d.fr_flags;
+  hipEvent_t const ev_start = l1 ? d.fl_start : d.start;
+  hipEvent_t const ev_recv[2] = {l1 ? d.fl_recv[0] : d.recv_done[0], l1 ? d.fl_recv[1] : d.recv_done[1]};
+  CPA_HIP(launch_ring_epoch(flags, st));  // this call's epoch, in flag word 0
   const int64_t kvs = w.kv_bytes;  // one slot of K (or V): the source's n_loc rows
-  char* const k2 = d.fr_slots;
-  char* const v2 = d.fr_slots + align256(int64_t(P - 1) * kvs);
+  char* const k2 = slots;
+  char* const v2 = slots + align256(int64_t(P - 1) * kvs);
   // the copy stream starts behind everything queued on st before this call
   // (an earlier call's kernel may still read the slots)
-  CPA_HIP(hipEventRecord(d.start, st));
-  CPA_HIP(hipStreamWaitEvent(d.copy, d.start, 0));
+  CPA_HIP(hipEventRecord(ev_start, st));
+  CPA_HIP(hipStreamWaitEvent(cps, ev_start, 0));
   for (int s = 1; s < P; ++s) {
     if (!d.fr_need[size_t(r) * P + s]) continue;  // no row of the rank sees that source (causal, contiguous)
     const RecvArgs ra = recv_ranges_to(p, k2 + int64_t(s - 1) * kvs, v2 + int64_t(s - 1) * kvs, k, v, p.step(r, s).src);
     // the first receive is needed soonest: the full grid; then the narrow one
-    CPA_HIP(launch_recv(ra, s == 1 ? 0 : c.recv_blocks_fused, d.copy));
-    CPA_HIP(launch_ring_signal(d.fr_flags + s, d.fr_flags, d.copy));
+    CPA_HIP(launch_recv(ra, s == 1 ? 0 : c.recv_blocks_fused, cps));
+    CPA_HIP(launch_ring_signal(flags + s, flags, cps));
   }
   if (c.fused_ring == 3) {
     // staged: every receive done before the launch starts (no wait is polled)
-    CPA_HIP(hipEventRecord(d.recv_done[0], d.copy));
-    CPA_HIP(hipStreamWaitEvent(st, d.recv_done[0], 0));
+    CPA_HIP(hipEventRecord(ev_recv[0], cps));
+    CPA_HIP(hipStreamWaitEvent(st, ev_recv[0], 0));
   }
   StepArgs a{};
   a.q = q;
@@ -823,7 +890,7 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
     if (split) a.seg[2 + i] = d.fr_split_segs[size_t(r) * 4 + 2 + i];
     a.total_tiles += a.seg[i].tiles;
   }
-  if (split) {
+  if (split && !l1) {
     for (int b = 0; b < 2; ++b) {
       a.split_o[b] = reinterpret_cast<float*>(c.ws + w.part_o[b]);
       a.split_lse[b] = reinterpret_cast<float*>(c.ws + w.part_lse[b]);
@@ -832,9 +899,17 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
     // (the kernel leaves its counters at zero; a caller may have written the
     // workspace since: cleared by a kernel, which a graph may hold)
     CPA_HIP(launch_fill_words(c.ws + w.split_cnt, split_counters(p), 0u, st));
+  } else if (split) {
+    const int64_t ob = align256(w.o_bytes), lb = align256(w.lse_bytes);
+    for (int b = 0; b < 2; ++b) {
+      a.split_o[b] = reinterpret_cast<float*>(d.fl_split + b * ob);
+      a.split_lse[b] = reinterpret_cast<float*>(d.fl_split + 2 * ob + b * lb);
+    }
+    a.split_cnt = reinterpret_cast<int32_t*>(d.fl_split + 2 * ob + 2 * lb);
+    CPA_HIP(launch_fill_words(d.fl_split + 2 * ob + 2 * lb, split_counters(p), 0u, st));
   }
   a.runs = d.fr_runs;
-  a.ring_flags = d.fr_flags;
+  a.ring_flags = flags;
   a.ring_err = d.fr_err_dev;
   // test mode: an epoch no signal ever stores, and few polls
   a.ring_epoch_add = c.fused_ring == 2 ? 0x40000000u : 0u;
@@ -851,8 +926,8 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   if (c.capturing) {
     // a capture must join every stream it forked (the launch itself only
     // waits on the flags)
-    CPA_HIP(hipEventRecord(d.recv_done[1], d.copy));
-    CPA_HIP(hipStreamWaitEvent(st, d.recv_done[1], 0));
+    CPA_HIP(hipEventRecord(ev_recv[1], cps));
+    CPA_HIP(hipStreamWaitEvent(st, ev_recv[1], 0));
   }
   d.fr_last = split ? 2 : 1;
   return CP_ATTN_OK;
@@ -1380,6 +1455,13 @@ int cp_attn_plan_destroy(cp_attn_plan_t h) {
       if (d.fr_flags) (void)hipFree(d.fr_flags);
       if (d.fr_runs) (void)hipFree(d.fr_runs);
       if (d.fr_err) (void)hipHostFree(d.fr_err);
+      if (d.fl_slots) (void)hipFree(d.fl_slots);
+      if (d.fl_flags) (void)hipFree(d.fl_flags);
+      if (d.fl_split) (void)hipFree(d.fl_split);
+      if (d.fl_comp) (void)hipStreamDestroy(d.fl_comp);
+      if (d.fl_copy) (void)hipStreamDestroy(d.fl_copy);
+      for (hipEvent_t e : {d.fl_enter, d.fl_join, d.fl_start, d.fl_recv[0], d.fl_recv[1]})
+        if (e) (void)hipEventDestroy(e);
       if (d.own_ws && d.ws) (void)hipFree(d.ws);
       if (d.own_copy && d.copy) (void)hipStreamDestroy(d.copy);
       if (d.own_merge && d.merge) (void)hipStreamDestroy(d.merge);
@@ -1731,7 +1813,29 @@ int cp_attn_full_forward(cp_attn_plan_t h, const void* q, const void* k, const v
   if (p.opt_graph) return run_graph(p, q, k, v, out, lse, -1, static_cast<hipStream_t>(stream));
   const RunCfg c = plan_cfg(p, false);
   if (lockstep_served(p, c)) return run_lockstep(p, c, q, k, v, out, lse, static_cast<hipStream_t>(stream));
-  for (int r = 0; r < p.cp; ++r) CPA_TRY(run_rank(p, c, q, k, v, out, lse, r, static_cast<hipStream_t>(stream)));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fused_ring_served(p, c)) {
+    CPA_TRY(ensure_fused_ring(p));
+    DeviceState& d = *p.dev;
+    if (d.fr_ok && d.fr_lanes) {
+      // two lanes: even ranks on the caller's stream, odd ranks on the
+      // second lane, which starts behind the caller's earlier work and
+      // which the caller's stream waits for at the end; a rank's launch then
+      // runs beside its neighbour's, filling the compute units each leaves
+      // idle at its end (results: the same bits as one rank at a time)
+      CPA_TRY(ensure_fused_lane(p));
+      CPA_HIP(hipEventRecord(d.fl_enter, st));
+      CPA_HIP(hipStreamWaitEvent(d.fl_comp, d.fl_enter, 0));
+      for (int r = 0; r < p.cp; ++r) {
+        if (p.valid_rows(r) == 0) continue;
+        CPA_TRY(run_rank_fused(p, c, q, k, v, out, lse, r, (r & 1) ? d.fl_comp : st, r & 1));
+      }
+      CPA_HIP(hipEventRecord(d.fl_join, d.fl_comp));
+      CPA_HIP(hipStreamWaitEvent(st, d.fl_join, 0));
+      return CP_ATTN_OK;
+    }
+  }
+  for (int r = 0; r < p.cp; ++r) CPA_TRY(run_rank(p, c, q, k, v, out, lse, r, st));
   return CP_ATTN_OK;
   CPA_GUARD_END
 }
