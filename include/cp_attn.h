@@ -357,7 +357,13 @@ int cp_attn_rank_forward_noalloc(cp_attn_plan_t plan, const void* q, const void*
 
 /* Every rank's share on `stream` (ranks 0..cp_size-1), back to back, or with
  * CP_ATTN_OPT_LOCKSTEP all ranks' ring step s in one launch; fills all rows
- * of out and lse.  Same arguments and errors as cp_attn_rank_forward. */
+ * of out and lse.  In the fused schedule, when a row tile sees at most 192
+ * key tiles (short launches), the odd ranks run on a second library-owned
+ * stream pair beside the even ones (own receive slots, flags and key-split
+ * buffers, allocated on first use); it starts behind the work queued on
+ * `stream` before the call, and `stream` waits for it at the end, so the
+ * call is ordered on `stream` as a whole.  Same arguments and errors as
+ * cp_attn_rank_forward. */
 int cp_attn_full_forward(cp_attn_plan_t plan, const void* q, const void* k, const void* v, void* out,
                          float* lse, void* stream);
 
