@@ -90,6 +90,11 @@ struct DeviceState {
   hipEvent_t fl_enter = nullptr, fl_join = nullptr, fl_start = nullptr, fl_recv[2] = {nullptr, nullptr};
   int fr_nseg = 2;               // row ranges per rank: 2 zigzag (late, early), 1 contiguous
   bool fr_lanes = false;         // full forward: two lanes (short launches only)
+  // calls recorded into a graph use their own flags, whose word 0 a kernel
+  // advances at the start of each replay; other calls are numbered by the
+  // host (fr_host_epoch) and leave word 0 of their flags at zero
+  uint32_t* fr_gflags = nullptr;
+  uint32_t fr_host_epoch = 0;
   bool fr_ok = false;            // the plan's runs are whole tiles (built once)
   bool fr_built = false;
   uint32_t* fr_err = nullptr;
@@ -763,6 +768,9 @@ int ensure_fused_ring(Plan& p) {
     CPA_HIP(hipMalloc(&m, size_t(p.cp) * sizeof(uint32_t)));
     d.fr_flags = static_cast<uint32_t*>(m);
     CPA_HIP(hipMemset(d.fr_flags, 0, size_t(p.cp) * sizeof(uint32_t)));
+    CPA_HIP(hipMalloc(&m, size_t(p.cp) * sizeof(uint32_t)));
+    d.fr_gflags = static_cast<uint32_t*>(m);
+    CPA_HIP(hipMemset(d.fr_gflags, 0, size_t(p.cp) * sizeof(uint32_t)));
     CPA_HIP(hipDeviceSynchronize());  // zero before any stream of the plan reads them
     void* h = nullptr;
     CPA_HIP(hipHostMalloc(&h, sizeof(uint32_t), hipHostMallocCoherent | hipHostMallocMapped));
@@ -841,10 +849,20 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   const bool l1 = lane == 1;
   hipStream_t const cps = l1 ? d.fl_copy : d.copy;
   char* const slots = l1 ? d.fl_slots : d.fr_slots;
-  uint32_t* const flags = l1 ? d.fl_flags : d.fr_flags;
+  // graph capture: the epoch lives in flag word 0, advanced by a kernel
+  // in every replay; otherwise the host numbers the call (never 0) and
+  // passes the number by value to the signals and the launch
+  const bool dev_epoch = c.capturing;
+  uint32_t* const flags = dev_epoch ? d.fr_gflags : l1 ? d.fl_flags : d.fr_flags;
   hipEvent_t const ev_start = l1 ? d.fl_start : d.start;
   hipEvent_t const ev_recv[2] = {l1 ? d.fl_recv[0] : d.recv_done[0], l1 ? d.fl_recv[1] : d.recv_done[1]};
-  CPA_HIP(launch_ring_epoch(flags, st));  // this call's epoch, in flag word 0
+  uint32_t host_ep = 0;
+  if (dev_epoch) {
+    CPA_HIP(launch_ring_epoch(flags, st));
+  } else {
+    host_ep = ++d.fr_host_epoch;
+    if (host_ep == 0) host_ep = d.fr_host_epoch = 1;
+  }
   const int64_t kvs = w.kv_bytes;  // one slot of K (or V): the source's n_loc rows
   char* const k2 = slots;
   char* const v2 = slots + align256(int64_t(P - 1) * kvs);
@@ -857,7 +875,8 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
     const RecvArgs ra = recv_ranges_to(p, k2 + int64_t(s - 1) * kvs, v2 + int64_t(s - 1) * kvs, k, v, p.step(r, s).src);
     // the first receive is needed soonest: the full grid; then the narrow one
     CPA_HIP(launch_recv(ra, s == 1 ? 0 : c.recv_blocks_fused, cps));
-    CPA_HIP(launch_ring_signal(flags + s, flags, cps));
+    if (dev_epoch) CPA_HIP(launch_ring_signal(flags + s, flags, cps));
+    else CPA_HIP(launch_ring_signal_value(flags + s, host_ep, cps));
   }
   if (c.fused_ring == 3) {
     // staged: every receive done before the launch starts (no wait is polled)
@@ -912,7 +931,7 @@ int run_rank_fused(Plan& p, const RunCfg& c, const void* q, const void* k, const
   a.ring_flags = flags;
   a.ring_err = d.fr_err_dev;
   // test mode: an epoch no signal ever stores, and few polls
-  a.ring_epoch_add = c.fused_ring == 2 ? 0x40000000u : 0u;
+  a.ring_epoch_add = host_ep + (c.fused_ring == 2 ? 0x40000000u : 0u);
   a.ring_polls = c.fused_ring == 2 ? 16 : kRingPolls;
   // step timing: the one launch is reported under step 0
   const size_t ti = size_t(r) * P;
@@ -1453,6 +1472,7 @@ int cp_attn_plan_destroy(cp_attn_plan_t h) {
       if (d.ls_uploaded) (void)hipEventDestroy(d.ls_uploaded);
       if (d.fr_slots) (void)hipFree(d.fr_slots);
       if (d.fr_flags) (void)hipFree(d.fr_flags);
+      if (d.fr_gflags) (void)hipFree(d.fr_gflags);
       if (d.fr_runs) (void)hipFree(d.fr_runs);
       if (d.fr_err) (void)hipHostFree(d.fr_err);
       if (d.fl_slots) (void)hipFree(d.fl_slots);

@@ -103,9 +103,11 @@ struct StepArgs {
   int32_t kpos_split;
   // fused ring (null runs: not fused): the receive slots of steps 1 .. P-1,
   // K and V each one buffer of rows (kv2_bytes addressable from each), the
-  // segments' key runs, and the per-step receive flags; ring_flags[0] holds
-  // the call's epoch (advanced by a kernel before the launch), flag s is
-  // done once it reaches that epoch plus ring_epoch_add; a workgroup polls
+  // segments' key runs, and the per-step receive flags; the call's epoch is
+  // ring_flags[0] plus ring_epoch_add (under graph capture word 0 is
+  // advanced by a kernel before the launch and the addend is 0; otherwise
+  // word 0 stays 0 and the host passes the epoch as the addend), flag s is
+  // done once it reaches that epoch; a workgroup polls
   // flag s (at most ring_polls times) before it loads any row of a run of
   // step s, and a wait that runs out stores 1 to *ring_err (host-visible)
   const void* k2;
@@ -176,6 +178,8 @@ hipError_t launch_attn_bf16_ring(const StepArgs& a, hipStream_t stream);
 // store *epoch to *flag (release, agent scope) from one thread, once every
 // kernel before it on the stream has completed
 hipError_t launch_ring_signal(uint32_t* flag, const uint32_t* epoch, hipStream_t stream);
+// the same with the epoch by value
+hipError_t launch_ring_signal_value(uint32_t* flag, uint32_t epoch, hipStream_t stream);
 // advance the epoch word by one (never to zero), one thread
 hipError_t launch_ring_epoch(uint32_t* epoch, hipStream_t stream);
 // Every rank's step of one ring step in one launch (bf16, head_dim 128, no

@@ -132,6 +132,12 @@ __global__ __launch_bounds__(64) void ring_signal(uint32_t* flag, const uint32_t
   if (threadIdx.x == 0) __hip_atomic_store(flag, *epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The same with the epoch passed by value (calls not recorded into a graph:
+// the host numbers them, and no kernel has to advance a device word first).
+__global__ __launch_bounds__(64) void ring_signal_value(uint32_t* flag, uint32_t epoch) {
+  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ __launch_bounds__(64) void ring_epoch(uint32_t* epoch) {
   if (threadIdx.x == 0) {
     const uint32_t e = *epoch + 1u;
@@ -253,6 +259,11 @@ hipError_t launch_recv(const RecvArgs& a, int blocks, hipStream_t stream) {
 
 hipError_t launch_ring_signal(uint32_t* flag, const uint32_t* epoch, hipStream_t stream) {
   ring_signal<<<1, 64, 0, stream>>>(flag, epoch);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_signal_value(uint32_t* flag, uint32_t epoch, hipStream_t stream) {
+  ring_signal_value<<<1, 64, 0, stream>>>(flag, epoch);
   return hipGetLastError();
 }
 
