@@ -802,15 +802,19 @@ int ensure_fused_ring(Plan& p) {
 int ensure_fused_lane(Plan& p) {
   DeviceState& d = *p.dev;
   if (!d.fl_comp) {
-    CPA_HIP(hipStreamCreateWithFlags(&d.fl_comp, hipStreamNonBlocking));
-    CPA_HIP(hipStreamCreateWithFlags(&d.fl_copy, hipStreamNonBlocking));
+    // (the compute stream last: it marks the lane as made, so a failure
+    // part way leaves the rest to be made again by the next call)
+    if (!d.fl_copy) CPA_HIP(hipStreamCreateWithFlags(&d.fl_copy, hipStreamNonBlocking));
     for (hipEvent_t* e : {&d.fl_enter, &d.fl_join, &d.fl_start, &d.fl_recv[0], &d.fl_recv[1]})
-      CPA_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
-    void* m = nullptr;
-    CPA_HIP(hipMalloc(&m, size_t(p.cp) * sizeof(uint32_t)));
-    d.fl_flags = static_cast<uint32_t*>(m);
-    CPA_HIP(hipMemset(d.fl_flags, 0, size_t(p.cp) * sizeof(uint32_t)));
-    CPA_HIP(hipDeviceSynchronize());
+      if (!*e) CPA_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
+    if (!d.fl_flags) {
+      void* m = nullptr;
+      CPA_HIP(hipMalloc(&m, size_t(p.cp) * sizeof(uint32_t)));
+      d.fl_flags = static_cast<uint32_t*>(m);
+      CPA_HIP(hipMemset(d.fl_flags, 0, size_t(p.cp) * sizeof(uint32_t)));
+      CPA_HIP(hipDeviceSynchronize());
+    }
+    CPA_HIP(hipStreamCreateWithFlags(&d.fl_comp, hipStreamNonBlocking));
   }
   bool odd_split = false;
   for (int r = 1; r < p.cp; r += 2) odd_split = odd_split || d.fr_split[size_t(r)];
